@@ -1,0 +1,163 @@
+/*
+ * ttt_mlp.h -- C ABI of the MI355X (gfx950) TTT-MLP layer scan.
+ *
+ * The operation is the TTT-MLP layer of "One-Minute Video Generation with
+ * Test-Time Training" (paper-notes page, key designs, "TTT-MLP layer" and
+ * "gate + bidirectional"):
+ *
+ *   per head h (channels [h*d, (h+1)*d) of D = H*d), per token t:
+ *     k_t = (X theta_K^T)[t, h],  v_t = (X theta_V^T)[t, h],  q_t = (X theta_Q^T)[t, h]
+ *     f(u; W) = GELU(u W1) W2,    W1: d x m,  W2: m x d  (fp32 state, m = 4d in the paper)
+ *     loss l(W; x_t) = ||f(k_t; W) - v_t||^2    (TTT_LOSS_SUM, the literal form)
+ *                    = (1/d) ||f(k_t; W) - v_t||^2   (TTT_LOSS_MEAN, the default reading)
+ *     W_t = W_{t-1} - eta * grad l            (one gradient step per token)
+ *     z_t = f(q_t; W_t)                       (read-out with the updated state)
+ *     y_t = x_t + tanh(alpha) * z_t           (per-channel gate)
+ *   bidirectional: X' = forward pass with alpha_f; Y = reversed pass over X'
+ *   with alpha_b; both passes start from the same W_0 and use the same theta.
+ *
+ * Mini-batches of b tokens (b = 1 is the per-token rule): every gradient of
+ * a mini-batch is taken at the state the mini-batch starts from; token t
+ * reads out with that state minus eta times the summed gradients of the
+ * tokens s <= t of its mini-batch.  If b does not divide T the last
+ * mini-batch is short.  The reversed pass cuts its mini-batches from the
+ * start of the reversed sequence (i.e. from token T-1 downwards).
+ *
+ * Conventions
+ *   - Every data pointer is a DEVICE pointer on the current HIP device, and
+ *     every buffer belongs to the caller.  The library never allocates or
+ *     frees device memory on a compute call; scratch space comes from the
+ *     caller's workspace (size from ttt_mlp_workspace_size).
+ *   - Dense row-major layouts:
+ *       X, Y      [B, T, D]   io_dtype (fp32, or bf16 as raw 16-bit words)
+ *       theta_qkv [3, D, D]   io_dtype; theta_Q, theta_K, theta_V, each [out, in]
+ *       W1_0      [H, d, m]   fp32, shared by all B sequences
+ *       W2_0      [H, m, d]   fp32
+ *       alpha     [D]         fp32
+ *       Z         [B, T, D]   fp32 pre-gate layer output (optional)
+ *       W1_T      [B, H, d, m], W2_T [B, H, m, d]  fp32 final state (optional)
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     compute call only enqueues work on it and returns; execution errors
+ *     surface at the caller's next synchronisation.  Calls on different
+ *     streams with separate workspaces and outputs may run concurrently.
+ *   - Errors: argument and shape errors are detected on the host before
+ *     anything is enqueued; the call then returns a negative status, writes
+ *     no output, and ttt_mlp_last_error() describes the problem.  A failed
+ *     kernel launch returns TTT_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Thread safety: all entry points may be called from several threads.
+ */
+#ifndef TTT_MLP_H
+#define TTT_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TTT_OK 0
+#define TTT_ERR_INVALID_ARG (-1) /* NULL required pointer, bad size, bad enum, aliasing */
+#define TTT_ERR_UNSUPPORTED (-2) /* valid arguments outside what the kernels implement */
+#define TTT_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than ttt_mlp_workspace_size */
+#define TTT_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed */
+
+/* io_dtype: element type of X, theta_qkv and Y */
+#define TTT_F32 0
+#define TTT_BF16 1
+
+/* loss reduction of the inner self-supervised loss */
+#define TTT_LOSS_MEAN 0 /* (1/d) ||f(k) - v||^2, gradient scale 2/d */
+#define TTT_LOSS_SUM 1  /* ||f(k) - v||^2, gradient scale 2 */
+
+/* GELU form of the inner MLP */
+#define TTT_GELU_ERF 0  /* a * Phi(a), exact */
+#define TTT_GELU_TANH 1 /* 0.5 a (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))) */
+
+/* scan kernel selection */
+#define TTT_ALGO_AUTO 0    /* fastest kernel that supports the shape and dtype */
+#define TTT_ALGO_GENERIC 1 /* fp32 VALU scan, any supported shape */
+#define TTT_ALGO_MFMA 2    /* bf16-operand MFMA scan, fp32 state (bf16 io only) */
+
+typedef struct ttt_mlp_config {
+  int64_t B;        /* sequences, >= 1 */
+  int64_t T;        /* tokens per sequence, >= 0 */
+  int32_t H;        /* heads, >= 1 */
+  int32_t d;        /* head width, D = H*d */
+  int32_t m;        /* hidden width of the inner MLP */
+  int32_t b;        /* mini-batch size, >= 1 */
+  float eta;        /* inner learning rate, finite, >= 0 */
+  int32_t loss;     /* TTT_LOSS_* */
+  int32_t gelu;     /* TTT_GELU_* */
+  int32_t io_dtype; /* TTT_F32 or TTT_BF16 */
+  int32_t algo;     /* TTT_ALGO_* */
+} ttt_mlp_config;
+
+/* Library version, (major << 16) | minor. */
+int32_t ttt_mlp_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* ttt_mlp_status_string(int32_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* ttt_mlp_last_error(void);
+
+/*
+ * Bytes of device workspace a call needs.  bidir = 0 for ttt_mlp_forward,
+ * 1 for ttt_mlp_bidir.  Writes *bytes; returns TTT_OK, or an error for an
+ * invalid or unsupported configuration (same checks as the compute calls).
+ */
+int32_t ttt_mlp_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t* bytes);
+
+/*
+ * One gated direction of the layer: Y = X + tanh(alpha) * TTT(X).
+ *   reverse = 0: tokens t = 0 .. T-1 (causal); 1: t = T-1 .. 0.
+ *   X, theta_qkv, W1_0, W2_0, alpha, Y, workspace: required.
+ *   Z, W1_T, W2_T: optional outputs (NULL to skip).
+ *   Y must not overlap X, and no output may overlap another buffer.
+ */
+int32_t ttt_mlp_forward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
+                        const float* W1_0, const float* W2_0, const float* alpha, int32_t reverse,
+                        void* Y, float* Z, float* W1_T, float* W2_T, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * The bidirectional layer: X' = forward pass (alpha_f) over X, then
+ * Y = reversed pass (alpha_b) over X'.  X' is held in Y between the passes
+ * (rounded to io_dtype, as a stored activation would be).
+ *   Z_f, Z_b: optional pre-gate outputs of the two passes.
+ *   W1_Tf/W2_Tf, W1_Tb/W2_Tb: optional final states of the two passes.
+ */
+int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
+                      const float* W1_0, const float* W2_0, const float* alpha_f,
+                      const float* alpha_b, void* Y, float* Z_f, float* Z_b, float* W1_Tf,
+                      float* W2_Tf, float* W1_Tb, float* W2_Tb, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * The projection step alone (the outer-loop theta_Q/K/V applied to every
+ * token), for inspection: QKV [3, B, H, T, d] fp32, QKV[p, s, h, t, :] =
+ * (X[s, t, :] theta_p^T)[h*d : (h+1)*d].  Accumulates in fp32.
+ */
+int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
+                        float* QKV, void* stream);
+
+/*
+ * Kernel timing, for measurement.  While enabled, every compute call brackets
+ * each kernel launch with HIP events on the stream the kernel runs on.
+ * ttt_mlp_kernel_timing waits for the recorded events and returns the summed
+ * duration (ms) and launch count of one kernel kind since the last reset.
+ *   kind: TTT_KERNEL_PROJECT (the projection GEMM) or TTT_KERNEL_SCAN (the scan).
+ */
+#define TTT_KERNEL_PROJECT 0
+#define TTT_KERNEL_SCAN 1
+int32_t ttt_mlp_set_kernel_timing(int32_t enable);
+int32_t ttt_mlp_kernel_timing(int32_t kind, double* total_ms, int64_t* launches);
+int32_t ttt_mlp_reset_kernel_timing(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_MLP_H */

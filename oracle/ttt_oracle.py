@@ -131,18 +131,21 @@ def inner_grad(W1, W2, K, V, loss: str = "mean", form: str = "erf"):
 # outer-loop projections (page 1, "TTT-MLP layer": theta_K, theta_V, theta_Q)
 # ----------------------------------------------------------------------------
 
-def project(X, theta, H: int):
+def project(X, theta, H: int, heads=None):
     """Q, K, V = X theta_Q^T, X theta_K^T, X theta_V^T, split per head.
 
-    X [T, D], theta [3, D, D] ([out, in]).  Returns three [H, T, d] arrays;
-    head h is channels [h d, (h+1) d) of the projection.
+    X [T, D], theta [3, D, D] ([out, in]).  Returns three [len(heads), T, d]
+    arrays (all H heads by default); head h is channels [h d, (h+1) d) of the
+    projection.
     """
     T, D = X.shape
     d = D // H
+    heads = list(range(H)) if heads is None else list(heads)
+    rows = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads]) if heads else np.zeros(0, int)
     out = []
     for p in range(3):
-        P = X @ theta[p].T
-        out.append(np.ascontiguousarray(P.reshape(T, H, d).transpose(1, 0, 2)))
+        P = X @ theta[p][rows].T
+        out.append(np.ascontiguousarray(P.reshape(T, len(heads), d).transpose(1, 0, 2)))
     return out
 
 
@@ -192,12 +195,14 @@ def _run_heads(jobs, workers: int):
 
 
 def ttt_forward(X, theta, W1_0, W2_0, alpha, *, eta: float, b: int, reverse: bool = False,
-                loss: str = "mean", gelu_form: str = "erf", workers: int = 1):
+                loss: str = "mean", gelu_form: str = "erf", workers: int = 1, heads=None):
     """One gated direction of the layer.
 
     X [B, T, D] float64 (or [T, D]); theta [3, D, D]; W1_0 [H, d, m];
     W2_0 [H, m, d]; alpha [D].  reverse=True runs over t = T..1.
-    Returns dict(Y, Z, W1_T [B, H, d, m], W2_T [B, H, m, d]);
+    heads: optional list of heads to compute (all by default); the outputs
+    then hold only those heads' channels, in the order given.
+    Returns dict(Y, Z, W1_T [B, nh, d, m], W2_T [B, nh, m, d]);
     Y = X + tanh(alpha) * Z, per channel.
     """
     X = np.asarray(X, dtype=np.float64)
@@ -207,24 +212,27 @@ def ttt_forward(X, theta, W1_0, W2_0, alpha, *, eta: float, b: int, reverse: boo
     Bn, T, D = X.shape
     H, d, m = W1_0.shape
     assert H * d == D
+    heads = list(range(H)) if heads is None else list(heads)
+    nh = len(heads)
+    cols = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads]) if heads else np.zeros(0, int)
     theta = np.asarray(theta, dtype=np.float64)
     W1_0 = np.asarray(W1_0, dtype=np.float64)
     W2_0 = np.asarray(W2_0, dtype=np.float64)
-    gate = np.tanh(np.asarray(alpha, dtype=np.float64))
-    Y = np.empty_like(X)
-    Z = np.empty_like(X)
-    W1_T = np.empty((Bn, H, d, m))
-    W2_T = np.empty((Bn, H, m, d))
+    gate = np.tanh(np.asarray(alpha, dtype=np.float64))[cols]
+    Y = np.empty((Bn, T, nh * d))
+    Z = np.empty((Bn, T, nh * d))
+    W1_T = np.empty((Bn, nh, d, m))
+    W2_T = np.empty((Bn, nh, m, d))
     for s in range(Bn):
         Xin = X[s, ::-1] if reverse else X[s]
-        Qh, Kh, Vh = project(np.ascontiguousarray(Xin), theta, H)
-        jobs = [(Qh[h], Kh[h], Vh[h], W1_0[h], W2_0[h], eta, b, loss, gelu_form) for h in range(H)]
+        Qh, Kh, Vh = project(np.ascontiguousarray(Xin), theta, H, heads)
+        jobs = [(Qh[i], Kh[i], Vh[i], W1_0[h], W2_0[h], eta, b, loss, gelu_form) for i, h in enumerate(heads)]
         res = _run_heads(jobs, workers)
-        Zs = np.empty((T, D))
-        for h, (Zh, w1, w2) in enumerate(res):
-            Zs[:, h * d:(h + 1) * d] = Zh
-            W1_T[s, h], W2_T[s, h] = w1, w2
-        Ys = Xin + gate * Zs
+        Zs = np.empty((T, nh * d))
+        for i, (Zh, w1, w2) in enumerate(res):
+            Zs[:, i * d:(i + 1) * d] = Zh
+            W1_T[s, i], W2_T[s, i] = w1, w2
+        Ys = Xin[:, cols] + gate * Zs
         if reverse:
             Zs, Ys = Zs[::-1], Ys[::-1]
         Z[s], Y[s] = Zs, Ys

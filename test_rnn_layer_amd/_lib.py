@@ -1,0 +1,171 @@
+"""Thin ctypes binding of libttt_mlp.so (the C ABI declared in include/ttt_mlp.h).
+
+Only argument marshalling lives here: torch supplies device memory (outputs
+and workspace are allocated with torch.empty on the input's device) and the
+current HIP stream; every arithmetic step runs in the library's kernels.  If
+the library is missing, loading raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libttt_mlp.so")
+
+TTT_OK, TTT_ERR_INVALID_ARG, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_HIP = 0, -1, -2, -3, -4
+TTT_F32, TTT_BF16 = 0, 1
+TTT_LOSS_MEAN, TTT_LOSS_SUM = 0, 1
+TTT_GELU_ERF, TTT_GELU_TANH = 0, 1
+TTT_ALGO_AUTO, TTT_ALGO_GENERIC, TTT_ALGO_MFMA = 0, 1, 2
+TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN = 0, 1
+
+EXPORTED = [
+    "ttt_mlp_version", "ttt_mlp_status_string", "ttt_mlp_last_error", "ttt_mlp_workspace_size",
+    "ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_project", "ttt_mlp_set_kernel_timing",
+    "ttt_mlp_kernel_timing", "ttt_mlp_reset_kernel_timing",
+]
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("T", ctypes.c_int64),
+        ("H", ctypes.c_int32), ("d", ctypes.c_int32), ("m", ctypes.c_int32), ("b", ctypes.c_int32),
+        ("eta", ctypes.c_float),
+        ("loss", ctypes.c_int32), ("gelu", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("algo", ctypes.c_int32),
+    ]
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)} ({status}): {detail}")
+        self.status = status
+
+
+_lib = None
+_vp, _fp, _i32, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m test_rnn_layer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ttt_mlp_version.restype = _i32
+        L.ttt_mlp_status_string.restype = ctypes.c_char_p
+        L.ttt_mlp_status_string.argtypes = [_i32]
+        L.ttt_mlp_last_error.restype = ctypes.c_char_p
+        L.ttt_mlp_workspace_size.restype = _i32
+        L.ttt_mlp_workspace_size.argtypes = [ctypes.POINTER(Config), _i32, ctypes.POINTER(_sz)]
+        L.ttt_mlp_forward.restype = _i32
+        L.ttt_mlp_forward.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _i32,
+                                      _vp, _fp, _fp, _fp, _vp, _sz, _vp]
+        L.ttt_mlp_bidir.restype = _i32
+        L.ttt_mlp_bidir.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _fp,
+                                    _vp, _fp, _fp, _fp, _fp, _fp, _fp, _vp, _sz, _vp]
+        L.ttt_mlp_project.restype = _i32
+        L.ttt_mlp_project.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _vp]
+        L.ttt_mlp_set_kernel_timing.restype = _i32
+        L.ttt_mlp_set_kernel_timing.argtypes = [_i32]
+        L.ttt_mlp_kernel_timing.restype = _i32
+        L.ttt_mlp_kernel_timing.argtypes = [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.ttt_mlp_reset_kernel_timing.restype = _i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ttt_mlp_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != TTT_OK:
+        raise TTTError(status, lib().ttt_mlp_last_error().decode())
+
+
+def make_config(B, T, H, d, m, b, eta, *, io_dtype="bf16", loss="mean", gelu="erf", algo="auto") -> Config:
+    return Config(B=B, T=T, H=H, d=d, m=m, b=b, eta=eta,
+                  loss={"mean": TTT_LOSS_MEAN, "sum": TTT_LOSS_SUM}[loss],
+                  gelu={"erf": TTT_GELU_ERF, "tanh": TTT_GELU_TANH}[gelu],
+                  io_dtype={"f32": TTT_F32, "bf16": TTT_BF16}[io_dtype],
+                  algo={"auto": TTT_ALGO_AUTO, "generic": TTT_ALGO_GENERIC, "mfma": TTT_ALGO_MFMA}[algo])
+
+
+def workspace_size(cfg: Config, bidir: bool) -> int:
+    n = _sz(0)
+    _check(lib().ttt_mlp_workspace_size(ctypes.byref(cfg), int(bidir), ctypes.byref(n)))
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _state_out(cfg, like):
+    import torch
+    kw = dict(dtype=torch.float32, device=like.device)
+    return (torch.empty((cfg.B, cfg.H, cfg.d, cfg.m), **kw), torch.empty((cfg.B, cfg.H, cfg.m, cfg.d), **kw))
+
+
+def _workspace(cfg, bidir, like):
+    import torch
+    return torch.empty(max(workspace_size(cfg, bidir), 1), dtype=torch.uint8, device=like.device)
+
+
+def forward(cfg: Config, X, theta, W1_0, W2_0, alpha, *, reverse=False, want_z=False, want_state=False,
+            workspace=None):
+    """ttt_mlp_forward.  Returns dict(Y, Z?, W1_T?, W2_T?)."""
+    import torch
+    Y = torch.empty_like(X)
+    Z = torch.empty(X.shape, dtype=torch.float32, device=X.device) if want_z else None
+    W1T, W2T = _state_out(cfg, X) if want_state else (None, None)
+    ws = _workspace(cfg, False, X) if workspace is None else workspace
+    _check(lib().ttt_mlp_forward(ctypes.byref(cfg), _ptr(X), _ptr(theta), _ptr(W1_0), _ptr(W2_0), _ptr(alpha),
+                                 int(reverse), _ptr(Y), _ptr(Z), _ptr(W1T), _ptr(W2T), _ptr(ws), ws.numel(),
+                                 _stream(X.device)))
+    return dict(Y=Y, Z=Z, W1_T=W1T, W2_T=W2T)
+
+
+def bidir(cfg: Config, X, theta, W1_0, W2_0, alpha_f, alpha_b, *, want_z=False, want_state=False,
+          workspace=None, out=None):
+    """ttt_mlp_bidir.  Returns dict(Y, Z_f?, Z_b?, W1_Tf?, W2_Tf?, W1_Tb?, W2_Tb?)."""
+    import torch
+    Y = torch.empty_like(X) if out is None else out
+    mk = lambda: torch.empty(X.shape, dtype=torch.float32, device=X.device)
+    Zf, Zb = (mk(), mk()) if want_z else (None, None)
+    (W1f, W2f), (W1b, W2b) = (_state_out(cfg, X), _state_out(cfg, X)) if want_state else ((None, None), (None, None))
+    ws = _workspace(cfg, True, X) if workspace is None else workspace
+    _check(lib().ttt_mlp_bidir(ctypes.byref(cfg), _ptr(X), _ptr(theta), _ptr(W1_0), _ptr(W2_0), _ptr(alpha_f),
+                               _ptr(alpha_b), _ptr(Y), _ptr(Zf), _ptr(Zb), _ptr(W1f), _ptr(W2f), _ptr(W1b),
+                               _ptr(W2b), _ptr(ws), ws.numel(), _stream(X.device)))
+    return dict(Y=Y, Z_f=Zf, Z_b=Zb, W1_Tf=W1f, W2_Tf=W2f, W1_Tb=W1b, W2_Tb=W2b)
+
+
+def project(cfg: Config, X, theta):
+    """ttt_mlp_project: QKV [3, B, H, T, d] fp32."""
+    import torch
+    out = torch.empty((3, cfg.B, cfg.H, cfg.T, cfg.d), dtype=torch.float32, device=X.device)
+    _check(lib().ttt_mlp_project(ctypes.byref(cfg), _ptr(X), _ptr(theta), _ptr(out), _stream(X.device)))
+    return out
+
+
+def set_kernel_timing(enable: bool):
+    _check(lib().ttt_mlp_set_kernel_timing(int(enable)))
+
+
+def kernel_timing(kind: int):
+    ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+    _check(lib().ttt_mlp_kernel_timing(kind, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def reset_kernel_timing():
+    _check(lib().ttt_mlp_reset_kernel_timing())

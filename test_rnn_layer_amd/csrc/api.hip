@@ -1,0 +1,374 @@
+// C ABI of the TTT-MLP layer scan: argument checks, workspace planning and
+// kernel launches.  The operation and the layouts are specified in
+// include/ttt_mlp.h.
+#include "../../include/ttt_mlp.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return TTT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+struct TimingRecord {
+  int kind;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRecord> g_timing_records;
+double g_timing_ms[2] = {0, 0};
+int64_t g_timing_n[2] = {0, 0};
+
+// Collect the finished records into the per-kind sums (caller holds the lock).
+hipError_t drain_timing_locked() {
+  hipError_t err = hipSuccess;
+  for (auto& r : g_timing_records) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e == hipSuccess) {
+      g_timing_ms[r.kind] += ms;
+      g_timing_n[r.kind] += 1;
+    } else {
+      err = e;
+    }
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_timing_records.clear();
+  return err;
+}
+
+// Launch `fn` on `stream`, bracketed by events when timing is on.
+template <class F>
+hipError_t timed_launch(int kind, hipStream_t stream, F&& fn) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    on = g_timing_on;
+  }
+  if (!on) return fn();
+  TimingRecord r{kind, nullptr, nullptr};
+  hipError_t e = hipEventCreate(&r.start);
+  if (e != hipSuccess) return e;
+  e = hipEventCreate(&r.stop);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    return e;
+  }
+  e = hipEventRecord(r.start, stream);
+  if (e == hipSuccess) e = fn();
+  if (e == hipSuccess) e = hipEventRecord(r.stop, stream);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+    return e;
+  }
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_records.push_back(r);
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// configuration checks and workspace plan
+// ---------------------------------------------------------------------------
+constexpr size_t kAlign = 256;
+constexpr size_t kGenericLdsMax = 64 * 1024;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int algo;            // TTT_ALGO_GENERIC or TTT_ALGO_MFMA
+  size_t qkv_off, qkv_bytes;
+  size_t wst_off, wst_bytes;
+  size_t total;
+  size_t io_elem;      // bytes per X / Y element
+};
+
+int32_t check_config(const ttt_mlp_config* c) {
+  if (!c) return fail(TTT_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->B < 1) return fail(TTT_ERR_INVALID_ARG, "B must be >= 1 (got %lld)", (long long)c->B);
+  if (c->T < 0) return fail(TTT_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)c->T);
+  if (c->H < 1 || c->d < 1 || c->m < 1)
+    return fail(TTT_ERR_INVALID_ARG, "H, d, m must be >= 1 (got %d, %d, %d)", c->H, c->d, c->m);
+  if (c->b < 1) return fail(TTT_ERR_INVALID_ARG, "mini-batch b must be >= 1 (got %d)", c->b);
+  if (!std::isfinite(c->eta) || c->eta < 0.0f)
+    return fail(TTT_ERR_INVALID_ARG, "eta must be finite and >= 0 (got %g)", (double)c->eta);
+  if (c->loss != TTT_LOSS_MEAN && c->loss != TTT_LOSS_SUM)
+    return fail(TTT_ERR_INVALID_ARG, "unknown loss %d", c->loss);
+  if (c->gelu != TTT_GELU_ERF && c->gelu != TTT_GELU_TANH)
+    return fail(TTT_ERR_INVALID_ARG, "unknown gelu %d", c->gelu);
+  if (c->io_dtype != TTT_F32 && c->io_dtype != TTT_BF16)
+    return fail(TTT_ERR_INVALID_ARG, "unknown io_dtype %d", c->io_dtype);
+  if (c->algo != TTT_ALGO_AUTO && c->algo != TTT_ALGO_GENERIC && c->algo != TTT_ALGO_MFMA)
+    return fail(TTT_ERR_INVALID_ARG, "unknown algo %d", c->algo);
+  const int64_t D = (int64_t)c->H * c->d;
+  if (D > (1 << 20) || c->m > (1 << 16) || c->b > (1 << 16))
+    return fail(TTT_ERR_UNSUPPORTED, "D = %lld, m = %d or b = %d too large", (long long)D, c->m, c->b);
+  if (c->T > ((int64_t)1 << 40) || c->B > ((int64_t)1 << 20) || c->B * c->H > (1 << 30))
+    return fail(TTT_ERR_UNSUPPORTED, "B or T too large");
+  return TTT_OK;
+}
+
+int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
+  int32_t st = check_config(c);
+  if (st != TTT_OK) return st;
+  const bool generic_fits = ttt::scan_generic_lds_bytes(c->d, c->m, c->b) <= kGenericLdsMax;
+  int algo = c->algo;
+  if (algo == TTT_ALGO_MFMA)
+    return fail(TTT_ERR_UNSUPPORTED, "the MFMA scan is not available for d=%d m=%d b=%d io=%d", c->d,
+                c->m, c->b, c->io_dtype);
+  if (algo == TTT_ALGO_AUTO) algo = TTT_ALGO_GENERIC;
+  if (!generic_fits)
+    return fail(TTT_ERR_UNSUPPORTED,
+                "generic scan: mini-batch working set of %zu bytes (d=%d m=%d b=%d) exceeds %zu bytes of LDS",
+                ttt::scan_generic_lds_bytes(c->d, c->m, c->b), c->d, c->m, c->b, kGenericLdsMax);
+  p->algo = algo;
+  p->io_elem = c->io_dtype == TTT_BF16 ? 2 : 4;
+  const size_t BHTd = (size_t)c->B * c->H * (size_t)c->T * c->d;
+  p->qkv_off = 0;
+  p->qkv_bytes = align_up(3 * BHTd * sizeof(float));
+  p->wst_off = p->qkv_off + p->qkv_bytes;
+  p->wst_bytes = align_up((size_t)c->B * c->H * 2 * (size_t)c->d * c->m * sizeof(float));
+  p->total = p->wst_off + p->wst_bytes;
+  return TTT_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+struct Buf {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+
+int32_t check_no_overlap(const Buf* outs, int nout, const Buf* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+        return fail(TTT_ERR_INVALID_ARG, "output %s overlaps output %s", outs[i].name, outs[j].name);
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n))
+        return fail(TTT_ERR_INVALID_ARG, "output %s overlaps input %s", outs[i].name, ins[j].name);
+  }
+  return TTT_OK;
+}
+
+// One direction: projection of xin, then the scan writing y (and z, W_T).
+int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, const void* theta,
+                      const float* W1_0, const float* W2_0, const float* alpha, int reverse, void* y,
+                      float* z, float* w1T, float* w2T, char* ws, hipStream_t stream) {
+  ttt::ProjArgs pa{};
+  pa.X = xin;
+  pa.theta = theta;
+  pa.out = ws + pl.qkv_off;
+  pa.B = c->B;
+  pa.T = c->T;
+  pa.H = c->H;
+  pa.d = c->d;
+  pa.bf16 = c->io_dtype == TTT_BF16;
+  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, stream, [&] { return ttt::launch_project_f32out(pa, stream); });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+
+  ttt::ScanArgs sa{};
+  sa.qkv = (const float*)(ws + pl.qkv_off);
+  sa.xin = xin;
+  sa.y = y;
+  sa.z = z;
+  sa.alpha = alpha;
+  sa.w1_0 = W1_0;
+  sa.w2_0 = W2_0;
+  sa.wstate = (float*)(ws + pl.wst_off);
+  sa.w1_T = w1T;
+  sa.w2_T = w2T;
+  sa.B = c->B;
+  sa.T = c->T;
+  sa.H = c->H;
+  sa.d = c->d;
+  sa.m = c->m;
+  sa.b = c->b;
+  sa.eta = c->eta;
+  sa.gscale = c->loss == TTT_LOSS_MEAN ? 2.0f / (float)c->d : 2.0f;
+  sa.gelu_tanh = c->gelu == TTT_GELU_TANH;
+  sa.reverse = reverse;
+  sa.bf16 = c->io_dtype == TTT_BF16;
+  e = timed_launch(TTT_KERNEL_SCAN, stream, [&] { return ttt::launch_scan_generic(sa, stream); });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ttt_mlp_version(void) { return (1 << 16) | 0; }
+
+const char* ttt_mlp_status_string(int32_t status) {
+  switch (status) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_INVALID_ARG: return "invalid argument";
+    case TTT_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TTT_ERR_WORKSPACE: return "workspace missing or too small";
+    case TTT_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ttt_mlp_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ttt_mlp_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t* bytes) {
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  if (bidir != 0 && bidir != 1) return fail(TTT_ERR_INVALID_ARG, "bidir must be 0 or 1");
+  Plan pl;
+  int32_t st = make_plan(cfg, &pl);
+  if (st != TTT_OK) return st;
+  *bytes = pl.total;
+  return ok();
+}
+
+int32_t ttt_mlp_forward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
+                        const float* W1_0, const float* W2_0, const float* alpha, int32_t reverse,
+                        void* Y, float* Z, float* W1_T, float* W2_T, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int32_t st = make_plan(cfg, &pl);
+  if (st != TTT_OK) return st;
+  if (!X || !theta_qkv || !W1_0 || !W2_0 || !alpha || !Y)
+    return fail(TTT_ERR_INVALID_ARG, "a required pointer (X, theta_qkv, W1_0, W2_0, alpha, Y) is NULL");
+  if (reverse != 0 && reverse != 1) return fail(TTT_ERR_INVALID_ARG, "reverse must be 0 or 1");
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                pl.total);
+  const size_t D = (size_t)cfg->H * cfg->d, BTD = (size_t)cfg->B * cfg->T * D;
+  const size_t st_bytes = (size_t)cfg->B * cfg->H * cfg->d * cfg->m * sizeof(float);
+  const Buf outs[] = {{Y, BTD * pl.io_elem, "Y"}, {Z, BTD * 4, "Z"}, {W1_T, st_bytes, "W1_T"},
+                      {W2_T, st_bytes, "W2_T"}, {workspace, pl.total, "workspace"}};
+  const Buf ins[] = {{X, BTD * pl.io_elem, "X"}, {theta_qkv, 3 * D * D * pl.io_elem, "theta_qkv"},
+                     {W1_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W1_0"},
+                     {W2_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W2_0"}, {alpha, D * 4, "alpha"}};
+  st = check_no_overlap(outs, 5, ins, 5);
+  if (st != TTT_OK) return st;
+  st = run_direction(cfg, pl, X, theta_qkv, W1_0, W2_0, alpha, reverse, Y, Z, W1_T, W2_T, (char*)workspace,
+                     (hipStream_t)stream);
+  return st == TTT_OK ? ok() : st;
+}
+
+int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
+                      const float* W1_0, const float* W2_0, const float* alpha_f,
+                      const float* alpha_b, void* Y, float* Z_f, float* Z_b, float* W1_Tf,
+                      float* W2_Tf, float* W1_Tb, float* W2_Tb, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int32_t st = make_plan(cfg, &pl);
+  if (st != TTT_OK) return st;
+  if (!X || !theta_qkv || !W1_0 || !W2_0 || !alpha_f || !alpha_b || !Y)
+    return fail(TTT_ERR_INVALID_ARG,
+                "a required pointer (X, theta_qkv, W1_0, W2_0, alpha_f, alpha_b, Y) is NULL");
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                pl.total);
+  const size_t D = (size_t)cfg->H * cfg->d, BTD = (size_t)cfg->B * cfg->T * D;
+  const size_t st_bytes = (size_t)cfg->B * cfg->H * cfg->d * cfg->m * sizeof(float);
+  const Buf outs[] = {{Y, BTD * pl.io_elem, "Y"},      {Z_f, BTD * 4, "Z_f"},
+                      {Z_b, BTD * 4, "Z_b"},           {W1_Tf, st_bytes, "W1_Tf"},
+                      {W2_Tf, st_bytes, "W2_Tf"},      {W1_Tb, st_bytes, "W1_Tb"},
+                      {W2_Tb, st_bytes, "W2_Tb"},      {workspace, pl.total, "workspace"}};
+  const Buf ins[] = {{X, BTD * pl.io_elem, "X"}, {theta_qkv, 3 * D * D * pl.io_elem, "theta_qkv"},
+                     {W1_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W1_0"},
+                     {W2_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W2_0"}, {alpha_f, D * 4, "alpha_f"},
+                     {alpha_b, D * 4, "alpha_b"}};
+  st = check_no_overlap(outs, 8, ins, 6);
+  if (st != TTT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // forward pass: X' lands in Y
+  st = run_direction(cfg, pl, X, theta_qkv, W1_0, W2_0, alpha_f, 0, Y, Z_f, W1_Tf, W2_Tf, (char*)workspace, s);
+  if (st != TTT_OK) return st;
+  // reversed pass over X' (read from Y, gated output written back in place)
+  st = run_direction(cfg, pl, Y, theta_qkv, W1_0, W2_0, alpha_b, 1, Y, Z_b, W1_Tb, W2_Tb, (char*)workspace, s);
+  return st == TTT_OK ? ok() : st;
+}
+
+int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv, float* QKV,
+                        void* stream) {
+  int32_t st = check_config(cfg);
+  if (st != TTT_OK) return st;
+  if (!X || !theta_qkv || !QKV) return fail(TTT_ERR_INVALID_ARG, "X, theta_qkv and QKV are required");
+  const size_t esz = cfg->io_dtype == TTT_BF16 ? 2 : 4;
+  const size_t D = (size_t)cfg->H * cfg->d, BTD = (size_t)cfg->B * cfg->T * D;
+  const Buf outs[] = {{QKV, 3 * BTD * 4, "QKV"}};
+  const Buf ins[] = {{X, BTD * esz, "X"}, {theta_qkv, 3 * D * D * esz, "theta_qkv"}};
+  st = check_no_overlap(outs, 1, ins, 2);
+  if (st != TTT_OK) return st;
+  ttt::ProjArgs pa{};
+  pa.X = X;
+  pa.theta = theta_qkv;
+  pa.out = QKV;
+  pa.B = cfg->B;
+  pa.T = cfg->T;
+  pa.H = cfg->H;
+  pa.d = cfg->d;
+  pa.bf16 = cfg->io_dtype == TTT_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, s, [&] { return ttt::launch_project_f32out(pa, s); });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t ttt_mlp_set_kernel_timing(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on = enable != 0;
+  return ok();
+}
+
+int32_t ttt_mlp_kernel_timing(int32_t kind, double* total_ms, int64_t* launches) {
+  if (kind != TTT_KERNEL_PROJECT && kind != TTT_KERNEL_SCAN)
+    return fail(TTT_ERR_INVALID_ARG, "unknown kernel kind %d", kind);
+  if (!total_ms || !launches) return fail(TTT_ERR_INVALID_ARG, "total_ms and launches are required");
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  hipError_t e = drain_timing_locked();
+  *total_ms = g_timing_ms[kind];
+  *launches = g_timing_n[kind];
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "timing events: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t ttt_mlp_reset_kernel_timing(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  hipError_t e = drain_timing_locked();
+  g_timing_ms[0] = g_timing_ms[1] = 0;
+  g_timing_n[0] = g_timing_n[1] = 0;
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "timing events: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

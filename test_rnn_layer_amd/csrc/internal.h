@@ -1,0 +1,48 @@
+// Internal interfaces between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+// Projection: QKV = X theta^T for theta_Q, theta_K, theta_V.
+struct ProjArgs {
+  const void* X;      // [B, T, D] io dtype
+  const void* theta;  // [3, D, D] io dtype, [out, in]
+  void* out;          // layout depends on the kernel
+  int64_t B, T;
+  int32_t H, d;
+  int32_t bf16;       // 1: X and theta are bf16, 0: fp32
+};
+
+// fp32 output, [3, B, H, T, d].
+hipError_t launch_project_f32out(const ProjArgs& a, hipStream_t s);
+
+// One direction of the scan.
+struct ScanArgs {
+  const float* qkv;      // generic path: fp32 [3, B, H, T, d]
+  const void* qkv_tiles; // MFMA path: bf16 tiled layout (see scan_mfma)
+  const void* xin;       // [B, T, D] io dtype: gate input
+  void* y;               // [B, T, D] io dtype: gated output (may equal xin)
+  float* z;              // [B, T, D] fp32 or null
+  const float* alpha;    // [D]
+  const float* w1_0;     // [H, d, m]
+  const float* w2_0;     // [H, m, d]
+  float* wstate;         // workspace, [B, H, d*m + m*d] fp32 (generic path)
+  float* w1_T;           // [B, H, d, m] or null
+  float* w2_T;           // [B, H, m, d] or null
+  int64_t B, T;
+  int32_t H, d, m, b;
+  float eta;
+  float gscale;          // 2/d (mean) or 2 (sum)
+  int32_t gelu_tanh;     // 0: erf form, 1: tanh form
+  int32_t reverse;
+  int32_t bf16;          // io dtype of xin / y
+};
+
+// LDS bytes the generic scan needs for (d, m, b).
+size_t scan_generic_lds_bytes(int d, int m, int b);
+hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t s);
+
+}  // namespace ttt

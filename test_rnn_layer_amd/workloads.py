@@ -24,6 +24,7 @@ X_CHUNK rows so that any token range can be regenerated on its own.
 from __future__ import annotations
 
 import dataclasses
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -87,9 +88,12 @@ WORKLOAD_ORDER = ["tiny_f32", "seg14k", "bidir100k", "bidir307k", "bigstate307k"
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); returns uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = a.view(np.uint32)
+    lsb = (u >> 16) & 1
+    lsb += 0x7FFF
+    lsb += u  # no wrap-around: finite values stay below 0xFF800000
+    lsb >>= 16
+    return lsb.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -136,16 +140,22 @@ def make_x(wl: Workload, t0: int = 0, t1: int | None = None, seq: int | None = N
     out = np.empty((len(seqs), t1 - t0, wl.D),
                    dtype=np.uint16 if wl.io_dtype == "bf16" else np.float32)
     mu = segment_means(wl) if wl.seg_len > 0 else None
-    for si, s in enumerate(seqs):
-        c0, c1 = t0 // X_CHUNK, -(-t1 // X_CHUNK)
-        for c in range(c0, c1):
-            r0, r1 = c * X_CHUNK, min((c + 1) * X_CHUNK, wl.T)
-            chunk = _rng(wl.seed, TID_X, s, c).standard_normal((r1 - r0, wl.D))
-            if mu is not None:
-                chunk += mu[np.arange(r0, r1) // wl.seg_len]
-            a, z = max(r0, t0), min(r1, t1)
-            if a < z:
-                out[si, a - t0:z - t0] = _store(chunk[a - r0:z - r0], wl.io_dtype)
+    def fill(job):
+        si, s, c = job
+        r0, r1 = c * X_CHUNK, min((c + 1) * X_CHUNK, wl.T)
+        a, z = max(r0, t0), min(r1, t1)
+        chunk = _rng(wl.seed, TID_X, s, c).standard_normal((r1 - r0, wl.D))[a - r0:z - r0]
+        if mu is not None:
+            chunk += mu[np.arange(a, z) // wl.seg_len]
+        out[si, a - t0:z - t0] = _store(chunk, wl.io_dtype)
+
+    jobs = [(si, s, c) for si, s in enumerate(seqs) for c in range(t0 // X_CHUNK, -(-t1 // X_CHUNK))]
+    if len(jobs) > 1:
+        with ThreadPoolExecutor(max_workers=min(16, len(jobs))) as ex:
+            list(ex.map(fill, jobs))
+    else:
+        for j in jobs:
+            fill(j)
     return out if seq is None else out[0]
 
 

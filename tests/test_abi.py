@@ -1,0 +1,92 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from test_rnn_layer_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ttt_mlp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_mlp_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_workspace_size", "ttt_mlp_status_string"):
+        assert n in names
+    assert sorted(L.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert lib.ttt_mlp_version() >> 16 == 1
+
+
+def test_config_struct_layout_matches_header():
+    # int64 B, T; int32 H, d, m, b; float eta; int32 loss, gelu, io_dtype, algo
+    assert ctypes.sizeof(L.Config) == 56
+    assert L.Config.eta.offset == 32 and L.Config.algo.offset == 48
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert L.status_string(s)
+    assert L.status_string(-99) == "unknown status"
+
+
+def cfg(**kw):
+    base = dict(B=1, T=64, H=2, d=64, m=256, b=16, eta=0.1 / 16)
+    base.update(kw)
+    return L.make_config(**base)
+
+
+def test_workspace_size_and_validation():
+    n = L.workspace_size(cfg(), False)
+    assert n >= 3 * 2 * 64 * 64 * 4
+    assert L.workspace_size(cfg(T=0), True) > 0
+    bad = [dict(B=0), dict(T=-1), dict(H=0), dict(d=0), dict(b=0), dict(eta=-1.0), dict(eta=float("nan"))]
+    for kw in bad:
+        with pytest.raises(L.TTTError) as e:
+            L.workspace_size(cfg(**kw), False)
+        assert e.value.status == L.TTT_ERR_INVALID_ARG
+    c = cfg()
+    c.loss = 7
+    with pytest.raises(L.TTTError) as e:
+        L.workspace_size(c, False)
+    assert e.value.status == L.TTT_ERR_INVALID_ARG
+    # a mini-batch working set beyond the generic kernel's LDS budget
+    with pytest.raises(L.TTTError) as e:
+        L.workspace_size(cfg(b=64, m=512, d=128), False)
+    assert e.value.status == L.TTT_ERR_UNSUPPORTED
+
+
+def test_compute_calls_reject_bad_pointers_on_the_host():
+    lib = L.lib()
+    c = cfg()
+    n = L.workspace_size(c, False)
+    fake = 1 << 40  # never dereferenced: every call below fails its host checks first
+    st = lib.ttt_mlp_forward(ctypes.byref(c), None, fake, fake, fake, fake, 0, fake, None, None, None, fake, n, None)
+    assert st == L.TTT_ERR_INVALID_ARG
+    st = lib.ttt_mlp_forward(ctypes.byref(c), fake, fake, fake, fake, fake, 0, fake + 4096, None, None, None,
+                             fake + (1 << 30), n - 1, None)
+    assert st == L.TTT_ERR_WORKSPACE
+    # Y overlapping X
+    st = lib.ttt_mlp_forward(ctypes.byref(c), fake, fake + (1 << 32), fake + (2 << 32), fake + (3 << 32),
+                             fake + (4 << 32), 0, fake + 64, None, None, None, fake + (5 << 32), n, None)
+    assert st == L.TTT_ERR_INVALID_ARG and b"overlaps" in lib.ttt_mlp_last_error()
+    st = lib.ttt_mlp_forward(ctypes.byref(c), fake, fake, fake, fake, fake, 2, fake, None, None, None, fake, n, None)
+    assert st == L.TTT_ERR_INVALID_ARG
+    st = lib.ttt_mlp_bidir(ctypes.byref(c), fake, fake, fake, fake, fake, None, fake, None, None, None, None,
+                           None, None, fake, n, None)
+    assert st == L.TTT_ERR_INVALID_ARG
+    st = lib.ttt_mlp_kernel_timing(5, ctypes.byref(ctypes.c_double()), ctypes.byref(ctypes.c_int64()))
+    assert st == L.TTT_ERR_INVALID_ARG

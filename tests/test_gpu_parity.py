@@ -1,0 +1,239 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded inputs.
+
+Tolerances: fp32 io -- max-abs <= 1e-4 on Y, Z and the final state;
+bf16 io -- relative L2 <= 2e-2 on Y, Z (each direction) and the final state.
+Every call goes through the C ABI (test_rnn_layer_amd._lib).
+"""
+import numpy as np
+import pytest
+
+from oracle import ttt_oracle as O
+from test_rnn_layer_amd import workloads as W
+
+from tests._common import device_inputs, f64_inputs, from_device, max_abs, rel_l2, rel_l2_tenths, workers
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+ALGOS = ["generic"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from test_rnn_layer_amd import _lib
+    _lib.lib()  # the HIP library must load: no fallback
+    yield
+
+
+def _cfg(wl, algo="auto", T=None):
+    from test_rnn_layer_amd import _lib
+    return _lib.make_config(wl.B, wl.T if T is None else T, wl.H, wl.d, wl.m, wl.b, wl.eta,
+                            io_dtype=wl.io_dtype, loss=wl.loss, gelu=wl.gelu, algo=algo)
+
+
+def _gpu_forward(wl, dev, algo, reverse=False, alpha="alpha_f"):
+    from test_rnn_layer_amd import _lib
+    r = _lib.forward(_cfg(wl, algo), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev[alpha],
+                     reverse=reverse, want_z=True, want_state=True)
+    torch.cuda.synchronize()
+    return r
+
+
+def _gpu_bidir(wl, dev, algo):
+    from test_rnn_layer_amd import _lib
+    r = _lib.bidir(_cfg(wl, algo), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"],
+                   dev["alpha_b"], want_z=True, want_state=True)
+    torch.cuda.synchronize()
+    return r
+
+
+def _oracle_forward(wl, f64, reverse=False, alpha="alpha_f"):
+    return O.ttt_forward(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64[alpha], eta=wl.eta, b=wl.b,
+                         reverse=reverse, loss=wl.loss, gelu_form=wl.gelu, workers=workers())
+
+
+def _check(name, got, ref, io_dtype):
+    if io_dtype == "f32":
+        err = max_abs(got, ref)
+        print(f"  {name}: max-abs {err:.3e}", flush=True)
+        assert err <= F32_TOL, (name, err)
+    else:
+        err = rel_l2(got, ref)
+        print(f"  {name}: rel-L2 {err:.3e}", flush=True)
+        assert err <= BF16_TOL, (name, err)
+
+
+def _check_forward(wl, got, ref):
+    _check("Y", from_device(got["Y"]), ref["Y"], wl.io_dtype)
+    _check("Z", from_device(got["Z"]), ref["Z"], wl.io_dtype)
+    _check("W1_T", from_device(got["W1_T"]), ref["W1_T"], wl.io_dtype)
+    _check("W2_T", from_device(got["W2_T"]), ref["W2_T"], wl.io_dtype)
+
+
+# ----------------------------------------------------------------------------
+# small and medium shapes, element by element
+# ----------------------------------------------------------------------------
+
+SMALL = {
+    # name: workload (several mini-batch tiles plus a ragged tail where b > 1)
+    "tiny_f32": W.WORKLOADS["tiny_f32"],
+    "tiny_f32_b4_ragged": W.WORKLOADS["tiny_f32"].replace(T=103, b=4, name="tiny_f32_b4_ragged"),
+    "h3_d64_b16_ragged": W.WORKLOADS["seg14k"].replace(T=200, H=3, name="h3_d64_b16_ragged"),
+    "h2_d128_b1": W.WORKLOADS["bigstate307k"].replace(T=96, H=2, name="h2_d128_b1"),
+    "seg_shift_b16": W.WORKLOADS["bidir307k"].replace(T=512, H=2, seg_len=160, name="seg_shift_b16"),
+    "sum_loss_tanh": W.WORKLOADS["seg14k"].replace(T=77, H=2, loss="sum", eta=0.1 / 16 / 64, gelu="tanh",
+                                                   name="sum_loss_tanh"),
+    "two_sequences": W.WORKLOADS["seg14k"].replace(B=2, T=64, H=2, name="two_sequences"),
+    "one_token": W.WORKLOADS["seg14k"].replace(T=1, H=2, name="one_token"),
+    "shorter_than_b": W.WORKLOADS["seg14k"].replace(T=9, H=2, name="shorter_than_b"),
+}
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("case", list(SMALL))
+@pytest.mark.parametrize("reverse", [False, True])
+def test_forward_matches_oracle(case, reverse, algo):
+    wl = SMALL[case]
+    print(f"[forward] case={case} reverse={reverse} algo={algo} shape=B{wl.B} T{wl.T} H{wl.H} d{wl.d} m{wl.m} b{wl.b}",
+          flush=True)
+    inp = W.make_inputs(wl)
+    got = _gpu_forward(wl, device_inputs(wl, inp), algo, reverse=reverse)
+    ref = _oracle_forward(wl, f64_inputs(wl, inp), reverse=reverse)
+    _check_forward(wl, got, ref)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("case", ["h3_d64_b16_ragged", "h2_d128_b1", "seg_shift_b16", "tiny_f32_b4_ragged"])
+def test_bidir_matches_oracle(case, algo):
+    wl = SMALL[case].replace(alpha_f=0.1, alpha_b=0.2)  # distinct gates catch a swap
+    print(f"[bidir] case={case} algo={algo}", flush=True)
+    inp = W.make_inputs(wl)
+    got = _gpu_bidir(wl, device_inputs(wl, inp), algo)
+    f64 = f64_inputs(wl, inp)
+    ref = O.ttt_bidir(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64["alpha_f"], f64["alpha_b"],
+                      eta=wl.eta, b=wl.b, loss=wl.loss, gelu_form=wl.gelu, workers=workers())
+    _check("Y", from_device(got["Y"]), ref["Y"], wl.io_dtype)
+    _check("Z_f", from_device(got["Z_f"]), ref["Z_f"], wl.io_dtype)
+    _check("Z_b", from_device(got["Z_b"]), ref["Z_b"], wl.io_dtype)
+    for k in ("W1_Tf", "W2_Tf", "W1_Tb", "W2_Tb"):
+        _check(k, from_device(got[k]), ref[k], wl.io_dtype)
+
+
+def test_empty_sequence_returns_initial_state():
+    from test_rnn_layer_amd import _lib
+    wl = SMALL["h3_d64_b16_ragged"].replace(T=0)
+    print("[empty] T=0", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    r = _lib.bidir(_cfg(wl), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dev["alpha_b"],
+                   want_z=True, want_state=True)
+    torch.cuda.synchronize()
+    assert r["Y"].numel() == 0
+    np.testing.assert_array_equal(r["W1_Tb"][0].cpu().numpy(), inp["W1_0"])
+    np.testing.assert_array_equal(r["W2_Tf"][0].cpu().numpy(), inp["W2_0"])
+
+
+# ----------------------------------------------------------------------------
+# properties that hold at any size (bitwise, on the GPU)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_properties_bitwise(algo):
+    from test_rnn_layer_amd import _lib
+    wl = SMALL["h3_d64_b16_ragged"]
+    print(f"[properties] algo={algo}", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    cfg = _cfg(wl, algo)
+    a = _gpu_forward(wl, dev, algo)
+    b = _gpu_forward(wl, dev, algo)
+    assert torch.equal(a["Y"], b["Y"]) and torch.equal(a["Z"], b["Z"]), "not deterministic"
+    # reversed pass == forward pass on the flipped sequence
+    rv = _gpu_forward(wl, dev, algo, reverse=True)
+    flipped = dict(dev, X=dev["X"].flip(1).contiguous())
+    fl = _gpu_forward(wl, flipped, algo)
+    assert torch.equal(rv["Z"], fl["Z"].flip(1)) and torch.equal(rv["Y"], fl["Y"].flip(1))
+    assert torch.equal(rv["W1_T"], fl["W1_T"])
+    # alpha = 0 leaves X untouched
+    z = _lib.forward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], torch.zeros_like(dev["alpha_f"]))
+    torch.cuda.synchronize()
+    assert torch.equal(z["Y"], dev["X"])
+    # bidir == forward (alpha_f) then reversed forward (alpha_b) on its output
+    bd = _gpu_bidir(wl, dev, algo)
+    f2 = _gpu_forward(wl, dict(dev, X=a["Y"]), algo, reverse=True, alpha="alpha_b")
+    assert torch.equal(bd["Y"], f2["Y"]) and torch.equal(bd["Z_f"], a["Z"]) and torch.equal(bd["Z_b"], f2["Z"])
+    # state hand-off: continuing from W_T1 over the rest equals the whole run
+    T1 = 96
+    first = _lib.forward(_cfg(wl, algo, T=T1), dev["X"][:, :T1].contiguous(), dev["theta"], dev["W1_0"],
+                         dev["W2_0"], dev["alpha_f"], want_z=True, want_state=True)
+    rest = _lib.forward(_cfg(wl, algo, T=wl.T - T1), dev["X"][:, T1:].contiguous(), dev["theta"],
+                        first["W1_T"][0].contiguous(), first["W2_T"][0].contiguous(), dev["alpha_f"], want_z=True,
+                        want_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([first["Z"], rest["Z"]], 1), a["Z"])
+    assert torch.equal(rest["W1_T"], a["W1_T"]) and torch.equal(rest["W2_T"], a["W2_T"])
+
+
+# ----------------------------------------------------------------------------
+# the five layer configurations at full size
+# ----------------------------------------------------------------------------
+
+def test_tiny_f32_full_config():
+    wl = W.WORKLOADS["tiny_f32"]
+    print("[config] tiny_f32 full", flush=True)
+    inp = W.make_inputs(wl)
+    got = _gpu_forward(wl, device_inputs(wl, inp), "auto")
+    ref = _oracle_forward(wl, f64_inputs(wl, inp))
+    _check_forward(wl, got, ref)
+
+
+def test_seg14k_full_config_all_heads():
+    wl = W.WORKLOADS["seg14k"]
+    print("[config] seg14k full, all heads", flush=True)
+    inp = W.make_inputs(wl)
+    got = _gpu_forward(wl, device_inputs(wl, inp), "auto")
+    ref = _oracle_forward(wl, f64_inputs(wl, inp))
+    _check_forward(wl, got, ref)
+    print("  Z rel-L2 per tenth:", " ".join(f"{e:.1e}" for e in rel_l2_tenths(from_device(got["Z"]), ref["Z"])))
+
+
+@pytest.mark.parametrize("name,prefix", [("bidir100k", 2048), ("bidir307k", 2048), ("bigstate307k", 768)])
+def test_full_size_bidir(name, prefix):
+    """Full-size bidirectional call, in the launch configuration the benchmark times.
+
+    The forward pass is causal, so its outputs on the first `prefix` tokens
+    are checked element by element against the oracle run on those tokens
+    alone (first and last head).  The reversed pass is checked through
+    properties: bidir == forward then reversed forward on its output, bitwise.
+    """
+    from test_rnn_layer_amd import _lib
+    wl = W.WORKLOADS[name]
+    print(f"[config] {name} full size, prefix {prefix}", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    cfg = _cfg(wl)
+    r = _lib.bidir(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dev["alpha_b"],
+                   want_z=True)
+    f = _lib.forward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(r["Z_b"]).all() and torch.isfinite(r["Y"].float()).all()
+    Zf_pre = from_device(r["Z_f"][:, :prefix])
+    Xp_pre = from_device(f["Y"][:, :prefix])
+    del r["Z_b"]
+    g = _lib.forward(cfg, f["Y"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_b"], reverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g["Y"], r["Y"])
+    del dev, r, f, g
+    torch.cuda.empty_cache()
+    sub = wl.replace(T=prefix)
+    f64 = f64_inputs(sub, dict(inp, X=inp["X"][:, :prefix]))
+    heads = [0, wl.H - 1]
+    ref = O.ttt_forward(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64["alpha_f"], eta=wl.eta, b=wl.b,
+                        heads=heads, workers=workers())
+    cols = np.concatenate([np.arange(h * wl.d, (h + 1) * wl.d) for h in heads])
+    _check("Z_f prefix", Zf_pre[:, :, cols], ref["Z"], wl.io_dtype)
+    _check("X' prefix", Xp_pre[:, :, cols], ref["Y"], wl.io_dtype)

@@ -429,3 +429,15 @@ def test_empty_sequence_and_batch_of_sequences():
     for s in range(3):
         rs = O.ttt_forward(X[s], theta, W1, W2, np.full(H * d, 0.1), eta=0.1, b=4)
         np.testing.assert_array_equal(rb["Y"][s], rs["Y"])
+
+
+def test_head_subset_matches_full_layer():
+    T, H, d, m = 14, 4, 4, 16
+    X, theta, W1, W2 = _small_problem(16, T, H, d, m)
+    alpha = np.linspace(0, 1, H * d)
+    full = O.ttt_forward(X, theta, W1, W2, alpha, eta=0.1, b=4, reverse=True)
+    sub = O.ttt_forward(X, theta, W1, W2, alpha, eta=0.1, b=4, reverse=True, heads=[3, 1])
+    cols = np.r_[12:16, 4:8]
+    np.testing.assert_allclose(sub["Z"], full["Z"][:, cols], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(sub["Y"], full["Y"][:, cols], rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(sub["W1_T"][0, 0], full["W1_T"][0, 3])
