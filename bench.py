@@ -1,0 +1,181 @@
+"""Benchmark of the TTT-MLP bidirectional layer (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bidir307k]
+
+A step is one ttt_mlp_bidir call over the whole sequence: projections, the
+forward scan with its gate, the projections of X', the reversed scan with its
+gate.  Inputs are seeded synthetic tensors already resident in device memory.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TTT-MLP bidirectional layer tokens/sec at 307,200 tokens; % of roofline"
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+SCAN_SOURCES = ["generic.hip", "scan_mfma.hip"]
+
+
+def scan_flops_per_token_head(d: int, m: int, b: int) -> int:
+    """Algorithmic flops of one scan step per token and head (multiply-add = 2):
+    seven d x m contractions (K W1, Hk W2, G2 W2^T, Q W1, Hq W2, K^T G1, Hk^T G2)
+    plus the causal halves of the b x b products (tril(QK^T), its product with
+    G1, tril(Hq Hk^T), its product with G2)."""
+    return 7 * 2 * d * m + (b + 1) * (2 * d + 2 * m)
+
+
+def proj_flops_per_token(D: int) -> int:
+    return 2 * 3 * D * D
+
+
+def source_digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        p = os.path.join(ROOT, "test_rnn_layer_amd", "csrc", n)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, digest: str):
+    """HBM bytes per scan launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = rec.get(kernel)
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, tokens: int):
+    """The fp64 oracle on the first `tokens` tokens of the same workload (both
+    directions, every head), timed on this host's cores."""
+    import numpy as np
+
+    from oracle import ttt_oracle as O
+    from test_rnn_layer_amd import workloads as W
+
+    sub = wl.replace(T=tokens)
+    inp = W.make_inputs(sub)
+    X = W.to_f64(inp["X"], sub.io_dtype)
+    th = W.to_f64(inp["theta"], sub.io_dtype)
+    nw = O.default_workers()
+    t0 = time.perf_counter()
+    O.ttt_bidir(X, th, inp["W1_0"].astype(np.float64), inp["W2_0"].astype(np.float64),
+                inp["alpha_f"].astype(np.float64), inp["alpha_b"].astype(np.float64),
+                eta=sub.eta, b=sub.b, loss=sub.loss, gelu_form=sub.gelu, workers=nw)
+    dt = time.perf_counter() - t0
+    return dict(value=tokens / dt, unit="tokens/s", cores=nw, kind="oracle",
+                sample=f"{wl.name} workload, first {tokens} tokens, all {wl.H} heads, both directions, "
+                       f"fp64 NumPy, {dt:.1f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="bidir307k")
+    ap.add_argument("--algo", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the layer's heads would shard across GPUs, but this build "
+              f"runs on a single MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from test_rnn_layer_amd import _lib
+    from test_rnn_layer_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# bench: workload {wl.name} B={wl.B} T={wl.T} H={wl.H} d={wl.d} m={wl.m} b={wl.b}", file=sys.stderr,
+          flush=True)
+    inp = W.make_inputs(wl)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    io = bf if wl.io_dtype == "bf16" else f32
+    X, th = io(inp["X"]), io(inp["theta"])
+    W1, W2 = f32(inp["W1_0"]), f32(inp["W2_0"])
+    af, ab = f32(inp["alpha_f"]), f32(inp["alpha_b"])
+    del inp
+    cfg = _lib.make_config(wl.B, wl.T, wl.H, wl.d, wl.m, wl.b, wl.eta, io_dtype=wl.io_dtype, loss=wl.loss,
+                           gelu=wl.gelu, algo=args.algo)
+    ws = torch.empty(_lib.workspace_size(cfg, True), dtype=torch.uint8, device=dev)
+    Y = torch.empty_like(X)
+    step = lambda: _lib.bidir(cfg, X, th, W1, W2, af, ab, workspace=ws, out=Y)
+    print("# bench: inputs resident, warming up", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.set_kernel_timing(True)
+    _lib.reset_kernel_timing()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    scan_ms, scan_n = _lib.kernel_timing(_lib.TTT_KERNEL_SCAN)
+    proj_ms, proj_n = _lib.kernel_timing(_lib.TTT_KERNEL_PROJECT)
+    _lib.set_kernel_timing(False)
+    print(f"# bench: {args.steps} steps in {elapsed:.3f} s; scan {scan_n} launches {scan_ms:.1f} ms; "
+          f"projection {proj_n} launches {proj_ms:.1f} ms", file=sys.stderr, flush=True)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = wl.B * wl.T
+    value = tokens / (ms_per_step / 1e3)
+    dirs = 2
+    # dominant kernel: the scan; one launch covers one direction of the whole batch
+    scan_flops_launch = scan_flops_per_token_head(wl.d, wl.m, wl.b) * wl.H * tokens * dirs * args.steps / scan_n
+    scan_avg_ms = scan_ms / scan_n
+    achieved = scan_flops_launch / (scan_avg_ms / 1e3) / 1e12
+    used_mfma = _lib.select_algo(cfg) == "mfma"
+    peak = PEAK_BF16_TFLOPS if used_mfma else PEAK_FP32_TFLOPS
+    kname = "scan_mfma" if used_mfma else "scan_generic"
+    traffic = traffic_from_profile(kname, source_digest(SCAN_SOURCES))
+    # layer roofline: projections at bf16 MFMA peak plus the scan at fp32 peak
+    proj_total = proj_flops_per_token(wl.D) * tokens * dirs
+    scan_total = scan_flops_per_token_head(wl.d, wl.m, wl.b) * wl.H * tokens * dirs
+    R_ms = (proj_total / (PEAK_BF16_TFLOPS * 1e12) + scan_total / (PEAK_FP32_TFLOPS * 1e12)) * 1e3
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "d": wl.d, "m": wl.m, "b": wl.b,
+                   "eta": wl.eta, "D": wl.D, "directions": dirs, "scan_kernel": kname},
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "flops_per_launch": scan_flops_launch, "avg_launch_ms": scan_avg_ms},
+        "layer_roofline": {"R_ms": R_ms, "frac": R_ms / ms_per_step,
+                           "definition": "projection flops at bf16 MFMA peak + scan flops at fp32 peak"},
+        "kernel_ms_per_step": {"scan": scan_ms / args.steps, "projection": proj_ms / args.steps},
+    }
+    if not args.no_cpu_baseline:
+        print("# bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

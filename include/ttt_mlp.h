@@ -111,9 +111,17 @@ const char* ttt_mlp_last_error(void);
 int32_t ttt_mlp_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t* bytes);
 
 /*
+ * The scan kernel a call with this configuration runs: writes TTT_ALGO_GENERIC
+ * or TTT_ALGO_MFMA to *algo (resolving TTT_ALGO_AUTO), or returns the error
+ * the compute calls would return.
+ */
+int32_t ttt_mlp_select_algo(const ttt_mlp_config* cfg, int32_t* algo);
+
+/*
  * One gated direction of the layer: Y = X + tanh(alpha) * TTT(X).
  *   reverse = 0: tokens t = 0 .. T-1 (causal); 1: t = T-1 .. 0.
- *   X, theta_qkv, W1_0, W2_0, alpha, Y, workspace: required.
+ *   X, theta_qkv, W1_0, W2_0, alpha, Y, workspace: required (X and Y may be
+ *   NULL when T = 0; the call then only writes the final state, = W_0).
  *   Z, W1_T, W2_T: optional outputs (NULL to skip).
  *   Y must not overlap X, and no output may overlap another buffer.
  */

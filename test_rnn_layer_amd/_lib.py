@@ -22,6 +22,7 @@ TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN = 0, 1
 
 EXPORTED = [
     "ttt_mlp_version", "ttt_mlp_status_string", "ttt_mlp_last_error", "ttt_mlp_workspace_size",
+    "ttt_mlp_select_algo",
     "ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_project", "ttt_mlp_set_kernel_timing",
     "ttt_mlp_kernel_timing", "ttt_mlp_reset_kernel_timing",
 ]
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.ttt_mlp_last_error.restype = ctypes.c_char_p
         L.ttt_mlp_workspace_size.restype = _i32
         L.ttt_mlp_workspace_size.argtypes = [ctypes.POINTER(Config), _i32, ctypes.POINTER(_sz)]
+        L.ttt_mlp_select_algo.restype = _i32
+        L.ttt_mlp_select_algo.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_i32)]
         L.ttt_mlp_forward.restype = _i32
         L.ttt_mlp_forward.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _i32,
                                       _vp, _fp, _fp, _fp, _vp, _sz, _vp]
@@ -98,6 +101,13 @@ def workspace_size(cfg: Config, bidir: bool) -> int:
     n = _sz(0)
     _check(lib().ttt_mlp_workspace_size(ctypes.byref(cfg), int(bidir), ctypes.byref(n)))
     return n.value
+
+
+def select_algo(cfg: Config) -> str:
+    """The scan kernel a call with cfg runs: "generic" or "mfma"."""
+    a = _i32(0)
+    _check(lib().ttt_mlp_select_algo(ctypes.byref(cfg), ctypes.byref(a)))
+    return {TTT_ALGO_GENERIC: "generic", TTT_ALGO_MFMA: "mfma"}[a.value]
 
 
 def _ptr(t):

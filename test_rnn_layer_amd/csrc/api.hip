@@ -256,6 +256,15 @@ int32_t ttt_mlp_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t*
   return ok();
 }
 
+int32_t ttt_mlp_select_algo(const ttt_mlp_config* cfg, int32_t* algo) {
+  if (!algo) return fail(TTT_ERR_INVALID_ARG, "algo is NULL");
+  Plan pl;
+  int32_t st = make_plan(cfg, &pl);
+  if (st != TTT_OK) return st;
+  *algo = pl.algo;
+  return ok();
+}
+
 int32_t ttt_mlp_forward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
                         const float* W1_0, const float* W2_0, const float* alpha, int32_t reverse,
                         void* Y, float* Z, float* W1_T, float* W2_T, void* workspace,
@@ -263,7 +272,8 @@ int32_t ttt_mlp_forward(const ttt_mlp_config* cfg, const void* X, const void* th
   Plan pl;
   int32_t st = make_plan(cfg, &pl);
   if (st != TTT_OK) return st;
-  if (!X || !theta_qkv || !W1_0 || !W2_0 || !alpha || !Y)
+  const bool no_tokens = cfg->T == 0;  // X and Y may then be NULL
+  if ((!no_tokens && (!X || !Y)) || !theta_qkv || !W1_0 || !W2_0 || !alpha)
     return fail(TTT_ERR_INVALID_ARG, "a required pointer (X, theta_qkv, W1_0, W2_0, alpha, Y) is NULL");
   if (reverse != 0 && reverse != 1) return fail(TTT_ERR_INVALID_ARG, "reverse must be 0 or 1");
   if (!workspace || workspace_bytes < pl.total)
@@ -291,7 +301,8 @@ int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* thet
   Plan pl;
   int32_t st = make_plan(cfg, &pl);
   if (st != TTT_OK) return st;
-  if (!X || !theta_qkv || !W1_0 || !W2_0 || !alpha_f || !alpha_b || !Y)
+  const bool no_tokens = cfg->T == 0;  // X and Y may then be NULL
+  if ((!no_tokens && (!X || !Y)) || !theta_qkv || !W1_0 || !W2_0 || !alpha_f || !alpha_b)
     return fail(TTT_ERR_INVALID_ARG,
                 "a required pointer (X, theta_qkv, W1_0, W2_0, alpha_f, alpha_b, Y) is NULL");
   if (!workspace || workspace_bytes < pl.total)
@@ -322,7 +333,8 @@ int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* th
                         void* stream) {
   int32_t st = check_config(cfg);
   if (st != TTT_OK) return st;
-  if (!X || !theta_qkv || !QKV) return fail(TTT_ERR_INVALID_ARG, "X, theta_qkv and QKV are required");
+  if ((cfg->T > 0 && (!X || !QKV)) || !theta_qkv)
+    return fail(TTT_ERR_INVALID_ARG, "X, theta_qkv and QKV are required");
   const size_t esz = cfg->io_dtype == TTT_BF16 ? 2 : 4;
   const size_t D = (size_t)cfg->H * cfg->d, BTD = (size_t)cfg->B * cfg->T * D;
   const Buf outs[] = {{QKV, 3 * BTD * 4, "QKV"}};
