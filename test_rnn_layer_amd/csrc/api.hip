@@ -135,16 +135,19 @@ int32_t check_config(const ttt_mlp_config* c) {
   return TTT_OK;
 }
 
+bool mfma_possible(const ttt_mlp_config* c) {
+  return c->io_dtype == TTT_BF16 && ttt::scan_mfma_supported(c->d, c->m, c->b) && ((int64_t)c->H * c->d) % 8 == 0;
+}
+
 int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   int32_t st = check_config(c);
   if (st != TTT_OK) return st;
-  const bool generic_fits = ttt::scan_generic_lds_bytes(c->d, c->m, c->b) <= kGenericLdsMax;
   int algo = c->algo;
-  if (algo == TTT_ALGO_MFMA)
-    return fail(TTT_ERR_UNSUPPORTED, "the MFMA scan is not available for d=%d m=%d b=%d io=%d", c->d,
-                c->m, c->b, c->io_dtype);
-  if (algo == TTT_ALGO_AUTO) algo = TTT_ALGO_GENERIC;
-  if (!generic_fits)
+  if (algo == TTT_ALGO_AUTO) algo = mfma_possible(c) ? TTT_ALGO_MFMA : TTT_ALGO_GENERIC;
+  if (algo == TTT_ALGO_MFMA && !mfma_possible(c))
+    return fail(TTT_ERR_UNSUPPORTED, "the MFMA scan needs bf16 io, d=64, m=256, b=16 (got d=%d m=%d b=%d io=%d)",
+                c->d, c->m, c->b, c->io_dtype);
+  if (algo == TTT_ALGO_GENERIC && ttt::scan_generic_lds_bytes(c->d, c->m, c->b) > kGenericLdsMax)
     return fail(TTT_ERR_UNSUPPORTED,
                 "generic scan: mini-batch working set of %zu bytes (d=%d m=%d b=%d) exceeds %zu bytes of LDS",
                 ttt::scan_generic_lds_bytes(c->d, c->m, c->b), c->d, c->m, c->b, kGenericLdsMax);
@@ -152,11 +155,22 @@ int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   p->io_elem = c->io_dtype == TTT_BF16 ? 2 : 4;
   const size_t BHTd = (size_t)c->B * c->H * (size_t)c->T * c->d;
   p->qkv_off = 0;
-  p->qkv_bytes = align_up(3 * BHTd * sizeof(float));
+  if (algo == TTT_ALGO_MFMA) {
+    p->qkv_bytes = align_up(ttt::scan_mfma_tile_bytes(c->B, c->T, c->H));
+    p->wst_bytes = 0;
+  } else {
+    p->qkv_bytes = align_up(3 * BHTd * sizeof(float));
+    p->wst_bytes = align_up((size_t)c->B * c->H * 2 * (size_t)c->d * c->m * sizeof(float));
+  }
   p->wst_off = p->qkv_off + p->qkv_bytes;
-  p->wst_bytes = align_up((size_t)c->B * c->H * 2 * (size_t)c->d * c->m * sizeof(float));
   p->total = p->wst_off + p->wst_bytes;
+  if (p->total == 0) p->total = kAlign;
   return TTT_OK;
+}
+
+hipError_t launch_projection(const ttt::ProjArgs& pa, int mode, hipStream_t s) {
+  if (ttt::project_mfma_supported(pa)) return ttt::launch_project_mfma(pa, mode, s);
+  return ttt::launch_project_f32out(pa, s);  // mode 0 only: the MFMA scan always has a supported GEMM
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -197,11 +211,15 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
   pa.H = c->H;
   pa.d = c->d;
   pa.bf16 = c->io_dtype == TTT_BF16;
-  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, stream, [&] { return ttt::launch_project_f32out(pa, stream); });
+  pa.reverse = reverse;
+  pa.blk_elems = ttt::scan_mfma_block_elems();
+  const bool mfma = pl.algo == TTT_ALGO_MFMA;
+  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, stream, [&] { return launch_projection(pa, mfma ? 1 : 0, stream); });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
 
   ttt::ScanArgs sa{};
   sa.qkv = (const float*)(ws + pl.qkv_off);
+  sa.qkv_tiles = ws + pl.qkv_off;
   sa.xin = xin;
   sa.y = y;
   sa.z = z;
@@ -222,7 +240,8 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
   sa.gelu_tanh = c->gelu == TTT_GELU_TANH;
   sa.reverse = reverse;
   sa.bf16 = c->io_dtype == TTT_BF16;
-  e = timed_launch(TTT_KERNEL_SCAN, stream, [&] { return ttt::launch_scan_generic(sa, stream); });
+  e = timed_launch(TTT_KERNEL_SCAN, stream,
+                   [&] { return mfma ? ttt::launch_scan_mfma(sa, stream) : ttt::launch_scan_generic(sa, stream); });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   return TTT_OK;
 }
@@ -350,8 +369,9 @@ int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* th
   pa.H = cfg->H;
   pa.d = cfg->d;
   pa.bf16 = cfg->io_dtype == TTT_BF16;
+  pa.reverse = 0;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, s, [&] { return ttt::launch_project_f32out(pa, s); });
+  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, s, [&] { return launch_projection(pa, 0, s); });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
   return ok();
 }

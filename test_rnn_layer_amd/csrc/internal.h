@@ -14,10 +14,16 @@ struct ProjArgs {
   int64_t B, T;
   int32_t H, d;
   int32_t bf16;       // 1: X and theta are bf16, 0: fp32
+  int32_t reverse;    // token-block layout only: blocks follow the reversed sequence
+  int32_t blk_elems;  // token-block layout only: bf16 elements per 16-token block
 };
 
-// fp32 output, [3, B, H, T, d].
+// fp32 output, [3, B, H, T, d] (VALU kernel, any dtype and shape).
 hipError_t launch_project_f32out(const ProjArgs& a, hipStream_t s);
+
+// bf16 MFMA GEMM; mode 0: fp32 [3, B, H, T, d]; mode 1: the MFMA scan's token blocks.
+bool project_mfma_supported(const ProjArgs& a);
+hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s);
 
 // One direction of the scan.
 struct ScanArgs {
@@ -44,5 +50,11 @@ struct ScanArgs {
 // LDS bytes the generic scan needs for (d, m, b).
 size_t scan_generic_lds_bytes(int d, int m, int b);
 hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t s);
+
+// MFMA scan (d = 64, m = 256, b = 16, bf16 io).
+bool scan_mfma_supported(int d, int m, int b);
+size_t scan_mfma_tile_bytes(int64_t B, int64_t T, int H);
+int scan_mfma_block_elems();
+hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s);
 
 }  // namespace ttt

@@ -90,3 +90,12 @@ def test_compute_calls_reject_bad_pointers_on_the_host():
     assert st == L.TTT_ERR_INVALID_ARG
     st = lib.ttt_mlp_kernel_timing(5, ctypes.byref(ctypes.c_double()), ctypes.byref(ctypes.c_int64()))
     assert st == L.TTT_ERR_INVALID_ARG
+
+
+def test_algo_selection():
+    assert L.select_algo(cfg()) == "mfma"
+    assert L.select_algo(cfg(algo="generic")) == "generic"
+    assert L.select_algo(L.make_config(1, 10, 1, 16, 64, 1, 0.1, io_dtype="f32")) == "generic"
+    with pytest.raises(L.TTTError) as e:
+        L.select_algo(cfg(b=8, algo="mfma"))
+    assert e.value.status == L.TTT_ERR_UNSUPPORTED

@@ -17,7 +17,17 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
 F32_TOL = 1e-4
-ALGOS = ["generic"]
+ALGOS = ["generic", "mfma"]
+
+
+def _skip_unsupported(wl, algo):
+    from test_rnn_layer_amd import _lib
+    try:
+        _lib.select_algo(_cfg(wl, algo))
+    except _lib.TTTError as e:
+        if e.status == _lib.TTT_ERR_UNSUPPORTED:
+            pytest.skip(f"{algo} does not support d={wl.d} m={wl.m} b={wl.b} io={wl.io_dtype}")
+        raise
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -98,6 +108,7 @@ SMALL = {
 @pytest.mark.parametrize("reverse", [False, True])
 def test_forward_matches_oracle(case, reverse, algo):
     wl = SMALL[case]
+    _skip_unsupported(wl, algo)
     print(f"[forward] case={case} reverse={reverse} algo={algo} shape=B{wl.B} T{wl.T} H{wl.H} d{wl.d} m{wl.m} b{wl.b}",
           flush=True)
     inp = W.make_inputs(wl)
@@ -110,6 +121,7 @@ def test_forward_matches_oracle(case, reverse, algo):
 @pytest.mark.parametrize("case", ["h3_d64_b16_ragged", "h2_d128_b1", "seg_shift_b16", "tiny_f32_b4_ragged"])
 def test_bidir_matches_oracle(case, algo):
     wl = SMALL[case].replace(alpha_f=0.1, alpha_b=0.2)  # distinct gates catch a swap
+    _skip_unsupported(wl, algo)
     print(f"[bidir] case={case} algo={algo}", flush=True)
     inp = W.make_inputs(wl)
     got = _gpu_bidir(wl, device_inputs(wl, inp), algo)
@@ -123,13 +135,14 @@ def test_bidir_matches_oracle(case, algo):
         _check(k, from_device(got[k]), ref[k], wl.io_dtype)
 
 
-def test_empty_sequence_returns_initial_state():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_empty_sequence_returns_initial_state(algo):
     from test_rnn_layer_amd import _lib
     wl = SMALL["h3_d64_b16_ragged"].replace(T=0)
-    print("[empty] T=0", flush=True)
+    print(f"[empty] T=0 algo={algo}", flush=True)
     inp = W.make_inputs(wl)
     dev = device_inputs(wl, inp)
-    r = _lib.bidir(_cfg(wl), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dev["alpha_b"],
+    r = _lib.bidir(_cfg(wl, algo), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dev["alpha_b"],
                    want_z=True, want_state=True)
     torch.cuda.synchronize()
     assert r["Y"].numel() == 0
