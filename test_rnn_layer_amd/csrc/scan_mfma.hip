@@ -78,17 +78,23 @@ struct Gelu {
   }
 };
 
+// tanh form: 0.5 a (1 + tanh(u)), u = sqrt(2/pi) (a + 0.044715 a^3), with
+// tanh(u) = 1 - 2 / (exp(2u) + 1) (exact identity; saturates to +-1 for large |u|).
 struct GeluTanh {
+  static __device__ __forceinline__ float tanh_u(float u) {
+    const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * u);  // exp(2u)
+    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  }
   static __device__ __forceinline__ void both(float a, float* g, float* dg) {
-    const float u = 0.7978845608028654f * (a + 0.044715f * a * a * a);
-    const float th = tanhf(u);
-    const float du = 0.7978845608028654f * (1.0f + 3.0f * 0.044715f * a * a);
+    const float u = 0.7978845608028654f * fmaf(0.044715f * a, a * a, a);
+    const float th = tanh_u(u);
+    const float du = 0.7978845608028654f * fmaf(3.0f * 0.044715f * a, a, 1.0f);
     *g = 0.5f * a * (1.0f + th);
-    *dg = 0.5f * (1.0f + th) + 0.5f * a * (1.0f - th * th) * du;
+    *dg = fmaf(0.5f * a * du, fmaf(-th, th, 1.0f), 0.5f * (1.0f + th));
   }
   static __device__ __forceinline__ float value(float a) {
-    const float u = 0.7978845608028654f * (a + 0.044715f * a * a * a);
-    return 0.5f * a * (1.0f + tanhf(u));
+    const float u = 0.7978845608028654f * fmaf(0.044715f * a, a * a, a);
+    return 0.5f * a * (1.0f + tanh_u(u));
   }
 };
 
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int ch0 = h * SD + 16 * w + 4 * g;
   float tg[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) tg[r] = tanhf(a.alpha[ch0 + r]);
+  for (int r = 0; r < 4; ++r) tg[r] = GeluTanh::tanh_u(a.alpha[ch0 + r]);
 
   const int64_t nblk = (T + SB - 1) / SB;
   const uint16_t* blocks = (const uint16_t*)a.qkv_tiles + ((int64_t)s * a.H + h) * nblk * BLK;

@@ -97,6 +97,8 @@ SMALL = {
     "seg_shift_b16": W.WORKLOADS["bidir307k"].replace(T=512, H=2, seg_len=160, name="seg_shift_b16"),
     "sum_loss_tanh": W.WORKLOADS["seg14k"].replace(T=77, H=2, loss="sum", eta=0.1 / 16 / 64, gelu="tanh",
                                                    name="sum_loss_tanh"),
+    "tanh_gelu": W.WORKLOADS["seg14k"].replace(T=77, H=2, gelu="tanh", name="tanh_gelu"),
+    "sum_loss": W.WORKLOADS["seg14k"].replace(T=77, H=2, loss="sum", eta=0.1 / 16 / 64, name="sum_loss"),
     "two_sequences": W.WORKLOADS["seg14k"].replace(B=2, T=64, H=2, name="two_sequences"),
     "one_token": W.WORKLOADS["seg14k"].replace(T=1, H=2, name="one_token"),
     "shorter_than_b": W.WORKLOADS["seg14k"].replace(T=9, H=2, name="shorter_than_b"),
