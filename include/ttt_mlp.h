@@ -78,7 +78,8 @@ extern "C" {
 /* scan kernel selection */
 #define TTT_ALGO_AUTO 0    /* fastest kernel that supports the shape and dtype */
 #define TTT_ALGO_GENERIC 1 /* fp32 VALU scan, any supported shape */
-#define TTT_ALGO_MFMA 2    /* bf16-operand MFMA scan, fp32 state (bf16 io only) */
+#define TTT_ALGO_MFMA 2    /* bf16-operand MFMA scan, fp32 state: bf16 io, erf GELU,
+                              d = 64, m = 256, b = 16 */
 
 typedef struct ttt_mlp_config {
   int64_t B;        /* sequences, >= 1 */

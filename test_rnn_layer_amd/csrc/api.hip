@@ -135,8 +135,10 @@ int32_t check_config(const ttt_mlp_config* c) {
   return TTT_OK;
 }
 
+// The MFMA scan implements the exact (erf) GELU; the tanh form runs on the generic kernel.
 bool mfma_possible(const ttt_mlp_config* c) {
-  return c->io_dtype == TTT_BF16 && ttt::scan_mfma_supported(c->d, c->m, c->b) && ((int64_t)c->H * c->d) % 8 == 0;
+  return c->io_dtype == TTT_BF16 && c->gelu == TTT_GELU_ERF && ttt::scan_mfma_supported(c->d, c->m, c->b) &&
+         ((int64_t)c->H * c->d) % 8 == 0;
 }
 
 int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
@@ -145,8 +147,9 @@ int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   int algo = c->algo;
   if (algo == TTT_ALGO_AUTO) algo = mfma_possible(c) ? TTT_ALGO_MFMA : TTT_ALGO_GENERIC;
   if (algo == TTT_ALGO_MFMA && !mfma_possible(c))
-    return fail(TTT_ERR_UNSUPPORTED, "the MFMA scan needs bf16 io, d=64, m=256, b=16 (got d=%d m=%d b=%d io=%d)",
-                c->d, c->m, c->b, c->io_dtype);
+    return fail(TTT_ERR_UNSUPPORTED,
+                "the MFMA scan needs bf16 io, erf GELU, d=64, m=256, b=16 (got d=%d m=%d b=%d io=%d gelu=%d)", c->d,
+                c->m, c->b, c->io_dtype, c->gelu);
   if (algo == TTT_ALGO_GENERIC && ttt::scan_generic_lds_bytes(c->d, c->m, c->b) > kGenericLdsMax)
     return fail(TTT_ERR_UNSUPPORTED,
                 "generic scan: mini-batch working set of %zu bytes (d=%d m=%d b=%d) exceeds %zu bytes of LDS",
