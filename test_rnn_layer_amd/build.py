@@ -7,6 +7,7 @@ hipcc cross-compiles without a GPU.  Every source is compiled on each call.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -29,11 +30,29 @@ FLAGS = [
 ]
 
 
+# kernels that must keep their whole working set in registers: the MFMA scan
+# holds the inner-model state in VGPRs for the whole sequence, and a spilling
+# build of it is refused.
+NO_SPILL_SOURCES = {"scan_mfma.hip"}
+
+
+def _check_no_spill(src, remarks):
+    spills = re.findall(r"VGPRs Spill: (\d+)", remarks) + re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", remarks)
+    if not spills:
+        raise RuntimeError(f"{src}: no resource-usage report from the compiler")
+    if any(int(x) for x in spills):
+        raise RuntimeError(f"{src}: the kernel spills registers to scratch:\n{remarks}")
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = r.stdout
+    src = os.path.basename(cmd[cmd.index("-c") + 1]) if "-c" in cmd else ""
+    if r.returncode == 0 and src in NO_SPILL_SOURCES:
+        _check_no_spill(src, "\n".join(l for l in out.splitlines() if "remark" in l))
+        out = "\n".join(l for l in out.splitlines() if "remark" not in l)
     # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
     out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l and l.strip())
     if r.returncode != 0:
@@ -48,7 +67,8 @@ def build(verbose: bool = False) -> str:
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        extra = ["-Rpass-analysis=kernel-resource-usage"] if src in NO_SPILL_SOURCES else []
+        cmds.append([HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

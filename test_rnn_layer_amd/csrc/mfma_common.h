@@ -56,6 +56,17 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
+// Wait until this wave's LDS stores have completed (lgkmcnt = 0) and keep the
+// scheduler from moving anything across.  Used after storing matrix-core
+// results to LDS: the store reads its data registers asynchronously, and a
+// following MFMA that reuses those registers as its destination must not
+// overwrite them first.
+__device__ __forceinline__ void lds_stores_done() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt and expcnt unconstrained, lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Position of feature j inside a row stored in the pair order (32-slices).
 __host__ __device__ __forceinline__ int pair_order_pos(int j) {
   const int jc = j & ~31, jl = j & 31;

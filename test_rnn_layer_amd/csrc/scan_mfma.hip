@@ -34,7 +34,8 @@ namespace {
 constexpr int SD = 64;   // head width
 constexpr int SM = 256;  // hidden width
 constexpr int SB = 16;   // mini-batch
-constexpr int NWAVE = 4;
+constexpr int NWAVE = 8;          // wave w owns hidden units [32w, 32w + 32)
+constexpr int NTHR = 64 * NWAVE;
 // Token block layout (bf16 elements), rows padded so that the 16 rows read by
 // one 16-lane group fall on distinct LDS banks:
 //   Q  [16 tokens][RS]  features in the pair order
@@ -133,263 +134,300 @@ __device__ __forceinline__ bf16x4 rd_v(const uint16_t* blk, int n, int w, int g,
 }
 
 template <class G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_mfma_kernel(ScanArgs a) {
-  __shared__ f32x4 Ypart[NWAVE][4][64];                      // partial Yhat^T per wave, d-tile, lane
-  __shared__ f32x4 Zpart[NWAVE][4][64];                      // partial Z^T
-  __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];         // G2 [token][feature, pair order]
-  __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];         // -eta G2 [feature][token]
-  __shared__ __attribute__((aligned(16))) uint16_t Stage[2][BLK];        // token blocks j (and j+1)
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_mfma_kernel(ScanArgs a) {
+  __shared__ f32x4 Ypart[NWAVE][4][64];                            // partial Yhat^T: wave, d-tile, lane
+  __shared__ f32x4 Zpart[NWAVE][4][64];                            // partial Z^T
+  __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // G2 [token][feature, pair order]
+  __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
+  __shared__ __attribute__((aligned(16))) uint16_t Stage[3][BLK];   // token blocks j-1, j, j+1
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int64_t T = a.T;
   const int D = a.H * SD;
-  const int m0 = 64 * w;
-  const float eta = a.eta, neta = -a.eta, gs = a.gscale;
+  const int m0 = 32 * w;
+  const float neta = -a.eta, gs = a.gscale;
 
-  // ---- state, D layout: W1 rows d / cols m, W2 rows m / cols d
-  f32x4 W1[4][4], W2[4][4];
+  // ---- state, D layout: W1 rows d (4 tiles) / cols m (2 tiles), W2 rows m (2 tiles) / cols d (4 tiles)
+  f32x4 W1[4][2], W2[2][4];
   {
     const float* w1 = a.w1_0 + (int64_t)h * SD * SM;
     const float* w2 = a.w2_0 + (int64_t)h * SM * SD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          W1[i][j][r] = w1[(16 * i + 4 * g + r) * SM + m0 + 16 * j + c];
-          W2[i][j][r] = w2[(m0 + 16 * i + 4 * g + r) * SD + 16 * j + c];
+        for (int nt = 0; nt < 2; ++nt) {
+          W1[dt][nt][r] = w1[(16 * dt + 4 * g + r) * SM + m0 + 16 * nt + c];
+          W2[nt][dt][r] = w2[(m0 + 16 * nt + 4 * g + r) * SD + 16 * dt + c];
         }
+    }
   }
   // the 16 x 16 identity as a K=16 B operand: lane holds rows 4g..4g+3 of column c
   bf16x4 ident;
 #pragma unroll
   for (int r = 0; r < 4; ++r) ident[r] = (__bf16)(4 * g + r == c ? 1.0f : 0.0f);
 
-  // gate factors of the 4 channels this lane finishes: 16w + 4g + r
-  const int ch0 = h * SD + 16 * w + 4 * g;
-  float tg[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) tg[r] = GeluTanh::tanh_u(a.alpha[ch0 + r]);
+  // The two finished values of this lane between the barriers: d-tile rd_dt,
+  // source lane rd_src (of each wave's partial tile), elements 2 rd_p, 2 rd_p + 1,
+  // i.e. token rd_t, features rd_d and rd_d + 1.
+  const int rd_dt = w >> 1;
+  const int rd_src = 32 * (w & 1) + (lane & 31);
+  const int rd_p = lane >> 5;
+  const int rd_t = rd_src & 15;
+  const int rd_d = 16 * rd_dt + 4 * (rd_src >> 4) + 2 * rd_p;
+  const int ch0 = h * SD + rd_d;
+  const float tg0 = GeluTanh::tanh_u(a.alpha[ch0]), tg1 = GeluTanh::tanh_u(a.alpha[ch0 + 1]);
 
   const int64_t nblk = (T + SB - 1) / SB;
   const uint16_t* blocks = (const uint16_t*)a.qkv_tiles + ((int64_t)s * a.H + h) * nblk * BLK;
   const uint16_t* xin = (const uint16_t*)a.xin;
   uint16_t* yout = (uint16_t*)a.y;
-
   auto tok_index = [&](int64_t pos) -> int64_t { return a.reverse ? T - 1 - pos : pos; };
   auto block_n = [&](int64_t j) -> int { return (int)((T - SB * j) < SB ? (T - SB * j) : SB); };
 
-  // reduce the Z partials of block jz, gate and store (each wave: d-tile w)
-  auto finish_z = [&](int64_t jz, bf16x4 xv) {
-    f32x4 z = Zpart[0][w][lane] + Zpart[1][w][lane] + Zpart[2][w][lane] + Zpart[3][w][lane];
-    const int64_t pos = SB * jz + c;
-    if (pos < T) {
-      const int64_t o = ((int64_t)s * T + tok_index(pos)) * D + ch0;
-      bf16x4 yv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) yv[r] = (__bf16)fmaf(tg[r], z[r], (float)xv[r]);
-      *(bf16x4*)(yout + o) = yv;
-      if (a.z) *(f32x4*)(a.z + o) = z;
-    }
-  };
-  auto load_x = [&](int64_t jx) -> bf16x4 {
-    const int64_t pos = SB * jx + c;
-    if (pos >= T) return bf16x4{(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
-    return ld4(xin + ((int64_t)s * T + tok_index(pos)) * D + ch0);
-  };
-
-  // block staging: global -> registers at the start of a mini-batch, -> LDS mid-way
-  uint4 pf[3];
+  // token blocks: global -> registers one step ahead, registers -> LDS two steps ahead of use
+  uint4 pf[2];
   auto fetch = [&](int64_t jb) {
     const uint4* src = (const uint4*)(blocks + jb * BLK);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int q = tid + 256 * i;
-      if (q < BLK_CHUNKS) pf[i] = src[q];
-    }
+    pf[0] = src[tid];
+    if (tid + NTHR < BLK_CHUNKS) pf[1] = src[tid + NTHR];
   };
   auto stage = [&](int buf) {
     uint4* dst = (uint4*)Stage[buf];
+    dst[tid] = pf[0];
+    if (tid + NTHR < BLK_CHUNKS) dst[tid + NTHR] = pf[1];
+    lds_stores_done();  // the staging registers are reloaded next
+  };
+  static_assert(BLK_CHUNKS > NTHR && BLK_CHUNKS <= 2 * NTHR, "two 16-byte chunks per thread");
+  auto load_x = [&](int64_t jx) -> uint32_t {  // two bf16 gate inputs of this lane's finished values
+    const int64_t pos = SB * jx + rd_t;
+    if (jx < 0 || pos >= T) return 0u;
+    return *(const uint32_t*)(xin + ((int64_t)s * T + tok_index(pos)) * D + ch0);
+  };
+  // the two values of (wave-summed) partial tile `part` this lane finishes
+  auto reduce2 = [&](const f32x4 (*part)[4][64]) -> float2 {
+    float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int q = tid + 256 * i;
-      if (q < BLK_CHUNKS) dst[q] = pf[i];
+    for (int q = 0; q < NWAVE; ++q) {
+      const float2 v = *((const float2*)&part[q][rd_dt][rd_src] + rd_p);
+      acc.x += v.x;
+      acc.y += v.y;
+    }
+    return acc;
+  };
+  auto finish_z = [&](int64_t jz, uint32_t xv) {
+    const float2 z = reduce2(Zpart);
+    const int64_t pos = SB * jz + rd_t;
+    if (pos < T) {
+      const int64_t o = ((int64_t)s * T + tok_index(pos)) * D + ch0;
+      const float x0 = __uint_as_float(xv << 16), x1 = __uint_as_float(xv & 0xffff0000u);
+      const __bf16 y0 = (__bf16)fmaf(tg0, z.x, x0), y1 = (__bf16)fmaf(tg1, z.y, x1);
+      *(uint32_t*)(yout + o) = (uint32_t)__builtin_bit_cast(uint16_t, y0) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, y1) << 16);
+      if (a.z) *(float2*)(a.z + o) = z;
     }
   };
+
+  // carried from block j-1 to its read-out during block j
+  f32x4 St_prev = zero4();
+  bf16x4 g1T_prev[2], g2T_prev[4];
+  bf16x8 hkB_prev = zero8();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) g1T_prev[i] = ident;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) g2T_prev[i] = ident;
+  uint32_t x_prev = 0u, x_cur = load_x(0);
+
   if (nblk > 0) {
     fetch(0);
     stage(0);
   }
+  if (nblk > 1) {
+    fetch(1);
+    stage(1);
+  }
+  if (nblk > 2) fetch(2);
   __syncthreads();
-  bf16x4 x_prev = bf16x4{(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
 
-  for (int64_t j = 0; j < nblk; ++j) {
-    const int n = block_n(j);
-    const uint16_t* blk = Stage[j & 1];
-    // prefetch the next block and this block's gate input
-    if (j + 1 < nblk) fetch(j + 1);
-    const bf16x4 x_cur = load_x(j);
+  // Iteration j runs block j's recurrence and block j-1's read-out; the extra
+  // iteration j = nblk only reads out the last block.
+  for (int64_t j = 0; j <= nblk && nblk > 0; ++j) {
+    const bool live = j < nblk;
+    const int n = live ? block_n(j) : 0;
+    const uint16_t* blk = Stage[j % 3];
+    const uint16_t* blk_prev = Stage[(j + 2) % 3];
 
-    // ---- 1. A^T = W1^T K^T (per hidden tile), S^T = K Q^T
-    f32x4 At[4];
-    f32x4 St;
+    // ---- bf16 operands of the current state
+    bf16x8 w1p[2][2], w2p[4];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) w1p[cc][nt] = pack8(W1[2 * cc][nt], W1[2 * cc + 1][nt]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) w2p[dt] = pack8(W2[0][dt], W2[1][dt]);
+
+    // ---- read-out of block j-1 with the state that follows it:
+    //   Aq = Q W1' + eta striu(Q K^T) G1,  Z = GELU(Aq) W2' + eta striu(Hq Hk^T) G2
+    if (j > 0) {
+      const int np = block_n(j - 1);
+      bf16x4 sT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sT[r] = (__bf16)(4 * g + r > c ? -St_prev[r] : 0.0f);
+      const bf16x8 q0 = rd_row8(blk_prev, OFF_Q, np, g, c, 0), q1 = rd_row8(blk_prev, OFF_Q, np, g, c, 1);
+      f32x4 Hq[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 aq = mfma32(w1p[0][nt], q0, zero4());
+        aq = mfma32(w1p[1][nt], q1, aq);
+        aq = mfma16(g1T_prev[nt], sT, aq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Hq[nt][r] = G::value(aq[r]);
+      }
+      const bf16x8 hqB = pack8(Hq[0], Hq[1]);
+      const f32x4 Pt = mfma32(hkB_prev, hqB, zero4());
+      bf16x4 pT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pT[r] = (__bf16)(4 * g + r > c ? -Pt[r] : 0.0f);
+      f32x4 zp[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        zp[dt] = mfma32(w2p[dt], hqB, zero4());
+        zp[dt] = mfma16(g2T_prev[dt], pT, zp[dt]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) Zpart[w][dt][lane] = zp[dt];
+      lds_stores_done();
+    }
+
+    // ---- A^T = W1^T K^T, S^T = K Q^T (block j)
+    f32x4 At[2], St;
     {
       const bf16x8 k0 = rd_row8(blk, OFF_K, n, g, c, 0), k1 = rd_row8(blk, OFF_K, n, g, c, 1);
       const bf16x8 q0 = rd_row8(blk, OFF_Q, n, g, c, 0), q1 = rd_row8(blk, OFF_Q, n, g, c, 1);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        At[nt] = mfma32(pack8(W1[0][nt], W1[1][nt]), k0, zero4());
-        At[nt] = mfma32(pack8(W1[2][nt], W1[3][nt]), k1, At[nt]);
+      for (int nt = 0; nt < 2; ++nt) {
+        At[nt] = mfma32(w1p[0][nt], k0, zero4());
+        At[nt] = mfma32(w1p[1][nt], k1, At[nt]);
       }
       St = mfma32(k0, q0, zero4());
       St = mfma32(k1, q1, St);
     }
-
-    // ---- 2. Hk^T = GELU(A^T), GELU'(A^T)
-    f32x4 Hk[4], Dg[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float hv, dv;
-        G::both(At[nt][r], &hv, &dv);
-        Hk[nt][r] = hv;
-        Dg[nt][r] = dv;
-      }
-    bf16x8 hkB[2];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) hkB[cc] = pack8(Hk[2 * cc], Hk[2 * cc + 1]);
-
-    // ---- 3. partial Yhat^T = W2^T Hk^T over this wave's hidden units
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      f32x4 yp = mfma32(pack8(W2[0][dt], W2[1][dt]), hkB[0], zero4());
-      yp = mfma32(pack8(W2[2][dt], W2[3][dt]), hkB[1], yp);
-      Ypart[w][dt][lane] = yp;
-    }
-    __syncthreads();
-
-    // ---- 4. finish d-tile w: G2 = c (Yhat - V); publish G2 and -eta G2
+    // ---- Hk^T = GELU(A^T), GELU'(A^T); partial Yhat^T = W2^T Hk^T over this wave's 32 hidden units
+    f32x4 Dg[2];
+    bf16x8 hkB;
     {
-      const f32x4 y = Ypart[0][w][lane] + Ypart[1][w][lane] + Ypart[2][w][lane] + Ypart[3][w][lane];
-      f32x4 g2;
-      const bf16x4 vv = rd_v(blk, n, w, g, c);
+      f32x4 Hk[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) g2[r] = gs * (y[r] - (float)vv[r]);
-      // G2[token c][feature 16w + 4g + r] in the pair order
-      *(bf16x4*)(&G2a[c * RS + 32 * (w >> 1) + 8 * g + 4 * (w & 1)]) = pack4(g2);
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const __bf16 b = (__bf16)(neta * g2[r]);
-        G2b[(16 * w + 4 * g + r) * TS + c] = __builtin_bit_cast(uint16_t, b);
-      }
-      if (j > 0) finish_z(j - 1, x_prev);
-      if (j + 1 < nblk) stage((j + 1) & 1);
+        for (int r = 0; r < 4; ++r) {
+          float hv, dv;
+          G::both(At[nt][r], &hv, &dv);
+          Hk[nt][r] = hv;
+          Dg[nt][r] = dv;
+        }
+      hkB = pack8(Hk[0], Hk[1]);
+      f32x4 yp[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) yp[dt] = mfma32(w2p[dt], hkB, zero4());
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) Ypart[w][dt][lane] = yp[dt];
+      lds_stores_done();
     }
+
     __syncthreads();
 
-    // ---- 5. Gh^T = W2 G2^T (W2 slice from the transposed copy)
+    // ---- finish this lane's two values: Z of block j-1 (gate, store), G2 of block j
+    if (j > 0) finish_z(j - 1, x_prev);
+    if (!live) break;
+    {
+      const float2 y = reduce2(Ypart);
+      const uint32_t vv = *(const uint32_t*)(blk + OFF_V + rd_t * RS + rd_d);
+      float g2x = 0.0f, g2y = 0.0f;
+      if (rd_t < n) {
+        g2x = gs * (y.x - __uint_as_float(vv << 16));
+        g2y = gs * (y.y - __uint_as_float(vv & 0xffff0000u));
+      }
+      const __bf16 b0 = (__bf16)g2x, b1 = (__bf16)g2y;
+      *(uint32_t*)&G2a[rd_t * RS + pair_order_pos(rd_d)] =
+          (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      G2b[rd_d * TS + rd_t] = __builtin_bit_cast(uint16_t, (__bf16)(neta * g2x));
+      G2b[(rd_d + 1) * TS + rd_t] = __builtin_bit_cast(uint16_t, (__bf16)(neta * g2y));
+    }
+
+    __syncthreads();
+
+    // ---- Gh^T = W2 G2^T (contraction over d: transposes of the W2 tiles), G1^T = Gh^T * GELU'(A^T)
     bf16x8 g2B[2];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) g2B[cc] = *(const bf16x8*)(&G2a[c * RS + 32 * cc + 8 * g]);
     bf16x4 g2T[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) g2T[dt] = *(const bf16x4*)(&G2b[(16 * dt + c) * TS + 4 * g]);
-    f32x4 G1[4];
+    bf16x4 g1T[2], hkT[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      // W2 slice rows m (tile mt), contraction over d: transposes of the W2 tiles
-      f32x4 t0 = mfma16(pack4(W2[mt][0]), ident, zero4());
-      f32x4 t1 = mfma16(pack4(W2[mt][1]), ident, zero4());
-      f32x4 t2 = mfma16(pack4(W2[mt][2]), ident, zero4());
-      f32x4 t3 = mfma16(pack4(W2[mt][3]), ident, zero4());
-      f32x4 gh = mfma32(pack8(t0, t1), g2B[0], zero4());
-      gh = mfma32(pack8(t2, t3), g2B[1], gh);
-      // ---- 6. G1^T = Gh^T * GELU'(A^T)
-      G1[mt] = gh * Dg[mt];
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 tt[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) tt[dt] = mfma16(pack4(W2[mt][dt]), ident, zero4());
+      f32x4 gh = mfma32(pack8(tt[0], tt[1]), g2B[0], zero4());
+      gh = mfma32(pack8(tt[2], tt[3]), g2B[1], gh);
+      const f32x4 g1 = gh * Dg[mt];
+      // token-major copies (tokens 4g..4g+3 of hidden unit m0 + 16mt + c)
+      g1T[mt] = pack4(mfma16(pack4(neta * g1), ident, zero4()));
+      bf16x4 hk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hk[r] = hkB[4 * mt + r];
+      hkT[mt] = pack4(mfma16(hk, ident, zero4()));
     }
-    // token-major copies of Hk and -eta G1 (tokens 4g..4g+3 of hidden unit 16mt + c)
-    bf16x4 hkT[4], g1T[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      hkT[mt] = pack4(mfma16(pack4(Hk[mt]), ident, zero4()));
-      g1T[mt] = pack4(mfma16(pack4(neta * G1[mt]), ident, zero4()));
-    }
-
-    // ---- 7. Aq^T = W1^T Q^T + (-eta G1)^T tril(S)^T
-    bf16x4 sT;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sT[r] = (__bf16)(4 * g + r <= c ? St[r] : 0.0f);
-    f32x4 Hq[4];
-    const bf16x8 q0 = rd_row8(blk, OFF_Q, n, g, c, 0), q1 = rd_row8(blk, OFF_Q, n, g, c, 1);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      f32x4 aq = mfma32(pack8(W1[0][nt], W1[1][nt]), q0, zero4());
-      aq = mfma32(pack8(W1[2][nt], W1[3][nt]), q1, aq);
-      aq = mfma16(g1T[nt], sT, aq);
-      // ---- 8. Hq^T = GELU(Aq^T)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Hq[nt][r] = G::value(aq[r]);
-    }
-    bf16x8 hqB[2];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) hqB[cc] = pack8(Hq[2 * cc], Hq[2 * cc + 1]);
-
-    // ---- 9. partial Z^T = W2^T Hq^T + (-eta G2)^T tril(Hq Hk^T)^T
-    f32x4 Pt = mfma32(hkB[0], hqB[0], zero4());
-    Pt = mfma32(hkB[1], hqB[1], Pt);
-    bf16x4 pT;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pT[r] = (__bf16)(4 * g + r <= c ? Pt[r] : 0.0f);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      f32x4 zp = mfma32(pack8(W2[0][dt], W2[1][dt]), hqB[0], zero4());
-      zp = mfma32(pack8(W2[2][dt], W2[3][dt]), hqB[1], zp);
-      zp = mfma16(g2T[dt], pT, zp);
-      Zpart[w][dt][lane] = zp;
-    }
-
-    // ---- 10. state update: W1 += K^T (-eta G1), W2 += Hk^T (-eta G2)
+    // ---- state update: W1 += K^T (-eta G1), W2 += Hk^T (-eta G2)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const bf16x4 kt = rd_kt(blk, n, g, c, dt);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) W1[dt][nt] = mfma16(kt, g1T[nt], W1[dt][nt]);
+      for (int nt = 0; nt < 2; ++nt) W1[dt][nt] = mfma16(kt, g1T[nt], W1[dt][nt]);
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) W2[mt][dt] = mfma16(hkT[mt], g2T[dt], W2[mt][dt]);
 
+    // ---- pipeline: stage block j+2 (its buffer held block j-1, read before the first barrier)
+    if (j + 2 < nblk) {
+      stage((int)((j + 2) % 3));
+      if (j + 3 < nblk) fetch(j + 3);
+    }
     x_prev = x_cur;
+    x_cur = load_x(j + 1);
+    St_prev = St;
+    g1T_prev[0] = g1T[0];
+    g1T_prev[1] = g1T[1];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) g2T_prev[dt] = g2T[dt];
+    hkB_prev = hkB;
   }
-  if (nblk > 0) {
-    __syncthreads();
-    finish_z(nblk - 1, x_prev);
-  }
-  (void)eta;
 
   // ---- final state
   if (a.w1_T) {
     float* o = a.w1_T + ((int64_t)s * a.H + h) * SD * SM;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[(16 * i + 4 * g + r) * SM + m0 + 16 * jj + c] = W1[i][jj][r];
+        for (int r = 0; r < 4; ++r) o[(16 * dt + 4 * g + r) * SM + m0 + 16 * nt + c] = W1[dt][nt][r];
   }
   if (a.w2_T) {
     float* o = a.w2_T + ((int64_t)s * a.H + h) * SM * SD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[(m0 + 16 * i + 4 * g + r) * SD + 16 * jj + c] = W2[i][jj][r];
+        for (int r = 0; r < 4; ++r) o[(m0 + 16 * mt + 4 * g + r) * SD + 16 * dt + c] = W2[mt][dt][r];
   }
 }
 
@@ -406,9 +444,9 @@ size_t scan_mfma_tile_bytes(int64_t B, int64_t T, int H) {
 
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s) {
   if (a.gelu_tanh)
-    hipLaunchKernelGGL(scan_mfma_kernel<GeluTanh>, dim3((unsigned)(a.B * a.H)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(scan_mfma_kernel<GeluTanh>, dim3((unsigned)(a.B * a.H)), dim3(NTHR), 0, s, a);
   else
-    hipLaunchKernelGGL(scan_mfma_kernel<Gelu>, dim3((unsigned)(a.B * a.H)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(scan_mfma_kernel<Gelu>, dim3((unsigned)(a.B * a.H)), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 
