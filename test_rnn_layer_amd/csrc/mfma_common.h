@@ -67,6 +67,14 @@ __device__ __forceinline__ void lds_stores_done() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Wait until this wave's vector-memory operations (including direct-to-LDS
+// loads) have completed.
+__device__ __forceinline__ void vmem_done() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Position of feature j inside a row stored in the pair order (32-slices).
 __host__ __device__ __forceinline__ int pair_order_pos(int j) {
   const int jc = j & ~31, jl = j & 31;

@@ -188,18 +188,16 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   auto tok_index = [&](int64_t pos) -> int64_t { return a.reverse ? T - 1 - pos : pos; };
   auto block_n = [&](int64_t j) -> int { return (int)((T - SB * j) < SB ? (T - SB * j) : SB); };
 
-  // token blocks: global -> registers one step ahead, registers -> LDS two steps ahead of use
-  uint4 pf[2];
-  auto fetch = [&](int64_t jb) {
+  // token blocks: direct global -> LDS loads two steps ahead of use (no registers);
+  // lane i of a wave fills bytes [16 i, 16 i + 16) of the wave's 1 KB slice
+  auto stage_async = [&](int64_t jb, int buf) {
     const uint4* src = (const uint4*)(blocks + jb * BLK);
-    pf[0] = src[tid];
-    if (tid + NTHR < BLK_CHUNKS) pf[1] = src[tid + NTHR];
-  };
-  auto stage = [&](int buf) {
     uint4* dst = (uint4*)Stage[buf];
-    dst[tid] = pf[0];
-    if (tid + NTHR < BLK_CHUNKS) dst[tid + NTHR] = pf[1];
-    lds_stores_done();  // the staging registers are reloaded next
+    __builtin_amdgcn_global_load_lds((const void*)(src + 64 * w + lane),
+                                     (__attribute__((address_space(3))) void*)(dst + 64 * w), 16, 0, 0);
+    if (NTHR + 64 * w + lane < BLK_CHUNKS)
+      __builtin_amdgcn_global_load_lds((const void*)(src + NTHR + 64 * w + lane),
+                                       (__attribute__((address_space(3))) void*)(dst + NTHR + 64 * w), 16, 0, 0);
   };
   static_assert(BLK_CHUNKS > NTHR && BLK_CHUNKS <= 2 * NTHR, "two 16-byte chunks per thread");
   auto load_x = [&](int64_t jx) -> uint32_t {  // two bf16 gate inputs of this lane's finished values
@@ -241,15 +239,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   for (int i = 0; i < 4; ++i) g2T_prev[i] = ident;
   uint32_t x_prev = 0u, x_cur = load_x(0);
 
-  if (nblk > 0) {
-    fetch(0);
-    stage(0);
-  }
-  if (nblk > 1) {
-    fetch(1);
-    stage(1);
-  }
-  if (nblk > 2) fetch(2);
+  if (nblk > 0) stage_async(0, 0);
+  if (nblk > 1) stage_async(1, 1);
+  vmem_done();
   __syncthreads();
 
   // Iteration j runs block j's recurrence and block j-1's read-out; the extra
@@ -340,6 +332,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 
     __syncthreads();
 
+    // this wave's block loads (issued last step) and gate inputs have landed; the
+    // second barrier publishes the staged block to every wave
+    vmem_done();
     // ---- finish this lane's two values: Z of block j-1 (gate, store), G2 of block j
     if (j > 0) finish_z(j - 1, x_prev);
     if (!live) break;
@@ -395,13 +390,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) W2[mt][dt] = mfma16(hkT[mt], g2T[dt], W2[mt][dt]);
 
-    // ---- pipeline: stage block j+2 (its buffer held block j-1, read before the first barrier)
-    if (j + 2 < nblk) {
-      stage((int)((j + 2) % 3));
-      if (j + 3 < nblk) fetch(j + 3);
-    }
+    // ---- pipeline: gate inputs one block ahead; block j+2 into the buffer that held
+    // block j-1 (last read before this step's first barrier)
     x_prev = x_cur;
     x_cur = load_x(j + 1);
+    if (j + 2 < nblk) stage_async(j + 2, (int)((j + 2) % 3));
     St_prev = St;
     g1T_prev[0] = g1T[0];
     g1T_prev[1] = g1T[1];
