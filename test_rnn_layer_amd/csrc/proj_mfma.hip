@@ -116,18 +116,9 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a) {
           const int64_t pos = a.reverse ? a.T - 1 - t : t;
           const int64_t jb = pos >> 4;
           const int tl = (int)(pos & 15);
-          // token block of the MFMA scan (d = 64): Q, K rows of 72 in the pair
-          // order, K^T rows of 20, V rows of 72
+          // token block of the MFMA scan (d = 64): Q, K, V rows of 72
           uint16_t* blk = out + (((int64_t)s * a.H + h) * nblk + jb) * (int64_t)a.blk_elems;
-          const uint16_t bits = to_bf16_bits(v);
-          if (p == 0) {
-            blk[tl * 72 + pair_order_pos(jj)] = bits;
-          } else if (p == 1) {
-            blk[16 * 72 + tl * 72 + pair_order_pos(jj)] = bits;
-            blk[32 * 72 + jj * 20 + tl] = bits;
-          } else {
-            blk[32 * 72 + 64 * 20 + tl * 72 + jj] = bits;
-          }
+          blk[(p * 16 + tl) * 72 + jj] = to_bf16_bits(v);
         }
       }
     }

@@ -36,17 +36,16 @@ constexpr int SM = 256;  // hidden width
 constexpr int SB = 16;   // mini-batch
 constexpr int NWAVE = 8;          // wave w owns hidden units [32w, 32w + 32)
 constexpr int NTHR = 64 * NWAVE;
-// Token block layout (bf16 elements), rows padded so that the 16 rows read by
-// one 16-lane group fall on distinct LDS banks:
-//   Q  [16 tokens][RS]  features in the pair order
-//   K  [16 tokens][RS]  features in the pair order
-//   KT [64 features][TS] tokens in order
-//   V  [16 tokens][RS]  features in order
+constexpr int NSTAGE = 4;         // token blocks in LDS: j-1 (read-out), j, and two in flight
+// Token block layout (bf16 elements): Q, K and V of 16 consecutive scan
+// positions, each [16 tokens][RS] with the features in order and rows padded to
+// RS = 72 (144 bytes) so that the 16 rows read by one 16-lane group fall on
+// distinct LDS banks.
 constexpr int RS = SD + 8;  // 72
-constexpr int TS = SB + 4;  // 20
-constexpr int OFF_Q = 0, OFF_K = SB * RS, OFF_KT = 2 * SB * RS, OFF_V = 2 * SB * RS + SD * TS;
-constexpr int BLK = 3 * SB * RS + SD * TS;  // 4736 elements, 9472 bytes
-constexpr int BLK_CHUNKS = BLK * 2 / 16;    // 592 chunks of 16 bytes
+constexpr int TS = SB + 4;  // 20: rows of the [feature][token] G2 copy
+constexpr int OFF_Q = 0, OFF_K = SB * RS, OFF_V = 2 * SB * RS;
+constexpr int BLK = 3 * SB * RS;          // 3456 elements, 6912 bytes
+constexpr int BLK_CHUNKS = BLK * 2 / 16;  // 432 chunks of 16 bytes
 static_assert((BLK * 2) % 16 == 0, "block must be a whole number of 16-byte chunks");
 
 // GELU and its derivative from one exponential.  erf by Abramowitz & Stegun
@@ -110,25 +109,16 @@ __device__ __forceinline__ bf16x8 zero8() {
 }
 
 // Readers of the staged token block (LDS), masking tokens >= n of a short block.
+// A K=32 operand row in the pair order: features 32cc + 4g .. +3 and 32cc + 16 + 4g .. +3.
 __device__ __forceinline__ bf16x8 rd_row8(const uint16_t* blk, int off, int n, int g, int c, int cc) {
-  return c < n ? *(const bf16x8*)(blk + off + c * RS + 32 * cc + 8 * g) : zero8();
-}
-
-__device__ __forceinline__ bf16x4 rd_kt(const uint16_t* blk, int n, int g, int c, int dt) {
-  bf16x4 k = *(const bf16x4*)(blk + OFF_KT + (16 * dt + c) * TS + 4 * g);
-  if (n < SB) {
+  if (c >= n) return zero8();
+  const uint16_t* row = blk + off + c * RS + 32 * cc + 4 * g;
+  const bf16x4 lo = *(const bf16x4*)row, hi = *(const bf16x4*)(row + 16);
+  bf16x8 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * g + i >= n) k[i] = (__bf16)0.0f;
-  }
-  return k;
-}
-
-__device__ __forceinline__ bf16x4 rd_v(const uint16_t* blk, int n, int w, int g, int c) {
-  bf16x4 v = *(const bf16x4*)(blk + OFF_V + c * RS + 16 * w + 4 * g);
-  if (c >= n) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (__bf16)0.0f;
+  for (int i = 0; i < 4; ++i) {
+    v[i] = lo[i];
+    v[4 + i] = hi[i];
   }
   return v;
 }
@@ -139,7 +129,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __shared__ f32x4 Zpart[NWAVE][4][64];                            // partial Z^T
   __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
-  __shared__ __attribute__((aligned(16))) uint16_t Stage[3][BLK];   // token blocks j-1, j, j+1
+  __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+2
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -170,6 +160,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
   for (int r = 0; r < 4; ++r) ident[r] = (__bf16)(4 * g + r == c ? 1.0f : 0.0f);
 
+  // 0/1 selectors that pick d-tile 2cc + half out of a pair-ordered 32-slice:
+  // K (rows t, pair-ordered d) times sel[half] is the D layout of K's d-tile,
+  // i.e. the token-major K^T operand of the W1 update.
+  bf16x8 sel[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int dpos = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);  // feature of position 8g + i
+      sel[half][i] = (__bf16)(dpos == 16 * half + c ? 1.0f : 0.0f);
+    }
+
   // The two finished values of this lane between the barriers: d-tile rd_dt,
   // source lane rd_src (of each wave's partial tile), elements 2 rd_p, 2 rd_p + 1,
   // i.e. token rd_t, features rd_d and rd_d + 1.
@@ -193,13 +195,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   auto stage_async = [&](int64_t jb, int buf) {
     const uint4* src = (const uint4*)(blocks + jb * BLK);
     uint4* dst = (uint4*)Stage[buf];
-    __builtin_amdgcn_global_load_lds((const void*)(src + 64 * w + lane),
-                                     (__attribute__((address_space(3))) void*)(dst + 64 * w), 16, 0, 0);
-    if (NTHR + 64 * w + lane < BLK_CHUNKS)
-      __builtin_amdgcn_global_load_lds((const void*)(src + NTHR + 64 * w + lane),
-                                       (__attribute__((address_space(3))) void*)(dst + NTHR + 64 * w), 16, 0, 0);
+    if (64 * w + lane < BLK_CHUNKS)
+      __builtin_amdgcn_global_load_lds((const void*)(src + 64 * w + lane),
+                                       (__attribute__((address_space(3))) void*)(dst + 64 * w), 16, 0, 0);
   };
-  static_assert(BLK_CHUNKS > NTHR && BLK_CHUNKS <= 2 * NTHR, "two 16-byte chunks per thread");
+  static_assert(BLK_CHUNKS <= NTHR, "one 16-byte chunk per thread");
   auto load_x = [&](int64_t jx) -> uint32_t {  // two bf16 gate inputs of this lane's finished values
     const int64_t pos = SB * jx + rd_t;
     if (jx < 0 || pos >= T) return 0u;
@@ -239,8 +239,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   for (int i = 0; i < 4; ++i) g2T_prev[i] = ident;
   uint32_t x_prev = 0u, x_cur = load_x(0);
 
-  if (nblk > 0) stage_async(0, 0);
-  if (nblk > 1) stage_async(1, 1);
+  for (int64_t jb = 0; jb < NSTAGE - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
   vmem_done();
   __syncthreads();
 
@@ -249,8 +248,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   for (int64_t j = 0; j <= nblk && nblk > 0; ++j) {
     const bool live = j < nblk;
     const int n = live ? block_n(j) : 0;
-    const uint16_t* blk = Stage[j % 3];
-    const uint16_t* blk_prev = Stage[(j + 2) % 3];
+    const uint16_t* blk = Stage[j % NSTAGE];
+    const uint16_t* blk_prev = Stage[(j + NSTAGE - 1) % NSTAGE];
 
     // ---- bf16 operands of the current state
     bf16x8 w1p[2][2], w2p[4];
@@ -379,9 +378,10 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       hkT[mt] = pack4(mfma16(hk, ident, zero4()));
     }
     // ---- state update: W1 += K^T (-eta G1), W2 += Hk^T (-eta G2)
+    const bf16x8 kr0 = rd_row8(blk, OFF_K, n, g, c, 0), kr1 = rd_row8(blk, OFF_K, n, g, c, 1);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const bf16x4 kt = rd_kt(blk, n, g, c, dt);
+      const bf16x4 kt = pack4(mfma32(dt < 2 ? kr0 : kr1, sel[dt & 1], zero4()));
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) W1[dt][nt] = mfma16(kt, g1T[nt], W1[dt][nt]);
     }
@@ -390,11 +390,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) W2[mt][dt] = mfma16(hkT[mt], g2T[dt], W2[mt][dt]);
 
-    // ---- pipeline: gate inputs one block ahead; block j+2 into the buffer that held
+    // ---- pipeline: gate inputs one block ahead; block j+3 into the buffer that held
     // block j-1 (last read before this step's first barrier)
     x_prev = x_cur;
     x_cur = load_x(j + 1);
-    if (j + 2 < nblk) stage_async(j + 2, (int)((j + 2) % 3));
+    if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) % NSTAGE));
     St_prev = St;
     g1T_prev[0] = g1T[0];
     g1T_prev[1] = g1T[1];
