@@ -78,8 +78,8 @@ struct Gelu {
   }
 };
 
-// tanh form: 0.5 a (1 + tanh(u)), u = sqrt(2/pi) (a + 0.044715 a^3), with
-// tanh(u) = 1 - 2 / (exp(2u) + 1) (exact identity; saturates to +-1 for large |u|).
+// tanh(u) = 1 - 2 / (exp(2u) + 1) (exact identity; saturates to +-1 for large |u|),
+// used for the gate factors tanh(alpha).
 struct GeluTanh {
   static __device__ __forceinline__ float tanh_u(float u) {
     const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * u);  // exp(2u)
@@ -435,11 +435,10 @@ size_t scan_mfma_tile_bytes(int64_t B, int64_t T, int H) {
   return (size_t)(B * H * nblk) * BLK * sizeof(uint16_t);
 }
 
+// Only the exact (erf) GELU is instantiated: the tanh form runs on the generic scan.
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s) {
-  if (a.gelu_tanh)
-    hipLaunchKernelGGL(scan_mfma_kernel<GeluTanh>, dim3((unsigned)(a.B * a.H)), dim3(NTHR), 0, s, a);
-  else
-    hipLaunchKernelGGL(scan_mfma_kernel<Gelu>, dim3((unsigned)(a.B * a.H)), dim3(NTHR), 0, s, a);
+  if (a.gelu_tanh) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scan_mfma_kernel<Gelu>, dim3((unsigned)(a.B * a.H)), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 
