@@ -44,12 +44,58 @@ def _check_no_spill(src, remarks):
         raise RuntimeError(f"{src}: the kernel spills registers to scratch:\n{remarks}")
 
 
+# kernels whose matrix-core accumulation chains must stay on one instruction: a
+# 16x16x32 result read as the accumulator of a 16x16x16 product a few
+# instructions later gave wrong values on gfx950 (the compiler inserts no wait
+# for it).  The build compiles these sources to assembly as well and refuses any
+# product whose accumulator comes from a product of another instruction.
+MFMA_CHAIN_SOURCES = {"scan_mfma.hip", "proj_mfma.hip"}
+_MFMA = re.compile(r"\s*(v_mfma\w*)\s+v\[(\d+):(\d+)\],\s*[^,]+,\s*[^,]+,\s*(?:v\[(\d+):(\d+)\]|\S+)")
+_VDST = re.compile(r"\s*(?:v_|ds_read|global_load|buffer_load|scratch_load|flat_load)\S*\s+(?:v(\d+)|v\[(\d+):(\d+)\])")
+
+
+def _vdst(line):
+    m = _VDST.match(line)
+    if not m or line.lstrip().startswith(("v_cmp", "v_readlane", "v_readfirstlane")):
+        return None
+    return (int(m.group(1)), int(m.group(1))) if m.group(1) else (int(m.group(2)), int(m.group(3)))
+
+
+def _check_mfma_chains(src, asm_path, window=48):
+    """Follows each matrix-core result until its registers are overwritten; a
+    product of another instruction that takes it as accumulator is refused."""
+    lines = [l.strip() for l in open(asm_path) if l.strip() and not l.strip().startswith((";", "."))]
+    bad = []
+    for i, line in enumerate(lines):
+        m = _MFMA.match(line)
+        if not m:
+            continue
+        d0, d1 = int(m.group(2)), int(m.group(3))
+        for k in range(i + 1, min(i + 1 + window, len(lines))):
+            if lines[k].endswith(":"):  # a label: the straight-line region ends
+                break
+            m2 = _MFMA.match(lines[k])
+            if m2 and m2.group(4) is not None and int(m2.group(4)) <= d1 and int(m2.group(5)) >= d0:
+                if m2.group(1) != m.group(1):
+                    bad.append(f"{line}  ->  {lines[k]}")
+                break
+            dst = _vdst(lines[k])
+            if dst is not None and dst[0] <= d1 and dst[1] >= d0:
+                break
+    if bad:
+        raise RuntimeError(f"{src}: accumulator taken from a product of another matrix-core instruction:\n" +
+                           "\n".join(bad))
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = r.stdout
     src = os.path.basename(cmd[cmd.index("-c") + 1]) if "-c" in cmd else ""
+    if r.returncode == 0 and "-S" in cmd:
+        _check_mfma_chains(src, cmd[cmd.index("-o") + 1])
+        src = ""
     if r.returncode == 0 and src in NO_SPILL_SOURCES:
         _check_no_spill(src, "\n".join(l for l in out.splitlines() if "remark" in l))
         out = "\n".join(l for l in out.splitlines() if "remark" not in l)
@@ -70,6 +116,9 @@ def build(verbose: bool = False) -> str:
         extra = ["-Rpass-analysis=kernel-resource-usage"] if src in NO_SPILL_SOURCES else []
         cmds.append([HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+        if src in MFMA_CHAIN_SOURCES:
+            asm = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".s")
+            cmds.append([HIPCC, *FLAGS, "--cuda-device-only", "-S", "-c", os.path.join(CSRC, src), "-o", asm])
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"

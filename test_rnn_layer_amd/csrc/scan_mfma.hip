@@ -36,7 +36,7 @@ constexpr int SM = 256;  // hidden width
 constexpr int SB = 16;   // mini-batch
 constexpr int NWAVE = 8;          // wave w owns hidden units [32w, 32w + 32)
 constexpr int NTHR = 64 * NWAVE;
-constexpr int NSTAGE = 4;         // token blocks in LDS: j-1 (read-out), j, and two in flight
+constexpr int NSTAGE = 3;         // token blocks in LDS: j-1 (read-out), j, and j+1 in flight
 // Token block layout (bf16 elements): Q, K and V of 16 consecutive scan
 // positions, each [16 tokens][RS] with the features in order and rows padded to
 // RS = 72 (144 bytes) so that the 16 rows read by one 16-lane group fall on
@@ -129,7 +129,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __shared__ f32x4 Zpart[NWAVE][4][64];                            // partial Z^T
   __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
-  __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+2
+  __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+1
+  __shared__ bf16x8 SelTab[2][64];                                  // K^T selectors (below), per lane
+  __shared__ float2 GateTab[NTHR];                                  // tanh(alpha) of each thread's two features
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -163,14 +165,20 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // 0/1 selectors that pick d-tile 2cc + half out of a pair-ordered 32-slice:
   // K (rows t, pair-ordered d) times sel[half] is the D layout of K's d-tile,
   // i.e. the token-major K^T operand of the W1 update.
-  bf16x8 sel[2];
+  // They are constants used once per step, so they live in LDS, not in registers
+  // (published by the barrier before the loop).
+  if (w == 0) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half)
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 sel;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int dpos = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);  // feature of position 8g + i
-      sel[half][i] = (__bf16)(dpos == 16 * half + c ? 1.0f : 0.0f);
+      for (int i = 0; i < 8; ++i) {
+        const int dpos = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);  // feature of position 8g + i
+        sel[i] = (__bf16)(dpos == 16 * half + c ? 1.0f : 0.0f);
+      }
+      SelTab[half][lane] = sel;
     }
+  }
 
   // The two finished values of this lane between the barriers: d-tile rd_dt,
   // source lane rd_src (of each wave's partial tile), elements 2 rd_p, 2 rd_p + 1,
@@ -181,7 +189,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int rd_t = rd_src & 15;
   const int rd_d = 16 * rd_dt + 4 * (rd_src >> 4) + 2 * rd_p;
   const int ch0 = h * SD + rd_d;
-  const float tg0 = GeluTanh::tanh_u(a.alpha[ch0]), tg1 = GeluTanh::tanh_u(a.alpha[ch0 + 1]);
+  // gate factors: loop constants used once per step, kept in this thread's LDS slot
+  GateTab[threadIdx.x] = make_float2(GeluTanh::tanh_u(a.alpha[ch0]), GeluTanh::tanh_u(a.alpha[ch0 + 1]));
 
   const int64_t nblk = (T + SB - 1) / SB;
   const uint16_t* blocks = (const uint16_t*)a.qkv_tiles + ((int64_t)s * a.H + h) * nblk * BLK;
@@ -191,13 +200,19 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   auto block_n = [&](int64_t j) -> int { return (int)((T - SB * j) < SB ? (T - SB * j) : SB); };
 
   // token blocks: direct global -> LDS loads two steps ahead of use (no registers);
-  // lane i of a wave fills bytes [16 i, 16 i + 16) of the wave's 1 KB slice
+  // lane i of a wave fills bytes [16 i, 16 i + 16) of the wave's 1 KB slice.  The
+  // load is written as a statement of its own rather than through the compiler's
+  // builtin: the compiler makes every later LDS read of Stage wait for all such
+  // loads in flight (it cannot tell the stages apart), which would expose their
+  // whole latency at the next step's first read.  The statement has no output
+  // registers; its completion is awaited explicitly (vmem_done) before the barrier
+  // that precedes the block's first use.
   auto stage_async = [&](int64_t jb, int buf) {
-    const uint4* src = (const uint4*)(blocks + jb * BLK);
-    uint4* dst = (uint4*)Stage[buf];
+    const uint4* src = (const uint4*)(blocks + jb * BLK) + 64 * w + lane;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)Stage[buf]) + 1024u * (uint32_t)w);
     if (64 * w + lane < BLK_CHUNKS)
-      __builtin_amdgcn_global_load_lds((const void*)(src + 64 * w + lane),
-                                       (__attribute__((address_space(3))) void*)(dst + 64 * w), 16, 0, 0);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(src) : "memory", "m0");
   };
   static_assert(BLK_CHUNKS <= NTHR, "one 16-byte chunk per thread");
   auto load_x = [&](int64_t jx) -> uint32_t {  // two bf16 gate inputs of this lane's finished values
@@ -216,13 +231,13 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     }
     return acc;
   };
-  auto finish_z = [&](int64_t jz, uint32_t xv) {
-    const float2 z = reduce2(Zpart);
+  auto store_z = [&](int64_t jz, uint32_t xv, float2 z) {
     const int64_t pos = SB * jz + rd_t;
     if (pos < T) {
       const int64_t o = ((int64_t)s * T + tok_index(pos)) * D + ch0;
       const float x0 = __uint_as_float(xv << 16), x1 = __uint_as_float(xv & 0xffff0000u);
-      const __bf16 y0 = (__bf16)fmaf(tg0, z.x, x0), y1 = (__bf16)fmaf(tg1, z.y, x1);
+      const float2 tg = GateTab[threadIdx.x];
+      const __bf16 y0 = (__bf16)fmaf(tg.x, z.x, x0), y1 = (__bf16)fmaf(tg.y, z.y, x1);
       *(uint32_t*)(yout + o) = (uint32_t)__builtin_bit_cast(uint16_t, y0) |
                                ((uint32_t)__builtin_bit_cast(uint16_t, y1) << 16);
       if (a.z) *(float2*)(a.z + o) = z;
@@ -237,7 +252,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   for (int i = 0; i < 2; ++i) g1T_prev[i] = ident;
 #pragma unroll
   for (int i = 0; i < 4; ++i) g2T_prev[i] = ident;
-  uint32_t x_prev = 0u, x_cur = load_x(0);
+  uint32_t x_blk = 0u;  // gate inputs of the block whose Z is finished next
 
   for (int64_t jb = 0; jb < NSTAGE - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
   vmem_done();
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 aq = mfma32(w1p[0][nt], q0, zero4());
         aq = mfma32(w1p[1][nt], q1, aq);
-        aq = mfma16(g1T_prev[nt], sT, aq);
+        aq = mfma16_as32(g1T_prev[nt], sT, aq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Hq[nt][r] = G::value(aq[r]);
       }
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         zp[dt] = mfma32(w2p[dt], hqB, zero4());
-        zp[dt] = mfma16(g2T_prev[dt], pT, zp[dt]);
+        zp[dt] = mfma16_as32(g2T_prev[dt], pT, zp[dt]);
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) Zpart[w][dt][lane] = zp[dt];
@@ -331,12 +346,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 
     __syncthreads();
 
-    // this wave's block loads (issued last step) and gate inputs have landed; the
-    // second barrier publishes the staged block to every wave
-    vmem_done();
-    // ---- finish this lane's two values: Z of block j-1 (gate, store), G2 of block j
-    if (j > 0) finish_z(j - 1, x_prev);
-    if (!live) break;
+    // ---- finish this lane's two values: Z of block j-1 (stored after the second
+    // barrier), G2 of block j.  No vector-memory operation is issued between the two
+    // barriers: each barrier's release fence waits for the wave's outstanding ones.
+    const float2 zfin = reduce2(Zpart);
+    if (!live) {
+      store_z(j - 1, x_blk, zfin);
+      break;
+    }
     {
       const float2 y = reduce2(Ypart);
       const uint32_t vv = *(const uint32_t*)(blk + OFF_V + rd_t * RS + rd_d);
@@ -352,7 +369,20 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       G2b[(rd_d + 1) * TS + rd_t] = __builtin_bit_cast(uint16_t, (__bf16)(neta * g2y));
     }
 
+    // this wave's vector-memory operations of the previous step (block j+1 into LDS,
+    // gate inputs of block j, stores) have had a whole step; the barrier then
+    // publishes block j+1 to every wave before its first use
+    vmem_done();
     __syncthreads();
+
+    // ---- vector-memory work of this step, issued right after the barrier and waited
+    // for just before the next step's second barrier: Y and Z of block j-1, the gate
+    // inputs of block j (one register, consumed before it is reloaded: no register
+    // rotation, which would make the compiler wait at once), block j+2 into the
+    // buffer that held block j-1 (last read before this step's first barrier)
+    if (j > 0) store_z(j - 1, x_blk, zfin);
+    x_blk = load_x(j);
+    if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) % NSTAGE));
 
     // ---- Gh^T = W2 G2^T (contraction over d: transposes of the W2 tiles), G1^T = Gh^T * GELU'(A^T)
     bf16x8 g2B[2];
@@ -381,7 +411,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const bf16x8 kr0 = rd_row8(blk, OFF_K, n, g, c, 0), kr1 = rd_row8(blk, OFF_K, n, g, c, 1);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const bf16x4 kt = pack4(mfma32(dt < 2 ? kr0 : kr1, sel[dt & 1], zero4()));
+      const bf16x4 kt = pack4(mfma32(dt < 2 ? kr0 : kr1, SelTab[dt & 1][lane], zero4()));
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) W1[dt][nt] = mfma16(kt, g1T[nt], W1[dt][nt]);
     }
@@ -390,11 +420,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) W2[mt][dt] = mfma16(hkT[mt], g2T[dt], W2[mt][dt]);
 
-    // ---- pipeline: gate inputs one block ahead; block j+3 into the buffer that held
-    // block j-1 (last read before this step's first barrier)
-    x_prev = x_cur;
-    x_cur = load_x(j + 1);
-    if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) % NSTAGE));
     St_prev = St;
     g1T_prev[0] = g1T[0];
     g1T_prev[1] = g1T[1];
@@ -403,24 +428,30 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     hkB_prev = hkB;
   }
 
-  // ---- final state
-  if (a.w1_T) {
-    float* o = a.w1_T + ((int64_t)s * a.H + h) * SD * SM;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[(16 * dt + 4 * g + r) * SM + m0 + 16 * nt + c] = W1[dt][nt][r];
-  }
-  if (a.w2_T) {
-    float* o = a.w2_T + ((int64_t)s * a.H + h) * SM * SD;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  // ---- final state.  The lane indices are derived afresh from an opaque copy of
+  // the thread index, so that no address term is kept live across the loop.
+  {
+    int t2 = tid;
+    asm volatile("" : "+v"(t2));
+    const int l2 = t2 & 63, g2 = l2 >> 4, c2 = l2 & 15, n0 = 32 * (t2 >> 6);
+    if (a.w1_T) {
+      float* o = a.w1_T + ((int64_t)s * a.H + h) * SD * SM;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[(m0 + 16 * mt + 4 * g + r) * SD + 16 * dt + c] = W2[mt][dt][r];
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[(16 * dt + 4 * g2 + r) * SM + n0 + 16 * nt + c2] = W1[dt][nt][r];
+    }
+    if (a.w2_T) {
+      float* o = a.w2_T + ((int64_t)s * a.H + h) * SM * SD;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[(n0 + 16 * mt + 4 * g2 + r) * SD + 16 * dt + c2] = W2[mt][dt][r];
+    }
   }
 }
 
