@@ -88,8 +88,8 @@ def cpu_baseline(wl, tokens: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="bidir307k")
     ap.add_argument("--algo", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--cpu-tokens", type=int, default=2048)
@@ -158,6 +158,8 @@ def main():
     proj_total = proj_flops_per_token(wl.D) * tokens * dirs
     scan_total = scan_flops_per_token_head(wl.d, wl.m, wl.b) * wl.H * tokens * dirs
     R_ms = (proj_total / (PEAK_BF16_TFLOPS * 1e12) + scan_total / (PEAK_FP32_TFLOPS * 1e12)) * 1e3
+    # the same with the scan's contractions priced at the bf16 peak (they run on bf16 operands)
+    R_exec_ms = (proj_total + scan_total) / (PEAK_BF16_TFLOPS * 1e12) * 1e3
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -168,7 +170,8 @@ def main():
                      "frac": achieved / peak, "traffic": traffic,
                      "flops_per_launch": scan_flops_launch, "avg_launch_ms": scan_avg_ms},
         "layer_roofline": {"R_ms": R_ms, "frac": R_ms / ms_per_step,
-                           "definition": "projection flops at bf16 MFMA peak + scan flops at fp32 peak"},
+                           "definition": "projection flops at bf16 MFMA peak + scan flops at fp32 peak",
+                           "R_exec_ms": R_exec_ms, "frac_exec": R_exec_ms / ms_per_step},
         "kernel_ms_per_step": {"scan": scan_ms / args.steps, "projection": proj_ms / args.steps},
     }
     if not args.no_cpu_baseline:

@@ -50,9 +50,9 @@ def cfg(**kw):
 
 
 def test_workspace_size_and_validation():
-    # generic: fp32 Q, K, V plus the fp32 state; MFMA: bf16 token blocks (4 per 64 tokens)
+    # generic: fp32 Q, K, V plus the fp32 state; MFMA: bf16 Q, K, V token blocks (4 per 64 tokens)
     assert L.workspace_size(cfg(algo="generic"), False) >= 3 * 2 * 64 * 64 * 4 + 2 * 2 * 64 * 256 * 4
-    assert L.workspace_size(cfg(algo="mfma"), False) >= 2 * 4 * 4 * 16 * 64 * 2
+    assert L.workspace_size(cfg(algo="mfma"), False) >= 2 * 4 * 3 * 16 * 64 * 2
     assert L.workspace_size(cfg(T=0), True) > 0
     bad = [dict(B=0), dict(T=-1), dict(H=0), dict(d=0), dict(b=0), dict(eta=-1.0), dict(eta=float("nan"))]
     for kw in bad:
