@@ -25,7 +25,7 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
-SCAN_SOURCES = ["generic.hip", "scan_mfma.hip"]
+SCAN_SOURCES = ["generic.hip", "scan_mfma.hip", "scan_coop.hip"]
 
 
 def scan_flops_per_token_head(d: int, m: int, b: int) -> int:

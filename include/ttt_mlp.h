@@ -80,6 +80,11 @@ extern "C" {
 #define TTT_ALGO_GENERIC 1 /* fp32 VALU scan, any supported shape */
 #define TTT_ALGO_MFMA 2    /* bf16-operand MFMA scan, fp32 state: bf16 io, erf GELU,
                               d = 64, m = 256, b = 16 */
+#define TTT_ALGO_COOP 3    /* per-token fp32 scan whose state (512 KB per head) is split
+                              over 8 cooperating workgroups: d = 128, m = 512, b = 1.
+                              Needs B*H*8 co-resident workgroups (cooperative launch);
+                              a workgroup that waits for its peers longer than about a
+                              second stops, and the outputs it had not written are NaN. */
 
 typedef struct ttt_mlp_config {
   int64_t B;        /* sequences, >= 1 */
@@ -112,9 +117,9 @@ const char* ttt_mlp_last_error(void);
 int32_t ttt_mlp_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t* bytes);
 
 /*
- * The scan kernel a call with this configuration runs: writes TTT_ALGO_GENERIC
- * or TTT_ALGO_MFMA to *algo (resolving TTT_ALGO_AUTO), or returns the error
- * the compute calls would return.
+ * The scan kernel a call with this configuration runs: writes TTT_ALGO_GENERIC,
+ * TTT_ALGO_MFMA or TTT_ALGO_COOP to *algo (resolving TTT_ALGO_AUTO), or returns
+ * the error the compute calls would return.
  */
 int32_t ttt_mlp_select_algo(const ttt_mlp_config* cfg, int32_t* algo);
 

@@ -17,7 +17,7 @@ TTT_OK, TTT_ERR_INVALID_ARG, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_HIP
 TTT_F32, TTT_BF16 = 0, 1
 TTT_LOSS_MEAN, TTT_LOSS_SUM = 0, 1
 TTT_GELU_ERF, TTT_GELU_TANH = 0, 1
-TTT_ALGO_AUTO, TTT_ALGO_GENERIC, TTT_ALGO_MFMA = 0, 1, 2
+TTT_ALGO_AUTO, TTT_ALGO_GENERIC, TTT_ALGO_MFMA, TTT_ALGO_COOP = 0, 1, 2, 3
 TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN = 0, 1
 
 EXPORTED = [
@@ -94,7 +94,8 @@ def make_config(B, T, H, d, m, b, eta, *, io_dtype="bf16", loss="mean", gelu="er
                   loss={"mean": TTT_LOSS_MEAN, "sum": TTT_LOSS_SUM}[loss],
                   gelu={"erf": TTT_GELU_ERF, "tanh": TTT_GELU_TANH}[gelu],
                   io_dtype={"f32": TTT_F32, "bf16": TTT_BF16}[io_dtype],
-                  algo={"auto": TTT_ALGO_AUTO, "generic": TTT_ALGO_GENERIC, "mfma": TTT_ALGO_MFMA}[algo])
+                  algo={"auto": TTT_ALGO_AUTO, "generic": TTT_ALGO_GENERIC, "mfma": TTT_ALGO_MFMA,
+                        "coop": TTT_ALGO_COOP}[algo])
 
 
 def workspace_size(cfg: Config, bidir: bool) -> int:
@@ -107,7 +108,7 @@ def select_algo(cfg: Config) -> str:
     """The scan kernel a call with cfg runs: "generic" or "mfma"."""
     a = _i32(0)
     _check(lib().ttt_mlp_select_algo(ctypes.byref(cfg), ctypes.byref(a)))
-    return {TTT_ALGO_GENERIC: "generic", TTT_ALGO_MFMA: "mfma"}[a.value]
+    return {TTT_ALGO_GENERIC: "generic", TTT_ALGO_MFMA: "mfma", TTT_ALGO_COOP: "coop"}[a.value]
 
 
 def _ptr(t):

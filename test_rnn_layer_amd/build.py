@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libttt_mlp.so")
-SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip"]
+SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_coop.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,10 +30,10 @@ FLAGS = [
 ]
 
 
-# kernels that must keep their whole working set in registers: the MFMA scan
-# holds the inner-model state in VGPRs for the whole sequence, and a spilling
-# build of it is refused.
-NO_SPILL_SOURCES = {"scan_mfma.hip"}
+# kernels that must keep their whole working set in registers: the MFMA and
+# cooperative scans hold the inner-model state in VGPRs for the whole
+# sequence, and a spilling build of either is refused.
+NO_SPILL_SOURCES = {"scan_mfma.hip", "scan_coop.hip"}
 
 
 def _check_no_spill(src, remarks):

@@ -103,9 +103,9 @@ constexpr size_t kGenericLdsMax = 64 * 1024;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  int algo;            // TTT_ALGO_GENERIC or TTT_ALGO_MFMA
+  int algo;            // TTT_ALGO_GENERIC, TTT_ALGO_MFMA or TTT_ALGO_COOP
   size_t qkv_off, qkv_bytes;
-  size_t wst_off, wst_bytes;
+  size_t wst_off, wst_bytes;  // generic: per-(sequence, head) state; coop: exchange slots + abort flag
   size_t total;
   size_t io_elem;      // bytes per X / Y element
 };
@@ -125,7 +125,8 @@ int32_t check_config(const ttt_mlp_config* c) {
     return fail(TTT_ERR_INVALID_ARG, "unknown gelu %d", c->gelu);
   if (c->io_dtype != TTT_F32 && c->io_dtype != TTT_BF16)
     return fail(TTT_ERR_INVALID_ARG, "unknown io_dtype %d", c->io_dtype);
-  if (c->algo != TTT_ALGO_AUTO && c->algo != TTT_ALGO_GENERIC && c->algo != TTT_ALGO_MFMA)
+  if (c->algo != TTT_ALGO_AUTO && c->algo != TTT_ALGO_GENERIC && c->algo != TTT_ALGO_MFMA &&
+      c->algo != TTT_ALGO_COOP)
     return fail(TTT_ERR_INVALID_ARG, "unknown algo %d", c->algo);
   const int64_t D = (int64_t)c->H * c->d;
   if (D > (1 << 20) || c->m > (1 << 16) || c->b > (1 << 16))
@@ -141,11 +142,17 @@ bool mfma_possible(const ttt_mlp_config* c) {
          ((int64_t)c->H * c->d) % 8 == 0;
 }
 
+bool coop_possible(const ttt_mlp_config* c) { return ttt::scan_coop_supported(c->d, c->m, c->b, c->T); }
+
 int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   int32_t st = check_config(c);
   if (st != TTT_OK) return st;
   int algo = c->algo;
-  if (algo == TTT_ALGO_AUTO) algo = mfma_possible(c) ? TTT_ALGO_MFMA : TTT_ALGO_GENERIC;
+  if (algo == TTT_ALGO_AUTO)
+    algo = mfma_possible(c) ? TTT_ALGO_MFMA : coop_possible(c) ? TTT_ALGO_COOP : TTT_ALGO_GENERIC;
+  if (algo == TTT_ALGO_COOP && !coop_possible(c))
+    return fail(TTT_ERR_UNSUPPORTED, "the cooperative scan needs d=128, m=512, b=1, T < 2^31 (got d=%d m=%d b=%d)",
+                c->d, c->m, c->b);
   if (algo == TTT_ALGO_MFMA && !mfma_possible(c))
     return fail(TTT_ERR_UNSUPPORTED,
                 "the MFMA scan needs bf16 io, erf GELU, d=64, m=256, b=16 (got d=%d m=%d b=%d io=%d gelu=%d)", c->d,
@@ -161,6 +168,9 @@ int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   if (algo == TTT_ALGO_MFMA) {
     p->qkv_bytes = align_up(ttt::scan_mfma_tile_bytes(c->B, c->T, c->H));
     p->wst_bytes = 0;
+  } else if (algo == TTT_ALGO_COOP) {
+    p->qkv_bytes = align_up(3 * BHTd * sizeof(float));
+    p->wst_bytes = align_up(ttt::scan_coop_xchg_bytes(c->B, c->H) + sizeof(uint32_t));
   } else {
     p->qkv_bytes = align_up(3 * BHTd * sizeof(float));
     p->wst_bytes = align_up((size_t)c->B * c->H * 2 * (size_t)c->d * c->m * sizeof(float));
@@ -230,6 +240,8 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
   sa.w1_0 = W1_0;
   sa.w2_0 = W2_0;
   sa.wstate = (float*)(ws + pl.wst_off);
+  sa.xchg = (uint64_t*)(ws + pl.wst_off);
+  sa.abort_flag = (uint32_t*)(ws + pl.wst_off + ttt::scan_coop_xchg_bytes(c->B, c->H));
   sa.w1_T = w1T;
   sa.w2_T = w2T;
   sa.B = c->B;
@@ -243,8 +255,14 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
   sa.gelu_tanh = c->gelu == TTT_GELU_TANH;
   sa.reverse = reverse;
   sa.bf16 = c->io_dtype == TTT_BF16;
-  e = timed_launch(TTT_KERNEL_SCAN, stream,
-                   [&] { return mfma ? ttt::launch_scan_mfma(sa, stream) : ttt::launch_scan_generic(sa, stream); });
+  if (pl.algo == TTT_ALGO_COOP && !ttt::scan_coop_fits(c->B, c->H))
+    return fail(TTT_ERR_UNSUPPORTED, "cooperative scan: %lld workgroups do not fit on this device at once",
+                (long long)(c->B * c->H * 8));
+  e = timed_launch(TTT_KERNEL_SCAN, stream, [&] {
+    if (mfma) return ttt::launch_scan_mfma(sa, stream);
+    if (pl.algo == TTT_ALGO_COOP) return ttt::launch_scan_coop(sa, stream);
+    return ttt::launch_scan_generic(sa, stream);
+  });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   return TTT_OK;
 }

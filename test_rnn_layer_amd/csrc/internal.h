@@ -36,6 +36,8 @@ struct ScanArgs {
   const float* w1_0;     // [H, d, m]
   const float* w2_0;     // [H, m, d]
   float* wstate;         // workspace, [B, H, d*m + m*d] fp32 (generic path)
+  uint64_t* xchg;        // cooperative path: exchange slots (see scan_coop)
+  uint32_t* abort_flag;  // cooperative path: raised by a workgroup that timed out
   float* w1_T;           // [B, H, d, m] or null
   float* w2_T;           // [B, H, m, d] or null
   int64_t B, T;
@@ -56,5 +58,12 @@ bool scan_mfma_supported(int d, int m, int b);
 size_t scan_mfma_tile_bytes(int64_t B, int64_t T, int H);
 int scan_mfma_block_elems();
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s);
+
+// Cooperative per-token scan (d = 128, m = 512, b = 1): each head's state is
+// split over 8 co-resident workgroups that exchange partial sums every token.
+bool scan_coop_supported(int d, int m, int b, int64_t T);
+bool scan_coop_fits(int64_t B, int H);  // co-residency on the current device
+size_t scan_coop_xchg_bytes(int64_t B, int H);
+hipError_t launch_scan_coop(const ScanArgs& a, hipStream_t s);
 
 }  // namespace ttt

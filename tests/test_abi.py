@@ -100,3 +100,13 @@ def test_algo_selection():
     with pytest.raises(L.TTTError) as e:
         L.select_algo(cfg(b=8, algo="mfma"))
     assert e.value.status == L.TTT_ERR_UNSUPPORTED
+    # the per-token large-state shape goes to the cooperative scan, in any io dtype and GELU form
+    big = dict(B=1, T=10, H=2, d=128, m=512, b=1, eta=0.05)
+    assert L.select_algo(L.make_config(**big)) == "coop"
+    assert L.select_algo(L.make_config(**big, io_dtype="f32", gelu="tanh")) == "coop"
+    assert L.select_algo(L.make_config(**big, algo="generic")) == "generic"
+    with pytest.raises(L.TTTError) as e:
+        L.select_algo(L.make_config(**dict(big, b=2), algo="coop"))
+    assert e.value.status == L.TTT_ERR_UNSUPPORTED
+    # coop workspace: fp32 Q, K, V plus the exchange slots (2 parities x 8 workgroups x 256 entries x 8 B per head)
+    assert L.workspace_size(L.make_config(**big), False) >= 3 * 2 * 10 * 128 * 4 + 2 * 2 * 8 * 256 * 8

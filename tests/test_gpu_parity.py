@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
 F32_TOL = 1e-4
-ALGOS = ["generic", "mfma"]
+ALGOS = ["generic", "mfma", "coop"]
 
 
 def _skip_unsupported(wl, algo):
@@ -94,6 +94,11 @@ SMALL = {
     "tiny_f32_b4_ragged": W.WORKLOADS["tiny_f32"].replace(T=103, b=4, name="tiny_f32_b4_ragged"),
     "h3_d64_b16_ragged": W.WORKLOADS["seg14k"].replace(T=200, H=3, name="h3_d64_b16_ragged"),
     "h2_d128_b1": W.WORKLOADS["bigstate307k"].replace(T=96, H=2, name="h2_d128_b1"),
+    "d128_b1_f32_tanh_sum": W.WORKLOADS["bigstate307k"].replace(T=33, H=1, io_dtype="f32", gelu="tanh", loss="sum",
+                                                                eta=0.05 / 128, name="d128_b1_f32_tanh_sum"),
+    "d128_b1_f32": W.WORKLOADS["bigstate307k"].replace(T=50, H=2, io_dtype="f32", name="d128_b1_f32"),
+    "d128_b1_two_sequences": W.WORKLOADS["bigstate307k"].replace(B=2, T=40, H=3, name="d128_b1_two_sequences"),
+    "d128_b1_one_token": W.WORKLOADS["bigstate307k"].replace(T=1, H=2, name="d128_b1_one_token"),
     "seg_shift_b16": W.WORKLOADS["bidir307k"].replace(T=512, H=2, seg_len=160, name="seg_shift_b16"),
     "sum_loss_tanh": W.WORKLOADS["seg14k"].replace(T=77, H=2, loss="sum", eta=0.1 / 16 / 64, gelu="tanh",
                                                    name="sum_loss_tanh"),
@@ -137,10 +142,14 @@ def test_bidir_matches_oracle(case, algo):
         _check(k, from_device(got[k]), ref[k], wl.io_dtype)
 
 
+# the shape each kernel's property tests run on
+PROP_CASE = {"generic": "h3_d64_b16_ragged", "mfma": "h3_d64_b16_ragged", "coop": "h2_d128_b1"}
+
+
 @pytest.mark.parametrize("algo", ALGOS)
 def test_empty_sequence_returns_initial_state(algo):
     from test_rnn_layer_amd import _lib
-    wl = SMALL["h3_d64_b16_ragged"].replace(T=0)
+    wl = SMALL[PROP_CASE[algo]].replace(T=0)
     print(f"[empty] T=0 algo={algo}", flush=True)
     inp = W.make_inputs(wl)
     dev = device_inputs(wl, inp)
@@ -159,7 +168,7 @@ def test_empty_sequence_returns_initial_state(algo):
 @pytest.mark.parametrize("algo", ALGOS)
 def test_properties_bitwise(algo):
     from test_rnn_layer_amd import _lib
-    wl = SMALL["h3_d64_b16_ragged"]
+    wl = SMALL[PROP_CASE[algo]]
     print(f"[properties] algo={algo}", flush=True)
     inp = W.make_inputs(wl)
     dev = device_inputs(wl, inp)
@@ -182,7 +191,7 @@ def test_properties_bitwise(algo):
     f2 = _gpu_forward(wl, dict(dev, X=a["Y"]), algo, reverse=True, alpha="alpha_b")
     assert torch.equal(bd["Y"], f2["Y"]) and torch.equal(bd["Z_f"], a["Z"]) and torch.equal(bd["Z_b"], f2["Z"])
     # state hand-off: continuing from W_T1 over the rest equals the whole run
-    T1 = 96
+    T1 = 96 if wl.T > 96 else wl.T // 2 + 1
     first = _lib.forward(_cfg(wl, algo, T=T1), dev["X"][:, :T1].contiguous(), dev["theta"], dev["W1_0"],
                          dev["W2_0"], dev["alpha_f"], want_z=True, want_state=True)
     rest = _lib.forward(_cfg(wl, algo, T=wl.T - T1), dev["X"][:, T1:].contiguous(), dev["theta"],
