@@ -63,7 +63,7 @@ hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s);
 // split over 8 co-resident workgroups that exchange partial sums every token.
 bool scan_coop_supported(int d, int m, int b, int64_t T);
 bool scan_coop_fits(int64_t B, int H);  // co-residency on the current device
-size_t scan_coop_xchg_bytes(int64_t B, int H);
+size_t scan_coop_xchg_bytes(int64_t B, int H);  // exchange slots
 hipError_t launch_scan_coop(const ScanArgs& a, hipStream_t s);
 
 }  // namespace ttt

@@ -81,10 +81,14 @@ __device__ __forceinline__ void gelu_both(float a, bool tanh_form, float* g, flo
   *dg = cdf + a * 0.3989422804014327f * expf(-0.5f * a * a);
 }
 
-__device__ __forceinline__ float ld_io(const void* p, int64_t i, bool bf16) {
-  if (bf16) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
-  return ((const float*)p)[i];
+// Raw bits of an io element; converted where used, so that the load's latency
+// is not waited for at the load.
+__device__ __forceinline__ uint32_t ld_io_bits(const void* p, int64_t i, bool bf16) {
+  if (bf16) return (uint32_t)((const uint16_t*)p)[i];
+  return ((const uint32_t*)p)[i];
 }
+
+__device__ __forceinline__ float io_bits_to_f32(uint32_t b, bool bf16) { return __uint_as_float(bf16 ? b << 16 : b); }
 
 __device__ __forceinline__ void st_io(void* p, int64_t i, float v, bool bf16) {
   if (bf16)
@@ -93,26 +97,30 @@ __device__ __forceinline__ void st_io(void* p, int64_t i, float v, bool bf16) {
     ((float*)p)[i] = v;
 }
 
-__device__ __forceinline__ void publish(uint64_t* e, uint32_t tag, float v) {
+// Exchange transport: relaxed device-scope atomic stores and loads, whose
+// coherence between workgroups the memory model guarantees wherever they run.
+// (On gfx950 workgroup-scope loads can be served from a stale L1 line even after
+// a workgroup-scope invalidate, and workgroup-scope atomics read L2 correctly but
+// are slower per poll.)
+__device__ __forceinline__ void put(uint64_t* e, uint32_t tag, float v) {
   __hip_atomic_store(e, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Sum over the NCU workgroups of entry `idx` of token `tag` (fixed order, so
-// every workgroup gets the same bits).  Returns false on abort or time-out.
-__device__ bool gather(const uint64_t* slot, int idx, uint32_t tag, uint32_t* abort_flag, float* out) {
-  float v[NCU];
-  uint32_t have = 0;
+// Polls the n (0..4) entries e_idx[0..n) of token `tag` until all carry the tag
+// and returns their values in out[].  A poll issues all its loads before it looks
+// at any of them, so it costs one round trip.  Returns false on abort or time-out.
+__device__ bool poll(const uint64_t* base, int n, const int64_t* e_idx, uint32_t tag, uint32_t* abort_flag,
+                     float* out) {
+  if (n == 0) return true;
+  uint64_t e[4];
   for (uint32_t spin = 0;; ++spin) {
 #pragma unroll
-    for (int q = 0; q < NCU; ++q) {
-      if (have & (1u << q)) continue;
-      const uint64_t e = __hip_atomic_load(slot + q * NVAL + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((uint32_t)(e >> 32) == tag) {
-        v[q] = __uint_as_float((uint32_t)e);
-        have |= 1u << q;
-      }
-    }
-    if (have == (1u << NCU) - 1) break;
+    for (int i = 0; i < 4; ++i)
+      e[i] = __hip_atomic_load(base + e_idx[i < n ? i : 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) all = all && (uint32_t)(e[i] >> 32) == tag;
+    if (all) break;
     if (spin >= SPIN_MAX) {
       __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
@@ -120,10 +128,9 @@ __device__ bool gather(const uint64_t* slot, int idx, uint32_t tag, uint32_t* ab
     if ((spin & 15) == 15 && __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
     __builtin_amdgcn_s_sleep(1);
   }
-  float acc = 0.0f;
 #pragma unroll
-  for (int q = 0; q < NCU; ++q) acc += v[q];
-  *out = acc;
+  for (int i = 0; i < 4; ++i)
+    if (i < n) out[i] = __uint_as_float((uint32_t)e[i]);
   return true;
 }
 
@@ -136,12 +143,22 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   __shared__ float Apart[2][NW][64];  // per-wave partials of a (k W1) and aq (q W1), by unit
   __shared__ float Ypart[NW][4][64];  // per-wave partials of yhat (j = l, l + 64) and z (same)
   __shared__ float GH[UNITS];         // G2 W2^T, by unit
+  __shared__ __attribute__((aligned(16))) float Ks[3][CD];  // k_t, k_{t+1}, k_{t+2} (by token mod 3)
+  __shared__ __attribute__((aligned(16))) float Qs[2][CD];  // q_t, q_{t+1} (by token mod 2)
+  __shared__ float Xv[NCU][CD];       // gathered yhat partials, by workgroup and feature
+  __shared__ float Zv[NCU][16];       // gathered z partials of this workgroup's 16 channels
+
+  // Workgroup -> (sequence-head bh, slice cu).  The NCU slices of a head get
+  // workgroup indices that are equal modulo 8, i.e. the same XCD under the
+  // round-robin dispatch of workgroups to XCDs (they then share L2 for the
+  // head's q, k, v); indices past B*H are idle.
+  const int64_t BH = a.B * a.H;
+  const int cu = (int)((blockIdx.x / 8) % NCU);
+  const int64_t bh = (int64_t)(blockIdx.x / (8 * NCU)) * 8 + blockIdx.x % 8;
+  if (bh >= BH) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t BH = a.B * a.H;
-  const int64_t bh = blockIdx.x % BH;
-  const int cu = (int)(blockIdx.x / BH);
   const int64_t s = bh / a.H;
   const int h = (int)(bh % a.H);
   const int64_t T = a.T;
@@ -149,6 +166,20 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   const int u0 = UNITS * cu;
   const bool bf16 = a.bf16;
   const float neta = -a.eta, gs = a.gscale;
+  const bool writer = (w == 0) && lane < 16;  // writes channels h*d + 16*cu + lane
+  const int ch = h * CD + 16 * cu + (lane & 15);
+  auto tok = [&](int64_t t) -> int64_t { return a.reverse ? T - 1 - t : t; };
+  auto fill_nan = [&](int64_t t_from) {  // after an abort: the rest of this workgroup's outputs
+    if (!writer) return;
+    for (int64_t t = t_from; t < T; ++t) {
+      const int64_t o = ((int64_t)s * T + tok(t)) * D + ch;
+      st_io(a.y, o, __builtin_nanf(""), bf16);
+      if (a.z) a.z[o] = __builtin_nanf("");
+    }
+  };
+
+  bool failed = false;  // this thread saw an abort or a time-out
+  const int64_t xslots = bh * 2 * NCU * NVAL;  // first entry of this head's slots
 
   // ---- state slices
   float W1r[PW];
@@ -169,58 +200,41 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   const float* qb = a.qkv + bh * T * CD;
   const float* kb = qb + plane;
   const float* vb = qb + 2 * plane;
-  auto tok = [&](int64_t t) -> int64_t { return a.reverse ? T - 1 - t : t; };
-  uint64_t* xslots = a.xchg + bh * 2 * NCU * NVAL;
-  // outputs of this workgroup: channels h*d + 16*cu + lane of wave 0, lanes 0..15
-  const bool writer = (w == 0) && lane < 16;
-  const int ch = h * CD + 16 * cu + (lane & 15);
   const float tg = tanhf(a.alpha[ch]);
 
-  auto fill_nan = [&](int64_t t_from) {  // after an abort: the rest of this workgroup's outputs
-    if (!writer) return;
-    for (int64_t t = t_from; t < T; ++t) {
-      const int64_t o = ((int64_t)s * T + tok(t)) * D + ch;
-      st_io(a.y, o, __builtin_nanf(""), bf16);
-      if (a.z) a.z[o] = __builtin_nanf("");
-    }
-  };
-
-  bool failed = false;  // this thread saw an abort or a time-out
   if (T > 0) {
-    // ---- prologue: a of token 0
+    // ---- prologue: k_0, k_1, q_0 into LDS, then the partial a of token 0
+    if (tid < CD) {
+      Ks[0][tid] = kb[tok(0) * CD + tid];
+      Qs[0][tid] = qb[tok(0) * CD + tid];
+    } else if (T > 1) {
+      Ks[1][tid - CD] = kb[tok(1) * CD + tid - CD];
+    }
+    __syncthreads();
     {
-      const float* k0 = kb + tok(0) * CD + PW * w;
       float acc = 0.0f;
 #pragma unroll
-      for (int k = 0; k < PW; ++k) acc = fmaf(k0[k], W1r[k], acc);
+      for (int k = 0; k < PW; ++k) acc = fmaf(Ks[0][PW * w + k], W1r[k], acc);
       Apart[0][w][lane] = acc;
       Apart[1][w][lane] = 0.0f;
     }
-    float kc[PW];  // k_t of this wave's rows
-#pragma unroll
-    for (int k = 0; k < PW; ++k) kc[k] = kb[tok(0) * CD + PW * w + k];
 
     for (int64_t t = 0; t <= T; ++t) {
       const bool live = t < T;
-      // loads for this iteration, used after the exchange
-      float kn[PW], qc[PW];
-      float v0 = 0.0f, v1 = 0.0f, xo = 0.0f;
+      // operands loaded now and used later in the iteration: v_t, the gate
+      // input of token t-1, and (staged into LDS at the end) k_{t+2}, q_{t+1}
+      float v0 = 0.0f, v1 = 0.0f, stage = 0.0f;
+      uint32_t xo = 0;
       if (live) {
-        const float* qrow = qb + tok(t) * CD + PW * w;
-#pragma unroll
-        for (int k = 0; k < PW; ++k) qc[k] = qrow[k];
-        if (t + 1 < T) {
-          const float* krow = kb + tok(t + 1) * CD + PW * w;
-#pragma unroll
-          for (int k = 0; k < PW; ++k) kn[k] = krow[k];
-        } else {
-#pragma unroll
-          for (int k = 0; k < PW; ++k) kn[k] = 0.0f;
-        }
         v0 = vb[tok(t) * CD + lane];
         v1 = vb[tok(t) * CD + lane + 64];
+        // one unconditional load per thread (token clamped into range; only
+        // valid values are written to LDS): divergent loads into one register
+        // would make the second wait for the first
+        const int64_t tk = t + 2 < T ? t + 2 : T - 1, tq = t + 1 < T ? t + 1 : T - 1;
+        stage = tid < CD ? kb[tok(tk) * CD + tid] : qb[tok(tq) * CD + tid - CD];
       }
-      if (writer && t > 0) xo = ld_io(a.xin, ((int64_t)s * T + tok(t - 1)) * D + ch, bf16);
+      if (writer && t > 0) xo = ld_io_bits(a.xin, ((int64_t)s * T + tok(t - 1)) * D + ch, bf16);
 
       __syncthreads();  // Apart of this iteration is complete
       // ---- unit u = lane: GELU of a_t and of aq_{t-1}
@@ -254,35 +268,70 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         Ypart[w][3][lane] = z1;
       }
       __syncthreads();
+      // ---- stage k_{t+2}, q_{t+1} (loaded at the top of this iteration); their
+      //      buffers held k_{t-1}, q_{t-1}, last read in the previous iteration
+      if (live) {
+        if (tid < CD) {
+          if (t + 2 < T) Ks[(t + 2) % 3][tid] = stage;
+        } else if (t + 1 < T) {
+          Qs[(t + 1) & 1][tid - CD] = stage;
+        }
+      }
       // ---- publish this workgroup's partial of value 64 w + lane (w < 2: yhat, else z)
-      uint64_t* slot = xslots + (t & 1) * NCU * NVAL;
+      const int64_t slot = xslots + (t & 1) * NCU * NVAL;
       {
         float p = 0.0f;
 #pragma unroll
         for (int q = 0; q < NW; ++q) p += Ypart[q][w][lane];
-        publish(slot + cu * NVAL + 64 * w + lane, (uint32_t)t, p);
+        put(a.xchg + slot + cu * NVAL + 64 * w + lane, (uint32_t)t, p);
       }
-      // ---- gather: yhat_t for j = lane, lane + 64; z_{t-1} for this workgroup's 16 channels
-      bool ok = !failed;
-      float yh0 = 0.0f, yh1 = 0.0f;
+      // ---- gather, spread over the workgroup: thread tid fetches yhat feature
+      //      tid mod 128 from workgroups 4 (tid / 128) .. +3, and (tid < 128) the z
+      //      partial of channel tid mod 16 from workgroup tid / 16; the sums follow
+      //      through LDS in a fixed order
+      {
+        int64_t e_idx[4];
+        float vals[4];
+        int n = 0;
+        if (live) {
+          for (int i = 0; i < 4; ++i) e_idx[i] = slot + (4 * (tid >> 7) + i) * NVAL + (tid & 127);
+          n = 4;
+        }
+        bool ok = !failed && poll(a.xchg, n, e_idx, (uint32_t)t, a.abort_flag, vals);
+        if (ok && live)
+          for (int i = 0; i < 4; ++i) Xv[4 * (tid >> 7) + i][tid & 127] = vals[i];
+        if (ok && t > 0 && tid < 16 * NCU) {
+          const int64_t ze = slot + (tid >> 4) * NVAL + CD + 16 * cu + (tid & 15);
+          float zv;
+          ok = poll(a.xchg, 1, &ze, (uint32_t)t, a.abort_flag, &zv);
+          if (ok) Zv[tid >> 4][tid & 15] = zv;
+        }
+        failed = !ok;
+      }
+      if (__syncthreads_or(failed)) {  // every thread of the workgroup leaves together
+        fill_nan(t > 0 ? t - 1 : 0);
+        return;
+      }
+      float got[2] = {0.0f, 0.0f};
       if (live) {
-        ok = gather(slot, lane, (uint32_t)t, a.abort_flag, &yh0);
-        ok = ok && gather(slot, lane + 64, (uint32_t)t, a.abort_flag, &yh1);
-      }
-      if (ok && writer && t > 0) {
-        float zv;
-        ok = gather(slot, CD + 16 * cu + lane, (uint32_t)t, a.abort_flag, &zv);
-        if (ok) {
-          const int64_t o = ((int64_t)s * T + tok(t - 1)) * D + ch;
-          st_io(a.y, o, fmaf(tg, zv, xo), bf16);
-          if (a.z) a.z[o] = zv;
+#pragma unroll
+        for (int q = 0; q < NCU; ++q) {
+          got[0] += Xv[q][lane];
+          got[1] += Xv[q][lane + 64];
         }
       }
-      failed = !ok;
+      if (writer && t > 0) {
+        float zv = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NCU; ++q) zv += Zv[q][lane];
+        const int64_t o = ((int64_t)s * T + tok(t - 1)) * D + ch;
+        st_io(a.y, o, fmaf(tg, zv, io_bits_to_f32(xo, bf16)), bf16);
+        if (a.z) a.z[o] = zv;
+      }
       if (!live) break;
 
       // ---- G2 for j = lane, lane + 64; second W2 pass: G2 W2^T partials and the W2 update
-      const float g20 = gs * (yh0 - v0), g21 = gs * (yh1 - v1);
+      const float g20 = gs * (got[0] - v0), g21 = gs * (got[1] - v1);
       float gp[UW];
 #pragma unroll
       for (int i = 0; i < UW; ++i) {
@@ -326,18 +375,27 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       }
       // ---- W1 pass: update with k_t and G1 of unit lane, then a_{t+1} = k_{t+1} W1_t, aq_t = q_t W1_t
       {
+        // (at t = T-1 the k_{t+1} buffer is stale; that a is never used)
+        const float4* kc = (const float4*)(Ks[t % 3] + PW * w);
+        const float4* kn = (const float4*)(Ks[(t + 1) % 3] + PW * w);
+        const float4* qc = (const float4*)(Qs[t & 1] + PW * w);
         const float ng1 = neta * GH[lane] * dg;
         float an = 0.0f, aq = 0.0f;
 #pragma unroll
-        for (int k = 0; k < PW; ++k) {
-          W1r[k] = fmaf(ng1, kc[k], W1r[k]);
-          an = fmaf(kn[k], W1r[k], an);
-          aq = fmaf(qc[k], W1r[k], aq);
+        for (int k4 = 0; k4 < PW / 4; ++k4) {
+          const float4 kv = kc[k4], nv = kn[k4], qv = qc[k4];
+          const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, nn[4] = {nv.x, nv.y, nv.z, nv.w},
+                      qq[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k = 4 * k4 + e;
+            W1r[k] = fmaf(ng1, kk[e], W1r[k]);
+            an = fmaf(nn[e], W1r[k], an);
+            aq = fmaf(qq[e], W1r[k], aq);
+          }
         }
         Apart[0][w][lane] = an;
         Apart[1][w][lane] = aq;
-#pragma unroll
-        for (int k = 0; k < PW; ++k) kc[k] = kn[k];
       }
     }
     if (__syncthreads_or(failed)) {
@@ -369,6 +427,8 @@ __global__ void coop_clear_kernel(uint64_t* x, int64_t n, uint32_t* abort_flag) 
   if (i == 0) *abort_flag = 0u;
 }
 
+int64_t coop_grid(int64_t B, int H) { return 8 * NCU * ((B * H + 7) / 8); }
+
 }  // namespace
 
 bool scan_coop_supported(int d, int m, int b, int64_t T) {
@@ -386,7 +446,7 @@ bool scan_coop_fits(int64_t B, int H) {
   int per_cu_t = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_t, scan_coop_kernel<true>, NT, 0) != hipSuccess) return false;
   const int64_t fit = (int64_t)cus * (per_cu < per_cu_t ? per_cu : per_cu_t);
-  return B * H * NCU <= fit;
+  return coop_grid(B, H) <= fit;
 }
 
 hipError_t launch_scan_coop(const ScanArgs& a, hipStream_t s) {
@@ -396,7 +456,7 @@ hipError_t launch_scan_coop(const ScanArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   ScanArgs args = a;
   void* kargs[] = {(void*)&args};
-  const dim3 grid((unsigned)(a.B * a.H * NCU)), block(NT);
+  const dim3 grid((unsigned)coop_grid(a.B, a.H)), block(NT);
   if (a.gelu_tanh) return hipLaunchCooperativeKernel((const void*)scan_coop_kernel<true>, grid, block, kargs, 0, s);
   return hipLaunchCooperativeKernel((const void*)scan_coop_kernel<false>, grid, block, kargs, 0, s);
 }
