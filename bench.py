@@ -10,7 +10,6 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -25,7 +24,6 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
-SCAN_SOURCES = ["generic.hip", "scan_mfma.hip", "scan_coop.hip"]
 
 
 def scan_flops_per_token_head(d: int, m: int, b: int) -> int:
@@ -40,13 +38,9 @@ def proj_flops_per_token(D: int) -> int:
     return 2 * 3 * D * D
 
 
-def source_digest(names) -> str:
-    h = hashlib.sha256()
-    for n in names:
-        p = os.path.join(ROOT, "test_rnn_layer_amd", "csrc", n)
-        if os.path.exists(p):
-            h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
+def kernel_digest(kernel: str) -> str:
+    from test_rnn_layer_amd.profile_counters import KERNEL_SOURCES, source_digest
+    return source_digest(KERNEL_SOURCES[kernel])
 
 
 def traffic_from_profile(kernel: str, digest: str):
@@ -150,10 +144,11 @@ def main():
     scan_flops_launch = scan_flops_per_token_head(wl.d, wl.m, wl.b) * wl.H * tokens * dirs * args.steps / scan_n
     scan_avg_ms = scan_ms / scan_n
     achieved = scan_flops_launch / (scan_avg_ms / 1e3) / 1e12
-    used_mfma = _lib.select_algo(cfg) == "mfma"
+    algo = _lib.select_algo(cfg)
+    used_mfma = algo == "mfma"
     peak = PEAK_BF16_TFLOPS if used_mfma else PEAK_FP32_TFLOPS
-    kname = "scan_mfma" if used_mfma else "scan_generic"
-    traffic = traffic_from_profile(kname, source_digest(SCAN_SOURCES))
+    kname = "scan_" + algo
+    traffic = traffic_from_profile(kname, kernel_digest(kname))
     # layer roofline: projections at bf16 MFMA peak plus the scan at fp32 peak
     proj_total = proj_flops_per_token(wl.D) * tokens * dirs
     scan_total = scan_flops_per_token_head(wl.d, wl.m, wl.b) * wl.H * tokens * dirs
