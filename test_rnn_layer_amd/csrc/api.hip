@@ -3,9 +3,11 @@
 // include/ttt_mlp.h.
 #include "../../include/ttt_mlp.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -167,7 +169,8 @@ int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   p->qkv_off = 0;
   if (algo == TTT_ALGO_MFMA) {
     p->qkv_bytes = align_up(ttt::scan_mfma_tile_bytes(c->B, c->T, c->H));
-    p->wst_bytes = 0;
+    // the state handed from one chunk of the scan to the next (W1 then W2)
+    p->wst_bytes = align_up((size_t)c->B * c->H * 2 * (size_t)c->d * c->m * sizeof(float));
   } else if (algo == TTT_ALGO_COOP) {
     p->qkv_bytes = align_up(3 * BHTd * sizeof(float));
     p->wst_bytes = align_up(ttt::scan_coop_xchg_bytes(c->B, c->H) + sizeof(uint32_t));
@@ -211,10 +214,8 @@ int32_t check_no_overlap(const Buf* outs, int nout, const Buf* ins, int nin) {
   return TTT_OK;
 }
 
-// One direction: projection of xin, then the scan writing y (and z, W_T).
-int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, const void* theta,
-                      const float* W1_0, const float* W2_0, const float* alpha, int reverse, void* y,
-                      float* z, float* w1T, float* w2T, char* ws, hipStream_t stream) {
+ttt::ProjArgs proj_args(const ttt_mlp_config* c, const Plan& pl, const void* xin, const void* theta, int reverse,
+                        char* ws) {
   ttt::ProjArgs pa{};
   pa.X = xin;
   pa.theta = theta;
@@ -226,10 +227,14 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
   pa.bf16 = c->io_dtype == TTT_BF16;
   pa.reverse = reverse;
   pa.blk_elems = ttt::scan_mfma_block_elems();
-  const bool mfma = pl.algo == TTT_ALGO_MFMA;
-  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, stream, [&] { return launch_projection(pa, mfma ? 1 : 0, stream); });
-  if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+  pa.tt0 = 0;
+  pa.tt1 = c->T;
+  return pa;
+}
 
+ttt::ScanArgs scan_args(const ttt_mlp_config* c, const Plan& pl, const void* xin, const float* W1_0,
+                        const float* W2_0, const float* alpha, int reverse, void* y, float* z, float* w1T, float* w2T,
+                        char* ws) {
   ttt::ScanArgs sa{};
   sa.qkv = (const float*)(ws + pl.qkv_off);
   sa.qkv_tiles = ws + pl.qkv_off;
@@ -239,6 +244,7 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
   sa.alpha = alpha;
   sa.w1_0 = W1_0;
   sa.w2_0 = W2_0;
+  sa.w_seq_stride = 0;
   sa.wstate = (float*)(ws + pl.wst_off);
   sa.xchg = (uint64_t*)(ws + pl.wst_off);
   sa.abort_flag = (uint32_t*)(ws + pl.wst_off + ttt::scan_coop_xchg_bytes(c->B, c->H));
@@ -246,6 +252,8 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
   sa.w2_T = w2T;
   sa.B = c->B;
   sa.T = c->T;
+  sa.p0 = 0;
+  sa.Tc = c->T;
   sa.H = c->H;
   sa.d = c->d;
   sa.m = c->m;
@@ -255,15 +263,157 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
   sa.gelu_tanh = c->gelu == TTT_GELU_TANH;
   sa.reverse = reverse;
   sa.bf16 = c->io_dtype == TTT_BF16;
+  return sa;
+}
+
+// One direction on the generic or cooperative path: projection of xin, then
+// the scan writing y (and z, W_T).
+int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, const void* theta,
+                      const float* W1_0, const float* W2_0, const float* alpha, int reverse, void* y,
+                      float* z, float* w1T, float* w2T, char* ws, hipStream_t stream) {
+  const ttt::ProjArgs pa = proj_args(c, pl, xin, theta, reverse, ws);
+  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, stream, [&] { return launch_projection(pa, 0, stream); });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+  const ttt::ScanArgs sa = scan_args(c, pl, xin, W1_0, W2_0, alpha, reverse, y, z, w1T, w2T, ws);
   if (pl.algo == TTT_ALGO_COOP && !ttt::scan_coop_fits(c->B, c->H))
     return fail(TTT_ERR_UNSUPPORTED, "cooperative scan: %lld workgroups do not fit on this device at once",
                 (long long)(c->B * c->H * 8));
   e = timed_launch(TTT_KERNEL_SCAN, stream, [&] {
-    if (mfma) return ttt::launch_scan_mfma(sa, stream);
     if (pl.algo == TTT_ALGO_COOP) return ttt::launch_scan_coop(sa, stream);
     return ttt::launch_scan_generic(sa, stream);
   });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+  return TTT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path: chunked scans overlapped with the projections
+// ---------------------------------------------------------------------------
+// The MFMA scan uses one CU per (sequence, head); the projection GEMM of the
+// next chunk of tokens runs on the remaining CUs at the same time.  Each
+// direction is cut into chunks of whole 16-token blocks; the projection of
+// chunk k runs on a side stream, the scan of chunk k on the caller's stream
+// after it, starting from the state the scan of chunk k-1 left in the
+// workspace.  In a bidirectional call the projection of a reverse chunk waits
+// for the forward scan chunks that wrote its tokens of X' (and read its part of
+// the token-block buffer).  Only the first chunk's projection of each
+// direction is exposed.
+
+struct Side {
+  hipStream_t stream = nullptr;
+  std::vector<hipEvent_t> events;
+};
+std::mutex g_side_mu;  // held while a call enqueues: events are reused between calls
+std::map<int, Side> g_side;
+
+hipError_t side_for_device(Side** out, size_t n_events) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  Side& sd = g_side[dev];
+  if (!sd.stream) {
+    e = hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking);  // default priority
+    if (e != hipSuccess) return e;
+  }
+  while (sd.events.size() < n_events) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    sd.events.push_back(ev);
+  }
+  *out = &sd;
+  return hipSuccess;
+}
+
+struct Chunking {
+  int64_t size, count;  // tokens per chunk (a multiple of 256), chunks (>= 1)
+};
+
+Chunking chunking(int64_t T) {
+  constexpr int64_t kMaxChunks = 16, kRows = 256;
+  int64_t size = (T + kMaxChunks - 1) / kMaxChunks;
+  size = std::max<int64_t>(kRows, (size + kRows - 1) / kRows * kRows);
+  return {size, std::max<int64_t>(1, (T + size - 1) / size)};
+}
+
+struct Direction {
+  const void* xin;
+  const float* alpha;
+  int reverse;
+  void* y;
+  float* z;
+  float* w1T;
+  float* w2T;
+};
+
+int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs, int ndir, const void* theta,
+                 const float* W1_0, const float* W2_0, char* ws, hipStream_t S) {
+  const int64_t T = c->T;
+  const Chunking ch = chunking(T);
+  const int64_t C = ch.count;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side* sd = nullptr;
+  // events: start, then per direction C projection + C scan events, then end
+  hipError_t e = side_for_device(&sd, 2 + 2 * (size_t)C * ndir);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+  hipStream_t S2 = sd->stream;
+  hipEvent_t* ev = sd->events.data();
+  hipEvent_t ev_start = ev[0], ev_end = ev[1];
+  auto ev_proj = [&](int d, int64_t k) { return ev[2 + (2 * d) * C + k]; };
+  auto ev_scan = [&](int d, int64_t k) { return ev[2 + (2 * d + 1) * C + k]; };
+  float* st1 = (float*)(ws + pl.wst_off);  // chunk-to-chunk state, [B, H, d, m] then [B, H, m, d]
+  float* st2 = st1 + (size_t)c->B * c->H * c->d * c->m;
+  const int64_t st_stride = (int64_t)c->H * c->d * c->m;
+
+#define TTT_TRY(x, what)                                                              \
+  do {                                                                                \
+    hipError_t err_ = (x);                                                            \
+    if (err_ != hipSuccess) return fail(TTT_ERR_HIP, "%s: %s", what, hipGetErrorString(err_)); \
+  } while (0)
+
+  TTT_TRY(hipEventRecord(ev_start, S), "event record");
+  TTT_TRY(hipStreamWaitEvent(S2, ev_start, 0), "stream wait");
+  for (int d = 0; d < ndir; ++d) {
+    const Direction& D = dirs[d];
+    // projections of this direction's chunks, on the side stream
+    for (int64_t k = 0; k < C; ++k) {
+      const int64_t p0 = k * ch.size, p1 = std::min(T, p0 + ch.size);
+      if (d > 0) {
+        // X' tokens of this chunk come from forward positions [T-p1, T-p0), and the
+        // chunk's token blocks were last read by the forward scan of positions [p0, p1)
+        const int64_t need = std::max(p1 > p0 ? (T - p0 - 1) / ch.size : 0, p1 > p0 ? (p1 - 1) / ch.size : 0);
+        TTT_TRY(hipStreamWaitEvent(S2, ev_scan(d - 1, std::min(need, C - 1)), 0), "stream wait");
+      }
+      ttt::ProjArgs pa = proj_args(c, pl, D.xin, theta, D.reverse, ws);
+      pa.tt0 = D.reverse ? T - p1 : p0;
+      pa.tt1 = D.reverse ? T - p0 : p1;
+      TTT_TRY(timed_launch(TTT_KERNEL_PROJECT, S2, [&] { return ttt::launch_project_mfma(pa, 1, S2); }),
+              "projection launch");
+      TTT_TRY(hipEventRecord(ev_proj(d, k), S2), "event record");
+    }
+    // the scan, chunk by chunk on the caller's stream
+    for (int64_t k = 0; k < C; ++k) {
+      const int64_t p0 = k * ch.size, p1 = std::min(T, p0 + ch.size);
+      TTT_TRY(hipStreamWaitEvent(S, ev_proj(d, k), 0), "stream wait");
+      ttt::ScanArgs sa = scan_args(c, pl, D.xin, W1_0, W2_0, D.alpha, D.reverse, D.y, D.z, D.w1T, D.w2T, ws);
+      sa.p0 = p0;
+      sa.Tc = p1 - p0;
+      if (k > 0) {
+        sa.w1_0 = st1;
+        sa.w2_0 = st2;
+        sa.w_seq_stride = st_stride;
+      }
+      if (k < C - 1) {
+        sa.w1_T = st1;
+        sa.w2_T = st2;
+      }
+      TTT_TRY(timed_launch(TTT_KERNEL_SCAN, S, [&] { return ttt::launch_scan_mfma(sa, S); }), "scan launch");
+      TTT_TRY(hipEventRecord(ev_scan(d, k), S), "event record");
+    }
+  }
+  TTT_TRY(hipEventRecord(ev_end, S2), "event record");
+  TTT_TRY(hipStreamWaitEvent(S, ev_end, 0), "stream wait");
+#undef TTT_TRY
   return TTT_OK;
 }
 
@@ -328,8 +478,13 @@ int32_t ttt_mlp_forward(const ttt_mlp_config* cfg, const void* X, const void* th
                      {W2_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W2_0"}, {alpha, D * 4, "alpha"}};
   st = check_no_overlap(outs, 5, ins, 5);
   if (st != TTT_OK) return st;
-  st = run_direction(cfg, pl, X, theta_qkv, W1_0, W2_0, alpha, reverse, Y, Z, W1_T, W2_T, (char*)workspace,
-                     (hipStream_t)stream);
+  if (pl.algo == TTT_ALGO_MFMA) {
+    const Direction dir{X, alpha, reverse, Y, Z, W1_T, W2_T};
+    st = run_mfma(cfg, pl, &dir, 1, theta_qkv, W1_0, W2_0, (char*)workspace, (hipStream_t)stream);
+  } else {
+    st = run_direction(cfg, pl, X, theta_qkv, W1_0, W2_0, alpha, reverse, Y, Z, W1_T, W2_T, (char*)workspace,
+                       (hipStream_t)stream);
+  }
   return st == TTT_OK ? ok() : st;
 }
 
@@ -361,6 +516,12 @@ int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* thet
   st = check_no_overlap(outs, 8, ins, 6);
   if (st != TTT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (pl.algo == TTT_ALGO_MFMA) {
+    // forward pass into Y, then the reversed pass over X' = Y, written back in place
+    const Direction dirs[2] = {{X, alpha_f, 0, Y, Z_f, W1_Tf, W2_Tf}, {Y, alpha_b, 1, Y, Z_b, W1_Tb, W2_Tb}};
+    st = run_mfma(cfg, pl, dirs, 2, theta_qkv, W1_0, W2_0, (char*)workspace, s);
+    return st == TTT_OK ? ok() : st;
+  }
   // forward pass: X' lands in Y
   st = run_direction(cfg, pl, X, theta_qkv, W1_0, W2_0, alpha_f, 0, Y, Z_f, W1_Tf, W2_Tf, (char*)workspace, s);
   if (st != TTT_OK) return st;
@@ -391,6 +552,8 @@ int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* th
   pa.d = cfg->d;
   pa.bf16 = cfg->io_dtype == TTT_BF16;
   pa.reverse = 0;
+  pa.tt0 = 0;
+  pa.tt1 = cfg->T;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = timed_launch(TTT_KERNEL_PROJECT, s, [&] { return launch_projection(pa, 0, s); });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));

@@ -16,6 +16,7 @@ struct ProjArgs {
   int32_t bf16;       // 1: X and theta are bf16, 0: fp32
   int32_t reverse;    // token-block layout only: blocks follow the reversed sequence
   int32_t blk_elems;  // token-block layout only: bf16 elements per 16-token block
+  int64_t tt0, tt1;   // token-block GEMM only: tokens [tt0, tt1) of every sequence (others: 0, T)
 };
 
 // fp32 output, [3, B, H, T, d] (VALU kernel, any dtype and shape).
@@ -33,14 +34,16 @@ struct ScanArgs {
   void* y;               // [B, T, D] io dtype: gated output (may equal xin)
   float* z;              // [B, T, D] fp32 or null
   const float* alpha;    // [D]
-  const float* w1_0;     // [H, d, m]
-  const float* w2_0;     // [H, m, d]
+  const float* w1_0;     // [H, d, m], or per sequence (see w_seq_stride)
+  const float* w2_0;     // [H, m, d], or per sequence
+  int64_t w_seq_stride;  // elements between sequences' initial states (0: shared by all)
   float* wstate;         // workspace, [B, H, d*m + m*d] fp32 (generic path)
   uint64_t* xchg;        // cooperative path: exchange slots (see scan_coop)
   uint32_t* abort_flag;  // cooperative path: raised by a workgroup that timed out
   float* w1_T;           // [B, H, d, m] or null
   float* w2_T;           // [B, H, m, d] or null
   int64_t B, T;
+  int64_t p0, Tc;        // this launch covers scan positions [p0, p0 + Tc) (MFMA scan; others: 0, T)
   int32_t H, d, m, b;
   float eta;
   float gscale;          // 2/d (mean) or 2 (sum)

@@ -148,7 +148,8 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T_STAGE];
   const int d = a.d;
   const int D = a.H * d;
-  const int64_t M = a.B * a.T;
+  const int64_t Tw = a.tt1 - a.tt0;  // tokens [tt0, tt1) of every sequence: GEMM row r is token
+  const int64_t M = a.B * Tw;        // tt0 + r mod Tw of sequence r / Tw
   const int N = 3 * D;
   const int K = D;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -173,6 +174,12 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // direct loads of one K-step: per matrix 256 rows x 8 chunks; instruction i of
   // wave w fills LDS rows 8 (8 i + w) .. +8, lane -> row + lane / 8, chunk lane % 8
+  int64_t xrow[4];  // X row of this lane's A rows (-1 past the end)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t ga = m0 + 8 * (8 * i + w) + (lane >> 3);
+    xrow[i] = ga < M ? (ga / Tw) * a.T + a.tt0 + ga % Tw : -1;
+  }
   auto issue = [&](int k0, int buf) {
     uint16_t* base = smem + buf * T_STAGE;
 #pragma unroll
@@ -181,10 +188,9 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
       const int gch = swz(row, lane & 7);
       uint16_t* ldsA = base + (8 * (8 * i + w)) * T_BK;
       uint16_t* ldsB = base + T_BM * T_BK + (8 * (8 * i + w)) * T_BK;
-      const int64_t ga = m0 + row;
       const int gb = n0 + row;
-      if (ga < M)
-        __builtin_amdgcn_global_load_lds((const void*)(X + ga * K + k0 + 8 * gch),
+      if (xrow[i] >= 0)
+        __builtin_amdgcn_global_load_lds((const void*)(X + xrow[i] * K + k0 + 8 * gch),
                                          (__attribute__((address_space(3))) void*)ldsA, 16, 0, 0);
       if (gb < N)
         __builtin_amdgcn_global_load_lds((const void*)(Th + (int64_t)gb * K + k0 + 8 * gch),
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int64_t grow = m0 + wm * 128 + row;
     if (grow >= M) continue;
     const uint4 v = *(const uint4*)(ctile + row * 64 + 8 * swz(row, ch));
-    const int64_t s = grow / a.T, tt = grow - s * a.T;
+    const int64_t s = grow / Tw, tt = a.tt0 + (grow - s * Tw);
     const int64_t pos = a.reverse ? a.T - 1 - tt : tt;
     uint16_t* blk = out + (((int64_t)s * a.H + h) * nblk + (pos >> 4)) * (int64_t)a.blk_elems;
     *(uint4*)(blk + (p * 16 + (int)(pos & 15)) * TOK_RS + 8 * ch) = v;
@@ -264,16 +270,19 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
 bool project_mfma_supported(const ProjArgs& a) { return a.bf16 && (a.H * a.d) % 8 == 0; }
 
 hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s) {
-  const int64_t M = a.B * a.T;
   const int N = 3 * a.H * a.d;
-  if (M == 0) return hipSuccess;
   if (mode == 1 && a.d == 64 && (a.H * a.d) % T_BK == 0) {
+    const int64_t M = a.B * (a.tt1 - a.tt0);
+    if (M == 0) return hipSuccess;
     const int mtiles = (int)((M + T_BM - 1) / T_BM), ntiles = (N + T_BN - 1) / T_BN;
     const int total = mtiles * ntiles;
     const int grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL(proj_tiles_kernel, dim3((unsigned)grid), dim3(T_THREADS), 0, s, a, mtiles, ntiles);
     return hipGetLastError();
   }
+  if (a.tt0 != 0 || a.tt1 != a.T) return hipErrorInvalidValue;  // the other kernels cover whole sequences
+  const int64_t M = a.B * a.T;
+  if (M == 0) return hipSuccess;
   dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
   if (mode == 0)
     hipLaunchKernelGGL(proj_mfma_kernel<0>, grid, dim3(256), 0, s, a);

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const int64_t T = a.T;
+  const int64_t T = a.T;             // whole sequence (token indexing, block layout)
+  const int64_t p0 = a.p0, Tc = a.Tc;  // this launch: scan positions p0 .. p0 + Tc - 1
   const int D = a.H * SD;
   const int m0 = 32 * w;
   const float neta = -a.eta, gs = a.gscale;
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // ---- state, D layout: W1 rows d (4 tiles) / cols m (2 tiles), W2 rows m (2 tiles) / cols d (4 tiles)
   f32x4 W1[4][2], W2[2][4];
   {
-    const float* w1 = a.w1_0 + (int64_t)h * SD * SM;
-    const float* w2 = a.w2_0 + (int64_t)h * SM * SD;
+    const float* w1 = a.w1_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * SD * SM;
+    const float* w2 = a.w2_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * SM * SD;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
@@ -192,12 +193,13 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // gate factors: loop constants used once per step, kept in this thread's LDS slot
   GateTab[threadIdx.x] = make_float2(GeluTanh::tanh_u(a.alpha[ch0]), GeluTanh::tanh_u(a.alpha[ch0 + 1]));
 
-  const int64_t nblk = (T + SB - 1) / SB;
-  const uint16_t* blocks = (const uint16_t*)a.qkv_tiles + ((int64_t)s * a.H + h) * nblk * BLK;
+  const int64_t nblk = (Tc + SB - 1) / SB;  // blocks of this launch
+  const uint16_t* blocks =
+      (const uint16_t*)a.qkv_tiles + (((int64_t)s * a.H + h) * ((T + SB - 1) / SB) + p0 / SB) * BLK;
   const uint16_t* xin = (const uint16_t*)a.xin;
   uint16_t* yout = (uint16_t*)a.y;
   auto tok_index = [&](int64_t pos) -> int64_t { return a.reverse ? T - 1 - pos : pos; };
-  auto block_n = [&](int64_t j) -> int { return (int)((T - SB * j) < SB ? (T - SB * j) : SB); };
+  auto block_n = [&](int64_t j) -> int { return (int)((Tc - SB * j) < SB ? (Tc - SB * j) : SB); };
 
   // token blocks: direct global -> LDS loads two steps ahead of use (no registers);
   // lane i of a wave fills bytes [16 i, 16 i + 16) of the wave's 1 KB slice.  The
@@ -216,9 +218,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   };
   static_assert(BLK_CHUNKS <= NTHR, "one 16-byte chunk per thread");
   auto load_x = [&](int64_t jx) -> uint32_t {  // two bf16 gate inputs of this lane's finished values
-    const int64_t pos = SB * jx + rd_t;
-    if (jx < 0 || pos >= T) return 0u;
-    return *(const uint32_t*)(xin + ((int64_t)s * T + tok_index(pos)) * D + ch0);
+    const int64_t lp = SB * jx + rd_t;  // position within this launch
+    if (jx < 0 || lp >= Tc) return 0u;
+    return *(const uint32_t*)(xin + ((int64_t)s * T + tok_index(p0 + lp)) * D + ch0);
   };
   // the two values of (wave-summed) partial tile `part` this lane finishes
   auto reduce2 = [&](const f32x4 (*part)[4][64]) -> float2 {
@@ -232,9 +234,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     return acc;
   };
   auto store_z = [&](int64_t jz, uint32_t xv, float2 z) {
-    const int64_t pos = SB * jz + rd_t;
-    if (pos < T) {
-      const int64_t o = ((int64_t)s * T + tok_index(pos)) * D + ch0;
+    const int64_t lp = SB * jz + rd_t;
+    if (lp < Tc) {
+      const int64_t o = ((int64_t)s * T + tok_index(p0 + lp)) * D + ch0;
       const float x0 = __uint_as_float(xv << 16), x1 = __uint_as_float(xv & 0xffff0000u);
       const float2 tg = GateTab[threadIdx.x];
       const __bf16 y0 = (__bf16)fmaf(tg.x, z.x, x0), y1 = (__bf16)fmaf(tg.y, z.y, x1);
