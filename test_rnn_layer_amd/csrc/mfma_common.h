@@ -31,23 +31,28 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                    0, 0, 0);
 }
 
-// A 16x16x16 product computed with the K=32 instruction (upper halves of both
-// operands zero).  Used where the product accumulates onto the result of a
-// 16x16x32 product: chains of dependent matrix-core products stay on one
-// instruction.  A 16x16x32 result read as the accumulator of a 16x16x16 product
-// a few instructions later, with no other matrix-core instruction between, gave
-// wrong values in the first two result registers on gfx950, and the compiler
-// inserts no wait for that case.
-__device__ __forceinline__ f32x4 mfma16_as32(bf16x4 a, bf16x4 b, f32x4 c) {
-  bf16x8 a8, b8;
+// Chains of dependent matrix-core products stay on one instruction: a 16x16x32
+// result read as the accumulator of a 16x16x16 product a few instructions
+// later, with no other matrix-core instruction between, gave wrong values in
+// the first two result registers on gfx950, and the compiler inserts no wait for
+// that case.  A K=16 product that accumulates onto a K=32 one is therefore done
+// with the K=32 instruction: with A = {a0, a1} (two K=16 operands side by side)
+// and B = {b, 0} the product is a0 b, with B = {0, b} it is a1 b.
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+  bf16x8 v;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a8[i] = a[i];
-    a8[4 + i] = (__bf16)0.0f;
-    b8[i] = b[i];
-    b8[4 + i] = (__bf16)0.0f;
+    v[i] = lo[i];
+    v[4 + i] = hi[i];
   }
-  return mfma32(a8, b8, c);
+  return v;
+}
+
+__device__ __forceinline__ bf16x4 zero4b() {
+  bf16x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (__bf16)0.0f;
+  return v;
 }
 
 __device__ __forceinline__ bf16x4 pack4(f32x4 x) {

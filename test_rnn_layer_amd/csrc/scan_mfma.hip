@@ -248,12 +248,12 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 
   // carried from block j-1 to its read-out during block j
   f32x4 St_prev = zero4();
-  bf16x4 g1T_prev[2], g2T_prev[4];
+  // -eta G1^T and -eta G2^T of the previous block, kept in pairs of K=16
+  // operands: tile 2i in the low half, 2i+1 in the high half of g?T_prev[i]
+  bf16x8 g1T_prev, g2T_prev[2];
   bf16x8 hkB_prev = zero8();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) g1T_prev[i] = ident;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) g2T_prev[i] = ident;
+  g1T_prev = cat8(ident, ident);
+  for (int i = 0; i < 2; ++i) g2T_prev[i] = cat8(ident, ident);
   uint32_t x_blk = 0u;  // gate inputs of the block whose Z is finished next
 
   for (int64_t jb = 0; jb < NSTAGE - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
@@ -284,13 +284,15 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       bf16x4 sT;
 #pragma unroll
       for (int r = 0; r < 4; ++r) sT[r] = (__bf16)(4 * g + r > c ? -St_prev[r] : 0.0f);
+      // K=16 products as K=32 ones: {x, 0} picks the low tile of a pair, {0, x} the high one
+      const bf16x8 sT_lo = cat8(sT, zero4b()), sT_hi = cat8(zero4b(), sT);
       const bf16x8 q0 = rd_row8(blk_prev, OFF_Q, np, g, c, 0), q1 = rd_row8(blk_prev, OFF_Q, np, g, c, 1);
       f32x4 Hq[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 aq = mfma32(w1p[0][nt], q0, zero4());
         aq = mfma32(w1p[1][nt], q1, aq);
-        aq = mfma16_as32(g1T_prev[nt], sT, aq);
+        aq = mfma32(g1T_prev, nt ? sT_hi : sT_lo, aq);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Hq[nt][r] = G::value(aq[r]);
       }
@@ -299,11 +301,12 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       bf16x4 pT;
 #pragma unroll
       for (int r = 0; r < 4; ++r) pT[r] = (__bf16)(4 * g + r > c ? -Pt[r] : 0.0f);
+      const bf16x8 pT_lo = cat8(pT, zero4b()), pT_hi = cat8(zero4b(), pT);
       f32x4 zp[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         zp[dt] = mfma32(w2p[dt], hqB, zero4());
-        zp[dt] = mfma16_as32(g2T_prev[dt], pT, zp[dt]);
+        zp[dt] = mfma32(g2T_prev[dt >> 1], (dt & 1) ? pT_hi : pT_lo, zp[dt]);
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) Zpart[w][dt][lane] = zp[dt];
@@ -423,10 +426,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       for (int dt = 0; dt < 4; ++dt) W2[mt][dt] = mfma16(hkT[mt], g2T[dt], W2[mt][dt]);
 
     St_prev = St;
-    g1T_prev[0] = g1T[0];
-    g1T_prev[1] = g1T[1];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) g2T_prev[dt] = g2T[dt];
+    g1T_prev = cat8(g1T[0], g1T[1]);
+    g2T_prev[0] = cat8(g2T[0], g2T[1]);
+    g2T_prev[1] = cat8(g2T[2], g2T[3]);
     hkB_prev = hkB;
   }
 
