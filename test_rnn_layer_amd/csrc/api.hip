@@ -389,6 +389,7 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
       pa.tt1 = D.reverse ? T - p0 : p1;
       TTT_TRY(timed_launch(TTT_KERNEL_PROJECT, S2, [&] { return ttt::launch_project_mfma(pa, 1, S2); }),
               "projection launch");
+      if (k == C - 1) TTT_TRY(ttt::launch_zero_block_padding(pa, S2), "padding launch");
       TTT_TRY(hipEventRecord(ev_proj(d, k), S2), "event record");
     }
     // the scan, chunk by chunk on the caller's stream

@@ -25,6 +25,8 @@ hipError_t launch_project_f32out(const ProjArgs& a, hipStream_t s);
 // bf16 MFMA GEMM; mode 0: fp32 [3, B, H, T, d]; mode 1: the MFMA scan's token blocks.
 bool project_mfma_supported(const ProjArgs& a);
 hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s);
+// Zeroes the rows past the end of each sequence's last token block (mode 1 layout).
+hipError_t launch_zero_block_padding(const ProjArgs& a, hipStream_t s);
 
 // One direction of the scan.
 struct ScanArgs {

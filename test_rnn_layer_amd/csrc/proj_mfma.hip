@@ -265,7 +265,28 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   }
 }
 
+// Rows of the last token block past the end of the sequence (T mod 16 of
+// them valid): zero in all three panels, so that the scan reads them
+// unmasked.  One workgroup per (sequence, head).
+__global__ void zero_block_padding_kernel(uint16_t* out, int64_t T, int H, int blk_elems) {
+  const int n = (int)(T & 15);
+  const int64_t nblk = (T + 15) / 16;
+  uint16_t* blk = out + ((int64_t)blockIdx.x * nblk + nblk - 1) * blk_elems;
+  const int rows = 16 - n;  // per panel
+  for (int i = threadIdx.x; i < 3 * rows * TOK_RS; i += blockDim.x) {
+    const int p = i / (rows * TOK_RS), r = n + (i / TOK_RS) % rows, col = i % TOK_RS;
+    blk[(p * 16 + r) * TOK_RS + col] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_zero_block_padding(const ProjArgs& a, hipStream_t s) {
+  if (a.T % 16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_block_padding_kernel, dim3((unsigned)(a.B * a.H)), dim3(256), 0, s, (uint16_t*)a.out, a.T,
+                     a.H, a.blk_elems);
+  return hipGetLastError();
+}
 
 bool project_mfma_supported(const ProjArgs& a) { return a.bf16 && (a.H * a.d) % 8 == 0; }
 

@@ -6,25 +6,23 @@
 // (see generic.hip) with fp32 state and fp32 accumulation; matrix operands
 // are rounded to bf16.
 //
-// One 256-thread workgroup per (sequence, head); wave w owns hidden units
-// [64w, 64w+64): its slices of W1 (64 x 64) and W2 (64 x 64) live in
+// One 512-thread workgroup per (sequence, head); wave w owns hidden units
+// [32w, 32w+32): its slices of W1 (64 x 32) and W2 (32 x 64) live in
 // registers in the MFMA D layout for the whole sequence, so the state never
 // leaves the CU.  Activations are kept "feature-major" (tokens along the 16
-// lanes of a tile):
+// lanes of a tile).  Step j runs block j's recurrence
 //   A^T = W1^T K^T, Hk^T = GELU(A^T)                     (local to the wave)
 //   Yhat^T = W2^T Hk^T                  partial over hidden units -> LDS reduce
-//   G2 = c (Yhat - V)                   each wave finishes one 16-wide d slice
+//   G2 = c (Yhat - V)                   each thread finishes two values
 //   Gh^T = W2 G2^T, G1^T = Gh^T * GELU'(A^T)
-//   Aq^T = W1^T Q^T - eta G1^T tril(Q K^T)^T, Hq^T = GELU(Aq^T)
-//   Z^T  = W2^T Hq^T - eta G2^T tril(Hq Hk^T)^T        partial -> LDS reduce
 //   W1 -= eta K^T G1,  W2 -= eta Hk^T G2                 (K=16 MFMAs)
-// A tile in the D layout is a K=16 operand of its own transpose, so an MFMA
-// against the identity turns it into the D layout of the transpose: that
-// gives the W2 operand of Gh (contracted over d, not m) and the token-major
-// copies of Hk and G1 that the K=16 products over tokens need.
-// The Z reduction, the gate y = x + tanh(alpha) z and the stores of a
-// mini-batch happen during the next mini-batch, off the recurrence's path.
-// Two workgroup barriers per mini-batch.
+// and block j-1's read-out with the state that follows block j-1 (exact):
+//   Aq^T = W1'^T Q^T + eta G1^T striu(Q K^T)^T, Hq^T = GELU(Aq^T)
+//   Z^T  = W2'^T Hq^T + eta G2^T striu(Hq Hk^T)^T       partial -> LDS reduce
+// with the gate y = x + tanh(alpha) z and the stores of block j-1.  The
+// transposed operands (W2 for Gh, contracted over d; token-major G1, Hk and
+// K for the updates) come from LDS transpose reads.  Two workgroup barriers
+// per block.
 #include "internal.h"
 #include "mfma_common.h"
 
@@ -108,10 +106,10 @@ __device__ __forceinline__ bf16x8 zero8() {
   return v;
 }
 
-// Readers of the staged token block (LDS), masking tokens >= n of a short block.
+// Readers of the staged token block (LDS).  Rows past the end of a short last
+// block are zero in the workspace (see zero_block_padding), so no masking.
 // A K=32 operand row in the pair order: features 32cc + 4g .. +3 and 32cc + 16 + 4g .. +3.
-__device__ __forceinline__ bf16x8 rd_row8(const uint16_t* blk, int off, int n, int g, int c, int cc) {
-  if (c >= n) return zero8();
+__device__ __forceinline__ bf16x8 rd_row8(const uint16_t* blk, int off, int g, int c, int cc) {
   const uint16_t* row = blk + off + c * RS + 32 * cc + 4 * g;
   const bf16x4 lo = *(const bf16x4*)row, hi = *(const bf16x4*)(row + 16);
   bf16x8 v;
@@ -123,6 +121,25 @@ __device__ __forceinline__ bf16x8 rd_row8(const uint16_t* blk, int off, int n, i
   return v;
 }
 
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i mod 4 of the 8 bytes addressed by lanes
+// i/4 + 4e (e = 0..3) of its group, as its element e.
+__device__ __forceinline__ bf16x4 ld_tr(const void* lds_addr) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)lds_addr);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// The transpose of a 16 x 16 tile held in the D layout (lane (g, c), element r:
+// row 4g + r, column c), whose 4 bf16 per lane were stored at base + lane *
+// stride (bytes): lane (g, c) receives row c, columns 4g .. 4g+3 of the tile's
+// transpose, i.e. the tile in the operand layout A[c][4g .. 4g+3].  Lane 16g + j
+// addresses the values stored by lane 16 (j mod 4) + 4g + j/4.
+__device__ __forceinline__ bf16x4 tr_tile(const char* base, int stride, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  return ld_tr(base + (16 * (j & 3) + 4 * g + (j >> 2)) * stride);
+}
+
 template <class G>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_mfma_kernel(ScanArgs a) {
   __shared__ f32x4 Ypart[NWAVE][4][64];                            // partial Yhat^T: wave, d-tile, lane
@@ -130,7 +147,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
   __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+1
-  __shared__ bf16x8 SelTab[2][64];                                  // K^T selectors (below), per lane
   __shared__ float2 GateTab[NTHR];                                  // tanh(alpha) of each thread's two features
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -156,28 +172,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           W1[dt][nt][r] = w1[(16 * dt + 4 * g + r) * SM + m0 + 16 * nt + c];
           W2[nt][dt][r] = w2[(m0 + 16 * nt + 4 * g + r) * SD + 16 * dt + c];
         }
-    }
-  }
-  // the 16 x 16 identity as a K=16 B operand: lane holds rows 4g..4g+3 of column c
-  bf16x4 ident;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) ident[r] = (__bf16)(4 * g + r == c ? 1.0f : 0.0f);
-
-  // 0/1 selectors that pick d-tile 2cc + half out of a pair-ordered 32-slice:
-  // K (rows t, pair-ordered d) times sel[half] is the D layout of K's d-tile,
-  // i.e. the token-major K^T operand of the W1 update.
-  // They are constants used once per step, so they live in LDS, not in registers
-  // (published by the barrier before the loop).
-  if (w == 0) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      bf16x8 sel;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int dpos = i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4);  // feature of position 8g + i
-        sel[i] = (__bf16)(dpos == 16 * half + c ? 1.0f : 0.0f);
-      }
-      SelTab[half][lane] = sel;
     }
   }
 
@@ -252,8 +246,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   // operands: tile 2i in the low half, 2i+1 in the high half of g?T_prev[i]
   bf16x8 g1T_prev, g2T_prev[2];
   bf16x8 hkB_prev = zero8();
-  g1T_prev = cat8(ident, ident);
-  for (int i = 0; i < 2; ++i) g2T_prev[i] = cat8(ident, ident);
+  g1T_prev = zero8();
+  for (int i = 0; i < 2; ++i) g2T_prev[i] = zero8();
   uint32_t x_blk = 0u;  // gate inputs of the block whose Z is finished next
 
   for (int64_t jb = 0; jb < NSTAGE - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
@@ -280,13 +274,12 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // ---- read-out of block j-1 with the state that follows it:
     //   Aq = Q W1' + eta striu(Q K^T) G1,  Z = GELU(Aq) W2' + eta striu(Hq Hk^T) G2
     if (j > 0) {
-      const int np = block_n(j - 1);
       bf16x4 sT;
 #pragma unroll
       for (int r = 0; r < 4; ++r) sT[r] = (__bf16)(4 * g + r > c ? -St_prev[r] : 0.0f);
       // K=16 products as K=32 ones: {x, 0} picks the low tile of a pair, {0, x} the high one
       const bf16x8 sT_lo = cat8(sT, zero4b()), sT_hi = cat8(zero4b(), sT);
-      const bf16x8 q0 = rd_row8(blk_prev, OFF_Q, np, g, c, 0), q1 = rd_row8(blk_prev, OFF_Q, np, g, c, 1);
+      const bf16x8 q0 = rd_row8(blk_prev, OFF_Q, g, c, 0), q1 = rd_row8(blk_prev, OFF_Q, g, c, 1);
       f32x4 Hq[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -316,8 +309,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // ---- A^T = W1^T K^T, S^T = K Q^T (block j)
     f32x4 At[2], St;
     {
-      const bf16x8 k0 = rd_row8(blk, OFF_K, n, g, c, 0), k1 = rd_row8(blk, OFF_K, n, g, c, 1);
-      const bf16x8 q0 = rd_row8(blk, OFF_Q, n, g, c, 0), q1 = rd_row8(blk, OFF_Q, n, g, c, 1);
+      const bf16x8 k0 = rd_row8(blk, OFF_K, g, c, 0), k1 = rd_row8(blk, OFF_K, g, c, 1);
+      const bf16x8 q0 = rd_row8(blk, OFF_Q, g, c, 0), q1 = rd_row8(blk, OFF_Q, g, c, 1);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         At[nt] = mfma32(w1p[0][nt], k0, zero4());
@@ -389,34 +382,46 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     x_blk = load_x(j);
     if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) % NSTAGE));
 
-    // ---- Gh^T = W2 G2^T (contraction over d: transposes of the W2 tiles), G1^T = Gh^T * GELU'(A^T)
+    // ---- Gh^T = W2 G2^T (contraction over d), G1^T = Gh^T * GELU'(A^T).  The
+    //      transposed operands come from LDS transpose reads of this wave's own
+    //      slices of Ypart / Zpart (free after the second barrier, rewritten by
+    //      this wave only in the next step): W2 tiles from the bf16 operands w2p,
+    //      -eta G1 and Hk tiles written here, K^T straight from the staged block.
     bf16x8 g2B[2];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) g2B[cc] = *(const bf16x8*)(&G2a[c * RS + 32 * cc + 8 * g]);
     bf16x4 g2T[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) g2T[dt] = *(const bf16x4*)(&G2b[(16 * dt + c) * TS + 4 * g]);
+    char* scrW = (char*)&Ypart[w][0][0];  // w2p[dt] of lane l at 1024 dt + 16 l (tile (mt, dt): + 8 mt)
+    char* scrG = (char*)&Zpart[w][0][0];  // -eta G1 tile mt at 512 mt + 8 l; Hk pair at 1024 + 16 l
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) *(bf16x8*)(scrW + 1024 * dt + 16 * lane) = w2p[dt];
+    *(bf16x8*)(scrG + 1024 + 16 * lane) = hkB;
+    lds_stores_done();
     bf16x4 g1T[2], hkT[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      f32x4 tt[4];
+      bf16x4 w2t[4];  // tile (mt, dt) transposed: row m = c, features 16 dt + 4g .. +3
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) tt[dt] = mfma16(pack4(W2[mt][dt]), ident, zero4());
-      f32x4 gh = mfma32(pack8(tt[0], tt[1]), g2B[0], zero4());
-      gh = mfma32(pack8(tt[2], tt[3]), g2B[1], gh);
-      const f32x4 g1 = gh * Dg[mt];
-      // token-major copies (tokens 4g..4g+3 of hidden unit m0 + 16mt + c)
-      g1T[mt] = pack4(mfma16(pack4(neta * g1), ident, zero4()));
-      bf16x4 hk;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hk[r] = hkB[4 * mt + r];
-      hkT[mt] = pack4(mfma16(hk, ident, zero4()));
+      for (int dt = 0; dt < 4; ++dt) w2t[dt] = tr_tile(scrW + 1024 * dt + 8 * mt, 16, lane);
+      f32x4 gh = mfma32(cat8(w2t[0], w2t[1]), g2B[0], zero4());
+      gh = mfma32(cat8(w2t[2], w2t[3]), g2B[1], gh);
+      *(bf16x4*)(scrG + 512 * mt + 8 * lane) = pack4(neta * (gh * Dg[mt]));
     }
-    // ---- state update: W1 += K^T (-eta G1), W2 += Hk^T (-eta G2)
-    const bf16x8 kr0 = rd_row8(blk, OFF_K, n, g, c, 0), kr1 = rd_row8(blk, OFF_K, n, g, c, 1);
+    lds_stores_done();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      // token-major copies (tokens 4g..4g+3 of hidden unit m0 + 16mt + c)
+      g1T[mt] = tr_tile(scrG + 512 * mt, 8, lane);
+      hkT[mt] = tr_tile(scrG + 1024 + 8 * mt, 16, lane);
+    }
+    // ---- state update: W1 += K^T (-eta G1), W2 += Hk^T (-eta G2).  K^T tile dt
+    //      (row d = 16 dt + c, tokens 4g .. 4g+3): lane 16g + j reads token
+    //      4g + j/4, features 16 dt + 4 (j mod 4) .. +3 of the staged block
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const bf16x4 kt = pack4(mfma32(dt < 2 ? kr0 : kr1, SelTab[dt & 1][lane], zero4()));
+      const bf16x4 kt = ld_tr(blk + OFF_K + (4 * g + ((lane & 15) >> 2)) * RS + 16 * dt + 4 * (lane & 3));
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) W1[dt][nt] = mfma16(kt, g1T[nt], W1[dt][nt]);
     }
