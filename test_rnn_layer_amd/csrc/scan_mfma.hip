@@ -25,6 +25,7 @@
 // per block.
 #include "internal.h"
 #include "mfma_common.h"
+#include "phi_poly.h"
 
 namespace ttt {
 namespace {
@@ -49,31 +50,27 @@ static_assert((BLK * 2) % 16 == 0, "block must be a whole number of 16-byte chun
 // GELU and its derivative from one exponential.  erf by Abramowitz & Stegun
 // 7.1.26 (Hastings' rational approximation, |error| <= 1.5e-7):
 //   erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),  t = 1 / (1 + p x),  x >= 0.
+// GELU(a) = a Phi(a), GELU'(a) = Phi(a) + a phi(a), with Phi from the
+// polynomial of phi_poly.h (|error| <= 1.5e-5, no reciprocal or exponential:
+// the values are rounded to bf16 matrix operands, or multiplied into them, so
+// this is far below the operands' own rounding) and phi(a) = exp(-a^2/2) /
+// sqrt(2 pi).
 struct Gelu {
-  static __device__ __forceinline__ float phi_tail(float ax_over_sqrt2, float* e) {
-    const float x = ax_over_sqrt2;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-    float p = fmaf(1.061405429f, t, -1.453152027f);
-    p = fmaf(p, t, 1.421413741f);
-    p = fmaf(p, t, -0.284496736f);
-    p = fmaf(p, t, 0.254829592f);
-    p *= t;
-    *e = __builtin_amdgcn_exp2f(-1.4426950408889634f * x * x);  // exp(-x^2) = exp(-a^2/2)
-    return 0.5f * p * (*e);  // 1 - Phi(|a|) = erfc(|a|/sqrt2) / 2
+  static __device__ __forceinline__ float cdf(float a) {
+    const float c = __builtin_amdgcn_fmed3f(a, -kPhiL, kPhiL);
+    const float sq = c * c;
+    float q = kPhiP[kPhiDeg];
+#pragma unroll
+    for (int k = kPhiDeg - 1; k >= 0; --k) q = fmaf(q, sq, kPhiP[k]);
+    return fmaf(c, q, 0.5f);
   }
-  // GELU(a) and GELU'(a) = Phi(a) + a phi(a)
   static __device__ __forceinline__ void both(float a, float* g, float* dg) {
-    float e;
-    const float tail = phi_tail(fabsf(a) * 0.7071067811865476f, &e);
-    const float cdf = a >= 0.0f ? 1.0f - tail : tail;
-    *g = a * cdf;
-    *dg = fmaf(a * 0.3989422804014327f, e, cdf);
+    const float p = cdf(a);
+    *g = a * p;
+    const float e = __builtin_amdgcn_exp2f(-0.7213475204444817f * a * a);  // exp(-a^2/2)
+    *dg = fmaf(a * 0.3989422804014327f, e, p);
   }
-  static __device__ __forceinline__ float value(float a) {
-    float e;
-    const float tail = phi_tail(fabsf(a) * 0.7071067811865476f, &e);
-    return a * (a >= 0.0f ? 1.0f - tail : tail);
-  }
+  static __device__ __forceinline__ float value(float a) { return a * cdf(a); }
 };
 
 // tanh(u) = 1 - 2 / (exp(2u) + 1) (exact identity; saturates to +-1 for large |u|),
