@@ -35,7 +35,7 @@ constexpr int SM = 256;  // hidden width
 constexpr int SB = 16;   // mini-batch
 constexpr int NWAVE = 8;          // wave w owns hidden units [32w, 32w + 32)
 constexpr int NTHR = 64 * NWAVE;
-constexpr int NSTAGE = 3;         // token blocks in LDS: j-1 (read-out), j, and j+1 in flight
+constexpr int NSTAGE = 4;         // token blocks in LDS: j-1 (read-out), j, j+1 and j+2 in flight
 // Token block layout (bf16 elements): Q, K and V of 16 consecutive scan
 // positions, each [16 tokens][RS] with the features in order and rows padded to
 // RS = 72 (144 bytes) so that the 16 rows read by one 16-lane group fall on
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __shared__ f32x4 Zpart[NWAVE][4][64];                            // partial Z^T
   __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
-  __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+1
+  __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+2
   __shared__ float2 GateTab[NTHR];                                  // tanh(alpha) of each thread's two features
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   auto tok_index = [&](int64_t pos) -> int64_t { return a.reverse ? T - 1 - pos : pos; };
   auto block_n = [&](int64_t j) -> int { return (int)((Tc - SB * j) < SB ? (Tc - SB * j) : SB); };
 
-  // token blocks: direct global -> LDS loads two steps ahead of use (no registers);
+  // token blocks: direct global -> LDS loads three steps ahead of use (no registers);
   // lane i of a wave fills bytes [16 i, 16 i + 16) of the wave's 1 KB slice.  The
   // load is written as a statement of its own rather than through the compiler's
   // builtin: the compiler makes every later LDS read of Stage wait for all such
@@ -208,10 +208,13 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(src) : "memory", "m0");
   };
   static_assert(BLK_CHUNKS <= NTHR, "one 16-byte chunk per thread");
-  auto load_x = [&](int64_t jx) -> uint32_t {  // two bf16 gate inputs of this lane's finished values
-    const int64_t lp = SB * jx + rd_t;  // position within this launch
-    if (jx < 0 || lp >= Tc) return 0u;
-    return *(const uint32_t*)(xin + ((int64_t)s * T + tok_index(p0 + lp)) * D + ch0);
+  // element offset (in X, Y, Z) of this lane's first finished value in block j:
+  // moves by +-16 D per block
+  const int64_t xstep = (a.reverse ? -(int64_t)SB : (int64_t)SB) * D;
+  int64_t xo = ((int64_t)s * T + tok_index(p0 + rd_t)) * D + ch0;
+  auto load_x = [&](int64_t jx, int64_t off) -> uint32_t {  // two bf16 gate inputs of this lane's values
+    if (SB * jx + rd_t >= Tc) return 0u;
+    return *(const uint32_t*)(xin + off);
   };
   // the two values of (wave-summed) partial tile `part` this lane finishes
   auto reduce2 = [&](const f32x4 (*part)[4][64]) -> float2 {
@@ -224,10 +227,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     }
     return acc;
   };
-  auto store_z = [&](int64_t jz, uint32_t xv, float2 z) {
-    const int64_t lp = SB * jz + rd_t;
-    if (lp < Tc) {
-      const int64_t o = ((int64_t)s * T + tok_index(p0 + lp)) * D + ch0;
+  auto store_z = [&](int64_t jz, int64_t o, uint32_t xv, float2 z) {
+    if (SB * jz + rd_t < Tc) {
       const float x0 = __uint_as_float(xv << 16), x1 = __uint_as_float(xv & 0xffff0000u);
       const float2 tg = GateTab[threadIdx.x];
       const __bf16 y0 = (__bf16)fmaf(tg.x, z.x, x0), y1 = (__bf16)fmaf(tg.y, z.y, x1);
@@ -256,8 +257,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   for (int64_t j = 0; j <= nblk && nblk > 0; ++j) {
     const bool live = j < nblk;
     const int n = live ? block_n(j) : 0;
-    const uint16_t* blk = Stage[j % NSTAGE];
-    const uint16_t* blk_prev = Stage[(j + NSTAGE - 1) % NSTAGE];
+    const uint16_t* blk = Stage[j & (NSTAGE - 1)];
+    const uint16_t* blk_prev = Stage[(j - 1) & (NSTAGE - 1)];
 
     // ---- bf16 operands of the current state
     bf16x8 w1p[2][2], w2p[4];
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // barriers: each barrier's release fence waits for the wave's outstanding ones.
     const float2 zfin = reduce2(Zpart);
     if (!live) {
-      store_z(j - 1, x_blk, zfin);
+      store_z(j - 1, xo - xstep, x_blk, zfin);
       break;
     }
     {
@@ -373,11 +374,12 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // ---- vector-memory work of this step, issued right after the barrier and waited
     // for just before the next step's second barrier: Y and Z of block j-1, the gate
     // inputs of block j (one register, consumed before it is reloaded: no register
-    // rotation, which would make the compiler wait at once), block j+2 into the
+    // rotation, which would make the compiler wait at once), block j+3 into the
     // buffer that held block j-1 (last read before this step's first barrier)
-    if (j > 0) store_z(j - 1, x_blk, zfin);
-    x_blk = load_x(j);
-    if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) % NSTAGE));
+    if (j > 0) store_z(j - 1, xo - xstep, x_blk, zfin);
+    x_blk = load_x(j, xo);
+    xo += xstep;
+    if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) & (NSTAGE - 1)));
 
     // ---- Gh^T = W2 G2^T (contraction over d), G1^T = Gh^T * GELU'(A^T).  The
     //      transposed operands come from LDS transpose reads of this wave's own
