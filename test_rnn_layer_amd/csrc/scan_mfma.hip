@@ -144,7 +144,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
   __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+2
-  __shared__ float2 GateTab[NTHR];                                  // tanh(alpha) of each thread's two features
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -182,7 +181,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int rd_d = 16 * rd_dt + 4 * (rd_src >> 4) + 2 * rd_p;
   const int ch0 = h * SD + rd_d;
   // gate factors: loop constants used once per step, kept in this thread's LDS slot
-  GateTab[threadIdx.x] = make_float2(GeluTanh::tanh_u(a.alpha[ch0]), GeluTanh::tanh_u(a.alpha[ch0 + 1]));
+  const float2 tg = make_float2(GeluTanh::tanh_u(a.alpha[ch0]), GeluTanh::tanh_u(a.alpha[ch0 + 1]));
 
   const int64_t nblk = (Tc + SB - 1) / SB;  // blocks of this launch
   const uint16_t* blocks =
@@ -216,21 +215,29 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     if (SB * jx + rd_t >= Tc) return 0u;
     return *(const uint32_t*)(xin + off);
   };
-  // the two values of (wave-summed) partial tile `part` this lane finishes
-  auto reduce2 = [&](const f32x4 (*part)[4][64]) -> float2 {
-    float2 acc = make_float2(0.0f, 0.0f);
+  // the two values of the wave-summed partial tiles Zpart and Ypart this lane
+  // finishes: all 16 loads are issued before any sum (fixed order of the sums)
+  auto reduce_zy = [&](float2* z, float2* y) {
+    float2 vz[NWAVE], vy[NWAVE];
 #pragma unroll
     for (int q = 0; q < NWAVE; ++q) {
-      const float2 v = *((const float2*)&part[q][rd_dt][rd_src] + rd_p);
-      acc.x += v.x;
-      acc.y += v.y;
+      vz[q] = *((const float2*)&Zpart[q][rd_dt][rd_src] + rd_p);
+      vy[q] = *((const float2*)&Ypart[q][rd_dt][rd_src] + rd_p);
     }
-    return acc;
+    float2 az = make_float2(0.0f, 0.0f), ay = make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) {
+      az.x += vz[q].x;
+      az.y += vz[q].y;
+      ay.x += vy[q].x;
+      ay.y += vy[q].y;
+    }
+    *z = az;
+    *y = ay;
   };
   auto store_z = [&](int64_t jz, int64_t o, uint32_t xv, float2 z) {
     if (SB * jz + rd_t < Tc) {
       const float x0 = __uint_as_float(xv << 16), x1 = __uint_as_float(xv & 0xffff0000u);
-      const float2 tg = GateTab[threadIdx.x];
       const __bf16 y0 = (__bf16)fmaf(tg.x, z.x, x0), y1 = (__bf16)fmaf(tg.y, z.y, x1);
       *(uint32_t*)(yout + o) = (uint32_t)__builtin_bit_cast(uint16_t, y0) |
                                ((uint32_t)__builtin_bit_cast(uint16_t, y1) << 16);
@@ -301,7 +308,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) Zpart[w][dt][lane] = zp[dt];
-      lds_stores_done();
     }
 
     // ---- A^T = W1^T K^T, S^T = K Q^T (block j)
@@ -337,7 +343,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       for (int dt = 0; dt < 4; ++dt) yp[dt] = mfma32(w2p[dt], hkB, zero4());
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) Ypart[w][dt][lane] = yp[dt];
-      lds_stores_done();
     }
 
     __syncthreads();
@@ -345,13 +350,13 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // ---- finish this lane's two values: Z of block j-1 (stored after the second
     // barrier), G2 of block j.  No vector-memory operation is issued between the two
     // barriers: each barrier's release fence waits for the wave's outstanding ones.
-    const float2 zfin = reduce2(Zpart);
+    float2 zfin, y;
+    reduce_zy(&zfin, &y);
     if (!live) {
       store_z(j - 1, xo - xstep, x_blk, zfin);
       break;
     }
     {
-      const float2 y = reduce2(Ypart);
       const uint32_t vv = *(const uint32_t*)(blk + OFF_V + rd_t * RS + rd_d);
       float g2x = 0.0f, g2y = 0.0f;
       if (rd_t < n) {
@@ -397,7 +402,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) *(bf16x8*)(scrW + 1024 * dt + 16 * lane) = w2p[dt];
     *(bf16x8*)(scrG + 1024 + 16 * lane) = hkB;
-    lds_stores_done();
     bf16x4 g1T[2], hkT[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -408,7 +412,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       gh = mfma32(cat8(w2t[2], w2t[3]), g2B[1], gh);
       *(bf16x4*)(scrG + 512 * mt + 8 * lane) = pack4(neta * (gh * Dg[mt]));
     }
-    lds_stores_done();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       // token-major copies (tokens 4g..4g+3 of hidden unit m0 + 16mt + c)
