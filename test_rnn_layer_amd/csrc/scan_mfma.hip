@@ -42,19 +42,18 @@ constexpr int NSTAGE = 4;         // token blocks in LDS: j-1 (read-out), j, j+1
 // distinct LDS banks.
 constexpr int RS = SD + 8;  // 72
 constexpr int TS = SB + 4;  // 20: rows of the [feature][token] G2 copy
+constexpr int DGS = SB + 4;  // 20: rows of the fp32 [hidden][token] GELU' tiles (bank spread of the column writes)
 constexpr int OFF_Q = 0, OFF_K = SB * RS, OFF_V = 2 * SB * RS;
 constexpr int BLK = 3 * SB * RS;          // 3456 elements, 6912 bytes
 constexpr int BLK_CHUNKS = BLK * 2 / 16;  // 432 chunks of 16 bytes
 static_assert((BLK * 2) % 16 == 0, "block must be a whole number of 16-byte chunks");
 
-// GELU and its derivative from one exponential.  erf by Abramowitz & Stegun
-// 7.1.26 (Hastings' rational approximation, |error| <= 1.5e-7):
-//   erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),  t = 1 / (1 + p x),  x >= 0.
-// GELU(a) = a Phi(a), GELU'(a) = Phi(a) + a phi(a), with Phi from the
-// polynomial of phi_poly.h (|error| <= 1.5e-5, no reciprocal or exponential:
-// the values are rounded to bf16 matrix operands, or multiplied into them, so
-// this is far below the operands' own rounding) and phi(a) = exp(-a^2/2) /
-// sqrt(2 pi).
+// GELU(a) = a Phi(a) and GELU'(a) = Phi(a) + a phi(a), with Phi from the
+// polynomial of phi_poly.h (|error| <= 6e-5, no reciprocal or exponential: the
+// values are rounded to bf16 matrix operands, or multiplied into them, so this
+// is about 1/30 of the operands' own rounding) and the density
+// phi(a) = exp(-a^2/2) / sqrt(2 pi) = 2^(-a^2 log2(e) / 2 + log2(1 / sqrt(2 pi))),
+// one exponential with the constant folded into its argument.
 struct Gelu {
   static __device__ __forceinline__ float cdf(float a) {
     const float c = __builtin_amdgcn_fmed3f(a, -kPhiL, kPhiL);
@@ -67,8 +66,8 @@ struct Gelu {
   static __device__ __forceinline__ void both(float a, float* g, float* dg) {
     const float p = cdf(a);
     *g = a * p;
-    const float e = __builtin_amdgcn_exp2f(-0.7213475204444817f * a * a);  // exp(-a^2/2)
-    *dg = fmaf(a * 0.3989422804014327f, e, p);
+    const float dens = __builtin_amdgcn_exp2f(fmaf(-0.7213475204444817f * a, a, -1.3257480647361593f));  // phi(a)
+    *dg = fmaf(a, dens, p);
   }
   static __device__ __forceinline__ float value(float a) { return a * cdf(a); }
 };
@@ -141,9 +140,13 @@ template <class G>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_mfma_kernel(ScanArgs a) {
   __shared__ f32x4 Ypart[NWAVE][4][64];                            // partial Yhat^T: wave, d-tile, lane
   __shared__ f32x4 Zpart[NWAVE][4][64];                            // partial Z^T
-  __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // G2 [token][feature, pair order]
+  __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // -eta G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
   __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+2
+  // per-wave slices for the transposed reads: bf16 W2 tiles, bf16 Hk^T, fp32 GELU'(A^T) as [m][t]
+  __shared__ bf16x8 W2s[NWAVE][4][64];
+  __shared__ bf16x8 HkS[NWAVE][64];
+  __shared__ __attribute__((aligned(16))) float DgS[NWAVE][2][16 * DGS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int64_t p0 = a.p0, Tc = a.Tc;  // this launch: scan positions p0 .. p0 + Tc - 1
   const int D = a.H * SD;
   const int m0 = 32 * w;
-  const float neta = -a.eta, gs = a.gscale;
+  const float ngs = -a.eta * a.gscale;  // -eta times the loss-gradient scale
 
   // ---- state, D layout: W1 rows d (4 tiles) / cols m (2 tiles), W2 rows m (2 tiles) / cols d (4 tiles)
   f32x4 W1[4][2], W2[2][4];
@@ -215,25 +218,19 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     if (SB * jx + rd_t >= Tc) return 0u;
     return *(const uint32_t*)(xin + off);
   };
-  // the two values of the wave-summed partial tiles Zpart and Ypart this lane
-  // finishes: all 16 loads are issued before any sum (fixed order of the sums)
-  auto reduce_zy = [&](float2* z, float2* y) {
-    float2 vz[NWAVE], vy[NWAVE];
+  // the two values of a wave-summed partial tile (Ypart or Zpart) this lane
+  // finishes: all loads are issued before the sum (fixed order of the sums)
+  auto reduce_part = [&](const f32x4 (&part)[NWAVE][4][64]) -> float2 {
+    float2 v[NWAVE];
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) v[q] = *((const float2*)&part[q][rd_dt][rd_src] + rd_p);
+    float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
     for (int q = 0; q < NWAVE; ++q) {
-      vz[q] = *((const float2*)&Zpart[q][rd_dt][rd_src] + rd_p);
-      vy[q] = *((const float2*)&Ypart[q][rd_dt][rd_src] + rd_p);
+      acc.x += v[q].x;
+      acc.y += v[q].y;
     }
-    float2 az = make_float2(0.0f, 0.0f), ay = make_float2(0.0f, 0.0f);
-#pragma unroll
-    for (int q = 0; q < NWAVE; ++q) {
-      az.x += vz[q].x;
-      az.y += vz[q].y;
-      ay.x += vy[q].x;
-      ay.y += vy[q].y;
-    }
-    *z = az;
-    *y = ay;
+    return acc;
   };
   auto store_z = [&](int64_t jz, int64_t o, uint32_t xv, float2 z) {
     if (SB * jz + rd_t < Tc) {
@@ -247,7 +244,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 
   // carried from block j-1 to its read-out during block j
   f32x4 St_prev = zero4();
-  // -eta G1^T and -eta G2^T of the previous block, kept in pairs of K=16
+  // -eta G1 and -eta G2^T of the previous block, kept in pairs of K=16
   // operands: tile 2i in the low half, 2i+1 in the high half of g?T_prev[i]
   bf16x8 g1T_prev, g2T_prev[2];
   bf16x8 hkB_prev = zero8();
@@ -255,60 +252,68 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   for (int i = 0; i < 2; ++i) g2T_prev[i] = zero8();
   uint32_t x_blk = 0u;  // gate inputs of the block whose Z is finished next
 
-  for (int64_t jb = 0; jb < NSTAGE - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
-  vmem_done();
-  __syncthreads();
-
-  // Iteration j runs block j's recurrence and block j-1's read-out; the extra
-  // iteration j = nblk only reads out the last block.
-  for (int64_t j = 0; j <= nblk && nblk > 0; ++j) {
-    const bool live = j < nblk;
-    const int n = live ? block_n(j) : 0;
-    const uint16_t* blk = Stage[j & (NSTAGE - 1)];
-    const uint16_t* blk_prev = Stage[(j - 1) & (NSTAGE - 1)];
-
-    // ---- bf16 operands of the current state
-    bf16x8 w1p[2][2], w2p[4];
+  // Read-out of the block staged at blk_prev with the state whose bf16 operands
+  // are w1p / w2p (the state that follows that block):
+  //   Aq = Q W1' + eta striu(Q K^T) G1,  Z = GELU(Aq) W2' + eta striu(Hq Hk^T) G2
+  // This wave's partial Z^T (its 32 hidden units) goes to Zpart[w].
+  auto readout = [&](const uint16_t* blk_prev, const bf16x8 (&w1p)[2][2], const bf16x8 (&w2p)[4]) {
+    bf16x4 sT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sT[r] = (__bf16)(4 * g + r > c ? -St_prev[r] : 0.0f);
+    // K=16 products as K=32 ones: {x, 0} picks the low tile of a pair, {0, x} the high one
+    const bf16x8 sT_lo = cat8(sT, zero4b()), sT_hi = cat8(zero4b(), sT);
+    const bf16x8 q0 = rd_row8(blk_prev, OFF_Q, g, c, 0), q1 = rd_row8(blk_prev, OFF_Q, g, c, 1);
+    f32x4 Hq[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 aq = mfma32(w1p[0][nt], q0, zero4());
+      aq = mfma32(w1p[1][nt], q1, aq);
+      aq = mfma32(g1T_prev, nt ? sT_hi : sT_lo, aq);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Hq[nt][r] = G::value(aq[r]);
+    }
+    const bf16x8 hqB = pack8(Hq[0], Hq[1]);
+    const f32x4 Pt = mfma32(hkB_prev, hqB, zero4());
+    bf16x4 pT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pT[r] = (__bf16)(4 * g + r > c ? -Pt[r] : 0.0f);
+    const bf16x8 pT_lo = cat8(pT, zero4b()), pT_hi = cat8(zero4b(), pT);
+    f32x4 zp[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      zp[dt] = mfma32(w2p[dt], hqB, zero4());
+      zp[dt] = mfma32(g2T_prev[dt >> 1], (dt & 1) ? pT_hi : pT_lo, zp[dt]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) Zpart[w][dt][lane] = zp[dt];
+  };
+  auto pack_state = [&](bf16x8 (&w1p)[2][2], bf16x8 (&w2p)[4]) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) w1p[cc][nt] = pack8(W1[2 * cc][nt], W1[2 * cc + 1][nt]);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) w2p[dt] = pack8(W2[0][dt], W2[1][dt]);
+  };
 
-    // ---- read-out of block j-1 with the state that follows it:
-    //   Aq = Q W1' + eta striu(Q K^T) G1,  Z = GELU(Aq) W2' + eta striu(Hq Hk^T) G2
-    if (j > 0) {
-      bf16x4 sT;
+  for (int64_t jb = 0; jb < NSTAGE - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
+  vmem_done();
+  __syncthreads();
+
+  // Step j runs block j's recurrence and, between its two barriers, block j-1's
+  // read-out (at j = 0 on zero operands, never stored); the last block's read-out
+  // follows the loop.
+  for (int64_t j = 0; j < nblk; ++j) {
+    const int n = block_n(j);
+    const uint16_t* blk = Stage[j & (NSTAGE - 1)];
+    const uint16_t* blk_prev = Stage[(j - 1) & (NSTAGE - 1)];
+
+    // ---- bf16 operands of the state that follows block j-1; W2's also to this
+    //      wave's LDS slice, read back transposed between the barriers
+    bf16x8 w1p[2][2], w2p[4];
+    pack_state(w1p, w2p);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sT[r] = (__bf16)(4 * g + r > c ? -St_prev[r] : 0.0f);
-      // K=16 products as K=32 ones: {x, 0} picks the low tile of a pair, {0, x} the high one
-      const bf16x8 sT_lo = cat8(sT, zero4b()), sT_hi = cat8(zero4b(), sT);
-      const bf16x8 q0 = rd_row8(blk_prev, OFF_Q, g, c, 0), q1 = rd_row8(blk_prev, OFF_Q, g, c, 1);
-      f32x4 Hq[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4 aq = mfma32(w1p[0][nt], q0, zero4());
-        aq = mfma32(w1p[1][nt], q1, aq);
-        aq = mfma32(g1T_prev, nt ? sT_hi : sT_lo, aq);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Hq[nt][r] = G::value(aq[r]);
-      }
-      const bf16x8 hqB = pack8(Hq[0], Hq[1]);
-      const f32x4 Pt = mfma32(hkB_prev, hqB, zero4());
-      bf16x4 pT;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pT[r] = (__bf16)(4 * g + r > c ? -Pt[r] : 0.0f);
-      const bf16x8 pT_lo = cat8(pT, zero4b()), pT_hi = cat8(zero4b(), pT);
-      f32x4 zp[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        zp[dt] = mfma32(w2p[dt], hqB, zero4());
-        zp[dt] = mfma32(g2T_prev[dt >> 1], (dt & 1) ? pT_hi : pT_lo, zp[dt]);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) Zpart[w][dt][lane] = zp[dt];
-    }
+    for (int dt = 0; dt < 4; ++dt) W2s[w][dt][lane] = w2p[dt];
 
     // ---- A^T = W1^T K^T, S^T = K Q^T (block j)
     f32x4 At[2], St;
@@ -323,11 +328,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       St = mfma32(k0, q0, zero4());
       St = mfma32(k1, q1, St);
     }
-    // ---- Hk^T = GELU(A^T), GELU'(A^T); partial Yhat^T = W2^T Hk^T over this wave's 32 hidden units
-    f32x4 Dg[2];
+    // ---- Hk^T = GELU(A^T) and GELU'(A^T) (both to this wave's LDS slices, for
+    //      the transposed reads); partial Yhat^T = W2^T Hk^T over this wave's 32 hidden units
     bf16x8 hkB;
     {
-      f32x4 Hk[2];
+      f32x4 Hk[2], Dg[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -338,6 +343,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           Dg[nt][r] = dv;
         }
       hkB = pack8(Hk[0], Hk[1]);
+      HkS[w][lane] = hkB;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) DgS[w][nt][(4 * g + r) * DGS + c] = Dg[nt][r];
       f32x4 yp[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) yp[dt] = mfma32(w2p[dt], hkB, zero4());
@@ -347,76 +357,55 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 
     __syncthreads();
 
-    // ---- finish this lane's two values: Z of block j-1 (stored after the second
-    // barrier), G2 of block j.  No vector-memory operation is issued between the two
-    // barriers: each barrier's release fence waits for the wave's outstanding ones.
-    float2 zfin, y;
-    reduce_zy(&zfin, &y);
-    if (!live) {
-      store_z(j - 1, xo - xstep, x_blk, zfin);
-      break;
-    }
+    // ---- between the barriers (no vector-memory operation: the second barrier
+    //      waits for the wave's outstanding ones):
+    //   G2 of block j from the wave-summed Yhat, this lane's two values;
+    //   block j-1's read-out, independent of the G2 chain;
+    //   this wave's transposed operands for the update.
     {
+      const float2 y = reduce_part(Ypart);
       const uint32_t vv = *(const uint32_t*)(blk + OFF_V + rd_t * RS + rd_d);
-      float g2x = 0.0f, g2y = 0.0f;
-      if (rd_t < n) {
-        g2x = gs * (y.x - __uint_as_float(vv << 16));
-        g2y = gs * (y.y - __uint_as_float(vv & 0xffff0000u));
-      }
-      const __bf16 b0 = (__bf16)g2x, b1 = (__bf16)g2y;
-      *(uint32_t*)&G2a[rd_t * RS + pair_order_pos(rd_d)] =
-          (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-      G2b[rd_d * TS + rd_t] = __builtin_bit_cast(uint16_t, (__bf16)(neta * g2x));
-      G2b[(rd_d + 1) * TS + rd_t] = __builtin_bit_cast(uint16_t, (__bf16)(neta * g2y));
+      const bool tv = rd_t < n;
+      const float g2x = tv ? ngs * (y.x - __uint_as_float(vv << 16)) : 0.0f;  // -eta G2
+      const float g2y = tv ? ngs * (y.y - __uint_as_float(vv & 0xffff0000u)) : 0.0f;
+      const uint16_t b0 = __builtin_bit_cast(uint16_t, (__bf16)g2x), b1 = __builtin_bit_cast(uint16_t, (__bf16)g2y);
+      *(uint32_t*)&G2a[rd_t * RS + pair_order_pos(rd_d)] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+      G2b[rd_d * TS + rd_t] = b0;
+      G2b[(rd_d + 1) * TS + rd_t] = b1;
+    }
+    readout(blk_prev, w1p, w2p);
+    // W2 tile (mt, dt) transposed: row m = c, features 16 dt + 4g .. +3; Hk in token-major
+    // form (tokens 4g .. 4g+3 of hidden unit m0 + 16 mt + c); GELU'(A) at the same places
+    bf16x4 w2t[2][4], hkT[2];
+    f32x4 DgT[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) w2t[mt][dt] = tr_tile((const char*)&W2s[w][dt][0] + 8 * mt, 16, lane);
+      hkT[mt] = tr_tile((const char*)&HkS[w][0] + 8 * mt, 16, lane);
+      DgT[mt] = *(const f32x4*)&DgS[w][mt][c * DGS + 4 * g];
     }
 
-    // this wave's vector-memory operations of the previous step (block j+1 into LDS,
-    // gate inputs of block j, stores) have had a whole step; the barrier then
-    // publishes block j+1 to every wave before its first use
+    // this wave's vector-memory operations of the previous step (block j+2 into LDS,
+    // gate inputs of block j-1, stores) have had a whole step; the barrier then
+    // publishes the next block to every wave before its first use
     vmem_done();
     __syncthreads();
 
-    // ---- vector-memory work of this step, issued right after the barrier and waited
-    // for just before the next step's second barrier: Y and Z of block j-1, the gate
-    // inputs of block j (one register, consumed before it is reloaded: no register
-    // rotation, which would make the compiler wait at once), block j+3 into the
-    // buffer that held block j-1 (last read before this step's first barrier)
-    if (j > 0) store_z(j - 1, xo - xstep, x_blk, zfin);
-    x_blk = load_x(j, xo);
-    xo += xstep;
-    if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) & (NSTAGE - 1)));
-
-    // ---- Gh^T = W2 G2^T (contraction over d), G1^T = Gh^T * GELU'(A^T).  The
-    //      transposed operands come from LDS transpose reads of this wave's own
-    //      slices of Ypart / Zpart (free after the second barrier, rewritten by
-    //      this wave only in the next step): W2 tiles from the bf16 operands w2p,
-    //      -eta G1 and Hk tiles written here, K^T straight from the staged block.
+    // ---- -eta Gh = (-eta G2) W2^T (token-major, contraction over d), -eta G1 =
+    //      -eta Gh * GELU'(A): directly the K=16 operand of the W1 update
     bf16x8 g2B[2];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) g2B[cc] = *(const bf16x8*)(&G2a[c * RS + 32 * cc + 8 * g]);
     bf16x4 g2T[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) g2T[dt] = *(const bf16x4*)(&G2b[(16 * dt + c) * TS + 4 * g]);
-    char* scrW = (char*)&Ypart[w][0][0];  // w2p[dt] of lane l at 1024 dt + 16 l (tile (mt, dt): + 8 mt)
-    char* scrG = (char*)&Zpart[w][0][0];  // -eta G1 tile mt at 512 mt + 8 l; Hk pair at 1024 + 16 l
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) *(bf16x8*)(scrW + 1024 * dt + 16 * lane) = w2p[dt];
-    *(bf16x8*)(scrG + 1024 + 16 * lane) = hkB;
-    bf16x4 g1T[2], hkT[2];
+    bf16x4 g1T[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      bf16x4 w2t[4];  // tile (mt, dt) transposed: row m = c, features 16 dt + 4g .. +3
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) w2t[dt] = tr_tile(scrW + 1024 * dt + 8 * mt, 16, lane);
-      f32x4 gh = mfma32(cat8(w2t[0], w2t[1]), g2B[0], zero4());
-      gh = mfma32(cat8(w2t[2], w2t[3]), g2B[1], gh);
-      *(bf16x4*)(scrG + 512 * mt + 8 * lane) = pack4(neta * (gh * Dg[mt]));
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      // token-major copies (tokens 4g..4g+3 of hidden unit m0 + 16mt + c)
-      g1T[mt] = tr_tile(scrG + 512 * mt, 8, lane);
-      hkT[mt] = tr_tile(scrG + 1024 + 8 * mt, 16, lane);
+      f32x4 gh = mfma32(g2B[0], cat8(w2t[mt][0], w2t[mt][1]), zero4());
+      gh = mfma32(g2B[1], cat8(w2t[mt][2], w2t[mt][3]), gh);
+      g1T[mt] = pack4(gh * DgT[mt]);
     }
     // ---- state update: W1 += K^T (-eta G1), W2 += Hk^T (-eta G2).  K^T tile dt
     //      (row d = 16 dt + c, tokens 4g .. 4g+3): lane 16g + j reads token
@@ -432,6 +421,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) W2[mt][dt] = mfma16(hkT[mt], g2T[dt], W2[mt][dt]);
 
+    // ---- Z of block j-1 and the vector-memory work of this step, waited for just
+    //      before the next step's second barrier: Y and Z of block j-1, the gate
+    //      inputs of block j (one register, consumed before it is reloaded: no
+    //      register rotation, which would make the compiler wait at once), block
+    //      j+3 into the buffer that held block j-1 (last read before this step's
+    //      second barrier)
+    const float2 zfin = reduce_part(Zpart);
+    if (j > 0) store_z(j - 1, xo - xstep, x_blk, zfin);
+    x_blk = load_x(j, xo);
+    xo += xstep;
+    if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) & (NSTAGE - 1)));
+
     St_prev = St;
     g1T_prev = cat8(g1T[0], g1T[1]);
     g2T_prev[0] = cat8(g2T[0], g2T[1]);
@@ -439,6 +440,16 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     hkB_prev = hkB;
   }
 
+  // ---- read-out of the last block with the final state (after every wave's last
+  //      reads of Zpart)
+  if (nblk > 0) {
+    bf16x8 w1p[2][2], w2p[4];
+    pack_state(w1p, w2p);
+    __syncthreads();
+    readout(Stage[(nblk - 1) & (NSTAGE - 1)], w1p, w2p);
+    __syncthreads();
+    store_z(nblk - 1, xo - xstep, x_blk, reduce_part(Zpart));
+  }
   // ---- final state.  The lane indices are derived afresh from an opaque copy of
   // the thread index, so that no address term is kept live across the loop.
   {
