@@ -20,6 +20,7 @@ namespace ttt {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -53,6 +54,14 @@ __device__ __forceinline__ bf16x4 zero4b() {
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = (__bf16)0.0f;
   return v;
+}
+
+// Two floats as bf16 (round to nearest even), x in the low half: one conversion.
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  bf16x2 v;
+  v[0] = (__bf16)x;
+  v[1] = (__bf16)y;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x4 pack4(f32x4 x) {

@@ -63,37 +63,21 @@ struct Gelu {
     for (int k = kPhiDeg - 1; k >= 0; --k) q = fmaf(q, sq, kPhiP[k]);
     return fmaf(c, q, 0.5f);
   }
-  static __device__ __forceinline__ void both(float a, float* g, float* dg) {
-    const float p = cdf(a);
-    *g = a * p;
+  // GELU'(a) from a and p = Phi(a)
+  static __device__ __forceinline__ float deriv(float a, float p) {
     const float dens = __builtin_amdgcn_exp2f(fmaf(-0.7213475204444817f * a, a, -1.3257480647361593f));  // phi(a)
-    *dg = fmaf(a, dens, p);
+    return fmaf(a, dens, p);
   }
   static __device__ __forceinline__ float value(float a) { return a * cdf(a); }
 };
 
 // tanh(u) = 1 - 2 / (exp(2u) + 1) (exact identity; saturates to +-1 for large |u|),
 // used for the gate factors tanh(alpha).
-struct GeluTanh {
-  static __device__ __forceinline__ float tanh_u(float u) {
-    const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * u);  // exp(2u)
-    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-  }
-  static __device__ __forceinline__ void both(float a, float* g, float* dg) {
-    const float u = 0.7978845608028654f * fmaf(0.044715f * a, a * a, a);
-    const float th = tanh_u(u);
-    const float du = 0.7978845608028654f * fmaf(3.0f * 0.044715f * a, a, 1.0f);
-    *g = 0.5f * a * (1.0f + th);
-    *dg = fmaf(0.5f * a * du, fmaf(-th, th, 1.0f), 0.5f * (1.0f + th));
-  }
-  static __device__ __forceinline__ float value(float a) {
-    const float u = 0.7978845608028654f * fmaf(0.044715f * a, a * a, a);
-    return 0.5f * a * (1.0f + tanh_u(u));
-  }
-};
+__device__ __forceinline__ float tanh_gate(float u) {
+  const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * u);  // exp(2u)
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
 
-__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return *(const bf16x8*)p; }
-__device__ __forceinline__ bf16x4 ld4(const uint16_t* p) { return *(const bf16x4*)p; }
 
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 v;
@@ -136,7 +120,6 @@ __device__ __forceinline__ bf16x4 tr_tile(const char* base, int stride, int lane
   return ld_tr(base + (16 * (j & 3) + 4 * g + (j >> 2)) * stride);
 }
 
-template <class G>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_mfma_kernel(ScanArgs a) {
   __shared__ f32x4 Ypart[NWAVE][4][64];                            // partial Yhat^T: wave, d-tile, lane
   __shared__ f32x4 Zpart[NWAVE][4][64];                            // partial Z^T
@@ -184,7 +167,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int rd_d = 16 * rd_dt + 4 * (rd_src >> 4) + 2 * rd_p;
   const int ch0 = h * SD + rd_d;
   // gate factors: loop constants used once per step, kept in this thread's LDS slot
-  const float2 tg = make_float2(GeluTanh::tanh_u(a.alpha[ch0]), GeluTanh::tanh_u(a.alpha[ch0 + 1]));
+  const float2 tg = make_float2(tanh_gate(a.alpha[ch0]), tanh_gate(a.alpha[ch0 + 1]));
 
   const int64_t nblk = (Tc + SB - 1) / SB;  // blocks of this launch
   const uint16_t* blocks =
@@ -252,14 +235,28 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   for (int i = 0; i < 2; ++i) g2T_prev[i] = zero8();
   uint32_t x_blk = 0u;  // gate inputs of the block whose Z is finished next
 
+  // -striu of a b x b tile in the D layout (element r: row 4g + r, column c): the
+  // entries with row > column, negated, else 0, as a bf16 operand.  The selects
+  // are kept in fp32 (one conversion per pair afterwards).
+  bool causal[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) causal[r] = 4 * g + r > c;
+  auto causal_neg = [&](f32x4 x) -> bf16x4 {
+    f32x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[r] = causal[r] ? -x[r] : 0.0f;
+      asm("" : "+v"(v[r]));
+    }
+    return pack4(v);
+  };
+
   // Read-out of the block staged at blk_prev with the state whose bf16 operands
   // are w1p / w2p (the state that follows that block):
   //   Aq = Q W1' + eta striu(Q K^T) G1,  Z = GELU(Aq) W2' + eta striu(Hq Hk^T) G2
   // This wave's partial Z^T (its 32 hidden units) goes to Zpart[w].
   auto readout = [&](const uint16_t* blk_prev, const bf16x8 (&w1p)[2][2], const bf16x8 (&w2p)[4]) {
-    bf16x4 sT;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sT[r] = (__bf16)(4 * g + r > c ? -St_prev[r] : 0.0f);
+    const bf16x4 sT = causal_neg(St_prev);
     // K=16 products as K=32 ones: {x, 0} picks the low tile of a pair, {0, x} the high one
     const bf16x8 sT_lo = cat8(sT, zero4b()), sT_hi = cat8(zero4b(), sT);
     const bf16x8 q0 = rd_row8(blk_prev, OFF_Q, g, c, 0), q1 = rd_row8(blk_prev, OFF_Q, g, c, 1);
@@ -270,13 +267,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       aq = mfma32(w1p[1][nt], q1, aq);
       aq = mfma32(g1T_prev, nt ? sT_hi : sT_lo, aq);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Hq[nt][r] = G::value(aq[r]);
+      for (int r = 0; r < 4; ++r) Hq[nt][r] = Gelu::value(aq[r]);
     }
     const bf16x8 hqB = pack8(Hq[0], Hq[1]);
     const f32x4 Pt = mfma32(hkB_prev, hqB, zero4());
-    bf16x4 pT;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pT[r] = (__bf16)(4 * g + r > c ? -Pt[r] : 0.0f);
+    const bf16x4 pT = causal_neg(Pt);
     const bf16x8 pT_lo = cat8(pT, zero4b()), pT_hi = cat8(zero4b(), pT);
     f32x4 zp[4];
 #pragma unroll
@@ -328,26 +323,22 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       St = mfma32(k0, q0, zero4());
       St = mfma32(k1, q1, St);
     }
-    // ---- Hk^T = GELU(A^T) and GELU'(A^T) (both to this wave's LDS slices, for
-    //      the transposed reads); partial Yhat^T = W2^T Hk^T over this wave's 32 hidden units
+    // ---- Hk^T = GELU(A^T) (also to this wave's LDS slice, for the transposed
+    //      read), keeping Phi(A^T) for GELU' between the barriers; partial
+    //      Yhat^T = W2^T Hk^T over this wave's 32 hidden units
     bf16x8 hkB;
+    f32x4 Pa[2];
     {
-      f32x4 Hk[2], Dg[2];
+      f32x4 Hk[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float hv, dv;
-          G::both(At[nt][r], &hv, &dv);
-          Hk[nt][r] = hv;
-          Dg[nt][r] = dv;
+          Pa[nt][r] = Gelu::cdf(At[nt][r]);
+          Hk[nt][r] = At[nt][r] * Pa[nt][r];
         }
       hkB = pack8(Hk[0], Hk[1]);
       HkS[w][lane] = hkB;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) DgS[w][nt][(4 * g + r) * DGS + c] = Dg[nt][r];
       f32x4 yp[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) yp[dt] = mfma32(w2p[dt], hkB, zero4());
@@ -368,12 +359,17 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       const bool tv = rd_t < n;
       const float g2x = tv ? ngs * (y.x - __uint_as_float(vv << 16)) : 0.0f;  // -eta G2
       const float g2y = tv ? ngs * (y.y - __uint_as_float(vv & 0xffff0000u)) : 0.0f;
-      const uint16_t b0 = __builtin_bit_cast(uint16_t, (__bf16)g2x), b1 = __builtin_bit_cast(uint16_t, (__bf16)g2y);
-      *(uint32_t*)&G2a[rd_t * RS + pair_order_pos(rd_d)] = (uint32_t)b0 | ((uint32_t)b1 << 16);
-      G2b[rd_d * TS + rd_t] = b0;
-      G2b[(rd_d + 1) * TS + rd_t] = b1;
+      const uint32_t pk = pack2(g2x, g2y);
+      *(uint32_t*)&G2a[rd_t * RS + pair_order_pos(rd_d)] = pk;
+      G2b[rd_d * TS + rd_t] = (uint16_t)pk;
+      G2b[(rd_d + 1) * TS + rd_t] = (uint16_t)(pk >> 16);
     }
     readout(blk_prev, w1p, w2p);
+    // GELU'(A^T) to this wave's LDS slice as [m][t], read back token-major below
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) DgS[w][nt][(4 * g + r) * DGS + c] = Gelu::deriv(At[nt][r], Pa[nt][r]);
     // W2 tile (mt, dt) transposed: row m = c, features 16 dt + 4g .. +3; Hk in token-major
     // form (tokens 4g .. 4g+3 of hidden unit m0 + 16 mt + c); GELU'(A) at the same places
     bf16x4 w2t[2][4], hkT[2];
@@ -491,7 +487,7 @@ size_t scan_mfma_tile_bytes(int64_t B, int64_t T, int H) {
 // Only the exact (erf) GELU is instantiated: the tanh form runs on the generic scan.
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s) {
   if (a.gelu_tanh) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(scan_mfma_kernel<Gelu>, dim3((unsigned)(a.B * a.H)), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL(scan_mfma_kernel, dim3((unsigned)(a.B * a.H)), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 
