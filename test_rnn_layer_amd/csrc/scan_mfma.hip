@@ -126,8 +126,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // -eta G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
   __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+2
-  // per-wave slices for the transposed reads: bf16 W2 tiles, bf16 Hk^T, fp32 GELU'(A^T) as [m][t]
-  __shared__ bf16x8 W2s[NWAVE][4][64];
+  // per-wave slices for the transposed reads: bf16 Hk^T, fp32 GELU'(A^T) as [m][t]
   __shared__ bf16x8 HkS[NWAVE][64];
   __shared__ __attribute__((aligned(16))) float DgS[NWAVE][2][16 * DGS];
 
@@ -140,8 +139,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int m0 = 32 * w;
   const float ngs = -a.eta * a.gscale;  // -eta times the loss-gradient scale
 
-  // ---- state, D layout: W1 rows d (4 tiles) / cols m (2 tiles), W2 rows m (2 tiles) / cols d (4 tiles)
-  f32x4 W1[4][2], W2[2][4];
+  // ---- state, D layout: W1 rows d (4 tiles) / cols m (2 tiles), W2 rows m (2 tiles) / cols d (4 tiles),
+  //      and W2 once more as its transpose W2T (rows d / cols m), the operand of the
+  //      contraction over d.  Both copies take the same products in the same order at
+  //      every update, so W2T stays exactly the transpose of W2.
+  f32x4 W1[4][2], W2[2][4], W2T[4][2];
   {
     const float* w1 = a.w1_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * SD * SM;
     const float* w2 = a.w2_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * SM * SD;
@@ -153,16 +155,18 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         for (int nt = 0; nt < 2; ++nt) {
           W1[dt][nt][r] = w1[(16 * dt + 4 * g + r) * SM + m0 + 16 * nt + c];
           W2[nt][dt][r] = w2[(m0 + 16 * nt + 4 * g + r) * SD + 16 * dt + c];
+          W2T[dt][nt][r] = w2[(m0 + 16 * nt + c) * SD + 16 * dt + 4 * g + r];
         }
     }
   }
 
   // The two finished values of this lane between the barriers: d-tile rd_dt,
   // source lane rd_src (of each wave's partial tile), elements 2 rd_p, 2 rd_p + 1,
-  // i.e. token rd_t, features rd_d and rd_d + 1.
+  // i.e. token rd_t, features rd_d and rd_d + 1.  A wave reads 512 consecutive
+  // bytes of each partial tile (lane l: bytes 8 l .. 8 l + 7 of its half).
   const int rd_dt = w >> 1;
-  const int rd_src = 32 * (w & 1) + (lane & 31);
-  const int rd_p = lane >> 5;
+  const int rd_src = 32 * (w & 1) + (lane >> 1);
+  const int rd_p = lane & 1;
   const int rd_t = rd_src & 15;
   const int rd_d = 16 * rd_dt + 4 * (rd_src >> 4) + 2 * rd_p;
   const int ch0 = h * SD + rd_d;
@@ -303,12 +307,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const uint16_t* blk = Stage[j & (NSTAGE - 1)];
     const uint16_t* blk_prev = Stage[(j - 1) & (NSTAGE - 1)];
 
-    // ---- bf16 operands of the state that follows block j-1; W2's also to this
-    //      wave's LDS slice, read back transposed between the barriers
+    // ---- bf16 operands of the state that follows block j-1
     bf16x8 w1p[2][2], w2p[4];
     pack_state(w1p, w2p);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) W2s[w][dt][lane] = w2p[dt];
 
     // ---- A^T = W1^T K^T, S^T = K Q^T (block j)
     f32x4 At[2], St;
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) w2t[mt][dt] = tr_tile((const char*)&W2s[w][dt][0] + 8 * mt, 16, lane);
+      for (int dt = 0; dt < 4; ++dt) w2t[mt][dt] = pack4(W2T[dt][mt]);
       hkT[mt] = tr_tile((const char*)&HkS[w][0] + 8 * mt, 16, lane);
       DgT[mt] = *(const f32x4*)&DgS[w][mt][c * DGS + 4 * g];
     }
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       gh = mfma32(g2B[1], cat8(w2t[mt][2], w2t[mt][3]), gh);
       g1T[mt] = pack4(gh * DgT[mt]);
     }
-    // ---- state update: W1 += K^T (-eta G1), W2 += Hk^T (-eta G2).  K^T tile dt
+    // ---- state update: W1 += K^T (-eta G1), W2 += Hk^T (-eta G2) (and W2T += (-eta G2)^T Hk).  K^T tile dt
     //      (row d = 16 dt + c, tokens 4g .. 4g+3): lane 16g + j reads token
     //      4g + j/4, features 16 dt + 4 (j mod 4) .. +3 of the staged block
 #pragma unroll
@@ -415,7 +416,10 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) W2[mt][dt] = mfma16(hkT[mt], g2T[dt], W2[mt][dt]);
+      for (int dt = 0; dt < 4; ++dt) {
+        W2[mt][dt] = mfma16(hkT[mt], g2T[dt], W2[mt][dt]);
+        W2T[dt][mt] = mfma16(g2T[dt], hkT[mt], W2T[dt][mt]);
+      }
 
     // ---- Z of block j-1 and the vector-memory work of this step, waited for just
     //      before the next step's second barrier: Y and Z of block j-1, the gate
