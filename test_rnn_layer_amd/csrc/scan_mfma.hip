@@ -41,7 +41,12 @@ constexpr int NSTAGE = 4;         // token blocks in LDS: j-1 (read-out), j, j+1
 // RS = 72 (144 bytes) so that the 16 rows read by one 16-lane group fall on
 // distinct LDS banks.
 constexpr int RS = SD + 8;  // 72
-constexpr int TS = SB + 4;  // 20: rows of the [feature][token] G2 copy
+constexpr int TS = SB + 8;  // 24: rows of the [feature][token] G2 copy (48 bytes: the 8-byte reads of
+                            // two lane groups fall on distinct banks)
+// Hk slice rows: source lane l at row l + 8 (l / 32), so that the 32 rows a transposed
+// read takes in one lane group pair map to distinct banks
+constexpr int HKS_ROWS = 72;
+__device__ __forceinline__ int hk_row(int l) { return l + 8 * (l >> 5); }
 constexpr int DGS = SB + 4;  // 20: rows of the fp32 [hidden][token] GELU' tiles (bank spread of the column writes)
 constexpr int OFF_Q = 0, OFF_K = SB * RS, OFF_V = 2 * SB * RS;
 constexpr int BLK = 3 * SB * RS;          // 3456 elements, 6912 bytes
@@ -110,24 +115,15 @@ __device__ __forceinline__ bf16x4 ld_tr(const void* lds_addr) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// The transpose of a 16 x 16 tile held in the D layout (lane (g, c), element r:
-// row 4g + r, column c), whose 4 bf16 per lane were stored at base + lane *
-// stride (bytes): lane (g, c) receives row c, columns 4g .. 4g+3 of the tile's
-// transpose, i.e. the tile in the operand layout A[c][4g .. 4g+3].  Lane 16g + j
-// addresses the values stored by lane 16 (j mod 4) + 4g + j/4.
-__device__ __forceinline__ bf16x4 tr_tile(const char* base, int stride, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  return ld_tr(base + (16 * (j & 3) + 4 * g + (j >> 2)) * stride);
-}
-
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_mfma_kernel(ScanArgs a) {
   __shared__ f32x4 Ypart[NWAVE][4][64];                            // partial Yhat^T: wave, d-tile, lane
   __shared__ f32x4 Zpart[NWAVE][4][64];                            // partial Z^T
   __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // -eta G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
   __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+2
-  // per-wave slices for the transposed reads: bf16 Hk^T, fp32 GELU'(A^T) as [m][t]
-  __shared__ bf16x8 HkS[NWAVE][64];
+  // per-wave slices for the transposed reads: bf16 Hk^T (one 8-byte row per source lane
+  // and hidden-unit tile, see hk_row), fp32 GELU'(A^T) as [m][t]
+  __shared__ __attribute__((aligned(16))) bf16x4 HkS[NWAVE][2][HKS_ROWS];
   __shared__ __attribute__((aligned(16))) float DgS[NWAVE][2][16 * DGS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -338,8 +334,10 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
           Pa[nt][r] = Gelu::cdf(At[nt][r]);
           Hk[nt][r] = At[nt][r] * Pa[nt][r];
         }
-      hkB = pack8(Hk[0], Hk[1]);
-      HkS[w][lane] = hkB;
+      const bf16x4 h0 = pack4(Hk[0]), h1 = pack4(Hk[1]);
+      hkB = cat8(h0, h1);
+      HkS[w][0][hk_row(lane)] = h0;
+      HkS[w][1][hk_row(lane)] = h1;
       f32x4 yp[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) yp[dt] = mfma32(w2p[dt], hkB, zero4());
@@ -379,7 +377,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) w2t[mt][dt] = pack4(W2T[dt][mt]);
-      hkT[mt] = tr_tile((const char*)&HkS[w][0] + 8 * mt, 16, lane);
+      // transpose of the D-layout tile (source lane (g', c') holds hidden units
+      // 4g' .. 4g'+3 of token c'): lane 16g + c addresses the row of source lane
+      // 16 (c mod 4) + 4g + c/4, so that (see ld_tr) lane (g, c) receives hidden unit
+      // c at tokens 4g .. 4g+3
+      hkT[mt] = ld_tr(&HkS[w][mt][hk_row(16 * (c & 3) + 4 * g + (c >> 2))]);
       DgT[mt] = *(const f32x4*)&DgS[w][mt][c * DGS + 4 * g];
     }
 
