@@ -79,7 +79,7 @@ extern "C" {
 #define TTT_ALGO_AUTO 0    /* fastest kernel that supports the shape and dtype */
 #define TTT_ALGO_GENERIC 1 /* fp32 VALU scan, any supported shape */
 #define TTT_ALGO_MFMA 2    /* bf16-operand MFMA scan, fp32 state: bf16 io, erf GELU,
-                              d = 64, m = 256, b = 16 */
+                              d = 64, m = 256, b = 16, T < 2^31 */
 #define TTT_ALGO_COOP 3    /* per-token fp32 scan whose state (512 KB per head) is split
                               over 8 cooperating workgroups: d = 128, m = 512, b = 1.
                               Needs B*H*8 co-resident workgroups (cooperative launch);

@@ -139,9 +139,10 @@ int32_t check_config(const ttt_mlp_config* c) {
 }
 
 // The MFMA scan implements the exact (erf) GELU; the tanh form runs on the generic kernel.
+// It indexes token rows of one sequence with 32-bit integers (T < 2^31).
 bool mfma_possible(const ttt_mlp_config* c) {
   return c->io_dtype == TTT_BF16 && c->gelu == TTT_GELU_ERF && ttt::scan_mfma_supported(c->d, c->m, c->b) &&
-         ((int64_t)c->H * c->d) % 8 == 0;
+         ((int64_t)c->H * c->d) % 8 == 0 && c->T < ((int64_t)1 << 31);
 }
 
 bool coop_possible(const ttt_mlp_config* c) { return ttt::scan_coop_supported(c->d, c->m, c->b, c->T); }

@@ -172,10 +172,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int64_t nblk = (Tc + SB - 1) / SB;  // blocks of this launch
   const uint16_t* blocks =
       (const uint16_t*)a.qkv_tiles + (((int64_t)s * a.H + h) * ((T + SB - 1) / SB) + p0 / SB) * BLK;
-  const uint16_t* xin = (const uint16_t*)a.xin;
-  uint16_t* yout = (uint16_t*)a.y;
-  auto tok_index = [&](int64_t pos) -> int64_t { return a.reverse ? T - 1 - pos : pos; };
-  auto block_n = [&](int64_t j) -> int { return (int)((Tc - SB * j) < SB ? (Tc - SB * j) : SB); };
+  // rows of this launch and of the sequence fit 32 bits (the MFMA path is chosen for T < 2^31 only)
+  const int Tc32 = (int)Tc, p032 = (int)p0, T32 = (int)T;
+  auto block_n = [&](int64_t j) -> int { return min(Tc32 - SB * (int)j, SB); };
 
   // token blocks: direct global -> LDS loads three steps ahead of use (no registers);
   // lane i of a wave fills bytes [16 i, 16 i + 16) of the wave's 1 KB slice.  The
@@ -193,13 +192,28 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(src) : "memory", "m0");
   };
   static_assert(BLK_CHUNKS <= NTHR, "one 16-byte chunk per thread");
-  // element offset (in X, Y, Z) of this lane's first finished value in block j:
-  // moves by +-16 D per block
-  const int64_t xstep = (a.reverse ? -(int64_t)SB : (int64_t)SB) * D;
-  int64_t xo = ((int64_t)s * T + tok_index(p0 + rd_t)) * D + ch0;
-  auto load_x = [&](int64_t jx, int64_t off) -> uint32_t {  // two bf16 gate inputs of this lane's values
-    if (SB * jx + rd_t >= Tc) return 0u;
-    return *(const uint32_t*)(xin + off);
+  // Gate inputs and outputs of block jb go through buffer descriptors that span
+  // the block's valid token rows (from its lowest valid token): the hardware
+  // zero-fills loads and drops stores outside them, so the last, partial block of
+  // a launch needs no branch, and the per-block address arithmetic is scalar.  In
+  // that span this lane's pair sits at row rd_t (forward) or nv - 1 - rd_t (reverse),
+  // a negative row counting as out of range.
+  constexpr int kRawBufferWord3 = 0x00020000;  // 32-bit data format, raw (untyped) access
+  const uint16_t* x_seq = (const uint16_t*)a.xin + (int64_t)s * T * D;
+  uint16_t* y_seq = (uint16_t*)a.y + (int64_t)s * T * D;
+  float* z_seq = a.z ? a.z + (int64_t)s * T * D : a.z;
+  auto io_elem0 = [&](int64_t jb, int nv) -> int64_t {  // element offset of the lowest valid row
+    const int p = p032 + SB * (int)jb;
+    return (int64_t)(a.reverse ? T32 - p - nv : p) * D;
+  };
+  auto io_voff = [&](int nv, int elem_bytes) -> int {
+    return ((a.reverse ? nv - 1 - rd_t : rd_t) * D + ch0) * elem_bytes;
+  };
+  auto load_x = [&](int64_t jb) -> uint32_t {  // two bf16 gate inputs of this lane's values
+    const int nv = block_n(jb);
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(x_seq + io_elem0(jb, nv)), 0, nv * D * 2, kRawBufferWord3);
+    return __builtin_amdgcn_raw_buffer_load_b32(rx, io_voff(nv, 2), 0, 0);
   };
   // the two values of a wave-summed partial tile (Ypart or Zpart) this lane
   // finishes: all loads are issued before the sum (fixed order of the sums)
@@ -215,14 +229,19 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     }
     return acc;
   };
-  auto store_z = [&](int64_t jz, int64_t o, uint32_t xv, float2 z) {
-    if (SB * jz + rd_t < Tc) {
-      const float x0 = __uint_as_float(xv << 16), x1 = __uint_as_float(xv & 0xffff0000u);
-      const __bf16 y0 = (__bf16)fmaf(tg.x, z.x, x0), y1 = (__bf16)fmaf(tg.y, z.y, x1);
-      *(uint32_t*)(yout + o) = (uint32_t)__builtin_bit_cast(uint16_t, y0) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, y1) << 16);
-      if (a.z) *(float2*)(a.z + o) = z;
-    }
+  // y = x + tanh(alpha) z of block jb (bf16), and z itself when it is requested
+  // (without it the z descriptor spans nothing and its store is dropped); nv = 0
+  // drops both
+  auto store_z = [&](int64_t jb, int nv, uint32_t xv, float2 z) {
+    const int64_t e0 = io_elem0(jb, nv);
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(y_seq + e0), 0, nv * D * 2, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(z_seq ? z_seq + e0 : z_seq), 0, z_seq ? nv * D * 4 : 0, kRawBufferWord3);
+    const float x0 = __uint_as_float(xv << 16), x1 = __uint_as_float(xv & 0xffff0000u);
+    __builtin_amdgcn_raw_buffer_store_b32(pack2(fmaf(tg.x, z.x, x0), fmaf(tg.y, z.y, x1)), ry, io_voff(nv, 2), 0, 0);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(z.x), __float_as_uint(z.y)}, rz, io_voff(nv, 4), 0, 0);
   };
 
   // carried from block j-1 to its read-out during block j
@@ -430,9 +449,16 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     //      j+3 into the buffer that held block j-1 (last read before this step's
     //      second barrier)
     const float2 zfin = reduce_part(Zpart);
-    if (j > 0) store_z(j - 1, xo - xstep, x_blk, zfin);
-    x_blk = load_x(j, xo);
-    xo += xstep;
+    store_z(j - 1, j > 0 ? block_n(j - 1) : 0, x_blk, zfin);  // nothing to store at j = 0
+    x_blk = load_x(j);
+    // issue order after the second barrier: every matrix-core product followed by
+    // two vector-ALU instructions, so that the reduction, gate and packing work
+    // runs beside the products instead of after them
+#pragma unroll
+    for (int i = 0; i < 28; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
     if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) & (NSTAGE - 1)));
 
     St_prev = St;
@@ -450,7 +476,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     __syncthreads();
     readout(Stage[(nblk - 1) & (NSTAGE - 1)], w1p, w2p);
     __syncthreads();
-    store_z(nblk - 1, xo - xstep, x_blk, reduce_part(Zpart));
+    store_z(nblk - 1, block_n(nblk - 1), x_blk, reduce_part(Zpart));
   }
   // ---- final state.  The lane indices are derived afresh from an opaque copy of
   // the thread index, so that no address term is kept live across the loop.

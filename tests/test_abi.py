@@ -97,6 +97,9 @@ def test_algo_selection():
     assert L.select_algo(cfg()) == "mfma"
     assert L.select_algo(cfg(algo="generic")) == "generic"
     assert L.select_algo(L.make_config(1, 10, 1, 16, 64, 1, 0.1, io_dtype="f32")) == "generic"
+    # the MFMA scan indexes token rows with 32-bit integers: longer sequences use the generic scan
+    assert L.select_algo(cfg(T=(1 << 31) - 1)) == "mfma"
+    assert L.select_algo(cfg(T=1 << 31)) == "generic"
     with pytest.raises(L.TTTError) as e:
         L.select_algo(cfg(b=8, algo="mfma"))
     assert e.value.status == L.TTT_ERR_UNSUPPORTED
