@@ -1,6 +1,8 @@
-"""HBM traffic of the scan kernel from rocprofv3 counters.
+"""Counters of the scan and projection kernels from rocprofv3 (HBM traffic, and
+the shader sequencer's issue, matrix-core and LDS counters).
 
-    # one counter per run (each run: a known-size copy, then one layer call)
+HBM traffic (one counter per run; each run: a known-size copy, then one layer call):
+
     rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d DIR_F -o run -- \
         python3 -m test_rnn_layer_amd.profile_counters run
     rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d DIR_W -o run -- \
@@ -10,9 +12,30 @@
 `run` makes one device-to-device copy of COPY_BYTES (the runtime's copy
 kernel reads and writes exactly that many bytes), then one ttt_mlp_bidir
 call of the workload.  `summarize` scales each counter by what it read for
-the copy, and writes the scan kernel's bytes per launch into
-profiles/scan_traffic.json, keyed by kernel, with a digest of the scan
-sources so that a later kernel change invalidates it.
+the copy, writes each kernel's bytes per launch into
+profiles/scan_traffic.json, keyed by kernel, with a digest of the kernel's
+sources so that a later kernel change invalidates it, and the table
+profiles/scan_mfma_proj_tiles_bidir307k_traffic.md.
+
+Sequencer counters (three passes, SQ_PASSES; each fits the per-run limit of
+eight SQ counters):
+
+    rocprofv3 --pmc <SQ_PASSES[i]> --kernel-trace --output-format csv -d DIR_i -o run -- \
+        python3 -m test_rnn_layer_amd.profile_counters run
+    python3 -m test_rnn_layer_amd.profile_counters summarize-sq DIR_1 DIR_2 DIR_3
+
+`summarize-sq` writes profiles/scan_mfma_bidir307k_sq_counters.md: per scan
+step, the cycles each unit is busy (vector ALU, matrix core, LDS), LDS bytes
+and bank-conflict cycles, waits, and instruction counts.
+
+Kernel times (the bench command under the kernel trace; its JSON line is kept
+beside the trace):
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- \
+        python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > DIR/bench.json
+    python3 -m test_rnn_layer_amd.profile_counters summarize-stats DIR
+
+`summarize-stats` writes profiles/scan_mfma_proj_tiles_bidir307k_stats.md.
 """
 from __future__ import annotations
 
@@ -25,6 +48,13 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30
+SQ_PASSES = [
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA SQ_WAIT_INST_ANY "
+    "SQ_WAIT_INST_LDS SQ_INSTS_VALU GRBM_GUI_ACTIVE",
+    "SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
+    "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU_MFMA_MOPS_BF16",
+    "SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_INSTS_LDS_STORE_BANDWIDTH SQ_INSTS_VALU_TRANS_F32 SQ_WAIT_ANY SQ_BUSY_CU_CYCLES",
+]
 KERNELS = {"scan_mfma": "scan_mfma_kernel", "scan_generic": "scan_generic_kernel", "scan_coop": "scan_coop_kernel",
            "projection": "proj_tiles_kernel"}
 # the sources each kernel is built from: its counters are stale once any of them changes
@@ -122,7 +152,172 @@ def summarize(dir_fetch: str, dir_write: str, out_json: str | None = None):
                       "source_digest": source_digest(KERNEL_SOURCES[k])}
     out_json = out_json or os.path.join(ROOT, "profiles", "scan_traffic.json")
     json.dump(rec, open(out_json, "w"), indent=1)
+    _traffic_markdown(rec, fetch["copy"], write["copy"], dir_fetch, dir_write)
     print(json.dumps(rec, indent=1))
+
+
+def _launch_stats(d: str):
+    """Per kernel: dispatch count, mean duration (ms) and resource columns, from the
+    kernel trace of a counter run."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    out = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = next((k for k, sub in KERNELS.items() if sub in r.get("Kernel_Name", "")), None)
+            if key is None:
+                continue
+            e = out.setdefault(key, {"n": 0, "ns": 0.0, "row": r})
+            e["n"] += 1
+            e["ns"] += float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def _traffic_markdown(rec, copy_f, copy_w, dir_f, dir_w):
+    from test_rnn_layer_amd import workloads as W
+    wl = W.WORKLOADS["bidir307k"]
+    launches = _launch_stats(dir_f)
+    tok = wl.B * wl.T
+    lines = [
+        "# HBM traffic per launch, bidir307k (rocprofv3 counters)", "",
+        f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ/Y, fp32 state; "
+        "one `ttt_mlp_bidir` call (each direction runs as chunked launches of the projection and the scan).", "",
+        "Commands (repo root, MI355X). The copy, of 1 GiB, comes first in each run:", "",
+        "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+        "python3 -m test_rnn_layer_amd.profile_counters run",
+        "    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d gpurun_out/pmc_write -o run -- "
+        "python3 -m test_rnn_layer_amd.profile_counters run",
+        "    python3 -m test_rnn_layer_amd.profile_counters summarize gpurun_out/pmc_fetch gpurun_out/pmc_write", "",
+        f"**Calibration.** The runtime's copy of 1 GiB read FETCH_SIZE = {copy_f:,.1f} and WRITE_SIZE = "
+        f"{copy_w:,.1f} (KiB as reported): bytes = FETCH_SIZE × {COPY_BYTES / copy_f:,.1f} and WRITE_SIZE × "
+        f"{COPY_BYTES / copy_w:,.1f}.", "",
+        "| Kernel | Launches | Read per launch | Written per launch | Whole call (read + written) | Algorithmic, whole call |",
+        "|---|---|---|---|---|---|",
+    ]
+    algo = {"scan_mfma": (2 * tok * wl.D * 2 * 3 + 2 * tok * wl.D * 2 + 2 * tok * wl.D * 2,
+                          "token blocks Q, K, V read + gate input read + Y written, both directions"),
+            "projection": (2 * (tok * wl.D * 2 + 3 * wl.D * wl.D * 2 + 3 * tok * wl.D * 2),
+                           "X read + θ read + token blocks written, both directions")}
+    for k, e in rec.items():
+        n = launches.get(k, {}).get("n", 0)
+        a, what = algo.get(k, (0, ""))
+        lines.append(f"| `{KERNELS[k]}` | {n} | {e['fetch_bytes'] / 1e9:.3f} GB | {e['write_bytes'] / 1e9:.3f} GB | "
+                     f"{e['bytes_per_launch'] * n / 1e9:.2f} GB | {a / 1e9:.2f} GB ({what}) |")
+    lines += ["", "Digests of the sources each row was taken on (profiles/scan_traffic.json): " +
+              ", ".join(f"{k} {e['source_digest']}" for k, e in rec.items()) + "."]
+    open(os.path.join(ROOT, "profiles", "scan_mfma_proj_tiles_bidir307k_traffic.md"), "w").write(
+        "\n".join(lines) + "\n")
+
+
+def _sq_totals(dirs):
+    """Sum of each counter over all dispatches of each kernel, across the pass directories."""
+    tot = {}
+    for d in dirs:
+        for r in _counter_rows(d):
+            key = next((k for k, sub in KERNELS.items() if sub in r.get("Kernel_Name", "")), None)
+            if key is None:
+                continue
+            t = tot.setdefault(key, {})
+            t[r["Counter_Name"]] = t.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return tot
+
+
+def summarize_sq(dirs, out_md: str | None = None):
+    from test_rnn_layer_amd import workloads as W
+    wl = W.WORKLOADS["bidir307k"]
+    tot = _sq_totals(dirs)["scan_mfma"]
+    launches = _launch_stats(dirs[0])["scan_mfma"]
+    row = launches["row"]
+    nblk = (wl.T + wl.b - 1) // wl.b
+    wg = wl.B * wl.H                      # workgroups (one per sequence and head), 8 waves, 4 SIMDs each
+    cu_steps = wg * 2 * nblk              # both directions
+    wave_steps = cu_steps * 8
+    simd_steps = cu_steps * 4
+    q = 4.0                               # quad-cycle counters
+    step = tot["SQ_WAVE_CYCLES"] * q / wave_steps      # cycles a wave spends per step
+    dur_ns = launches["ns"]
+    clock = tot["GRBM_GUI_ACTIVE"] / 8 / dur_ns      # GHz: summed over the 8 XCDs
+    valu = tot["SQ_ACTIVE_INST_VALU"] * q / wave_steps * 2    # two waves per SIMD
+    mfma = tot["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_steps
+    coex = tot["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_steps
+    lds = tot["SQ_LDS_IDX_ACTIVE"] / cu_steps
+    bank = tot["SQ_LDS_BANK_CONFLICT"] / cu_steps
+    lds_bytes = (tot["SQ_INSTS_LDS_LOAD_BANDWIDTH"] + tot["SQ_INSTS_LDS_STORE_BANDWIDTH"]) * 64 / cu_steps
+    mops = tot["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / cu_steps
+    pct = lambda x: f"{100 * x / step:.0f}%"
+    lines = [
+        "# Sequencer counters of `scan_mfma_kernel`, bidir307k", "",
+        f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}; one `ttt_mlp_bidir` call: "
+        f"{launches['n']} scan launches, {wg} workgroups of 8 waves each (one CU per head), "
+        f"{2 * nblk:,} steps of 16 tokens per workgroup.", "",
+        "Commands (repo root, MI355X), one run per counter set:", "",
+    ]
+    for i, p in enumerate(SQ_PASSES):
+        lines.append(f"    rocprofv3 --pmc {p} --kernel-trace --output-format csv -d gpurun_out/pmc_sq{i + 1} -o run -- "
+                     "python3 -m test_rnn_layer_amd.profile_counters run")
+    lines += [f"    python3 -m test_rnn_layer_amd.profile_counters summarize-sq " +
+              " ".join(f"gpurun_out/pmc_sq{i + 1}" for i in range(len(SQ_PASSES))), "",
+              f"Kernel resources (kernel trace): scratch {row.get('Scratch_Size')} B per lane, LDS "
+              f"{row.get('LDS_Block_Size')} B per workgroup (the build refuses any register spill).", "",
+              f"A step takes {step:,.0f} cycles of a wave ({step / clock / 1e3:.2f} µs at the {clock:.2f} GHz that "
+              f"GRBM_GUI_ACTIVE over the kernels' duration gives).", "",
+              "| Per step | Value | Share of the step |", "|---|---|---|",
+              f"| vector ALU busy, per SIMD (2 waves) | {valu:,.0f} cycles | {pct(valu)} |",
+              f"| matrix core busy, per SIMD | {mfma:,.0f} cycles | {pct(mfma)} |",
+              f"| of which beside a vector-ALU issue (co-execution) | {coex:,.0f} cycles | {pct(coex)} |",
+              f"| LDS busy, per CU | {lds:,.0f} cycles | {pct(lds)} |",
+              f"| of which bank-conflict stalls | {bank:,.0f} cycles | {pct(bank)} |",
+              f"| LDS bytes moved, per CU | {lds_bytes / 1024:,.1f} KiB | — |",
+              f"| wave waiting to issue (any / LDS), per wave | {tot['SQ_WAIT_INST_ANY'] * q / wave_steps:,.0f} / "
+              f"{tot['SQ_WAIT_INST_LDS'] * q / wave_steps:,.0f} cycles | — |",
+              f"| instructions per wave: vector ALU (incl. matrix) / matrix / LDS / scalar | "
+              f"{tot['SQ_INSTS_VALU'] / wave_steps:.0f} / {tot['SQ_INSTS_MFMA'] / wave_steps:.0f} / "
+              f"{tot['SQ_INSTS_LDS'] / wave_steps:.0f} / {tot['SQ_INSTS_SALU'] / wave_steps:.0f} | — |",
+              f"| transcendental instructions per wave | {tot['SQ_INSTS_VALU_TRANS_F32'] / wave_steps:.1f} | — |",
+              f"| bf16 matrix flops per CU (counter) | {mops / 1e6:.3f} M | — |", ""]
+    out_md = out_md or os.path.join(ROOT, "profiles", "scan_mfma_bidir307k_sq_counters.md")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_stats(d: str, out_md: str | None = None):
+    from test_rnn_layer_amd import workloads as W
+    wl = W.WORKLOADS["bidir307k"]
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    bench = json.loads(open(os.path.join(d, "bench.json")).read().strip().splitlines()[-1])
+    steps, warm = bench["steps"], bench["warmup"]
+    calls = steps + warm
+    tok = wl.B * wl.T
+    lines = [
+        "# Kernel time, bidir307k (one ttt_mlp_bidir call = both directions, each as chunked projection and scan launches)",
+        "",
+        f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ/Y, fp32 state; "
+        f"{steps} timed + {warm} warm-up calls under the trace.", "",
+        "Commands (repo root, MI355X):", "",
+        f"    rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
+        f"python3 bench.py --steps {steps} --warmup {warm} --no-cpu-baseline > {d}/bench.json",
+        f"    python3 -m test_rnn_layer_amd.profile_counters summarize-stats {d}", "",
+        "| Kernel | Launches | Average per launch | Per call | Share of kernel time |", "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        name = r["Name"].replace("ttt::(anonymous namespace)::", "")
+        n = int(r["Calls"])
+        lines.append(f"| `{name}` | {n} | {float(r['AverageNs']) / 1e6:.3f} ms | "
+                     f"{float(r['TotalDurationNs']) / 1e6 / calls:.2f} ms | {float(r['Percentage']):.1f}% |")
+    rf = bench["roofline"]
+    lines += ["", f"The bench line of the same run: {bench['ms_per_step']:.2f} ms per call "
+              f"({bench['value'] / 1e6:.3f} M tokens/s, {100 * bench['layer_roofline']['frac']:.1f}% of the layer "
+              f"roofline R = {bench['layer_roofline']['R_ms']:.2f} ms); the scan's launches averaged "
+              f"{rf['avg_launch_ms']:.3f} ms from HIP events on their stream, "
+              f"{rf['flops_per_launch'] / 1e9:.1f} GFLOP each, {rf['achieved']:.1f} TFLOP/s. The projection runs on "
+              "a second stream beside the scan; the call's time is the scan's plus the first projection chunk of "
+              "each direction.",
+              f"Tokens per call: {tok:,} (both directions over every token)."]
+    out_md = out_md or os.path.join(ROOT, "profiles", "scan_mfma_proj_tiles_bidir307k_stats.md")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":
@@ -131,6 +326,12 @@ if __name__ == "__main__":
         run(*sys.argv[2:3])
     elif len(sys.argv) >= 4 and sys.argv[1] == "summarize":
         summarize(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 3 and sys.argv[1] == "summarize-stats":
+        summarize_stats(sys.argv[2])
+    elif len(sys.argv) >= 3 and sys.argv[1] == "summarize-sq":
+        summarize_sq(sys.argv[2:])
     else:
         print(__doc__)
         sys.exit(2)
+
+
