@@ -86,7 +86,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="bidir307k")
     ap.add_argument("--algo", default="auto", choices=["auto", "generic", "mfma"])
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-tokens", type=int, default=24576)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

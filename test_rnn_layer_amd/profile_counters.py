@@ -31,7 +31,7 @@ and bank-conflict cycles, waits, and instruction counts.
 Kernel times (the bench command under the kernel trace; its JSON line is kept
 beside the trace):
 
-    rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- \
+    mkdir -p DIR && rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- \
         python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > DIR/bench.json
     python3 -m test_rnn_layer_amd.profile_counters summarize-stats DIR
 
@@ -296,7 +296,7 @@ def summarize_stats(d: str, out_md: str | None = None):
         f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ/Y, fp32 state; "
         f"{steps} timed + {warm} warm-up calls under the trace.", "",
         "Commands (repo root, MI355X):", "",
-        f"    rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
+        f"    mkdir -p {d} && rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
         f"python3 bench.py --steps {steps} --warmup {warm} --no-cpu-baseline > {d}/bench.json",
         f"    python3 -m test_rnn_layer_amd.profile_counters summarize-stats {d}", "",
         "| Kernel | Launches | Average per launch | Per call | Share of kernel time |", "|---|---|---|---|---|",
