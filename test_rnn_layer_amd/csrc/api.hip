@@ -306,6 +306,7 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
 struct Side {
   hipStream_t stream = nullptr;
   std::vector<hipEvent_t> events;
+  int cus = 0;  // compute units of the device
 };
 std::mutex g_side_mu;  // held while a call enqueues: events are reused between calls
 std::map<int, Side> g_side;
@@ -317,6 +318,8 @@ hipError_t side_for_device(Side** out, size_t n_events) {
   Side& sd = g_side[dev];
   if (!sd.stream) {
     e = hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking);  // default priority
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&sd.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
   }
   while (sd.events.size() < n_events) {
@@ -351,6 +354,18 @@ Chunking chunking(int64_t T) {
   return ch;
 }
 
+// Projection workgroups beside the scan: at most this many, and no more than the
+// CUs the scan leaves free (a workgroup takes a whole CU's LDS, and one that
+// waits for a CU would run its share of tiles after the others); no cap when
+// fewer than kProjMinWorkgroups are free.
+constexpr int kProjWorkgroupsBesideScan = 160, kProjMinWorkgroups = 64;
+
+int proj_workgroups_beside_scan(int cus, int64_t scan_workgroups) {
+  const int64_t free_cus = (int64_t)cus - scan_workgroups;
+  const int64_t cap = std::min<int64_t>(kProjWorkgroupsBesideScan, free_cus) / 8 * 8;
+  return cap >= kProjMinWorkgroups ? (int)cap : 0;
+}
+
 struct Direction {
   const void* xin;
   const float* alpha;
@@ -372,6 +387,7 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
   hipError_t e = side_for_device(&sd, 2 + 2 * (size_t)C * ndir);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
   hipStream_t S2 = sd->stream;
+  const int proj_wg = proj_workgroups_beside_scan(sd->cus, c->B * c->H);
   hipEvent_t* ev = sd->events.data();
   hipEvent_t ev_start = ev[0], ev_end = ev[1];
   auto ev_proj = [&](int d, int64_t k) { return ev[2 + (2 * d) * C + k]; };
@@ -402,6 +418,9 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
       ttt::ProjArgs pa = proj_args(c, pl, D.xin, theta, D.reverse, ws);
       pa.tt0 = D.reverse ? T - p1 : p0;
       pa.tt1 = D.reverse ? T - p0 : p1;
+      // beside the scan, the projection runs on few enough CUs that its power draw
+      // does not pull the shared clock down (the first chunk, exposed, takes them all)
+      if (k > 0) pa.max_wg = proj_wg;
       TTT_TRY(timed_launch(TTT_KERNEL_PROJECT, S2, [&] { return ttt::launch_project_mfma(pa, 1, S2); }),
               "projection launch");
       if (k == C - 1) TTT_TRY(ttt::launch_zero_block_padding(pa, S2), "padding launch");

@@ -17,6 +17,8 @@ struct ProjArgs {
   int32_t reverse;    // token-block layout only: blocks follow the reversed sequence
   int32_t blk_elems;  // token-block layout only: bf16 elements per 16-token block
   int64_t tt0, tt1;   // token-block GEMM only: tokens [tt0, tt1) of every sequence (others: 0, T)
+  int32_t max_wg;     // token-block GEMM only: at most this many workgroups, each taking several
+                      // tiles in turn (0: one workgroup per tile)
 };
 
 // fp32 output, [3, B, H, T, d] (VALU kernel, any dtype and shape).

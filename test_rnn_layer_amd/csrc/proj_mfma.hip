@@ -11,6 +11,8 @@
 //
 // Two epilogues: fp32 [3, B, H, T, d] (inspection / generic scan) and the
 // bf16 token-block layout the MFMA scan reads (see scan_mfma.hip).
+#include <algorithm>
+
 #include "internal.h"
 #include "mfma_common.h"
 
@@ -156,112 +158,118 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int g = lane >> 4, c = lane & 15;
   const int wm = w >> 2, wn = w & 3;
 
-  // tile of this workgroup: XCD-contiguous ranges, grouped 8 m-tiles at a time
+  // tiles: XCD-contiguous ranges (workgroup b runs on XCD b mod 8), grouped 8
+  // m-tiles at a time; the workgroups of an XCD take its range in turn
   const int total = mtiles * ntiles;
   const int per_xcd = (total + 7) / 8;
-  const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (t >= total) return;
-  const int group = t / (T_GROUP_M * ntiles);
-  const int first_m = group * T_GROUP_M;
-  const int gm = min(mtiles - first_m, T_GROUP_M);
-  const int rem = t - group * T_GROUP_M * ntiles;
-  const int mt = first_m + rem % gm;
-  const int nt = rem / gm;
-  const int64_t m0 = (int64_t)mt * T_BM;
-  const int n0 = nt * T_BN;
-  const uint16_t* X = (const uint16_t*)a.X;
-  const uint16_t* Th = (const uint16_t*)a.theta;
+  const int slots = (int)(gridDim.x / 8);
+  for (int ti = (int)(blockIdx.x / 8); ti < per_xcd; ti += slots) {
+    const int t = (int)(blockIdx.x % 8) * per_xcd + ti;
+    if (t >= total) break;
+    const int group = t / (T_GROUP_M * ntiles);
+    const int first_m = group * T_GROUP_M;
+    const int gm = min(mtiles - first_m, T_GROUP_M);
+    const int rem = t - group * T_GROUP_M * ntiles;
+    const int mt = first_m + rem % gm;
+    const int nt = rem / gm;
+    const int64_t m0 = (int64_t)mt * T_BM;
+    const int n0 = nt * T_BN;
+    const uint16_t* X = (const uint16_t*)a.X;
+    const uint16_t* Th = (const uint16_t*)a.theta;
 
-  // direct loads of one K-step: per matrix 256 rows x 8 chunks; instruction i of
-  // wave w fills LDS rows 8 (8 i + w) .. +8, lane -> row + lane / 8, chunk lane % 8
-  int64_t xrow[4];  // X row of this lane's A rows (-1 past the end)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t ga = m0 + 8 * (8 * i + w) + (lane >> 3);
-    xrow[i] = ga < M ? (ga / Tw) * a.T + a.tt0 + ga % Tw : -1;
-  }
-  auto issue = [&](int k0, int buf) {
-    uint16_t* base = smem + buf * T_STAGE;
-#pragma unroll
+    // direct loads of one K-step: per matrix 256 rows x 8 chunks; instruction i of
+    // wave w fills LDS rows 8 (8 i + w) .. +8, lane -> row + lane / 8, chunk lane % 8
+    int64_t xrow[4];  // X row of this lane's A rows (-1 past the end)
+  #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 8 * (8 * i + w) + (lane >> 3);
-      const int gch = swz(row, lane & 7);
-      uint16_t* ldsA = base + (8 * (8 * i + w)) * T_BK;
-      uint16_t* ldsB = base + T_BM * T_BK + (8 * (8 * i + w)) * T_BK;
-      const int gb = n0 + row;
-      if (xrow[i] >= 0)
-        __builtin_amdgcn_global_load_lds((const void*)(X + xrow[i] * K + k0 + 8 * gch),
-                                         (__attribute__((address_space(3))) void*)ldsA, 16, 0, 0);
-      if (gb < N)
-        __builtin_amdgcn_global_load_lds((const void*)(Th + (int64_t)gb * K + k0 + 8 * gch),
-                                         (__attribute__((address_space(3))) void*)ldsB, 16, 0, 0);
+      const int64_t ga = m0 + 8 * (8 * i + w) + (lane >> 3);
+      xrow[i] = ga < M ? (ga / Tw) * a.T + a.tt0 + ga % Tw : -1;
     }
-  };
-
-  f32x4 acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-
-  const int nk = K / T_BK;
-  issue(0, 0);
-  for (int ks = 0; ks < nk; ++ks) {
-    vmem_done();  // this wave's loads of step ks have landed
-    __syncthreads();  // ... everyone's, and everyone is done with step ks - 1
-    if (ks + 1 < nk) issue((ks + 1) * T_BK, (ks + 1) & 1);
-    const uint16_t* As = smem + (ks & 1) * T_STAGE;
-    const uint16_t* Bs = As + T_BM * T_BK;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[8], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = wm * 128 + i * 16 + c;
-        af[i] = *(const bf16x8*)(As + row * T_BK + 8 * swz(row, 4 * kk + g));
+    auto issue = [&](int k0, int buf) {
+      uint16_t* base = smem + buf * T_STAGE;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (8 * i + w) + (lane >> 3);
+        const int gch = swz(row, lane & 7);
+        uint16_t* ldsA = base + (8 * (8 * i + w)) * T_BK;
+        uint16_t* ldsB = base + T_BM * T_BK + (8 * (8 * i + w)) * T_BK;
+        const int gb = n0 + row;
+        if (xrow[i] >= 0)
+          __builtin_amdgcn_global_load_lds((const void*)(X + xrow[i] * K + k0 + 8 * gch),
+                                           (__attribute__((address_space(3))) void*)ldsA, 16, 0, 0);
+        if (gb < N)
+          __builtin_amdgcn_global_load_lds((const void*)(Th + (int64_t)gb * K + k0 + 8 * gch),
+                                           (__attribute__((address_space(3))) void*)ldsB, 16, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 64 + j * 16 + c;
-        bfr[j] = *(const bf16x8*)(Bs + row * T_BK + 8 * swz(row, 4 * kk + g));
+    };
+
+    f32x4 acc[8][4];
+  #pragma unroll
+    for (int i = 0; i < 8; ++i)
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
+
+    const int nk = K / T_BK;
+    issue(0, 0);
+    for (int ks = 0; ks < nk; ++ks) {
+      vmem_done();  // this wave's loads of step ks have landed
+      __syncthreads();  // ... everyone's, and everyone is done with step ks - 1
+      if (ks + 1 < nk) issue((ks + 1) * T_BK, (ks + 1) & 1);
+      const uint16_t* As = smem + (ks & 1) * T_STAGE;
+      const uint16_t* Bs = As + T_BM * T_BK;
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 af[8], bfr[4];
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = wm * 128 + i * 16 + c;
+          af[i] = *(const bf16x8*)(As + row * T_BK + 8 * swz(row, 4 * kk + g));
+        }
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = wn * 64 + j * 16 + c;
+          bfr[j] = *(const bf16x8*)(Bs + row * T_BK + 8 * swz(row, 4 * kk + g));
+        }
+  #pragma unroll
+        for (int i = 0; i < 8; ++i)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
     }
-  }
 
-  // ---- epilogue: this wave's 128 x 64 sub-tile as bf16 rows in LDS, then 16-byte stores
-  __syncthreads();
-  uint16_t* ctile = smem + w * (128 * 64);
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = i * 16 + 4 * g + r, col = j * 16 + c;
-        ctile[row * 64 + 8 * swz(row, col >> 3) + (col & 7)] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][r]);
+    // ---- epilogue: this wave's 128 x 64 sub-tile as bf16 rows in LDS, then 16-byte stores
+    __syncthreads();
+    uint16_t* ctile = smem + w * (128 * 64);
+  #pragma unroll
+    for (int i = 0; i < 8; ++i)
+  #pragma unroll
+      for (int j = 0; j < 4; ++j)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = i * 16 + 4 * g + r, col = j * 16 + c;
+          ctile[row * 64 + 8 * swz(row, col >> 3) + (col & 7)] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][r]);
+        }
+    lds_stores_done();
+    __builtin_amdgcn_wave_barrier();
+    const int col0 = n0 + wn * 64;
+    if (col0 < N) {
+      const int p = col0 / D, h = (col0 - p * D) / d;
+      const int64_t nblk = (a.T + 15) / 16;
+      uint16_t* out = (uint16_t*)a.out;
+  #pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int q = it * 64 + lane;
+        const int row = q >> 3, ch = q & 7;
+        const int64_t grow = m0 + wm * 128 + row;
+        if (grow >= M) continue;
+        const uint4 v = *(const uint4*)(ctile + row * 64 + 8 * swz(row, ch));
+        const int64_t s = grow / Tw, tt = a.tt0 + (grow - s * Tw);
+        const int64_t pos = a.reverse ? a.T - 1 - tt : tt;
+        uint16_t* blk = out + (((int64_t)s * a.H + h) * nblk + (pos >> 4)) * (int64_t)a.blk_elems;
+        *(uint4*)(blk + (p * 16 + (int)(pos & 15)) * TOK_RS + 8 * ch) = v;
       }
-  lds_stores_done();
-  __builtin_amdgcn_wave_barrier();
-  const int col0 = n0 + wn * 64;
-  if (col0 >= N) return;
-  const int p = col0 / D, h = (col0 - p * D) / d;
-  const int64_t nblk = (a.T + 15) / 16;
-  uint16_t* out = (uint16_t*)a.out;
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int q = it * 64 + lane;
-    const int row = q >> 3, ch = q & 7;
-    const int64_t grow = m0 + wm * 128 + row;
-    if (grow >= M) continue;
-    const uint4 v = *(const uint4*)(ctile + row * 64 + 8 * swz(row, ch));
-    const int64_t s = grow / Tw, tt = a.tt0 + (grow - s * Tw);
-    const int64_t pos = a.reverse ? a.T - 1 - tt : tt;
-    uint16_t* blk = out + (((int64_t)s * a.H + h) * nblk + (pos >> 4)) * (int64_t)a.blk_elems;
-    *(uint4*)(blk + (p * 16 + (int)(pos & 15)) * TOK_RS + 8 * ch) = v;
+    }
+    __syncthreads();  // every wave has read its sub-tile before the next tile's loads reuse the stages
   }
 }
 
@@ -297,7 +305,8 @@ hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s) {
     if (M == 0) return hipSuccess;
     const int mtiles = (int)((M + T_BM - 1) / T_BM), ntiles = (N + T_BN - 1) / T_BN;
     const int total = mtiles * ntiles;
-    const int grid = (total + 7) / 8 * 8;
+    int grid = (total + 7) / 8 * 8;
+    if (a.max_wg > 0) grid = std::min(grid, std::max(8, a.max_wg / 8 * 8));
     hipLaunchKernelGGL(proj_tiles_kernel, dim3((unsigned)grid), dim3(T_THREADS), 0, s, a, mtiles, ntiles);
     return hipGetLastError();
   }
