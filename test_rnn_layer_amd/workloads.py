@@ -55,6 +55,7 @@ class Workload:
     seed: int = 0
     loss: str = "mean"  # "mean" (1/d)||e||^2, or "sum" ||e||^2
     gelu: str = "erf"  # "erf" (exact) or "tanh" (approximation)
+    model: str = "mlp"  # "mlp": f(u; W) = GELU(u W1) W2; "linear": f(u; W) = u W with W = W1 (m = d)
 
     @property
     def D(self) -> int:
@@ -79,6 +80,8 @@ WORKLOADS = {
                              eta=0.05, bidir=True, io_dtype="bf16"),
 }
 WORKLOAD_ORDER = ["tiny_f32", "seg14k", "bidir100k", "bidir307k", "bigstate307k"]
+# TTT-Linear (the same layer with a linear inner model, d x d state) at the shape of bidir307k
+WORKLOADS["linear307k"] = WORKLOADS["bidir307k"].replace(name="linear307k", m=64, model="linear")
 
 
 # ----------------------------------------------------------------------------
@@ -169,7 +172,8 @@ def make_theta(wl: Workload) -> np.ndarray:
 
 
 def make_w0(wl: Workload) -> tuple[np.ndarray, np.ndarray]:
-    """Initial state W1_0 [H, d, m] ~ N(0, 1/d) and W2_0 [H, m, d] ~ N(0, 1/m), float32."""
+    """Initial state W1_0 [H, d, m] ~ N(0, 1/d) and W2_0 [H, m, d] ~ N(0, 1/m), float32.
+    For the linear model (m = d) W1_0 is the state W_0 and W2_0 goes unused."""
     w1 = _rng(wl.seed, TID_W1).standard_normal((wl.H, wl.d, wl.m)) / np.sqrt(wl.d)
     w2 = _rng(wl.seed, TID_W2).standard_normal((wl.H, wl.m, wl.d)) / np.sqrt(wl.m)
     return w1.astype(np.float32), w2.astype(np.float32)
