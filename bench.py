@@ -19,6 +19,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "TTT-MLP bidirectional layer tokens/sec at 307,200 tokens; % of roofline"
+METRIC_LINEAR = "TTT-Linear bidirectional layer tokens/sec at 307,200 tokens; % of roofline"
 # MI355X published peaks
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
@@ -32,6 +33,12 @@ def scan_flops_per_token_head(d: int, m: int, b: int) -> int:
     plus the causal halves of the b x b products (tril(QK^T), its product with
     G1, tril(Hq Hk^T), its product with G2)."""
     return 7 * 2 * d * m + (b + 1) * (2 * d + 2 * m)
+
+
+def linear_scan_flops_per_token_head(d: int, b: int) -> int:
+    """The linear inner model: three d x d contractions (K W, Q W, K^T G) plus the
+    causal halves of tril(Q K^T) and of its product with G."""
+    return 3 * 2 * d * d + (b + 1) * 2 * d
 
 
 def proj_flops_per_token(D: int) -> int:
@@ -61,6 +68,7 @@ def cpu_baseline(wl, tokens: int):
     directions, every head), timed on this host's cores."""
     import numpy as np
 
+    from oracle import ttt_linear_oracle as LO
     from oracle import ttt_oracle as O
     from test_rnn_layer_amd import workloads as W
 
@@ -70,9 +78,13 @@ def cpu_baseline(wl, tokens: int):
     th = W.to_f64(inp["theta"], sub.io_dtype)
     nw = O.default_workers()
     t0 = time.perf_counter()
-    O.ttt_bidir(X, th, inp["W1_0"].astype(np.float64), inp["W2_0"].astype(np.float64),
-                inp["alpha_f"].astype(np.float64), inp["alpha_b"].astype(np.float64),
-                eta=sub.eta, b=sub.b, loss=sub.loss, gelu_form=sub.gelu, workers=nw)
+    if sub.model == "linear":
+        LO.ttt_linear_bidir(X, th, inp["W1_0"].astype(np.float64), inp["alpha_f"].astype(np.float64),
+                            inp["alpha_b"].astype(np.float64), eta=sub.eta, b=sub.b, loss=sub.loss, workers=nw)
+    else:
+        O.ttt_bidir(X, th, inp["W1_0"].astype(np.float64), inp["W2_0"].astype(np.float64),
+                    inp["alpha_f"].astype(np.float64), inp["alpha_b"].astype(np.float64),
+                    eta=sub.eta, b=sub.b, loss=sub.loss, gelu_form=sub.gelu, workers=nw)
     dt = time.perf_counter() - t0
     return dict(value=tokens / dt, unit="tokens/s", cores=nw, kind="oracle",
                 sample=f"{wl.name} workload, first {tokens} tokens, all {wl.H} heads, both directions, "
@@ -113,8 +125,11 @@ def main():
     W1, W2 = f32(inp["W1_0"]), f32(inp["W2_0"])
     af, ab = f32(inp["alpha_f"]), f32(inp["alpha_b"])
     del inp
+    linear = wl.model == "linear"
     cfg = _lib.make_config(wl.B, wl.T, wl.H, wl.d, wl.m, wl.b, wl.eta, io_dtype=wl.io_dtype, loss=wl.loss,
-                           gelu=wl.gelu, algo=args.algo)
+                           gelu=wl.gelu, algo=args.algo, model=wl.model)
+    if linear:
+        W2 = None  # the linear model has one d x d state
     ws = torch.empty(_lib.workspace_size(cfg, True), dtype=torch.uint8, device=dev)
     Y = torch.empty_like(X)
     step = lambda: _lib.bidir(cfg, X, th, W1, W2, af, ab, workspace=ws, out=Y)
@@ -141,26 +156,27 @@ def main():
     value = tokens / (ms_per_step / 1e3)
     dirs = 2
     # dominant kernel: the scan; one launch covers one direction of the whole batch
-    scan_flops_launch = scan_flops_per_token_head(wl.d, wl.m, wl.b) * wl.H * tokens * dirs * args.steps / scan_n
+    scan_fpt = linear_scan_flops_per_token_head(wl.d, wl.b) if linear else scan_flops_per_token_head(wl.d, wl.m, wl.b)
+    scan_flops_launch = scan_fpt * wl.H * tokens * dirs * args.steps / scan_n
     scan_avg_ms = scan_ms / scan_n
     achieved = scan_flops_launch / (scan_avg_ms / 1e3) / 1e12
     algo = _lib.select_algo(cfg)
     used_mfma = algo == "mfma"
     peak = PEAK_BF16_TFLOPS if used_mfma else PEAK_FP32_TFLOPS
-    kname = "scan_" + algo
+    kname = ("scan_linear_" if linear else "scan_") + algo
     traffic = traffic_from_profile(kname, kernel_digest(kname))
     # layer roofline: projections at bf16 MFMA peak plus the scan at fp32 peak
     proj_total = proj_flops_per_token(wl.D) * tokens * dirs
-    scan_total = scan_flops_per_token_head(wl.d, wl.m, wl.b) * wl.H * tokens * dirs
+    scan_total = scan_fpt * wl.H * tokens * dirs
     R_ms = (proj_total / (PEAK_BF16_TFLOPS * 1e12) + scan_total / (PEAK_FP32_TFLOPS * 1e12)) * 1e3
     # the same with the scan's contractions priced at the bf16 peak (they run on bf16 operands)
     R_exec_ms = (proj_total + scan_total) / (PEAK_BF16_TFLOPS * 1e12) * 1e3
     out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_LINEAR if linear else METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "d": wl.d, "m": wl.m, "b": wl.b,
-                   "eta": wl.eta, "D": wl.D, "directions": dirs, "scan_kernel": kname},
+                   "eta": wl.eta, "D": wl.D, "directions": dirs, "scan_kernel": kname, "model": wl.model},
         "roofline": {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "flops_per_launch": scan_flops_launch, "avg_launch_ms": scan_avg_ms},

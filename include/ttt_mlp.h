@@ -16,6 +16,14 @@
  *   bidirectional: X' = forward pass with alpha_f; Y = reversed pass over X'
  *   with alpha_b; both passes start from the same W_0 and use the same theta.
  *
+ * TTT-Linear (model = TTT_MODEL_LINEAR): the same layer with a linear inner
+ * model, f(u; W) = u W with W a d x d matrix per head (the linear-state
+ * variant of the notes page's ablation table).  Its gradient step is
+ * W_t = W_{t-1} - eta * k_t^T c (k_t W_{t-1} - v_t), c = 2/d (mean) or 2 (sum);
+ * everything else (projections, read-out, mini-batches, gate, directions) is
+ * as above.  W1_0 then holds W_0 [H, d, d] (m must equal d), W1_T the final
+ * W [B, H, d, d]; W2_0, W2_T and gelu are not used (W2_0 may be NULL).
+ *
  * Mini-batches of b tokens (b = 1 is the per-token rule): every gradient of
  * a mini-batch is taken at the state the mini-batch starts from; token t
  * reads out with that state minus eta times the summed gradients of the
@@ -71,6 +79,10 @@ extern "C" {
 #define TTT_LOSS_MEAN 0 /* (1/d) ||f(k) - v||^2, gradient scale 2/d */
 #define TTT_LOSS_SUM 1  /* ||f(k) - v||^2, gradient scale 2 */
 
+/* inner model */
+#define TTT_MODEL_MLP 0    /* f(u; W) = GELU(u W1) W2 */
+#define TTT_MODEL_LINEAR 1 /* f(u; W) = u W, W = W1 (d x d) */
+
 /* GELU form of the inner MLP */
 #define TTT_GELU_ERF 0  /* a * Phi(a), exact */
 #define TTT_GELU_TANH 1 /* 0.5 a (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))) */
@@ -79,8 +91,9 @@ extern "C" {
 #define TTT_ALGO_AUTO 0    /* fastest kernel that supports the shape and dtype */
 #define TTT_ALGO_GENERIC 1 /* fp32 VALU scan, any supported shape */
 #define TTT_ALGO_MFMA 2    /* bf16-operand MFMA scan, fp32 state: bf16 io, erf GELU,
-                              d = 64, m = 256, b = 16, T < 2^31 */
-#define TTT_ALGO_COOP 3    /* per-token fp32 scan whose state (512 KB per head) is split
+                              d = 64, m = 256, b = 16, T < 2^31; for TTT_MODEL_LINEAR
+                              d = m = 64, b = 16, bf16 io, T < 2^31 */
+#define TTT_ALGO_COOP 3    /* (TTT_MODEL_MLP only) per-token fp32 scan whose state (512 KB per head) is split
                               over 8 cooperating workgroups: d = 128, m = 512, b = 1.
                               Needs B*H*8 co-resident workgroups (cooperative launch);
                               a workgroup that waits for its peers longer than about a
@@ -98,6 +111,7 @@ typedef struct ttt_mlp_config {
   int32_t gelu;     /* TTT_GELU_* */
   int32_t io_dtype; /* TTT_F32 or TTT_BF16 */
   int32_t algo;     /* TTT_ALGO_* */
+  int32_t model;    /* TTT_MODEL_* (0, the MLP, when zero-initialised) */
 } ttt_mlp_config;
 
 /* Library version, (major << 16) | minor. */

@@ -17,6 +17,7 @@ TTT_OK, TTT_ERR_INVALID_ARG, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_HIP
 TTT_F32, TTT_BF16 = 0, 1
 TTT_LOSS_MEAN, TTT_LOSS_SUM = 0, 1
 TTT_GELU_ERF, TTT_GELU_TANH = 0, 1
+TTT_MODEL_MLP, TTT_MODEL_LINEAR = 0, 1
 TTT_ALGO_AUTO, TTT_ALGO_GENERIC, TTT_ALGO_MFMA, TTT_ALGO_COOP = 0, 1, 2, 3
 TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN = 0, 1
 
@@ -34,7 +35,7 @@ class Config(ctypes.Structure):
         ("H", ctypes.c_int32), ("d", ctypes.c_int32), ("m", ctypes.c_int32), ("b", ctypes.c_int32),
         ("eta", ctypes.c_float),
         ("loss", ctypes.c_int32), ("gelu", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
-        ("algo", ctypes.c_int32),
+        ("algo", ctypes.c_int32), ("model", ctypes.c_int32),
     ]
 
 
@@ -89,8 +90,10 @@ def _check(status: int):
         raise TTTError(status, lib().ttt_mlp_last_error().decode())
 
 
-def make_config(B, T, H, d, m, b, eta, *, io_dtype="bf16", loss="mean", gelu="erf", algo="auto") -> Config:
+def make_config(B, T, H, d, m, b, eta, *, io_dtype="bf16", loss="mean", gelu="erf", algo="auto",
+                model="mlp") -> Config:
     return Config(B=B, T=T, H=H, d=d, m=m, b=b, eta=eta,
+                  model={"mlp": TTT_MODEL_MLP, "linear": TTT_MODEL_LINEAR}[model],
                   loss={"mean": TTT_LOSS_MEAN, "sum": TTT_LOSS_SUM}[loss],
                   gelu={"erf": TTT_GELU_ERF, "tanh": TTT_GELU_TANH}[gelu],
                   io_dtype={"f32": TTT_F32, "bf16": TTT_BF16}[io_dtype],
@@ -121,9 +124,11 @@ def _stream(device):
 
 
 def _state_out(cfg, like):
+    """Final-state outputs: W1_T, W2_T (the linear model has only W = W1, [B, H, d, d])."""
     import torch
     kw = dict(dtype=torch.float32, device=like.device)
-    return (torch.empty((cfg.B, cfg.H, cfg.d, cfg.m), **kw), torch.empty((cfg.B, cfg.H, cfg.m, cfg.d), **kw))
+    w1 = torch.empty((cfg.B, cfg.H, cfg.d, cfg.m), **kw)
+    return (w1, None) if cfg.model == TTT_MODEL_LINEAR else (w1, torch.empty((cfg.B, cfg.H, cfg.m, cfg.d), **kw))
 
 
 def _workspace(cfg, bidir, like):

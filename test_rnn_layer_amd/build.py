@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libttt_mlp.so")
-SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_coop.hip"]
+SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_linear.hip", "scan_coop.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,8 +32,9 @@ FLAGS = [
 
 # kernels that must keep their whole working set in registers: the MFMA and
 # cooperative scans hold the inner-model state in VGPRs for the whole
-# sequence, and a spilling build of either is refused.
-NO_SPILL_SOURCES = {"scan_mfma.hip", "scan_coop.hip"}
+# sequence (and the linear scan counts its vector-memory instructions per
+# step), so a spilling build of any of them is refused.
+NO_SPILL_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "scan_coop.hip"}
 
 
 def _check_no_spill(src, remarks):
@@ -49,7 +50,7 @@ def _check_no_spill(src, remarks):
 # instructions later gave wrong values on gfx950 (the compiler inserts no wait
 # for it).  The build compiles these sources to assembly as well and refuses any
 # product whose accumulator comes from a product of another instruction.
-MFMA_CHAIN_SOURCES = {"scan_mfma.hip", "proj_mfma.hip"}
+MFMA_CHAIN_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "proj_mfma.hip"}
 _MFMA = re.compile(r"\s*(v_mfma\w*)\s+v\[(\d+):(\d+)\],\s*[^,]+,\s*[^,]+,\s*(?:v\[(\d+):(\d+)\]|\S+)")
 _VDST = re.compile(r"\s*(?:v_|ds_read|global_load|buffer_load|scratch_load|flat_load)\S*\s+(?:v(\d+)|v\[(\d+):(\d+)\])")
 

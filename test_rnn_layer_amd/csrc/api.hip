@@ -130,6 +130,11 @@ int32_t check_config(const ttt_mlp_config* c) {
   if (c->algo != TTT_ALGO_AUTO && c->algo != TTT_ALGO_GENERIC && c->algo != TTT_ALGO_MFMA &&
       c->algo != TTT_ALGO_COOP)
     return fail(TTT_ERR_INVALID_ARG, "unknown algo %d", c->algo);
+  if (c->model != TTT_MODEL_MLP && c->model != TTT_MODEL_LINEAR)
+    return fail(TTT_ERR_INVALID_ARG, "unknown model %d", c->model);
+  if (c->model == TTT_MODEL_LINEAR && c->m != c->d)
+    return fail(TTT_ERR_INVALID_ARG, "the linear model's state is d x d: m must equal d (got d=%d m=%d)", c->d,
+                c->m);
   const int64_t D = (int64_t)c->H * c->d;
   if (D > (1 << 20) || c->m > (1 << 16) || c->b > (1 << 16))
     return fail(TTT_ERR_UNSUPPORTED, "D = %lld, m = %d or b = %d too large", (long long)D, c->m, c->b);
@@ -138,14 +143,27 @@ int32_t check_config(const ttt_mlp_config* c) {
   return TTT_OK;
 }
 
-// The MFMA scan implements the exact (erf) GELU; the tanh form runs on the generic kernel.
-// It indexes token rows of one sequence with 32-bit integers (T < 2^31).
+bool is_linear(const ttt_mlp_config* c) { return c->model == TTT_MODEL_LINEAR; }
+
+// The MFMA scans take bf16 io; the MLP one implements the exact (erf) GELU (the
+// tanh form runs on the generic kernel).  They index token rows of one sequence
+// with 32-bit integers (T < 2^31).
 bool mfma_possible(const ttt_mlp_config* c) {
-  return c->io_dtype == TTT_BF16 && c->gelu == TTT_GELU_ERF && ttt::scan_mfma_supported(c->d, c->m, c->b) &&
-         ((int64_t)c->H * c->d) % 8 == 0 && c->T < ((int64_t)1 << 31);
+  const bool shape = is_linear(c) ? ttt::scan_linear_mfma_supported(c->d, c->m, c->b)
+                                  : c->gelu == TTT_GELU_ERF && ttt::scan_mfma_supported(c->d, c->m, c->b);
+  return c->io_dtype == TTT_BF16 && shape && ((int64_t)c->H * c->d) % 8 == 0 && c->T < ((int64_t)1 << 31);
 }
 
-bool coop_possible(const ttt_mlp_config* c) { return ttt::scan_coop_supported(c->d, c->m, c->b, c->T); }
+bool coop_possible(const ttt_mlp_config* c) {
+  return !is_linear(c) && ttt::scan_coop_supported(c->d, c->m, c->b, c->T);
+}
+
+size_t generic_lds_bytes(const ttt_mlp_config* c) {
+  return is_linear(c) ? ttt::scan_linear_generic_lds_bytes(c->d, c->b) : ttt::scan_generic_lds_bytes(c->d, c->m, c->b);
+}
+
+// fp32 state elements of one (sequence, head): W1 and W2, or the linear model's W
+size_t state_elems(const ttt_mlp_config* c) { return (is_linear(c) ? 1 : 2) * (size_t)c->d * c->m; }
 
 int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   int32_t st = check_config(c);
@@ -154,30 +172,33 @@ int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   if (algo == TTT_ALGO_AUTO)
     algo = mfma_possible(c) ? TTT_ALGO_MFMA : coop_possible(c) ? TTT_ALGO_COOP : TTT_ALGO_GENERIC;
   if (algo == TTT_ALGO_COOP && !coop_possible(c))
-    return fail(TTT_ERR_UNSUPPORTED, "the cooperative scan needs d=128, m=512, b=1, T < 2^31 (got d=%d m=%d b=%d)",
-                c->d, c->m, c->b);
+    return fail(TTT_ERR_UNSUPPORTED,
+                "the cooperative scan needs the MLP model, d=128, m=512, b=1, T < 2^31 (got d=%d m=%d b=%d)", c->d,
+                c->m, c->b);
   if (algo == TTT_ALGO_MFMA && !mfma_possible(c))
     return fail(TTT_ERR_UNSUPPORTED,
-                "the MFMA scan needs bf16 io, erf GELU, d=64, m=256, b=16 (got d=%d m=%d b=%d io=%d gelu=%d)", c->d,
-                c->m, c->b, c->io_dtype, c->gelu);
-  if (algo == TTT_ALGO_GENERIC && ttt::scan_generic_lds_bytes(c->d, c->m, c->b) > kGenericLdsMax)
+                is_linear(c) ? "the linear MFMA scan needs bf16 io, d=m=64, b=16 (got d=%d m=%d b=%d io=%d)"
+                             : "the MFMA scan needs bf16 io, erf GELU, d=64, m=256, b=16 (got d=%d m=%d b=%d io=%d "
+                               "gelu=%d)",
+                c->d, c->m, c->b, c->io_dtype, c->gelu);
+  if (algo == TTT_ALGO_GENERIC && generic_lds_bytes(c) > kGenericLdsMax)
     return fail(TTT_ERR_UNSUPPORTED,
                 "generic scan: mini-batch working set of %zu bytes (d=%d m=%d b=%d) exceeds %zu bytes of LDS",
-                ttt::scan_generic_lds_bytes(c->d, c->m, c->b), c->d, c->m, c->b, kGenericLdsMax);
+                generic_lds_bytes(c), c->d, c->m, c->b, kGenericLdsMax);
   p->algo = algo;
   p->io_elem = c->io_dtype == TTT_BF16 ? 2 : 4;
   const size_t BHTd = (size_t)c->B * c->H * (size_t)c->T * c->d;
   p->qkv_off = 0;
   if (algo == TTT_ALGO_MFMA) {
     p->qkv_bytes = align_up(ttt::scan_mfma_tile_bytes(c->B, c->T, c->H));
-    // the state handed from one chunk of the scan to the next (W1 then W2)
-    p->wst_bytes = align_up((size_t)c->B * c->H * 2 * (size_t)c->d * c->m * sizeof(float));
+    // the state handed from one chunk of the scan to the next (W1 then W2, or W)
+    p->wst_bytes = align_up((size_t)c->B * c->H * state_elems(c) * sizeof(float));
   } else if (algo == TTT_ALGO_COOP) {
     p->qkv_bytes = align_up(3 * BHTd * sizeof(float));
     p->wst_bytes = align_up(ttt::scan_coop_xchg_bytes(c->B, c->H) + sizeof(uint32_t));
   } else {
     p->qkv_bytes = align_up(3 * BHTd * sizeof(float));
-    p->wst_bytes = align_up((size_t)c->B * c->H * 2 * (size_t)c->d * c->m * sizeof(float));
+    p->wst_bytes = align_up((size_t)c->B * c->H * state_elems(c) * sizeof(float));
   }
   p->wst_off = p->qkv_off + p->qkv_bytes;
   p->total = p->wst_off + p->wst_bytes;
@@ -264,6 +285,7 @@ ttt::ScanArgs scan_args(const ttt_mlp_config* c, const Plan& pl, const void* xin
   sa.gelu_tanh = c->gelu == TTT_GELU_TANH;
   sa.reverse = reverse;
   sa.bf16 = c->io_dtype == TTT_BF16;
+  sa.linear = is_linear(c);
   return sa;
 }
 
@@ -281,7 +303,7 @@ int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, 
                 (long long)(c->B * c->H * 8));
   e = timed_launch(TTT_KERNEL_SCAN, stream, [&] {
     if (pl.algo == TTT_ALGO_COOP) return ttt::launch_scan_coop(sa, stream);
-    return ttt::launch_scan_generic(sa, stream);
+    return sa.linear ? ttt::launch_scan_linear_generic(sa, stream) : ttt::launch_scan_generic(sa, stream);
   });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   return TTT_OK;
@@ -442,7 +464,9 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
         sa.w1_T = st1;
         sa.w2_T = st2;
       }
-      TTT_TRY(timed_launch(TTT_KERNEL_SCAN, S, [&] { return ttt::launch_scan_mfma(sa, S); }), "scan launch");
+      TTT_TRY(timed_launch(TTT_KERNEL_SCAN, S,
+                           [&] { return sa.linear ? ttt::launch_scan_linear_mfma(sa, S) : ttt::launch_scan_mfma(sa, S); }),
+              "scan launch");
       TTT_TRY(hipEventRecord(ev_scan(d, k), S), "event record");
     }
   }
@@ -498,19 +522,21 @@ int32_t ttt_mlp_forward(const ttt_mlp_config* cfg, const void* X, const void* th
   int32_t st = make_plan(cfg, &pl);
   if (st != TTT_OK) return st;
   const bool no_tokens = cfg->T == 0;  // X and Y may then be NULL
-  if ((!no_tokens && (!X || !Y)) || !theta_qkv || !W1_0 || !W2_0 || !alpha)
+  const bool lin = is_linear(cfg);     // W2_0 and W2_T unused
+  if ((!no_tokens && (!X || !Y)) || !theta_qkv || !W1_0 || (!lin && !W2_0) || !alpha)
     return fail(TTT_ERR_INVALID_ARG, "a required pointer (X, theta_qkv, W1_0, W2_0, alpha, Y) is NULL");
+  if (lin) W2_T = nullptr;
   if (reverse != 0 && reverse != 1) return fail(TTT_ERR_INVALID_ARG, "reverse must be 0 or 1");
   if (!workspace || workspace_bytes < pl.total)
     return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                 pl.total);
   const size_t D = (size_t)cfg->H * cfg->d, BTD = (size_t)cfg->B * cfg->T * D;
   const size_t st_bytes = (size_t)cfg->B * cfg->H * cfg->d * cfg->m * sizeof(float);
+  const size_t w0_bytes = (size_t)cfg->H * cfg->d * cfg->m * 4;
   const Buf outs[] = {{Y, BTD * pl.io_elem, "Y"}, {Z, BTD * 4, "Z"}, {W1_T, st_bytes, "W1_T"},
                       {W2_T, st_bytes, "W2_T"}, {workspace, pl.total, "workspace"}};
   const Buf ins[] = {{X, BTD * pl.io_elem, "X"}, {theta_qkv, 3 * D * D * pl.io_elem, "theta_qkv"},
-                     {W1_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W1_0"},
-                     {W2_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W2_0"}, {alpha, D * 4, "alpha"}};
+                     {W1_0, w0_bytes, "W1_0"}, {lin ? nullptr : W2_0, w0_bytes, "W2_0"}, {alpha, D * 4, "alpha"}};
   st = check_no_overlap(outs, 5, ins, 5);
   if (st != TTT_OK) return st;
   if (pl.algo == TTT_ALGO_MFMA) {
@@ -532,9 +558,11 @@ int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* thet
   int32_t st = make_plan(cfg, &pl);
   if (st != TTT_OK) return st;
   const bool no_tokens = cfg->T == 0;  // X and Y may then be NULL
-  if ((!no_tokens && (!X || !Y)) || !theta_qkv || !W1_0 || !W2_0 || !alpha_f || !alpha_b)
+  const bool lin = is_linear(cfg);     // W2_0 and the W2 outputs unused
+  if ((!no_tokens && (!X || !Y)) || !theta_qkv || !W1_0 || (!lin && !W2_0) || !alpha_f || !alpha_b)
     return fail(TTT_ERR_INVALID_ARG,
                 "a required pointer (X, theta_qkv, W1_0, W2_0, alpha_f, alpha_b, Y) is NULL");
+  if (lin) W2_Tf = W2_Tb = nullptr;
   if (!workspace || workspace_bytes < pl.total)
     return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                 pl.total);
@@ -544,9 +572,9 @@ int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* thet
                       {Z_b, BTD * 4, "Z_b"},           {W1_Tf, st_bytes, "W1_Tf"},
                       {W2_Tf, st_bytes, "W2_Tf"},      {W1_Tb, st_bytes, "W1_Tb"},
                       {W2_Tb, st_bytes, "W2_Tb"},      {workspace, pl.total, "workspace"}};
+  const size_t w0_bytes = (size_t)cfg->H * cfg->d * cfg->m * 4;
   const Buf ins[] = {{X, BTD * pl.io_elem, "X"}, {theta_qkv, 3 * D * D * pl.io_elem, "theta_qkv"},
-                     {W1_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W1_0"},
-                     {W2_0, (size_t)cfg->H * cfg->d * cfg->m * 4, "W2_0"}, {alpha_f, D * 4, "alpha_f"},
+                     {W1_0, w0_bytes, "W1_0"}, {lin ? nullptr : W2_0, w0_bytes, "W2_0"}, {alpha_f, D * 4, "alpha_f"},
                      {alpha_b, D * 4, "alpha_b"}};
   st = check_no_overlap(outs, 8, ins, 6);
   if (st != TTT_OK) return st;

@@ -255,6 +255,89 @@ __global__ __launch_bounds__(GS_THREADS) void scan_generic_kernel(ScanArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// generic linear scan (inner model f(u; W) = u W, W: d x d): one workgroup per
+// (sequence, head), the mini-batch dual form G = c (K W - V),
+// Z = Q W - eta tril(Q K^T) G, W -= eta K^T G, with W the state the mini-batch
+// starts from
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(GS_THREADS) void scan_linear_generic_kernel(ScanArgs a) {
+  extern __shared__ float lds[];
+  const int d = a.d, b = a.b, tid = threadIdx.x;
+  const int64_t T = a.T;
+  const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int D = a.H * d;
+  const float eta = a.eta;
+
+  float* Ks = lds;         // [b, d]
+  float* Qs = Ks + b * d;  // [b, d]
+  float* Vs = Qs + b * d;  // [b, d]; becomes G
+  float* S = Vs + b * d;   // [b, b] tril(Q K^T), diagonal included
+
+  float* W = a.wstate + ((int64_t)s * a.H + h) * (int64_t)d * d;
+  const float* w0 = a.w1_0 + (int64_t)h * d * d;
+  for (int i = tid; i < d * d; i += GS_THREADS) W[i] = w0[i];
+  __syncthreads();
+
+  const int64_t plane = a.B * a.H * T * d;
+  const float* qb = a.qkv + ((int64_t)s * a.H + h) * T * d;
+  const float* kb = qb + plane;
+  const float* vb = kb + plane;
+
+  for (int64_t n0 = 0; n0 < T; n0 += b) {
+    const int n = (int)((T - n0) < b ? (T - n0) : b);
+    for (int i = tid; i < n * d; i += GS_THREADS) {
+      const int r = i / d, j = i % d;
+      const int64_t t = a.reverse ? T - 1 - (n0 + r) : n0 + r;
+      Ks[r * d + j] = kb[t * d + j];
+      Qs[r * d + j] = qb[t * d + j];
+      Vs[r * d + j] = vb[t * d + j];
+    }
+    __syncthreads();
+    // G = c (K W - V), in place of V; S = tril(Q K^T)
+    for (int i = tid; i < n * d; i += GS_THREADS) {
+      const int r = i / d, j = i % d;
+      float acc = 0.0f;
+      for (int k = 0; k < d; ++k) acc = fmaf(Ks[r * d + k], W[k * d + j], acc);
+      Vs[r * d + j] = a.gscale * (acc - Vs[r * d + j]);
+    }
+    for (int i = tid; i < n * n; i += GS_THREADS) {
+      const int r = i / n, c = i % n;
+      float acc = 0.0f;
+      if (c <= r)
+        for (int k = 0; k < d; ++k) acc = fmaf(Qs[r * d + k], Ks[c * d + k], acc);
+      S[r * b + c] = acc;
+    }
+    __syncthreads();
+    // Z = Q W - eta tril(Q K^T) G, then the gate
+    for (int i = tid; i < n * d; i += GS_THREADS) {
+      const int r = i / d, j = i % d;
+      float acc = 0.0f, corr = 0.0f;
+      for (int k = 0; k < d; ++k) acc = fmaf(Qs[r * d + k], W[k * d + j], acc);
+      for (int c = 0; c <= r; ++c) corr = fmaf(S[r * b + c], Vs[c * d + j], corr);
+      const float z = acc - eta * corr;
+      const int64_t t = a.reverse ? T - 1 - (n0 + r) : n0 + r;
+      const int64_t o = ((int64_t)s * T + t) * D + (int64_t)h * d + j;
+      if (a.z) a.z[o] = z;
+      const float x = load_io(a.xin, o, a.bf16);
+      store_io(a.y, o, x + tanhf(a.alpha[h * d + j]) * z, a.bf16);
+    }
+    __syncthreads();
+    // W -= eta K^T G
+    for (int i = tid; i < d * d; i += GS_THREADS) {
+      const int k = i / d, j = i % d;
+      float acc = 0.0f;
+      for (int r = 0; r < n; ++r) acc = fmaf(Ks[r * d + k], Vs[r * d + j], acc);
+      W[i] -= eta * acc;
+    }
+    __syncthreads();
+  }
+  if (a.w1_T) {
+    float* o = a.w1_T + ((int64_t)s * a.H + h) * (int64_t)d * d;
+    for (int i = tid; i < d * d; i += GS_THREADS) o[i] = W[i];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_project_f32out(const ProjArgs& a, hipStream_t s) {
@@ -273,6 +356,16 @@ size_t scan_generic_lds_bytes(int d, int m, int b) {
 hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t s) {
   const size_t lds = scan_generic_lds_bytes(a.d, a.m, a.b);
   hipLaunchKernelGGL(scan_generic_kernel, dim3((unsigned)(a.B * a.H)), dim3(GS_THREADS), lds, s, a);
+  return hipGetLastError();
+}
+
+size_t scan_linear_generic_lds_bytes(int d, int b) {
+  return sizeof(float) * ((size_t)3 * b * d + (size_t)b * b);
+}
+
+hipError_t launch_scan_linear_generic(const ScanArgs& a, hipStream_t s) {
+  const size_t lds = scan_linear_generic_lds_bytes(a.d, a.b);
+  hipLaunchKernelGGL(scan_linear_generic_kernel, dim3((unsigned)(a.B * a.H)), dim3(GS_THREADS), lds, s, a);
   return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ struct ScanArgs {
   int32_t gelu_tanh;     // 0: erf form, 1: tanh form
   int32_t reverse;
   int32_t bf16;          // io dtype of xin / y
+  int32_t linear;        // 1: linear inner model f(u; W) = u W (W = w1, d x d; w2 unused)
 };
 
 // LDS bytes the generic scan needs for (d, m, b).
@@ -65,6 +66,13 @@ bool scan_mfma_supported(int d, int m, int b);
 size_t scan_mfma_tile_bytes(int64_t B, int64_t T, int H);
 int scan_mfma_block_elems();
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s);
+
+// Linear inner model.  MFMA scan: d = m = 64, b = 16, bf16 io (token blocks as for
+// the MFMA scan); generic scan: any supported shape and dtype (fp32 Q/K/V).
+bool scan_linear_mfma_supported(int d, int m, int b);
+hipError_t launch_scan_linear_mfma(const ScanArgs& a, hipStream_t s);
+size_t scan_linear_generic_lds_bytes(int d, int b);
+hipError_t launch_scan_linear_generic(const ScanArgs& a, hipStream_t s);
 
 // Cooperative per-token scan (d = 128, m = 512, b = 1): each head's state is
 // split over 8 co-resident workgroups that exchange partial sums every token.

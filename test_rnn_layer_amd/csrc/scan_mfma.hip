@@ -26,21 +26,16 @@
 #include "internal.h"
 #include "mfma_common.h"
 #include "phi_poly.h"
+#include "token_block.h"
 
 namespace ttt {
 namespace {
 
-constexpr int SD = 64;   // head width
+using namespace tb;  // SD = 64 head width, SB = 16 mini-batch, the token-block layout and readers
 constexpr int SM = 256;  // hidden width
-constexpr int SB = 16;   // mini-batch
 constexpr int NWAVE = 8;          // wave w owns hidden units [32w, 32w + 32)
 constexpr int NTHR = 64 * NWAVE;
 constexpr int NSTAGE = 4;         // token blocks in LDS: j-1 (read-out), j, j+1 and j+2 in flight
-// Token block layout (bf16 elements): Q, K and V of 16 consecutive scan
-// positions, each [16 tokens][RS] with the features in order and rows padded to
-// RS = 72 (144 bytes) so that the 16 rows read by one 16-lane group fall on
-// distinct LDS banks.
-constexpr int RS = SD + 8;  // 72
 constexpr int TS = SB + 8;  // 24: rows of the [feature][token] G2 copy (48 bytes: the 8-byte reads of
                             // two lane groups fall on distinct banks)
 // Hk slice rows: source lane l at row l + 8 (l / 32), so that the 32 rows a transposed
@@ -48,10 +43,6 @@ constexpr int TS = SB + 8;  // 24: rows of the [feature][token] G2 copy (48 byte
 constexpr int HKS_ROWS = 72;
 __device__ __forceinline__ int hk_row(int l) { return l + 8 * (l >> 5); }
 constexpr int DGS = SB + 4;  // 20: rows of the fp32 [hidden][token] GELU' tiles (bank spread of the column writes)
-constexpr int OFF_Q = 0, OFF_K = SB * RS, OFF_V = 2 * SB * RS;
-constexpr int BLK = 3 * SB * RS;          // 3456 elements, 6912 bytes
-constexpr int BLK_CHUNKS = BLK * 2 / 16;  // 432 chunks of 16 bytes
-static_assert((BLK * 2) % 16 == 0, "block must be a whole number of 16-byte chunks");
 
 // GELU(a) = a Phi(a) and GELU'(a) = Phi(a) + a phi(a), with Phi from the
 // polynomial of phi_poly.h (|error| <= 6e-5, no reciprocal or exponential: the
@@ -75,45 +66,6 @@ struct Gelu {
   }
   static __device__ __forceinline__ float value(float a) { return a * cdf(a); }
 };
-
-// tanh(u) = 1 - 2 / (exp(2u) + 1) (exact identity; saturates to +-1 for large |u|),
-// used for the gate factors tanh(alpha).
-__device__ __forceinline__ float tanh_gate(float u) {
-  const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * u);  // exp(2u)
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-}
-
-
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 v;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.0f;
-  return v;
-}
-
-// Readers of the staged token block (LDS).  Rows past the end of a short last
-// block are zero in the workspace (see zero_block_padding), so no masking.
-// A K=32 operand row in the pair order: features 32cc + 4g .. +3 and 32cc + 16 + 4g .. +3.
-__device__ __forceinline__ bf16x8 rd_row8(const uint16_t* blk, int off, int g, int c, int cc) {
-  const uint16_t* row = blk + off + c * RS + 32 * cc + 4 * g;
-  const bf16x4 lo = *(const bf16x4*)row, hi = *(const bf16x4*)(row + 16);
-  bf16x8 v;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = lo[i];
-    v[4 + i] = hi[i];
-  }
-  return v;
-}
-
-// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// lane i receives element i mod 4 of the 8 bytes addressed by lanes
-// i/4 + 4e (e = 0..3) of its group, as its element e.
-__device__ __forceinline__ bf16x4 ld_tr(const void* lds_addr) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)lds_addr);
-  return __builtin_bit_cast(bf16x4, v);
-}
 
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_mfma_kernel(ScanArgs a) {
   __shared__ f32x4 Ypart[NWAVE][4][64];                            // partial Yhat^T: wave, d-tile, lane
@@ -176,20 +128,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   const int Tc32 = (int)Tc, p032 = (int)p0, T32 = (int)T;
   auto block_n = [&](int64_t j) -> int { return min(Tc32 - SB * (int)j, SB); };
 
-  // token blocks: direct global -> LDS loads three steps ahead of use (no registers);
-  // lane i of a wave fills bytes [16 i, 16 i + 16) of the wave's 1 KB slice.  The
-  // load is written as a statement of its own rather than through the compiler's
-  // builtin: the compiler makes every later LDS read of Stage wait for all such
-  // loads in flight (it cannot tell the stages apart), which would expose their
-  // whole latency at the next step's first read.  The statement has no output
-  // registers; its completion is awaited explicitly (vmem_done) before the barrier
-  // that precedes the block's first use.
+  // token blocks: direct global -> LDS loads three steps ahead of use (no
+  // registers); lane i of a wave fills bytes [16 i, 16 i + 16) of the wave's 1 KB
+  // slice; completion is awaited (vmem_done) before the barrier that precedes the
+  // block's first use
   auto stage_async = [&](int64_t jb, int buf) {
     const uint4* src = (const uint4*)(blocks + jb * BLK) + 64 * w + lane;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)Stage[buf]) + 1024u * (uint32_t)w);
-    if (64 * w + lane < BLK_CHUNKS)
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(dst), "v"(src) : "memory", "m0");
+    const uint32_t dst = lds_addr_uniform(Stage[buf], 1024u * (uint32_t)w);
+    if (64 * w + lane < BLK_CHUNKS) dma16(src, dst);
   };
   static_assert(BLK_CHUNKS <= NTHR, "one 16-byte chunk per thread");
   // Gate inputs and outputs of block jb go through buffer descriptors that span

@@ -56,11 +56,14 @@ SQ_PASSES = [
     "SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_INSTS_LDS_STORE_BANDWIDTH SQ_INSTS_VALU_TRANS_F32 SQ_WAIT_ANY SQ_BUSY_CU_CYCLES",
 ]
 KERNELS = {"scan_mfma": "scan_mfma_kernel", "scan_generic": "scan_generic_kernel", "scan_coop": "scan_coop_kernel",
+           "scan_linear_mfma": "scan_linear_mfma_kernel", "scan_linear_generic": "scan_linear_generic_kernel",
            "projection": "proj_tiles_kernel"}
 # the sources each kernel is built from: its counters are stale once any of them changes
-KERNEL_SOURCES = {"scan_mfma": ["scan_mfma.hip", "mfma_common.h", "internal.h"],
+KERNEL_SOURCES = {"scan_mfma": ["scan_mfma.hip", "token_block.h", "mfma_common.h", "phi_poly.h", "internal.h"],
                   "scan_generic": ["generic.hip", "internal.h"],
                   "scan_coop": ["scan_coop.hip", "internal.h"],
+                  "scan_linear_mfma": ["scan_linear.hip", "token_block.h", "mfma_common.h", "internal.h"],
+                  "scan_linear_generic": ["generic.hip", "internal.h"],
                   "projection": ["proj_mfma.hip", "mfma_common.h", "internal.h"]}
 
 

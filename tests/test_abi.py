@@ -3,6 +3,7 @@ arguments on the host before touching a device (no GPU needed)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -31,10 +32,21 @@ def test_library_exports_every_declared_symbol():
     assert lib.ttt_mlp_version() >> 16 == 1
 
 
-def test_config_struct_layout_matches_header():
-    # int64 B, T; int32 H, d, m, b; float eta; int32 loss, gelu, io_dtype, algo
+def test_config_struct_layout_matches_header(tmp_path):
+    # int64 B, T; int32 H, d, m, b; float eta; int32 loss, gelu, io_dtype, algo, model
     assert ctypes.sizeof(L.Config) == 56
-    assert L.Config.eta.offset == 32 and L.Config.algo.offset == 48
+    assert L.Config.eta.offset == 32 and L.Config.algo.offset == 48 and L.Config.model.offset == 52
+    # the C compiler's view of the header agrees with the binding
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "ttt_mlp.h"\n'
+                   "int main(void) { printf(\"%zu %zu %zu %zu\\n\", sizeof(ttt_mlp_config), "
+                   "offsetof(ttt_mlp_config, eta), offsetof(ttt_mlp_config, algo), offsetof(ttt_mlp_config, model)); "
+                   "return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert [int(x) for x in out] == [ctypes.sizeof(L.Config), L.Config.eta.offset, L.Config.algo.offset,
+                                     L.Config.model.offset]
 
 
 def test_status_strings():
@@ -113,3 +125,35 @@ def test_algo_selection():
     assert e.value.status == L.TTT_ERR_UNSUPPORTED
     # coop workspace: fp32 Q, K, V plus the exchange slots (2 parities x 8 workgroups x 256 entries x 8 B per head)
     assert L.workspace_size(L.make_config(**big), False) >= 3 * 2 * 10 * 128 * 4 + 2 * 2 * 8 * 256 * 8
+
+
+def test_linear_model_selection_and_validation():
+    lin = dict(B=1, T=100, H=3, d=64, m=64, b=16, eta=0.1 / 16, model="linear")
+    assert L.select_algo(L.make_config(**lin)) == "mfma"
+    assert L.select_algo(L.make_config(**lin, io_dtype="f32")) == "generic"
+    assert L.select_algo(L.make_config(**dict(lin, b=4))) == "generic"
+    assert L.select_algo(L.make_config(**lin, algo="generic")) == "generic"
+    # the tanh GELU switch does not concern the linear model
+    assert L.select_algo(L.make_config(**lin, gelu="tanh")) == "mfma"
+    for bad in (dict(lin, m=256), dict(lin, d=32, m=64)):
+        with pytest.raises(L.TTTError) as e:
+            L.workspace_size(L.make_config(**bad), False)
+        assert e.value.status == L.TTT_ERR_INVALID_ARG
+    with pytest.raises(L.TTTError) as e:
+        L.select_algo(L.make_config(**dict(lin, d=128, m=128, b=1), algo="coop"))
+    assert e.value.status == L.TTT_ERR_UNSUPPORTED
+    c = L.make_config(**lin)
+    c.model = 5
+    with pytest.raises(L.TTTError) as e:
+        L.workspace_size(c, False)
+    assert e.value.status == L.TTT_ERR_INVALID_ARG
+    # workspace: bf16 Q, K, V token blocks plus one d x d state per head
+    assert L.workspace_size(L.make_config(**lin), True) >= 3 * 7 * 3 * 16 * 64 * 2 + 3 * 64 * 64 * 4
+    # W2_0 may be NULL for the linear model (the host checks pass it; a NULL W1_0 is refused)
+    lib = L.lib()
+    n = L.workspace_size(c.__class__(**{f: getattr(L.make_config(**lin), f) for f, _ in L.Config._fields_}), False)
+    fake = 1 << 40
+    cl = L.make_config(**lin)
+    st = lib.ttt_mlp_forward(ctypes.byref(cl), fake, fake + (1 << 32), None, None, fake + (2 << 32), 0,
+                             fake + (3 << 32), None, None, None, fake + (4 << 32), n, None)
+    assert st == L.TTT_ERR_INVALID_ARG and b"W1_0" in lib.ttt_mlp_last_error()
