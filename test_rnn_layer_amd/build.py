@@ -33,8 +33,10 @@ FLAGS = [
 # kernels that must keep their whole working set in registers: the MFMA and
 # cooperative scans hold the inner-model state in VGPRs for the whole
 # sequence (and the linear scan counts its vector-memory instructions per
-# step), so a spilling build of any of them is refused.
-NO_SPILL_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "scan_coop.hip"}
+# step), and the projection GEMM's accumulators and operands fill the register
+# file (a spill there cost a fifth of its speed), so a spilling build of any of
+# them is refused.
+NO_SPILL_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "scan_coop.hip", "proj_mfma.hip"}
 
 
 def _check_no_spill(src, remarks):

@@ -379,8 +379,11 @@ Chunking chunking(int64_t T) {
 // Projection workgroups beside the scan: at most this many, and no more than the
 // CUs the scan leaves free (a workgroup takes a whole CU's LDS, and one that
 // waits for a CU would run its share of tiles after the others); no cap when
-// fewer than kProjMinWorkgroups are free.
-constexpr int kProjWorkgroupsBesideScan = 160, kProjMinWorkgroups = 64;
+// fewer than kProjMinWorkgroups are free.  The chip shares one power budget:
+// every CU the projection keeps busy lowers the clock the scan runs at, so the
+// cap is the fewest workgroups that still keep the projection ahead of the
+// scan (bidirectional layer at 307,200 tokens, 48 heads: 96 beats 80 and 112-160).
+constexpr int kProjWorkgroupsBesideScan = 96, kProjMinWorkgroups = 64;
 
 int proj_workgroups_beside_scan(int cus, int64_t scan_workgroups) {
   const int64_t free_cus = (int64_t)cus - scan_workgroups;
@@ -409,7 +412,9 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
   hipError_t e = side_for_device(&sd, 2 + 2 * (size_t)C * ndir);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
   hipStream_t S2 = sd->stream;
-  const int proj_wg = proj_workgroups_beside_scan(sd->cus, c->B * c->H);
+  // the cap pays where the scan is the longer of the two (the MLP); the linear
+  // model's scan is a third of its projection, which then takes every free CU
+  const int proj_wg = is_linear(c) ? 0 : proj_workgroups_beside_scan(sd->cus, c->B * c->H);
   hipEvent_t* ev = sd->events.data();
   hipEvent_t ev_start = ev[0], ev_end = ev[1];
   auto ev_proj = [&](int d, int64_t k) { return ev[2 + (2 * d) * C + k]; };

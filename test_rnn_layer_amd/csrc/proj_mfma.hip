@@ -131,12 +131,17 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a) {
 // Token-block projection for the MFMA scan: 256 x 256 output tiles per
 // 512-thread workgroup (2 x 4 waves of 128 x 64), K-steps of 64 staged by
 // direct global -> LDS loads into two buffers (the next step loads while this
-// one computes).  LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled
-// by (row / 2) mod 8, so the 16 rows one 16-lane group reads hit 16 distinct
-// bank groups.  Tiles are grouped 8 (M) x all (N) and handed out per XCD so the
-// workgroups resident on one XCD share A and theta slices in its L2.  The
-// epilogue stages each wave's 128 x 64 bf16 sub-tile through LDS and writes
-// whole 128-byte token rows of the scan's token blocks.
+// one computes).  Each step reads both 32-deep halves of its operands from LDS
+// up front, the second half's reads spread over the first half's products, so
+// the matrix cores do not wait on LDS inside a step.  LDS rows are 128 bytes
+// with the 16-byte chunks XOR-swizzled by (row / 2) mod 8, so the 16 rows one
+// 16-lane group reads hit 16 distinct bank groups.  Tiles are grouped 8 (M) x
+// all (N) and handed out per XCD so the workgroups resident on one XCD share A
+// and theta slices in its L2; a workgroup takes the tiles of its XCD's range
+// in turn.  Rows past the end of X load its last row (never stored), so every
+// step issues the same loads.  The epilogue stages each wave's 128 x 64 bf16
+// sub-tile through LDS and writes whole 128-byte token rows of the scan's
+// token blocks.
 // ---------------------------------------------------------------------------
 constexpr int T_BM = 256, T_BN = 256, T_BK = 64, T_THREADS = 512;
 constexpr int T_STAGE = (T_BM + T_BN) * T_BK;  // bf16 elements per stage (64 KB)
@@ -154,8 +159,7 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int64_t M = a.B * Tw;        // tt0 + r mod Tw of sequence r / Tw
   const int N = 3 * D;
   const int K = D;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 4, c = lane & 15;
+  const int tid = threadIdx.x, lane_ = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 2, wn = w & 3;
 
   // tiles: XCD-contiguous ranges (workgroup b runs on XCD b mod 8), grouped 8
@@ -166,6 +170,10 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   for (int ti = (int)(blockIdx.x / 8); ti < per_xcd; ti += slots) {
     const int t = (int)(blockIdx.x % 8) * per_xcd + ti;
     if (t >= total) break;
+    // lane-derived addresses are recomputed per tile: hoisted out of the tile
+    // loop they would stay live across it and spill
+    int lane = lane_, g = lane_ >> 4, c = lane_ & 15;
+    asm volatile("" : "+v"(lane), "+v"(g), "+v"(c));
     const int group = t / (T_GROUP_M * ntiles);
     const int first_m = group * T_GROUP_M;
     const int gm = min(mtiles - first_m, T_GROUP_M);
@@ -179,11 +187,11 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
 
     // direct loads of one K-step: per matrix 256 rows x 8 chunks; instruction i of
     // wave w fills LDS rows 8 (8 i + w) .. +8, lane -> row + lane / 8, chunk lane % 8
-    int64_t xrow[4];  // X row of this lane's A rows (-1 past the end)
+    int64_t xrow[4];  // X row of this lane's A rows (rows past the end load the last row, never stored)
   #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t ga = m0 + 8 * (8 * i + w) + (lane >> 3);
-      xrow[i] = ga < M ? (ga / Tw) * a.T + a.tt0 + ga % Tw : -1;
+      const int64_t ga = min(m0 + 8 * (8 * i + w) + (lane >> 3), M - 1);
+      xrow[i] = (ga / Tw) * a.T + a.tt0 + ga % Tw;
     }
     auto issue = [&](int k0, int buf) {
       uint16_t* base = smem + buf * T_STAGE;
@@ -193,12 +201,10 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int gch = swz(row, lane & 7);
         uint16_t* ldsA = base + (8 * (8 * i + w)) * T_BK;
         uint16_t* ldsB = base + T_BM * T_BK + (8 * (8 * i + w)) * T_BK;
-        const int gb = n0 + row;
-        if (xrow[i] >= 0)
-          __builtin_amdgcn_global_load_lds((const void*)(X + xrow[i] * K + k0 + 8 * gch),
-                                           (__attribute__((address_space(3))) void*)ldsA, 16, 0, 0);
-        if (gb < N)
-          __builtin_amdgcn_global_load_lds((const void*)(Th + (int64_t)gb * K + k0 + 8 * gch),
+        const int gb = min(n0 + row, N - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(X + xrow[i] * K + k0 + 8 * gch),
+                                         (__attribute__((address_space(3))) void*)ldsA, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(Th + (int64_t)gb * K + k0 + 8 * gch),
                                            (__attribute__((address_space(3))) void*)ldsB, 16, 0, 0);
       }
     };
@@ -217,24 +223,34 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
       if (ks + 1 < nk) issue((ks + 1) * T_BK, (ks + 1) & 1);
       const uint16_t* As = smem + (ks & 1) * T_STAGE;
       const uint16_t* Bs = As + T_BM * T_BK;
+      bf16x8 af[2][8], bfr[2][4];
   #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 af[8], bfr[4];
   #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int row = wm * 128 + i * 16 + c;
-          af[i] = *(const bf16x8*)(As + row * T_BK + 8 * swz(row, 4 * kk + g));
+          af[kk][i] = *(const bf16x8*)(As + row * T_BK + 8 * swz(row, 4 * kk + g));
         }
   #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = wn * 64 + j * 16 + c;
-          bfr[j] = *(const bf16x8*)(Bs + row * T_BK + 8 * swz(row, 4 * kk + g));
+          bfr[kk][j] = *(const bf16x8*)(Bs + row * T_BK + 8 * swz(row, 4 * kk + g));
         }
+      }
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
   #pragma unroll
         for (int i = 0; i < 8; ++i)
   #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[kk][i], bfr[kk][j], acc[i][j]);
+      // the first half's operands, then the second half's reads spread over the first half's products
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+  #pragma unroll
+      for (int q = 0; q < 12; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 40, 0);
     }
 
     // ---- epilogue: this wave's 128 x 64 sub-tile as bf16 rows in LDS, then 16-byte stores

@@ -35,7 +35,7 @@ beside the trace):
         python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > DIR/bench.json
     python3 -m test_rnn_layer_amd.profile_counters summarize-stats DIR
 
-`summarize-stats` writes profiles/scan_mfma_proj_tiles_bidir307k_stats.md.
+`summarize-stats` writes profiles/<scan kernel>_proj_tiles_<workload>_stats.md.
 """
 from __future__ import annotations
 
@@ -283,24 +283,29 @@ def summarize_sq(dirs, out_md: str | None = None):
 
 
 def summarize_stats(d: str, out_md: str | None = None):
+    """Kernel-time table of a traced bench run (DIR/bench.json names the workload)."""
     from test_rnn_layer_amd import workloads as W
-    wl = W.WORKLOADS["bidir307k"]
     files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {d}")
     rows = list(csv.DictReader(open(files[0])))
     bench = json.loads(open(os.path.join(d, "bench.json")).read().strip().splitlines()[-1])
+    wname = bench["config"]["workload"]
+    wl = W.WORKLOADS[wname]
+    wl_arg = "" if wname == "bidir307k" else f" --workload {wname}"
+    model = "TTT-Linear, d x d state" if wl.model == "linear" else "TTT-MLP"
     steps, warm = bench["steps"], bench["warmup"]
     calls = steps + warm
     tok = wl.B * wl.T
     lines = [
-        "# Kernel time, bidir307k (one ttt_mlp_bidir call = both directions, each as chunked projection and scan launches)",
+        f"# Kernel time, {wname} (one ttt_mlp_bidir call = both directions, each as chunked projection and scan "
+        "launches)",
         "",
-        f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ/Y, fp32 state; "
+        f"Workload: {model}, B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ/Y, fp32 state; "
         f"{steps} timed + {warm} warm-up calls under the trace.", "",
         "Commands (repo root, MI355X):", "",
         f"    mkdir -p {d} && rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
-        f"python3 bench.py --steps {steps} --warmup {warm} --no-cpu-baseline > {d}/bench.json",
+        f"python3 bench.py{wl_arg} --steps {steps} --warmup {warm} --no-cpu-baseline > {d}/bench.json",
         f"    python3 -m test_rnn_layer_amd.profile_counters summarize-stats {d}", "",
         "| Kernel | Launches | Average per launch | Per call | Share of kernel time |", "|---|---|---|---|---|",
     ]
@@ -315,10 +320,10 @@ def summarize_stats(d: str, out_md: str | None = None):
               f"roofline R = {bench['layer_roofline']['R_ms']:.2f} ms); the scan's launches averaged "
               f"{rf['avg_launch_ms']:.3f} ms from HIP events on their stream, "
               f"{rf['flops_per_launch'] / 1e9:.1f} GFLOP each, {rf['achieved']:.1f} TFLOP/s. The projection runs on "
-              "a second stream beside the scan; the call's time is the scan's plus the first projection chunk of "
-              "each direction.",
+              "a second stream beside the scan; the call's time is that of the longer stream plus what cannot "
+              "overlap (the first projection chunk of each direction, the last scan chunk).",
               f"Tokens per call: {tok:,} (both directions over every token)."]
-    out_md = out_md or os.path.join(ROOT, "profiles", "scan_mfma_proj_tiles_bidir307k_stats.md")
+    out_md = out_md or os.path.join(ROOT, "profiles", f"{bench['config']['scan_kernel']}_proj_tiles_{wname}_stats.md")
     open(out_md, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
