@@ -12,6 +12,7 @@
 // Two epilogues: fp32 [3, B, H, T, d] (inspection / generic scan) and the
 // bf16 token-block layout the MFMA scan reads (see scan_mfma.hip).
 #include <algorithm>
+#include <cmath>
 
 #include "internal.h"
 #include "mfma_common.h"
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a) {
 // up front, the second half's reads spread over the first half's products, so
 // the matrix cores do not wait on LDS inside a step.  LDS rows are 128 bytes
 // with the 16-byte chunks XOR-swizzled by (row / 2) mod 8, so the 16 rows one
-// 16-lane group reads hit 16 distinct bank groups.  Tiles are grouped 8 (M) x
+// 16-lane group reads hit 16 distinct bank groups.  Tiles are grouped group_m (M) x
 // all (N) and handed out per XCD so the workgroups resident on one XCD share A
 // and theta slices in its L2; a workgroup takes the tiles of its XCD's range
 // in turn.  Rows past the end of X load its last row (never stored), so every
@@ -145,13 +146,12 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int T_BM = 256, T_BN = 256, T_BK = 64, T_THREADS = 512;
 constexpr int T_STAGE = (T_BM + T_BN) * T_BK;  // bf16 elements per stage (64 KB)
-constexpr int T_GROUP_M = 8;
 constexpr int TOK_RS = 72;                     // row stride of a token block (bf16)
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_tiles_kernel(
-    ProjArgs a, int mtiles, int ntiles) {
+    ProjArgs a, int mtiles, int ntiles, int group_m) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T_STAGE];
   const int d = a.d;
   const int D = a.H * d;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int tid = threadIdx.x, lane_ = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 2, wn = w & 3;
 
-  // tiles: XCD-contiguous ranges (workgroup b runs on XCD b mod 8), grouped 8
+  // tiles: XCD-contiguous ranges (workgroup b runs on XCD b mod 8), grouped group_m
   // m-tiles at a time; the workgroups of an XCD take its range in turn
   const int total = mtiles * ntiles;
   const int per_xcd = (total + 7) / 8;
@@ -174,10 +174,10 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
     // loop they would stay live across it and spill
     int lane = lane_, g = lane_ >> 4, c = lane_ & 15;
     asm volatile("" : "+v"(lane), "+v"(g), "+v"(c));
-    const int group = t / (T_GROUP_M * ntiles);
-    const int first_m = group * T_GROUP_M;
-    const int gm = min(mtiles - first_m, T_GROUP_M);
-    const int rem = t - group * T_GROUP_M * ntiles;
+    const int group = t / (group_m * ntiles);
+    const int first_m = group * group_m;
+    const int gm = min(mtiles - first_m, group_m);
+    const int rem = t - group * group_m * ntiles;
     const int mt = first_m + rem % gm;
     const int nt = rem / gm;
     const int64_t m0 = (int64_t)mt * T_BM;
@@ -323,7 +323,12 @@ hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s) {
     const int total = mtiles * ntiles;
     int grid = (total + 7) / 8 * 8;
     if (a.max_wg > 0) grid = std::min(grid, std::max(8, a.max_wg / 8 * 8));
-    hipLaunchKernelGGL(proj_tiles_kernel, dim3((unsigned)grid), dim3(T_THREADS), 0, s, a, mtiles, ntiles);
+    // the tiles an XCD runs at once (one workgroup per CU, 32 CUs per XCD) span
+    // group_m m-tiles x (that many / group_m) n-tiles: about square, so they
+    // share the fewest A and theta slices in the XCD's L2
+    const int resident = std::min(grid / 8, 32);
+    const int group_m = std::max(1, std::min(8, (int)std::lround(std::sqrt((double)resident))));
+    hipLaunchKernelGGL(proj_tiles_kernel, dim3((unsigned)grid), dim3(T_THREADS), 0, s, a, mtiles, ntiles, group_m);
     return hipGetLastError();
   }
   if (a.tt0 != 0 || a.tt1 != a.T) return hipErrorInvalidValue;  // the other kernels cover whole sequences
