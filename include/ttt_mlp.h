@@ -172,14 +172,49 @@ int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* th
                         float* QKV, void* stream);
 
 /*
+ * Backward of the layer (TTT_MODEL_MLP; the generic fp32 kernels, algo AUTO or
+ * GENERIC).  The outer loop of the notes page's training learns theta, the
+ * initial state and the gates through the layer; for the gradient dY of the
+ * layer output these calls return the gradients of sum(dY * Y):
+ *   dX     [B, T, D] fp32,   dtheta [3, D, D] fp32 ([out, in], as theta_qkv),
+ *   dW1_0  [H, d, m] fp32,   dW2_0  [H, m, d] fp32 (summed over the B sequences),
+ *   dalpha [D] fp32.
+ * dY is [B, T, D] fp32.  Every output is overwritten.  The call runs the
+ * forward pass again (projection and scan, keeping a checkpoint of the state
+ * every 32 mini-batches in the workspace), then the backward scan, which
+ * replays one segment of 32 mini-batches at a time from its checkpoint and
+ * walks it backwards carrying the gradient of the state, then two GEMMs:
+ * dX = dY + [dQ dK dV] theta and dtheta = [dQ dK dV]^T X.
+ * Workspace: ttt_mlp_backward_workspace_size (bidir = 0 or 1).
+ */
+int32_t ttt_mlp_backward_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t* bytes);
+
+/* One gated direction (reverse as for ttt_mlp_forward). */
+int32_t ttt_mlp_backward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv, const float* W1_0,
+                         const float* W2_0, const float* alpha, int32_t reverse, const float* dY, float* dX,
+                         float* dtheta, float* dW1_0, float* dW2_0, float* dalpha, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* The bidirectional layer (as ttt_mlp_bidir: X' is rounded to io_dtype and its
+ * rounding is passed through unchanged): dX, dtheta and dW*_0 collect both
+ * directions; dalpha_f and dalpha_b are the two gates' gradients. */
+int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv, const float* W1_0,
+                               const float* W2_0, const float* alpha_f, const float* alpha_b, const float* dY,
+                               float* dX, float* dtheta, float* dW1_0, float* dW2_0, float* dalpha_f,
+                               float* dalpha_b, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing, for measurement.  While enabled, every compute call brackets
  * each kernel launch with HIP events on the stream the kernel runs on.
  * ttt_mlp_kernel_timing waits for the recorded events and returns the summed
  * duration (ms) and launch count of one kernel kind since the last reset.
- *   kind: TTT_KERNEL_PROJECT (the projection GEMM) or TTT_KERNEL_SCAN (the scan).
+ *   kind: TTT_KERNEL_PROJECT (the projection GEMM), TTT_KERNEL_SCAN (the scan),
+ *   TTT_KERNEL_BACKWARD or TTT_KERNEL_GRAD_GEMM (below).
  */
 #define TTT_KERNEL_PROJECT 0
 #define TTT_KERNEL_SCAN 1
+#define TTT_KERNEL_BACKWARD 2  /* the backward scan */
+#define TTT_KERNEL_GRAD_GEMM 3 /* the backward's dX and dtheta GEMMs */
 int32_t ttt_mlp_set_kernel_timing(int32_t enable);
 int32_t ttt_mlp_kernel_timing(int32_t kind, double* total_ms, int64_t* launches);
 int32_t ttt_mlp_reset_kernel_timing(void);

@@ -19,13 +19,14 @@ TTT_LOSS_MEAN, TTT_LOSS_SUM = 0, 1
 TTT_GELU_ERF, TTT_GELU_TANH = 0, 1
 TTT_MODEL_MLP, TTT_MODEL_LINEAR = 0, 1
 TTT_ALGO_AUTO, TTT_ALGO_GENERIC, TTT_ALGO_MFMA, TTT_ALGO_COOP = 0, 1, 2, 3
-TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN = 0, 1
+TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN, TTT_KERNEL_BACKWARD, TTT_KERNEL_GRAD_GEMM = 0, 1, 2, 3
 
 EXPORTED = [
     "ttt_mlp_version", "ttt_mlp_status_string", "ttt_mlp_last_error", "ttt_mlp_workspace_size",
     "ttt_mlp_select_algo",
     "ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_project", "ttt_mlp_set_kernel_timing",
     "ttt_mlp_kernel_timing", "ttt_mlp_reset_kernel_timing",
+    "ttt_mlp_backward_workspace_size", "ttt_mlp_backward", "ttt_mlp_bidir_backward",
 ]
 
 
@@ -77,6 +78,14 @@ def lib() -> ctypes.CDLL:
         L.ttt_mlp_kernel_timing.restype = _i32
         L.ttt_mlp_kernel_timing.argtypes = [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.ttt_mlp_reset_kernel_timing.restype = _i32
+        L.ttt_mlp_backward_workspace_size.restype = _i32
+        L.ttt_mlp_backward_workspace_size.argtypes = [ctypes.POINTER(Config), _i32, ctypes.POINTER(_sz)]
+        L.ttt_mlp_backward.restype = _i32
+        L.ttt_mlp_backward.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _i32, _fp,
+                                       _fp, _fp, _fp, _fp, _fp, _vp, _sz, _vp]
+        L.ttt_mlp_bidir_backward.restype = _i32
+        L.ttt_mlp_bidir_backward.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _fp, _fp,
+                                             _fp, _fp, _fp, _fp, _fp, _fp, _vp, _sz, _vp]
         _lib = L
     return _lib
 
@@ -163,6 +172,50 @@ def bidir(cfg: Config, X, theta, W1_0, W2_0, alpha_f, alpha_b, *, want_z=False, 
                                _ptr(alpha_b), _ptr(Y), _ptr(Zf), _ptr(Zb), _ptr(W1f), _ptr(W2f), _ptr(W1b),
                                _ptr(W2b), _ptr(ws), ws.numel(), _stream(X.device)))
     return dict(Y=Y, Z_f=Zf, Z_b=Zb, W1_Tf=W1f, W2_Tf=W2f, W1_Tb=W1b, W2_Tb=W2b)
+
+
+def backward_workspace_size(cfg: Config, bidir: bool) -> int:
+    n = _sz(0)
+    _check(lib().ttt_mlp_backward_workspace_size(ctypes.byref(cfg), int(bidir), ctypes.byref(n)))
+    return n.value
+
+
+def _grad_outs(cfg, X):
+    import torch
+    kw = dict(dtype=torch.float32, device=X.device)
+    D = cfg.H * cfg.d
+    return dict(dX=torch.empty(X.shape, **kw), dtheta=torch.empty((3, D, D), **kw),
+                dW1_0=torch.empty((cfg.H, cfg.d, cfg.m), **kw), dW2_0=torch.empty((cfg.H, cfg.m, cfg.d), **kw))
+
+
+def backward(cfg: Config, X, theta, W1_0, W2_0, alpha, dY, *, reverse=False, workspace=None):
+    """ttt_mlp_backward: gradients of sum(dY * Y) for one direction.
+    Returns dict(dX, dtheta, dW1_0, dW2_0, dalpha), all fp32."""
+    import torch
+    g = _grad_outs(cfg, X)
+    g["dalpha"] = torch.empty(alpha.shape, dtype=torch.float32, device=X.device)
+    ws = (torch.empty(max(backward_workspace_size(cfg, False), 1), dtype=torch.uint8, device=X.device)
+          if workspace is None else workspace)
+    _check(lib().ttt_mlp_backward(ctypes.byref(cfg), _ptr(X), _ptr(theta), _ptr(W1_0), _ptr(W2_0), _ptr(alpha),
+                                  int(reverse), _ptr(dY), _ptr(g["dX"]), _ptr(g["dtheta"]), _ptr(g["dW1_0"]),
+                                  _ptr(g["dW2_0"]), _ptr(g["dalpha"]), _ptr(ws), ws.numel(), _stream(X.device)))
+    return g
+
+
+def bidir_backward(cfg: Config, X, theta, W1_0, W2_0, alpha_f, alpha_b, dY, *, workspace=None):
+    """ttt_mlp_bidir_backward: gradients of sum(dY * Y) for the bidirectional layer.
+    Returns dict(dX, dtheta, dW1_0, dW2_0, dalpha_f, dalpha_b), all fp32."""
+    import torch
+    g = _grad_outs(cfg, X)
+    g["dalpha_f"] = torch.empty(alpha_f.shape, dtype=torch.float32, device=X.device)
+    g["dalpha_b"] = torch.empty(alpha_b.shape, dtype=torch.float32, device=X.device)
+    ws = (torch.empty(max(backward_workspace_size(cfg, True), 1), dtype=torch.uint8, device=X.device)
+          if workspace is None else workspace)
+    _check(lib().ttt_mlp_bidir_backward(ctypes.byref(cfg), _ptr(X), _ptr(theta), _ptr(W1_0), _ptr(W2_0),
+                                        _ptr(alpha_f), _ptr(alpha_b), _ptr(dY), _ptr(g["dX"]), _ptr(g["dtheta"]),
+                                        _ptr(g["dW1_0"]), _ptr(g["dW2_0"]), _ptr(g["dalpha_f"]),
+                                        _ptr(g["dalpha_b"]), _ptr(ws), ws.numel(), _stream(X.device)))
+    return g
 
 
 def project(cfg: Config, X, theta):

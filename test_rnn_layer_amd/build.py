@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libttt_mlp.so")
-SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_linear.hip", "scan_coop.hip"]
+SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_linear.hip", "scan_coop.hip",
+           "backward.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -43,8 +43,9 @@ struct TimingRecord {
 std::mutex g_timing_mu;
 bool g_timing_on = false;
 std::vector<TimingRecord> g_timing_records;
-double g_timing_ms[2] = {0, 0};
-int64_t g_timing_n[2] = {0, 0};
+constexpr int kTimingKinds = 4;
+double g_timing_ms[kTimingKinds] = {};
+int64_t g_timing_n[kTimingKinds] = {};
 
 // Collect the finished records into the per-kind sums (caller holds the lock).
 hipError_t drain_timing_locked() {
@@ -481,6 +482,138 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
   return TTT_OK;
 }
 
+// ---------------------------------------------------------------------------
+// backward (generic fp32 path)
+// ---------------------------------------------------------------------------
+// The forward pass runs again inside the backward call (projection, then the
+// generic scan, which leaves a checkpoint of the state every kCkptEvery
+// mini-batches); the backward scan replays one segment at a time from its
+// checkpoint.  The checkpoints of a direction take B*H*ceil(T/b/kCkptEvery)
+// states, the replayed segment B*H*kCkptEvery.
+constexpr int kCkptEvery = 32;
+
+struct BwdPlan {
+  Plan fwd;  // the forward pass's Q/K/V and state slices (generic layout)
+  size_t dqkv_off, z_off[2], y_off, xp_off, dxp_off, ckpt_off[2], segst_off, dstate_off, scratch_off, dwseq_off,
+      dal_off, total;
+};
+
+int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
+  int32_t st = check_config(c);
+  if (st != TTT_OK) return st;
+  if (is_linear(c)) return fail(TTT_ERR_UNSUPPORTED, "the backward covers the MLP model only");
+  if (c->algo != TTT_ALGO_AUTO && c->algo != TTT_ALGO_GENERIC)
+    return fail(TTT_ERR_UNSUPPORTED, "the backward runs the generic fp32 scans (algo AUTO or GENERIC, got %d)",
+                c->algo);
+  if (ttt::scan_generic_lds_bytes(c->d, c->m, c->b) > kGenericLdsMax ||
+      ttt::scan_backward_lds_bytes(c->d, c->b) > kGenericLdsMax)
+    return fail(TTT_ERR_UNSUPPORTED, "backward: mini-batch working set (d=%d m=%d b=%d) exceeds %zu bytes of LDS",
+                c->d, c->m, c->b, kGenericLdsMax);
+  const size_t D = (size_t)c->H * c->d, BTD = (size_t)c->B * c->T * D, BH = (size_t)c->B * c->H;
+  const size_t st2 = 2 * (size_t)c->d * c->m * sizeof(float);  // one (W1, W2) state
+  const size_t nseg = ((size_t)(c->T + c->b - 1) / c->b + kCkptEvery - 1) / kCkptEvery;
+  const size_t io = c->io_dtype == TTT_BF16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  Plan& f = p->fwd;
+  f.algo = TTT_ALGO_GENERIC;
+  f.io_elem = io;
+  f.qkv_bytes = align_up(3 * BTD * sizeof(float));
+  f.qkv_off = take(3 * BTD * sizeof(float));
+  f.wst_bytes = align_up(BH * st2);
+  f.wst_off = take(BH * st2);  // the forward scan's state, then the backward's replayed state
+  p->dqkv_off = take(3 * BTD * sizeof(float));
+  p->z_off[0] = take(BTD * sizeof(float));
+  p->z_off[1] = bidir ? take(BTD * sizeof(float)) : 0;
+  p->y_off = take(BTD * io);
+  p->xp_off = bidir ? take(BTD * io) : 0;
+  p->dxp_off = bidir ? take(BTD * sizeof(float)) : 0;
+  p->ckpt_off[0] = take(BH * nseg * st2);
+  p->ckpt_off[1] = bidir ? take(BH * nseg * st2) : 0;
+  p->segst_off = take(BH * kCkptEvery * st2);
+  p->dstate_off = take(BH * st2);
+  p->scratch_off = take(BH * ttt::kBwdScratchPanels * (size_t)c->b * c->m * sizeof(float));
+  p->dwseq_off = take(BH * st2);
+  p->dal_off = take(ttt::dalpha_partial_elems((int)D) * sizeof(float));
+  p->total = off;
+  f.total = off;
+  return TTT_OK;
+}
+
+// Projection of xin into the plan's Q/K/V slice (fp32, [3, B, H, T, d]).
+int32_t bwd_project(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin, const void* theta, char* ws,
+                    hipStream_t s) {
+  const ttt::ProjArgs pa = proj_args(c, bp.fwd, xin, theta, 0, ws);
+  hipError_t e = timed_launch(TTT_KERNEL_PROJECT, s, [&] { return launch_projection(pa, 0, s); });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+  return TTT_OK;
+}
+
+// The forward pass of one direction, keeping Z and the state checkpoints.
+int32_t bwd_forward(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin, const void* theta, const float* W1_0,
+                    const float* W2_0, const float* alpha, int reverse, void* y, float* z, float* ckpt, char* ws,
+                    hipStream_t s) {
+  int32_t st = bwd_project(c, bp, xin, theta, ws, s);
+  if (st != TTT_OK) return st;
+  ttt::ScanArgs sa = scan_args(c, bp.fwd, xin, W1_0, W2_0, alpha, reverse, y, z, nullptr, nullptr, ws);
+  sa.ckpt = ckpt;
+  sa.ckpt_every = kCkptEvery;
+  hipError_t e = timed_launch(TTT_KERNEL_SCAN, s, [&] { return ttt::launch_scan_generic(sa, s); });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+  return TTT_OK;
+}
+
+// The backward of one direction whose forward pass (bwd_forward) left its Q/K/V in
+// the workspace: dX = dyin + dQKV theta; dtheta, dW1_0, dW2_0 written or accumulated.
+int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin, const void* theta,
+                      const float* alpha, int reverse, const float* dyin, const float* ckpt, const float* z, float* dX,
+                      float* dtheta, float* dW1_0, float* dW2_0, int accumulate, float* dalpha, char* ws,
+                      hipStream_t s) {
+  const int64_t D = (int64_t)c->H * c->d, BT = c->B * c->T;
+  const bool bf16 = c->io_dtype == TTT_BF16;
+  float* dqkv = (float*)(ws + bp.dqkv_off);
+  float* dw_seq = (float*)(ws + bp.dwseq_off);
+  ttt::BwdArgs ba{};
+  ba.qkv = (const float*)(ws + bp.fwd.qkv_off);
+  ba.dy = dyin;
+  ba.alpha = alpha;
+  ba.ckpt = ckpt;
+  ba.segst = (float*)(ws + bp.segst_off);
+  ba.wcur = (float*)(ws + bp.fwd.wst_off);
+  ba.dstate = (float*)(ws + bp.dstate_off);
+  ba.scratch = (float*)(ws + bp.scratch_off);
+  ba.dqkv = dqkv;
+  ba.dw_seq = dw_seq;
+  ba.B = c->B;
+  ba.T = c->T;
+  ba.H = c->H;
+  ba.d = c->d;
+  ba.m = c->m;
+  ba.b = c->b;
+  ba.ckpt_every = kCkptEvery;
+  ba.eta = c->eta;
+  ba.gscale = c->loss == TTT_LOSS_MEAN ? 2.0f / (float)c->d : 2.0f;
+  ba.gelu_tanh = c->gelu == TTT_GELU_TANH;
+  ba.reverse = reverse;
+  hipError_t e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] { return ttt::launch_scan_backward(ba, s); });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
+  e = ttt::launch_dalpha(dyin, z, alpha, (float*)(ws + bp.dal_off), dalpha, BT, (int)D, s);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "dalpha launch: %s", hipGetErrorString(e));
+  e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
+    hipError_t r = ttt::launch_gemm_f32(false, bf16, dqkv, 3 * D, theta, D, dX, D, dyin, BT, D, 3 * D, 0, s);
+    if (r != hipSuccess) return r;
+    return ttt::launch_gemm_f32(true, bf16, dqkv, 3 * D, xin, D, dtheta, D, nullptr, 3 * D, D, BT, accumulate, s);
+  });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "gradient GEMM launch: %s", hipGetErrorString(e));
+  e = ttt::launch_sum_state(dw_seq, dW1_0, dW2_0, c->B, c->H, c->d, c->m, accumulate, s);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "state gradient launch: %s", hipGetErrorString(e));
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -598,6 +731,97 @@ int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* thet
   return st == TTT_OK ? ok() : st;
 }
 
+int32_t ttt_mlp_backward_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t* bytes) {
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  BwdPlan bp;
+  int32_t st = make_bwd_plan(cfg, bidir != 0, &bp);
+  if (st != TTT_OK) return st;
+  *bytes = bp.total;
+  return ok();
+}
+
+int32_t ttt_mlp_backward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv, const float* W1_0,
+                         const float* W2_0, const float* alpha, int32_t reverse, const float* dY, float* dX,
+                         float* dtheta, float* dW1_0, float* dW2_0, float* dalpha, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  BwdPlan bp;
+  int32_t st = make_bwd_plan(cfg, 0, &bp);
+  if (st != TTT_OK) return st;
+  const bool no_tokens = cfg->T == 0;
+  if ((!no_tokens && (!X || !dY || !dX)) || !theta_qkv || !W1_0 || !W2_0 || !alpha || !dtheta || !dW1_0 ||
+      !dW2_0 || !dalpha)
+    return fail(TTT_ERR_INVALID_ARG, "a required pointer (X, theta_qkv, W1_0, W2_0, alpha, dY, dX, dtheta, dW1_0, "
+                                     "dW2_0, dalpha) is NULL");
+  if (!workspace || workspace_bytes < bp.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                bp.total);
+  const size_t io = bp.fwd.io_elem;
+  const size_t D = (size_t)cfg->H * cfg->d, BTD = (size_t)cfg->B * cfg->T * D;
+  const size_t w0 = (size_t)cfg->H * cfg->d * cfg->m * 4;
+  const Buf outs[] = {{dX, BTD * 4, "dX"},         {dtheta, 3 * D * D * 4, "dtheta"}, {dW1_0, w0, "dW1_0"},
+                      {dW2_0, w0, "dW2_0"},        {dalpha, D * 4, "dalpha"},        {workspace, bp.total, "workspace"}};
+  const Buf ins[] = {{X, BTD * io, "X"},   {theta_qkv, 3 * D * D * io, "theta_qkv"}, {W1_0, w0, "W1_0"},
+                     {W2_0, w0, "W2_0"}, {alpha, D * 4, "alpha"},                 {dY, BTD * 4, "dY"}};
+  st = check_no_overlap(outs, 6, ins, 6);
+  if (st != TTT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* z = (float*)(ws + bp.z_off[0]);
+  float* ck = (float*)(ws + bp.ckpt_off[0]);
+  st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha, reverse != 0, ws + bp.y_off, z, ck, ws, s);
+  if (st != TTT_OK) return st;
+  st = bwd_direction(cfg, bp, X, theta_qkv, alpha, reverse != 0, dY, ck, z, dX, dtheta, dW1_0, dW2_0, 0, dalpha, ws, s);
+  return st == TTT_OK ? ok() : st;
+}
+
+int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv, const float* W1_0,
+                               const float* W2_0, const float* alpha_f, const float* alpha_b, const float* dY,
+                               float* dX, float* dtheta, float* dW1_0, float* dW2_0, float* dalpha_f,
+                               float* dalpha_b, void* workspace, size_t workspace_bytes, void* stream) {
+  BwdPlan bp;
+  int32_t st = make_bwd_plan(cfg, 1, &bp);
+  if (st != TTT_OK) return st;
+  const bool no_tokens = cfg->T == 0;
+  if ((!no_tokens && (!X || !dY || !dX)) || !theta_qkv || !W1_0 || !W2_0 || !alpha_f || !alpha_b || !dtheta ||
+      !dW1_0 || !dW2_0 || !dalpha_f || !dalpha_b)
+    return fail(TTT_ERR_INVALID_ARG, "a required pointer (X, theta_qkv, W1_0, W2_0, alpha_f, alpha_b, dY, dX, "
+                                     "dtheta, dW1_0, dW2_0, dalpha_f, dalpha_b) is NULL");
+  if (!workspace || workspace_bytes < bp.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                bp.total);
+  const size_t io = bp.fwd.io_elem;
+  const size_t D = (size_t)cfg->H * cfg->d, BTD = (size_t)cfg->B * cfg->T * D;
+  const size_t w0 = (size_t)cfg->H * cfg->d * cfg->m * 4;
+  const Buf outs[] = {{dX, BTD * 4, "dX"},           {dtheta, 3 * D * D * 4, "dtheta"}, {dW1_0, w0, "dW1_0"},
+                      {dW2_0, w0, "dW2_0"},          {dalpha_f, D * 4, "dalpha_f"},    {dalpha_b, D * 4, "dalpha_b"},
+                      {workspace, bp.total, "workspace"}};
+  const Buf ins[] = {{X, BTD * io, "X"},         {theta_qkv, 3 * D * D * io, "theta_qkv"}, {W1_0, w0, "W1_0"},
+                     {W2_0, w0, "W2_0"},       {alpha_f, D * 4, "alpha_f"},            {alpha_b, D * 4, "alpha_b"},
+                     {dY, BTD * 4, "dY"}};
+  st = check_no_overlap(outs, 7, ins, 7);
+  if (st != TTT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* xp = ws + bp.xp_off;  // X', the forward pass's output (io_dtype, as the forward call keeps it)
+  float* dxp = (float*)(ws + bp.dxp_off);
+  float* zf = (float*)(ws + bp.z_off[0]);
+  float* zb = (float*)(ws + bp.z_off[1]);
+  float* ckf = (float*)(ws + bp.ckpt_off[0]);
+  float* ckb = (float*)(ws + bp.ckpt_off[1]);
+  // the two forward passes, keeping X', Z and the checkpoints
+  st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha_f, 0, xp, zf, ckf, ws, s);
+  if (st == TTT_OK) st = bwd_forward(cfg, bp, xp, theta_qkv, W1_0, W2_0, alpha_b, 1, ws + bp.y_off, zb, ckb, ws, s);
+  // the reversed pass's backward (its Q/K/V, of X', are in the workspace): dX' = dY + ...
+  if (st == TTT_OK)
+    st = bwd_direction(cfg, bp, xp, theta_qkv, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws,
+                       s);
+  // the forward pass's backward, with dY = dX' and X's Q/K/V projected again
+  if (st == TTT_OK) st = bwd_project(cfg, bp, X, theta_qkv, ws, s);
+  if (st == TTT_OK)
+    st = bwd_direction(cfg, bp, X, theta_qkv, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s);
+  return st == TTT_OK ? ok() : st;
+}
+
 int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv, float* QKV,
                         void* stream) {
   int32_t st = check_config(cfg);
@@ -635,8 +859,7 @@ int32_t ttt_mlp_set_kernel_timing(int32_t enable) {
 }
 
 int32_t ttt_mlp_kernel_timing(int32_t kind, double* total_ms, int64_t* launches) {
-  if (kind != TTT_KERNEL_PROJECT && kind != TTT_KERNEL_SCAN)
-    return fail(TTT_ERR_INVALID_ARG, "unknown kernel kind %d", kind);
+  if (kind < 0 || kind >= kTimingKinds) return fail(TTT_ERR_INVALID_ARG, "unknown kernel kind %d", kind);
   if (!total_ms || !launches) return fail(TTT_ERR_INVALID_ARG, "total_ms and launches are required");
   std::lock_guard<std::mutex> lk(g_timing_mu);
   hipError_t e = drain_timing_locked();
@@ -649,8 +872,10 @@ int32_t ttt_mlp_kernel_timing(int32_t kind, double* total_ms, int64_t* launches)
 int32_t ttt_mlp_reset_kernel_timing(void) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   hipError_t e = drain_timing_locked();
-  g_timing_ms[0] = g_timing_ms[1] = 0;
-  g_timing_n[0] = g_timing_n[1] = 0;
+  for (int k = 0; k < kTimingKinds; ++k) {
+    g_timing_ms[k] = 0;
+    g_timing_n[k] = 0;
+  }
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "timing events: %s", hipGetErrorString(e));
   return ok();
 }

@@ -55,6 +55,8 @@ struct ScanArgs {
   int32_t reverse;
   int32_t bf16;          // io dtype of xin / y
   int32_t linear;        // 1: linear inner model f(u; W) = u W (W = w1, d x d; w2 unused)
+  float* ckpt;           // generic MLP scan only, or null: the state (W1 then W2) at the start of
+  int32_t ckpt_every;    // every ckpt_every-th mini-batch, [B, H, nseg, 2 d m]
 };
 
 // LDS bytes the generic scan needs for (d, m, b).
@@ -80,5 +82,40 @@ bool scan_coop_supported(int d, int m, int b, int64_t T);
 bool scan_coop_fits(int64_t B, int H);  // co-residency on the current device
 size_t scan_coop_xchg_bytes(int64_t B, int H);  // exchange slots
 hipError_t launch_scan_coop(const ScanArgs& a, hipStream_t s);
+
+// Backward of one direction of the MLP layer (generic, fp32): the backward scan
+// (one workgroup per (sequence, head)) walks segments of ckpt_every
+// mini-batches from the last, replaying each from its checkpoint.
+constexpr int kBwdScratchPanels = 11;  // b x m fp32 panels per workgroup
+struct BwdArgs {
+  const float* qkv;    // [3, B, H, T, d] fp32: the direction's projections of its input
+  const float* dy;     // [B, T, D] fp32: gradient of the direction's output Y
+  const float* alpha;  // [D] the direction's gate
+  const float* ckpt;   // [B, H, nseg, 2 d m]: written by the generic scan
+  float* segst;        // [B, H, ckpt_every, 2 d m] workspace: states of one segment's mini-batches
+  float* wcur;         // [B, H, 2 d m] workspace: replayed state
+  float* dstate;       // [B, H, 2 d m] workspace: adjoint of the state
+  float* scratch;      // [B, H, kBwdScratchPanels, b, m] workspace
+  float* dqkv;         // [B, T, 3 D] out: dQ | dK | dV per token
+  float* dw_seq;       // [B, H, 2 d m] out: adjoint of the initial state, per sequence
+  int64_t B, T;
+  int32_t H, d, m, b, ckpt_every;
+  float eta, gscale;
+  int32_t gelu_tanh, reverse;
+};
+size_t scan_backward_lds_bytes(int d, int b);
+hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
+// C = (accumulate ? C : Cadd or 0) + A B, fp32 (A [M, K] row-major, or [K, M] when
+// a_transposed; B [K, N] row-major, fp32 or bf16)
+hipError_t launch_gemm_f32(bool a_transposed, bool b_bf16, const float* A, int64_t lda, const void* Bm, int64_t ldb,
+                           float* C, int64_t ldc, const float* Cadd, int64_t M, int64_t N, int64_t K, int accumulate,
+                           hipStream_t s);
+// dalpha[c] = (1 - tanh(alpha[c])^2) sum_r dy[r, c] z[r, c]; part: dalpha_partial_elems(D) floats
+size_t dalpha_partial_elems(int D);
+hipError_t launch_dalpha(const float* dy, const float* z, const float* alpha, float* part, float* dalpha,
+                         int64_t rows, int D, hipStream_t s);
+// dW1 [H, d, m], dW2 [H, m, d] (+)= sum over sequences of dw_seq [B, H, 2 d m]
+hipError_t launch_sum_state(const float* dw_seq, float* dW1, float* dW2, int64_t B, int H, int d, int m,
+                            int accumulate, hipStream_t s);
 
 }  // namespace ttt

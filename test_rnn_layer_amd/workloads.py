@@ -30,7 +30,7 @@ from dataclasses import dataclass
 import numpy as np
 
 # tensor ids inside the seed sequence
-TID_X, TID_THETA_Q, TID_THETA_K, TID_THETA_V, TID_W1, TID_W2, TID_SEGMEAN = range(7)
+TID_X, TID_THETA_Q, TID_THETA_K, TID_THETA_V, TID_W1, TID_W2, TID_SEGMEAN, TID_DY = range(8)
 X_CHUNK = 4096
 
 
@@ -182,6 +182,21 @@ def make_w0(wl: Workload) -> tuple[np.ndarray, np.ndarray]:
 def make_alpha(wl: Workload, value: float | None = None) -> np.ndarray:
     """Gate vector alpha [D], float32 (every channel starts at the same value)."""
     return np.full(wl.D, wl.alpha_f if value is None else value, dtype=np.float32)
+
+
+def make_dy(wl: Workload, t1: int | None = None, heads=None) -> np.ndarray:
+    """An upstream gradient of the layer output, dY [B, T, D] float32 ~ N(0, 1).
+    t1 / heads: zero from token t1 on (only the first t1 rows are drawn), and
+    outside the listed heads' channels."""
+    n = wl.T if t1 is None else t1
+    g = np.zeros((wl.B, wl.T, wl.D), dtype=np.float32)
+    g[:, :n] = _rng(wl.seed, TID_DY).standard_normal((wl.B, n, wl.D))
+    if heads is not None:
+        keep = np.zeros(wl.D, dtype=bool)
+        for h in heads:
+            keep[h * wl.d:(h + 1) * wl.d] = True
+        g[..., ~keep] = 0.0
+    return g
 
 
 def make_inputs(wl: Workload) -> dict:

@@ -157,3 +157,34 @@ def test_linear_model_selection_and_validation():
     st = lib.ttt_mlp_forward(ctypes.byref(cl), fake, fake + (1 << 32), None, None, fake + (2 << 32), 0,
                              fake + (3 << 32), None, None, None, fake + (4 << 32), n, None)
     assert st == L.TTT_ERR_INVALID_ARG and b"W1_0" in lib.ttt_mlp_last_error()
+
+
+def test_backward_workspace_and_validation():
+    c = cfg(algo="auto")
+    one, two = L.backward_workspace_size(c, False), L.backward_workspace_size(c, True)
+    # at least Q/K/V and their gradients in fp32, Z, and one checkpoint per direction
+    assert one >= 2 * 3 * 64 * 128 * 4 + 64 * 128 * 4 + 2 * 2 * 64 * 256 * 4
+    assert two > one
+    assert L.backward_workspace_size(cfg(T=0), True) > 0
+    for bad, status in [(dict(model="linear", m=64), L.TTT_ERR_UNSUPPORTED), (dict(algo="mfma"), L.TTT_ERR_UNSUPPORTED),
+                        (dict(b=64, m=512, d=128), L.TTT_ERR_UNSUPPORTED), (dict(eta=-1.0), L.TTT_ERR_INVALID_ARG)]:
+        with pytest.raises(L.TTTError) as e:
+            L.backward_workspace_size(cfg(**bad), False)
+        assert e.value.status == status, bad
+    lib = L.lib()
+    n = L.backward_workspace_size(c, False)
+    fake = 1 << 40  # never dereferenced: the host checks fail first
+    f = lambda k: fake + (k << 32)
+    st = lib.ttt_mlp_backward(ctypes.byref(c), f(0), f(1), f(2), f(3), f(4), 0, None, f(5), f(6), f(7), f(8), f(9),
+                              f(10), n, None)
+    assert st == L.TTT_ERR_INVALID_ARG  # dY missing
+    st = lib.ttt_mlp_backward(ctypes.byref(c), f(0), f(1), f(2), f(3), f(4), 0, f(11), f(5), f(6), f(7), f(8), f(9),
+                              f(10), n - 1, None)
+    assert st == L.TTT_ERR_WORKSPACE
+    st = lib.ttt_mlp_backward(ctypes.byref(c), f(0), f(1), f(2), f(3), f(4), 0, f(11), f(11) + 64, f(6), f(7), f(8),
+                              f(9), f(10), n, None)
+    assert st == L.TTT_ERR_INVALID_ARG and b"overlaps" in lib.ttt_mlp_last_error()  # dX over dY
+    n2 = L.backward_workspace_size(c, True)
+    st = lib.ttt_mlp_bidir_backward(ctypes.byref(c), f(0), f(1), f(2), f(3), f(4), None, f(11), f(5), f(6), f(7),
+                                    f(8), f(9), f(12), f(10), n2, None)
+    assert st == L.TTT_ERR_INVALID_ARG  # alpha_b missing

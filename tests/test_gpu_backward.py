@@ -1,0 +1,151 @@
+"""GPU parity of the layer's backward (ttt_mlp_backward, ttt_mlp_bidir_backward)
+against the fp64 backward oracle (autograd through the primal-form layer) on
+the same seeded inputs and upstream gradient.
+
+Tolerance: the backward computes in fp32 throughout (bf16 inputs are exact in
+fp32), so every gradient must match to 1e-4 of its own largest magnitude
+(max-abs error / max |reference|).  The bidirectional layer with bf16 io rounds
+X' to bf16 between the passes, as the forward call does, while the oracle keeps
+it in fp64: there the bf16 bar applies, relative L2 <= 2e-2."""
+import numpy as np
+import pytest
+
+from oracle import ttt_backward_oracle as BO
+from test_rnn_layer_amd import workloads as W
+
+from tests._common import device_inputs, f64_inputs, from_device, rel_l2
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL_MAX_TOL = 1e-4
+BF16_TOL = 2e-2
+
+_F32 = W.WORKLOADS["tiny_f32"]
+CASES = {
+    # per-token steps, d = 16, m = 64
+    "f32_b1": _F32.replace(T=40, name="f32_b1"),
+    # mini-batches with a ragged tail; 75 mini-batches = three checkpoint segments of 32
+    "f32_b4_segments": _F32.replace(T=298, H=2, d=8, m=32, b=4, eta=0.2, name="f32_b4_segments"),
+    # the sum loss and the tanh GELU
+    "f32_sum_tanh": _F32.replace(T=37, H=2, d=8, m=16, b=3, eta=0.02, loss="sum", gelu="tanh",
+                                 name="f32_sum_tanh"),
+    # the bidir307k head shape (bf16 X and theta), two heads, ragged tail
+    "bf16_d64": W.WORKLOADS["bidir307k"].replace(T=72, H=2, seg_len=0, name="bf16_d64"),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from test_rnn_layer_amd import _lib
+    _lib.lib()  # the HIP library must load: no fallback
+    yield
+
+
+def _cfg(wl):
+    from test_rnn_layer_amd import _lib
+    return _lib.make_config(wl.B, wl.T, wl.H, wl.d, wl.m, wl.b, wl.eta, io_dtype=wl.io_dtype, loss=wl.loss,
+                            gelu=wl.gelu)
+
+
+def _check(name, got, ref, tol=REL_MAX_TOL):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    print(f"  {name}: max-abs {err:.3e} of max |ref| {scale:.3e}", flush=True)
+    assert err <= tol * max(scale, 1e-30), (name, err, scale)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("case", list(CASES))
+def test_backward_matches_oracle(case, reverse):
+    from test_rnn_layer_amd import _lib
+    wl = CASES[case]
+    print(f"[backward] case={case} reverse={reverse} B{wl.B} T{wl.T} H{wl.H} d{wl.d} m{wl.m} b{wl.b}", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    dy = W.make_dy(wl)
+    g = _lib.backward(_cfg(wl), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"],
+                      torch.from_numpy(dy).cuda(), reverse=reverse)
+    torch.cuda.synchronize()
+    f64 = f64_inputs(wl, inp)
+    ref = BO.ttt_mlp_backward(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64["alpha_f"], dy.astype(np.float64),
+                              eta=wl.eta, b=wl.b, reverse=reverse, loss=wl.loss, gelu_form=wl.gelu)
+    for k in ["dX", "dtheta", "dW1_0", "dW2_0", "dalpha"]:
+        _check(k, from_device(g[k]), ref[k])
+
+
+@pytest.mark.parametrize("case", ["f32_b1", "f32_b4_segments", "bf16_d64"])
+def test_bidir_backward_matches_oracle(case):
+    from test_rnn_layer_amd import _lib
+    wl = CASES[case].replace(alpha_f=0.3, alpha_b=-0.2)  # distinct gates catch a swap
+    print(f"[bidir backward] case={case}", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    dy = W.make_dy(wl)
+    g = _lib.bidir_backward(_cfg(wl), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"],
+                            dev["alpha_b"], torch.from_numpy(dy).cuda())
+    torch.cuda.synchronize()
+    f64 = f64_inputs(wl, inp)
+    ref = BO.ttt_mlp_bidir_backward(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64["alpha_f"],
+                                    f64["alpha_b"], dy.astype(np.float64), eta=wl.eta, b=wl.b, loss=wl.loss,
+                                    gelu_form=wl.gelu)
+    for k in ["dX", "dtheta", "dW1_0", "dW2_0", "dalpha_f", "dalpha_b"]:
+        if wl.io_dtype == "f32":
+            _check(k, from_device(g[k]), ref[k])
+        else:
+            err = rel_l2(from_device(g[k]), ref[k])
+            print(f"  {k}: rel-L2 {err:.3e}", flush=True)
+            assert err <= BF16_TOL, (k, err)
+
+
+def test_backward_properties_bitwise():
+    """Determinism; a zero gate passes dY straight through (dX = dY, nothing else
+    moves); causality (dY on the first P tokens only leaves dX zero after them);
+    the bidirectional call equals the reversed pass's backward followed by the
+    forward pass's backward with dY = the reversed pass's dX."""
+    from test_rnn_layer_amd import _lib
+    wl = CASES["f32_b4_segments"]
+    print("[backward properties]", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    cfg = _cfg(wl)
+    dy = torch.from_numpy(W.make_dy(wl)).cuda()
+    a = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dy)
+    b = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dy)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    z = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], torch.zeros_like(dev["alpha_f"]), dy)
+    torch.cuda.synchronize()
+    assert torch.equal(z["dX"], dy)
+    for k in ["dtheta", "dW1_0", "dW2_0"]:
+        assert not torch.any(z[k]), k
+    P = 100
+    dyp = torch.from_numpy(W.make_dy(wl, t1=P)).cuda()
+    c = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dyp)
+    torch.cuda.synchronize()
+    assert not torch.any(c["dX"][:, P:]) and torch.any(c["dX"][:, :P])
+    # the bidirectional chain, bitwise
+    fw = _lib.forward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"])
+    bd = _lib.bidir_backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dev["alpha_b"], dy)
+    r = _lib.backward(cfg, fw["Y"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_b"], dy, reverse=True)
+    f = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], r["dX"])
+    torch.cuda.synchronize()
+    assert torch.equal(bd["dX"], f["dX"])
+    assert torch.equal(bd["dalpha_b"], r["dalpha"]) and torch.equal(bd["dalpha_f"], f["dalpha"])
+    assert torch.allclose(bd["dtheta"], f["dtheta"] + r["dtheta"], rtol=1e-6, atol=1e-6)
+
+
+def test_backward_no_tokens():
+    from test_rnn_layer_amd import _lib
+    wl = CASES["f32_b1"].replace(T=0)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    g = _lib.backward(_cfg(wl), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"],
+                      torch.zeros_like(dev["X"], dtype=torch.float32))
+    torch.cuda.synchronize()
+    for k in ["dtheta", "dW1_0", "dW2_0", "dalpha"]:
+        assert not torch.any(g[k]), k
