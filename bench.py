@@ -1,11 +1,12 @@
 """Benchmark of the TTT-MLP bidirectional layer (one GPU).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bidir307k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bidir307k] [--backward]
 
 A step is one ttt_mlp_bidir call over the whole sequence: projections, the
 forward scan with its gate, the projections of X', the reversed scan with its
-gate.  Inputs are seeded synthetic tensors already resident in device memory.
-Prints one JSON line.
+gate.  With --backward a step is one ttt_mlp_bidir_backward call instead (the
+gradients of sum(dY * Y) for a seeded dY).  Inputs are seeded synthetic
+tensors already resident in device memory.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TTT-MLP bidirectional layer tokens/sec at 307,200 tokens; % of roofline"
 METRIC_LINEAR = "TTT-Linear bidirectional layer tokens/sec at 307,200 tokens; % of roofline"
+METRIC_BACKWARD = "TTT-MLP bidirectional layer backward tokens/sec at 307,200 tokens; % of roofline"
 # MI355X published peaks
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
@@ -39,6 +41,17 @@ def linear_scan_flops_per_token_head(d: int, b: int) -> int:
     """The linear inner model: three d x d contractions (K W, Q W, K^T G) plus the
     causal halves of tril(Q K^T) and of its product with G."""
     return 3 * 2 * d * d + (b + 1) * 2 * d
+
+
+def backward_scan_flops_per_token_head(d: int, m: int, b: int) -> int:
+    """Algorithmic flops of the backward scan per token and head: the mini-batch's
+    forward quantities again (K W1, Hk W2, G2 W2^T, Q W1: 4 d x m contractions), the
+    gradient contractions (dZ W2^T, dAq W1^T, G2 dW2^T, Hk dW2, K dW1, G1 dW1^T, dGh W2,
+    dYh W2^T, dA W1^T: 9) and the state adjoints (Q^T dAq, K^T dA, Hq^T dZ, dGh^T G2,
+    Hk^T dYh: 5), plus the causal halves of the b x b products (5 over d, 6 over m).
+    The replay of each segment from its checkpoint (10 d m per token) is
+    recomputation and not counted."""
+    return 18 * 2 * d * m + (b + 1) * (5 * d + 6 * m)
 
 
 def proj_flops_per_token(D: int) -> int:
@@ -91,6 +104,104 @@ def cpu_baseline(wl, tokens: int):
                        f"fp64 NumPy, {dt:.1f} s wall")
 
 
+def cpu_baseline_backward(wl, tokens: int):
+    """The fp64 backward oracle (autograd through the primal-form layer) on the
+    first `tokens` tokens of the same workload, every head, both directions."""
+    import numpy as np
+    import torch
+
+    from oracle import ttt_backward_oracle as BO
+    from test_rnn_layer_amd import workloads as W
+
+    sub = wl.replace(T=tokens)
+    inp = W.make_inputs(sub)
+    X = W.to_f64(inp["X"], sub.io_dtype)
+    th = W.to_f64(inp["theta"], sub.io_dtype)
+    dy = W.make_dy(sub).astype(np.float64)
+    t0 = time.perf_counter()
+    BO.ttt_mlp_bidir_backward(X, th, inp["W1_0"].astype(np.float64), inp["W2_0"].astype(np.float64),
+                              inp["alpha_f"].astype(np.float64), inp["alpha_b"].astype(np.float64), dy,
+                              eta=sub.eta, b=sub.b, loss=sub.loss, gelu_form=sub.gelu)
+    dt = time.perf_counter() - t0
+    return dict(value=tokens / dt, unit="tokens/s", cores=torch.get_num_threads(), kind="oracle",
+                sample=f"{wl.name} workload, first {tokens} tokens, all {wl.H} heads, both directions, "
+                       f"fp64 torch autograd, {dt:.1f} s wall")
+
+
+def bench_backward(args, wl):
+    """--backward: one ttt_mlp_bidir_backward call per step."""
+    import numpy as np
+    import torch
+
+    from test_rnn_layer_amd import _lib
+    from test_rnn_layer_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(wl)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    io = bf if wl.io_dtype == "bf16" else f32
+    X, th = io(inp["X"]), io(inp["theta"])
+    W1, W2 = f32(inp["W1_0"]), f32(inp["W2_0"])
+    af, ab = f32(inp["alpha_f"]), f32(inp["alpha_b"])
+    dY = f32(W.make_dy(wl))
+    del inp
+    cfg = _lib.make_config(wl.B, wl.T, wl.H, wl.d, wl.m, wl.b, wl.eta, io_dtype=wl.io_dtype, loss=wl.loss,
+                           gelu=wl.gelu)
+    ws = torch.empty(_lib.backward_workspace_size(cfg, True), dtype=torch.uint8, device=dev)
+    step = lambda: _lib.bidir_backward(cfg, X, th, W1, W2, af, ab, dY, workspace=ws)
+    print(f"# bench: backward, inputs resident ({ws.numel() / 1e9:.1f} GB workspace), warming up", file=sys.stderr,
+          flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.set_kernel_timing(True)
+    _lib.reset_kernel_timing()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        torch.cuda.synchronize()
+        print(f"# bench: backward step {i + 1} done", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kinds = {"backward_scan": _lib.TTT_KERNEL_BACKWARD, "forward_scan": _lib.TTT_KERNEL_SCAN,
+             "projection": _lib.TTT_KERNEL_PROJECT, "gradient_gemms": _lib.TTT_KERNEL_GRAD_GEMM}
+    km = {k: _lib.kernel_timing(v) for k, v in kinds.items()}
+    _lib.set_kernel_timing(False)
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = wl.B * wl.T
+    dirs = 2
+    bms, bn = km["backward_scan"]
+    fpt = backward_scan_flops_per_token_head(wl.d, wl.m, wl.b)
+    flops_launch = fpt * wl.H * tokens * dirs * args.steps / bn
+    avg_ms = bms / bn
+    achieved = flops_launch / (avg_ms / 1e3) / 1e12
+    # layer: the gradient GEMMs (dX and dtheta, 12 D^2 per token and direction) at the bf16 peak,
+    # both scans (the forward pass again, and the backward) at the fp32 peak
+    gemm_total = 12 * wl.D * wl.D * tokens * dirs
+    scan_total = (fpt + scan_flops_per_token_head(wl.d, wl.m, wl.b)) * wl.H * tokens * dirs
+    R_ms = (gemm_total / (PEAK_BF16_TFLOPS * 1e12) + scan_total / (PEAK_FP32_TFLOPS * 1e12)) * 1e3
+    out = {
+        "metric": METRIC_BACKWARD, "value": tokens / (ms_per_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "d": wl.d, "m": wl.m, "b": wl.b,
+                   "eta": wl.eta, "D": wl.D, "directions": dirs, "pass": "backward",
+                   "scan_kernel": "scan_backward", "model": wl.model},
+        "roofline": {"bound": "alu", "kernel": "scan_backward", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops_launch, "avg_launch_ms": avg_ms},
+        "layer_roofline": {"R_ms": R_ms, "frac": R_ms / ms_per_step,
+                           "definition": "gradient GEMM flops at bf16 MFMA peak + forward and backward scan flops "
+                                         "at fp32 peak"},
+        "kernel_ms_per_step": {k: ms / args.steps for k, (ms, n) in km.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("# bench: timing the CPU backward oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_backward(wl, args.cpu_tokens or 16)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,8 +209,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="bidir307k")
     ap.add_argument("--algo", default="auto", choices=["auto", "generic", "mfma"])
-    ap.add_argument("--cpu-tokens", type=int, default=24576)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens of the CPU oracle's sample (default 24576; 16 with --backward)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true", help="time ttt_mlp_bidir_backward instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer's heads would shard across GPUs, but this build "
@@ -117,6 +230,11 @@ def main():
     torch.cuda.set_device(dev)
     print(f"# bench: workload {wl.name} B={wl.B} T={wl.T} H={wl.H} d={wl.d} m={wl.m} b={wl.b}", file=sys.stderr,
           flush=True)
+    if args.backward:
+        if wl.model != "mlp":
+            print("bench.py --backward: the backward covers the MLP model only", file=sys.stderr)
+            sys.exit(2)
+        return bench_backward(args, wl)
     inp = W.make_inputs(wl)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -187,7 +305,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("# bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens or 24576)
     print(json.dumps(out), flush=True)
 
 

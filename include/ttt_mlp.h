@@ -172,7 +172,7 @@ int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* th
                         float* QKV, void* stream);
 
 /*
- * Backward of the layer (TTT_MODEL_MLP; the generic fp32 kernels, algo AUTO or
+ * Backward of the layer (TTT_MODEL_MLP, d and m multiples of 4; fp32 kernels, algo AUTO or
  * GENERIC).  The outer loop of the notes page's training learns theta, the
  * initial state and the gates through the layer; for the gradient dY of the
  * layer output these calls return the gradients of sum(dY * Y):

@@ -485,10 +485,10 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
 // ---------------------------------------------------------------------------
 // backward (generic fp32 path)
 // ---------------------------------------------------------------------------
-// The forward pass runs again inside the backward call (projection, then the
-// generic scan, which leaves a checkpoint of the state every kCkptEvery
-// mini-batches); the backward scan replays one segment at a time from its
-// checkpoint.  The checkpoints of a direction take B*H*ceil(T/b/kCkptEvery)
+// The forward pass runs again inside the backward call (projection, then a
+// forward scan built from the backward's own steps, which leaves a checkpoint
+// of the state every kCkptEvery mini-batches); the backward scan replays one
+// segment at a time from its checkpoint.  The checkpoints of a direction take B*H*ceil(T/b/kCkptEvery)
 // states, the replayed segment B*H*kCkptEvery.
 constexpr int kCkptEvery = 32;
 
@@ -505,10 +505,11 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   if (c->algo != TTT_ALGO_AUTO && c->algo != TTT_ALGO_GENERIC)
     return fail(TTT_ERR_UNSUPPORTED, "the backward runs the generic fp32 scans (algo AUTO or GENERIC, got %d)",
                 c->algo);
-  if (ttt::scan_generic_lds_bytes(c->d, c->m, c->b) > kGenericLdsMax ||
-      ttt::scan_backward_lds_bytes(c->d, c->b) > kGenericLdsMax)
-    return fail(TTT_ERR_UNSUPPORTED, "backward: mini-batch working set (d=%d m=%d b=%d) exceeds %zu bytes of LDS",
-                c->d, c->m, c->b, kGenericLdsMax);
+  if (ttt::scan_backward_lds_bytes(c->d, c->b) > kGenericLdsMax)
+    return fail(TTT_ERR_UNSUPPORTED, "backward: mini-batch working set (d=%d b=%d) exceeds %zu bytes of LDS", c->d,
+                c->b, kGenericLdsMax);
+  if (c->d % 4 != 0 || c->m % 4 != 0)
+    return fail(TTT_ERR_UNSUPPORTED, "backward: d and m must be multiples of 4 (got d=%d m=%d)", c->d, c->m);
   const size_t D = (size_t)c->H * c->d, BTD = (size_t)c->B * c->T * D, BH = (size_t)c->B * c->H;
   const size_t st2 = 2 * (size_t)c->d * c->m * sizeof(float);  // one (W1, W2) state
   const size_t nseg = ((size_t)(c->T + c->b - 1) / c->b + kCkptEvery - 1) / kCkptEvery;
@@ -562,7 +563,8 @@ int32_t bwd_forward(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin,
   ttt::ScanArgs sa = scan_args(c, bp.fwd, xin, W1_0, W2_0, alpha, reverse, y, z, nullptr, nullptr, ws);
   sa.ckpt = ckpt;
   sa.ckpt_every = kCkptEvery;
-  hipError_t e = timed_launch(TTT_KERNEL_SCAN, s, [&] { return ttt::launch_scan_generic(sa, s); });
+  sa.scratch = (float*)(ws + bp.scratch_off);
+  hipError_t e = timed_launch(TTT_KERNEL_SCAN, s, [&] { return ttt::launch_scan_fwd_ckpt(sa, s); });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   return TTT_OK;
 }

@@ -5,8 +5,8 @@
 // respect to the projections' outputs Q, K, V, the initial state and the gate,
 // and the two GEMMs that carry dQ, dK, dV back to X and theta.
 //
-// The forward pass runs first (the generic scan) and leaves the state at the
-// start of every C-th mini-batch in the workspace.  The backward scan then
+// The forward pass runs first (scan_fwd_ckpt_kernel) and leaves the state at
+// the start of every C-th mini-batch in the workspace.  The backward scan then
 // walks the segments of C mini-batches from the last to the first: it replays
 // the segment's forward updates from its checkpoint, keeping the state each
 // mini-batch starts from, and walks the segment's mini-batches backwards,
@@ -29,18 +29,37 @@
 //   dW1 = dW1' + Q^T dAq + K^T dA
 //   dW2 = dW2' + Hq^T dZ + dGh^T G2 + Hk^T (c dG2)
 // and dW1, dW2 are the adjoints handed to the mini-batch before.  fp32
-// throughout; one workgroup per (sequence, head), the b x d and b x b
-// operands in LDS, the b x m ones in a per-workgroup workspace slice.
+// throughout; one 1024-thread workgroup per (sequence, head), the b x d and
+// b x b operands in LDS, the b x m ones in a per-workgroup workspace slice,
+// the state and its adjoint in the workspace.  Products with the state give
+// each thread one output column and a few rows, reading operands 16 bytes at
+// a time (d and m multiples of 4).
 #include "internal.h"
 
 namespace ttt {
 namespace {
 
-constexpr int BW = 256;  // threads of the backward scan's workgroup
+constexpr int BW = 1024;  // threads of the scan kernels' workgroups (16 waves, 4 per SIMD)
 
 __device__ inline float load_io(const void* p, int64_t i, int bf16) {
   if (bf16) return __uint_as_float((uint32_t)(((const uint16_t*)p)[i]) << 16);
   return ((const float*)p)[i];
+}
+
+__device__ inline void store_io(void* p, int64_t i, float v, int bf16) {
+  if (bf16) {
+    uint32_t u = __float_as_uint(v);
+    uint16_t r;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      r = (uint16_t)((u >> 16) | 0x40u);  // keep NaN a NaN
+    } else {
+      u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even
+      r = (uint16_t)(u >> 16);
+    }
+    ((uint16_t*)p)[i] = r;
+  } else {
+    ((float*)p)[i] = v;
+  }
 }
 
 // GELU and its first two derivatives.  erf form: GELU = a Phi(a),
@@ -64,16 +83,115 @@ __device__ inline void gelu3(float a, int tanh_form, float* g, float* dg, float*
   *ddg = phi * (2.0f - a * a);
 }
 
-// out[r, c] (R x C, row stride ldo) = s * sum_k A(r, k) B(k, c), added to out when acc;
-// tril: entries with c > r are zero.
-template <class FA, class FB>
-__device__ inline void mm(float* out, int ldo, int R, int C, int K, FA A, FB B, float s, bool acc, bool tril = false) {
-  for (int i = threadIdx.x; i < R * C; i += BW) {
-    const int r = i / C, c = i - (i / C) * C;
+// out[r, c] = (acc ? out[r, c] : 0) + s sum_{k<K} X[r, k] W(k, c) for r < n, c < C, with
+// W(k, c) = W[k ldw + c], or W[c ldw + k] when WT.  K, ldx and ldw are multiples of 4 and
+// X, W 16-byte aligned.  A thread takes one column and RG rows; k advances by 4 (X, and
+// W when WT, in 16-byte loads), in order, so every sum runs k = 0, 1, ... .
+template <int RG, bool WT>
+__device__ void prod(float* out, int ldo, int n, int C, int K, const float* X, int ldx, const float* W, int ldw,
+                     float s, bool acc) {
+  const int groups = (n + RG - 1) / RG;
+  for (int it = threadIdx.x; it < C * groups; it += BW) {
+    const int c = it % C, r0 = (it / C) * RG;
+    float a[RG];
+    const float* xr[RG];
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      a[i] = 0.0f;
+      xr[i] = X + (int64_t)min(r0 + i, n - 1) * ldx;
+    }
+    for (int k = 0; k < K; k += 4) {
+      float4 w;
+      if (WT) {
+        w = *(const float4*)(W + (int64_t)c * ldw + k);
+      } else {
+        w.x = W[(int64_t)k * ldw + c];
+        w.y = W[(int64_t)(k + 1) * ldw + c];
+        w.z = W[(int64_t)(k + 2) * ldw + c];
+        w.w = W[(int64_t)(k + 3) * ldw + c];
+      }
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+        const float4 x = *(const float4*)(xr[i] + k);
+        a[i] = fmaf(x.x, w.x, a[i]);
+        a[i] = fmaf(x.y, w.y, a[i]);
+        a[i] = fmaf(x.z, w.z, a[i]);
+        a[i] = fmaf(x.w, w.w, a[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RG; ++i)
+      if (r0 + i < n) {
+        float* o = out + (r0 + i) * ldo + c;
+        *o = (acc ? *o : 0.0f) + s * a[i];
+      }
+  }
+}
+
+// Up to three rank-n terms of a state-shaped update: S[k, c] += s sum_p sum_{r<n} P_p[r, k] Q_p[r, c]
+// for k < R, c < C.  P rows are contiguous in k (row stride a multiple of 4); KG divides R.
+// A thread takes one column and KG consecutive k.
+struct Terms {
+  int np;
+  const float* P[3];
+  int ldp[3];
+  const float* Q[3];
+  int ldq[3];
+};
+
+template <int KG>
+__device__ void rank_update(float* S, int ldS, int R, int C, int n, const Terms& tm, float s) {
+  const int kg = R / KG;
+  for (int it = threadIdx.x; it < C * kg; it += BW) {
+    const int c = it % C, k0 = (it / C) * KG;
+    float a[KG];
+#pragma unroll
+    for (int i = 0; i < KG; ++i) a[i] = 0.0f;
+    for (int p = 0; p < tm.np; ++p)
+      for (int r = 0; r < n; ++r) {
+        const float q = tm.Q[p][r * tm.ldq[p] + c];
+        const float* pr = tm.P[p] + r * tm.ldp[p] + k0;
+#pragma unroll
+        for (int i = 0; i < KG; i += 4) {
+          const float4 v = *(const float4*)(pr + i);
+          a[i] = fmaf(v.x, q, a[i]);
+          a[i + 1] = fmaf(v.y, q, a[i + 1]);
+          a[i + 2] = fmaf(v.z, q, a[i + 2]);
+          a[i + 3] = fmaf(v.w, q, a[i + 3]);
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < KG; ++i) S[(int64_t)(k0 + i) * ldS + c] += s * a[i];
+  }
+}
+
+__device__ inline void rank_update_any(float* S, int ldS, int R, int C, int n, const Terms& tm, float s) {
+  if (R % 16 == 0)
+    rank_update<16>(S, ldS, R, C, n, tm, s);
+  else
+    rank_update<4>(S, ldS, R, C, n, tm, s);
+}
+
+// out[r, c] (n x n, row stride ldo) = s sum_{k<K} X[r, k] Y[c, k] for c <= r, 0 above the
+// diagonal.  Four lanes share an output, each summing every fourth k; lane exchanges add the
+// four partial sums.
+__device__ void rowdot_tril(float* out, int ldo, int n, int K, const float* X, int ldx, const float* Y, int ldy,
+                            float s) {
+  const int nn = n * n;
+  for (int base = 0; base < 4 * nn; base += BW) {  // the same trip count in every lane
+    const int it = base + (int)threadIdx.x;
+    const int o = it >> 2, q = it & 3;
+    int r = 0, c = 0;
     float v = 0.0f;
-    if (!tril || c <= r)
-      for (int k = 0; k < K; ++k) v = fmaf(A(r, k), B(k, c), v);
-    out[r * ldo + c] = acc ? out[r * ldo + c] + s * v : s * v;
+    if (o < nn) {
+      r = o / n;
+      c = o - r * n;
+      if (c <= r)
+        for (int k = q; k < K; k += 4) v = fmaf(X[r * ldx + k], Y[c * ldy + k], v);
+    }
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    if (o < nn && q == 0) out[r * ldo + c] = s * v;
   }
 }
 
@@ -87,54 +205,7 @@ struct MB {
   float *A, *Hk, *S1, *Gh, *G1, *Aq, *Hq, *dAq, *dHk, *dG1, *dGh;
 };
 
-// The forward quantities of one mini-batch that the state update needs:
-// A, Hk, S1, G2 (in place of V), Gh, G1.
-__device__ void forward_core(const MB& t, const float* W1, const float* W2, int n, int d, int m, float gscale,
-                             int gelu_tanh) {
-  // A = K W1
-  mm(t.A, m, n, m, d, [&](int r, int k) { return t.K[r * d + k]; }, [&](int k, int c) { return W1[k * m + c]; },
-     1.0f, false);
-  __syncthreads();
-  for (int i = threadIdx.x; i < n * m; i += BW) {
-    float g, dg, ddg;
-    gelu3(t.A[i], gelu_tanh, &g, &dg, &ddg);
-    t.Hk[i] = g;
-    t.S1[i] = dg;
-  }
-  __syncthreads();
-  // G2 = c (Hk W2 - V), in place of V
-  for (int i = threadIdx.x; i < n * d; i += BW) {
-    const int r = i / d, c = i - (i / d) * d;
-    float v = 0.0f;
-    for (int k = 0; k < m; ++k) v = fmaf(t.Hk[r * m + k], W2[k * d + c], v);
-    t.G2[i] = gscale * (v - t.G2[i]);
-  }
-  __syncthreads();
-  // Gh = G2 W2^T; G1 = Gh * S1
-  for (int i = threadIdx.x; i < n * m; i += BW) {
-    const int r = i / m, c = i - (i / m) * m;
-    float v = 0.0f;
-    for (int k = 0; k < d; ++k) v = fmaf(t.G2[r * d + k], W2[c * d + k], v);
-    t.Gh[i] = v;
-    t.G1[i] = v * t.S1[i];
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
-  extern __shared__ float lds[];
-  const int d = a.d, m = a.m, b = a.b, tid = threadIdx.x;
-  const int64_t T = a.T;
-  const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const int D = a.H * d;
-  const float eta = a.eta;
-  const int64_t dm = (int64_t)d * m;
-  const int64_t nmb = (T + b - 1) / b;
-  const int C = a.ckpt_every;
-  const int64_t nseg = (nmb + C - 1) / C;
-  const int64_t sh = (int64_t)s * a.H + h;
-
-  MB t;
+__device__ void bind_panels(MB& t, float* lds, float* sc, int b, int d, int m) {
   t.K = lds;
   t.Q = t.K + b * d;
   t.G2 = t.Q + b * d;
@@ -147,10 +218,147 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   t.N = t.M + b * b;
   t.dM = t.N + b * b;
   t.dN = t.dM + b * b;
-  float* sc = a.scratch + sh * (int64_t)kBwdScratchPanels * b * m;
   float** panels[] = {&t.A, &t.Hk, &t.S1, &t.Gh, &t.G1, &t.Aq, &t.Hq, &t.dAq, &t.dHk, &t.dG1, &t.dGh};
   for (int i = 0; i < kBwdScratchPanels; ++i) *panels[i] = sc + (int64_t)i * b * m;
+}
 
+// The forward quantities of one mini-batch that the state update needs:
+// A, Hk, S1, G2 (in place of V), Gh, G1.
+__device__ void forward_core(const MB& t, const float* W1, const float* W2, int n, int d, int m, float gscale,
+                             int gelu_tanh) {
+  prod<4, false>(t.A, m, n, m, d, t.K, d, W1, m, 1.0f, false);  // A = K W1
+  __syncthreads();
+  for (int i = threadIdx.x; i < n * m; i += BW) {
+    float g, dg, ddg;
+    gelu3(t.A[i], gelu_tanh, &g, &dg, &ddg);
+    t.Hk[i] = g;
+    t.S1[i] = dg;
+  }
+  for (int i = threadIdx.x; i < n * d; i += BW) t.G2[i] *= -gscale;  // -c V
+  __syncthreads();
+  prod<1, false>(t.G2, d, n, d, m, t.Hk, m, W2, d, gscale, true);  // G2 = c (Hk W2 - V)
+  __syncthreads();
+  prod<4, true>(t.Gh, m, n, m, d, t.G2, d, W2, d, 1.0f, false);  // Gh = G2 W2^T
+  __syncthreads();
+  for (int i = threadIdx.x; i < n * m; i += BW) t.G1[i] = t.Gh[i] * t.S1[i];
+  __syncthreads();
+}
+
+// W1 -= eta K^T G1; W2 -= eta Hk^T G2
+__device__ void state_step(const MB& t, float* W1, float* W2, int n, int d, int m, float eta) {
+  Terms t1{1, {t.K}, {d}, {t.G1}, {m}};
+  rank_update_any(W1, m, d, m, n, t1, -eta);
+  Terms t2{1, {t.Hk}, {m}, {t.G2}, {d}};
+  rank_update_any(W2, d, m, d, n, t2, -eta);
+}
+
+// Aq = Q W1 - eta tril(Q K^T) G1 and Hq = GELU(Aq) (GELU'(Aq) into dq when non-null).
+__device__ void readout_hidden(const MB& t, const float* W1, int n, int b, int d, int m, float eta, int gelu_tanh,
+                               float* dq) {
+  rowdot_tril(t.M, b, n, d, t.Q, d, t.K, d, 1.0f);  // M = tril(Q K^T)
+  prod<4, false>(t.Aq, m, n, m, d, t.Q, d, W1, m, 1.0f, false);
+  __syncthreads();
+  for (int i = threadIdx.x; i < n * m; i += BW) {
+    const int r = i / m, c = i - r * m;
+    float corr = 0.0f;
+    for (int k = 0; k <= r; ++k) corr = fmaf(t.M[r * b + k], t.G1[k * m + c], corr);
+    const float aq = t.Aq[i] - eta * corr;
+    float g, dg, ddg;
+    gelu3(aq, gelu_tanh, &g, &dg, &ddg);
+    t.Aq[i] = aq;
+    t.Hq[i] = g;
+    if (dq) dq[i] = dg;
+  }
+  __syncthreads();
+}
+
+struct Rows {
+  const float *qb, *kb, *vb;
+  int64_t T;
+  int reverse;
+  __device__ int64_t tok(int64_t pos) const { return reverse ? T - 1 - pos : pos; }
+};
+
+// K, V (into G2), Q rows of the mini-batch starting at scan position p0
+__device__ void load_qkv(const MB& t, const Rows& rw, int64_t p0, int n, int d) {
+  for (int i = threadIdx.x; i < n * d; i += BW) {
+    const int r = i / d, c = i - r * d;
+    const int64_t tt = rw.tok(p0 + r);
+    t.K[i] = rw.kb[tt * d + c];
+    t.G2[i] = rw.vb[tt * d + c];
+    t.Q[i] = rw.qb[tt * d + c];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward pass for the backward: one direction, Z and Y out, and the state at
+// the start of every ckpt_every-th mini-batch (the same steps the backward
+// replays, so the replayed states are these states bit for bit).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(BW) void scan_fwd_ckpt_kernel(ScanArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int d = a.d, m = a.m, b = a.b;
+  const int64_t T = a.T;
+  const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int D = a.H * d;
+  const int64_t dm = (int64_t)d * m;
+  const int64_t sh = (int64_t)s * a.H + h;
+  const int64_t nmb = (T + b - 1) / b;
+  const int64_t nseg = (nmb + a.ckpt_every - 1) / a.ckpt_every;
+  MB t;
+  bind_panels(t, lds, a.scratch + sh * (int64_t)kBwdScratchPanels * b * m, b, d, m);
+  float* W1 = a.wstate + sh * 2 * dm;
+  float* W2 = W1 + dm;
+  for (int64_t i = threadIdx.x; i < dm; i += BW) {
+    W1[i] = a.w1_0[(int64_t)h * dm + i];
+    W2[i] = a.w2_0[(int64_t)h * dm + i];
+  }
+  const int64_t plane = a.B * a.H * T * d;
+  Rows rw{a.qkv + sh * T * d, a.qkv + plane + sh * T * d, a.qkv + 2 * plane + sh * T * d, T, a.reverse};
+  __syncthreads();
+  for (int64_t j = 0; j < nmb; ++j) {
+    const int n = (int)min((int64_t)b, T - j * b);
+    if (j % a.ckpt_every == 0) {
+      float* ck = a.ckpt + (sh * nseg + j / a.ckpt_every) * 2 * dm;
+      for (int64_t i = threadIdx.x; i < 2 * dm; i += BW) ck[i] = W1[i];
+    }
+    load_qkv(t, rw, j * b, n, d);
+    __syncthreads();
+    forward_core(t, W1, W2, n, d, m, a.gscale, a.gelu_tanh);
+    readout_hidden(t, W1, n, b, d, m, a.eta, a.gelu_tanh, nullptr);
+    rowdot_tril(t.N, b, n, m, t.Hq, m, t.Hk, m, 1.0f);  // N = tril(Hq Hk^T)
+    prod<1, false>(t.dZ, d, n, d, m, t.Hq, m, W2, d, 1.0f, false);  // Hq W2
+    __syncthreads();
+    // Z = Hq W2 - eta N G2, the gate, and the state step
+    for (int i = threadIdx.x; i < n * d; i += BW) {
+      const int r = i / d, c = i - r * d;
+      float corr = 0.0f;
+      for (int k = 0; k <= r; ++k) corr = fmaf(t.N[r * b + k], t.G2[k * d + c], corr);
+      const float z = t.dZ[i] - a.eta * corr;
+      const int64_t o = ((int64_t)s * T + rw.tok(j * b + r)) * D + (int64_t)h * d + c;
+      a.z[o] = z;
+      store_io(a.y, o, load_io(a.xin, o, a.bf16) + tanhf(a.alpha[h * d + c]) * z, a.bf16);
+    }
+    state_step(t, W1, W2, n, d, m, a.eta);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int d = a.d, m = a.m, b = a.b, tid = threadIdx.x;
+  const int64_t T = a.T;
+  const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int D = a.H * d;
+  const float eta = a.eta;
+  const int64_t dm = (int64_t)d * m;
+  const int64_t nmb = (T + b - 1) / b;
+  const int C = a.ckpt_every;
+  const int64_t nseg = (nmb + C - 1) / C;
+  const int64_t sh = (int64_t)s * a.H + h;
+
+  MB t;
+  bind_panels(t, lds, a.scratch + sh * (int64_t)kBwdScratchPanels * b * m, b, d, m);
   float* Wc1 = a.wcur + sh * 2 * dm;  // replayed state
   float* Wc2 = Wc1 + dm;
   float* dW1 = a.dstate + sh * 2 * dm;  // adjoint of the state after the current mini-batch
@@ -159,29 +367,11 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   for (int64_t i = tid; i < 2 * dm; i += BW) dW1[i] = 0.0f;
 
   const int64_t plane = a.B * a.H * T * d;
-  const float* qb = a.qkv + sh * T * d;
-  const float* kb = qb + plane;
-  const float* vb = kb + plane;
-  auto tok = [&](int64_t pos) { return a.reverse ? T - 1 - pos : pos; };
-  // K, V (and Q, dZ) rows of mini-batch j into LDS
-  auto load_rows = [&](int64_t j, int n, bool all) {
-    for (int i = tid; i < n * d; i += BW) {
-      const int r = i / d, c = i - (i / d) * d;
-      const int64_t t_ = tok(j * b + r);
-      t.K[i] = kb[t_ * d + c];
-      t.G2[i] = vb[t_ * d + c];
-      if (all) {
-        t.Q[i] = qb[t_ * d + c];
-        const int ch = h * d + c;
-        t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + t_) * D + ch];
-      }
-    }
-    __syncthreads();
-  };
+  Rows rw{a.qkv + sh * T * d, a.qkv + plane + sh * T * d, a.qkv + 2 * plane + sh * T * d, T, a.reverse};
 
   for (int64_t sg = nseg - 1; sg >= 0; --sg) {
     const int64_t j0 = sg * C, j1 = min(nmb, j0 + C);
-    // replay the segment's forward updates from its checkpoint
+    // replay the segment's forward steps from its checkpoint, keeping each mini-batch's start state
     const float* ck = a.ckpt + (sh * nseg + sg) * 2 * dm;
     for (int64_t i = tid; i < 2 * dm; i += BW) Wc1[i] = ck[i];
     __syncthreads();
@@ -190,14 +380,10 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       for (int64_t i = tid; i < 2 * dm; i += BW) dst[i] = Wc1[i];
       if (j + 1 == j1) break;
       const int n = (int)min((int64_t)b, T - j * b);
+      load_qkv(t, rw, j * b, n, d);
       __syncthreads();
-      load_rows(j, n, false);
       forward_core(t, Wc1, Wc2, n, d, m, a.gscale, a.gelu_tanh);
-      // W1 -= eta K^T G1; W2 -= eta Hk^T G2
-      mm(Wc1, m, d, m, n, [&](int r, int k) { return t.K[k * d + r]; }, [&](int k, int c) { return t.G1[k * m + c]; },
-         -eta, true);
-      mm(Wc2, d, m, d, n, [&](int r, int k) { return t.Hk[k * m + r]; }, [&](int k, int c) { return t.G2[k * d + c]; },
-         -eta, true);
+      state_step(t, Wc1, Wc2, n, d, m, eta);
       __syncthreads();
     }
     __syncthreads();
@@ -206,77 +392,62 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       const int n = (int)min((int64_t)b, T - j * b);
       const float* W1 = seg + (j - j0) * 2 * dm;
       const float* W2 = W1 + dm;
-      load_rows(j, n, true);
-      forward_core(t, W1, W2, n, d, m, a.gscale, a.gelu_tanh);
-      // M = tril(Q K^T)
-      mm(t.M, b, n, n, d, [&](int r, int k) { return t.Q[r * d + k]; }, [&](int k, int c) { return t.K[c * d + k]; },
-         1.0f, false, true);
-      __syncthreads();
-      // Aq = Q W1 - eta M G1; Hq = GELU(Aq), keeping GELU'(Aq) in dAq
-      for (int i = tid; i < n * m; i += BW) {
-        const int r = i / m, c = i - (i / m) * m;
-        float v = 0.0f, corr = 0.0f;
-        for (int k = 0; k < d; ++k) v = fmaf(t.Q[r * d + k], W1[k * m + c], v);
-        for (int k = 0; k <= r; ++k) corr = fmaf(t.M[r * b + k], t.G1[k * m + c], corr);
-        const float aq = v - eta * corr;
-        float g, dg, ddg;
-        gelu3(aq, a.gelu_tanh, &g, &dg, &ddg);
-        t.Aq[i] = aq;
-        t.Hq[i] = g;
-        t.dAq[i] = dg;
+      load_qkv(t, rw, j * b, n, d);
+      for (int i = tid; i < n * d; i += BW) {
+        const int r = i / d, c = i - r * d;
+        const int ch = h * d + c;
+        t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + ch];
       }
       __syncthreads();
-      // N = tril(Hq Hk^T); dN = tril(-eta dZ G2^T)
-      mm(t.N, b, n, n, m, [&](int r, int k) { return t.Hq[r * m + k]; }, [&](int k, int c) { return t.Hk[c * m + k]; },
-         1.0f, false, true);
-      mm(t.dN, b, n, n, d, [&](int r, int k) { return t.dZ[r * d + k]; }, [&](int k, int c) { return t.G2[c * d + k]; },
-         -eta, false, true);
+      forward_core(t, W1, W2, n, d, m, a.gscale, a.gelu_tanh);
+      readout_hidden(t, W1, n, b, d, m, eta, a.gelu_tanh, t.dAq);  // dAq holds GELU'(Aq) for now
+      // N = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
+      rowdot_tril(t.N, b, n, m, t.Hq, m, t.Hk, m, 1.0f);
+      rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta);
+      prod<4, true>(t.dGh, m, n, m, d, t.dZ, d, W2, d, 1.0f, false);
       __syncthreads();
-      // dAq = (dZ W2^T + dN Hk) * GELU'(Aq)
+      // dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dG2 = -eta N^T dZ; dHk = dN^T Hq
       for (int i = tid; i < n * m; i += BW) {
-        const int r = i / m, c = i - (i / m) * m;
-        float v = 0.0f;
-        for (int k = 0; k < d; ++k) v = fmaf(t.dZ[r * d + k], W2[c * d + k], v);
+        const int r = i / m, c = i - r * m;
+        float v = t.dGh[i];
         for (int k = 0; k <= r; ++k) v = fmaf(t.dN[r * b + k], t.Hk[k * m + c], v);
         t.dAq[i] *= v;
-      }
-      // dG2 = -eta N^T dZ
-      mm(t.dG2, d, n, d, n, [&](int r, int k) { return t.N[k * b + r]; }, [&](int k, int c) { return t.dZ[k * d + c]; },
-         -eta, false);
-      // dHk = dN^T Hq
-      mm(t.dHk, m, n, m, n, [&](int r, int k) { return t.dN[k * b + r]; }, [&](int k, int c) { return t.Hq[k * m + c]; },
-         1.0f, false);
-      __syncthreads();
-      // dQ = dAq W1^T; dM = tril(-eta dAq G1^T)
-      mm(t.dQ, d, n, d, m, [&](int r, int k) { return t.dAq[r * m + k]; }, [&](int k, int c) { return W1[c * m + k]; },
-         1.0f, false);
-      mm(t.dM, b, n, n, m, [&](int r, int k) { return t.dAq[r * m + k]; }, [&](int k, int c) { return t.G1[c * m + k]; },
-         -eta, false, true);
-      // the state-update paths, with the adjoints of the state after this mini-batch:
-      // dHk += -eta G2 dW2'^T; dG2 += -eta Hk dW2'
-      mm(t.dHk, m, n, m, d, [&](int r, int k) { return t.G2[r * d + k]; }, [&](int k, int c) { return dW2[c * d + k]; },
-         -eta, true);
-      mm(t.dG2, d, n, d, m, [&](int r, int k) { return t.Hk[r * m + k]; }, [&](int k, int c) { return dW2[k * d + c]; },
-         -eta, true);
-      __syncthreads();
-      // dG1 = -eta M^T dAq - eta K dW1'; dQ += dM K; dK = dM^T Q - eta G1 dW1'^T
-      for (int i = tid; i < n * m; i += BW) {
-        const int r = i / m, c = i - (i / m) * m;
-        float v = 0.0f, w = 0.0f;
-        for (int k = r; k < n; ++k) v = fmaf(t.M[k * b + r], t.dAq[k * m + c], v);
-        for (int k = 0; k < d; ++k) w = fmaf(t.K[r * d + k], dW1[k * m + c], w);
-        t.dG1[i] = -eta * (v + w);
+        float w = 0.0f;
+        for (int k = r; k < n; ++k) w = fmaf(t.dN[k * b + r], t.Hq[k * m + c], w);
+        t.dHk[i] = w;
       }
       for (int i = tid; i < n * d; i += BW) {
-        const int r = i / d, c = i - (i / d) * d;
-        float q = 0.0f, k1 = 0.0f, k2 = 0.0f;
+        const int r = i / d, c = i - r * d;
+        float v = 0.0f;
+        for (int k = r; k < n; ++k) v = fmaf(t.N[k * b + r], t.dZ[k * d + c], v);
+        t.dG2[i] = -eta * v;
+      }
+      __syncthreads();
+      // dQ = dAq W1^T; dM = tril(-eta dAq G1^T); with the adjoints of the state after this
+      // mini-batch: dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK = -eta G1 dW1'^T
+      prod<1, true>(t.dQ, d, n, d, m, t.dAq, m, W1, m, 1.0f, false);
+      rowdot_tril(t.dM, b, n, m, t.dAq, m, t.G1, m, -eta);
+      prod<4, true>(t.dHk, m, n, m, d, t.G2, d, dW2, d, -eta, true);
+      prod<1, false>(t.dG2, d, n, d, m, t.Hk, m, dW2, d, -eta, true);
+      prod<4, false>(t.dG1, m, n, m, d, t.K, d, dW1, m, -eta, false);
+      prod<1, true>(t.dK, d, n, d, m, t.G1, m, dW1, m, -eta, false);
+      __syncthreads();
+      // dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q
+      for (int i = tid; i < n * m; i += BW) {
+        const int r = i / m, c = i - r * m;
+        float v = 0.0f;
+        for (int k = r; k < n; ++k) v = fmaf(t.M[k * b + r], t.dAq[k * m + c], v);
+        t.dG1[i] -= eta * v;
+      }
+      for (int i = tid; i < n * d; i += BW) {
+        const int r = i / d, c = i - r * d;
+        float q = 0.0f, k1 = 0.0f;
         for (int k = 0; k < n; ++k) {
           q = fmaf(t.dM[r * b + k], t.K[k * d + c], q);
           k1 = fmaf(t.dM[k * b + r], t.Q[k * d + c], k1);
         }
-        for (int k = 0; k < m; ++k) k2 = fmaf(t.G1[r * m + k], dW1[c * m + k], k2);
         t.dQ[i] += q;
-        t.dK[i] = k1 - eta * k2;
+        t.dK[i] += k1;
       }
       __syncthreads();
       // dGh = dG1 * S1; dA (in dG1) = dG1 * Gh * GELU''(A)
@@ -288,57 +459,29 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
         t.dG1[i] = x * t.Gh[i] * ddg;
       }
       __syncthreads();
-      // dG2 += dGh W2; then dYh = c dG2 (the gradient of Y-hat = Hk W2)
-      for (int i = tid; i < n * d; i += BW) {
-        const int r = i / d, c = i - (i / d) * d;
-        float v = 0.0f;
-        for (int k = 0; k < m; ++k) v = fmaf(t.dGh[r * m + k], W2[k * d + c], v);
-        const float g2 = t.dG2[i] + v;
-        t.dG2[i] = g2;
-        t.dYh[i] = a.gscale * g2;
-      }
+      prod<1, false>(t.dG2, d, n, d, m, t.dGh, m, W2, d, 1.0f, true);  // dG2 += dGh W2
       __syncthreads();
-      // dHk += dYh W2^T; dA += dHk * S1
-      for (int i = tid; i < n * m; i += BW) {
-        const int r = i / m, c = i - (i / m) * m;
-        float v = 0.0f;
-        for (int k = 0; k < d; ++k) v = fmaf(t.dYh[r * d + k], W2[c * d + k], v);
-        const float dhk = t.dHk[i] + v;
-        t.dHk[i] = dhk;
-        t.dG1[i] += dhk * t.S1[i];
-      }
+      for (int i = tid; i < n * d; i += BW) t.dYh[i] = a.gscale * t.dG2[i];  // gradient of Y-hat = Hk W2
       __syncthreads();
-      // dK += dA W1^T; write dQ, dK, dV = -dYh to their columns of [B, T, 3D]
+      prod<4, true>(t.dHk, m, n, m, d, t.dYh, d, W2, d, 1.0f, true);  // dHk += dYh W2^T
+      __syncthreads();
+      for (int i = tid; i < n * m; i += BW) t.dG1[i] += t.dHk[i] * t.S1[i];  // dA += dHk * S1
+      __syncthreads();
+      prod<1, true>(t.dK, d, n, d, m, t.dG1, m, W1, m, 1.0f, true);  // dK += dA W1^T
+      __syncthreads();
+      // dQ, dK, dV = -dYh to their columns of [B, T, 3D]; the adjoints handed back:
+      // dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
       for (int i = tid; i < n * d; i += BW) {
-        const int r = i / d, c = i - (i / d) * d;
-        float v = 0.0f;
-        for (int k = 0; k < m; ++k) v = fmaf(t.dG1[r * m + k], W1[c * m + k], v);
-        const int64_t t_ = tok(j * b + r);
-        float* row = a.dqkv + ((int64_t)s * T + t_) * 3 * D + h * d + c;
+        const int r = i / d, c = i - r * d;
+        float* row = a.dqkv + ((int64_t)s * T + rw.tok(j * b + r)) * 3 * D + h * d + c;
         row[0] = t.dQ[i];
-        row[D] = t.dK[i] + v;
+        row[D] = t.dK[i];
         row[2 * D] = -t.dYh[i];
       }
-      // dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
-      for (int64_t i = tid; i < dm; i += BW) {
-        const int r = (int)(i / m), c = (int)(i - (i / m) * m);
-        float v = 0.0f;
-        for (int k = 0; k < n; ++k) {
-          v = fmaf(t.Q[k * d + r], t.dAq[k * m + c], v);
-          v = fmaf(t.K[k * d + r], t.dG1[k * m + c], v);
-        }
-        dW1[i] += v;
-      }
-      for (int64_t i = tid; i < dm; i += BW) {
-        const int r = (int)(i / d), c = (int)(i - (i / d) * d);
-        float v = 0.0f;
-        for (int k = 0; k < n; ++k) {
-          v = fmaf(t.Hq[k * m + r], t.dZ[k * d + c], v);
-          v = fmaf(t.dGh[k * m + r], t.G2[k * d + c], v);
-          v = fmaf(t.Hk[k * m + r], t.dYh[k * d + c], v);
-        }
-        dW2[i] += v;
-      }
+      Terms u1{2, {t.Q, t.K}, {d, d}, {t.dAq, t.dG1}, {m, m}};
+      rank_update_any(dW1, m, d, m, n, u1, 1.0f);
+      Terms u2{3, {t.Hq, t.dGh, t.Hk}, {m, m, m}, {t.dZ, t.G2, t.dYh}, {d, d, d}};
+      rank_update_any(dW2, d, m, d, n, u2, 1.0f);
       __syncthreads();
     }
   }
@@ -448,6 +591,12 @@ __global__ __launch_bounds__(256) void sum_state_kernel(const float* dw_seq, flo
 }  // namespace
 
 size_t scan_backward_lds_bytes(int d, int b) { return sizeof(float) * ((size_t)8 * b * d + (size_t)4 * b * b); }
+
+hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(scan_fwd_ckpt_kernel, dim3((unsigned)(a.B * a.H)), dim3(BW), scan_backward_lds_bytes(a.d, a.b),
+                     s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s) {
   // T = 0 runs too: no segments, and the kernel writes the zero adjoint of the initial state

@@ -154,13 +154,8 @@ __global__ __launch_bounds__(GS_THREADS) void scan_generic_kernel(ScanArgs a) {
   const float* kb = qb + plane;
   const float* vb = kb + plane;
 
-  const int64_t nseg = a.ckpt ? ((T + b - 1) / b + a.ckpt_every - 1) / a.ckpt_every : 0;
   for (int64_t n0 = 0; n0 < T; n0 += b) {
     const int n = (int)((T - n0) < b ? (T - n0) : b);
-    if (a.ckpt && (n0 / b) % a.ckpt_every == 0) {  // the state this mini-batch starts from
-      float* ck = a.ckpt + (((int64_t)s * a.H + h) * nseg + (n0 / b) / a.ckpt_every) * (2LL * d * m);
-      for (int64_t i = tid; i < 2LL * d * m; i += GS_THREADS) ck[i] = W1[i];
-    }
     for (int i = tid; i < n * d; i += GS_THREADS) {
       const int r = i / d, j = i % d;
       const int64_t t = a.reverse ? T - 1 - (n0 + r) : n0 + r;

@@ -55,8 +55,9 @@ struct ScanArgs {
   int32_t reverse;
   int32_t bf16;          // io dtype of xin / y
   int32_t linear;        // 1: linear inner model f(u; W) = u W (W = w1, d x d; w2 unused)
-  float* ckpt;           // generic MLP scan only, or null: the state (W1 then W2) at the start of
-  int32_t ckpt_every;    // every ckpt_every-th mini-batch, [B, H, nseg, 2 d m]
+  float* ckpt;           // forward pass for the backward only: the state (W1 then W2) at the
+  int32_t ckpt_every;    // start of every ckpt_every-th mini-batch, [B, H, nseg, 2 d m],
+  float* scratch;        // and its [B, H, kBwdScratchPanels, b, m] operand panels
 };
 
 // LDS bytes the generic scan needs for (d, m, b).
@@ -103,7 +104,10 @@ struct BwdArgs {
   float eta, gscale;
   int32_t gelu_tanh, reverse;
 };
-size_t scan_backward_lds_bytes(int d, int b);
+size_t scan_backward_lds_bytes(int d, int b);  // also the forward pass's (below)
+// The forward pass of one direction with the backward's own steps, writing Z, Y and
+// the checkpoints (ScanArgs: qkv, xin, y, z, alpha, w1_0, w2_0, wstate, ckpt, scratch).
+hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
 // C = (accumulate ? C : Cadd or 0) + A B, fp32 (A [M, K] row-major, or [K, M] when
 // a_transposed; B [K, N] row-major, fp32 or bf16)
