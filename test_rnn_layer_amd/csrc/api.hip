@@ -491,6 +491,7 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
 // segment at a time from its checkpoint.  The checkpoints of a direction take B*H*ceil(T/b/kCkptEvery)
 // states, the replayed segment B*H*kCkptEvery.
 constexpr int kCkptEvery = 32;
+constexpr size_t kBackwardLdsMax = 160 * 1024;
 
 struct BwdPlan {
   Plan fwd;  // the forward pass's Q/K/V and state slices (generic layout)
@@ -505,9 +506,9 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   if (c->algo != TTT_ALGO_AUTO && c->algo != TTT_ALGO_GENERIC)
     return fail(TTT_ERR_UNSUPPORTED, "the backward runs the generic fp32 scans (algo AUTO or GENERIC, got %d)",
                 c->algo);
-  if (ttt::scan_backward_lds_bytes(c->d, c->b) > kGenericLdsMax)
+  if (ttt::scan_backward_lds_bytes(c->d, c->m, c->b) > kBackwardLdsMax)
     return fail(TTT_ERR_UNSUPPORTED, "backward: mini-batch working set (d=%d b=%d) exceeds %zu bytes of LDS", c->d,
-                c->b, kGenericLdsMax);
+                c->b, kBackwardLdsMax);
   if (c->d % 4 != 0 || c->m % 4 != 0)
     return fail(TTT_ERR_UNSUPPORTED, "backward: d and m must be multiples of 4 (got d=%d m=%d)", c->d, c->m);
   const size_t D = (size_t)c->H * c->d, BTD = (size_t)c->B * c->T * D, BH = (size_t)c->B * c->H;
@@ -537,7 +538,7 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   p->ckpt_off[1] = bidir ? take(BH * nseg * st2) : 0;
   p->segst_off = take(BH * kCkptEvery * st2);
   p->dstate_off = take(BH * st2);
-  p->scratch_off = take(BH * ttt::kBwdScratchPanels * (size_t)c->b * c->m * sizeof(float));
+  p->scratch_off = take(BH * ttt::scan_backward_scratch_elems(c->d, c->m, c->b) * sizeof(float));
   p->dwseq_off = take(BH * st2);
   p->dal_off = take(ttt::dalpha_partial_elems((int)D) * sizeof(float));
   p->total = off;

@@ -198,12 +198,25 @@ __device__ void rowdot_tril(float* out, int ldo, int n, int K, const float* X, i
 // Operand panels of one mini-batch.
 struct MB {
   // LDS, b x d (row stride d)
-  float *K, *Q, *G2, *dZ, *dG2, *dQ, *dK, *dYh;
+  float *K, *Q, *G2, *dZ, *dG2, *dYh;
   // LDS, b x b (row stride b)
   float *M, *N, *dM, *dN;
-  // workspace slice, b x m (row stride m)
-  float *A, *Hk, *S1, *Gh, *G1, *Aq, *Hq, *dAq, *dHk, *dG1, *dGh;
+  // workspace slice: b x m (row stride m), then dQ, dK (b x d)
+  float *A, *Hk, *S1, *Gh, *G1, *Aq, *Hq, *dAq, *dHk, *dG1, *dGh, *dQ, *dK;
 };
+
+// LDS floats of the b x d and b x b panels
+__host__ __device__ constexpr int64_t panel_lds_floats(int d, int b) { return 6LL * b * d + 4LL * b * b; }
+constexpr int64_t kLdsBytes = 160 * 1024;
+// The state (W1, W2: 2 d m floats) is kept in LDS when it fits beside the panels.
+__host__ __device__ constexpr bool state_in_lds(int d, int m, int b) {
+  return (2LL * d * m + panel_lds_floats(d, b)) * 4 <= kLdsBytes;
+}
+
+// workspace floats of one workgroup: the b x m panels, then dQ and dK
+__host__ __device__ constexpr int64_t scratch_floats(int d, int m, int b) {
+  return (int64_t)kBwdScratchPanels * b * m + 2LL * b * d;
+}
 
 __device__ void bind_panels(MB& t, float* lds, float* sc, int b, int d, int m) {
   t.K = lds;
@@ -211,15 +224,20 @@ __device__ void bind_panels(MB& t, float* lds, float* sc, int b, int d, int m) {
   t.G2 = t.Q + b * d;
   t.dZ = t.G2 + b * d;
   t.dG2 = t.dZ + b * d;
-  t.dQ = t.dG2 + b * d;
-  t.dK = t.dQ + b * d;
-  t.dYh = t.dK + b * d;
+  t.dYh = t.dG2 + b * d;
   t.M = t.dYh + b * d;
   t.N = t.M + b * b;
   t.dM = t.N + b * b;
   t.dN = t.dM + b * b;
   float** panels[] = {&t.A, &t.Hk, &t.S1, &t.Gh, &t.G1, &t.Aq, &t.Hq, &t.dAq, &t.dHk, &t.dG1, &t.dGh};
   for (int i = 0; i < kBwdScratchPanels; ++i) *panels[i] = sc + (int64_t)i * b * m;
+  t.dQ = sc + (int64_t)kBwdScratchPanels * b * m;
+  t.dK = t.dQ + b * d;
+}
+
+// copy n floats (n a multiple of 4, both 16-byte aligned) with the whole workgroup
+__device__ inline void copy4(float* dst, const float* src, int64_t n) {
+  for (int64_t i = 4 * (int64_t)threadIdx.x; i < n; i += 4 * BW) *(float4*)(dst + i) = *(const float4*)(src + i);
 }
 
 // The forward quantities of one mini-batch that the state update needs:
@@ -305,23 +323,19 @@ __global__ __launch_bounds__(BW) void scan_fwd_ckpt_kernel(ScanArgs a) {
   const int64_t sh = (int64_t)s * a.H + h;
   const int64_t nmb = (T + b - 1) / b;
   const int64_t nseg = (nmb + a.ckpt_every - 1) / a.ckpt_every;
+  const bool wl = state_in_lds(d, m, b);
   MB t;
-  bind_panels(t, lds, a.scratch + sh * (int64_t)kBwdScratchPanels * b * m, b, d, m);
-  float* W1 = a.wstate + sh * 2 * dm;
+  bind_panels(t, lds + (wl ? 2 * dm : 0), a.scratch + sh * scratch_floats(d, m, b), b, d, m);
+  float* W1 = wl ? lds : a.wstate + sh * 2 * dm;
   float* W2 = W1 + dm;
-  for (int64_t i = threadIdx.x; i < dm; i += BW) {
-    W1[i] = a.w1_0[(int64_t)h * dm + i];
-    W2[i] = a.w2_0[(int64_t)h * dm + i];
-  }
+  copy4(W1, a.w1_0 + (int64_t)h * dm, dm);
+  copy4(W2, a.w2_0 + (int64_t)h * dm, dm);
   const int64_t plane = a.B * a.H * T * d;
   Rows rw{a.qkv + sh * T * d, a.qkv + plane + sh * T * d, a.qkv + 2 * plane + sh * T * d, T, a.reverse};
   __syncthreads();
   for (int64_t j = 0; j < nmb; ++j) {
     const int n = (int)min((int64_t)b, T - j * b);
-    if (j % a.ckpt_every == 0) {
-      float* ck = a.ckpt + (sh * nseg + j / a.ckpt_every) * 2 * dm;
-      for (int64_t i = threadIdx.x; i < 2 * dm; i += BW) ck[i] = W1[i];
-    }
+    if (j % a.ckpt_every == 0) copy4(a.ckpt + (sh * nseg + j / a.ckpt_every) * 2 * dm, W1, 2 * dm);
     load_qkv(t, rw, j * b, n, d);
     __syncthreads();
     forward_core(t, W1, W2, n, d, m, a.gscale, a.gelu_tanh);
@@ -357,9 +371,10 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   const int64_t nseg = (nmb + C - 1) / C;
   const int64_t sh = (int64_t)s * a.H + h;
 
+  const bool wl = state_in_lds(d, m, b);
   MB t;
-  bind_panels(t, lds, a.scratch + sh * (int64_t)kBwdScratchPanels * b * m, b, d, m);
-  float* Wc1 = a.wcur + sh * 2 * dm;  // replayed state
+  bind_panels(t, lds + (wl ? 2 * dm : 0), a.scratch + sh * scratch_floats(d, m, b), b, d, m);
+  float* Wc1 = wl ? lds : a.wcur + sh * 2 * dm;  // replayed state, then each mini-batch's start state
   float* Wc2 = Wc1 + dm;
   float* dW1 = a.dstate + sh * 2 * dm;  // adjoint of the state after the current mini-batch
   float* dW2 = dW1 + dm;
@@ -372,12 +387,10 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   for (int64_t sg = nseg - 1; sg >= 0; --sg) {
     const int64_t j0 = sg * C, j1 = min(nmb, j0 + C);
     // replay the segment's forward steps from its checkpoint, keeping each mini-batch's start state
-    const float* ck = a.ckpt + (sh * nseg + sg) * 2 * dm;
-    for (int64_t i = tid; i < 2 * dm; i += BW) Wc1[i] = ck[i];
+    copy4(Wc1, a.ckpt + (sh * nseg + sg) * 2 * dm, 2 * dm);
     __syncthreads();
     for (int64_t j = j0; j < j1; ++j) {
-      float* dst = seg + (j - j0) * 2 * dm;
-      for (int64_t i = tid; i < 2 * dm; i += BW) dst[i] = Wc1[i];
+      copy4(seg + (j - j0) * 2 * dm, Wc1, 2 * dm);
       if (j + 1 == j1) break;
       const int n = (int)min((int64_t)b, T - j * b);
       load_qkv(t, rw, j * b, n, d);
@@ -391,6 +404,10 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
     for (int64_t j = j1 - 1; j >= j0; --j) {
       const int n = (int)min((int64_t)b, T - j * b);
       const float* W1 = seg + (j - j0) * 2 * dm;
+      if (wl) {
+        copy4(Wc1, W1, 2 * dm);
+        W1 = Wc1;
+      }
       const float* W2 = W1 + dm;
       load_qkv(t, rw, j * b, n, d);
       for (int i = tid; i < n * d; i += BW) {
@@ -590,17 +607,29 @@ __global__ __launch_bounds__(256) void sum_state_kernel(const float* dw_seq, flo
 
 }  // namespace
 
-size_t scan_backward_lds_bytes(int d, int b) { return sizeof(float) * ((size_t)8 * b * d + (size_t)4 * b * b); }
+size_t scan_backward_lds_bytes(int d, int m, int b) {
+  return sizeof(float) * (size_t)(panel_lds_floats(d, b) + (state_in_lds(d, m, b) ? 2LL * d * m : 0));
+}
+
+size_t scan_backward_scratch_elems(int d, int m, int b) { return (size_t)scratch_floats(d, m, b); }
 
 hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(scan_fwd_ckpt_kernel, dim3((unsigned)(a.B * a.H)), dim3(BW), scan_backward_lds_bytes(a.d, a.b),
+  const size_t lds = scan_backward_lds_bytes(a.d, a.m, a.b);
+  hipError_t e = hipFuncSetAttribute((const void*)scan_fwd_ckpt_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_fwd_ckpt_kernel, dim3((unsigned)(a.B * a.H)), dim3(BW), lds,
                      s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s) {
   // T = 0 runs too: no segments, and the kernel writes the zero adjoint of the initial state
-  hipLaunchKernelGGL(scan_backward_kernel, dim3((unsigned)(a.B * a.H)), dim3(BW), scan_backward_lds_bytes(a.d, a.b),
+  const size_t lds = scan_backward_lds_bytes(a.d, a.m, a.b);
+  hipError_t e = hipFuncSetAttribute((const void*)scan_backward_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_backward_kernel, dim3((unsigned)(a.B * a.H)), dim3(BW), lds,
                      s, a);
   return hipGetLastError();
 }

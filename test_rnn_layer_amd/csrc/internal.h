@@ -57,7 +57,7 @@ struct ScanArgs {
   int32_t linear;        // 1: linear inner model f(u; W) = u W (W = w1, d x d; w2 unused)
   float* ckpt;           // forward pass for the backward only: the state (W1 then W2) at the
   int32_t ckpt_every;    // start of every ckpt_every-th mini-batch, [B, H, nseg, 2 d m],
-  float* scratch;        // and its [B, H, kBwdScratchPanels, b, m] operand panels
+  float* scratch;        // and its operand panels, scan_backward_scratch_elems per (sequence, head)
 };
 
 // LDS bytes the generic scan needs for (d, m, b).
@@ -87,7 +87,7 @@ hipError_t launch_scan_coop(const ScanArgs& a, hipStream_t s);
 // Backward of one direction of the MLP layer (generic, fp32): the backward scan
 // (one workgroup per (sequence, head)) walks segments of ckpt_every
 // mini-batches from the last, replaying each from its checkpoint.
-constexpr int kBwdScratchPanels = 11;  // b x m fp32 panels per workgroup
+constexpr int kBwdScratchPanels = 11;  // b x m fp32 panels per workgroup (plus dQ, dK)
 struct BwdArgs {
   const float* qkv;    // [3, B, H, T, d] fp32: the direction's projections of its input
   const float* dy;     // [B, T, D] fp32: gradient of the direction's output Y
@@ -96,7 +96,7 @@ struct BwdArgs {
   float* segst;        // [B, H, ckpt_every, 2 d m] workspace: states of one segment's mini-batches
   float* wcur;         // [B, H, 2 d m] workspace: replayed state
   float* dstate;       // [B, H, 2 d m] workspace: adjoint of the state
-  float* scratch;      // [B, H, kBwdScratchPanels, b, m] workspace
+  float* scratch;      // workspace, scan_backward_scratch_elems per (sequence, head)
   float* dqkv;         // [B, T, 3 D] out: dQ | dK | dV per token
   float* dw_seq;       // [B, H, 2 d m] out: adjoint of the initial state, per sequence
   int64_t B, T;
@@ -104,7 +104,11 @@ struct BwdArgs {
   float eta, gscale;
   int32_t gelu_tanh, reverse;
 };
-size_t scan_backward_lds_bytes(int d, int b);  // also the forward pass's (below)
+// LDS bytes of the backward's scan kernels (the forward pass below too): the b x d and
+// b x b panels, and the state when it fits beside them (at most 160 KB); workspace
+// floats per workgroup (the b x m panels, dQ, dK)
+size_t scan_backward_lds_bytes(int d, int m, int b);
+size_t scan_backward_scratch_elems(int d, int m, int b);
 // The forward pass of one direction with the backward's own steps, writing Z, Y and
 // the checkpoints (ScanArgs: qkv, xin, y, z, alpha, w1_0, w2_0, wstate, ckpt, scratch).
 hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s);

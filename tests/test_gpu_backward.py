@@ -32,6 +32,8 @@ CASES = {
                                  name="f32_sum_tanh"),
     # the bidir307k head shape (bf16 X and theta), two heads, ragged tail
     "bf16_d64": W.WORKLOADS["bidir307k"].replace(T=72, H=2, seg_len=0, name="bf16_d64"),
+    # the bigstate307k head shape: a state too large for LDS stays in the workspace
+    "bf16_d128_b1": W.WORKLOADS["bigstate307k"].replace(T=24, H=1, seg_len=0, name="bf16_d128_b1"),
 }
 
 
