@@ -198,24 +198,43 @@ __device__ void rowdot_tril(float* out, int ldo, int n, int K, const float* X, i
 // Operand panels of one mini-batch.
 struct MB {
   // LDS, b x d (row stride d)
-  float *K, *Q, *G2, *dZ, *dG2, *dYh;
+  float *K, *Q, *G2, *dZ, *dG2;
   // LDS, b x b (row stride b)
   float *M, *N, *dM, *dN;
-  // workspace slice: b x m (row stride m), then dQ, dK (b x d)
-  float *A, *Hk, *S1, *Gh, *G1, *Aq, *Hq, *dAq, *dHk, *dG1, *dGh, *dQ, *dK;
+  // workspace slice: b x m (row stride m), then dQ, dK, dYh (b x d)
+  float *A, *Hk, *S1, *Gh, *G1, *Aq, *Hq, *dAq, *dHk, *dG1, *dGh, *dQ, *dK, *dYh;
 };
 
 // LDS floats of the b x d and b x b panels
-__host__ __device__ constexpr int64_t panel_lds_floats(int d, int b) { return 6LL * b * d + 4LL * b * b; }
+__host__ __device__ constexpr int64_t panel_lds_floats(int d, int b) { return 5LL * b * d + 4LL * b * b; }
 constexpr int64_t kLdsBytes = 160 * 1024;
-// The state (W1, W2: 2 d m floats) is kept in LDS when it fits beside the panels.
+// The state is kept in LDS when it fits beside the panels, its rows padded by 4 floats
+// (W1 rows of m + 4, W2 rows of d + 4), so that a transposed read, one row per lane,
+// falls on distinct banks.
+__host__ __device__ constexpr int64_t state_lds_floats(int d, int m) { return 2LL * d * m + 4LL * (d + m); }
 __host__ __device__ constexpr bool state_in_lds(int d, int m, int b) {
-  return (2LL * d * m + panel_lds_floats(d, b)) * 4 <= kLdsBytes;
+  return (state_lds_floats(d, m) + panel_lds_floats(d, b)) * 4 <= kLdsBytes;
+}
+
+// Where a (W1, W2) state lives and its row strides.
+struct St {
+  float* w1;
+  float* w2;
+  int ld1, ld2;
+};
+
+__device__ inline St state_at(float* base, bool padded, int d, int m) {
+  St st;
+  st.ld1 = padded ? m + 4 : m;
+  st.ld2 = padded ? d + 4 : d;
+  st.w1 = base;
+  st.w2 = base + (int64_t)d * st.ld1;
+  return st;
 }
 
 // workspace floats of one workgroup: the b x m panels, then dQ and dK
 __host__ __device__ constexpr int64_t scratch_floats(int d, int m, int b) {
-  return (int64_t)kBwdScratchPanels * b * m + 2LL * b * d;
+  return (int64_t)kBwdScratchPanels * b * m + 3LL * b * d;
 }
 
 __device__ void bind_panels(MB& t, float* lds, float* sc, int b, int d, int m) {
@@ -224,8 +243,7 @@ __device__ void bind_panels(MB& t, float* lds, float* sc, int b, int d, int m) {
   t.G2 = t.Q + b * d;
   t.dZ = t.G2 + b * d;
   t.dG2 = t.dZ + b * d;
-  t.dYh = t.dG2 + b * d;
-  t.M = t.dYh + b * d;
+  t.M = t.dG2 + b * d;
   t.N = t.M + b * b;
   t.dM = t.N + b * b;
   t.dN = t.dM + b * b;
@@ -233,18 +251,32 @@ __device__ void bind_panels(MB& t, float* lds, float* sc, int b, int d, int m) {
   for (int i = 0; i < kBwdScratchPanels; ++i) *panels[i] = sc + (int64_t)i * b * m;
   t.dQ = sc + (int64_t)kBwdScratchPanels * b * m;
   t.dK = t.dQ + b * d;
+  t.dYh = t.dK + b * d;
 }
 
-// copy n floats (n a multiple of 4, both 16-byte aligned) with the whole workgroup
-__device__ inline void copy4(float* dst, const float* src, int64_t n) {
-  for (int64_t i = 4 * (int64_t)threadIdx.x; i < n; i += 4 * BW) *(float4*)(dst + i) = *(const float4*)(src + i);
+// copy rows x cols floats (cols a multiple of 4, rows 16-byte aligned) between row strides
+__device__ inline void copy_rows(float* dst, int ldd, const float* src, int lds_, int rows, int cols) {
+  const int q = cols / 4;
+  for (int i = threadIdx.x; i < rows * q; i += BW) {
+    const int r = i / q, c = 4 * (i - r * q);
+    *(float4*)(dst + (int64_t)r * ldd + c) = *(const float4*)(src + (int64_t)r * lds_ + c);
+  }
+}
+
+// a dense state (W1 [d, m] then W2 [m, d]) to or from a St
+__device__ inline void state_in(const St& st, const float* src, int d, int m) {
+  copy_rows(st.w1, st.ld1, src, m, d, m);
+  copy_rows(st.w2, st.ld2, src + (int64_t)d * m, d, m, d);
+}
+__device__ inline void state_out(float* dst, const St& st, int d, int m) {
+  copy_rows(dst, m, st.w1, st.ld1, d, m);
+  copy_rows(dst + (int64_t)d * m, d, st.w2, st.ld2, m, d);
 }
 
 // The forward quantities of one mini-batch that the state update needs:
 // A, Hk, S1, G2 (in place of V), Gh, G1.
-__device__ void forward_core(const MB& t, const float* W1, const float* W2, int n, int d, int m, float gscale,
-                             int gelu_tanh) {
-  prod<4, false>(t.A, m, n, m, d, t.K, d, W1, m, 1.0f, false);  // A = K W1
+__device__ void forward_core(const MB& t, const St& W, int n, int d, int m, float gscale, int gelu_tanh) {
+  prod<4, false>(t.A, m, n, m, d, t.K, d, W.w1, W.ld1, 1.0f, false);  // A = K W1
   __syncthreads();
   for (int i = threadIdx.x; i < n * m; i += BW) {
     float g, dg, ddg;
@@ -254,27 +286,27 @@ __device__ void forward_core(const MB& t, const float* W1, const float* W2, int 
   }
   for (int i = threadIdx.x; i < n * d; i += BW) t.G2[i] *= -gscale;  // -c V
   __syncthreads();
-  prod<1, false>(t.G2, d, n, d, m, t.Hk, m, W2, d, gscale, true);  // G2 = c (Hk W2 - V)
+  prod<1, false>(t.G2, d, n, d, m, t.Hk, m, W.w2, W.ld2, gscale, true);  // G2 = c (Hk W2 - V)
   __syncthreads();
-  prod<4, true>(t.Gh, m, n, m, d, t.G2, d, W2, d, 1.0f, false);  // Gh = G2 W2^T
+  prod<4, true>(t.Gh, m, n, m, d, t.G2, d, W.w2, W.ld2, 1.0f, false);  // Gh = G2 W2^T
   __syncthreads();
   for (int i = threadIdx.x; i < n * m; i += BW) t.G1[i] = t.Gh[i] * t.S1[i];
   __syncthreads();
 }
 
 // W1 -= eta K^T G1; W2 -= eta Hk^T G2
-__device__ void state_step(const MB& t, float* W1, float* W2, int n, int d, int m, float eta) {
+__device__ void state_step(const MB& t, const St& W, int n, int d, int m, float eta) {
   Terms t1{1, {t.K}, {d}, {t.G1}, {m}};
-  rank_update_any(W1, m, d, m, n, t1, -eta);
+  rank_update_any(W.w1, W.ld1, d, m, n, t1, -eta);
   Terms t2{1, {t.Hk}, {m}, {t.G2}, {d}};
-  rank_update_any(W2, d, m, d, n, t2, -eta);
+  rank_update_any(W.w2, W.ld2, m, d, n, t2, -eta);
 }
 
 // Aq = Q W1 - eta tril(Q K^T) G1 and Hq = GELU(Aq) (GELU'(Aq) into dq when non-null).
-__device__ void readout_hidden(const MB& t, const float* W1, int n, int b, int d, int m, float eta, int gelu_tanh,
+__device__ void readout_hidden(const MB& t, const St& W, int n, int b, int d, int m, float eta, int gelu_tanh,
                                float* dq) {
   rowdot_tril(t.M, b, n, d, t.Q, d, t.K, d, 1.0f);  // M = tril(Q K^T)
-  prod<4, false>(t.Aq, m, n, m, d, t.Q, d, W1, m, 1.0f, false);
+  prod<4, false>(t.Aq, m, n, m, d, t.Q, d, W.w1, W.ld1, 1.0f, false);
   __syncthreads();
   for (int i = threadIdx.x; i < n * m; i += BW) {
     const int r = i / m, c = i - r * m;
@@ -325,23 +357,22 @@ __global__ __launch_bounds__(BW) void scan_fwd_ckpt_kernel(ScanArgs a) {
   const int64_t nseg = (nmb + a.ckpt_every - 1) / a.ckpt_every;
   const bool wl = state_in_lds(d, m, b);
   MB t;
-  bind_panels(t, lds + (wl ? 2 * dm : 0), a.scratch + sh * scratch_floats(d, m, b), b, d, m);
-  float* W1 = wl ? lds : a.wstate + sh * 2 * dm;
-  float* W2 = W1 + dm;
-  copy4(W1, a.w1_0 + (int64_t)h * dm, dm);
-  copy4(W2, a.w2_0 + (int64_t)h * dm, dm);
+  bind_panels(t, lds + (wl ? state_lds_floats(d, m) : 0), a.scratch + sh * scratch_floats(d, m, b), b, d, m);
+  const St W = state_at(wl ? lds : a.wstate + sh * 2 * dm, wl, d, m);
+  copy_rows(W.w1, W.ld1, a.w1_0 + (int64_t)h * dm, m, d, m);
+  copy_rows(W.w2, W.ld2, a.w2_0 + (int64_t)h * dm, d, m, d);
   const int64_t plane = a.B * a.H * T * d;
   Rows rw{a.qkv + sh * T * d, a.qkv + plane + sh * T * d, a.qkv + 2 * plane + sh * T * d, T, a.reverse};
   __syncthreads();
   for (int64_t j = 0; j < nmb; ++j) {
     const int n = (int)min((int64_t)b, T - j * b);
-    if (j % a.ckpt_every == 0) copy4(a.ckpt + (sh * nseg + j / a.ckpt_every) * 2 * dm, W1, 2 * dm);
+    if (j % a.ckpt_every == 0) state_out(a.ckpt + (sh * nseg + j / a.ckpt_every) * 2 * dm, W, d, m);
     load_qkv(t, rw, j * b, n, d);
     __syncthreads();
-    forward_core(t, W1, W2, n, d, m, a.gscale, a.gelu_tanh);
-    readout_hidden(t, W1, n, b, d, m, a.eta, a.gelu_tanh, nullptr);
+    forward_core(t, W, n, d, m, a.gscale, a.gelu_tanh);
+    readout_hidden(t, W, n, b, d, m, a.eta, a.gelu_tanh, nullptr);
     rowdot_tril(t.N, b, n, m, t.Hq, m, t.Hk, m, 1.0f);  // N = tril(Hq Hk^T)
-    prod<1, false>(t.dZ, d, n, d, m, t.Hq, m, W2, d, 1.0f, false);  // Hq W2
+    prod<1, false>(t.dZ, d, n, d, m, t.Hq, m, W.w2, W.ld2, 1.0f, false);  // Hq W2
     __syncthreads();
     // Z = Hq W2 - eta N G2, the gate, and the state step
     for (int i = threadIdx.x; i < n * d; i += BW) {
@@ -353,7 +384,7 @@ __global__ __launch_bounds__(BW) void scan_fwd_ckpt_kernel(ScanArgs a) {
       a.z[o] = z;
       store_io(a.y, o, load_io(a.xin, o, a.bf16) + tanhf(a.alpha[h * d + c]) * z, a.bf16);
     }
-    state_step(t, W1, W2, n, d, m, a.eta);
+    state_step(t, W, n, d, m, a.eta);
     __syncthreads();
   }
 }
@@ -373,9 +404,9 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
 
   const bool wl = state_in_lds(d, m, b);
   MB t;
-  bind_panels(t, lds + (wl ? 2 * dm : 0), a.scratch + sh * scratch_floats(d, m, b), b, d, m);
-  float* Wc1 = wl ? lds : a.wcur + sh * 2 * dm;  // replayed state, then each mini-batch's start state
-  float* Wc2 = Wc1 + dm;
+  bind_panels(t, lds + (wl ? state_lds_floats(d, m) : 0), a.scratch + sh * scratch_floats(d, m, b), b, d, m);
+  // replayed state, then (state in LDS) each mini-batch's start state
+  const St Wc = state_at(wl ? lds : a.wcur + sh * 2 * dm, wl, d, m);
   float* dW1 = a.dstate + sh * 2 * dm;  // adjoint of the state after the current mini-batch
   float* dW2 = dW1 + dm;
   float* seg = a.segst + sh * (int64_t)C * 2 * dm;
@@ -387,28 +418,27 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   for (int64_t sg = nseg - 1; sg >= 0; --sg) {
     const int64_t j0 = sg * C, j1 = min(nmb, j0 + C);
     // replay the segment's forward steps from its checkpoint, keeping each mini-batch's start state
-    copy4(Wc1, a.ckpt + (sh * nseg + sg) * 2 * dm, 2 * dm);
+    state_in(Wc, a.ckpt + (sh * nseg + sg) * 2 * dm, d, m);
     __syncthreads();
     for (int64_t j = j0; j < j1; ++j) {
-      copy4(seg + (j - j0) * 2 * dm, Wc1, 2 * dm);
+      state_out(seg + (j - j0) * 2 * dm, Wc, d, m);
       if (j + 1 == j1) break;
       const int n = (int)min((int64_t)b, T - j * b);
       load_qkv(t, rw, j * b, n, d);
       __syncthreads();
-      forward_core(t, Wc1, Wc2, n, d, m, a.gscale, a.gelu_tanh);
-      state_step(t, Wc1, Wc2, n, d, m, eta);
+      forward_core(t, Wc, n, d, m, a.gscale, a.gelu_tanh);
+      state_step(t, Wc, n, d, m, eta);
       __syncthreads();
     }
     __syncthreads();
     // the segment's mini-batches, last to first
     for (int64_t j = j1 - 1; j >= j0; --j) {
       const int n = (int)min((int64_t)b, T - j * b);
-      const float* W1 = seg + (j - j0) * 2 * dm;
+      St W = state_at(seg + (j - j0) * 2 * dm, false, d, m);
       if (wl) {
-        copy4(Wc1, W1, 2 * dm);
-        W1 = Wc1;
+        state_in(Wc, W.w1, d, m);
+        W = Wc;
       }
-      const float* W2 = W1 + dm;
       load_qkv(t, rw, j * b, n, d);
       for (int i = tid; i < n * d; i += BW) {
         const int r = i / d, c = i - r * d;
@@ -416,12 +446,12 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
         t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + ch];
       }
       __syncthreads();
-      forward_core(t, W1, W2, n, d, m, a.gscale, a.gelu_tanh);
-      readout_hidden(t, W1, n, b, d, m, eta, a.gelu_tanh, t.dAq);  // dAq holds GELU'(Aq) for now
+      forward_core(t, W, n, d, m, a.gscale, a.gelu_tanh);
+      readout_hidden(t, W, n, b, d, m, eta, a.gelu_tanh, t.dAq);  // dAq holds GELU'(Aq) for now
       // N = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
       rowdot_tril(t.N, b, n, m, t.Hq, m, t.Hk, m, 1.0f);
       rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta);
-      prod<4, true>(t.dGh, m, n, m, d, t.dZ, d, W2, d, 1.0f, false);
+      prod<4, true>(t.dGh, m, n, m, d, t.dZ, d, W.w2, W.ld2, 1.0f, false);
       __syncthreads();
       // dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dG2 = -eta N^T dZ; dHk = dN^T Hq
       for (int i = tid; i < n * m; i += BW) {
@@ -442,7 +472,7 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       __syncthreads();
       // dQ = dAq W1^T; dM = tril(-eta dAq G1^T); with the adjoints of the state after this
       // mini-batch: dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK = -eta G1 dW1'^T
-      prod<1, true>(t.dQ, d, n, d, m, t.dAq, m, W1, m, 1.0f, false);
+      prod<1, true>(t.dQ, d, n, d, m, t.dAq, m, W.w1, W.ld1, 1.0f, false);
       rowdot_tril(t.dM, b, n, m, t.dAq, m, t.G1, m, -eta);
       prod<4, true>(t.dHk, m, n, m, d, t.G2, d, dW2, d, -eta, true);
       prod<1, false>(t.dG2, d, n, d, m, t.Hk, m, dW2, d, -eta, true);
@@ -476,15 +506,15 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
         t.dG1[i] = x * t.Gh[i] * ddg;
       }
       __syncthreads();
-      prod<1, false>(t.dG2, d, n, d, m, t.dGh, m, W2, d, 1.0f, true);  // dG2 += dGh W2
+      prod<1, false>(t.dG2, d, n, d, m, t.dGh, m, W.w2, W.ld2, 1.0f, true);  // dG2 += dGh W2
       __syncthreads();
       for (int i = tid; i < n * d; i += BW) t.dYh[i] = a.gscale * t.dG2[i];  // gradient of Y-hat = Hk W2
       __syncthreads();
-      prod<4, true>(t.dHk, m, n, m, d, t.dYh, d, W2, d, 1.0f, true);  // dHk += dYh W2^T
+      prod<4, true>(t.dHk, m, n, m, d, t.dYh, d, W.w2, W.ld2, 1.0f, true);  // dHk += dYh W2^T
       __syncthreads();
       for (int i = tid; i < n * m; i += BW) t.dG1[i] += t.dHk[i] * t.S1[i];  // dA += dHk * S1
       __syncthreads();
-      prod<1, true>(t.dK, d, n, d, m, t.dG1, m, W1, m, 1.0f, true);  // dK += dA W1^T
+      prod<1, true>(t.dK, d, n, d, m, t.dG1, m, W.w1, W.ld1, 1.0f, true);  // dK += dA W1^T
       __syncthreads();
       // dQ, dK, dV = -dYh to their columns of [B, T, 3D]; the adjoints handed back:
       // dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
@@ -608,7 +638,7 @@ __global__ __launch_bounds__(256) void sum_state_kernel(const float* dw_seq, flo
 }  // namespace
 
 size_t scan_backward_lds_bytes(int d, int m, int b) {
-  return sizeof(float) * (size_t)(panel_lds_floats(d, b) + (state_in_lds(d, m, b) ? 2LL * d * m : 0));
+  return sizeof(float) * (size_t)(panel_lds_floats(d, b) + (state_in_lds(d, m, b) ? state_lds_floats(d, m) : 0));
 }
 
 size_t scan_backward_scratch_elems(int d, int m, int b) { return (size_t)scratch_floats(d, m, b); }
