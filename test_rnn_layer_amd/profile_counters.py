@@ -35,7 +35,9 @@ beside the trace):
         python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > DIR/bench.json
     python3 -m test_rnn_layer_amd.profile_counters summarize-stats DIR
 
-`summarize-stats` writes profiles/<scan kernel>_proj_tiles_<workload>_stats.md.
+`summarize-stats` writes profiles/<scan kernel>_proj_tiles_<workload>_stats.md;
+`summarize-backward DIR` (a traced `bench.py --backward` run) writes
+profiles/scan_backward_<workload>_stats.md.
 """
 from __future__ import annotations
 
@@ -64,6 +66,7 @@ KERNEL_SOURCES = {"scan_mfma": ["scan_mfma.hip", "token_block.h", "mfma_common.h
                   "scan_coop": ["scan_coop.hip", "internal.h"],
                   "scan_linear_mfma": ["scan_linear.hip", "token_block.h", "mfma_common.h", "internal.h"],
                   "scan_linear_generic": ["generic.hip", "internal.h"],
+                  "scan_backward": ["backward.hip", "internal.h"],
                   "projection": ["proj_mfma.hip", "mfma_common.h", "internal.h"]}
 
 
@@ -328,6 +331,45 @@ def summarize_stats(d: str, out_md: str | None = None):
     print("\n".join(lines))
 
 
+def summarize_backward(d: str, out_md: str | None = None):
+    """Kernel-time table of a traced `bench.py --backward` run (DIR/bench.json)."""
+    from test_rnn_layer_amd import workloads as W
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    bench = json.loads(open(os.path.join(d, "bench.json")).read().strip().splitlines()[-1])
+    wname = bench["config"]["workload"]
+    wl = W.WORKLOADS[wname]
+    steps, warm = bench["steps"], bench["warmup"]
+    calls = steps + warm
+    wl_arg = "" if wname == "bidir307k" else f" --workload {wname}"
+    lines = [
+        f"# Kernel time, backward of the bidirectional layer, {wname} (one ttt_mlp_bidir_backward call)", "",
+        f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ, fp32 arithmetic and "
+        f"gradients; {steps} timed + {warm} warm-up calls under the trace.  One call: both forward passes again "
+        "(projection, then the scan that keeps a checkpoint every 32 mini-batches), then per direction the "
+        "backward scan, the dalpha reduction and the two gradient GEMMs (dX, dθ).", "",
+        "Commands (repo root, MI355X):", "",
+        f"    mkdir -p {d} && rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
+        f"python3 bench.py --backward{wl_arg} --steps {steps} --warmup {warm} --no-cpu-baseline > {d}/bench.json",
+        f"    python3 -m test_rnn_layer_amd.profile_counters summarize-backward {d}", "",
+        "| Kernel | Launches | Average per launch | Per call | Share of kernel time |", "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        name = r["Name"].replace("ttt::(anonymous namespace)::", "")
+        lines.append(f"| `{name}` | {int(r['Calls'])} | {float(r['AverageNs']) / 1e6:.3f} ms | "
+                     f"{float(r['TotalDurationNs']) / 1e6 / calls:.1f} ms | {float(r['Percentage']):.1f}% |")
+    rf = bench["roofline"]
+    lines += ["", f"The bench line of the same run: {bench['ms_per_step']:.0f} ms per call "
+              f"({bench['value']:,.0f} tokens/s); the backward scan's launches averaged {rf['avg_launch_ms']:.0f} ms "
+              f"from HIP events, {rf['flops_per_launch'] / 1e12:.2f} TFLOP each (algorithmic, replay excluded), "
+              f"{rf['achieved']:.2f} TFLOP/s = {100 * rf['frac']:.1f}% of the fp32 peak."]
+    out_md = out_md or os.path.join(ROOT, "profiles", f"scan_backward_{wname}_stats.md")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     sys.path.insert(0, ROOT)
     if len(sys.argv) >= 2 and sys.argv[1] == "run":
@@ -336,6 +378,8 @@ if __name__ == "__main__":
         summarize(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 3 and sys.argv[1] == "summarize-stats":
         summarize_stats(sys.argv[2])
+    elif len(sys.argv) == 3 and sys.argv[1] == "summarize-backward":
+        summarize_backward(sys.argv[2])
     elif len(sys.argv) >= 3 and sys.argv[1] == "summarize-sq":
         summarize_sq(sys.argv[2:])
     else:
