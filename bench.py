@@ -22,6 +22,8 @@ sys.path.insert(0, ROOT)
 METRIC = "TTT-MLP bidirectional layer tokens/sec at 307,200 tokens; % of roofline"
 METRIC_LINEAR = "TTT-Linear bidirectional layer tokens/sec at 307,200 tokens; % of roofline"
 METRIC_BACKWARD = "TTT-MLP bidirectional layer backward tokens/sec at 307,200 tokens; % of roofline"
+METRIC_HYBRID = ("Hybrid block (segment-local attention, then the TTT-MLP bidirectional layer) tokens/sec at "
+                 "307,200 tokens; % of roofline")
 # MI355X published peaks
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
@@ -202,6 +204,107 @@ def bench_backward(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def attention_flops(T: int, L: int, H: int, d: int) -> int:
+    """Q K^T and P V over every segment of one sequence (all pairs within a segment)."""
+    full, rest = divmod(T, L)
+    return 4 * d * H * (full * L * L + rest * rest)
+
+
+def cpu_baseline_hybrid(wl, tokens: int):
+    """The fp64 oracle's hybrid block on the first `tokens` tokens (one segment:
+    attention over those tokens, then the bidirectional TTT layer), every head."""
+    import numpy as np
+
+    from oracle import attention_oracle as AO
+    from oracle import ttt_oracle as O
+    from test_rnn_layer_amd import workloads as W
+
+    sub = wl.replace(T=tokens)
+    inp = W.make_inputs(sub)
+    thA, thO = W.make_attention_weights(sub)
+    X = W.to_f64(inp["X"], sub.io_dtype)
+    nw = O.default_workers()
+    t0 = time.perf_counter()
+    AO.hybrid_block(X, W.to_f64(thA, sub.io_dtype), W.to_f64(thO, sub.io_dtype), wl.attn_seg,
+                    W.to_f64(inp["theta"], sub.io_dtype), inp["W1_0"].astype(np.float64),
+                    inp["W2_0"].astype(np.float64), inp["alpha_f"].astype(np.float64),
+                    inp["alpha_b"].astype(np.float64), eta=sub.eta, b=sub.b, loss=sub.loss, gelu_form=sub.gelu,
+                    workers=nw)
+    dt = time.perf_counter() - t0
+    return dict(value=tokens / dt, unit="tokens/s", cores=nw, kind="oracle",
+                sample=f"{wl.name} workload, first {tokens} tokens (one segment), all {wl.H} heads, attention and "
+                       f"both TTT directions, fp64 NumPy, {dt:.1f} s wall")
+
+
+def bench_hybrid(args, wl):
+    """A step is one ttt_hybrid_block call: the attention projections, the segment
+    attention, the output projection with the residual, and the bidirectional TTT layer."""
+    import numpy as np
+    import torch
+
+    from test_rnn_layer_amd import _lib
+    from test_rnn_layer_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(wl)
+    thA, thO = W.make_attention_weights(wl)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    X, th, tA, tO = bf(inp["X"]), bf(inp["theta"]), bf(thA), bf(thO)
+    W1, W2 = f32(inp["W1_0"]), f32(inp["W2_0"])
+    af, ab = f32(inp["alpha_f"]), f32(inp["alpha_b"])
+    del inp, thA, thO
+    cfg = _lib.make_config(wl.B, wl.T, wl.H, wl.d, wl.m, wl.b, wl.eta, io_dtype=wl.io_dtype, loss=wl.loss,
+                           gelu=wl.gelu, algo=args.algo)
+    ws = torch.empty(_lib.hybrid_workspace_size(cfg, wl.attn_seg), dtype=torch.uint8, device=dev)
+    Y = torch.empty_like(X)
+    step = lambda: _lib.hybrid_block(cfg, wl.attn_seg, X, tA, tO, th, W1, W2, af, ab, workspace=ws, out=Y)
+    print("# bench: hybrid block, inputs resident, warming up", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.set_kernel_timing(True)
+    _lib.reset_kernel_timing()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kinds = {"attention": _lib.TTT_KERNEL_ATTENTION, "scan": _lib.TTT_KERNEL_SCAN, "projection": _lib.TTT_KERNEL_PROJECT}
+    km = {k: _lib.kernel_timing(v) for k, v in kinds.items()}
+    _lib.set_kernel_timing(False)
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = wl.B * wl.T
+    ams, an = km["attention"]
+    af_launch = attention_flops(wl.T, wl.attn_seg, wl.H, wl.d) * wl.B
+    avg_ms = ams / an
+    achieved = af_launch / (avg_ms / 1e3) / 1e12
+    # block roofline: attention, the attention projections (Q|K|V and output: 8 D^2 per token) and the TTT
+    # projections at the bf16 peak, the TTT scan at the fp32 peak
+    mm_total = af_launch + (8 * wl.D * wl.D + proj_flops_per_token(wl.D) * 2) * tokens
+    scan_total = scan_flops_per_token_head(wl.d, wl.m, wl.b) * wl.H * tokens * 2
+    R_ms = (mm_total / (PEAK_BF16_TFLOPS * 1e12) + scan_total / (PEAK_FP32_TFLOPS * 1e12)) * 1e3
+    out = {
+        "metric": METRIC_HYBRID, "value": tokens / (ms_per_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "d": wl.d, "m": wl.m, "b": wl.b,
+                   "eta": wl.eta, "D": wl.D, "attention_segment": wl.attn_seg, "directions": 2,
+                   "scan_kernel": "scan_" + _lib.select_algo(cfg), "model": wl.model},
+        "roofline": {"bound": "mfma", "kernel": "segment_attention", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": af_launch, "avg_launch_ms": avg_ms},
+        "layer_roofline": {"R_ms": R_ms, "frac": R_ms / ms_per_step,
+                           "definition": "attention and projection flops at bf16 MFMA peak + TTT scan flops at "
+                                         "fp32 peak"},
+        "kernel_ms_per_step": {k: ms / args.steps for k, (ms, n) in km.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("# bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_hybrid(wl, args.cpu_tokens or 4096)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,7 +313,8 @@ def main():
     ap.add_argument("--workload", default="bidir307k")
     ap.add_argument("--algo", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--cpu-tokens", type=int, default=None,
-                    help="tokens of the CPU oracle's sample (default 24576; 16 with --backward)")
+                    help="tokens of the CPU oracle's sample (default 24576; 16 with --backward, 4096 for the "
+                         "hybrid block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time ttt_mlp_bidir_backward instead")
     args = ap.parse_args()
@@ -235,6 +339,8 @@ def main():
             print("bench.py --backward: the backward covers the MLP model only", file=sys.stderr)
             sys.exit(2)
         return bench_backward(args, wl)
+    if wl.attn_seg > 0:
+        return bench_hybrid(args, wl)
     inp = W.make_inputs(wl)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)

@@ -204,17 +204,42 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
                                float* dalpha_b, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Segment-local attention, the hybrid block's step before the TTT layer (the
+ * notes page's framework: self-attention within each 3-second segment, the
+ * TTT layer over the whole sequence).  bf16 io, head width d = 64.
+ *   QKV [B, T, 3D] bf16: Q | K | V of every token (head h at columns 64 h of
+ *   each); O [B, T, D] bf16.  Segments are [s L, (s+1) L) of every sequence,
+ *   L = seg_len (the last one shorter); within a segment every query attends
+ *   to every key (no causal mask): O = softmax(Q K^T / sqrt(d)) V per head,
+ *   fp32 scores, softmax and accumulation.
+ */
+int32_t ttt_segment_attention(const ttt_mlp_config* cfg, int64_t seg_len, const void* QKV, void* O, void* stream);
+
+/*
+ * The hybrid block: U = X + attention(X theta_attn^T) theta_out^T (no biases or
+ * norms), then Y = ttt_mlp_bidir over U.  theta_attn [3, D, D] and theta_out
+ * [D, D] are bf16, [out, in]; the rest as for ttt_mlp_bidir (bf16 io, d = 64).
+ * Workspace: ttt_hybrid_block_workspace_size.
+ */
+int32_t ttt_hybrid_block_workspace_size(const ttt_mlp_config* cfg, int64_t seg_len, size_t* bytes);
+int32_t ttt_hybrid_block(const ttt_mlp_config* cfg, int64_t seg_len, const void* X, const void* theta_attn,
+                         const void* theta_out, const void* theta_qkv, const float* W1_0, const float* W2_0,
+                         const float* alpha_f, const float* alpha_b, void* Y, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * Kernel timing, for measurement.  While enabled, every compute call brackets
  * each kernel launch with HIP events on the stream the kernel runs on.
  * ttt_mlp_kernel_timing waits for the recorded events and returns the summed
  * duration (ms) and launch count of one kernel kind since the last reset.
  *   kind: TTT_KERNEL_PROJECT (the projection GEMM), TTT_KERNEL_SCAN (the scan),
- *   TTT_KERNEL_BACKWARD or TTT_KERNEL_GRAD_GEMM (below).
+ *   TTT_KERNEL_BACKWARD, TTT_KERNEL_GRAD_GEMM or TTT_KERNEL_ATTENTION (below).
  */
 #define TTT_KERNEL_PROJECT 0
 #define TTT_KERNEL_SCAN 1
 #define TTT_KERNEL_BACKWARD 2  /* the backward scan */
 #define TTT_KERNEL_GRAD_GEMM 3 /* the backward's dX and dtheta GEMMs */
+#define TTT_KERNEL_ATTENTION 4 /* the segment attention */
 int32_t ttt_mlp_set_kernel_timing(int32_t enable);
 int32_t ttt_mlp_kernel_timing(int32_t kind, double* total_ms, int64_t* launches);
 int32_t ttt_mlp_reset_kernel_timing(void);

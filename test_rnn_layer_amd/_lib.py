@@ -19,7 +19,7 @@ TTT_LOSS_MEAN, TTT_LOSS_SUM = 0, 1
 TTT_GELU_ERF, TTT_GELU_TANH = 0, 1
 TTT_MODEL_MLP, TTT_MODEL_LINEAR = 0, 1
 TTT_ALGO_AUTO, TTT_ALGO_GENERIC, TTT_ALGO_MFMA, TTT_ALGO_COOP = 0, 1, 2, 3
-TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN, TTT_KERNEL_BACKWARD, TTT_KERNEL_GRAD_GEMM = 0, 1, 2, 3
+TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN, TTT_KERNEL_BACKWARD, TTT_KERNEL_GRAD_GEMM, TTT_KERNEL_ATTENTION = 0, 1, 2, 3, 4
 
 EXPORTED = [
     "ttt_mlp_version", "ttt_mlp_status_string", "ttt_mlp_last_error", "ttt_mlp_workspace_size",
@@ -27,6 +27,7 @@ EXPORTED = [
     "ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_project", "ttt_mlp_set_kernel_timing",
     "ttt_mlp_kernel_timing", "ttt_mlp_reset_kernel_timing",
     "ttt_mlp_backward_workspace_size", "ttt_mlp_backward", "ttt_mlp_bidir_backward",
+    "ttt_segment_attention", "ttt_hybrid_block_workspace_size", "ttt_hybrid_block",
 ]
 
 
@@ -86,6 +87,13 @@ def lib() -> ctypes.CDLL:
         L.ttt_mlp_bidir_backward.restype = _i32
         L.ttt_mlp_bidir_backward.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _fp, _fp,
                                              _fp, _fp, _fp, _fp, _fp, _fp, _vp, _sz, _vp]
+        L.ttt_segment_attention.restype = _i32
+        L.ttt_segment_attention.argtypes = [ctypes.POINTER(Config), ctypes.c_int64, _vp, _vp, _vp]
+        L.ttt_hybrid_block_workspace_size.restype = _i32
+        L.ttt_hybrid_block_workspace_size.argtypes = [ctypes.POINTER(Config), ctypes.c_int64, ctypes.POINTER(_sz)]
+        L.ttt_hybrid_block.restype = _i32
+        L.ttt_hybrid_block.argtypes = [ctypes.POINTER(Config), ctypes.c_int64, _vp, _vp, _vp, _vp, _fp, _fp, _fp, _fp,
+                                       _vp, _vp, _sz, _vp]
         _lib = L
     return _lib
 
@@ -216,6 +224,33 @@ def bidir_backward(cfg: Config, X, theta, W1_0, W2_0, alpha_f, alpha_b, dY, *, w
                                         _ptr(g["dW1_0"]), _ptr(g["dW2_0"]), _ptr(g["dalpha_f"]),
                                         _ptr(g["dalpha_b"]), _ptr(ws), ws.numel(), _stream(X.device)))
     return g
+
+
+def segment_attention(cfg: Config, seg_len: int, QKV):
+    """ttt_segment_attention: QKV [B, T, 3 D] bf16 -> O [B, T, D] bf16."""
+    import torch
+    O = torch.empty((cfg.B, cfg.T, cfg.H * cfg.d), dtype=QKV.dtype, device=QKV.device)
+    _check(lib().ttt_segment_attention(ctypes.byref(cfg), seg_len, _ptr(QKV), _ptr(O), _stream(QKV.device)))
+    return O
+
+
+def hybrid_workspace_size(cfg: Config, seg_len: int) -> int:
+    n = _sz(0)
+    _check(lib().ttt_hybrid_block_workspace_size(ctypes.byref(cfg), seg_len, ctypes.byref(n)))
+    return n.value
+
+
+def hybrid_block(cfg: Config, seg_len: int, X, theta_attn, theta_out, theta, W1_0, W2_0, alpha_f, alpha_b, *,
+                 workspace=None, out=None):
+    """ttt_hybrid_block: returns Y [B, T, D] bf16."""
+    import torch
+    Y = torch.empty_like(X) if out is None else out
+    ws = (torch.empty(max(hybrid_workspace_size(cfg, seg_len), 1), dtype=torch.uint8, device=X.device)
+          if workspace is None else workspace)
+    _check(lib().ttt_hybrid_block(ctypes.byref(cfg), seg_len, _ptr(X), _ptr(theta_attn), _ptr(theta_out), _ptr(theta),
+                                  _ptr(W1_0), _ptr(W2_0), _ptr(alpha_f), _ptr(alpha_b), _ptr(Y), _ptr(ws), ws.numel(),
+                                  _stream(X.device)))
+    return Y
 
 
 def project(cfg: Config, X, theta):

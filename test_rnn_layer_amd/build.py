@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libttt_mlp.so")
 SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_linear.hip", "scan_coop.hip",
-           "backward.hip"]
+           "backward.hip", "attention.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -53,7 +53,7 @@ def _check_no_spill(src, remarks):
 # instructions later gave wrong values on gfx950 (the compiler inserts no wait
 # for it).  The build compiles these sources to assembly as well and refuses any
 # product whose accumulator comes from a product of another instruction.
-MFMA_CHAIN_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "proj_mfma.hip"}
+MFMA_CHAIN_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "proj_mfma.hip", "attention.hip"}
 _MFMA = re.compile(r"\s*(v_mfma\w*)\s+v\[(\d+):(\d+)\],\s*[^,]+,\s*[^,]+,\s*(?:v\[(\d+):(\d+)\]|\S+)")
 _VDST = re.compile(r"\s*(?:v_|ds_read|global_load|buffer_load|scratch_load|flat_load)\S*\s+(?:v(\d+)|v\[(\d+):(\d+)\])")
 

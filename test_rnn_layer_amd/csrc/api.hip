@@ -43,7 +43,7 @@ struct TimingRecord {
 std::mutex g_timing_mu;
 bool g_timing_on = false;
 std::vector<TimingRecord> g_timing_records;
-constexpr int kTimingKinds = 4;
+constexpr int kTimingKinds = 5;
 double g_timing_ms[kTimingKinds] = {};
 int64_t g_timing_n[kTimingKinds] = {};
 
@@ -617,6 +617,58 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xi
   return TTT_OK;
 }
 
+// ---------------------------------------------------------------------------
+// hybrid block: segment-local attention feeding the bidirectional TTT layer
+// ---------------------------------------------------------------------------
+int32_t check_attention(const ttt_mlp_config* c, int64_t seg_len) {
+  int32_t st = check_config(c);
+  if (st != TTT_OK) return st;
+  if (seg_len < 1) return fail(TTT_ERR_INVALID_ARG, "seg_len must be >= 1 (got %lld)", (long long)seg_len);
+  if (c->io_dtype != TTT_BF16 || !ttt::segment_attention_supported(c->d) || ((int64_t)c->H * c->d) % 8 != 0)
+    return fail(TTT_ERR_UNSUPPORTED, "segment attention needs bf16 io and head width 64 (got d=%d io=%d)", c->d,
+                c->io_dtype);
+  return TTT_OK;
+}
+
+struct HybridPlan {
+  size_t qkv_off, o_off, u_off, ttt_off, ttt_bytes, total;
+};
+
+int32_t make_hybrid_plan(const ttt_mlp_config* c, int64_t seg_len, HybridPlan* p) {
+  int32_t st = check_attention(c, seg_len);
+  if (st != TTT_OK) return st;
+  Plan tp;
+  st = make_plan(c, &tp);
+  if (st != TTT_OK) return st;
+  const size_t BTD = (size_t)c->B * c->T * c->H * c->d;
+  p->qkv_off = 0;
+  p->o_off = p->qkv_off + align_up(3 * BTD * 2);
+  p->u_off = p->o_off + align_up(BTD * 2);
+  p->ttt_off = p->u_off + align_up(BTD * 2);
+  p->ttt_bytes = tp.total;
+  p->total = p->ttt_off + align_up(tp.total);
+  return TTT_OK;
+}
+
+// row-major bf16 GEMM out[B*T, N] = X theta^T (+ resid), theta [N, D]
+hipError_t launch_rowmajor_gemm(const ttt_mlp_config* c, const void* X, const void* theta, int N, const void* resid,
+                                void* out, hipStream_t s) {
+  ttt::ProjArgs pa{};
+  pa.X = X;
+  pa.theta = theta;
+  pa.out = out;
+  pa.B = c->B;
+  pa.T = c->T;
+  pa.H = c->H;
+  pa.d = c->d;
+  pa.bf16 = 1;
+  pa.tt0 = 0;
+  pa.tt1 = c->T;
+  pa.n_out = N;
+  pa.resid = resid;
+  return timed_launch(TTT_KERNEL_PROJECT, s, [&] { return ttt::launch_project_mfma(pa, 2, s); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -822,6 +874,76 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   if (st == TTT_OK) st = bwd_project(cfg, bp, X, theta_qkv, ws, s);
   if (st == TTT_OK)
     st = bwd_direction(cfg, bp, X, theta_qkv, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s);
+  return st == TTT_OK ? ok() : st;
+}
+
+int32_t ttt_segment_attention(const ttt_mlp_config* cfg, int64_t seg_len, const void* QKV, void* O, void* stream) {
+  int32_t st = check_attention(cfg, seg_len);
+  if (st != TTT_OK) return st;
+  if (cfg->T > 0 && (!QKV || !O)) return fail(TTT_ERR_INVALID_ARG, "QKV and O are required");
+  const size_t BTD = (size_t)cfg->B * cfg->T * cfg->H * cfg->d;
+  const Buf outs[] = {{O, BTD * 2, "O"}};
+  const Buf ins[] = {{QKV, 3 * BTD * 2, "QKV"}};
+  st = check_no_overlap(outs, 1, ins, 1);
+  if (st != TTT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed_launch(TTT_KERNEL_ATTENTION, s, [&] {
+    return ttt::launch_segment_attention((const uint16_t*)QKV, (uint16_t*)O, cfg->B, cfg->T, cfg->H, seg_len, s);
+  });
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t ttt_hybrid_block_workspace_size(const ttt_mlp_config* cfg, int64_t seg_len, size_t* bytes) {
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  HybridPlan hp;
+  int32_t st = make_hybrid_plan(cfg, seg_len, &hp);
+  if (st != TTT_OK) return st;
+  *bytes = hp.total;
+  return ok();
+}
+
+int32_t ttt_hybrid_block(const ttt_mlp_config* cfg, int64_t seg_len, const void* X, const void* theta_attn,
+                         const void* theta_out, const void* theta_qkv, const float* W1_0, const float* W2_0,
+                         const float* alpha_f, const float* alpha_b, void* Y, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  HybridPlan hp;
+  int32_t st = make_hybrid_plan(cfg, seg_len, &hp);
+  if (st != TTT_OK) return st;
+  const bool lin = is_linear(cfg);
+  if ((cfg->T > 0 && (!X || !Y)) || !theta_attn || !theta_out || !theta_qkv || !W1_0 || (!lin && !W2_0) ||
+      !alpha_f || !alpha_b)
+    return fail(TTT_ERR_INVALID_ARG, "a required pointer (X, theta_attn, theta_out, theta_qkv, W1_0, W2_0, alpha_f, "
+                                     "alpha_b, Y) is NULL");
+  if (!workspace || workspace_bytes < hp.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                hp.total);
+  const size_t D = (size_t)cfg->H * cfg->d, BTD = (size_t)cfg->B * cfg->T * D;
+  const size_t w0 = (size_t)cfg->H * cfg->d * cfg->m * 4;
+  const Buf outs[] = {{Y, BTD * 2, "Y"}, {workspace, hp.total, "workspace"}};
+  const Buf ins[] = {{X, BTD * 2, "X"},           {theta_attn, 3 * D * D * 2, "theta_attn"},
+                     {theta_out, D * D * 2, "theta_out"}, {theta_qkv, 3 * D * D * 2, "theta_qkv"},
+                     {W1_0, w0, "W1_0"},          {lin ? nullptr : W2_0, w0, "W2_0"},
+                     {alpha_f, D * 4, "alpha_f"}, {alpha_b, D * 4, "alpha_b"}};
+  st = check_no_overlap(outs, 2, ins, 8);
+  if (st != TTT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* qkv = ws + hp.qkv_off;
+  void* o = ws + hp.o_off;
+  void* u = ws + hp.u_off;
+  if (cfg->T > 0) {
+    hipError_t e = launch_rowmajor_gemm(cfg, X, theta_attn, (int)(3 * D), nullptr, qkv, s);  // Q | K | V
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "attention projection launch: %s", hipGetErrorString(e));
+    e = timed_launch(TTT_KERNEL_ATTENTION, s, [&] {
+      return ttt::launch_segment_attention((const uint16_t*)qkv, (uint16_t*)o, cfg->B, cfg->T, cfg->H, seg_len, s);
+    });
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+    e = launch_rowmajor_gemm(cfg, o, theta_out, (int)D, X, u, s);  // U = X + O theta_out^T
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "output projection launch: %s", hipGetErrorString(e));
+  }
+  st = ttt_mlp_bidir(cfg, cfg->T > 0 ? u : nullptr, theta_qkv, W1_0, W2_0, alpha_f, alpha_b, Y, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, ws + hp.ttt_off, hp.ttt_bytes, stream);
   return st == TTT_OK ? ok() : st;
 }
 

@@ -19,12 +19,15 @@ struct ProjArgs {
   int64_t tt0, tt1;   // token-block GEMM only: tokens [tt0, tt1) of every sequence (others: 0, T)
   int32_t max_wg;     // token-block GEMM only: at most this many workgroups, each taking several
                       // tiles in turn (0: one workgroup per tile)
+  int32_t n_out;      // row-major mode only: output columns N (theta is [N, D]); 0 elsewhere (N = 3 D)
+  const void* resid;  // row-major mode only: bf16 [B*T, N] added to the product, or null
 };
 
 // fp32 output, [3, B, H, T, d] (VALU kernel, any dtype and shape).
 hipError_t launch_project_f32out(const ProjArgs& a, hipStream_t s);
 
-// bf16 MFMA GEMM; mode 0: fp32 [3, B, H, T, d]; mode 1: the MFMA scan's token blocks.
+// bf16 MFMA GEMM; mode 0: fp32 [3, B, H, T, d]; mode 1: the MFMA scan's token blocks;
+// mode 2: bf16 row-major [B*T, n_out] (+ resid).
 bool project_mfma_supported(const ProjArgs& a);
 hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s);
 // Zeroes the rows past the end of each sequence's last token block (mode 1 layout).
@@ -125,5 +128,11 @@ hipError_t launch_dalpha(const float* dy, const float* z, const float* alpha, fl
 // dW1 [H, d, m], dW2 [H, m, d] (+)= sum over sequences of dw_seq [B, H, 2 d m]
 hipError_t launch_sum_state(const float* dw_seq, float* dW1, float* dW2, int64_t B, int H, int d, int m,
                             int accumulate, hipStream_t s);
+
+// Segment-local attention (head width 64, bf16): qkv [B, T, 3 D] (Q | K | V, head h at
+// columns 64 h of each), out [B, T, D]; segments of L tokens (the last one shorter).
+bool segment_attention_supported(int d);
+hipError_t launch_segment_attention(const uint16_t* qkv, uint16_t* out, int64_t B, int64_t T, int H, int64_t L,
+                                    hipStream_t s);
 
 }  // namespace ttt

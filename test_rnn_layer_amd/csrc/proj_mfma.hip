@@ -9,8 +9,10 @@
 // 144 bytes: the 16 rows read by one 16-lane group land on distinct banks),
 // fp32 accumulation in v_mfma_f32_16x16x32_bf16.
 //
-// Two epilogues: fp32 [3, B, H, T, d] (inspection / generic scan) and the
-// bf16 token-block layout the MFMA scan reads (see scan_mfma.hip).
+// Three epilogues: fp32 [3, B, H, T, d] (inspection / generic scan), the
+// bf16 token-block layout the MFMA scan reads (see scan_mfma.hip), and plain
+// row-major bf16 [B*T, N] with an optional bf16 residual of the same shape
+// added in fp32 (the hybrid block's attention projections; N = n_out).
 #include <algorithm>
 #include <cmath>
 
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a) {
   const int d = a.d;
   const int D = a.H * d;
   const int64_t M = a.B * a.T;
-  const int N = 3 * D;
+  const int N = a.n_out > 0 ? a.n_out : 3 * D;
   const int K = D;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -102,6 +104,21 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int col = n0 + wn * 64 + j * 16 + c;
     if (col >= N) continue;
+    if (MODE == 2) {
+      uint16_t* out = (uint16_t*)a.out;
+      const uint16_t* res = (const uint16_t*)a.resid;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = m0 + wm * 64 + i * 16 + 4 * g + r;
+          if (row >= M) continue;
+          float v = acc[i][j][r];
+          if (res) v += bf16_to_f32(res[row * N + col]);
+          out[row * N + col] = to_bf16_bits(v);
+        }
+      continue;
+    }
     const int p = col / D, rem = col - p * D, h = rem / d, jj = rem - h * d;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -316,7 +333,7 @@ bool project_mfma_supported(const ProjArgs& a) { return a.bf16 && (a.H * a.d) % 
 
 hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s) {
   const int N = 3 * a.H * a.d;
-  if (mode == 1 && a.d == 64 && (a.H * a.d) % T_BK == 0) {
+  if (mode == 1 && a.n_out <= 0 && a.d == 64 && (a.H * a.d) % T_BK == 0) {
     const int64_t M = a.B * (a.tt1 - a.tt0);
     if (M == 0) return hipSuccess;
     const int mtiles = (int)((M + T_BM - 1) / T_BM), ntiles = (N + T_BN - 1) / T_BN;
@@ -334,11 +351,14 @@ hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s) {
   if (a.tt0 != 0 || a.tt1 != a.T) return hipErrorInvalidValue;  // the other kernels cover whole sequences
   const int64_t M = a.B * a.T;
   if (M == 0) return hipSuccess;
-  dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
+  const int Nk = a.n_out > 0 ? a.n_out : N;
+  dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((Nk + BN - 1) / BN));
   if (mode == 0)
     hipLaunchKernelGGL(proj_mfma_kernel<0>, grid, dim3(256), 0, s, a);
-  else
+  else if (mode == 1)
     hipLaunchKernelGGL(proj_mfma_kernel<1>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(proj_mfma_kernel<2>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ from dataclasses import dataclass
 import numpy as np
 
 # tensor ids inside the seed sequence
-TID_X, TID_THETA_Q, TID_THETA_K, TID_THETA_V, TID_W1, TID_W2, TID_SEGMEAN, TID_DY = range(8)
+TID_X, TID_THETA_Q, TID_THETA_K, TID_THETA_V, TID_W1, TID_W2, TID_SEGMEAN, TID_DY, TID_THETA_A, TID_THETA_O = range(10)
 X_CHUNK = 4096
 
 
@@ -56,6 +56,7 @@ class Workload:
     loss: str = "mean"  # "mean" (1/d)||e||^2, or "sum" ||e||^2
     gelu: str = "erf"  # "erf" (exact) or "tanh" (approximation)
     model: str = "mlp"  # "mlp": f(u; W) = GELU(u W1) W2; "linear": f(u; W) = u W with W = W1 (m = d)
+    attn_seg: int = 0  # > 0: the hybrid block, segment-local attention over segments of this many tokens
 
     @property
     def D(self) -> int:
@@ -82,6 +83,9 @@ WORKLOADS = {
 WORKLOAD_ORDER = ["tiny_f32", "seg14k", "bidir100k", "bidir307k", "bigstate307k"]
 # TTT-Linear (the same layer with a linear inner model, d x d state) at the shape of bidir307k
 WORKLOADS["linear307k"] = WORKLOADS["bidir307k"].replace(name="linear307k", m=64, model="linear")
+# the hybrid block (segment-local attention over 3-second segments of 14,400 tokens, then the
+# bidirectional TTT-MLP layer) at the shape of bidir307k
+WORKLOADS["hybrid307k"] = WORKLOADS["bidir307k"].replace(name="hybrid307k", attn_seg=14_400)
 
 
 # ----------------------------------------------------------------------------
@@ -197,6 +201,15 @@ def make_dy(wl: Workload, t1: int | None = None, heads=None) -> np.ndarray:
             keep[h * wl.d:(h + 1) * wl.d] = True
         g[..., ~keep] = 0.0
     return g
+
+
+def make_attention_weights(wl: Workload) -> tuple[np.ndarray, np.ndarray]:
+    """The hybrid block's attention projections, stored format: theta_A [3, D, D]
+    (Q, K, V, each [out, in]) and theta_O [D, D], every entry N(0, 1/D)."""
+    D = wl.D
+    thA = _store(_rng(wl.seed, TID_THETA_A).standard_normal((3, D, D)) / np.sqrt(D), wl.io_dtype)
+    thO = _store(_rng(wl.seed, TID_THETA_O).standard_normal((D, D)) / np.sqrt(D), wl.io_dtype)
+    return thA, thO
 
 
 def make_inputs(wl: Workload) -> dict:

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ttt_mlp_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ttt_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -188,3 +188,21 @@ def test_backward_workspace_and_validation():
     st = lib.ttt_mlp_bidir_backward(ctypes.byref(c), f(0), f(1), f(2), f(3), f(4), None, f(11), f(5), f(6), f(7),
                                     f(8), f(9), f(12), f(10), n2, None)
     assert st == L.TTT_ERR_INVALID_ARG  # alpha_b missing
+
+
+def test_attention_and_hybrid_validation():
+    lib = L.lib()
+    c = cfg()
+    assert L.hybrid_workspace_size(c, 14400) > L.workspace_size(c, True)
+    for bad, status in [(dict(io_dtype="f32"), L.TTT_ERR_UNSUPPORTED), (dict(d=32, m=128), L.TTT_ERR_UNSUPPORTED)]:
+        with pytest.raises(L.TTTError) as e:
+            L.hybrid_workspace_size(cfg(**bad), 100)
+        assert e.value.status == status, bad
+    with pytest.raises(L.TTTError) as e:
+        L.hybrid_workspace_size(c, 0)
+    assert e.value.status == L.TTT_ERR_INVALID_ARG
+    fake = 1 << 40
+    st = lib.ttt_segment_attention(ctypes.byref(c), 16, fake, None, None)
+    assert st == L.TTT_ERR_INVALID_ARG
+    st = lib.ttt_segment_attention(ctypes.byref(c), 16, fake, fake + 64, None)  # O over QKV
+    assert st == L.TTT_ERR_INVALID_ARG and b"overlaps" in lib.ttt_mlp_last_error()
