@@ -6,8 +6,9 @@
 // [64 h, 64 h + 64)):  O = softmax(Q K^T / sqrt(64)) V over the segment's keys,
 // no causal mask.  bf16 Q, K, V and O, fp32 scores, softmax and accumulation.
 //
-// One 512-thread workgroup (8 waves) takes 128 queries of one segment and
-// head; each wave owns 16 queries.  Keys arrive in blocks of 64 (K and V
+// One 512-thread workgroup (8 waves) takes 128 QT queries of one segment and
+// head; each wave owns QT tiles of 16 queries, which share every K and V
+// fragment it reads from LDS.  Keys arrive in blocks of 128 (K and V
 // staged through two LDS buffers, the next block's rows held in registers
 // while this block computes).  A wave computes the transposed scores
 // S^T = K Q^T (keys x its 16 queries), so that each lane holds scores of one
@@ -24,11 +25,15 @@ namespace ttt {
 namespace {
 
 constexpr int AD = 64;           // head width
-constexpr int AQ = 128;          // queries per workgroup (8 waves x 16)
-constexpr int AKB = 64;          // keys per block
-constexpr int ARS = 72;          // LDS row stride (bf16): 144-byte rows, conflict-free fragment reads
+constexpr int QT = 2;            // 16-query tiles per wave: they share every K and V fragment read
+constexpr int AQ = 128 * QT;     // queries per workgroup (8 waves)
+constexpr int AKB = 128;         // keys per block
+constexpr int NT = AKB / 16;     // 16-key tiles per block
+constexpr int ARS = 72;          // LDS row stride of K (bf16): 144-byte rows, conflict-free fragment reads
+constexpr int VRS = AKB + 8;     // LDS row stride of V^T
 constexpr int A_THREADS = 512;
-constexpr int A_STAGE = 2 * AKB * ARS;  // bf16 elements of one stage: K rows, then V^T rows
+constexpr int A_STAGE = AKB * ARS + AD * VRS;  // bf16 elements of one stage: K rows, then V^T rows
+constexpr int SCH = AKB / 64;    // 16-byte chunks of K (and of V) each thread stages per block
 
 __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint16_t* __restrict__ qkv,
                                                                      uint16_t* __restrict__ out, int64_t T, int H,
@@ -50,33 +55,51 @@ __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint
   const int64_t D = (int64_t)H * AD, row = 3 * D;
   const uint16_t* base = qkv + (b * T + s0) * row + (int64_t)h * AD;  // Q of the segment's token 0, head h
 
-  // this wave's 16 queries as the B operand (Q rows, 8 consecutive features per lane)
-  const int64_t myq = q0 + w * 16 + c;
-  const uint16_t* qrow = base + std::min(myq, n - 1) * row;
-  const bf16x8 qf0 = *(const bf16x8*)(qrow + 8 * g);
-  const bf16x8 qf1 = *(const bf16x8*)(qrow + 32 + 8 * g);
+  // this wave's queries (QT tiles of 16) as B operands (Q rows, 8 consecutive features per lane)
+  int64_t myq[QT];
+  bf16x8 qf0[QT], qf1[QT];
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    myq[u] = q0 + (w * QT + u) * 16 + c;
+    const uint16_t* qrow = base + std::min(myq[u], n - 1) * row;
+    qf0[u] = *(const bf16x8*)(qrow + 8 * g);
+    qf1[u] = *(const bf16x8*)(qrow + 32 + 8 * g);
+  }
 
-  // staging: thread t moves one 16-byte chunk of K and one of V per block
-  const int sj = tid >> 3, sc = (tid & 7) * 8;  // key row 0..63 of the block, feature chunk
-  uint4 kreg, vreg;
+  // staging: thread t moves SCH 16-byte chunks of K and of V per block (key row sj + 64 i)
+  const int sj = tid >> 3, sc = (tid & 7) * 8;  // key row of the block, feature chunk
+  uint4 kreg[SCH], vreg[SCH];
   auto fetch = [&](int64_t kb) {
-    const int64_t key = std::min(kb * AKB + sj, n - 1);  // keys past the end load the last key (masked)
-    const uint16_t* kr = base + key * row + D + sc;
-    kreg = *(const uint4*)kr;
-    vreg = *(const uint4*)(kr + D);
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const int64_t key = std::min(kb * AKB + sj + 64 * i, n - 1);  // keys past the end load the last key
+      const uint16_t* kr = base + key * row + D + sc;
+      kreg[i] = *(const uint4*)kr;
+      vreg[i] = *(const uint4*)(kr + D);
+    }
   };
   auto stage = [&](int buf) {
     uint16_t* ks = smem + buf * A_STAGE;
     uint16_t* vt = ks + AKB * ARS;
-    *(uint4*)(ks + sj * ARS + sc) = kreg;
-    const uint16_t* v = (const uint16_t*)&vreg;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) vt[(sc + i) * ARS + sj] = v[i];  // V^T: feature rows, key columns
+    for (int i = 0; i < SCH; ++i) {
+      *(uint4*)(ks + (sj + 64 * i) * ARS + sc) = kreg[i];
+      const uint16_t* v = (const uint16_t*)&vreg[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(sc + e) * VRS + sj + 64 * i] = v[e];  // V^T: feature rows, key columns
+    }
   };
 
   const float qk_scale = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) and log2(e): p = exp2(s c - m)
-  float mrun = -INFINITY, lrun = 0.0f;
-  f32x4 o[4] = {zero4(), zero4(), zero4(), zero4()};  // O^T: feature tile dt, rows 4g..4g+3, query c
+  float mrun[QT], lrun[QT];
+  f32x4 o[QT][4];  // O^T: query tile u, feature tile dt, rows 4g..4g+3, query c
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    mrun[u] = -INFINITY;
+    lrun[u] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[u][dt] = zero4();
+  }
   const int64_t nkb = (n + AKB - 1) / AKB;
   fetch(0);
   stage(0);
@@ -86,67 +109,88 @@ __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint
     if (kb + 1 < nkb) fetch(kb + 1);
     const uint16_t* ks = smem + buf * A_STAGE;
     const uint16_t* vt = ks + AKB * ARS;
-    // S^T tiles: keys 16 t + 4g + r, query c
-    f32x4 s[4];
+    // S^T tiles: keys 16 t + 4g + r, query c of tile u
+    f32x4 sc_[QT][NT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const uint16_t* kr = ks + (t * 16 + c) * ARS;
-      s[t] = mfma32(*(const bf16x8*)(kr + 8 * g), qf0, zero4());
-      s[t] = mfma32(*(const bf16x8*)(kr + 32 + 8 * g), qf1, s[t]);
+      const bf16x8 k0 = *(const bf16x8*)(kr + 8 * g), k1 = *(const bf16x8*)(kr + 32 + 8 * g);
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        sc_[u][t] = mfma32(k0, qf0[u], zero4());
+        sc_[u][t] = mfma32(k1, qf1[u], sc_[u][t]);
+      }
     }
-    // mask keys past the segment's end, then the block's maximum for this query
     const int64_t kvalid = n - kb * AKB;
-    float bm = -INFINITY;
+    if (kvalid < AKB) {  // the segment's last, short block: mask keys past its end
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int u = 0; u < QT; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (t * 16 + 4 * g + r >= kvalid) s[t][r] = -INFINITY;
-        bm = fmaxf(bm, s[t][r]);
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (t * 16 + 4 * g + r >= kvalid) sc_[u][t][r] = -INFINITY;
+    }
+    bf16x8 pb[QT][NT / 2];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      f32x4* s = sc_[u];
+      // the block's maximum for this query
+      float bm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[t][r]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mnew = fmaxf(mrun[u], bm * qk_scale);
+      // exponents are <= 0: the hardware exp2 (results below 2^-126 flush to 0, harmlessly)
+      const float alpha = __builtin_amdgcn_exp2f(mrun[u] - mnew);  // 0 on the first block (mrun = -inf)
+      mrun[u] = mnew;
+      float ps = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], qk_scale, -mnew));
+          s[t][r] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      lrun[u] = lrun[u] * alpha + ps;
+      if (__any(alpha != 1.0f)) {  // once the maxima settle, most blocks leave them unchanged
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[u][dt] *= alpha;
       }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mnew = fmaxf(mrun, bm * qk_scale);
-    const float alpha = exp2f(mrun - mnew);  // 0 on the first block (mrun = -inf)
-    mrun = mnew;
-    float ps = 0.0f;
+      // keys of a K=32 chunk in pair order: tiles 2k (4g..4g+3) and 2k+1
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int k2 = 0; k2 < NT / 2; ++k2) pb[u][k2] = pack8(s[2 * k2], s[2 * k2 + 1]);
+    }
+    // O^T += V^T P^T
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(fmaf(s[t][r], qk_scale, -mnew));
-        s[t][r] = p;
-        ps += p;
-      }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    lrun = lrun * alpha + ps;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    // O^T += V^T P^T, keys of the K=32 chunk in pair order: tiles 2k (4g..4g+3) and 2k+1
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const bf16x8 pb = pack8(s[2 * k2], s[2 * k2 + 1]);
+    for (int k2 = 0; k2 < NT / 2; ++k2)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* vr = vt + (dt * 16 + c) * ARS + 32 * k2 + 4 * g;
-        const bf16x4 lo = *(const bf16x4*)vr;
-        const bf16x4 hi = *(const bf16x4*)(vr + 16);
-        o[dt] = mfma32(cat8(lo, hi), pb, o[dt]);
+        const uint16_t* vr = vt + (dt * 16 + c) * VRS + 32 * k2 + 4 * g;
+        const bf16x8 v8 = cat8(*(const bf16x4*)vr, *(const bf16x4*)(vr + 16));
+#pragma unroll
+        for (int u = 0; u < QT; ++u) o[u][dt] = mfma32(v8, pb[u][k2], o[u][dt]);
       }
-    }
     if (kb + 1 < nkb) stage(buf ^ 1);
     __syncthreads();
   }
   // O[query c][feature 16 dt + 4g + r] = O^T / l
-  if (myq < n) {
-    const float inv = 1.0f / lrun;
-    uint16_t* orow = out + (b * T + s0 + myq) * D + (int64_t)h * AD;
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    if (myq[u] >= n) continue;
+    const float inv = 1.0f / lrun[u];
+    uint16_t* orow = out + (b * T + s0 + myq[u]) * D + (int64_t)h * AD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       uint2 v;
-      v.x = pack2(o[dt][0] * inv, o[dt][1] * inv);
-      v.y = pack2(o[dt][2] * inv, o[dt][3] * inv);
+      v.x = pack2(o[u][dt][0] * inv, o[u][dt][1] * inv);
+      v.y = pack2(o[u][dt][2] * inv, o[u][dt][3] * inv);
       *(uint2*)(orow + dt * 16 + 4 * g) = v;
     }
   }
