@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a) {
 // in turn.  Rows past the end of X load its last row (never stored), so every
 // step issues the same loads.  The epilogue stages each wave's 128 x 64 bf16
 // sub-tile through LDS and writes whole 128-byte token rows of the scan's
-// token blocks.
+// token blocks, or (row-major mode) 128-byte row pieces of [B*T, N] with the
+// residual added.
 // ---------------------------------------------------------------------------
 constexpr int T_BM = 256, T_BN = 256, T_BK = 64, T_THREADS = 512;
 constexpr int T_STAGE = (T_BM + T_BN) * T_BK;  // bf16 elements per stage (64 KB)
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int D = a.H * d;
   const int64_t Tw = a.tt1 - a.tt0;  // tokens [tt0, tt1) of every sequence: GEMM row r is token
   const int64_t M = a.B * Tw;        // tt0 + r mod Tw of sequence r / Tw
-  const int N = 3 * D;
+  const int N = a.n_out > 0 ? a.n_out : 3 * D;
   const int K = D;
   const int tid = threadIdx.x, lane_ = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 2, wn = w & 3;
@@ -285,7 +286,29 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
     lds_stores_done();
     __builtin_amdgcn_wave_barrier();
     const int col0 = n0 + wn * 64;
-    if (col0 < N) {
+    if (a.n_out > 0) {
+      // row-major bf16 [M, N], plus the residual
+      uint16_t* out = (uint16_t*)a.out;
+      const uint16_t* res = (const uint16_t*)a.resid;
+  #pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int q = it * 64 + lane;
+        const int row = q >> 3, ch = q & 7;
+        const int64_t grow = m0 + wm * 128 + row;
+        if (grow >= M || col0 + 8 * ch >= N) continue;
+        uint4 v = *(const uint4*)(ctile + row * 64 + 8 * swz(row, ch));
+        if (res) {
+          const uint4 rv = *(const uint4*)(res + grow * N + col0 + 8 * ch);
+          const uint16_t* a16 = (const uint16_t*)&v;
+          const uint16_t* r16 = (const uint16_t*)&rv;
+          uint16_t o16[8];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) o16[e] = to_bf16_bits(bf16_to_f32(a16[e]) + bf16_to_f32(r16[e]));
+          v = *(const uint4*)o16;
+        }
+        *(uint4*)(out + grow * N + col0 + 8 * ch) = v;
+      }
+    } else if (col0 < N) {
       const int p = col0 / D, h = (col0 - p * D) / d;
       const int64_t nblk = (a.T + 15) / 16;
       uint16_t* out = (uint16_t*)a.out;
@@ -333,10 +356,12 @@ bool project_mfma_supported(const ProjArgs& a) { return a.bf16 && (a.H * a.d) % 
 
 hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s) {
   const int N = 3 * a.H * a.d;
-  if (mode == 1 && a.n_out <= 0 && a.d == 64 && (a.H * a.d) % T_BK == 0) {
+  // token blocks (mode 1, d = 64) and row-major output (mode 2, N a multiple of 8) on the 256 x 256 tiles
+  if (((mode == 1 && a.n_out <= 0 && a.d == 64) || (mode == 2 && a.n_out % 8 == 0)) && (a.H * a.d) % T_BK == 0) {
     const int64_t M = a.B * (a.tt1 - a.tt0);
     if (M == 0) return hipSuccess;
-    const int mtiles = (int)((M + T_BM - 1) / T_BM), ntiles = (N + T_BN - 1) / T_BN;
+    const int Nt = mode == 2 ? a.n_out : N;
+    const int mtiles = (int)((M + T_BM - 1) / T_BM), ntiles = (Nt + T_BN - 1) / T_BN;
     const int total = mtiles * ntiles;
     int grid = (total + 7) / 8 * 8;
     if (a.max_wg > 0) grid = std::min(grid, std::max(8, a.max_wg / 8 * 8));
