@@ -297,6 +297,8 @@ def summarize_stats(d: str, out_md: str | None = None):
     wl = W.WORKLOADS[wname]
     wl_arg = "" if wname == "bidir307k" else f" --workload {wname}"
     model = "TTT-Linear, d x d state" if wl.model == "linear" else "TTT-MLP"
+    if wl.attn_seg > 0:
+        model = f"segment attention (segments of {wl.attn_seg:,}, head width {wl.d}) + TTT-MLP"
     steps, warm = bench["steps"], bench["warmup"]
     calls = steps + warm
     tok = wl.B * wl.T
@@ -318,15 +320,26 @@ def summarize_stats(d: str, out_md: str | None = None):
         lines.append(f"| `{name}` | {n} | {float(r['AverageNs']) / 1e6:.3f} ms | "
                      f"{float(r['TotalDurationNs']) / 1e6 / calls:.2f} ms | {float(r['Percentage']):.1f}% |")
     rf = bench["roofline"]
+    if wl.attn_seg > 0:
+        lines[0] = (f"# Kernel time, {wname} (one ttt_hybrid_block call: attention projections, segment attention "
+                    "over segments of {:,} tokens, output projection, then the bidirectional TTT-MLP layer)"
+                    .format(wl.attn_seg))
+        what = (f"the attention's launches averaged {rf['avg_launch_ms']:.3f} ms from HIP events, "
+                f"{rf['flops_per_launch'] / 1e12:.2f} TFLOP each, {rf['achieved']:.1f} TFLOP/s. The attention and "
+                "its projections run before the TTT layer (it needs their output); inside the TTT layer the "
+                "projection runs on a second stream beside the scan.")
+        out_default = os.path.join(ROOT, "profiles", f"segment_attention_{wname}_stats.md")
+    else:
+        what = (f"the scan's launches averaged {rf['avg_launch_ms']:.3f} ms from HIP events on their stream, "
+                f"{rf['flops_per_launch'] / 1e9:.1f} GFLOP each, {rf['achieved']:.1f} TFLOP/s. The projection runs "
+                "on a second stream beside the scan; the call's time is that of the longer stream plus what cannot "
+                "overlap (the first projection chunk of each direction, the last scan chunk).")
+        out_default = os.path.join(ROOT, "profiles", f"{bench['config']['scan_kernel']}_proj_tiles_{wname}_stats.md")
     lines += ["", f"The bench line of the same run: {bench['ms_per_step']:.2f} ms per call "
-              f"({bench['value'] / 1e6:.3f} M tokens/s, {100 * bench['layer_roofline']['frac']:.1f}% of the layer "
-              f"roofline R = {bench['layer_roofline']['R_ms']:.2f} ms); the scan's launches averaged "
-              f"{rf['avg_launch_ms']:.3f} ms from HIP events on their stream, "
-              f"{rf['flops_per_launch'] / 1e9:.1f} GFLOP each, {rf['achieved']:.1f} TFLOP/s. The projection runs on "
-              "a second stream beside the scan; the call's time is that of the longer stream plus what cannot "
-              "overlap (the first projection chunk of each direction, the last scan chunk).",
+              f"({bench['value'] / 1e6:.3f} M tokens/s, {100 * bench['layer_roofline']['frac']:.1f}% of the "
+              f"roofline R = {bench['layer_roofline']['R_ms']:.2f} ms); " + what,
               f"Tokens per call: {tok:,} (both directions over every token)."]
-    out_md = out_md or os.path.join(ROOT, "profiles", f"{bench['config']['scan_kernel']}_proj_tiles_{wname}_stats.md")
+    out_md = out_md or out_default
     open(out_md, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
