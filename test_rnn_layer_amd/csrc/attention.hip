@@ -26,14 +26,16 @@ namespace {
 
 constexpr int AD = 64;           // head width
 constexpr int QT = 2;            // 16-query tiles per wave: they share every K and V fragment read
-constexpr int AQ = 128 * QT;     // queries per workgroup (8 waves)
+constexpr int NW = 8;            // waves per workgroup
+constexpr int AQ = NW * 16 * QT; // queries per workgroup
 constexpr int AKB = 128;         // keys per block
 constexpr int NT = AKB / 16;     // 16-key tiles per block
 constexpr int ARS = 72;          // LDS row stride of K (bf16): 144-byte rows, conflict-free fragment reads
 constexpr int VRS = AKB + 8;     // LDS row stride of V^T
-constexpr int A_THREADS = 512;
+constexpr int A_THREADS = 64 * NW;
+constexpr int SROWS = A_THREADS / 8;  // key rows staged per pass (8 threads per 128-byte row)
 constexpr int A_STAGE = AKB * ARS + AD * VRS;  // bf16 elements of one stage: K rows, then V^T rows
-constexpr int SCH = AKB / 64;    // 16-byte chunks of K (and of V) each thread stages per block
+constexpr int SCH = AKB / SROWS;  // 16-byte chunks of K (and of V) each thread stages per block
 
 __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint16_t* __restrict__ qkv,
                                                                      uint16_t* __restrict__ out, int64_t T, int H,
@@ -66,13 +68,13 @@ __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint
     qf1[u] = *(const bf16x8*)(qrow + 32 + 8 * g);
   }
 
-  // staging: thread t moves SCH 16-byte chunks of K and of V per block (key row sj + 64 i)
+  // staging: thread t moves SCH 16-byte chunks of K and of V per block (key rows sj + SROWS i)
   const int sj = tid >> 3, sc = (tid & 7) * 8;  // key row of the block, feature chunk
   uint4 kreg[SCH], vreg[SCH];
   auto fetch = [&](int64_t kb) {
 #pragma unroll
     for (int i = 0; i < SCH; ++i) {
-      const int64_t key = std::min(kb * AKB + sj + 64 * i, n - 1);  // keys past the end load the last key
+      const int64_t key = std::min(kb * AKB + sj + SROWS * i, n - 1);  // keys past the end load the last key
       const uint16_t* kr = base + key * row + D + sc;
       kreg[i] = *(const uint4*)kr;
       vreg[i] = *(const uint4*)(kr + D);
@@ -83,10 +85,10 @@ __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint
     uint16_t* vt = ks + AKB * ARS;
 #pragma unroll
     for (int i = 0; i < SCH; ++i) {
-      *(uint4*)(ks + (sj + 64 * i) * ARS + sc) = kreg[i];
+      *(uint4*)(ks + (sj + SROWS * i) * ARS + sc) = kreg[i];
       const uint16_t* v = (const uint16_t*)&vreg[i];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(sc + e) * VRS + sj + 64 * i] = v[e];  // V^T: feature rows, key columns
+      for (int e = 0; e < 8; ++e) vt[(sc + e) * VRS + sj + SROWS * i] = v[e];  // V^T: feature rows, key columns
     }
   };
 
