@@ -392,6 +392,23 @@ int proj_workgroups_beside_scan(int cus, int64_t scan_workgroups) {
   return cap >= kProjMinWorkgroups ? (int)cap : 0;
 }
 
+// Overlapping chunk k+1's projection with chunk k's scan pays while the
+// projection, squeezed onto the CUs the scan leaves free, keeps pace with the
+// scan.  With many (sequence, head) chains there are too few free CUs: each
+// direction then projects all its tokens on the whole chip first and scans
+// after.  Per token: the projection takes 6 D^2 flops at about 1.1 PFLOP/s on
+// the whole chip (cus / free times as long on the free CUs, beside the scan),
+// a chain's scan step about 2.3 us per 16 tokens (MLP) or 0.05 us per token
+// (linear), measured on MI355X.
+bool overlap_pays(const ttt_mlp_config* c, int cus) {
+  const int64_t free_cus = (int64_t)cus - c->B * c->H;
+  if (free_cus < kProjMinWorkgroups) return false;
+  const double D = (double)c->H * c->d;
+  const double proj_tok = 6.0 * D * D / 1.1e15;
+  const double scan_tok = is_linear(c) ? 0.05e-6 : 2.3e-6 / 16;
+  return (double)c->B * proj_tok * ((double)cus / (double)free_cus - 1.0) <= scan_tok;
+}
+
 struct Direction {
   const void* xin;
   const float* alpha;
@@ -405,17 +422,25 @@ struct Direction {
 int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs, int ndir, const void* theta,
                  const float* W1_0, const float* W2_0, char* ws, hipStream_t S) {
   const int64_t T = c->T;
-  const Chunking ch = chunking(T);
-  const int64_t C = ch.count();
   std::lock_guard<std::mutex> lk(g_side_mu);
   Side* sd = nullptr;
+  hipError_t e = side_for_device(&sd, 2);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+  const bool overlap = overlap_pays(c, sd->cus);
+  Chunking ch;
+  if (overlap) {
+    ch = chunking(T);
+  } else {  // one chunk per direction: the projection on the whole chip, then the scan
+    ch.b = {0, T};
+  }
+  const int64_t C = ch.count();
   // events: start, then per direction C projection + C scan events, then end
-  hipError_t e = side_for_device(&sd, 2 + 2 * (size_t)C * ndir);
+  e = side_for_device(&sd, 2 + 2 * (size_t)C * ndir);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
   hipStream_t S2 = sd->stream;
   // the cap pays where the scan is the longer of the two (the MLP); the linear
   // model's scan is a third of its projection, which then takes every free CU
-  const int proj_wg = is_linear(c) ? 0 : proj_workgroups_beside_scan(sd->cus, c->B * c->H);
+  const int proj_wg = (is_linear(c) || !overlap) ? 0 : proj_workgroups_beside_scan(sd->cus, c->B * c->H);
   hipEvent_t* ev = sd->events.data();
   hipEvent_t ev_start = ev[0], ev_end = ev[1];
   auto ev_proj = [&](int d, int64_t k) { return ev[2 + (2 * d) * C + k]; };

@@ -86,6 +86,9 @@ WORKLOADS["linear307k"] = WORKLOADS["bidir307k"].replace(name="linear307k", m=64
 # the hybrid block (segment-local attention over 3-second segments of 14,400 tokens, then the
 # bidirectional TTT-MLP layer) at the shape of bidir307k
 WORKLOADS["hybrid307k"] = WORKLOADS["bidir307k"].replace(name="hybrid307k", attn_seg=14_400)
+# the same 307,200 tokens as 2 or 4 sequences: the scan then runs on 96 or 192 CUs
+WORKLOADS["batch2x153k"] = WORKLOADS["bidir307k"].replace(name="batch2x153k", B=2, T=153_600)
+WORKLOADS["batch4x76k"] = WORKLOADS["bidir307k"].replace(name="batch4x76k", B=4, T=76_800)
 
 
 # ----------------------------------------------------------------------------

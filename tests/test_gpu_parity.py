@@ -261,3 +261,19 @@ def test_full_size_bidir(name, prefix):
     cols = np.concatenate([np.arange(h * wl.d, (h + 1) * wl.d) for h in heads])
     _check("Z_f prefix", Zf_pre[:, :, cols], ref["Z"], wl.io_dtype)
     _check("X' prefix", Xp_pre[:, :, cols], ref["Y"], wl.io_dtype)
+
+
+def test_many_chains_project_then_scan():
+    """Four sequences of 48 heads (192 scan chains): too few CUs are left beside the
+    scan, so each direction projects all its tokens on the whole chip and then scans
+    (one chunk per direction).  Against the oracle, every head."""
+    wl = W.WORKLOADS["batch4x76k"].replace(T=300, seg_len=0, alpha_f=0.1, alpha_b=0.2, name="batch4_small")
+    print(f"[many chains] B{wl.B} T{wl.T} H{wl.H}", flush=True)
+    inp = W.make_inputs(wl)
+    got = _gpu_bidir(wl, device_inputs(wl, inp), "mfma")
+    f64 = f64_inputs(wl, inp)
+    ref = O.ttt_bidir(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64["alpha_f"], f64["alpha_b"],
+                      eta=wl.eta, b=wl.b, loss=wl.loss, gelu_form=wl.gelu, workers=workers())
+    _check("Y", from_device(got["Y"]), ref["Y"], wl.io_dtype)
+    _check("Z_f", from_device(got["Z_f"]), ref["Z_f"], wl.io_dtype)
+    _check("Z_b", from_device(got["Z_b"]), ref["Z_b"], wl.io_dtype)
