@@ -35,6 +35,7 @@
 // each thread one output column and a few rows, reading operands 16 bytes at
 // a time (d and m multiples of 4).
 #include "internal.h"
+#include "mfma_common.h"
 
 namespace ttt {
 namespace {
@@ -88,7 +89,7 @@ __device__ inline void gelu3(float a, int tanh_form, float* g, float* dg, float*
 // X, W 16-byte aligned.  A thread takes one column and RG rows; k advances by 4 (X, and
 // W when WT, in 16-byte loads), in order, so every sum runs k = 0, 1, ... .
 template <int RG, bool WT>
-__device__ void prod(float* out, int ldo, int n, int C, int K, const float* X, int ldx, const float* W, int ldw,
+__device__ void prod_valu(float* out, int ldo, int n, int C, int K, const float* X, int ldx, const float* W, int ldw,
                      float s, bool acc) {
   const int groups = (n + RG - 1) / RG;
   for (int it = threadIdx.x; it < C * groups; it += BW) {
@@ -165,7 +166,7 @@ __device__ void rank_update(float* S, int ldS, int R, int C, int n, const Terms&
   }
 }
 
-__device__ inline void rank_update_any(float* S, int ldS, int R, int C, int n, const Terms& tm, float s) {
+__device__ inline void rank_update_valu(float* S, int ldS, int R, int C, int n, const Terms& tm, float s) {
   if (R % 16 == 0)
     rank_update<16>(S, ldS, R, C, n, tm, s);
   else
@@ -175,8 +176,8 @@ __device__ inline void rank_update_any(float* S, int ldS, int R, int C, int n, c
 // out[r, c] (n x n, row stride ldo) = s sum_{k<K} X[r, k] Y[c, k] for c <= r, 0 above the
 // diagonal.  Four lanes share an output, each summing every fourth k; lane exchanges add the
 // four partial sums.
-__device__ void rowdot_tril(float* out, int ldo, int n, int K, const float* X, int ldx, const float* Y, int ldy,
-                            float s) {
+__device__ void rowdot_tril_valu(float* out, int ldo, int n, int K, const float* X, int ldx, const float* Y,
+                                 int ldy, float s) {
   const int nn = n * n;
   for (int base = 0; base < 4 * nn; base += BW) {  // the same trip count in every lane
     const int it = base + (int)threadIdx.x;
@@ -192,6 +193,153 @@ __device__ void rowdot_tril(float* out, int ldo, int n, int K, const float* X, i
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
     if (o < nn && q == 0) out[r * ldo + c] = s * v;
+  }
+}
+
+// The same three operations on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32
+// products and sums like the VALU forms, in another order), for the shapes they tile:
+// each wave takes 16 x 16 output tiles; for lane l, i = l % 16 and q = l / 16,
+//   A[i][q] (row i, contraction index q), B[q][i], D[4q .. 4q+3][i].
+// In the products the lane group q takes the contraction range [q K/4, (q+1) K/4), one
+// index per instruction, so an operand that is contiguous along k arrives 16 bytes at a
+// time.  The first wave of a call is w0: calls in one phase start on different waves.  The
+// product routines stay out of line: inlined into the scan kernels, their operand addresses
+// pushed the kernels past 128 registers (the limit at 16 waves per workgroup) into spills.
+constexpr int kBwdWaves = BW / 64;
+
+__device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int bwd_wave() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
+// sum_k X(row, k) W(k, col) over k < K (K a multiple of 16) for this lane's row and column;
+// X(r, k) = X[r ldx + k], or X[k ldx + r] when XT; W(k, c) = W[k ldw + c], or W[c ldw + k] when WT
+template <bool XT, bool WT>
+__device__ __forceinline__ f32x4 tile_xw(const float* X, int ldx, int row, const float* W, int ldw, int col, int K,
+                                         int q) {
+  const int kq = K >> 2, kb = q * kq;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+  for (int k = 0; k < kq; k += 4) {
+    float x[4], y[4];
+    if (XT) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = X[(int64_t)(kb + k + e) * ldx + row];
+    } else {
+      const float4 v = *(const float4*)(X + (int64_t)row * ldx + kb + k);
+      x[0] = v.x, x[1] = v.y, x[2] = v.z, x[3] = v.w;
+    }
+    if (WT) {
+      const float4 v = *(const float4*)(W + (int64_t)col * ldw + kb + k);
+      y[0] = v.x, y[1] = v.y, y[2] = v.z, y[3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = W[(int64_t)(kb + k + e) * ldw + col];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_f32x4(x[e], y[e], acc);
+  }
+  return acc;
+}
+
+template <bool XT, bool WT>
+__device__ __attribute__((noinline)) void prod_mfma(float* out, int ldo, int n, int C, int K, const float* X, int ldx,
+                                                    const float* W, int ldw, float s, bool acc, int w0) {
+  const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+  const int ct = C >> 4, tiles = ((n + 15) >> 4) * ct;
+  for (int tile = (bwd_wave() + kBwdWaves - w0) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
+    const int r0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
+    const f32x4 v = tile_xw<XT, WT>(X, ldx, min(r0 + i, n - 1), W, ldw, c0 + i, K, q);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = r0 + 4 * q + rr;
+      if (r < n) {
+        float* o = out + (int64_t)r * ldo + c0 + i;
+        *o = (acc ? *o : 0.0f) + s * v[rr];
+      }
+    }
+  }
+}
+
+// out = (acc ? out : 0) + s X W (see prod_valu): on the matrix cores when C and K are multiples of 16
+template <int RG, bool WT>
+__device__ inline void prod(float* out, int ldo, int n, int C, int K, const float* X, int ldx, const float* W,
+                            int ldw, float s, bool acc, int w0 = 0) {
+  if (C % 16 == 0 && K % 16 == 0)
+    prod_mfma<false, WT>(out, ldo, n, C, K, X, ldx, W, ldw, s, acc, w0);
+  else
+    prod_valu<RG, WT>(out, ldo, n, C, K, X, ldx, W, ldw, s, acc);
+}
+
+// S += s sum_p P_p^T Q_p (see rank_update): tile (k0, c0) takes A[i][q] = P[r][k0 + i] and
+// B[q][i] = Q[r][c0 + i] with r = r4 + q, four rows per instruction (rows past n read as 0);
+// the tile of S is read before the products, so that its latency overlaps theirs.
+// The up to three terms come as scalar arguments (an out-of-line call would otherwise fetch
+// them from private memory at every use); a tile's operands are loaded before its products.
+__device__ __attribute__((noinline)) void rank_update_mfma(float* S, int ldS, int R, int C, int n, int np,
+                                                           const float* P0, int lp0, const float* Q0, int lq0,
+                                                           const float* P1, int lp1, const float* Q1, int lq1,
+                                                           const float* P2, int lp2, const float* Q2, int lq2,
+                                                           float s, int w0) {
+  const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+  const int ct = C >> 4, tiles = (R >> 4) * ct;
+  for (int tile = (bwd_wave() + kBwdWaves - w0) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
+    const int k0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
+    float* srow = S + (int64_t)(k0 + 4 * q) * ldS + c0 + i;
+    float old[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) old[rr] = srow[(int64_t)rr * ldS];
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r16 = 0; r16 < n; r16 += 16) {
+      float a[3][4], bq[3][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r16 + 4 * u + q;
+        const bool ok = r < n;
+        a[0][u] = ok ? P0[r * lp0 + k0 + i] : 0.0f;
+        bq[0][u] = ok ? Q0[r * lq0 + c0 + i] : 0.0f;
+        a[1][u] = ok && np > 1 ? P1[r * lp1 + k0 + i] : 0.0f;
+        bq[1][u] = ok && np > 1 ? Q1[r * lq1 + c0 + i] : 0.0f;
+        a[2][u] = ok && np > 2 ? P2[r * lp2 + k0 + i] : 0.0f;
+        bq[2][u] = ok && np > 2 ? Q2[r * lq2 + c0 + i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v = mfma_f32x4(a[0][u], bq[0][u], v);
+        if (np > 1) v = mfma_f32x4(a[1][u], bq[1][u], v);
+        if (np > 2) v = mfma_f32x4(a[2][u], bq[2][u], v);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) srow[(int64_t)rr * ldS] = old[rr] + s * v[rr];
+  }
+}
+
+__device__ inline void rank_update_any(float* S, int ldS, int R, int C, int n, const Terms& tm, float s,
+                                       int w0 = 0) {
+  if (R % 16 == 0 && C % 16 == 0)
+    rank_update_mfma(S, ldS, R, C, n, tm.np, tm.P[0], tm.ldp[0], tm.Q[0], tm.ldq[0], tm.P[1], tm.ldp[1], tm.Q[1],
+                     tm.ldq[1], tm.P[2], tm.ldp[2], tm.Q[2], tm.ldq[2], s, w0);
+  else
+    rank_update_valu(S, ldS, R, C, n, tm, s);
+}
+
+// tril(s X Y^T) (see rowdot_tril_valu): one tile on wave w0 when n <= 16 and K is a multiple of 16
+__device__ inline void rowdot_tril(float* out, int ldo, int n, int K, const float* X, int ldx, const float* Y,
+                                   int ldy, float s, int w0 = 0) {
+  if (n > 16 || K % 16 != 0) {
+    rowdot_tril_valu(out, ldo, n, K, X, ldx, Y, ldy, s);
+    return;
+  }
+  if (bwd_wave() != w0 % kBwdWaves) return;
+  const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+  const int ci = min(i, n - 1);
+  const f32x4 v = tile_xw<false, true>(X, ldx, ci, Y, ldy, ci, K, q);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = 4 * q + rr;
+    if (r < n && i < n) out[r * ldo + i] = i <= r ? s * v[rr] : 0.0f;
   }
 }
 
@@ -306,12 +454,18 @@ __device__ void state_step(const MB& t, const St& W, int n, int d, int m, float 
 __device__ void readout_hidden(const MB& t, const St& W, int n, int b, int d, int m, float eta, int gelu_tanh,
                                float* dq) {
   rowdot_tril(t.M, b, n, d, t.Q, d, t.K, d, 1.0f);  // M = tril(Q K^T)
-  prod<4, false>(t.Aq, m, n, m, d, t.Q, d, W.w1, W.ld1, 1.0f, false);
+  prod<4, false>(t.Aq, m, n, m, d, t.Q, d, W.w1, W.ld1, 1.0f, false, 1);
   __syncthreads();
+  const bool tiled = n % 16 == 0 && m % 16 == 0;  // M G1 on the matrix cores (M is 0 above its diagonal)
+  if (tiled) {
+    prod_mfma<false, false>(t.Aq, m, n, m, n, t.M, b, t.G1, m, -eta, true, 0);
+    __syncthreads();
+  }
   for (int i = threadIdx.x; i < n * m; i += BW) {
     const int r = i / m, c = i - r * m;
     float corr = 0.0f;
-    for (int k = 0; k <= r; ++k) corr = fmaf(t.M[r * b + k], t.G1[k * m + c], corr);
+    if (!tiled)
+      for (int k = 0; k <= r; ++k) corr = fmaf(t.M[r * b + k], t.G1[k * m + c], corr);
     const float aq = t.Aq[i] - eta * corr;
     float g, dg, ddg;
     gelu3(aq, gelu_tanh, &g, &dg, &ddg);
@@ -450,34 +604,42 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       readout_hidden(t, W, n, b, d, m, eta, a.gelu_tanh, t.dAq);  // dAq holds GELU'(Aq) for now
       // N = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
       rowdot_tril(t.N, b, n, m, t.Hq, m, t.Hk, m, 1.0f);
-      rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta);
-      prod<4, true>(t.dGh, m, n, m, d, t.dZ, d, W.w2, W.ld2, 1.0f, false);
+      rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
+      prod<4, true>(t.dGh, m, n, m, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
       __syncthreads();
       // dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dG2 = -eta N^T dZ; dHk = dN^T Hq
-      for (int i = tid; i < n * m; i += BW) {
-        const int r = i / m, c = i - r * m;
-        float v = t.dGh[i];
-        for (int k = 0; k <= r; ++k) v = fmaf(t.dN[r * b + k], t.Hk[k * m + c], v);
-        t.dAq[i] *= v;
-        float w = 0.0f;
-        for (int k = r; k < n; ++k) w = fmaf(t.dN[k * b + r], t.Hq[k * m + c], w);
-        t.dHk[i] = w;
-      }
-      for (int i = tid; i < n * d; i += BW) {
-        const int r = i / d, c = i - r * d;
-        float v = 0.0f;
-        for (int k = r; k < n; ++k) v = fmaf(t.N[k * b + r], t.dZ[k * d + c], v);
-        t.dG2[i] = -eta * v;
+      if (n % 16 == 0 && m % 16 == 0 && d % 16 == 0) {  // on the matrix cores (N, dN are 0 above the diagonal)
+        prod_mfma<false, false>(t.dGh, m, n, m, n, t.dN, b, t.Hk, m, 1.0f, true, 0);
+        prod_mfma<true, false>(t.dHk, m, n, m, n, t.dN, b, t.Hq, m, 1.0f, false, 0);
+        prod_mfma<true, false>(t.dG2, d, n, d, n, t.N, b, t.dZ, d, -eta, false, 0);
+        __syncthreads();
+        for (int i = tid; i < n * m; i += BW) t.dAq[i] *= t.dGh[i];
+      } else {
+        for (int i = tid; i < n * m; i += BW) {
+          const int r = i / m, c = i - r * m;
+          float v = t.dGh[i];
+          for (int k = 0; k <= r; ++k) v = fmaf(t.dN[r * b + k], t.Hk[k * m + c], v);
+          t.dAq[i] *= v;
+          float w = 0.0f;
+          for (int k = r; k < n; ++k) w = fmaf(t.dN[k * b + r], t.Hq[k * m + c], w);
+          t.dHk[i] = w;
+        }
+        for (int i = tid; i < n * d; i += BW) {
+          const int r = i / d, c = i - r * d;
+          float v = 0.0f;
+          for (int k = r; k < n; ++k) v = fmaf(t.N[k * b + r], t.dZ[k * d + c], v);
+          t.dG2[i] = -eta * v;
+        }
       }
       __syncthreads();
       // dQ = dAq W1^T; dM = tril(-eta dAq G1^T); with the adjoints of the state after this
       // mini-batch: dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK = -eta G1 dW1'^T
       prod<1, true>(t.dQ, d, n, d, m, t.dAq, m, W.w1, W.ld1, 1.0f, false);
-      rowdot_tril(t.dM, b, n, m, t.dAq, m, t.G1, m, -eta);
-      prod<4, true>(t.dHk, m, n, m, d, t.G2, d, dW2, d, -eta, true);
-      prod<1, false>(t.dG2, d, n, d, m, t.Hk, m, dW2, d, -eta, true);
-      prod<4, false>(t.dG1, m, n, m, d, t.K, d, dW1, m, -eta, false);
-      prod<1, true>(t.dK, d, n, d, m, t.G1, m, dW1, m, -eta, false);
+      rowdot_tril(t.dM, b, n, m, t.dAq, m, t.G1, m, -eta, 4);
+      prod<4, true>(t.dHk, m, n, m, d, t.G2, d, dW2, d, -eta, true, 5);
+      prod<1, false>(t.dG2, d, n, d, m, t.Hk, m, dW2, d, -eta, true, 5);
+      prod<4, false>(t.dG1, m, n, m, d, t.K, d, dW1, m, -eta, false, 9);
+      prod<1, true>(t.dK, d, n, d, m, t.G1, m, dW1, m, -eta, false, 9);
       __syncthreads();
       // dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q
       for (int i = tid; i < n * m; i += BW) {
