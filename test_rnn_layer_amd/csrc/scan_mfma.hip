@@ -45,9 +45,9 @@ __device__ __forceinline__ int hk_row(int l) { return l + 8 * (l >> 5); }
 constexpr int DGS = SB + 4;  // 20: rows of the fp32 [hidden][token] GELU' tiles (bank spread of the column writes)
 
 // GELU(a) = a Phi(a) and GELU'(a) = Phi(a) + a phi(a), with Phi from the
-// polynomial of phi_poly.h (|error| <= 6e-5, no reciprocal or exponential: the
+// polynomial of phi_poly.h (|error| <= 1.8e-4, no reciprocal or exponential: the
 // values are rounded to bf16 matrix operands, or multiplied into them, so this
-// is about 1/30 of the operands' own rounding) and the density
+// is about 1/11 of the operands' own rounding) and the density
 // phi(a) = exp(-a^2/2) / sqrt(2 pi) = 2^(-a^2 log2(e) / 2 + log2(1 / sqrt(2 pi))),
 // one exponential with the constant folded into its argument.
 struct Gelu {
