@@ -325,8 +325,8 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time ttt_mlp_bidir_backward instead")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the layer's heads would shard across GPUs, but this build "
-              f"runs on a single MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        print(f"bench.py measures one GPU: the layer's heads would shard across GPUs, and this program "
+              f"times the one GPU's share only; --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

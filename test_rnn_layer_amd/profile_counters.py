@@ -188,11 +188,11 @@ def _traffic_markdown(rec, copy_f, copy_w, dir_f, dir_w):
         f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ/Y, fp32 state; "
         "one `ttt_mlp_bidir` call (each direction runs as chunked launches of the projection and the scan).", "",
         "Commands (repo root, MI355X). The copy, of 1 GiB, comes first in each run:", "",
-        "    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+        f"    rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {dir_f} -o run -- "
         "python3 -m test_rnn_layer_amd.profile_counters run",
-        "    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d gpurun_out/pmc_write -o run -- "
+        f"    rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {dir_w} -o run -- "
         "python3 -m test_rnn_layer_amd.profile_counters run",
-        "    python3 -m test_rnn_layer_amd.profile_counters summarize gpurun_out/pmc_fetch gpurun_out/pmc_write", "",
+        f"    python3 -m test_rnn_layer_amd.profile_counters summarize {dir_f} {dir_w}", "",
         f"**Calibration.** The runtime's copy of 1 GiB read FETCH_SIZE = {copy_f:,.1f} and WRITE_SIZE = "
         f"{copy_w:,.1f} (KiB as reported): bytes = FETCH_SIZE × {COPY_BYTES / copy_f:,.1f} and WRITE_SIZE × "
         f"{COPY_BYTES / copy_w:,.1f}.", "",
@@ -258,10 +258,10 @@ def summarize_sq(dirs, out_md: str | None = None):
         "Commands (repo root, MI355X), one run per counter set:", "",
     ]
     for i, p in enumerate(SQ_PASSES):
-        lines.append(f"    rocprofv3 --pmc {p} --kernel-trace --output-format csv -d gpurun_out/pmc_sq{i + 1} -o run -- "
+        lines.append(f"    rocprofv3 --pmc {p} --kernel-trace --output-format csv -d {dirs[i]} -o run -- "
                      "python3 -m test_rnn_layer_amd.profile_counters run")
     lines += [f"    python3 -m test_rnn_layer_amd.profile_counters summarize-sq " +
-              " ".join(f"gpurun_out/pmc_sq{i + 1}" for i in range(len(SQ_PASSES))), "",
+              " ".join(dirs[:len(SQ_PASSES)]), "",
               f"Kernel resources (kernel trace): scratch {row.get('Scratch_Size')} B per lane, LDS "
               f"{row.get('LDS_Block_Size')} B per workgroup (the build refuses any register spill).", "",
               f"A step takes {step:,.0f} cycles of a wave ({step / clock / 1e3:.2f} µs at the {clock:.2f} GHz that "
