@@ -514,7 +514,7 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
 // forward scan built from the backward's own steps, which leaves a checkpoint
 // of the state every kCkptEvery mini-batches); the backward scan replays one
 // segment at a time from its checkpoint.  The checkpoints of a direction take B*H*ceil(T/b/kCkptEvery)
-// states, the replayed segment B*H*kCkptEvery.
+// states, the replayed segment B*H*kCkptEvery states and forward quantities.
 constexpr int kCkptEvery = 32;
 constexpr size_t kBackwardLdsMax = 160 * 1024;
 
@@ -561,7 +561,7 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   p->dxp_off = bidir ? take(BTD * sizeof(float)) : 0;
   p->ckpt_off[0] = take(BH * nseg * st2);
   p->ckpt_off[1] = bidir ? take(BH * nseg * st2) : 0;
-  p->segst_off = take(BH * kCkptEvery * st2);
+  p->segst_off = take(BH * kCkptEvery * ttt::scan_backward_segment_elems(c->d, c->m, c->b) * sizeof(float));
   p->dstate_off = take(BH * st2);
   p->scratch_off = take(BH * ttt::scan_backward_scratch_elems(c->d, c->m, c->b) * sizeof(float));
   p->dwseq_off = take(BH * st2);

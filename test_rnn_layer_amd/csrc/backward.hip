@@ -9,8 +9,10 @@
 // the start of every C-th mini-batch in the workspace.  The backward scan then
 // walks the segments of C mini-batches from the last to the first: it replays
 // the segment's forward updates from its checkpoint, keeping the state each
-// mini-batch starts from, and walks the segment's mini-batches backwards,
-// carrying the adjoint of the state (dW1, dW2).
+// mini-batch starts from and the forward quantities it computed (A, Hk,
+// GELU'(A), G2, Gh, G1: the backward walk reads them instead of computing them
+// again, for every mini-batch but the segment's last), and walks the segment's
+// mini-batches backwards, carrying the adjoint of the state (dW1, dW2).
 //
 // One mini-batch of n tokens from state (W1, W2) computes (dual form, tril
 // keeps the diagonal, c = 2/d or 2):
@@ -380,6 +382,12 @@ __device__ inline St state_at(float* base, bool padded, int d, int m) {
   return st;
 }
 
+// workspace floats of one replayed mini-batch: its start state (W1, W2), then A, Hk, GELU'(A),
+// Gh, G1 (b x m each) and G2 (b x d)
+__host__ __device__ constexpr int64_t segment_slot_floats(int d, int m, int b) {
+  return 2LL * d * m + 5LL * b * m + (int64_t)b * d;
+}
+
 // workspace floats of one workgroup: the b x m panels, then dQ and dK
 __host__ __device__ constexpr int64_t scratch_floats(int d, int m, int b) {
   return (int64_t)kBwdScratchPanels * b * m + 3LL * b * d;
@@ -483,13 +491,13 @@ struct Rows {
   __device__ int64_t tok(int64_t pos) const { return reverse ? T - 1 - pos : pos; }
 };
 
-// K, V (into G2), Q rows of the mini-batch starting at scan position p0
-__device__ void load_qkv(const MB& t, const Rows& rw, int64_t p0, int n, int d) {
+// K, V (into G2, unless with_v is false), Q rows of the mini-batch starting at scan position p0
+__device__ void load_qkv(const MB& t, const Rows& rw, int64_t p0, int n, int d, bool with_v = true) {
   for (int i = threadIdx.x; i < n * d; i += BW) {
     const int r = i / d, c = i - r * d;
     const int64_t tt = rw.tok(p0 + r);
     t.K[i] = rw.kb[tt * d + c];
-    t.G2[i] = rw.vb[tt * d + c];
+    if (with_v) t.G2[i] = rw.vb[tt * d + c];
     t.Q[i] = rw.qb[tt * d + c];
   }
 }
@@ -563,7 +571,18 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   const St Wc = state_at(wl ? lds : a.wcur + sh * 2 * dm, wl, d, m);
   float* dW1 = a.dstate + sh * 2 * dm;  // adjoint of the state after the current mini-batch
   float* dW2 = dW1 + dm;
-  float* seg = a.segst + sh * (int64_t)C * 2 * dm;
+  // one slot per mini-batch of a segment: its start state, then the forward quantities the
+  // replay computed for it (A, Hk, GELU'(A), Gh, G1, each b x m, and G2, b x d)
+  const int64_t bm = (int64_t)b * m, slot = segment_slot_floats(d, m, b);
+  float* seg = a.segst + sh * (int64_t)C * slot;
+  float* const scratch_A = t.A;  // the workgroup's own b x m panels (the unkept last mini-batch)
+  auto bind_fwd = [&](float* base) {
+    t.A = base;
+    t.Hk = base + bm;
+    t.S1 = base + 2 * bm;
+    t.Gh = base + 3 * bm;
+    t.G1 = base + 4 * bm;
+  };
   for (int64_t i = tid; i < 2 * dm; i += BW) dW1[i] = 0.0f;
 
   const int64_t plane = a.B * a.H * T * d;
@@ -575,12 +594,15 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
     state_in(Wc, a.ckpt + (sh * nseg + sg) * 2 * dm, d, m);
     __syncthreads();
     for (int64_t j = j0; j < j1; ++j) {
-      state_out(seg + (j - j0) * 2 * dm, Wc, d, m);
+      float* sl = seg + (j - j0) * slot;
+      state_out(sl, Wc, d, m);
       if (j + 1 == j1) break;
       const int n = (int)min((int64_t)b, T - j * b);
       load_qkv(t, rw, j * b, n, d);
+      bind_fwd(sl + 2 * dm);
       __syncthreads();
       forward_core(t, Wc, n, d, m, a.gscale, a.gelu_tanh);
+      copy_rows(sl + 2 * dm + 5 * bm, d, t.G2, d, n, d);
       state_step(t, Wc, n, d, m, eta);
       __syncthreads();
     }
@@ -588,19 +610,28 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
     // the segment's mini-batches, last to first
     for (int64_t j = j1 - 1; j >= j0; --j) {
       const int n = (int)min((int64_t)b, T - j * b);
-      St W = state_at(seg + (j - j0) * 2 * dm, false, d, m);
+      float* sl = seg + (j - j0) * slot;
+      St W = state_at(sl, false, d, m);
       if (wl) {
         state_in(Wc, W.w1, d, m);
         W = Wc;
       }
-      load_qkv(t, rw, j * b, n, d);
+      // every mini-batch but the segment's last has its forward quantities from the replay
+      const bool kept = j + 1 < j1;
+      load_qkv(t, rw, j * b, n, d, !kept);
+      if (kept) {
+        bind_fwd(sl + 2 * dm);
+        copy_rows(t.G2, d, sl + 2 * dm + 5 * bm, d, n, d);
+      } else {
+        bind_fwd(scratch_A);
+      }
       for (int i = tid; i < n * d; i += BW) {
         const int r = i / d, c = i - r * d;
         const int ch = h * d + c;
         t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + ch];
       }
       __syncthreads();
-      forward_core(t, W, n, d, m, a.gscale, a.gelu_tanh);
+      if (!kept) forward_core(t, W, n, d, m, a.gscale, a.gelu_tanh);
       readout_hidden(t, W, n, b, d, m, eta, a.gelu_tanh, t.dAq);  // dAq holds GELU'(Aq) for now
       // N = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
       rowdot_tril(t.N, b, n, m, t.Hq, m, t.Hk, m, 1.0f);
@@ -804,6 +835,7 @@ size_t scan_backward_lds_bytes(int d, int m, int b) {
 }
 
 size_t scan_backward_scratch_elems(int d, int m, int b) { return (size_t)scratch_floats(d, m, b); }
+size_t scan_backward_segment_elems(int d, int m, int b) { return (size_t)segment_slot_floats(d, m, b); }
 
 hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s) {
   const size_t lds = scan_backward_lds_bytes(a.d, a.m, a.b);

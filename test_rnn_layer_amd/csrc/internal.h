@@ -96,7 +96,8 @@ struct BwdArgs {
   const float* dy;     // [B, T, D] fp32: gradient of the direction's output Y
   const float* alpha;  // [D] the direction's gate
   const float* ckpt;   // [B, H, nseg, 2 d m]: written by the generic scan
-  float* segst;        // [B, H, ckpt_every, 2 d m] workspace: states of one segment's mini-batches
+  float* segst;        // [B, H, ckpt_every, segment elems] workspace: one segment's start states and
+                       // forward quantities
   float* wcur;         // [B, H, 2 d m] workspace: replayed state
   float* dstate;       // [B, H, 2 d m] workspace: adjoint of the state
   float* scratch;      // workspace, scan_backward_scratch_elems per (sequence, head)
@@ -112,6 +113,9 @@ struct BwdArgs {
 // floats per workgroup (the b x m panels, dQ, dK)
 size_t scan_backward_lds_bytes(int d, int m, int b);
 size_t scan_backward_scratch_elems(int d, int m, int b);
+// workspace floats per (sequence, head) and replayed mini-batch: the start state, then the
+// forward quantities the replay keeps for the backward walk
+size_t scan_backward_segment_elems(int d, int m, int b);
 // The forward pass of one direction with the backward's own steps, writing Z, Y and
 // the checkpoints (ScanArgs: qkv, xin, y, z, alpha, w1_0, w2_0, wstate, ckpt, scratch).
 hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s);
