@@ -520,7 +520,8 @@ constexpr size_t kBackwardLdsMax = 160 * 1024;
 
 struct BwdPlan {
   Plan fwd;  // the forward pass's Q/K/V and state slices (generic layout)
-  size_t dqkv_off, z_off[2], y_off, xp_off, dxp_off, ckpt_off[2], segst_off, dstate_off, scratch_off, dwseq_off,
+  size_t dqkv_off, dqkv2_off, z_off[2], y_off, xp_off, dxp_off, ckpt_off[2], segst_off, dstate_off, scratch_off,
+      dwseq_off,
       dal_off, total;
 };
 
@@ -554,6 +555,9 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   f.wst_bytes = align_up(BH * st2);
   f.wst_off = take(BH * st2);  // the forward scan's state, then the backward's replayed state
   p->dqkv_off = take(3 * BTD * sizeof(float));
+  // the reversed pass's dQ|dK|dV of its own: its dtheta GEMM reads them while the forward pass's
+  // backward scan writes the other buffer
+  p->dqkv2_off = bidir ? take(3 * BTD * sizeof(float)) : 0;
   p->z_off[0] = take(BTD * sizeof(float));
   p->z_off[1] = bidir ? take(BTD * sizeof(float)) : 0;
   p->y_off = take(BTD * io);
@@ -597,13 +601,26 @@ int32_t bwd_forward(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin,
 
 // The backward of one direction whose forward pass (bwd_forward) left its Q/K/V in
 // the workspace: dX = dyin + dQKV theta; dtheta, dW1_0, dW2_0 written or accumulated.
+// One direction's backward: the backward scan (dQ|dK|dV into dqkv), dalpha, dX = dY + dqkv theta,
+// dtheta (+)= dqkv^T X and the initial state's gradient.  skip_theta leaves this direction's dtheta
+// GEMM to the next call; a call with side set runs that deferred GEMM (operands prev_dqkv,
+// prev_x; it writes dtheta) on the side stream, released together with this call's backward scan
+// (ev_ready) and enqueued after it, so that the scan's workgroups take their CUs first and the
+// GEMM fills the rest; this call's own dtheta GEMM then adds to it after ev_done.
+struct ThetaOverlap {
+  bool skip_theta = false;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_ready = nullptr, ev_done = nullptr;
+  const float* prev_dqkv = nullptr;
+  const void* prev_x = nullptr;
+};
+
 int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin, const void* theta,
                       const float* alpha, int reverse, const float* dyin, const float* ckpt, const float* z, float* dX,
                       float* dtheta, float* dW1_0, float* dW2_0, int accumulate, float* dalpha, char* ws,
-                      hipStream_t s) {
+                      hipStream_t s, float* dqkv, const ThetaOverlap& ov = ThetaOverlap()) {
   const int64_t D = (int64_t)c->H * c->d, BT = c->B * c->T;
   const bool bf16 = c->io_dtype == TTT_BF16;
-  float* dqkv = (float*)(ws + bp.dqkv_off);
   float* dw_seq = (float*)(ws + bp.dwseq_off);
   ttt::BwdArgs ba{};
   ba.qkv = (const float*)(ws + bp.fwd.qkv_off);
@@ -627,15 +644,30 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xi
   ba.gscale = c->loss == TTT_LOSS_MEAN ? 2.0f / (float)c->d : 2.0f;
   ba.gelu_tanh = c->gelu == TTT_GELU_TANH;
   ba.reverse = reverse;
-  hipError_t e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] { return ttt::launch_scan_backward(ba, s); });
+  hipError_t e = ov.side ? hipEventRecord(ov.ev_ready, s) : hipSuccess;
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+  e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] { return ttt::launch_scan_backward(ba, s); });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
+  if (ov.side) {
+    e = hipStreamWaitEvent(ov.side, ov.ev_ready, 0);
+    if (e == hipSuccess)
+      e = timed_launch(TTT_KERNEL_GRAD_GEMM, ov.side, [&] {
+        return ttt::launch_gemm_f32(true, bf16, ov.prev_dqkv, 3 * D, ov.prev_x, D, dtheta, D, nullptr, 3 * D, D, BT,
+                                    0, ov.side);
+      });
+    if (e == hipSuccess) e = hipEventRecord(ov.ev_done, ov.side);
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "deferred gradient GEMM launch: %s", hipGetErrorString(e));
+  }
   e = ttt::launch_dalpha(dyin, z, alpha, (float*)(ws + bp.dal_off), dalpha, BT, (int)D, s);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "dalpha launch: %s", hipGetErrorString(e));
   e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
-    hipError_t r = ttt::launch_gemm_f32(false, bf16, dqkv, 3 * D, theta, D, dX, D, dyin, BT, D, 3 * D, 0, s);
-    if (r != hipSuccess) return r;
-    return ttt::launch_gemm_f32(true, bf16, dqkv, 3 * D, xin, D, dtheta, D, nullptr, 3 * D, D, BT, accumulate, s);
+    return ttt::launch_gemm_f32(false, bf16, dqkv, 3 * D, theta, D, dX, D, dyin, BT, D, 3 * D, 0, s);
   });
+  if (e == hipSuccess && ov.side) e = hipStreamWaitEvent(s, ov.ev_done, 0);
+  if (e == hipSuccess && !ov.skip_theta)
+    e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
+      return ttt::launch_gemm_f32(true, bf16, dqkv, 3 * D, xin, D, dtheta, D, nullptr, 3 * D, D, BT, accumulate, s);
+    });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "gradient GEMM launch: %s", hipGetErrorString(e));
   e = ttt::launch_sum_state(dw_seq, dW1_0, dW2_0, c->B, c->H, c->d, c->m, accumulate, s);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "state gradient launch: %s", hipGetErrorString(e));
@@ -850,7 +882,8 @@ int32_t ttt_mlp_backward(const ttt_mlp_config* cfg, const void* X, const void* t
   float* ck = (float*)(ws + bp.ckpt_off[0]);
   st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha, reverse != 0, ws + bp.y_off, z, ck, ws, s);
   if (st != TTT_OK) return st;
-  st = bwd_direction(cfg, bp, X, theta_qkv, alpha, reverse != 0, dY, ck, z, dX, dtheta, dW1_0, dW2_0, 0, dalpha, ws, s);
+  st = bwd_direction(cfg, bp, X, theta_qkv, alpha, reverse != 0, dY, ck, z, dX, dtheta, dW1_0, dW2_0, 0, dalpha, ws, s,
+                     (float*)(ws + bp.dqkv_off));
   return st == TTT_OK ? ok() : st;
 }
 
@@ -891,14 +924,28 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   // the two forward passes, keeping X', Z and the checkpoints
   st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha_f, 0, xp, zf, ckf, ws, s);
   if (st == TTT_OK) st = bwd_forward(cfg, bp, xp, theta_qkv, W1_0, W2_0, alpha_b, 1, ws + bp.y_off, zb, ckb, ws, s);
-  // the reversed pass's backward (its Q/K/V, of X', are in the workspace): dX' = dY + ...
+  // the reversed pass's backward (its Q/K/V, of X', are in the workspace): dX' = dY + ...; its
+  // dtheta GEMM is deferred to the side stream, beside the forward pass's backward scan (which
+  // takes one CU per head), and the forward pass's dtheta GEMM adds to it afterwards
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side* sd = nullptr;
+  hipError_t e = side_for_device(&sd, 2);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+  ThetaOverlap ov_b, ov_f;
+  ov_b.skip_theta = true;
+  ov_f.side = sd->stream;
+  ov_f.ev_ready = sd->events[0];
+  ov_f.ev_done = sd->events[1];
+  ov_f.prev_dqkv = (const float*)(ws + bp.dqkv2_off);
+  ov_f.prev_x = xp;
   if (st == TTT_OK)
     st = bwd_direction(cfg, bp, xp, theta_qkv, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws,
-                       s);
+                       s, (float*)(ws + bp.dqkv2_off), ov_b);
   // the forward pass's backward, with dY = dX' and X's Q/K/V projected again
   if (st == TTT_OK) st = bwd_project(cfg, bp, X, theta_qkv, ws, s);
   if (st == TTT_OK)
-    st = bwd_direction(cfg, bp, X, theta_qkv, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s);
+    st = bwd_direction(cfg, bp, X, theta_qkv, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s,
+                       (float*)(ws + bp.dqkv_off), ov_f);
   return st == TTT_OK ? ok() : st;
 }
 
