@@ -362,7 +362,9 @@ def summarize_backward(d: str, out_md: str | None = None):
         f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ, fp32 arithmetic and "
         f"gradients; {steps} timed + {warm} warm-up calls under the trace.  One call: both forward passes again "
         "(projection, then the scan that keeps a checkpoint every 32 mini-batches), then per direction the "
-        "backward scan, the dalpha reduction and the two gradient GEMMs (dX, dθ).", "",
+        "backward scan, the dalpha reduction and the two gradient GEMMs (dX, dθ); the reversed pass's dθ GEMM "
+        "runs on a second stream beside the forward pass's backward scan, so kernel times overlap and their "
+        "shares are of the summed kernel time.", "",
         "Commands (repo root, MI355X):", "",
         f"    mkdir -p {d} && rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
         f"python3 bench.py --backward{wl_arg} --steps {steps} --warmup {warm} --no-cpu-baseline > {d}/bench.json",
