@@ -31,11 +31,12 @@
 //   dW1 = dW1' + Q^T dAq + K^T dA
 //   dW2 = dW2' + Hq^T dZ + dGh^T G2 + Hk^T (c dG2)
 // and dW1, dW2 are the adjoints handed to the mini-batch before.  fp32
-// throughout; one 1024-thread workgroup per (sequence, head), the b x d and
-// b x b operands in LDS, the b x m ones in a per-workgroup workspace slice,
-// the state and its adjoint in the workspace.  Products with the state give
-// each thread one output column and a few rows, reading operands 16 bytes at
-// a time (d and m multiples of 4).
+// throughout; one 1024-thread workgroup per (sequence, head), the state (when
+// it fits) and the b x d and b x b operands in LDS, the b x m ones in a
+// per-workgroup workspace slice, the adjoint in the workspace.  The products
+// run on the fp32 matrix cores where d, m and the mini-batch tile by 16, on the
+// vector ALU otherwise (one output column and a few rows per thread, operands
+// read 16 bytes at a time; d and m multiples of 4).
 #include "internal.h"
 #include "mfma_common.h"
 
