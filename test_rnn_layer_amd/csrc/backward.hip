@@ -319,13 +319,81 @@ __device__ __attribute__((noinline)) void rank_update_mfma(float* S, int ldS, in
   }
 }
 
+// The same for n <= 16 and NP terms, software-pipelined: a wave loads its next tile's operands
+// and old values while the current tile's products run, so that one tile's load latency is
+// paid per call rather than per tile (NP sizes the register sets: two of 8 NP + 4 floats).
+template <int NP>
+__device__ __attribute__((noinline)) void rank_update_pipe(float* S, int ldS, int R, int C, int n,
+                                                           const float* P0, int lp0, const float* Q0, int lq0,
+                                                           const float* P1, int lp1, const float* Q1, int lq1,
+                                                           const float* P2, int lp2, const float* Q2, int lq2,
+                                                           float s, int w0) {
+  const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+  const int ct = C >> 4, tiles = (R >> 4) * ct;
+  const float* P[3] = {P0, P1, P2};
+  const float* Q[3] = {Q0, Q1, Q2};
+  const int lp[3] = {lp0, lp1, lp2}, lq[3] = {lq0, lq1, lq2};
+  float a[2][NP][4], bq[2][NP][4], old[2][4];
+  auto load = [&](int tile, int set) {
+    const int k0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
+    const float* srow = S + (int64_t)(k0 + 4 * q) * ldS + c0 + i;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) old[set][rr] = srow[(int64_t)rr * ldS];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * u + q;
+        const bool ok = r < n;
+        a[set][p][u] = ok ? P[p][r * lp[p] + k0 + i] : 0.0f;
+        bq[set][p][u] = ok ? Q[p][r * lq[p] + c0 + i] : 0.0f;
+      }
+  };
+  auto finish = [&](int tile, int set) {
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) v = mfma_f32x4(a[set][p][u], bq[set][p][u], v);
+    const int k0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
+    float* srow = S + (int64_t)(k0 + 4 * q) * ldS + c0 + i;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) srow[(int64_t)rr * ldS] = old[set][rr] + s * v[rr];
+  };
+  int tile = (bwd_wave() + kBwdWaves - w0) % kBwdWaves;
+  if (tile >= tiles) return;
+  load(tile, 0);
+  for (;;) {  // two tiles per trip, so that the register sets keep fixed names
+    int next = tile + kBwdWaves;
+    if (next < tiles) load(next, 1);
+    finish(tile, 0);
+    if (next >= tiles) return;
+    tile = next;
+    next = tile + kBwdWaves;
+    if (next < tiles) load(next, 0);
+    finish(tile, 1);
+    if (next >= tiles) return;
+    tile = next;
+  }
+}
+
 __device__ inline void rank_update_any(float* S, int ldS, int R, int C, int n, const Terms& tm, float s,
                                        int w0 = 0) {
-  if (R % 16 == 0 && C % 16 == 0)
+  if (R % 16 != 0 || C % 16 != 0) {
+    rank_update_valu(S, ldS, R, C, n, tm, s);
+  } else if (n > 16) {
     rank_update_mfma(S, ldS, R, C, n, tm.np, tm.P[0], tm.ldp[0], tm.Q[0], tm.ldq[0], tm.P[1], tm.ldp[1], tm.Q[1],
                      tm.ldq[1], tm.P[2], tm.ldp[2], tm.Q[2], tm.ldq[2], s, w0);
-  else
-    rank_update_valu(S, ldS, R, C, n, tm, s);
+  } else if (tm.np == 1) {
+    rank_update_pipe<1>(S, ldS, R, C, n, tm.P[0], tm.ldp[0], tm.Q[0], tm.ldq[0], nullptr, 0, nullptr, 0, nullptr,
+                        0, nullptr, 0, s, w0);
+  } else if (tm.np == 2) {
+    rank_update_pipe<2>(S, ldS, R, C, n, tm.P[0], tm.ldp[0], tm.Q[0], tm.ldq[0], tm.P[1], tm.ldp[1], tm.Q[1],
+                        tm.ldq[1], nullptr, 0, nullptr, 0, s, w0);
+  } else {
+    rank_update_pipe<3>(S, ldS, R, C, n, tm.P[0], tm.ldp[0], tm.Q[0], tm.ldq[0], tm.P[1], tm.ldp[1], tm.Q[1],
+                        tm.ldq[1], tm.P[2], tm.ldp[2], tm.Q[2], tm.ldq[2], s, w0);
+  }
 }
 
 // tril(s X Y^T) (see rowdot_tril_valu): one tile on wave w0 when n <= 16 and K is a multiple of 16
