@@ -36,6 +36,7 @@ constexpr int A_THREADS = 64 * NW;
 constexpr int SROWS = A_THREADS / 8;  // key rows staged per pass (8 threads per 128-byte row)
 constexpr int A_STAGE = AKB * ARS + AD * VRS;  // bf16 elements of one stage: K rows, then V^T rows
 constexpr int SCH = AKB / SROWS;  // 16-byte chunks of K (and of V) each thread stages per block
+static_assert(SCH == 2, "V^T staging pairs two adjacent keys per thread");
 
 __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint16_t* __restrict__ qkv,
                                                                      uint16_t* __restrict__ out, int64_t T, int H,
@@ -68,13 +69,14 @@ __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint
     qf1[u] = *(const bf16x8*)(qrow + 32 + 8 * g);
   }
 
-  // staging: thread t moves SCH 16-byte chunks of K and of V per block (key rows sj + SROWS i)
-  const int sj = tid >> 3, sc = (tid & 7) * 8;  // key row of the block, feature chunk
+  // staging: thread t moves SCH 16-byte chunks of K and of V per block, of the adjacent key rows
+  // SCH sj + i, so that V^T takes their features two keys to a 32-bit LDS write
+  const int sj = tid >> 3, sc = (tid & 7) * 8;  // key-row group of the block, feature chunk
   uint4 kreg[SCH], vreg[SCH];
   auto fetch = [&](int64_t kb) {
 #pragma unroll
     for (int i = 0; i < SCH; ++i) {
-      const int64_t key = std::min(kb * AKB + sj + SROWS * i, n - 1);  // keys past the end load the last key
+      const int64_t key = std::min(kb * AKB + SCH * sj + i, n - 1);  // keys past the end load the last key
       const uint16_t* kr = base + key * row + D + sc;
       kreg[i] = *(const uint4*)kr;
       vreg[i] = *(const uint4*)(kr + D);
@@ -84,11 +86,15 @@ __global__ __launch_bounds__(A_THREADS) void segment_attention_kernel(const uint
     uint16_t* ks = smem + buf * A_STAGE;
     uint16_t* vt = ks + AKB * ARS;
 #pragma unroll
-    for (int i = 0; i < SCH; ++i) {
-      *(uint4*)(ks + (sj + SROWS * i) * ARS + sc) = kreg[i];
-      const uint16_t* v = (const uint16_t*)&vreg[i];
+    for (int i = 0; i < SCH; ++i) *(uint4*)(ks + (SCH * sj + i) * ARS + sc) = kreg[i];
+    // V^T: feature rows, key columns; keys 2 sj and 2 sj + 1 of feature sc + e in one word
+    const uint32_t* v0 = (const uint32_t*)&vreg[0];
+    const uint32_t* v1 = (const uint32_t*)&vreg[1];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(sc + e) * VRS + sj + SROWS * i] = v[e];  // V^T: feature rows, key columns
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t a = v0[e / 2], b = v1[e / 2];  // features sc + e (low half) and sc + e + 1
+      *(uint32_t*)(vt + (sc + e) * VRS + SCH * sj) = (a & 0xffffu) | (b << 16);
+      *(uint32_t*)(vt + (sc + e + 1) * VRS + SCH * sj) = (a >> 16) | (b & 0xffff0000u);
     }
   };
 
