@@ -31,7 +31,7 @@ constexpr int AQ = NW * 16 * QT; // queries per workgroup
 constexpr int AKB = 128;         // keys per block
 constexpr int NT = AKB / 16;     // 16-key tiles per block
 constexpr int ARS = 72;          // LDS row stride of K (bf16): 144-byte rows, conflict-free fragment reads
-constexpr int VRS = AKB + 8;     // LDS row stride of V^T
+constexpr int VRS = AKB + 4;     // LDS row stride of V^T: 8 feature rows apart fall 16 banks apart
 constexpr int A_THREADS = 64 * NW;
 constexpr int SROWS = A_THREADS / 8;  // key rows staged per pass (8 threads per 128-byte row)
 constexpr int A_STAGE = AKB * ARS + AD * VRS;  // bf16 elements of one stage: K rows, then V^T rows
