@@ -197,7 +197,11 @@ int32_t ttt_mlp_backward(const ttt_mlp_config* cfg, const void* X, const void* t
 
 /* The bidirectional layer (as ttt_mlp_bidir: X' is rounded to io_dtype and its
  * rounding is passed through unchanged): dX, dtheta and dW*_0 collect both
- * directions; dalpha_f and dalpha_b are the two gates' gradients. */
+ * directions; dalpha_f and dalpha_b are the two gates' gradients.  The reversed
+ * pass's dtheta GEMM runs on the library's second stream of the device, beside
+ * the forward pass's backward scan, ordered by events after this call's earlier
+ * work on `stream` and before its later work (its dQ|dK|dV get a buffer of their
+ * own in the workspace); calls on one device are serialised while they enqueue. */
 int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv, const float* W1_0,
                                const float* W2_0, const float* alpha_f, const float* alpha_b, const float* dY,
                                float* dX, float* dtheta, float* dW1_0, float* dW2_0, float* dalpha_f,
