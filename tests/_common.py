@@ -64,3 +64,48 @@ def f64_inputs(wl, inp):
     return dict(X=W.to_f64(inp["X"], wl.io_dtype), theta=W.to_f64(inp["theta"], wl.io_dtype),
                 W1_0=inp["W1_0"].astype(np.float64), W2_0=inp["W2_0"].astype(np.float64),
                 alpha_f=inp["alpha_f"].astype(np.float64), alpha_b=inp["alpha_b"].astype(np.float64))
+
+
+def host_f32(t, cols=None):
+    """float32 host copy of a device tensor [B, T, D] (bf16 widened exactly),
+    optionally only the channel columns `cols`."""
+    import torch
+    if cols is not None:
+        t = t[..., torch.as_tensor(cols, device=t.device)]
+    if t.dtype == torch.bfloat16:
+        return W.bf16_bits_to_f32(t.detach().view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.detach().cpu().numpy().astype(np.float32, copy=False)
+
+
+def head_cols(heads, d):
+    """Channel indices of the listed heads, in that order."""
+    return np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads]) if len(heads) else np.zeros(0, int)
+
+
+class TenthsError:
+    """Relative L2 error over the whole sequence and per tenth of it, accumulated
+    over several pieces of the channel axis (sums of squares in float64)."""
+
+    def __init__(self, T):
+        self.T = T
+        self.bounds = [(i * T // 10, (i + 1) * T // 10) for i in range(10)]
+        self.num = np.zeros(10)
+        self.den = np.zeros(10)
+
+    def add(self, got, ref):
+        """got, ref: [B, T, n] (or [T, n]) pieces of the same columns."""
+        got = np.asarray(got)
+        ref = np.asarray(ref)
+        if ref.ndim == 2:
+            got, ref = got[None], ref[None]
+        for i, (a, b) in enumerate(self.bounds):
+            r = ref[:, a:b].astype(np.float64)
+            e = got[:, a:b].astype(np.float64) - r
+            self.num[i] += float(np.sum(e * e))
+            self.den[i] += float(np.sum(r * r))
+
+    def overall(self):
+        return float(np.sqrt(self.num.sum() / max(self.den.sum(), 1e-300)))
+
+    def tenths(self):
+        return [float(np.sqrt(n / max(d, 1e-300))) for n, d in zip(self.num, self.den)]

@@ -184,3 +184,35 @@ def test_backward_full_size_prefix():
                               heads=heads)
     for k in ["dX", "dtheta", "dW1_0", "dW2_0", "dalpha"]:
         _check(k, got[k], ref[k])
+
+
+def test_backward_full_size_reversed_suffix():
+    """The reversed direction at bidir307k's shape: dY on the last 64 tokens of heads 0
+    and 47.  In scan order those are the first 64 positions, so the backward walks every
+    checkpoint segment of the sequence (with a zero adjoint) before it reaches them; the
+    reversed pass over the last 64 tokens alone starts from W_0 at token T-1 and cuts the
+    same mini-batches, so the oracle on that suffix gives every gradient, and dX is exactly
+    zero before it."""
+    from test_rnn_layer_amd import _lib
+    wl = W.WORKLOADS["bidir307k"]
+    P, heads = 64, [0, wl.H - 1]
+    T = wl.T
+    print(f"[backward full size, reversed] {wl.name} T={T}, dY on the last {P} tokens of heads {heads}", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    dy = np.zeros((wl.B, T, wl.D), dtype=np.float32)
+    dy[:, T - P:] = W.make_dy(wl.replace(T=P), heads=heads)
+    g = _lib.backward(_cfg(wl), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"],
+                      torch.from_numpy(dy).cuda(), reverse=True)
+    torch.cuda.synchronize()
+    assert not torch.any(g["dX"][:, :T - P])
+    got = {k: from_device(v[:, T - P:] if k == "dX" else v) for k, v in g.items()}
+    del g, dev
+    torch.cuda.empty_cache()
+    sub = wl.replace(T=P)
+    f64 = f64_inputs(sub, dict(inp, X=inp["X"][:, T - P:]))
+    ref = BO.ttt_mlp_backward(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64["alpha_f"],
+                              dy[:, T - P:].astype(np.float64), eta=wl.eta, b=wl.b, reverse=True, loss=wl.loss,
+                              gelu_form=wl.gelu, heads=heads)
+    for k in ["dX", "dtheta", "dW1_0", "dW2_0", "dalpha"]:
+        _check(k, got[k], ref[k])

@@ -93,6 +93,10 @@ SMALL = {
     "tiny_f32": W.WORKLOADS["tiny_f32"],
     "tiny_f32_b4_ragged": W.WORKLOADS["tiny_f32"].replace(T=103, b=4, name="tiny_f32_b4_ragged"),
     "h3_d64_b16_ragged": W.WORKLOADS["seg14k"].replace(T=200, H=3, name="h3_d64_b16_ragged"),
+    # several scan launches per direction on the MFMA path (chunks of 512 + 512 + 512 + 467 tokens),
+    # so the reversed pass starts launches at positions p0 > 0 and hands its state between them;
+    # 2,003 = 125 mini-batches of 16 and a ragged one of 3
+    "h2_d64_b16_chunks": W.WORKLOADS["seg14k"].replace(T=2003, H=2, name="h2_d64_b16_chunks"),
     "h2_d128_b1": W.WORKLOADS["bigstate307k"].replace(T=96, H=2, name="h2_d128_b1"),
     "d128_b1_f32_tanh_sum": W.WORKLOADS["bigstate307k"].replace(T=33, H=1, io_dtype="f32", gelu="tanh", loss="sum",
                                                                 eta=0.05 / 128, name="d128_b1_f32_tanh_sum"),
@@ -125,7 +129,8 @@ def test_forward_matches_oracle(case, reverse, algo):
 
 
 @pytest.mark.parametrize("algo", ALGOS)
-@pytest.mark.parametrize("case", ["h3_d64_b16_ragged", "h2_d128_b1", "seg_shift_b16", "tiny_f32_b4_ragged"])
+@pytest.mark.parametrize("case", ["h3_d64_b16_ragged", "h2_d64_b16_chunks", "h2_d128_b1", "seg_shift_b16",
+                                  "tiny_f32_b4_ragged"])
 def test_bidir_matches_oracle(case, algo):
     wl = SMALL[case].replace(alpha_f=0.1, alpha_b=0.2)  # distinct gates catch a swap
     _skip_unsupported(wl, algo)
@@ -222,45 +227,9 @@ def test_seg14k_full_config_all_heads():
     got = _gpu_forward(wl, device_inputs(wl, inp), "auto")
     ref = _oracle_forward(wl, f64_inputs(wl, inp))
     _check_forward(wl, got, ref)
-    print("  Z rel-L2 per tenth:", " ".join(f"{e:.1e}" for e in rel_l2_tenths(from_device(got["Z"]), ref["Z"])))
-
-
-@pytest.mark.parametrize("name,prefix", [("bidir100k", 2048), ("bidir307k", 2048), ("bigstate307k", 768)])
-def test_full_size_bidir(name, prefix):
-    """Full-size bidirectional call, in the launch configuration the benchmark times.
-
-    The forward pass is causal, so its outputs on the first `prefix` tokens
-    are checked element by element against the oracle run on those tokens
-    alone (first and last head).  The reversed pass is checked through
-    properties: bidir == forward then reversed forward on its output, bitwise.
-    """
-    from test_rnn_layer_amd import _lib
-    wl = W.WORKLOADS[name]
-    print(f"[config] {name} full size, prefix {prefix}", flush=True)
-    inp = W.make_inputs(wl)
-    dev = device_inputs(wl, inp)
-    cfg = _cfg(wl)
-    r = _lib.bidir(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dev["alpha_b"],
-                   want_z=True)
-    f = _lib.forward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"])
-    torch.cuda.synchronize()
-    assert torch.isfinite(r["Z_b"]).all() and torch.isfinite(r["Y"].float()).all()
-    Zf_pre = from_device(r["Z_f"][:, :prefix])
-    Xp_pre = from_device(f["Y"][:, :prefix])
-    del r["Z_b"]
-    g = _lib.forward(cfg, f["Y"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_b"], reverse=True)
-    torch.cuda.synchronize()
-    assert torch.equal(g["Y"], r["Y"])
-    del dev, r, f, g
-    torch.cuda.empty_cache()
-    sub = wl.replace(T=prefix)
-    f64 = f64_inputs(sub, dict(inp, X=inp["X"][:, :prefix]))
-    heads = [0, wl.H - 1]
-    ref = O.ttt_forward(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64["alpha_f"], eta=wl.eta, b=wl.b,
-                        heads=heads, workers=workers())
-    cols = np.concatenate([np.arange(h * wl.d, (h + 1) * wl.d) for h in heads])
-    _check("Z_f prefix", Zf_pre[:, :, cols], ref["Z"], wl.io_dtype)
-    _check("X' prefix", Xp_pre[:, :, cols], ref["Y"], wl.io_dtype)
+    ten = rel_l2_tenths(from_device(got["Z"]), ref["Z"])
+    print("  Z rel-L2 per tenth:", " ".join(f"{e:.1e}" for e in ten), flush=True)
+    assert max(ten) <= BF16_TOL, ten
 
 
 def test_many_chains_project_then_scan():
