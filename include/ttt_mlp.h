@@ -164,6 +164,30 @@ int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* thet
                       size_t workspace_bytes, void* stream);
 
 /*
+ * ttt_mlp_bidir without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The call's scratch space is a device array of the
+ * library, TTT_STATIC_WORKSPACE_BYTES (320 MiB) on every GPU the library runs
+ * on, held until the process ends; the call allocates nothing and creates no
+ * stream or event after its first call on a device (that first call looks up
+ * the array's device address and creates the side stream and events).  A
+ * configuration whose workspace (ttt_mlp_workspace_size with bidir = 1) exceeds
+ * the array returns TTT_ERR_WORKSPACE before anything is enqueued; it holds,
+ * for instance, 14,400 tokens at 48 heads of width 64 (b = 16, bf16 io).
+ * Kernel timing (ttt_mlp_set_kernel_timing) does not record these calls.
+ * Every call on one GPU uses the same array: calls that overlap on one GPU
+ * (on different streams, or from several threads) race and give wrong results;
+ * serialise them.  No part of the array needs to start at zero, and a call
+ * leaves its contents behind.  Arguments, outputs and errors otherwise as for
+ * ttt_mlp_bidir.
+ */
+#define TTT_STATIC_WORKSPACE_BYTES ((size_t)320 << 20)
+int32_t ttt_mlp_bidir_noalloc(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
+                              const float* W1_0, const float* W2_0, const float* alpha_f,
+                              const float* alpha_b, void* Y, float* Z_f, float* Z_b, float* W1_Tf,
+                              float* W2_Tf, float* W1_Tb, float* W2_Tb, void* stream);
+
+/*
  * The projection step alone (the outer-loop theta_Q/K/V applied to every
  * token), for inspection: QKV [3, B, H, T, d] fp32, QKV[p, s, h, t, :] =
  * (X[s, t, :] theta_p^T)[h*d : (h+1)*d].  Accumulates in fp32.

@@ -24,7 +24,7 @@ TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN, TTT_KERNEL_BACKWARD, TTT_KERNEL_GRAD_GEMM, 
 EXPORTED = [
     "ttt_mlp_version", "ttt_mlp_status_string", "ttt_mlp_last_error", "ttt_mlp_workspace_size",
     "ttt_mlp_select_algo",
-    "ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_project", "ttt_mlp_set_kernel_timing",
+    "ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_bidir_noalloc", "ttt_mlp_project", "ttt_mlp_set_kernel_timing",
     "ttt_mlp_kernel_timing", "ttt_mlp_reset_kernel_timing",
     "ttt_mlp_backward_workspace_size", "ttt_mlp_backward", "ttt_mlp_bidir_backward",
     "ttt_segment_attention", "ttt_hybrid_block_workspace_size", "ttt_hybrid_block",
@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.ttt_mlp_bidir.restype = _i32
         L.ttt_mlp_bidir.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _fp,
                                     _vp, _fp, _fp, _fp, _fp, _fp, _fp, _vp, _sz, _vp]
+        L.ttt_mlp_bidir_noalloc.restype = _i32
+        L.ttt_mlp_bidir_noalloc.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _fp,
+                                            _vp, _fp, _fp, _fp, _fp, _fp, _fp, _vp]
         L.ttt_mlp_project.restype = _i32
         L.ttt_mlp_project.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _vp]
         L.ttt_mlp_set_kernel_timing.restype = _i32
@@ -179,6 +182,19 @@ def bidir(cfg: Config, X, theta, W1_0, W2_0, alpha_f, alpha_b, *, want_z=False, 
     _check(lib().ttt_mlp_bidir(ctypes.byref(cfg), _ptr(X), _ptr(theta), _ptr(W1_0), _ptr(W2_0), _ptr(alpha_f),
                                _ptr(alpha_b), _ptr(Y), _ptr(Zf), _ptr(Zb), _ptr(W1f), _ptr(W2f), _ptr(W1b),
                                _ptr(W2b), _ptr(ws), ws.numel(), _stream(X.device)))
+    return dict(Y=Y, Z_f=Zf, Z_b=Zb, W1_Tf=W1f, W2_Tf=W2f, W1_Tb=W1b, W2_Tb=W2b)
+
+
+def bidir_noalloc(cfg: Config, X, theta, W1_0, W2_0, alpha_f, alpha_b, *, want_z=False, want_state=False, out=None):
+    """ttt_mlp_bidir_noalloc (the library's static workspace).  Returns as bidir()."""
+    import torch
+    Y = torch.empty_like(X) if out is None else out
+    mk = lambda: torch.empty(X.shape, dtype=torch.float32, device=X.device)
+    Zf, Zb = (mk(), mk()) if want_z else (None, None)
+    (W1f, W2f), (W1b, W2b) = (_state_out(cfg, X), _state_out(cfg, X)) if want_state else ((None, None), (None, None))
+    _check(lib().ttt_mlp_bidir_noalloc(ctypes.byref(cfg), _ptr(X), _ptr(theta), _ptr(W1_0), _ptr(W2_0),
+                                       _ptr(alpha_f), _ptr(alpha_b), _ptr(Y), _ptr(Zf), _ptr(Zb), _ptr(W1f),
+                                       _ptr(W2f), _ptr(W1b), _ptr(W2b), _stream(X.device)))
     return dict(Y=Y, Z_f=Zf, Z_b=Zb, W1_Tf=W1f, W2_Tf=W2f, W1_Tb=W1b, W2_Tb=W2b)
 
 

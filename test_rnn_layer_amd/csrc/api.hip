@@ -67,13 +67,17 @@ hipError_t drain_timing_locked() {
   return err;
 }
 
+// Set while ttt_mlp_bidir_noalloc enqueues on this thread: its launches record no
+// timing events (creating them would be an allocation).
+thread_local bool g_untimed = false;
+
 // Launch `fn` on `stream`, bracketed by events when timing is on.
 template <class F>
 hipError_t timed_launch(int kind, hipStream_t stream, F&& fn) {
   bool on;
   {
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    on = g_timing_on;
+    on = g_timing_on && !g_untimed;
   }
   if (!on) return fn();
   TimingRecord r{kind, nullptr, nullptr};
@@ -354,6 +358,11 @@ hipError_t side_for_device(Side** out, size_t n_events) {
   *out = &sd;
   return hipSuccess;
 }
+
+// Chunks per direction never exceed 41 for T < 2^31 (512 tokens, growing by half
+// up to T/12, then T/12 at a time); ttt_mlp_bidir_noalloc creates the events of
+// this many at set-up, so that no later call creates one.
+constexpr int kMaxChunks = 48;
 
 struct Chunking {
   std::vector<int64_t> b;  // chunk k covers positions [b[k], b[k+1]); b[0] = 0, b.back() = T
@@ -726,6 +735,54 @@ hipError_t launch_rowmajor_gemm(const ttt_mlp_config* c, const void* X, const vo
   return timed_launch(TTT_KERNEL_PROJECT, s, [&] { return ttt::launch_project_mfma(pa, 2, s); });
 }
 
+// ---------------------------------------------------------------------------
+// the workspace of ttt_mlp_bidir_noalloc: a device array of the library
+// ---------------------------------------------------------------------------
+// Every GPU the library runs on holds its own copy until the process ends.  It
+// is sized for one 3-second segment of the video model at the layer's shape:
+// 14,400 tokens, 48 heads of width 64, b = 16 on the MFMA path (the projected
+// token blocks, 298.6 MB, and the state handed from one scan launch to the next,
+// 6.3 MB).
+constexpr size_t kStaticWorkspaceBytes = TTT_STATIC_WORKSPACE_BYTES;
+
+std::mutex g_static_mu;
+std::map<int, char*> g_static_ws;  // device -> device address of the array
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+namespace {
+
+// The array's device address on the current device (looked up once per device,
+// with that device current; the host-side name is not a device address), and
+// the side stream and events that the MFMA path may need, created here once so
+// that no later call creates any.
+int32_t static_workspace(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  auto it = g_static_ws.find(dev);
+  if (it != g_static_ws.end()) {
+    *out = it->second;
+    return TTT_OK;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p)
+    return fail(TTT_ERR_HIP, "hipGetSymbolAddress of the static workspace: %s", hipGetErrorString(e));
+  {
+    std::lock_guard<std::mutex> lk2(g_side_mu);
+    Side* sd = nullptr;
+    e = side_for_device(&sd, 2 + 2 * (size_t)kMaxChunks * 2);
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+  }
+  g_static_ws[dev] = (char*)p;
+  *out = (char*)p;
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -841,6 +898,29 @@ int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* thet
   // reversed pass over X' (read from Y, gated output written back in place)
   st = run_direction(cfg, pl, Y, theta_qkv, W1_0, W2_0, alpha_b, 1, Y, Z_b, W1_Tb, W2_Tb, (char*)workspace, s);
   return st == TTT_OK ? ok() : st;
+}
+
+
+int32_t ttt_mlp_bidir_noalloc(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
+                              const float* W1_0, const float* W2_0, const float* alpha_f,
+                              const float* alpha_b, void* Y, float* Z_f, float* Z_b, float* W1_Tf,
+                              float* W2_Tf, float* W1_Tb, float* W2_Tb, void* stream) {
+  Plan pl;
+  int32_t st = make_plan(cfg, &pl);
+  if (st != TTT_OK) return st;
+  if (pl.total > kStaticWorkspaceBytes)
+    return fail(TTT_ERR_WORKSPACE,
+                "the call needs %zu bytes of workspace; the library's static workspace holds %zu (use "
+                "ttt_mlp_bidir with a workspace of its size)",
+                pl.total, kStaticWorkspaceBytes);
+  char* ws = nullptr;
+  st = static_workspace(&ws);
+  if (st != TTT_OK) return st;
+  g_untimed = true;
+  st = ttt_mlp_bidir(cfg, X, theta_qkv, W1_0, W2_0, alpha_f, alpha_b, Y, Z_f, Z_b, W1_Tf, W2_Tf, W1_Tb, W2_Tb, ws,
+                     kStaticWorkspaceBytes, stream);
+  g_untimed = false;
+  return st;
 }
 
 int32_t ttt_mlp_backward_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t* bytes) {

@@ -105,6 +105,23 @@ def test_compute_calls_reject_bad_pointers_on_the_host():
     assert st == L.TTT_ERR_INVALID_ARG
 
 
+def test_noalloc_rejects_a_workspace_beyond_the_static_array_on_the_host():
+    lib = L.lib()
+    fake = 1 << 40  # never dereferenced: the size check comes first
+    limit = 320 << 20
+    # one 3-second segment (14,400 tokens, 48 heads of width 64) fits the array; 20,000 tokens do not
+    assert L.workspace_size(cfg(H=48, T=14_400), True) <= limit
+    big = cfg(H=48, T=20_000)
+    assert L.workspace_size(big, True) > limit
+    st = lib.ttt_mlp_bidir_noalloc(ctypes.byref(big), fake, fake + (1 << 34), fake + (2 << 34), fake + (3 << 34),
+                                   fake + (4 << 34), fake + (5 << 34), fake + (6 << 34), None, None, None, None, None,
+                                   None, None)
+    assert st == L.TTT_ERR_WORKSPACE and b"static workspace" in lib.ttt_mlp_last_error()
+    st = lib.ttt_mlp_bidir_noalloc(ctypes.byref(cfg(b=0)), fake, fake, fake, fake, fake, fake, fake, None, None, None,
+                                   None, None, None, None)
+    assert st == L.TTT_ERR_INVALID_ARG
+
+
 def test_algo_selection():
     assert L.select_algo(cfg()) == "mfma"
     assert L.select_algo(cfg(algo="generic")) == "generic"
