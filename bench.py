@@ -108,8 +108,9 @@ def cpu_baseline(wl, tokens: int):
                     eta=sub.eta, b=sub.b, loss=sub.loss, gelu_form=sub.gelu, workers=nw)
     dt = time.perf_counter() - t0
     return dict(value=tokens / dt, unit="tokens/s", cores=nw, kind="oracle",
-                sample=f"{wl.name} workload, first {tokens} tokens, all {wl.H} heads, both directions, "
-                       f"fp64 NumPy, {dt:.1f} s wall")
+                sample=f"{wl.name} workload, first {tokens} of {wl.T} tokens per sequence "
+                       f"({100.0 * tokens / wl.T:.1f}% of it), all {wl.H} heads, both directions, fp64 NumPy, "
+                       f"{dt:.1f} s wall")
 
 
 def cpu_baseline_backward(wl, tokens: int):
@@ -132,8 +133,9 @@ def cpu_baseline_backward(wl, tokens: int):
                               eta=sub.eta, b=sub.b, loss=sub.loss, gelu_form=sub.gelu)
     dt = time.perf_counter() - t0
     return dict(value=tokens / dt, unit="tokens/s", cores=torch.get_num_threads(), kind="oracle",
-                sample=f"{wl.name} workload, first {tokens} tokens, all {wl.H} heads, both directions, "
-                       f"fp64 torch autograd, {dt:.1f} s wall")
+                sample=f"{wl.name} workload, first {tokens} of {wl.T} tokens per sequence "
+                       f"({100.0 * tokens / wl.T:.3f}% of it), all {wl.H} heads, both directions, fp64 torch "
+                       f"autograd, {dt:.1f} s wall")
 
 
 def bench_backward(args, wl):
@@ -238,8 +240,9 @@ def cpu_baseline_hybrid(wl, tokens: int):
                     workers=nw)
     dt = time.perf_counter() - t0
     return dict(value=tokens / dt, unit="tokens/s", cores=nw, kind="oracle",
-                sample=f"{wl.name} workload, first {tokens} tokens (one segment), all {wl.H} heads, attention and "
-                       f"both TTT directions, fp64 NumPy, {dt:.1f} s wall")
+                sample=f"{wl.name} workload, first {tokens} of {wl.T} tokens per sequence "
+                       f"({100.0 * tokens / wl.T:.1f}% of it, within one attention segment), all {wl.H} heads, "
+                       f"attention and both TTT directions, fp64 NumPy, {dt:.1f} s wall")
 
 
 def bench_hybrid(args, wl):
@@ -407,14 +410,16 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H": wl.H, "d": wl.d, "m": wl.m, "b": wl.b,
                    "eta": wl.eta, "D": wl.D, "directions": dirs, "scan_kernel": kname, "model": wl.model},
-        "roofline": {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma" if used_mfma else "alu", "kernel": kname, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "flops_per_launch": scan_flops_launch, "avg_launch_ms": scan_avg_ms},
         "layer_roofline": {"R_ms": R_ms, "frac": R_ms / ms_per_step,
-                           "definition": "projection flops at bf16 MFMA peak + scan flops at fp32 peak",
-                           "R_exec_ms": R_exec_ms, "frac_exec": R_exec_ms / ms_per_step},
+                           "definition": "projection flops at bf16 MFMA peak + scan flops at fp32 peak"},
         "kernel_ms_per_step": {"scan": scan_ms / args.steps, "projection": proj_ms / args.steps},
     }
+    if used_mfma:  # the scan's contractions run on bf16 operands: the same sum with them at the bf16 peak
+        out["layer_roofline"].update(R_exec_ms=R_exec_ms, frac_exec=R_exec_ms / ms_per_step)
     if not args.no_cpu_baseline:
         print("# bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens or 24576)
