@@ -188,6 +188,21 @@ int32_t ttt_mlp_bidir_noalloc(const ttt_mlp_config* cfg, const void* X, const vo
                               float* W2_Tf, float* W1_Tb, float* W2_Tb, void* stream);
 
 /*
+ * Whether the cooperative scan (TTT_ALGO_COOP) of the last ttt_mlp_forward or
+ * ttt_mlp_bidir call that used `workspace` stopped early: a workgroup waited for
+ * its peers longer than the spin limit, every workgroup of the launch then
+ * stopped, and the outputs they had not written yet hold NaN.  The call waits
+ * for `stream` (the stream of that call), then writes *aborted = 1 (stopped) or
+ * 0.  cfg and bidir are those of that call; for a configuration that runs
+ * another scan nothing is read and *aborted = 0.  The flag lives in the
+ * workspace, is cleared by the first scan launch of each call and is kept
+ * through a bidirectional call's reversed pass, so it covers the whole call
+ * until the workspace is used again.
+ */
+int32_t ttt_mlp_coop_aborted(const ttt_mlp_config* cfg, int32_t bidir, const void* workspace,
+                             size_t workspace_bytes, void* stream, int32_t* aborted);
+
+/*
  * The projection step alone (the outer-loop theta_Q/K/V applied to every
  * token), for inspection: QKV [3, B, H, T, d] fp32, QKV[p, s, h, t, :] =
  * (X[s, t, :] theta_p^T)[h*d : (h+1)*d].  Accumulates in fp32.

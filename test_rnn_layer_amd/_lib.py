@@ -24,7 +24,7 @@ TTT_KERNEL_PROJECT, TTT_KERNEL_SCAN, TTT_KERNEL_BACKWARD, TTT_KERNEL_GRAD_GEMM, 
 EXPORTED = [
     "ttt_mlp_version", "ttt_mlp_status_string", "ttt_mlp_last_error", "ttt_mlp_workspace_size",
     "ttt_mlp_select_algo",
-    "ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_bidir_noalloc", "ttt_mlp_project", "ttt_mlp_set_kernel_timing",
+    "ttt_mlp_forward", "ttt_mlp_bidir", "ttt_mlp_bidir_noalloc", "ttt_mlp_coop_aborted", "ttt_mlp_project", "ttt_mlp_set_kernel_timing",
     "ttt_mlp_kernel_timing", "ttt_mlp_reset_kernel_timing",
     "ttt_mlp_backward_workspace_size", "ttt_mlp_backward", "ttt_mlp_bidir_backward",
     "ttt_segment_attention", "ttt_hybrid_block_workspace_size", "ttt_hybrid_block",
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.ttt_mlp_bidir_noalloc.restype = _i32
         L.ttt_mlp_bidir_noalloc.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _fp, _fp, _fp,
                                             _vp, _fp, _fp, _fp, _fp, _fp, _fp, _vp]
+        L.ttt_mlp_coop_aborted.restype = _i32
+        L.ttt_mlp_coop_aborted.argtypes = [ctypes.POINTER(Config), _i32, _vp, _sz, _vp, ctypes.POINTER(_i32)]
         L.ttt_mlp_project.restype = _i32
         L.ttt_mlp_project.argtypes = [ctypes.POINTER(Config), _vp, _vp, _fp, _vp]
         L.ttt_mlp_set_kernel_timing.restype = _i32
@@ -196,6 +198,17 @@ def bidir_noalloc(cfg: Config, X, theta, W1_0, W2_0, alpha_f, alpha_b, *, want_z
                                        _ptr(alpha_f), _ptr(alpha_b), _ptr(Y), _ptr(Zf), _ptr(Zb), _ptr(W1f),
                                        _ptr(W2f), _ptr(W1b), _ptr(W2b), _stream(X.device)))
     return dict(Y=Y, Z_f=Zf, Z_b=Zb, W1_Tf=W1f, W2_Tf=W2f, W1_Tb=W1b, W2_Tb=W2b)
+
+
+def coop_aborted(cfg: Config, bidir: bool, workspace, device=None) -> bool:
+    """ttt_mlp_coop_aborted: whether the cooperative scan of the last call on
+    `workspace` stopped early (waits for the current stream)."""
+    v = _i32(0)
+    _check(lib().ttt_mlp_coop_aborted(ctypes.byref(cfg), int(bidir), _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(),
+                                      _stream(device if workspace is None else workspace.device),
+                                      ctypes.byref(v)))
+    return bool(v.value)
 
 
 def backward_workspace_size(cfg: Config, bidir: bool) -> int:

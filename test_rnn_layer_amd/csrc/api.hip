@@ -275,6 +275,7 @@ ttt::ScanArgs scan_args(const ttt_mlp_config* c, const Plan& pl, const void* xin
   sa.wstate = (float*)(ws + pl.wst_off);
   sa.xchg = (uint64_t*)(ws + pl.wst_off);
   sa.abort_flag = (uint32_t*)(ws + pl.wst_off + ttt::scan_coop_xchg_bytes(c->B, c->H));
+  sa.clear_abort = 1;
   sa.w1_T = w1T;
   sa.w2_T = w2T;
   sa.B = c->B;
@@ -298,11 +299,12 @@ ttt::ScanArgs scan_args(const ttt_mlp_config* c, const Plan& pl, const void* xin
 // the scan writing y (and z, W_T).
 int32_t run_direction(const ttt_mlp_config* c, const Plan& pl, const void* xin, const void* theta,
                       const float* W1_0, const float* W2_0, const float* alpha, int reverse, void* y,
-                      float* z, float* w1T, float* w2T, char* ws, hipStream_t stream) {
+                      float* z, float* w1T, float* w2T, char* ws, hipStream_t stream, bool first = true) {
   const ttt::ProjArgs pa = proj_args(c, pl, xin, theta, reverse, ws);
   hipError_t e = timed_launch(TTT_KERNEL_PROJECT, stream, [&] { return launch_projection(pa, 0, stream); });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
-  const ttt::ScanArgs sa = scan_args(c, pl, xin, W1_0, W2_0, alpha, reverse, y, z, w1T, w2T, ws);
+  ttt::ScanArgs sa = scan_args(c, pl, xin, W1_0, W2_0, alpha, reverse, y, z, w1T, w2T, ws);
+  sa.clear_abort = first;
   if (pl.algo == TTT_ALGO_COOP && !ttt::scan_coop_fits(c->B, c->H))
     return fail(TTT_ERR_UNSUPPORTED, "cooperative scan: %lld workgroups do not fit on this device at once",
                 (long long)(c->B * c->H * 8));
@@ -896,10 +898,33 @@ int32_t ttt_mlp_bidir(const ttt_mlp_config* cfg, const void* X, const void* thet
   st = run_direction(cfg, pl, X, theta_qkv, W1_0, W2_0, alpha_f, 0, Y, Z_f, W1_Tf, W2_Tf, (char*)workspace, s);
   if (st != TTT_OK) return st;
   // reversed pass over X' (read from Y, gated output written back in place)
-  st = run_direction(cfg, pl, Y, theta_qkv, W1_0, W2_0, alpha_b, 1, Y, Z_b, W1_Tb, W2_Tb, (char*)workspace, s);
+  st = run_direction(cfg, pl, Y, theta_qkv, W1_0, W2_0, alpha_b, 1, Y, Z_b, W1_Tb, W2_Tb, (char*)workspace, s,
+                     false);
   return st == TTT_OK ? ok() : st;
 }
 
+int32_t ttt_mlp_coop_aborted(const ttt_mlp_config* cfg, int32_t bidir, const void* workspace, size_t workspace_bytes,
+                             void* stream, int32_t* aborted) {
+  if (!aborted) return fail(TTT_ERR_INVALID_ARG, "aborted is NULL");
+  if (bidir != 0 && bidir != 1) return fail(TTT_ERR_INVALID_ARG, "bidir must be 0 or 1");
+  Plan pl;
+  int32_t st = make_plan(cfg, &pl);
+  if (st != TTT_OK) return st;
+  if (pl.algo != TTT_ALGO_COOP) {  // only the cooperative scan can stop early
+    *aborted = 0;
+    return ok();
+  }
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                pl.total);
+  const char* flag = (const char*)workspace + pl.wst_off + ttt::scan_coop_xchg_bytes(cfg->B, cfg->H);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, flag, sizeof v, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "reading the abort flag: %s", hipGetErrorString(e));
+  *aborted = v != 0;
+  return ok();
+}
 
 int32_t ttt_mlp_bidir_noalloc(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv,
                               const float* W1_0, const float* W2_0, const float* alpha_f,

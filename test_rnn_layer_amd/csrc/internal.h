@@ -47,6 +47,8 @@ struct ScanArgs {
   float* wstate;         // workspace, [B, H, d*m + m*d] fp32 (generic path)
   uint64_t* xchg;        // cooperative path: exchange slots (see scan_coop)
   uint32_t* abort_flag;  // cooperative path: raised by a workgroup that timed out
+  int32_t clear_abort;   // cooperative path: 1 clears abort_flag before the launch (the first
+                         // launch of a call), 0 keeps it (a bidirectional call's reversed pass)
   float* w1_T;           // [B, H, d, m] or null
   float* w2_T;           // [B, H, m, d] or null
   int64_t B, T;

@@ -420,11 +420,13 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   }
 }
 
-// Marks every exchange entry as not yet written (tag 0xffffffff) and clears the abort flag.
-__global__ void coop_clear_kernel(uint64_t* x, int64_t n, uint32_t* abort_flag) {
+// Marks every exchange entry as not yet written (tag 0xffffffff) and, for the first
+// launch of a call, clears the abort flag (a bidirectional call's reversed pass keeps
+// what its forward pass raised, so the flag reports the whole call).
+__global__ void coop_clear_kernel(uint64_t* x, int64_t n, uint32_t* abort_flag, int clear_abort) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) x[i] = ~(uint64_t)0;
-  if (i == 0) *abort_flag = 0u;
+  if (i == 0 && clear_abort) *abort_flag = 0u;
 }
 
 int64_t coop_grid(int64_t B, int H) { return 8 * NCU * ((B * H + 7) / 8); }
@@ -451,7 +453,8 @@ bool scan_coop_fits(int64_t B, int H) {
 
 hipError_t launch_scan_coop(const ScanArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)(a.B * a.H) * 2 * NCU * NVAL;
-  hipLaunchKernelGGL(coop_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.xchg, n, a.abort_flag);
+  hipLaunchKernelGGL(coop_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.xchg, n, a.abort_flag,
+                     (int)a.clear_abort);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ScanArgs args = a;

@@ -122,6 +122,19 @@ def test_noalloc_rejects_a_workspace_beyond_the_static_array_on_the_host():
     assert st == L.TTT_ERR_INVALID_ARG
 
 
+def test_coop_aborted_query_on_the_host():
+    lib = L.lib()
+    v = ctypes.c_int32(7)
+    # a configuration that runs another scan: nothing is read, the answer is "no"
+    assert lib.ttt_mlp_coop_aborted(ctypes.byref(cfg()), 1, None, 0, None, ctypes.byref(v)) == L.TTT_OK
+    assert v.value == 0
+    big = cfg(d=128, m=512, b=1, eta=0.05, algo="coop")
+    assert lib.ttt_mlp_coop_aborted(ctypes.byref(big), 1, None, 0, None, ctypes.byref(v)) == L.TTT_ERR_WORKSPACE
+    assert lib.ttt_mlp_coop_aborted(ctypes.byref(big), 1, 1 << 40, 1, None, ctypes.byref(v)) == L.TTT_ERR_WORKSPACE
+    assert lib.ttt_mlp_coop_aborted(ctypes.byref(big), 2, None, 0, None, ctypes.byref(v)) == L.TTT_ERR_INVALID_ARG
+    assert lib.ttt_mlp_coop_aborted(ctypes.byref(big), 1, None, 0, None, None) == L.TTT_ERR_INVALID_ARG
+
+
 def test_algo_selection():
     assert L.select_algo(cfg()) == "mfma"
     assert L.select_algo(cfg(algo="generic")) == "generic"

@@ -205,6 +205,10 @@ def test_properties_bitwise(algo):
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([first["Z"], rest["Z"]], 1), a["Z"])
     assert torch.equal(rest["W1_T"], a["W1_T"]) and torch.equal(rest["W2_T"], a["W2_T"])
+    # a call that ran to the end reports that its cooperative scan did not stop early
+    ws = _lib._workspace(cfg, True, dev["X"])
+    _lib.bidir(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dev["alpha_b"], workspace=ws)
+    assert not _lib.coop_aborted(cfg, True, ws)
 
 
 # ----------------------------------------------------------------------------
