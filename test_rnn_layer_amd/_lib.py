@@ -51,6 +51,15 @@ _lib = None
 _vp, _fp, _i32, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 
 
+def use_library(path: str):
+    """Load the library from `path` instead (the phase-marks measurement build);
+    only before the first call that loads it."""
+    global LIB_PATH
+    if _lib is not None and os.path.abspath(path) != LIB_PATH:
+        raise RuntimeError(f"{LIB_PATH} is already loaded")
+    LIB_PATH = os.path.abspath(path)
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library (raises if it has not been built)."""
     global _lib

@@ -43,6 +43,9 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "phase_marks.h"
+
+TTT_MARKS_BUFFER(g_marks_scan_coop);
 
 namespace ttt {
 namespace {
@@ -221,6 +224,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
 
     for (int64_t t = 0; t <= T; ++t) {
       const bool live = t < T;
+      TTT_MARK(g_marks_scan_coop, t, 0);
       // operands loaded now and used later in the iteration: v_t, the gate
       // input of token t-1, and (staged into LDS at the end) k_{t+2}, q_{t+1}
       float v0 = 0.0f, v1 = 0.0f, stage = 0.0f;
@@ -237,6 +241,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       if (writer && t > 0) xo = ld_io_bits(a.xin, ((int64_t)s * T + tok(t - 1)) * D + ch, bf16);
 
       __syncthreads();  // Apart of this iteration is complete
+      TTT_MARK(g_marks_scan_coop, t, 1);
       // ---- unit u = lane: GELU of a_t and of aq_{t-1}
       float hk = 0.0f, dg = 0.0f, hq = 0.0f;
       {
@@ -268,6 +273,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         Ypart[w][3][lane] = z1;
       }
       __syncthreads();
+      TTT_MARK(g_marks_scan_coop, t, 2);
       // ---- stage k_{t+2}, q_{t+1} (loaded at the top of this iteration); their
       //      buffers held k_{t-1}, q_{t-1}, last read in the previous iteration
       if (live) {
@@ -285,6 +291,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         for (int q = 0; q < NW; ++q) p += Ypart[q][w][lane];
         put(a.xchg + slot + cu * NVAL + 64 * w + lane, (uint32_t)t, p);
       }
+      TTT_MARK(g_marks_scan_coop, t, 3);
       // ---- gather, spread over the workgroup: thread tid fetches yhat feature
       //      tid mod 128 from workgroups 4 (tid / 128) .. +3, and (tid < 128) the z
       //      partial of channel tid mod 16 from workgroup tid / 16; the sums follow
@@ -308,10 +315,12 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         }
         failed = !ok;
       }
+      TTT_MARK(g_marks_scan_coop, t, 4);
       if (__syncthreads_or(failed)) {  // every thread of the workgroup leaves together
         fill_nan(t > 0 ? t - 1 : 0);
         return;
       }
+      TTT_MARK(g_marks_scan_coop, t, 5);
       float got[2] = {0.0f, 0.0f};
       if (live) {
 #pragma unroll
@@ -373,6 +382,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         fill_nan(t > 0 ? t - 1 : 0);
         return;
       }
+      TTT_MARK(g_marks_scan_coop, t, 6);
       // ---- W1 pass: update with k_t and G1 of unit lane, then a_{t+1} = k_{t+1} W1_t, aq_t = q_t W1_t
       {
         // (at t = T-1 the k_{t+1} buffer is stale; that a is never used)
@@ -397,6 +407,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         Apart[0][w][lane] = an;
         Apart[1][w][lane] = aq;
       }
+      TTT_MARK(g_marks_scan_coop, t, 7);
     }
     if (__syncthreads_or(failed)) {
       fill_nan(T - 1);
@@ -465,3 +476,5 @@ hipError_t launch_scan_coop(const ScanArgs& a, hipStream_t s) {
 }
 
 }  // namespace ttt
+
+TTT_MARKS_EXPORT(ttt_phase_marks_scan_coop, g_marks_scan_coop);

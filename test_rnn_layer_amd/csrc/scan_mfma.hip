@@ -25,8 +25,11 @@
 // per block.
 #include "internal.h"
 #include "mfma_common.h"
+#include "phase_marks.h"
 #include "phi_poly.h"
 #include "token_block.h"
+
+TTT_MARKS_BUFFER(g_marks_scan_mfma);
 
 namespace ttt {
 namespace {
@@ -267,6 +270,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     const int n = block_n(j);
     const uint16_t* blk = Stage[j & (NSTAGE - 1)];
     const uint16_t* blk_prev = Stage[(j - 1) & (NSTAGE - 1)];
+    TTT_MARK(g_marks_scan_mfma, j, 0);
 
     // ---- bf16 operands of the state that follows block j-1
     bf16x8 w1p[2][2], w2p[4];
@@ -310,7 +314,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       for (int dt = 0; dt < 4; ++dt) Ypart[w][dt][lane] = yp[dt];
     }
 
+    TTT_MARK(g_marks_scan_mfma, j, 1);
     __syncthreads();
+    TTT_MARK(g_marks_scan_mfma, j, 2);
 
     // ---- between the barriers (no vector-memory operation: the second barrier
     //      waits for the wave's outstanding ones):
@@ -328,7 +334,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       G2b[rd_d * TS + rd_t] = (uint16_t)pk;
       G2b[(rd_d + 1) * TS + rd_t] = (uint16_t)(pk >> 16);
     }
+    TTT_MARK(g_marks_scan_mfma, j, 3);
     readout(blk_prev, w1p, w2p);
+    TTT_MARK(g_marks_scan_mfma, j, 4);
     // GELU'(A^T) to this wave's LDS slice as [m][t], read back token-major below
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -354,7 +362,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // gate inputs of block j-1, stores) have had a whole step; the barrier then
     // publishes the next block to every wave before its first use
     vmem_done();
+    TTT_MARK(g_marks_scan_mfma, j, 5);
     __syncthreads();
+    TTT_MARK(g_marks_scan_mfma, j, 6);
 
     // ---- -eta Gh = (-eta G2) W2^T (token-major, contraction over d), -eta G1 =
     //      -eta Gh * GELU'(A): directly the K=16 operand of the W1 update
@@ -412,6 +422,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     g2T_prev[0] = cat8(g2T[0], g2T[1]);
     g2T_prev[1] = cat8(g2T[2], g2T[3]);
     hkB_prev = hkB;
+    TTT_MARK(g_marks_scan_mfma, j, 7);
   }
 
   // ---- read-out of the last block with the final state (after every wave's last
@@ -470,3 +481,5 @@ hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s) {
 }
 
 }  // namespace ttt
+
+TTT_MARKS_EXPORT(ttt_phase_marks_scan_mfma, g_marks_scan_mfma);
