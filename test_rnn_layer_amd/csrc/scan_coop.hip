@@ -137,6 +137,12 @@ __device__ bool poll(const uint64_t* base, int n, const int64_t* e_idx, uint32_t
   return true;
 }
 
+// keep + the value `send` holds in the lane that the DPP control CTRL selects
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float keep, float send) {
+  return keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -349,33 +355,38 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         W2r[i][0] = fmaf(nh, g20, W2r[i][0]);
         W2r[i][1] = fmaf(nh, g21, W2r[i][1]);
       }
-      // ---- sum gp over the 64 lanes (recursive halving): lane ends with unit
-      //      8 b5 + 4 b4 + 2 b3 + b2 of its wave's 16 (b = bits of the lane index)
+      // ---- sum gp over the 64 lanes (recursive halving, in registers): lane ends
+      //      with unit 8 b5 + 4 b4 + 2 b3 + b2 of its wave's 16 (b = bits of the lane
+      //      index).  Each halving pairs every lane with one lane of the other half of
+      //      its group; the lane keeps the units of its half and adds the partner's
+      //      partial of them.  Halves of 32 and 16 lanes trade with the lane swaps
+      //      (lanes 32..63 of the first operand with lanes 0..31 of the second, and
+      //      likewise odd with even rows of 16), halves of 8 and 4 through DPP moves
+      //      (rotate a row by 8; mirror each half-row), pairs and single lanes of a quad
+      //      by quad permutations.
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const bool hi = lane & 32;
-        const float send = hi ? gp[i] : gp[8 + i], keep = hi ? gp[8 + i] : gp[i];
-        gp[i] = keep + __shfl_xor(send, 32);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gp[i]), __float_as_uint(gp[8 + i]), false,
+                                                         false);
+        gp[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool hi = lane & 16;
-        const float send = hi ? gp[i] : gp[4 + i], keep = hi ? gp[4 + i] : gp[i];
-        gp[i] = keep + __shfl_xor(send, 16);
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(gp[i]), __float_as_uint(gp[4 + i]), false,
+                                                         false);
+        gp[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const bool hi = lane & 8;
-        const float send = hi ? gp[i] : gp[2 + i], keep = hi ? gp[2 + i] : gp[i];
-        gp[i] = keep + __shfl_xor(send, 8);
+        gp[i] = dpp_add<0x128>(hi ? gp[2 + i] : gp[i], hi ? gp[i] : gp[2 + i]);  // row_ror:8: lane ^ 8
       }
       {
         const bool hi = lane & 4;
-        const float send = hi ? gp[0] : gp[1], keep = hi ? gp[1] : gp[0];
-        gp[0] = keep + __shfl_xor(send, 4);
+        gp[0] = dpp_add<0x141>(hi ? gp[1] : gp[0], hi ? gp[0] : gp[1]);  // row_half_mirror: lane ^ 7 in 8
       }
-      gp[0] += __shfl_xor(gp[0], 2);
-      gp[0] += __shfl_xor(gp[0], 1);
+      gp[0] = dpp_add<0x4e>(gp[0], gp[0]);  // quad_perm [2,3,0,1]: lane ^ 2
+      gp[0] = dpp_add<0xb1>(gp[0], gp[0]);  // quad_perm [1,0,3,2]: lane ^ 1
       if ((lane & 3) == 0) GH[UW * w + 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) +
                              ((lane >> 2) & 1)] = gp[0];
       if (__syncthreads_or(failed)) {  // every thread of the workgroup leaves together
