@@ -251,7 +251,7 @@ __device__ __attribute__((noinline)) void prod_mfma(float* out, int ldo, int n, 
                                                     const float* W, int ldw, float s, bool acc, int w0) {
   const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
   const int ct = C >> 4, tiles = ((n + 15) >> 4) * ct;
-  for (int tile = (bwd_wave() + kBwdWaves - w0) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
+  for (int tile = (bwd_wave() + kBwdWaves - w0 % kBwdWaves) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
     const int r0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
     const f32x4 v = tile_xw<XT, WT>(X, ldx, min(r0 + i, n - 1), W, ldw, c0 + i, K, q);
 #pragma unroll
@@ -287,7 +287,7 @@ __device__ __attribute__((noinline)) void rank_update_mfma(float* S, int ldS, in
                                                            float s, int w0) {
   const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
   const int ct = C >> 4, tiles = (R >> 4) * ct;
-  for (int tile = (bwd_wave() + kBwdWaves - w0) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
+  for (int tile = (bwd_wave() + kBwdWaves - w0 % kBwdWaves) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
     const int k0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
     float* srow = S + (int64_t)(k0 + 4 * q) * ldS + c0 + i;
     float old[4];
@@ -360,7 +360,7 @@ __device__ __attribute__((noinline)) void rank_update_pipe(float* S, int ldS, in
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) srow[(int64_t)rr * ldS] = old[set][rr] + s * v[rr];
   };
-  int tile = (bwd_wave() + kBwdWaves - w0) % kBwdWaves;
+  int tile = (bwd_wave() + kBwdWaves - w0 % kBwdWaves) % kBwdWaves;
   if (tile >= tiles) return;
   load(tile, 0);
   for (;;) {  // two tiles per trip, so that the register sets keep fixed names
