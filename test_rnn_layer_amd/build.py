@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(PKG, "libttt_mlp.so")
 MARKS_BUILD_DIR = os.path.join(PKG, "_build_marks")
 MARKS_LIB_PATH = os.path.join(PKG, "libttt_mlp_marks.so")
 SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_linear.hip", "scan_coop.hip",
-           "backward.hip", "attention.hip"]
+           "backward.hip", "grad_gemm.hip", "attention.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -136,7 +136,9 @@ def build(verbose: bool = False, phase_marks: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = lib_path + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    # rocBLAS runs the backward's two plain fp32 gradient GEMMs (grad_gemm.hip)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lrocblas",
+          "-Wl,-rpath,/opt/rocm/lib"], verbose)
     shutil.move(tmp, lib_path)
     return lib_path
 

@@ -534,6 +534,9 @@ struct BwdPlan {
   size_t dqkv_off, dqkv2_off, z_off[2], y_off, xp_off, dxp_off, ckpt_off[2], segst_off, dstate_off, scratch_off,
       dwseq_off,
       dal_off, total;
+  // fp32 copies of bf16 operands of the gradient GEMMs (theta, X, X'; unused with fp32 io),
+  // and the two rocBLAS workspace slices (caller's stream, side stream)
+  size_t th32_off, x32_off, xp32_off, blas_off[2];
 };
 
 int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
@@ -581,6 +584,12 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   p->scratch_off = take(BH * ttt::scan_backward_scratch_elems(c->d, c->m, c->b) * sizeof(float));
   p->dwseq_off = take(BH * st2);
   p->dal_off = take(ttt::dalpha_partial_elems((int)D) * sizeof(float));
+  const bool bf16 = c->io_dtype == TTT_BF16;
+  p->th32_off = bf16 ? take(3 * D * D * sizeof(float)) : 0;
+  p->x32_off = bf16 ? take(BTD * sizeof(float)) : 0;
+  p->xp32_off = bf16 && bidir ? take(BTD * sizeof(float)) : 0;
+  p->blas_off[0] = take(ttt::grad_gemm_workspace_bytes());
+  p->blas_off[1] = bidir ? take(ttt::grad_gemm_workspace_bytes()) : 0;
   p->total = off;
   f.total = off;
   return TTT_OK;
@@ -623,15 +632,62 @@ struct ThetaOverlap {
   hipStream_t side = nullptr;
   hipEvent_t ev_ready = nullptr, ev_done = nullptr;
   const float* prev_dqkv = nullptr;
-  const void* prev_x = nullptr;
+  const float* prev_x32 = nullptr;  // fp32 X of the deferred GEMM
 };
 
-int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin, const void* theta,
+// The gradient GEMMs on rocBLAS (fp32 operands: theta32 and x32 are theta and the
+// direction's input, widened when the io dtype is bf16).
+int32_t grad_dx(const BwdPlan& bp, char* ws, int slot, const float* dqkv, const float* theta32, const float* dyin,
+                float* dX, int64_t BT, int64_t D, hipStream_t s) {
+  const char* err = nullptr;
+  hipError_t e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
+    err = ttt::grad_gemm_dx(slot, dqkv, theta32, dyin, dX, BT, D, ws + bp.blas_off[slot],
+                            ttt::grad_gemm_workspace_bytes(), s);
+    return err ? hipErrorUnknown : hipSuccess;
+  });
+  if (err) return fail(TTT_ERR_HIP, "rocBLAS dX GEMM: %s", err);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "dX GEMM timing: %s", hipGetErrorString(e));
+  return TTT_OK;
+}
+
+int32_t grad_dtheta(const BwdPlan& bp, char* ws, int slot, const float* dqkv, const float* x32, float* dtheta,
+                    int64_t BT, int64_t D, int accumulate, hipStream_t s) {
+  if (BT == 0) {  // no tokens: dtheta is zero, or unchanged
+    if (accumulate) return TTT_OK;
+    hipError_t e = ttt::launch_gemm_f32(true, false, nullptr, 3 * D, nullptr, D, dtheta, D, nullptr, 3 * D, D, 0, 0, s);
+    return e == hipSuccess ? TTT_OK : fail(TTT_ERR_HIP, "dtheta clear: %s", hipGetErrorString(e));
+  }
+  const char* err = nullptr;
+  hipError_t e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
+    err = ttt::grad_gemm_dtheta(slot, dqkv, x32, dtheta, BT, D, accumulate, ws + bp.blas_off[slot],
+                                ttt::grad_gemm_workspace_bytes(), s);
+    return err ? hipErrorUnknown : hipSuccess;
+  });
+  if (err) return fail(TTT_ERR_HIP, "rocBLAS dtheta GEMM: %s", err);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "dtheta GEMM timing: %s", hipGetErrorString(e));
+  return TTT_OK;
+}
+
+// fp32 view of an io-dtype buffer of n elements: the buffer itself (fp32 io) or its
+// widened copy at ws + off (bf16 io), written on s.
+int32_t as_f32(const ttt_mlp_config* c, const void* src, int64_t n, char* ws, size_t off, hipStream_t s,
+               const float** out) {
+  if (c->io_dtype != TTT_BF16) {
+    *out = (const float*)src;
+    return TTT_OK;
+  }
+  float* dst = (float*)(ws + off);
+  hipError_t e = ttt::widen_bf16((const uint16_t*)src, dst, n, s);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "widening launch: %s", hipGetErrorString(e));
+  *out = dst;
+  return TTT_OK;
+}
+
+int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* xin32, const float* theta32,
                       const float* alpha, int reverse, const float* dyin, const float* ckpt, const float* z, float* dX,
                       float* dtheta, float* dW1_0, float* dW2_0, int accumulate, float* dalpha, char* ws,
                       hipStream_t s, float* dqkv, const ThetaOverlap& ov = ThetaOverlap()) {
   const int64_t D = (int64_t)c->H * c->d, BT = c->B * c->T;
-  const bool bf16 = c->io_dtype == TTT_BF16;
   float* dw_seq = (float*)(ws + bp.dwseq_off);
   ttt::BwdArgs ba{};
   ba.qkv = (const float*)(ws + bp.fwd.qkv_off);
@@ -659,27 +715,27 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xi
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
   e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] { return ttt::launch_scan_backward(ba, s); });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
+  int32_t st = TTT_OK;
   if (ov.side) {
     e = hipStreamWaitEvent(ov.side, ov.ev_ready, 0);
-    if (e == hipSuccess)
-      e = timed_launch(TTT_KERNEL_GRAD_GEMM, ov.side, [&] {
-        return ttt::launch_gemm_f32(true, bf16, ov.prev_dqkv, 3 * D, ov.prev_x, D, dtheta, D, nullptr, 3 * D, D, BT,
-                                    0, ov.side);
-      });
-    if (e == hipSuccess) e = hipEventRecord(ov.ev_done, ov.side);
-    if (e != hipSuccess) return fail(TTT_ERR_HIP, "deferred gradient GEMM launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream wait: %s", hipGetErrorString(e));
+    st = grad_dtheta(bp, ws, 1, ov.prev_dqkv, ov.prev_x32, dtheta, BT, D, 0, ov.side);
+    if (st != TTT_OK) return st;
+    e = hipEventRecord(ov.ev_done, ov.side);
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream event: %s", hipGetErrorString(e));
   }
   e = ttt::launch_dalpha(dyin, z, alpha, (float*)(ws + bp.dal_off), dalpha, BT, (int)D, s);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "dalpha launch: %s", hipGetErrorString(e));
-  e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
-    return ttt::launch_gemm_f32(false, bf16, dqkv, 3 * D, theta, D, dX, D, dyin, BT, D, 3 * D, 0, s);
-  });
-  if (e == hipSuccess && ov.side) e = hipStreamWaitEvent(s, ov.ev_done, 0);
-  if (e == hipSuccess && !ov.skip_theta)
-    e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
-      return ttt::launch_gemm_f32(true, bf16, dqkv, 3 * D, xin, D, dtheta, D, nullptr, 3 * D, D, BT, accumulate, s);
-    });
-  if (e != hipSuccess) return fail(TTT_ERR_HIP, "gradient GEMM launch: %s", hipGetErrorString(e));
+  st = grad_dx(bp, ws, 0, dqkv, theta32, dyin, dX, BT, D, s);
+  if (st != TTT_OK) return st;
+  if (ov.side) {
+    e = hipStreamWaitEvent(s, ov.ev_done, 0);
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "stream wait: %s", hipGetErrorString(e));
+  }
+  if (!ov.skip_theta) {
+    st = grad_dtheta(bp, ws, 0, dqkv, xin32, dtheta, BT, D, accumulate, s);
+    if (st != TTT_OK) return st;
+  }
   e = ttt::launch_sum_state(dw_seq, dW1_0, dW2_0, c->B, c->H, c->d, c->m, accumulate, s);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "state gradient launch: %s", hipGetErrorString(e));
   return TTT_OK;
@@ -987,7 +1043,12 @@ int32_t ttt_mlp_backward(const ttt_mlp_config* cfg, const void* X, const void* t
   float* ck = (float*)(ws + bp.ckpt_off[0]);
   st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha, reverse != 0, ws + bp.y_off, z, ck, ws, s);
   if (st != TTT_OK) return st;
-  st = bwd_direction(cfg, bp, X, theta_qkv, alpha, reverse != 0, dY, ck, z, dX, dtheta, dW1_0, dW2_0, 0, dalpha, ws, s,
+  const int64_t D_ = (int64_t)cfg->H * cfg->d, BTD_ = cfg->B * cfg->T * D_;
+  const float *th32 = nullptr, *x32 = nullptr;
+  st = as_f32(cfg, theta_qkv, 3 * D_ * D_, ws, bp.th32_off, s, &th32);
+  if (st == TTT_OK) st = as_f32(cfg, X, BTD_, ws, bp.x32_off, s, &x32);
+  if (st != TTT_OK) return st;
+  st = bwd_direction(cfg, bp, x32, th32, alpha, reverse != 0, dY, ck, z, dX, dtheta, dW1_0, dW2_0, 0, dalpha, ws, s,
                      (float*)(ws + bp.dqkv_off));
   return st == TTT_OK ? ok() : st;
 }
@@ -1029,6 +1090,12 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   // the two forward passes, keeping X', Z and the checkpoints
   st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha_f, 0, xp, zf, ckf, ws, s);
   if (st == TTT_OK) st = bwd_forward(cfg, bp, xp, theta_qkv, W1_0, W2_0, alpha_b, 1, ws + bp.y_off, zb, ckb, ws, s);
+  // fp32 operands of the gradient GEMMs: theta, X and X'
+  const int64_t D_ = (int64_t)cfg->H * cfg->d, BTD_ = cfg->B * cfg->T * D_;
+  const float *th32 = nullptr, *x32 = nullptr, *xp32 = nullptr;
+  if (st == TTT_OK) st = as_f32(cfg, theta_qkv, 3 * D_ * D_, ws, bp.th32_off, s, &th32);
+  if (st == TTT_OK) st = as_f32(cfg, X, BTD_, ws, bp.x32_off, s, &x32);
+  if (st == TTT_OK) st = as_f32(cfg, xp, BTD_, ws, bp.xp32_off, s, &xp32);
   // the reversed pass's backward (its Q/K/V, of X', are in the workspace): dX' = dY + ...; its
   // dtheta GEMM is deferred to the side stream, beside the forward pass's backward scan (which
   // takes one CU per head), and the forward pass's dtheta GEMM adds to it afterwards
@@ -1042,14 +1109,14 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   ov_f.ev_ready = sd->events[0];
   ov_f.ev_done = sd->events[1];
   ov_f.prev_dqkv = (const float*)(ws + bp.dqkv2_off);
-  ov_f.prev_x = xp;
+  ov_f.prev_x32 = xp32;
   if (st == TTT_OK)
-    st = bwd_direction(cfg, bp, xp, theta_qkv, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws,
+    st = bwd_direction(cfg, bp, xp32, th32, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws,
                        s, (float*)(ws + bp.dqkv2_off), ov_b);
   // the forward pass's backward, with dY = dX' and X's Q/K/V projected again
   if (st == TTT_OK) st = bwd_project(cfg, bp, X, theta_qkv, ws, s);
   if (st == TTT_OK)
-    st = bwd_direction(cfg, bp, X, theta_qkv, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s,
+    st = bwd_direction(cfg, bp, x32, th32, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s,
                        (float*)(ws + bp.dqkv_off), ov_f);
   return st == TTT_OK ? ok() : st;
 }

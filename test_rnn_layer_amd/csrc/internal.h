@@ -127,6 +127,16 @@ hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32(bool a_transposed, bool b_bf16, const float* A, int64_t lda, const void* Bm, int64_t ldb,
                            float* C, int64_t ldc, const float* Cadd, int64_t M, int64_t N, int64_t K, int accumulate,
                            hipStream_t s);
+// The same two gradient GEMMs on rocBLAS (grad_gemm.hip): dX [BT, D] = dY + dQKV [BT, 3D] theta
+// [3D, D], and dtheta [3D, D] (+)= dQKV^T X [BT, D], all fp32 row-major.  slot 0: the caller's
+// stream, 1: the side stream; ws: a workspace slice of grad_gemm_workspace_bytes() for that slot.
+// Return NULL or rocBLAS's description of its error.
+size_t grad_gemm_workspace_bytes();
+hipError_t widen_bf16(const uint16_t* in, float* out, int64_t n, hipStream_t s);
+const char* grad_gemm_dx(int slot, const float* dqkv, const float* theta32, const float* dy, float* dx, int64_t BT,
+                         int64_t D, void* ws, size_t ws_bytes, hipStream_t s);
+const char* grad_gemm_dtheta(int slot, const float* dqkv, const float* x32, float* dtheta, int64_t BT, int64_t D,
+                             int accumulate, void* ws, size_t ws_bytes, hipStream_t s);
 // dalpha[c] = (1 - tanh(alpha[c])^2) sum_r dy[r, c] z[r, c]; part: dalpha_partial_elems(D) floats
 size_t dalpha_partial_elems(int D);
 hipError_t launch_dalpha(const float* dy, const float* z, const float* alpha, float* part, float* dalpha,
