@@ -61,9 +61,10 @@ KERNELS = {"scan_mfma": "scan_mfma_kernel", "scan_generic": "scan_generic_kernel
            "scan_linear_mfma": "scan_linear_mfma_kernel", "scan_linear_generic": "scan_linear_generic_kernel",
            "projection": "proj_tiles_kernel"}
 # the sources each kernel is built from: its counters are stale once any of them changes
-KERNEL_SOURCES = {"scan_mfma": ["scan_mfma.hip", "token_block.h", "mfma_common.h", "phi_poly.h", "internal.h"],
+KERNEL_SOURCES = {"scan_mfma": ["scan_mfma.hip", "token_block.h", "mfma_common.h", "phi_poly.h", "phase_marks.h",
+                                "internal.h"],
                   "scan_generic": ["generic.hip", "internal.h"],
-                  "scan_coop": ["scan_coop.hip", "internal.h"],
+                  "scan_coop": ["scan_coop.hip", "phase_marks.h", "internal.h"],
                   "scan_linear_mfma": ["scan_linear.hip", "token_block.h", "mfma_common.h", "internal.h"],
                   "scan_linear_generic": ["generic.hip", "internal.h"],
                   "scan_backward": ["backward.hip", "internal.h"],
@@ -329,12 +330,19 @@ def summarize_stats(d: str, out_md: str | None = None):
                 "its projections run before the TTT layer (it needs their output); inside the TTT layer the "
                 "projection runs on a second stream beside the scan.")
         out_default = os.path.join(ROOT, "profiles", f"segment_attention_{wname}_stats.md")
-    else:
+    elif bench["config"]["scan_kernel"].endswith("mfma"):
         what = (f"the scan's launches averaged {rf['avg_launch_ms']:.3f} ms from HIP events on their stream, "
                 f"{rf['flops_per_launch'] / 1e9:.1f} GFLOP each, {rf['achieved']:.1f} TFLOP/s. The projection runs "
                 "on a second stream beside the scan; the call's time is that of the longer stream plus what cannot "
                 "overlap (the first projection chunk of each direction, the last scan chunk).")
         out_default = os.path.join(ROOT, "profiles", f"{bench['config']['scan_kernel']}_proj_tiles_{wname}_stats.md")
+    else:
+        lines[0] = (f"# Kernel time, {wname} (one ttt_mlp_bidir call = both directions, each a projection of the "
+                    "whole sequence, then one scan launch)")
+        what = (f"the scan's launches averaged {rf['avg_launch_ms']:.3f} ms from HIP events on their stream, "
+                f"{rf['flops_per_launch'] / 1e12:.2f} TFLOP each, {rf['achieved']:.2f} TFLOP/s. Each direction "
+                "projects all its tokens, then scans them.")
+        out_default = os.path.join(ROOT, "profiles", f"{bench['config']['scan_kernel']}_{wname}_stats.md")
     lines += ["", f"The bench line of the same run: {bench['ms_per_step']:.2f} ms per call "
               f"({bench['value'] / 1e6:.3f} M tokens/s, {100 * bench['layer_roofline']['frac']:.1f}% of the "
               f"roofline R = {bench['layer_roofline']['R_ms']:.2f} ms); " + what,
