@@ -14,8 +14,8 @@
 // and, with working registers, its VGPR file.  The state is split by hidden
 // unit over NCU = 8 workgroups (one per CU), 64 units each, held entirely in
 // VGPRs:
-//   W1 slice (128 x 64): lane u of wave w holds W1[32w .. 32w+31][u];
-//   W2 slice (64 x 128): lane l of wave w holds W2[16w .. 16w+15][l, l+64].
+//   W1 slice (128 x 64): lane u of wave w (of 8) holds W1[16w .. 16w+15][u];
+//   W2 slice (64 x 128): lane l of wave w holds W2[8w .. 8w+7][l, l+64].
 // Per token every workgroup holds the full q, k, v of its head.  a = k W1 and
 // aq = q W1 are local to a unit, so only the contractions over hidden units,
 // yhat = GELU(a) W2 and z = GELU(aq) W2, need partial sums from all NCU
@@ -62,13 +62,13 @@ constexpr int CD = 128;               // head width d
 constexpr int CM = 512;               // hidden width m
 constexpr int NCU = 8;                // cooperating workgroups per head
 constexpr int UNITS = CM / NCU;       // hidden units per workgroup
-constexpr int NW = 4;                 // waves per workgroup
+constexpr int NW = 8;                 // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;           // threads per workgroup
 constexpr int PW = CD / NW;           // rows of W1 per wave
 constexpr int UW = UNITS / NW;        // units of W2 per wave
 constexpr int NVAL = 2 * CD;          // exchanged values per workgroup and token: yhat, z partials
 constexpr uint32_t SPIN_MAX = 1u << 20;
-static_assert(UNITS == 64 && UW == 16 && PW == 32 && CD == 128, "lane mapping assumes these sizes");
+static_assert(UNITS == 64 && UW == 8 && PW == 16 && CD == 128 && NT == 4 * CD, "lane mapping assumes these sizes");
 
 __device__ __forceinline__ float gelu_val(float a, bool tanh_form) {
   if (tanh_form) {
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
     if (tid < CD) {
       Ks[0][tid] = kb[tok(0) * CD + tid];
       Qs[0][tid] = qb[tok(0) * CD + tid];
-    } else if (T > 1) {
+    } else if (tid < 2 * CD && T > 1) {
       Ks[1][tid - CD] = kb[tok(1) * CD + tid - CD];
     }
     __syncthreads();
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         // valid values are written to LDS): divergent loads into one register
         // would make the second wait for the first
         const int64_t tk = t + 2 < T ? t + 2 : T - 1, tq = t + 1 < T ? t + 1 : T - 1;
-        stage = tid < CD ? kb[tok(tk) * CD + tid] : qb[tok(tq) * CD + tid - CD];
+        if (tid < 2 * CD) stage = tid < CD ? kb[tok(tk) * CD + tid] : qb[tok(tq) * CD + tid - CD];
       }
       if (writer && t > 0) xo = ld_io_bits(a.xin, ((int64_t)s * T + tok(t - 1)) * D + ch, bf16);
 
@@ -331,13 +331,13 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       if (live) {
         if (tid < CD) {
           if (t + 2 < T) Ks[(t + 2) & 3][tid] = stage;
-        } else if (t + 1 < T) {
+        } else if (tid < 2 * CD && t + 1 < T) {
           Qs[(t + 1) & 1][tid - CD] = stage;
         }
       }
-      // ---- publish this workgroup's partial of value 64 w + lane (w < 2: yhat, else z)
+      // ---- publish this workgroup's partial of value 64 w + lane (waves 0, 1: yhat; 2, 3: z)
       const int64_t slot = xslots + (t & 1) * NCU * NVAL;
-      {
+      if (w < 4) {
         float p = 0.0f;
 #pragma unroll
         for (int q = 0; q < NW; ++q) p += Ypart[q][w][lane];
@@ -381,20 +381,20 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         }
       }
       // ---- gather, spread over the workgroup: thread tid fetches yhat feature
-      //      tid mod 128 from workgroups 4 (tid / 128) .. +3, and (tid < 128) the z
-      //      partial of channel tid mod 16 from workgroup tid / 16; the sums follow
-      //      through LDS in a fixed order
+      //      tid mod 128 from workgroups 2 (tid / 128) and 2 (tid / 128) + 1, and
+      //      (tid < 128) the z partial of channel tid mod 16 from workgroup tid / 16;
+      //      the sums follow through LDS in a fixed order
       {
-        int64_t e_idx[4];
+        int64_t e_idx[4] = {0, 0, 0, 0};
         float vals[4];
         int n = 0;
         if (live) {
-          for (int i = 0; i < 4; ++i) e_idx[i] = slot + (4 * (tid >> 7) + i) * NVAL + (tid & 127);
-          n = 4;
+          for (int i = 0; i < 2; ++i) e_idx[i] = slot + (2 * (tid >> 7) + i) * NVAL + (tid & 127);
+          n = 2;
         }
         bool ok = !failed && poll(a.xchg, n, e_idx, (uint32_t)t, a.abort_flag, vals);
         if (ok && live)
-          for (int i = 0; i < 4; ++i) Xv[4 * (tid >> 7) + i][tid & 127] = vals[i];
+          for (int i = 0; i < 2; ++i) Xv[2 * (tid >> 7) + i][tid & 127] = vals[i];
         if (ok && t > 0 && tid < 16 * NCU) {
           const int64_t ze = slot + (tid >> 4) * NVAL + CD + 16 * cu + (tid & 15);
           float zv;
@@ -438,39 +438,33 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         W2r[i][1] = fmaf(nh, g21, W2r[i][1]);
       }
       // ---- sum gp over the 64 lanes (recursive halving, in registers): lane ends
-      //      with unit 8 b5 + 4 b4 + 2 b3 + b2 of its wave's 16 (b = bits of the lane
-      //      index).  Each halving pairs every lane with one lane of the other half of
-      //      its group; the lane keeps the units of its half and adds the partner's
-      //      partial of them.  Halves of 32 and 16 lanes trade with the lane swaps
-      //      (lanes 32..63 of the first operand with lanes 0..31 of the second, and
-      //      likewise odd with even rows of 16), halves of 8 and 4 through DPP moves
-      //      (rotate a row by 8; mirror each half-row), pairs and single lanes of a quad
-      //      by quad permutations.
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gp[i]), __float_as_uint(gp[8 + i]), false,
-                                                         false);
-        gp[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      }
+      //      with unit 4 b5 + 2 b4 + b3 of its wave's 8 (b = bits of the lane index).
+      //      Each halving pairs every lane with one lane of the other half of its group;
+      //      the lane keeps the units of its half and adds the partner's partial of
+      //      them.  Halves of 32 and 16 lanes trade with the lane swaps (lanes 32..63 of
+      //      the first operand with lanes 0..31 of the second, and likewise odd with even
+      //      rows of 16), halves of 8 through a DPP row rotation; the 8 lanes that then
+      //      hold one unit sum it with the half-row mirror and quad permutations.
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(gp[i]), __float_as_uint(gp[4 + i]), false,
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gp[i]), __float_as_uint(gp[4 + i]), false,
                                                          false);
         gp[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const bool hi = lane & 8;
-        gp[i] = dpp_add<0x128>(hi ? gp[2 + i] : gp[i], hi ? gp[i] : gp[2 + i]);  // row_ror:8: lane ^ 8
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(gp[i]), __float_as_uint(gp[2 + i]), false,
+                                                         false);
+        gp[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
       {
-        const bool hi = lane & 4;
-        gp[0] = dpp_add<0x141>(hi ? gp[1] : gp[0], hi ? gp[0] : gp[1]);  // row_half_mirror: lane ^ 7 in 8
+        const bool hi = lane & 8;
+        gp[0] = dpp_add<0x128>(hi ? gp[1] : gp[0], hi ? gp[0] : gp[1]);  // row_ror:8: lane ^ 8
       }
-      gp[0] = dpp_add<0x4e>(gp[0], gp[0]);  // quad_perm [2,3,0,1]: lane ^ 2
-      gp[0] = dpp_add<0xb1>(gp[0], gp[0]);  // quad_perm [1,0,3,2]: lane ^ 1
-      if ((lane & 3) == 0) GH[UW * w + 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) +
-                             ((lane >> 2) & 1)] = gp[0];
+      gp[0] = dpp_add<0x141>(gp[0], gp[0]);  // row_half_mirror: lane ^ 7 in 8
+      gp[0] = dpp_add<0x4e>(gp[0], gp[0]);   // quad_perm [2,3,0,1]: lane ^ 2
+      gp[0] = dpp_add<0xb1>(gp[0], gp[0]);   // quad_perm [1,0,3,2]: lane ^ 1
+      if ((lane & 7) == 0) GH[UW * w + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1)] = gp[0];
       if (__syncthreads_or(failed)) {  // every thread of the workgroup leaves together
         fill_nan(t > 0 ? t - 1 : 0);
         return;
