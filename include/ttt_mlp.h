@@ -88,7 +88,8 @@ extern "C" {
 #define TTT_GELU_TANH 1 /* 0.5 a (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))) */
 
 /* scan kernel selection */
-#define TTT_ALGO_AUTO 0    /* fastest kernel that supports the shape and dtype */
+#define TTT_ALGO_AUTO 0    /* fastest kernel that supports the shape and dtype (the cooperative
+                              scan only where its workgroups fit co-resident on the device) */
 #define TTT_ALGO_GENERIC 1 /* fp32 VALU scan, any supported shape */
 #define TTT_ALGO_MFMA 2    /* bf16-operand MFMA scan, fp32 state: bf16 io, erf GELU,
                               d = 64, m = 256, b = 16, T < 2^31; for TTT_MODEL_LINEAR

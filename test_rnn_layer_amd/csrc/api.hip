@@ -163,6 +163,17 @@ bool coop_possible(const ttt_mlp_config* c) {
   return !is_linear(c) && ttt::scan_coop_supported(c->d, c->m, c->b, c->T);
 }
 
+// Whether the cooperative scan's 8 B H workgroups fit co-resident on the current
+// device; with no device (planning on a host without a GPU) the plan assumes they do.
+bool coop_fits_here(const ttt_mlp_config* c) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n == 0) {
+    (void)hipGetLastError();  // a failed query leaves no error behind for the next call
+    return true;
+  }
+  return ttt::scan_coop_fits(c->B, c->H);
+}
+
 size_t generic_lds_bytes(const ttt_mlp_config* c) {
   return is_linear(c) ? ttt::scan_linear_generic_lds_bytes(c->d, c->b) : ttt::scan_generic_lds_bytes(c->d, c->m, c->b);
 }
@@ -175,11 +186,16 @@ int32_t make_plan(const ttt_mlp_config* c, Plan* p) {
   if (st != TTT_OK) return st;
   int algo = c->algo;
   if (algo == TTT_ALGO_AUTO)
-    algo = mfma_possible(c) ? TTT_ALGO_MFMA : coop_possible(c) ? TTT_ALGO_COOP : TTT_ALGO_GENERIC;
+    algo = mfma_possible(c)                         ? TTT_ALGO_MFMA
+           : coop_possible(c) && coop_fits_here(c) ? TTT_ALGO_COOP
+                                                   : TTT_ALGO_GENERIC;
   if (algo == TTT_ALGO_COOP && !coop_possible(c))
     return fail(TTT_ERR_UNSUPPORTED,
                 "the cooperative scan needs the MLP model, d=128, m=512, b=1, T < 2^31 (got d=%d m=%d b=%d)", c->d,
                 c->m, c->b);
+  if (algo == TTT_ALGO_COOP && !coop_fits_here(c))
+    return fail(TTT_ERR_UNSUPPORTED, "cooperative scan: %lld workgroups do not fit on this device at once",
+                (long long)(c->B * c->H * 8));
   if (algo == TTT_ALGO_MFMA && !mfma_possible(c))
     return fail(TTT_ERR_UNSUPPORTED,
                 is_linear(c) ? "the linear MFMA scan needs bf16 io, d=m=64, b=16 (got d=%d m=%d b=%d io=%d)"

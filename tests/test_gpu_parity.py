@@ -103,6 +103,8 @@ SMALL = {
     "d128_b1_f32": W.WORKLOADS["bigstate307k"].replace(T=50, H=2, io_dtype="f32", name="d128_b1_f32"),
     "d128_b1_two_sequences": W.WORKLOADS["bigstate307k"].replace(B=2, T=40, H=3, name="d128_b1_two_sequences"),
     "d128_b1_one_token": W.WORKLOADS["bigstate307k"].replace(T=1, H=2, name="d128_b1_one_token"),
+    # 5 x 8 heads need 320 cooperating workgroups, more than fit at once: AUTO takes the generic scan
+    "d128_b1_many_chains": W.WORKLOADS["bigstate307k"].replace(B=5, T=20, H=8, name="d128_b1_many_chains"),
     "seg_shift_b16": W.WORKLOADS["bidir307k"].replace(T=512, H=2, seg_len=160, name="seg_shift_b16"),
     "sum_loss_tanh": W.WORKLOADS["seg14k"].replace(T=77, H=2, loss="sum", eta=0.1 / 16 / 64, gelu="tanh",
                                                    name="sum_loss_tanh"),
@@ -149,6 +151,17 @@ def test_bidir_matches_oracle(case, algo):
 
 # the shape each kernel's property tests run on
 PROP_CASE = {"generic": "h3_d64_b16_ragged", "mfma": "h3_d64_b16_ragged", "coop": "h2_d128_b1"}
+
+
+def test_auto_leaves_the_cooperative_scan_when_it_does_not_fit():
+    from test_rnn_layer_amd import _lib
+    wl = SMALL["d128_b1_many_chains"]
+    assert _lib.select_algo(_cfg(wl)) == "generic"
+    assert _lib.select_algo(_cfg(wl.replace(B=1, H=2))) == "coop"
+    print("[auto] d=128 b=1: 5 x 8 heads on the generic scan, 1 x 2 on the cooperative one", flush=True)
+    inp = W.make_inputs(wl)
+    got = _gpu_forward(wl, device_inputs(wl, inp), "auto")
+    _check_forward(wl, got, _oracle_forward(wl, f64_inputs(wl, inp)))
 
 
 @pytest.mark.parametrize("algo", ALGOS)
