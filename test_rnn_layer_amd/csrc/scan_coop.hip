@@ -116,7 +116,9 @@ __device__ __forceinline__ void st_io(void* p, int64_t i, float v, bool bf16) {
 // workgroup-scope invalidate; plain stores with polls that invalidate the L1 at
 // device scope before plain loads are correct between workgroups of one XCD and
 // faster for a single polling thread, but with every thread of the workgroup
-// polling the invalidates cost 14,400 cycles per token against 3,000.)
+// polling the invalidates cost 14,400 cycles per token against 3,000.  Loads with
+// the workgroup-scope bit alone are served from L1 as well, stale also between
+// workgroups of one XCD.)
 __device__ __forceinline__ void put(uint64_t* e, uint32_t tag, float v) {
   __hip_atomic_store(e, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
