@@ -221,7 +221,10 @@ int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* th
  *   dalpha [D] fp32.
  * dY is [B, T, D] fp32.  Every output is overwritten.  The call runs the
  * forward pass again (projection and scan, keeping a checkpoint of the state
- * every 32 mini-batches in the workspace), then the backward scan, which
+ * every 32 mini-batches in the workspace; with algo AUTO at d = 64, m = 256,
+ * b = 16 and the erf GELU that scan runs on the fp32 matrix cores with the
+ * state in registers, otherwise, and with algo GENERIC, with the backward's own
+ * steps: both fp32, in different summation orders), then the backward scan, which
  * replays one segment of 32 mini-batches at a time from its checkpoint and
  * walks it backwards carrying the gradient of the state, then two GEMMs:
  * dX = dY + [dQ dK dV] theta and dtheta = [dQ dK dV]^T X.

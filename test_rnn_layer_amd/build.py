@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(PKG, "libttt_mlp.so")
 MARKS_BUILD_DIR = os.path.join(PKG, "_build_marks")
 MARKS_LIB_PATH = os.path.join(PKG, "libttt_mlp_marks.so")
 SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_linear.hip", "scan_coop.hip",
-           "backward.hip", "grad_gemm.hip", "attention.hip"]
+           "backward.hip", "scan_fwd_f32.hip", "grad_gemm.hip", "attention.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,12 +38,13 @@ FLAGS = [
 
 
 # kernels that must keep their whole working set in registers: the MFMA and
-# cooperative scans hold the inner-model state in VGPRs for the whole
-# sequence (and the linear scan counts its vector-memory instructions per
+# cooperative scans and the backward's fp32 matrix-core forward pass hold the
+# inner-model state in VGPRs for the whole sequence (and the linear scan counts
+# its vector-memory instructions per
 # step), and the projection GEMM's accumulators and operands fill the register
 # file (a spill there cost a fifth of its speed), so a spilling build of any of
 # them is refused.
-NO_SPILL_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "scan_coop.hip", "proj_mfma.hip"}
+NO_SPILL_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "scan_coop.hip", "proj_mfma.hip", "scan_fwd_f32.hip"}
 
 
 def _check_no_spill(src, remarks):
@@ -59,7 +60,7 @@ def _check_no_spill(src, remarks):
 # instructions later gave wrong values on gfx950 (the compiler inserts no wait
 # for it).  The build compiles these sources to assembly as well and refuses any
 # product whose accumulator comes from a product of another instruction.
-MFMA_CHAIN_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "proj_mfma.hip", "attention.hip"}
+MFMA_CHAIN_SOURCES = {"scan_mfma.hip", "scan_linear.hip", "proj_mfma.hip", "attention.hip", "scan_fwd_f32.hip"}
 _MFMA = re.compile(r"\s*(v_mfma\w*)\s+v\[(\d+):(\d+)\],\s*[^,]+,\s*[^,]+,\s*(?:v\[(\d+):(\d+)\]|\S+)")
 _VDST = re.compile(r"\s*(?:v_|ds_read|global_load|buffer_load|scratch_load|flat_load)\S*\s+(?:v(\d+)|v\[(\d+):(\d+)\])")
 

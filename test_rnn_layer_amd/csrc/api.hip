@@ -630,7 +630,12 @@ int32_t bwd_forward(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin,
   sa.ckpt = ckpt;
   sa.ckpt_every = kCkptEvery;
   sa.scratch = (float*)(ws + bp.scratch_off);
-  hipError_t e = timed_launch(TTT_KERNEL_SCAN, s, [&] { return ttt::launch_scan_fwd_ckpt(sa, s); });
+  // AUTO: the fp32 matrix-core forward pass with the state in registers where it applies
+  const bool f32mfma = c->algo == TTT_ALGO_AUTO && ttt::scan_fwd_f32_supported(c->d, c->m, c->b) &&
+                       c->gelu != TTT_GELU_TANH;
+  hipError_t e = timed_launch(TTT_KERNEL_SCAN, s, [&] {
+    return f32mfma ? ttt::launch_scan_fwd_f32(sa, s) : ttt::launch_scan_fwd_ckpt(sa, s);
+  });
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   return TTT_OK;
 }

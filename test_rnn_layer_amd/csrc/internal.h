@@ -121,6 +121,10 @@ size_t scan_backward_segment_elems(int d, int m, int b);
 // The forward pass of one direction with the backward's own steps, writing Z, Y and
 // the checkpoints (ScanArgs: qkv, xin, y, z, alpha, w1_0, w2_0, wstate, ckpt, scratch).
 hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s);
+// The same forward pass on the fp32 matrix cores with the state in registers (d = 64, m = 256,
+// b = 16, erf GELU; ScanArgs: qkv, xin, y, z, alpha, w1_0, w2_0, ckpt, ckpt_every).
+bool scan_fwd_f32_supported(int d, int m, int b);
+hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
 // C = (accumulate ? C : Cadd or 0) + A B, fp32 (A [M, K] row-major, or [K, M] when
 // a_transposed; B [K, N] row-major, fp32 or bf16)

@@ -1,0 +1,376 @@
+// Forward pass of one direction for the backward, on the fp32 matrix cores:
+// head width d = 64, hidden m = 256, mini-batch b = 16, erf GELU ("One-Minute
+// Video Generation with Test-Time Training", paper-notes page, key designs
+// "TTT-MLP layer" and "gate + bidirectional"; the training section learns the
+// outer parameters through the layer, so the backward needs this pass's Z, Y
+// and the state every C mini-batches).  The same outputs as the generic
+// forward with checkpoints (backward.hip), fp32 throughout: fp32 operands,
+// products and sums (v_mfma_f32_16x16x4_f32), in another order.
+//
+// One 512-thread workgroup per (sequence, head); wave w owns hidden units
+// [32w, 32w + 32): its slices of W1 (64 x 32), W2 (32 x 64) and W2 once more as
+// its transpose W2T (the operand of the contraction over d) stay in registers
+// in the matrix-core D layout for the whole sequence.  A D-layout tile X
+// (lane (g, c) = (lane / 16, lane % 16) holds X[4g + r][c] in register r) is
+// directly the operand of four K=4 products over its row index: register r
+// covers rows {r, 4 + r, 8 + r, 12 + r}, lane group g row 4g + r, and the other
+// operand lists the contraction index in the same order.  Step j (the
+// mini-batch dual form of generic.hip, c = 2/d or 2, N* = -eta *):
+//   A^T = W1^T K^T, Hk^T = GELU(A^T), S1^T = GELU'(A^T)        (local)
+//   Yhat^T = W2^T Hk^T         partial over the wave's units -> LDS, summed
+//   NG2 = -eta c (Yhat - V)    each thread two values -> LDS
+//   NGh = NG2 W2^T, NG1 = NGh * S1 (token-major: S1 and Hk transposed in LDS)
+//   W1 += K^T NG1, W2 += Hk^T NG2, W2T += NG2^T Hk
+// and, with the state that follows block j-1 (which holds the updates of all its
+// tokens), block j-1's read-out, taking back the updates of the tokens after each
+// one (striu keeps the entries [t][t'] with t' > t):
+//   Aq^T = W1^T Q^T - NG1^T striu(Q K^T)^T, Hq^T = GELU(Aq^T)
+//   Z^T  = W2^T Hq^T - NG2^T striu(Hq Hk^T)^T               partial -> LDS, summed
+// with y = x + tanh(alpha) z.  A last, short block is padded with zero tokens,
+// which add exact zeros to every sum.  Two workgroup barriers per step.
+#include "internal.h"
+#include "mfma_common.h"
+#include "token_block.h"
+
+namespace ttt {
+namespace {
+
+constexpr int FD = 64;           // head width
+constexpr int FM = 256;          // hidden width
+constexpr int FB = 16;           // mini-batch
+constexpr int FW = 8;            // waves; wave w owns hidden units [32 w, 32 w + 32)
+constexpr int FT = 64 * FW;      // threads
+constexpr int NSTG = 3;          // staged token blocks: j-1 (read-out), j, j+1 in flight
+constexpr int RW = FD + 4;       // 68: row stride of the staged panels and of the NG2 panel
+constexpr int GS = RW;
+constexpr int PAN = FB * RW;     // floats of one staged 16 x 64 panel (Q, K or V), rows padded
+constexpr int BLKF = 3 * PAN;    // floats of a staged block: Q, then K, then V
+constexpr int BLK_CH = BLKF / 4; // 816 chunks of 16 bytes, 17 per row (the last one padding)
+constexpr int TT = FB + 4;       // 20: row stride of the per-wave transposed tiles
+constexpr int OQ = 0, OK = PAN, OV = 2 * PAN;
+
+// Staged panels have rows of 68 floats (17 chunks of 16 bytes): the 16-byte reads of
+// one chunk column over rows 0..7 and the 4-byte reads of 16 columns of rows 4g + r
+// (g = 0, 1) fall on distinct banks, and every offset is affine in the row and column.
+__device__ __forceinline__ int sw(int r, int col) { return r * RW + col; }
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// GELU and GELU' (erf form) as the generic steps compute them.
+__device__ __forceinline__ void gelu2(float a, float* g, float* dg) {
+  const float cdf = 0.5f * (1.0f + erff(a * 0.7071067811865476f));
+  *g = a * cdf;
+  *dg = cdf + a * (0.3989422804014327f * expf(-0.5f * a * a));
+}
+__device__ __forceinline__ float gelu1(float a) { return a * (0.5f * (1.0f + erff(a * 0.7071067811865476f))); }
+
+__device__ float4 g_zero_chunk;  // zero-initialised, never written: the source of padding rows
+
+__global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_fwd_f32_kernel(ScanArgs a) {
+  __shared__ __attribute__((aligned(16))) float Stage[NSTG][BLKF];  // token blocks j-1 .. j+1
+  __shared__ f32x4 Ypart[FW][4][64];                              // partial Yhat^T: wave, d-tile, lane
+  __shared__ f32x4 Zpart[FW][4][64];                              // partial Z^T
+  __shared__ __attribute__((aligned(16))) float G2s[2][FB * GS];   // NG2 [token][feature], by block parity
+  // per-wave transposes: Hk^T and S1^T tiles as [unit][token], read back token-major
+  __shared__ __attribute__((aligned(16))) float HkS[FW][2][16 * TT];
+  __shared__ __attribute__((aligned(16))) float DgS[FW][2][16 * TT];
+  __shared__ float2 Tg[FT];  // this thread's two gate factors tanh(alpha), read once per step
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int64_t T = a.T;
+  const int D = a.H * FD;
+  const int u0 = 32 * w;
+  const int64_t sh = (int64_t)s * a.H + h;
+  const int64_t dm = (int64_t)FD * FM;
+  const float ngs = -a.eta * a.gscale;
+  const int64_t nblk = (T + FB - 1) / FB;
+  const int C = a.ckpt_every;
+  const int64_t nseg = (nblk + C - 1) / C;
+
+  f32x4 W1[4][2], W2[2][4], W2T[4][2];
+  {
+    const float* w1 = a.w1_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * dm;
+    const float* w2 = a.w2_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * dm;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int ut = 0; ut < 2; ++ut) {
+          W1[dt][ut][r] = w1[(16 * dt + 4 * g + r) * FM + u0 + 16 * ut + c];
+          W2[ut][dt][r] = w2[(u0 + 16 * ut + 4 * g + r) * FD + 16 * dt + c];
+          W2T[dt][ut][r] = w2[(u0 + 16 * ut + c) * FD + 16 * dt + 4 * g + r];
+        }
+  }
+
+  // the two values this thread finishes between the barriers (Yhat, then Z of the
+  // block before): d-tile rd_dt, source lane rd_src of each wave's partial tile,
+  // registers 2 rd_p and 2 rd_p + 1, i.e. token row rd_t, features rd_d, rd_d + 1
+  const int rd_dt = w >> 1;
+  const int rd_src = 32 * (w & 1) + (lane >> 1);
+  const int rd_p = lane & 1;
+  const int rd_t = rd_src & 15;
+  const int rd_d = 16 * rd_dt + 4 * (rd_src >> 4) + 2 * rd_p;
+  const int ch0 = h * FD + rd_d;
+  Tg[tid] = make_float2(tanhf(a.alpha[ch0]), tanhf(a.alpha[ch0 + 1]));
+  auto reduce_part = [&](const f32x4 (&part)[FW][4][64]) -> float2 {
+    float2 v[FW];
+#pragma unroll
+    for (int q = 0; q < FW; ++q) v[q] = *((const float2*)&part[q][rd_dt][rd_src] + rd_p);
+    float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int q = 0; q < FW; ++q) {
+      acc.x += v[q].x;
+      acc.y += v[q].y;
+    }
+    return acc;
+  };
+  auto tok = [&](int64_t p) -> int64_t { return a.reverse ? T - 1 - p : p; };
+
+  // token block jb into stage buf: chunk i (thread i, and i + 512 for the first 304
+  // threads) is chunk q of row r of panel i / 272 (a wave fills 1 KB of consecutive
+  // LDS); the padding chunk of each row and rows past the sequence come from the
+  // zero chunk
+  const int64_t plane = a.B * a.H * T * FD;
+  const float* qkv_h = a.qkv + sh * T * FD;
+  auto stage_async = [&](int64_t jb, int buf) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + FT * k;
+      if (k == 1 && 64 * w >= BLK_CH - FT) break;  // whole waves past the block
+      const int pnl = i / (FB * 17), pc = i - pnl * (FB * 17), r = pc / 17, q = pc - 17 * r;
+      const int64_t p = jb * FB + r;
+      const bool real = i < BLK_CH && q < 16 && p < T;
+      const void* src = real ? (const void*)(qkv_h + pnl * plane + tok(p) * FD + 4 * q) : (const void*)&g_zero_chunk;
+      if (i < BLK_CH) tb::dma16(src, tb::lds_addr_uniform(Stage[buf], 16u * (uint32_t)(FT * k + 64 * w)));
+    }
+  };
+
+  // carried from block j-1 to its read-out during step j
+  f32x4 St_prev = zero4();                 // S^T = K Q^T of block j-1: [t'][t]
+  f32x4 g1_prev[2] = {zero4(), zero4()};   // NG1 of block j-1, token-major [t][u]
+  f32x4 hkT_prev[2] = {zero4(), zero4()};  // Hk^T of block j-1: [u][t]
+
+  // -striu of a D-layout [t'][t] tile: the entries with t' = 4g + r > t = c, negated
+  bool later[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) later[r] = 4 * g + r > c;
+
+  // Read-out of the block staged at `prev` with the current state (the one that
+  // follows that block); this wave's partial Z^T goes to Zpart[w].
+  auto readout = [&](const float* prev, const float* g2prev) {
+    f32x4 aq[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const f32x4 qf = *(const f32x4*)&prev[OQ + sw(c, 16 * dt + 4 * g)];
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) aq[ut] = mfma4(W1[dt][ut][r], qf[r], aq[ut]);
+    }
+    f32x4 hqT[2];
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) aq[ut] = mfma4(g1_prev[ut][r], later[r] ? -St_prev[r] : 0.0f, aq[ut]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hqT[ut][r] = gelu1(aq[ut][r]);
+    }
+    f32x4 pt = zero4();  // this wave's part of (Hq Hk^T)^T: [t'][t]
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pt = mfma4(hkT_prev[ut][r], hqT[ut][r], pt);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x4 zp = zero4();
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zp = mfma4(W2[ut][dt][r], hqT[ut][r], zp);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) zp = mfma4(g2prev[(4 * g + r) * GS + 16 * dt + c], later[r] ? -pt[r] : 0.0f, zp);
+      Zpart[w][dt][lane] = zp;
+    }
+  };
+  // z and y = x + tanh(alpha) z of this thread's two values of block jb
+  auto store_z = [&](int64_t jb, float2 z) {
+    const int64_t p = jb * FB + rd_t;
+    if (jb < 0 || p >= T) return;
+    const int64_t o = ((int64_t)s * T + tok(p)) * D + ch0;
+    *(float2*)(a.z + o) = z;
+    const float2 tg = Tg[tid];
+    float x0, x1;
+    if (a.bf16) {
+      const uint32_t xv = *(const uint32_t*)((const uint16_t*)a.xin + o);
+      x0 = __uint_as_float(xv << 16);
+      x1 = __uint_as_float(xv & 0xffff0000u);
+      *(uint32_t*)((uint16_t*)a.y + o) = pack2(fmaf(tg.x, z.x, x0), fmaf(tg.y, z.y, x1));
+    } else {
+      const float2 xv = *(const float2*)((const float*)a.xin + o);
+      *(float2*)((float*)a.y + o) = make_float2(fmaf(tg.x, z.x, xv.x), fmaf(tg.y, z.y, xv.y));
+    }
+  };
+
+  for (int64_t jb = 0; jb < NSTG - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
+  // G2s of the block before block 0 is read by the read-out at j = 0 (whose result is
+  // never stored): keep it finite
+  for (int i = tid; i < FB * GS; i += FT) G2s[1][i] = 0.0f;
+  int sj = 0;  // stage of block j; block j-1 sits in stage (sj + 2) mod 3
+  vmem_done();
+  __syncthreads();
+
+  for (int64_t j = 0; j < nblk; ++j) {
+    const int sp = sj == 0 ? NSTG - 1 : sj - 1;
+    const float* blk = Stage[sj];
+    const float* blk_prev = Stage[sp];
+    float* g2cur = G2s[j & 1];
+    const float* g2prev = G2s[(j & 1) ^ 1];
+
+    // ---- checkpoint: the state at the start of block j, W1 [d][m] then W2 [m][d]
+    if (j % C == 0) {
+      float* o = a.ckpt + (sh * nseg + j / C) * 2 * dm;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            o[(16 * dt + 4 * g + r) * FM + u0 + 16 * ut + c] = W1[dt][ut][r];
+            o[dm + (u0 + 16 * ut + 4 * g + r) * FD + 16 * dt + c] = W2[ut][dt][r];
+          }
+    }
+
+    // ---- A^T = W1^T K^T (this wave's units), S^T = K Q^T
+    f32x4 At[2] = {zero4(), zero4()}, St = zero4();
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const f32x4 kf = *(const f32x4*)&blk[OK + sw(c, 16 * dt + 4 * g)];
+      const f32x4 qf = *(const f32x4*)&blk[OQ + sw(c, 16 * dt + 4 * g)];
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) At[ut] = mfma4(W1[dt][ut][r], kf[r], At[ut]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) St = mfma4(kf[r], qf[r], St);
+    }
+    // ---- Hk^T = GELU(A^T), S1^T = GELU'(A^T) (both also to this wave's LDS slices
+    //      for the token-major reads); partial Yhat^T over this wave's units
+    f32x4 hkT[2];
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float hv, dv;
+        gelu2(At[ut][r], &hv, &dv);
+        hkT[ut][r] = hv;
+        HkS[w][ut][(4 * g + r) * TT + c] = hv;
+        DgS[w][ut][(4 * g + r) * TT + c] = dv;
+      }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x4 yp = zero4();
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yp = mfma4(W2[ut][dt][r], hkT[ut][r], yp);
+      Ypart[w][dt][lane] = yp;
+    }
+
+    __syncthreads();
+
+    // ---- NG2 = -eta c (Yhat - V): this thread's two values
+    {
+      const float2 y = reduce_part(Ypart);
+      const float2 v = *(const float2*)&blk[OV + sw(rd_t, rd_d)];
+      *(float2*)&g2cur[rd_t * GS + rd_d] = make_float2(ngs * (y.x - v.x), ngs * (y.y - v.y));
+    }
+    // ---- read-out of block j-1 (at j = 0 on zero operands, never stored)
+    readout(blk_prev, g2prev);
+    // ---- this wave's token-major Hk and S1: [t = 4g + r][u = c]
+    f32x4 hkF[2], s1F[2];
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut) {
+      hkF[ut] = *(const f32x4*)&HkS[w][ut][c * TT + 4 * g];
+      s1F[ut] = *(const f32x4*)&DgS[w][ut][c * TT + 4 * g];
+    }
+    // block j+1's loads (issued in the previous step) are complete before the barrier
+    // that publishes them
+    vmem_done();
+    __syncthreads();
+
+    // ---- NGh = NG2 W2^T (token-major), NG1 = NGh * S1
+    f32x4 g1[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const f32x4 gA = *(const f32x4*)&g2cur[c * GS + 16 * dt + 4 * g];
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) g1[ut] = mfma4(gA[r], W2T[dt][ut][r], g1[ut]);
+    }
+    g1[0] = g1[0] * s1F[0];
+    g1[1] = g1[1] * s1F[1];
+    // ---- state update: W1 += K^T NG1, W2 += Hk^T NG2, W2T += NG2^T Hk (contraction over
+    //      the 16 tokens: register r of a token-major tile is tokens 4g + r)
+    f32x4 g2c[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x4 kc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kc[r] = blk[OK + sw(4 * g + r, 16 * dt + c)];
+        g2c[dt][r] = g2cur[(4 * g + r) * GS + 16 * dt + c];
+      }
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) W1[dt][ut] = mfma4(kc[r], g1[ut][r], W1[dt][ut]);
+    }
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          W2[ut][dt] = mfma4(hkF[ut][r], g2c[dt][r], W2[ut][dt]);
+          W2T[dt][ut] = mfma4(g2c[dt][r], hkF[ut][r], W2T[dt][ut]);
+        }
+
+    // ---- Z of block j-1 and its gate; block j+2 into the stage that held block j-1
+    store_z(j - 1, reduce_part(Zpart));
+    if (j + NSTG - 1 < nblk) stage_async(j + NSTG - 1, sp);
+
+    St_prev = St;
+    g1_prev[0] = g1[0];
+    g1_prev[1] = g1[1];
+    hkT_prev[0] = hkT[0];
+    hkT_prev[1] = hkT[1];
+    sj = sj == NSTG - 1 ? 0 : sj + 1;
+  }
+
+  // ---- read-out of the last block with the final state (after every wave's last
+  //      reads of Zpart)
+  if (nblk > 0) {
+    __syncthreads();
+    readout(Stage[sj == 0 ? NSTG - 1 : sj - 1], G2s[(nblk - 1) & 1]);
+    __syncthreads();
+    store_z(nblk - 1, reduce_part(Zpart));
+  }
+}
+
+}  // namespace
+
+bool scan_fwd_f32_supported(int d, int m, int b) { return d == FD && m == FM && b == FB; }
+
+hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s) {
+  if (a.gelu_tanh || !scan_fwd_f32_supported(a.d, a.m, a.b) || a.ckpt_every <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scan_fwd_f32_kernel, dim3((unsigned)(a.B * a.H)), dim3(FT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

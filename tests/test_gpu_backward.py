@@ -30,8 +30,13 @@ CASES = {
     # the sum loss and the tanh GELU
     "f32_sum_tanh": _F32.replace(T=37, H=2, d=8, m=16, b=3, eta=0.02, loss="sum", gelu="tanh",
                                  name="f32_sum_tanh"),
-    # the bidir307k head shape (bf16 X and theta), two heads, ragged tail
+    # the bidir307k head shape (bf16 X and theta), two heads, ragged tail: with algo AUTO the
+    # forward pass runs on the fp32 matrix cores (state in registers), with GENERIC on the
+    # backward's own steps
     "bf16_d64": W.WORKLOADS["bidir307k"].replace(T=72, H=2, seg_len=0, name="bf16_d64"),
+    "bf16_d64_generic": W.WORKLOADS["bidir307k"].replace(T=72, H=2, seg_len=0, name="bf16_d64_generic"),
+    # the same shape over three checkpoint segments of 32 mini-batches and a 12-token tail
+    "bf16_d64_segments": W.WORKLOADS["bidir307k"].replace(T=1100, H=2, seg_len=0, name="bf16_d64_segments"),
     # the bigstate307k head shape: a state too large for LDS stays in the workspace
     "bf16_d128_b1": W.WORKLOADS["bigstate307k"].replace(T=24, H=1, seg_len=0, name="bf16_d128_b1"),
 }
@@ -49,7 +54,7 @@ def _gpu():
 def _cfg(wl):
     from test_rnn_layer_amd import _lib
     return _lib.make_config(wl.B, wl.T, wl.H, wl.d, wl.m, wl.b, wl.eta, io_dtype=wl.io_dtype, loss=wl.loss,
-                            gelu=wl.gelu)
+                            gelu=wl.gelu, algo="generic" if wl.name.endswith("_generic") else "auto")
 
 
 def _check(name, got, ref, tol=REL_MAX_TOL):
@@ -79,7 +84,7 @@ def test_backward_matches_oracle(case, reverse):
         _check(k, from_device(g[k]), ref[k])
 
 
-@pytest.mark.parametrize("case", ["f32_b1", "f32_b4_segments", "bf16_d64"])
+@pytest.mark.parametrize("case", ["f32_b1", "f32_b4_segments", "bf16_d64", "bf16_d64_segments"])
 def test_bidir_backward_matches_oracle(case):
     from test_rnn_layer_amd import _lib
     wl = CASES[case].replace(alpha_f=0.3, alpha_b=-0.2)  # distinct gates catch a swap
@@ -143,6 +148,35 @@ def test_backward_properties_bitwise():
                       (bd["dW2_0"], f["dW2_0"] + r["dW2_0"])]:
         scale = want.abs().max().item()
         assert (got - want).abs().max().item() <= 1e-5 * scale, scale
+
+
+def test_backward_f32_matrix_core_forward_properties():
+    """The d = 64 backward whose forward pass runs on the fp32 matrix cores (algo AUTO):
+    determinism, a zero gate that passes dY straight through with no other gradient, and
+    causality (dY on the first P tokens only leaves dX zero after them), all bitwise,
+    over three checkpoint segments and a ragged tail."""
+    from test_rnn_layer_amd import _lib
+    wl = CASES["bf16_d64_segments"]
+    print("[backward properties, fp32 matrix-core forward]", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    cfg = _cfg(wl)
+    dy = torch.from_numpy(W.make_dy(wl)).cuda()
+    a = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dy)
+    b = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dy)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    z = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], torch.zeros_like(dev["alpha_f"]), dy)
+    torch.cuda.synchronize()
+    assert torch.equal(z["dX"], dy)
+    for k in ["dtheta", "dW1_0", "dW2_0"]:
+        assert not torch.any(z[k]), k
+    P = 100
+    dyp = torch.from_numpy(W.make_dy(wl, t1=P)).cuda()
+    c = _lib.backward(cfg, dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"], dyp)
+    torch.cuda.synchronize()
+    assert not torch.any(c["dX"][:, P:]) and torch.any(c["dX"][:, :P])
 
 
 def test_backward_no_tokens():
