@@ -544,6 +544,14 @@ int32_t run_mfma(const ttt_mlp_config* c, const Plan& pl, const Direction* dirs,
 // states, the replayed segment B*H*kCkptEvery states and forward quantities.
 constexpr int kCkptEvery = 32;
 constexpr size_t kBackwardLdsMax = 160 * 1024;
+// With the fp32 matrix-core forward steps (algo AUTO, d = 64, m = 256, b = 16, erf GELU), the
+// backward scan's segments are replayed beforehand, kReplayWindow segments of every chain per
+// launch on as many workgroups, and the backward scan walks them without replaying.
+constexpr int kReplayWindow = 4;
+
+bool bwd_f32mfma(const ttt_mlp_config* c) {
+  return c->algo == TTT_ALGO_AUTO && ttt::scan_fwd_f32_supported(c->d, c->m, c->b) && c->gelu != TTT_GELU_TANH;
+}
 
 struct BwdPlan {
   Plan fwd;  // the forward pass's Q/K/V and state slices (generic layout)
@@ -567,6 +575,8 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
                 c->b, kBackwardLdsMax);
   if (c->d % 4 != 0 || c->m % 4 != 0)
     return fail(TTT_ERR_UNSUPPORTED, "backward: d and m must be multiples of 4 (got d=%d m=%d)", c->d, c->m);
+  if (bwd_f32mfma(c) && ttt::scan_replay_f32_slot_elems() != ttt::scan_backward_segment_elems(c->d, c->m, c->b))
+    return fail(TTT_ERR_UNSUPPORTED, "backward: the segment replay's slot layout differs from the backward scan's");
   const size_t D = (size_t)c->H * c->d, BTD = (size_t)c->B * c->T * D, BH = (size_t)c->B * c->H;
   const size_t st2 = 2 * (size_t)c->d * c->m * sizeof(float);  // one (W1, W2) state
   const size_t nseg = ((size_t)(c->T + c->b - 1) / c->b + kCkptEvery - 1) / kCkptEvery;
@@ -595,7 +605,8 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   p->dxp_off = bidir ? take(BTD * sizeof(float)) : 0;
   p->ckpt_off[0] = take(BH * nseg * st2);
   p->ckpt_off[1] = bidir ? take(BH * nseg * st2) : 0;
-  p->segst_off = take(BH * kCkptEvery * ttt::scan_backward_segment_elems(c->d, c->m, c->b) * sizeof(float));
+  p->segst_off = take(BH * (bwd_f32mfma(c) ? kReplayWindow : 1) * kCkptEvery *
+                      ttt::scan_backward_segment_elems(c->d, c->m, c->b) * sizeof(float));
   p->dstate_off = take(BH * st2);
   p->scratch_off = take(BH * ttt::scan_backward_scratch_elems(c->d, c->m, c->b) * sizeof(float));
   p->dwseq_off = take(BH * st2);
@@ -631,8 +642,7 @@ int32_t bwd_forward(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin,
   sa.ckpt_every = kCkptEvery;
   sa.scratch = (float*)(ws + bp.scratch_off);
   // AUTO: the fp32 matrix-core forward pass with the state in registers where it applies
-  const bool f32mfma = c->algo == TTT_ALGO_AUTO && ttt::scan_fwd_f32_supported(c->d, c->m, c->b) &&
-                       c->gelu != TTT_GELU_TANH;
+  const bool f32mfma = bwd_f32mfma(c);
   hipError_t e = timed_launch(TTT_KERNEL_SCAN, s, [&] {
     return f32mfma ? ttt::launch_scan_fwd_f32(sa, s) : ttt::launch_scan_fwd_ckpt(sa, s);
   });
@@ -732,12 +742,43 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* x
   ba.gscale = c->loss == TTT_LOSS_MEAN ? 2.0f / (float)c->d : 2.0f;
   ba.gelu_tanh = c->gelu == TTT_GELU_TANH;
   ba.reverse = reverse;
-  hipError_t e = ov.side ? hipEventRecord(ov.ev_ready, s) : hipSuccess;
-  if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
-  e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] { return ttt::launch_scan_backward(ba, s); });
-  if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
   int32_t st = TTT_OK;
-  if (ov.side) {
+  hipError_t e = hipSuccess;
+  const bool replay = bwd_f32mfma(c) && c->T > 0;
+  if (replay) {
+    // the deferred dtheta GEMM first, on this stream: beside the per-window launches below it
+    // would hold the CUs that each relaunch needs
+    if (ov.side) {
+      st = grad_dtheta(bp, ws, 0, ov.prev_dqkv, ov.prev_x32, dtheta, BT, D, 0, s);
+      if (st != TTT_OK) return st;
+    }
+    // windows of kReplayWindow segments from the last: replay them (one workgroup per chain and
+    // segment), then walk them
+    const int64_t nseg = ((c->T + c->b - 1) / c->b + kCkptEvery - 1) / kCkptEvery;
+    ttt::ScanArgs ra = scan_args(c, bp.fwd, nullptr, nullptr, nullptr, nullptr, reverse, nullptr, nullptr, nullptr,
+                                 nullptr, ws);
+    ra.ckpt = const_cast<float*>(ckpt);
+    ra.ckpt_every = kCkptEvery;
+    ra.seg_slots = ba.segst;
+    ba.replayed = 1;
+    for (int64_t hi = nseg - 1; hi >= 0; hi -= kReplayWindow) {
+      const int64_t lo = std::max<int64_t>(0, hi - kReplayWindow + 1);
+      ra.seg_lo = ba.seg_lo = lo;
+      ba.seg_hi = hi;
+      ra.seg_count = ba.seg_count = (int32_t)(hi - lo + 1);
+      ba.first = hi == nseg - 1;
+      e = timed_launch(TTT_KERNEL_SCAN, s, [&] { return ttt::launch_scan_replay_f32(ra, s); });
+      if (e != hipSuccess) return fail(TTT_ERR_HIP, "segment replay launch: %s", hipGetErrorString(e));
+      e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] { return ttt::launch_scan_backward(ba, s); });
+      if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
+    }
+  } else {
+    e = ov.side ? hipEventRecord(ov.ev_ready, s) : hipSuccess;
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+    e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] { return ttt::launch_scan_backward(ba, s); });
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
+  }
+  if (ov.side && !replay) {
     e = hipStreamWaitEvent(ov.side, ov.ev_ready, 0);
     if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream wait: %s", hipGetErrorString(e));
     st = grad_dtheta(bp, ws, 1, ov.prev_dqkv, ov.prev_x32, dtheta, BT, D, 0, ov.side);
@@ -749,7 +790,7 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* x
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "dalpha launch: %s", hipGetErrorString(e));
   st = grad_dx(bp, ws, 0, dqkv, theta32, dyin, dX, BT, D, s);
   if (st != TTT_OK) return st;
-  if (ov.side) {
+  if (ov.side && !replay) {
     e = hipStreamWaitEvent(s, ov.ev_done, 0);
     if (e != hipSuccess) return fail(TTT_ERR_HIP, "stream wait: %s", hipGetErrorString(e));
   }

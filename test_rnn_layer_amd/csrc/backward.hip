@@ -620,6 +620,9 @@ __global__ __launch_bounds__(BW) void scan_fwd_ckpt_kernel(ScanArgs a) {
   }
 }
 
+// REPLAYED false: one launch walks every segment, replaying each from its checkpoint;
+// true: the segments seg_hi .. seg_lo were replayed into segst beforehand.
+template <bool REPLAYED>
 __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int d = a.d, m = a.m, b = a.b, tid = threadIdx.x;
@@ -645,6 +648,7 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   const int64_t bm = (int64_t)b * m, slot = segment_slot_floats(d, m, b);
   float* seg = a.segst + sh * (int64_t)C * slot;
   float* const scratch_A = t.A;  // the workgroup's own b x m panels (the unkept last mini-batch)
+  (void)scratch_A;
   auto bind_fwd = [&](float* base) {
     t.A = base;
     t.Hk = base + bm;
@@ -652,17 +656,20 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
     t.Gh = base + 3 * bm;
     t.G1 = base + 4 * bm;
   };
-  for (int64_t i = tid; i < 2 * dm; i += BW) dW1[i] = 0.0f;
+  if (!REPLAYED || a.first)
+    for (int64_t i = tid; i < 2 * dm; i += BW) dW1[i] = 0.0f;
 
   const int64_t plane = a.B * a.H * T * d;
   Rows rw{a.qkv + sh * T * d, a.qkv + plane + sh * T * d, a.qkv + 2 * plane + sh * T * d, T, a.reverse};
 
-  for (int64_t sg = nseg - 1; sg >= 0; --sg) {
+  const int64_t sg_hi = REPLAYED ? a.seg_hi : nseg - 1, sg_lo = REPLAYED ? a.seg_lo : 0;
+  for (int64_t sg = sg_hi; sg >= sg_lo; --sg) {
     const int64_t j0 = sg * C, j1 = min(nmb, j0 + C);
+    if (REPLAYED) seg = a.segst + ((sh * a.seg_count + (sg - sg_lo)) * C) * slot;
     // replay the segment's forward steps from its checkpoint, keeping each mini-batch's start state
-    state_in(Wc, a.ckpt + (sh * nseg + sg) * 2 * dm, d, m);
+    if (!REPLAYED) state_in(Wc, a.ckpt + (sh * nseg + sg) * 2 * dm, d, m);
     __syncthreads();
-    for (int64_t j = j0; j < j1; ++j) {
+    for (int64_t j = j0; j < j1 && !REPLAYED; ++j) {
       float* sl = seg + (j - j0) * slot;
       state_out(sl, Wc, d, m);
       if (j + 1 == j1) break;
@@ -686,7 +693,8 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
         W = Wc;
       }
       // every mini-batch but the segment's last has its forward quantities from the replay
-      const bool kept = j + 1 < j1;
+      // (all of them when the segments were replayed beforehand)
+      const bool kept = REPLAYED || j + 1 < j1;
       load_qkv(t, rw, j * b, n, d, !kept);
       if (kept) {
         bind_fwd(sl + 2 * dm);
@@ -794,8 +802,10 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       __syncthreads();
     }
   }
-  float* o = a.dw_seq + sh * 2 * dm;
-  for (int64_t i = tid; i < 2 * dm; i += BW) o[i] = dW1[i];
+  if (!REPLAYED || sg_lo == 0) {
+    float* o = a.dw_seq + sh * 2 * dm;
+    for (int64_t i = tid; i < 2 * dm; i += BW) o[i] = dW1[i];
+  }
 }
 
 // C[M x N] = (accumulate ? C : Cadd or 0) + A B, fp32; A(r, k) = A[r lda + k], or
@@ -919,11 +929,13 @@ hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s) {
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s) {
   // T = 0 runs too: no segments, and the kernel writes the zero adjoint of the initial state
   const size_t lds = scan_backward_lds_bytes(a.d, a.m, a.b);
-  hipError_t e = hipFuncSetAttribute((const void*)scan_backward_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  const void* fn = a.replayed ? (const void*)scan_backward_kernel<true> : (const void*)scan_backward_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_backward_kernel, dim3((unsigned)(a.B * a.H)), dim3(BW), lds,
-                     s, a);
+  if (a.replayed)
+    hipLaunchKernelGGL(scan_backward_kernel<true>, dim3((unsigned)(a.B * a.H)), dim3(BW), lds, s, a);
+  else
+    hipLaunchKernelGGL(scan_backward_kernel<false>, dim3((unsigned)(a.B * a.H)), dim3(BW), lds, s, a);
   return hipGetLastError();
 }
 

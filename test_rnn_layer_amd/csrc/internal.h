@@ -63,6 +63,9 @@ struct ScanArgs {
   float* ckpt;           // forward pass for the backward only: the state (W1 then W2) at the
   int32_t ckpt_every;    // start of every ckpt_every-th mini-batch, [B, H, nseg, 2 d m],
   float* scratch;        // and its operand panels, scan_backward_scratch_elems per (sequence, head)
+  float* seg_slots;      // segment replay only: [B, H, seg_count, ckpt_every, slot] (see backward.hip)
+  int64_t seg_lo;        // segment replay only: segments seg_lo .. seg_lo + seg_count - 1
+  int32_t seg_count;
 };
 
 // LDS bytes the generic scan needs for (d, m, b).
@@ -109,6 +112,12 @@ struct BwdArgs {
   int32_t H, d, m, b, ckpt_every;
   float eta, gscale;
   int32_t gelu_tanh, reverse;
+  // 1: the segments were replayed beforehand (launch_scan_replay_f32): this launch walks
+  // segments seg_hi down to seg_lo from segst laid out [B, H, seg_count, ckpt_every, slot],
+  // clearing the adjoint first when `first` is set and writing dw_seq when seg_lo is 0;
+  // 0: one launch walks every segment, replaying each itself (segst: one segment per chain)
+  int32_t replayed, first, seg_count;
+  int64_t seg_lo, seg_hi;
 };
 // LDS bytes of the backward's scan kernels (the forward pass below too): the b x d and
 // b x b panels, and the state when it fits beside them (at most 160 KB); workspace
@@ -125,6 +134,12 @@ hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s);
 // b = 16, erf GELU; ScanArgs: qkv, xin, y, z, alpha, w1_0, w2_0, ckpt, ckpt_every).
 bool scan_fwd_f32_supported(int d, int m, int b);
 hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s);
+// The same steps replaying segments seg_lo .. seg_lo + seg_count - 1 of every (sequence, head)
+// from their checkpoints (ScanArgs: qkv, ckpt, ckpt_every, seg_slots, seg_lo, seg_count): each
+// mini-batch's slot gets its start state and forward quantities (scan_replay_f32_slot_elems
+// floats, the layout scan_backward_segment_elems describes).
+size_t scan_replay_f32_slot_elems();
+hipError_t launch_scan_replay_f32(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
 // C = (accumulate ? C : Cadd or 0) + A B, fp32 (A [M, K] row-major, or [K, M] when
 // a_transposed; B [K, N] row-major, fp32 or bf16)

@@ -7,6 +7,13 @@
 // forward with checkpoints (backward.hip), fp32 throughout: fp32 operands,
 // products and sums (v_mfma_f32_16x16x4_f32), in another order.
 //
+// The same steps also replay checkpoint segments for the backward scan: one
+// workgroup per (sequence, head, segment) of a window of segments starts from the
+// segment's checkpoint and writes, for each of its mini-batches, the state it
+// starts from and the forward quantities A, Hk, GELU'(A), Gh, G1 and G2 into the
+// backward scan's slot for it (backward.hip), with no read-out.  The replayed
+// states are the checkpointed trajectory bit for bit.
+//
 // One 512-thread workgroup per (sequence, head); wave w owns hidden units
 // [32w, 32w + 32): its slices of W1 (64 x 32), W2 (32 x 64) and W2 once more as
 // its transpose W2T (the operand of the contraction over d) stay in registers
@@ -18,14 +25,14 @@
 // mini-batch dual form of generic.hip, c = 2/d or 2, N* = -eta *):
 //   A^T = W1^T K^T, Hk^T = GELU(A^T), S1^T = GELU'(A^T)        (local)
 //   Yhat^T = W2^T Hk^T         partial over the wave's units -> LDS, summed
-//   NG2 = -eta c (Yhat - V)    each thread two values -> LDS
-//   NGh = NG2 W2^T, NG1 = NGh * S1 (token-major: S1 and Hk transposed in LDS)
+//   G2 = c (Yhat - V)          each thread two values -> LDS
+//   Gh = G2 W2^T, G1 = Gh * S1 (token-major: S1 and Hk transposed in LDS)
 //   W1 += K^T NG1, W2 += Hk^T NG2, W2T += NG2^T Hk
 // and, with the state that follows block j-1 (which holds the updates of all its
 // tokens), block j-1's read-out, taking back the updates of the tokens after each
 // one (striu keeps the entries [t][t'] with t' > t):
 //   Aq^T = W1^T Q^T - NG1^T striu(Q K^T)^T, Hq^T = GELU(Aq^T)
-//   Z^T  = W2^T Hq^T - NG2^T striu(Hq Hk^T)^T               partial -> LDS, summed
+//   Z^T  = W2^T Hq^T + eta G2^T striu(Hq Hk^T)^T            partial -> LDS, summed
 // with y = x + tanh(alpha) z.  A last, short block is padded with zero tokens,
 // which add exact zeros to every sum.  Two workgroup barriers per step.
 #include "internal.h"
@@ -48,6 +55,11 @@ constexpr int BLKF = 3 * PAN;    // floats of a staged block: Q, then K, then V
 constexpr int BLK_CH = BLKF / 4; // 816 chunks of 16 bytes, 17 per row (the last one padding)
 constexpr int TT = FB + 4;       // 20: row stride of the per-wave transposed tiles
 constexpr int OQ = 0, OK = PAN, OV = 2 * PAN;
+// a replayed mini-batch's slot: W1 [d][m], W2 [m][d], then A, Hk, GELU'(A), Gh, G1
+// ([b][m] each) and G2 ([b][d]), as the backward scan reads it
+constexpr int64_t SL_W2 = (int64_t)FD * FM, SL_A = 2 * SL_W2, SL_HK = SL_A + FB * FM, SL_S1 = SL_HK + FB * FM,
+                  SL_GH = SL_S1 + FB * FM, SL_G1 = SL_GH + FB * FM, SL_G2 = SL_G1 + FB * FM,
+                  SLOT = SL_G2 + FB * FD;
 
 // Staged panels have rows of 68 floats (17 chunks of 16 bytes): the 16-byte reads of
 // one chunk column over rows 0..7 and the 4-byte reads of 16 columns of rows 4g + r
@@ -68,11 +80,15 @@ __device__ __forceinline__ float gelu1(float a) { return a * (0.5f * (1.0f + erf
 
 __device__ float4 g_zero_chunk;  // zero-initialised, never written: the source of padding rows
 
+// REPLAY false: the forward pass of a whole direction (grid: sequences x heads);
+// REPLAY true: segments seg_lo .. seg_lo + seg_count - 1 of every (sequence, head)
+// (grid: sequences x heads x seg_count)
+template <bool REPLAY>
 __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_fwd_f32_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float Stage[NSTG][BLKF];  // token blocks j-1 .. j+1
   __shared__ f32x4 Ypart[FW][4][64];                              // partial Yhat^T: wave, d-tile, lane
   __shared__ f32x4 Zpart[FW][4][64];                              // partial Z^T
-  __shared__ __attribute__((aligned(16))) float G2s[2][FB * GS];   // NG2 [token][feature], by block parity
+  __shared__ __attribute__((aligned(16))) float G2s[2][FB * GS];   // G2 [token][feature], by block parity
   // per-wave transposes: Hk^T and S1^T tiles as [unit][token], read back token-major
   __shared__ __attribute__((aligned(16))) float HkS[FW][2][16 * TT];
   __shared__ __attribute__((aligned(16))) float DgS[FW][2][16 * TT];
@@ -80,21 +96,28 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int64_t chain = REPLAY ? blockIdx.x / a.seg_count : blockIdx.x;  // sequence * H + head
+  const int s = (int)(chain / a.H), h = (int)(chain % a.H);
   const int64_t T = a.T;
   const int D = a.H * FD;
   const int u0 = 32 * w;
   const int64_t sh = (int64_t)s * a.H + h;
   const int64_t dm = (int64_t)FD * FM;
-  const float ngs = -a.eta * a.gscale;
-  const int64_t nblk = (T + FB - 1) / FB;
+  const float neta = -a.eta, gs = a.gscale;
+  const int64_t nblk_all = (T + FB - 1) / FB;
   const int C = a.ckpt_every;
-  const int64_t nseg = (nblk + C - 1) / C;
+  const int64_t nseg = (nblk_all + C - 1) / C;
+  // mini-batches j0 .. j1 - 1: the whole sequence, or one replayed segment
+  const int64_t seg = REPLAY ? a.seg_lo + blockIdx.x % a.seg_count : 0;
+  const int64_t j0 = REPLAY ? seg * C : 0;
+  const int64_t j1 = REPLAY ? min(nblk_all, j0 + C) : nblk_all;
+  float* const slots = REPLAY ? a.seg_slots + (chain * a.seg_count + blockIdx.x % a.seg_count) * C * SLOT : nullptr;
 
   f32x4 W1[4][2], W2[2][4], W2T[4][2];
   {
-    const float* w1 = a.w1_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * dm;
-    const float* w2 = a.w2_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * dm;
+    const float* w1 = REPLAY ? a.ckpt + (chain * nseg + seg) * 2 * dm
+                             : a.w1_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * dm;
+    const float* w2 = REPLAY ? w1 + dm : a.w2_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * dm;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -116,7 +139,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int rd_t = rd_src & 15;
   const int rd_d = 16 * rd_dt + 4 * (rd_src >> 4) + 2 * rd_p;
   const int ch0 = h * FD + rd_d;
-  Tg[tid] = make_float2(tanhf(a.alpha[ch0]), tanhf(a.alpha[ch0 + 1]));
+  if (!REPLAY) Tg[tid] = make_float2(tanhf(a.alpha[ch0]), tanhf(a.alpha[ch0 + 1]));
   auto reduce_part = [&](const f32x4 (&part)[FW][4][64]) -> float2 {
     float2 v[FW];
 #pragma unroll
@@ -152,7 +175,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // carried from block j-1 to its read-out during step j
   f32x4 St_prev = zero4();                 // S^T = K Q^T of block j-1: [t'][t]
-  f32x4 g1_prev[2] = {zero4(), zero4()};   // NG1 of block j-1, token-major [t][u]
+  f32x4 g1_prev[2] = {zero4(), zero4()};   // NG1 = -eta G1 of block j-1, token-major [t][u]
   f32x4 hkT_prev[2] = {zero4(), zero4()};  // Hk^T of block j-1: [u][t]
 
   // -striu of a D-layout [t'][t] tile: the entries with t' = 4g + r > t = c, negated
@@ -193,7 +216,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int r = 0; r < 4; ++r) zp = mfma4(W2[ut][dt][r], hqT[ut][r], zp);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) zp = mfma4(g2prev[(4 * g + r) * GS + 16 * dt + c], later[r] ? -pt[r] : 0.0f, zp);
+      for (int r = 0; r < 4; ++r) zp = mfma4(g2prev[(4 * g + r) * GS + 16 * dt + c], later[r] ? a.eta * pt[r] : 0.0f, zp);
       Zpart[w][dt][lane] = zp;
     }
   };
@@ -216,7 +239,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
   };
 
-  for (int64_t jb = 0; jb < NSTG - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
+  for (int64_t jb = j0; jb < j0 + NSTG - 1 && jb < j1; ++jb) stage_async(jb, (int)(jb - j0));
   // G2s of the block before block 0 is read by the read-out at j = 0 (whose result is
   // never stored): keep it finite
   for (int i = tid; i < FB * GS; i += FT) G2s[1][i] = 0.0f;
@@ -224,16 +247,18 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   vmem_done();
   __syncthreads();
 
-  for (int64_t j = 0; j < nblk; ++j) {
+  for (int64_t j = j0; j < j1; ++j) {
     const int sp = sj == 0 ? NSTG - 1 : sj - 1;
+    float* const sl = REPLAY ? slots + (j - j0) * SLOT : nullptr;
     const float* blk = Stage[sj];
     const float* blk_prev = Stage[sp];
     float* g2cur = G2s[j & 1];
     const float* g2prev = G2s[(j & 1) ^ 1];
 
-    // ---- checkpoint: the state at the start of block j, W1 [d][m] then W2 [m][d]
-    if (j % C == 0) {
-      float* o = a.ckpt + (sh * nseg + j / C) * 2 * dm;
+    // ---- checkpoint (every C-th block), or the replayed block's slot: the state at the
+    //      start of block j, W1 [d][m] then W2 [m][d]
+    if (REPLAY || j % C == 0) {
+      float* o = REPLAY ? sl : a.ckpt + (sh * nseg + j / C) * 2 * dm;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -270,6 +295,13 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         hkT[ut][r] = hv;
         HkS[w][ut][(4 * g + r) * TT + c] = hv;
         DgS[w][ut][(4 * g + r) * TT + c] = dv;
+        if (REPLAY) sl[SL_S1 + c * FM + u0 + 16 * ut + 4 * g + r] = dv;
+      }
+    if (REPLAY)  // A and Hk [t][m]: lane (g, c) holds token c, units u0 + 16 ut + 4g .. +3
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut) {
+        *(f32x4*)&sl[SL_A + c * FM + u0 + 16 * ut + 4 * g] = At[ut];
+        *(f32x4*)&sl[SL_HK + c * FM + u0 + 16 * ut + 4 * g] = hkT[ut];
       }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -283,14 +315,16 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
     __syncthreads();
 
-    // ---- NG2 = -eta c (Yhat - V): this thread's two values
+    // ---- G2 = c (Yhat - V): this thread's two values
     {
       const float2 y = reduce_part(Ypart);
       const float2 v = *(const float2*)&blk[OV + sw(rd_t, rd_d)];
-      *(float2*)&g2cur[rd_t * GS + rd_d] = make_float2(ngs * (y.x - v.x), ngs * (y.y - v.y));
+      const float2 g2 = make_float2(gs * (y.x - v.x), gs * (y.y - v.y));
+      *(float2*)&g2cur[rd_t * GS + rd_d] = g2;
+      if (REPLAY) *(float2*)&sl[SL_G2 + rd_t * FD + rd_d] = g2;
     }
     // ---- read-out of block j-1 (at j = 0 on zero operands, never stored)
-    readout(blk_prev, g2prev);
+    if (!REPLAY) readout(blk_prev, g2prev);
     // ---- this wave's token-major Hk and S1: [t = 4g + r][u = c]
     f32x4 hkF[2], s1F[2];
 #pragma unroll
@@ -303,7 +337,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     vmem_done();
     __syncthreads();
 
-    // ---- NGh = NG2 W2^T (token-major), NG1 = NGh * S1
+    // ---- Gh = G2 W2^T (token-major), G1 = Gh * S1, NG1 = -eta G1
     f32x4 g1[2] = {zero4(), zero4()};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -313,8 +347,16 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int r = 0; r < 4; ++r) g1[ut] = mfma4(gA[r], W2T[dt][ut][r], g1[ut]);
     }
-    g1[0] = g1[0] * s1F[0];
-    g1[1] = g1[1] * s1F[1];
+    if (REPLAY)  // Gh, then G1 [t][m]: lane (g, c) holds tokens 4g .. 4g+3 of unit u0 + 16 ut + c
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sl[SL_GH + (4 * g + r) * FM + u0 + 16 * ut + c] = g1[ut][r];
+          sl[SL_G1 + (4 * g + r) * FM + u0 + 16 * ut + c] = g1[ut][r] * s1F[ut][r];
+        }
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut) g1[ut] = neta * (g1[ut] * s1F[ut]);
     // ---- state update: W1 += K^T NG1, W2 += Hk^T NG2, W2T += NG2^T Hk (contraction over
     //      the 16 tokens: register r of a token-major tile is tokens 4g + r)
     f32x4 g2c[4];
@@ -324,7 +366,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         kc[r] = blk[OK + sw(4 * g + r, 16 * dt + c)];
-        g2c[dt][r] = g2cur[(4 * g + r) * GS + 16 * dt + c];
+        g2c[dt][r] = neta * g2cur[(4 * g + r) * GS + 16 * dt + c];
       }
 #pragma unroll
       for (int ut = 0; ut < 2; ++ut)
@@ -342,8 +384,8 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
 
     // ---- Z of block j-1 and its gate; block j+2 into the stage that held block j-1
-    store_z(j - 1, reduce_part(Zpart));
-    if (j + NSTG - 1 < nblk) stage_async(j + NSTG - 1, sp);
+    if (!REPLAY) store_z(j - 1, reduce_part(Zpart));
+    if (j + NSTG - 1 < j1) stage_async(j + NSTG - 1, sp);
 
     St_prev = St;
     g1_prev[0] = g1[0];
@@ -355,11 +397,11 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // ---- read-out of the last block with the final state (after every wave's last
   //      reads of Zpart)
-  if (nblk > 0) {
+  if (!REPLAY && j1 > 0) {
     __syncthreads();
-    readout(Stage[sj == 0 ? NSTG - 1 : sj - 1], G2s[(nblk - 1) & 1]);
+    readout(Stage[sj == 0 ? NSTG - 1 : sj - 1], G2s[(j1 - 1) & 1]);
     __syncthreads();
-    store_z(nblk - 1, reduce_part(Zpart));
+    store_z(j1 - 1, reduce_part(Zpart));
   }
 }
 
@@ -367,9 +409,19 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 bool scan_fwd_f32_supported(int d, int m, int b) { return d == FD && m == FM && b == FB; }
 
+size_t scan_replay_f32_slot_elems() { return (size_t)SLOT; }
+
 hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s) {
   if (a.gelu_tanh || !scan_fwd_f32_supported(a.d, a.m, a.b) || a.ckpt_every <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(scan_fwd_f32_kernel, dim3((unsigned)(a.B * a.H)), dim3(FT), 0, s, a);
+  hipLaunchKernelGGL(scan_fwd_f32_kernel<false>, dim3((unsigned)(a.B * a.H)), dim3(FT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_replay_f32(const ScanArgs& a, hipStream_t s) {
+  if (a.gelu_tanh || !scan_fwd_f32_supported(a.d, a.m, a.b) || a.ckpt_every <= 0 || a.seg_count <= 0 ||
+      !a.seg_slots)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scan_fwd_f32_kernel<true>, dim3((unsigned)(a.B * a.H * a.seg_count)), dim3(FT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -35,8 +35,9 @@ CASES = {
     # backward's own steps
     "bf16_d64": W.WORKLOADS["bidir307k"].replace(T=72, H=2, seg_len=0, name="bf16_d64"),
     "bf16_d64_generic": W.WORKLOADS["bidir307k"].replace(T=72, H=2, seg_len=0, name="bf16_d64_generic"),
-    # the same shape over three checkpoint segments of 32 mini-batches and a 12-token tail
-    "bf16_d64_segments": W.WORKLOADS["bidir307k"].replace(T=1100, H=2, seg_len=0, name="bf16_d64_segments"),
+    # the same shape over six checkpoint segments of 32 mini-batches and a 12-token tail: with algo
+    # AUTO the backward scan walks them in two windows of segments replayed beforehand
+    "bf16_d64_segments": W.WORKLOADS["bidir307k"].replace(T=2700, H=1, seg_len=0, name="bf16_d64_segments"),
     # the bigstate307k head shape: a state too large for LDS stays in the workspace
     "bf16_d128_b1": W.WORKLOADS["bigstate307k"].replace(T=24, H=1, seg_len=0, name="bf16_d128_b1"),
 }
@@ -154,7 +155,7 @@ def test_backward_f32_matrix_core_forward_properties():
     """The d = 64 backward whose forward pass runs on the fp32 matrix cores (algo AUTO):
     determinism, a zero gate that passes dY straight through with no other gradient, and
     causality (dY on the first P tokens only leaves dX zero after them), all bitwise,
-    over three checkpoint segments and a ragged tail."""
+    over six checkpoint segments (two replay windows) and a ragged tail."""
     from test_rnn_layer_amd import _lib
     wl = CASES["bf16_d64_segments"]
     print("[backward properties, fp32 matrix-core forward]", flush=True)
