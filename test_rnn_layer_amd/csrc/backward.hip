@@ -39,6 +39,9 @@
 // read 16 bytes at a time; d and m multiples of 4).
 #include "internal.h"
 #include "mfma_common.h"
+#include "phase_marks.h"
+
+TTT_MARKS_BUFFER(g_marks_scan_backward);
 
 namespace ttt {
 namespace {
@@ -685,6 +688,9 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
     __syncthreads();
     // the segment's mini-batches, last to first
     for (int64_t j = j1 - 1; j >= j0; --j) {
+      // marks (measurement build): mini-batches of this launch in walking order
+      const int64_t mk = (sg_hi - sg) * C + (j1 - 1 - j);
+      TTT_MARK(g_marks_scan_backward, mk, 0);
       const int n = (int)min((int64_t)b, T - j * b);
       float* sl = seg + (j - j0) * slot;
       St W = state_at(sl, false, d, m);
@@ -708,13 +714,16 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
         t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + ch];
       }
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 1);
       if (!kept) forward_core(t, W, n, d, m, a.gscale, a.gelu_tanh);
       readout_hidden(t, W, n, b, d, m, eta, a.gelu_tanh, t.dAq);  // dAq holds GELU'(Aq) for now
+      TTT_MARK(g_marks_scan_backward, mk, 2);
       // N = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
       rowdot_tril(t.N, b, n, m, t.Hq, m, t.Hk, m, 1.0f);
       rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
       prod<4, true>(t.dGh, m, n, m, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 3);
       // dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dG2 = -eta N^T dZ; dHk = dN^T Hq
       if (n % 16 == 0 && m % 16 == 0 && d % 16 == 0) {  // on the matrix cores (N, dN are 0 above the diagonal)
         prod_mfma<false, false>(t.dGh, m, n, m, n, t.dN, b, t.Hk, m, 1.0f, true, 0);
@@ -742,6 +751,7 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       __syncthreads();
       // dQ = dAq W1^T; dM = tril(-eta dAq G1^T); with the adjoints of the state after this
       // mini-batch: dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK = -eta G1 dW1'^T
+      TTT_MARK(g_marks_scan_backward, mk, 4);
       prod<1, true>(t.dQ, d, n, d, m, t.dAq, m, W.w1, W.ld1, 1.0f, false);
       rowdot_tril(t.dM, b, n, m, t.dAq, m, t.G1, m, -eta, 4);
       prod<4, true>(t.dHk, m, n, m, d, t.G2, d, dW2, d, -eta, true, 5);
@@ -749,6 +759,7 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       prod<4, false>(t.dG1, m, n, m, d, t.K, d, dW1, m, -eta, false, 9);
       prod<1, true>(t.dK, d, n, d, m, t.G1, m, dW1, m, -eta, false, 9);
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 5);
       // dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q
       for (int i = tid; i < n * m; i += BW) {
         const int r = i / m, c = i - r * m;
@@ -768,6 +779,7 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       }
       __syncthreads();
       // dGh = dG1 * S1; dA (in dG1) = dG1 * Gh * GELU''(A)
+      TTT_MARK(g_marks_scan_backward, mk, 6);
       for (int i = tid; i < n * m; i += BW) {
         float g, dg, ddg;
         gelu3(t.A[i], a.gelu_tanh, &g, &dg, &ddg);
@@ -786,6 +798,7 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       __syncthreads();
       prod<1, true>(t.dK, d, n, d, m, t.dG1, m, W.w1, W.ld1, 1.0f, true);  // dK += dA W1^T
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 7);
       // dQ, dK, dV = -dYh to their columns of [B, T, 3D]; the adjoints handed back:
       // dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
       for (int i = tid; i < n * d; i += BW) {
@@ -983,3 +996,5 @@ hipError_t launch_sum_state(const float* dw_seq, float* dW1, float* dW2, int64_t
 }
 
 }  // namespace ttt
+
+TTT_MARKS_EXPORT(ttt_phase_marks_scan_backward, g_marks_scan_backward);

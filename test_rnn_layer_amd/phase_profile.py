@@ -3,10 +3,12 @@
     python -m test_rnn_layer_amd.build --phase-marks
     python -m test_rnn_layer_amd.phase_profile --kernel mfma [--workload bidir307k] [--tokens N] [--out FILE]
 
-Runs one direction of the layer (ttt_mlp_forward) on the measurement build
-libttt_mlp_marks.so, whose scan kernels store the shader clock at the phase
-boundaries of kMarkSteps steps of workgroup 0, wave 0 (see csrc/phase_marks.h),
-and prints the median cycles of each phase and of a whole step.  The marks add
+Runs one direction of the layer (ttt_mlp_forward; with --kernel backward its
+backward, ttt_mlp_backward, whose backward scan is marked per mini-batch) on the
+measurement build libttt_mlp_marks.so, whose scan kernels store the shader clock
+at the phase boundaries of kMarkSteps steps of workgroup 0, wave 0 (see
+csrc/phase_marks.h), and prints the median cycles of each phase and of a whole
+step.  The marks add
 a wait for each clock read, so the marked step is somewhat longer than the
 library's; the clock is estimated from the marked step's cycles and the
 launch times of the same run (HIP events).
@@ -48,8 +50,19 @@ PHASES = {
         "G1 of this token (its W1 update follows in the next token's exchange)",
         "loop to the next token",
     ],
+    "backward": [
+        "the mini-batch's slot state into LDS, its Q/K/V rows, dZ = tanh(alpha) dY, G2; barrier",
+        "read-out again: M = tril(Q K^T), Aq = Q W1 - eta M G1, Hq, GELU'(Aq)",
+        "N = tril(Hq Hk^T), dN, dZ W2^T; barrier",
+        "dN Hk, dN^T Hq, N^T dZ (matrix cores); barrier; dAq",
+        "dQ = dAq W1^T, dM, the products with the adjoint (dHk, dG2, dG1, dK); barrier",
+        "dG1 -= eta M^T dAq, dQ += dM K, dK += dM^T Q; barrier",
+        "dGh, dA (GELU''); dG2 += dGh W2; dYh; dHk += dYh W2^T; dA += dHk S1; dK += dA W1^T (five barriers)",
+        "dQ|dK|dV stores, the rank-16 adjoint updates; barrier; loop",
+    ],
 }
-ENTRY = {"mfma": "ttt_phase_marks_scan_mfma", "coop": "ttt_phase_marks_scan_coop"}
+ENTRY = {"mfma": "ttt_phase_marks_scan_mfma", "coop": "ttt_phase_marks_scan_coop",
+         "backward": "ttt_phase_marks_scan_backward"}
 
 
 def main():
@@ -74,7 +87,7 @@ def main():
     fn.restype = ctypes.c_int32
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int64]
 
-    name = args.workload or ("bidir307k" if args.kernel == "mfma" else "bigstate307k")
+    name = args.workload or ("bigstate307k" if args.kernel == "coop" else "bidir307k")
     wl = W.WORKLOADS[name]
     if args.tokens:
         wl = wl.replace(T=args.tokens)
@@ -84,22 +97,30 @@ def main():
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     X, th = bf(inp["X"]), bf(inp["theta"])
     W1, W2, al = f32(inp["W1_0"]), f32(inp["W2_0"]), f32(inp["alpha_f"])
-    cfg = _lib.make_config(wl.B, wl.T, wl.H, wl.d, wl.m, wl.b, wl.eta, io_dtype=wl.io_dtype, algo=args.kernel)
+    bwd = args.kernel == "backward"
+    cfg = _lib.make_config(wl.B, wl.T, wl.H, wl.d, wl.m, wl.b, wl.eta, io_dtype=wl.io_dtype,
+                           algo="auto" if bwd else args.kernel)
     print(f"# phase marks: {args.kernel} scan, {wl.name} B={wl.B} T={wl.T} H={wl.H}, one direction", flush=True)
-    ws = torch.empty(_lib.workspace_size(cfg, False), dtype=torch.uint8, device=dev)
-    _lib.forward(cfg, X, th, W1, W2, al, reverse=args.reverse, workspace=ws)
+    if bwd:
+        dY = torch.from_numpy(W.make_dy(wl)).to(dev)
+        ws = torch.empty(_lib.backward_workspace_size(cfg, False), dtype=torch.uint8, device=dev)
+        run = lambda: _lib.backward(cfg, X, th, W1, W2, al, dY, reverse=args.reverse, workspace=ws)
+    else:
+        ws = torch.empty(_lib.workspace_size(cfg, False), dtype=torch.uint8, device=dev)
+        run = lambda: _lib.forward(cfg, X, th, W1, W2, al, reverse=args.reverse, workspace=ws)
+    run()
     torch.cuda.synchronize()
     _lib.set_kernel_timing(True)
     _lib.reset_kernel_timing()
-    _lib.forward(cfg, X, th, W1, W2, al, reverse=args.reverse, workspace=ws)
+    run()
     torch.cuda.synchronize()
-    scan_ms, scan_n = _lib.kernel_timing(_lib.TTT_KERNEL_SCAN)
+    scan_ms, scan_n = _lib.kernel_timing(_lib.TTT_KERNEL_BACKWARD if bwd else _lib.TTT_KERNEL_SCAN)
     _lib.set_kernel_timing(False)
     marks = np.zeros(MARK_STEPS * MARK_PHASES, dtype=np.uint64)
     assert fn(marks.ctypes.data, marks.size) == 0, "reading the marks failed"
     m = marks.reshape(MARK_STEPS, MARK_PHASES).astype(np.int64)
     # the launches of one direction together take every step of the sequence once
-    steps = -(-wl.T // wl.b) if args.kernel == "mfma" else wl.T
+    steps = wl.T if args.kernel == "coop" else -(-wl.T // wl.b)
     step_us = scan_ms * 1e3 / steps
     valid = np.all(m > 0, axis=1)
     n = int(np.argmin(valid)) if not valid.all() else MARK_STEPS

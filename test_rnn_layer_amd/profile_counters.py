@@ -369,10 +369,11 @@ def summarize_backward(d: str, out_md: str | None = None):
         f"# Kernel time, backward of the bidirectional layer, {wname} (one ttt_mlp_bidir_backward call)", "",
         f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ, fp32 arithmetic and "
         f"gradients; {steps} timed + {warm} warm-up calls under the trace.  One call: both forward passes again "
-        "(projection, then the scan that keeps a checkpoint every 32 mini-batches), then per direction the "
-        "backward scan, the dalpha reduction and the two gradient GEMMs (dX, dθ); the reversed pass's dθ GEMM "
-        "runs on a second stream beside the forward pass's backward scan, so kernel times overlap and their "
-        "shares are of the summed kernel time.", "",
+        "(projection, then the scan that keeps a checkpoint every 32 mini-batches: `scan_fwd_f32_kernel<false>`, "
+        "fp32 matrix cores), then per direction windows of 4 checkpoint segments from the last, each replayed "
+        "(`scan_fwd_f32_kernel<true>`, one workgroup per head and segment) and then walked by the backward scan "
+        "(`scan_backward_kernel<true>`), the dalpha reduction and the two gradient GEMMs (dX, dθ; rocBLAS), all "
+        "on one stream.", "",
         "Commands (repo root, MI355X):", "",
         f"    mkdir -p {d} && rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
         f"python3 bench.py --backward{wl_arg} --steps {steps} --warmup {warm} --no-cpu-baseline > {d}/bench.json",
@@ -385,9 +386,11 @@ def summarize_backward(d: str, out_md: str | None = None):
                      f"{float(r['TotalDurationNs']) / 1e6 / calls:.1f} ms | {float(r['Percentage']):.1f}% |")
     rf = bench["roofline"]
     lines += ["", f"The bench line of the same run: {bench['ms_per_step']:.0f} ms per call "
-              f"({bench['value']:,.0f} tokens/s); the backward scan's launches averaged {rf['avg_launch_ms']:.0f} ms "
-              f"from HIP events, {rf['flops_per_launch'] / 1e12:.2f} TFLOP each (algorithmic, replay excluded), "
-              f"{rf['achieved']:.2f} TFLOP/s = {100 * rf['frac']:.1f}% of the fp32 peak."]
+              f"({bench['value']:,.0f} tokens/s); the backward scan's launches averaged {rf['avg_launch_ms']:.2f} ms "
+              f"from HIP events, {rf['flops_per_launch'] / 1e9:.1f} GFLOP each (algorithmic, replay excluded), "
+              f"{rf['achieved']:.2f} TFLOP/s = {100 * rf['frac']:.1f}% of the fp32 peak.  Kernel time per call "
+              "(HIP events): " + ", ".join(f"{k.replace('_', ' ')} {v:.0f} ms"
+                                            for k, v in bench.get("kernel_ms_per_step", {}).items()) + "."]
     out_md = out_md or os.path.join(ROOT, "profiles", f"scan_backward_{wname}_stats.md")
     open(out_md, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
