@@ -455,9 +455,11 @@ __device__ inline St state_at(float* base, bool padded, int d, int m) {
 }
 
 // workspace floats of one replayed mini-batch: its start state (W1, W2), then A, Hk, GELU'(A),
-// Gh, G1 (b x m each) and G2 (b x d)
+// Gh, G1 (b x m each), G2 (b x d), and the read-out's Aq, Hq, GELU'(Aq) (b x m each) and
+// M = tril(Q K^T) (b x b).  The read-out's four are written only by the fp32 matrix-core replay
+// (the generic replay leaves them to the backward scan).
 __host__ __device__ constexpr int64_t segment_slot_floats(int d, int m, int b) {
-  return 2LL * d * m + 5LL * b * m + (int64_t)b * d;
+  return 2LL * d * m + 8LL * b * m + (int64_t)b * d + (int64_t)b * b;
 }
 
 // workspace floats of one workgroup: the b x m panels, then dQ and dK
@@ -702,7 +704,17 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       // (all of them when the segments were replayed beforehand)
       const bool kept = REPLAYED || j + 1 < j1;
       load_qkv(t, rw, j * b, n, d, !kept);
-      if (kept) {
+      if (REPLAYED) {
+        // the read-out's quantities from the slot too: Hq and GELU'(Aq) (into dAq) copied to
+        // this workgroup's panels (pointing the panels at the slot instead cost 30 more spilled
+        // registers), M into LDS
+        bind_fwd(sl + 2 * dm);
+        const float* ro = sl + 2 * dm + 5 * bm + (int64_t)b * d;
+        copy_rows(t.G2, d, sl + 2 * dm + 5 * bm, d, n, d);
+        copy_rows(t.Hq, m, ro + bm, m, n, m);
+        copy_rows(t.dAq, m, ro + 2 * bm, m, n, m);
+        for (int i = tid; i < b * b; i += BW) t.M[i] = ro[3 * bm + i];
+      } else if (kept) {
         bind_fwd(sl + 2 * dm);
         copy_rows(t.G2, d, sl + 2 * dm + 5 * bm, d, n, d);
       } else {
@@ -716,7 +728,7 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 1);
       if (!kept) forward_core(t, W, n, d, m, a.gscale, a.gelu_tanh);
-      readout_hidden(t, W, n, b, d, m, eta, a.gelu_tanh, t.dAq);  // dAq holds GELU'(Aq) for now
+      if (!REPLAYED) readout_hidden(t, W, n, b, d, m, eta, a.gelu_tanh, t.dAq);  // dAq holds GELU'(Aq) for now
       TTT_MARK(g_marks_scan_backward, mk, 2);
       // N = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
       rowdot_tril(t.N, b, n, m, t.Hq, m, t.Hk, m, 1.0f);

@@ -10,9 +10,10 @@
 // The same steps also replay checkpoint segments for the backward scan: one
 // workgroup per (sequence, head, segment) of a window of segments starts from the
 // segment's checkpoint and writes, for each of its mini-batches, the state it
-// starts from and the forward quantities A, Hk, GELU'(A), Gh, G1 and G2 into the
-// backward scan's slot for it (backward.hip), with no read-out.  The replayed
-// states are the checkpointed trajectory bit for bit.
+// starts from, the forward quantities A, Hk, GELU'(A), Gh, G1 and G2, and its
+// read-out's Aq, Hq, GELU'(Aq) and tril(Q K^T) into the backward scan's slot for it
+// (backward.hip); no Z or Y.  The replayed states are the checkpointed trajectory
+// bit for bit.
 //
 // One 512-thread workgroup per (sequence, head); wave w owns hidden units
 // [32w, 32w + 32): its slices of W1 (64 x 32), W2 (32 x 64) and W2 once more as
@@ -56,10 +57,12 @@ constexpr int BLK_CH = BLKF / 4; // 816 chunks of 16 bytes, 17 per row (the last
 constexpr int TT = FB + 4;       // 20: row stride of the per-wave transposed tiles
 constexpr int OQ = 0, OK = PAN, OV = 2 * PAN;
 // a replayed mini-batch's slot: W1 [d][m], W2 [m][d], then A, Hk, GELU'(A), Gh, G1
-// ([b][m] each) and G2 ([b][d]), as the backward scan reads it
+// ([b][m] each), G2 ([b][d]), Aq, Hq, GELU'(Aq) ([b][m] each) and M = tril(Q K^T)
+// ([b][b]), as the backward scan reads it
 constexpr int64_t SL_W2 = (int64_t)FD * FM, SL_A = 2 * SL_W2, SL_HK = SL_A + FB * FM, SL_S1 = SL_HK + FB * FM,
                   SL_GH = SL_S1 + FB * FM, SL_G1 = SL_GH + FB * FM, SL_G2 = SL_G1 + FB * FM,
-                  SLOT = SL_G2 + FB * FD;
+                  SL_AQ = SL_G2 + FB * FD, SL_HQ = SL_AQ + FB * FM, SL_SQ = SL_HQ + FB * FM,
+                  SL_M = SL_SQ + FB * FM, SLOT = SL_M + FB * FB;
 
 // Staged panels have rows of 68 floats (17 chunks of 16 bytes): the 16-byte reads of
 // one chunk column over rows 0..7 and the 4-byte reads of 16 columns of rows 4g + r
@@ -184,8 +187,9 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   for (int r = 0; r < 4; ++r) later[r] = 4 * g + r > c;
 
   // Read-out of the block staged at `prev` with the current state (the one that
-  // follows that block); this wave's partial Z^T goes to Zpart[w].
-  auto readout = [&](const float* prev, const float* g2prev) {
+  // follows that block); this wave's partial Z^T goes to Zpart[w].  Replaying, the
+  // block's Aq, Hq, GELU'(Aq) and M go to its slot rs instead (no Z).
+  auto readout = [&](const float* prev, const float* g2prev, float* rs) {
     f32x4 aq[2] = {zero4(), zero4()};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -200,8 +204,31 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int ut = 0; ut < 2; ++ut) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) aq[ut] = mfma4(g1_prev[ut][r], later[r] ? -St_prev[r] : 0.0f, aq[ut]);
+      if (REPLAY) {  // [t][m]: lane (g, c) holds token c, units u0 + 16 ut + 4g .. +3
+        f32x4 sq;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hqT[ut][r] = gelu1(aq[ut][r]);
+        for (int r = 0; r < 4; ++r) {
+          float hv, dv;
+          gelu2(aq[ut][r], &hv, &dv);
+          hqT[ut][r] = hv;
+          sq[r] = dv;
+        }
+        *(f32x4*)&rs[SL_AQ + c * FM + u0 + 16 * ut + 4 * g] = aq[ut];
+        *(f32x4*)&rs[SL_HQ + c * FM + u0 + 16 * ut + 4 * g] = hqT[ut];
+        *(f32x4*)&rs[SL_SQ + c * FM + u0 + 16 * ut + 4 * g] = sq;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hqT[ut][r] = gelu1(aq[ut][r]);
+      }
+    }
+    if (REPLAY) {
+      if (w == 0) {  // M[t][t'] = Q[t] . K[t'] for t' <= t: lane (g, c) holds t = c, t' = 4g .. 4g+3
+        f32x4 mv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mv[r] = later[r] ? 0.0f : St_prev[r];
+        *(f32x4*)&rs[SL_M + c * FB + 4 * g] = mv;
+      }
+      return;
     }
     f32x4 pt = zero4();  // this wave's part of (Hq Hk^T)^T: [t'][t]
 #pragma unroll
@@ -323,8 +350,10 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       *(float2*)&g2cur[rd_t * GS + rd_d] = g2;
       if (REPLAY) *(float2*)&sl[SL_G2 + rd_t * FD + rd_d] = g2;
     }
-    // ---- read-out of block j-1 (at j = 0 on zero operands, never stored)
-    if (!REPLAY) readout(blk_prev, g2prev);
+    // ---- read-out of block j-1 (at j = 0 on zero operands, never stored; replaying, into
+    //      block j-1's slot, from the segment's second block on)
+    if (!REPLAY) readout(blk_prev, g2prev, nullptr);
+    else if (j > j0) readout(blk_prev, g2prev, sl - SLOT);
     // ---- this wave's token-major Hk and S1: [t = 4g + r][u = c]
     f32x4 hkF[2], s1F[2];
 #pragma unroll
@@ -399,10 +428,13 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   //      reads of Zpart)
   if (!REPLAY && j1 > 0) {
     __syncthreads();
-    readout(Stage[sj == 0 ? NSTG - 1 : sj - 1], G2s[(j1 - 1) & 1]);
+    readout(Stage[sj == 0 ? NSTG - 1 : sj - 1], G2s[(j1 - 1) & 1], nullptr);
     __syncthreads();
     store_z(j1 - 1, reduce_part(Zpart));
   }
+  // ---- replaying: the read-out of the segment's last block (registers and its staged
+  //      block only, which nothing overwrites any more)
+  if (REPLAY && j1 > j0) readout(Stage[sj == 0 ? NSTG - 1 : sj - 1], nullptr, slots + (j1 - 1 - j0) * SLOT);
 }
 
 }  // namespace
