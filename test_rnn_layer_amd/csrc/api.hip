@@ -558,6 +558,8 @@ struct BwdPlan {
   size_t dqkv_off, dqkv2_off, z_off[2], y_off, xp_off, dxp_off, ckpt_off[2], segst_off, dstate_off, scratch_off,
       dwseq_off,
       dal_off, total;
+  // the split backward scan's exchange entries, then its abort flag (0 when it does not apply)
+  size_t bxchg_off = 0;
   // fp32 copies of bf16 operands of the gradient GEMMs (theta, X, X'; unused with fp32 io),
   // and the two rocBLAS workspace slices (caller's stream, side stream)
   size_t th32_off, x32_off, xp32_off, blas_off[2];
@@ -610,6 +612,8 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   p->dstate_off = take(BH * st2);
   p->scratch_off = take(BH * ttt::scan_backward_scratch_elems(c->d, c->m, c->b) * sizeof(float));
   p->dwseq_off = take(BH * st2);
+  if (bwd_f32mfma(c) && ttt::scan_backward_split_fits(c->B, c->H, c->d, c->m, c->b))
+    p->bxchg_off = take(ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b) * sizeof(uint64_t) + 256);
   p->dal_off = take(ttt::dalpha_partial_elems((int)D) * sizeof(float));
   const bool bf16 = c->io_dtype == TTT_BF16;
   p->th32_off = bf16 ? take(3 * D * D * sizeof(float)) : 0;
@@ -761,6 +765,17 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* x
     ra.ckpt_every = kCkptEvery;
     ra.seg_slots = ba.segst;
     ba.replayed = 1;
+    // the split walk (two workgroups per chain) where its workgroups fit co-resident: dQ and dK
+    // are added into dqkv, so it starts from zero, and so do the exchange entries and abort flag
+    const bool split = bp.bxchg_off != 0;
+    if (split) {
+      const int64_t nx = (int64_t)ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b);
+      ba.xchg = (uint64_t*)(ws + bp.bxchg_off);
+      ba.abort_flag = (uint32_t*)(ba.xchg + nx);
+      e = ttt::launch_zero_u64(ba.xchg, nx + 1, s);
+      if (e == hipSuccess) e = ttt::launch_zero_u64((uint64_t*)dqkv, 3 * BT * D / 2, s);
+      if (e != hipSuccess) return fail(TTT_ERR_HIP, "clearing launch: %s", hipGetErrorString(e));
+    }
     for (int64_t hi = nseg - 1; hi >= 0; hi -= kReplayWindow) {
       const int64_t lo = std::max<int64_t>(0, hi - kReplayWindow + 1);
       ra.seg_lo = ba.seg_lo = lo;
@@ -769,7 +784,9 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* x
       ba.first = hi == nseg - 1;
       e = timed_launch(TTT_KERNEL_SCAN, s, [&] { return ttt::launch_scan_replay_f32(ra, s); });
       if (e != hipSuccess) return fail(TTT_ERR_HIP, "segment replay launch: %s", hipGetErrorString(e));
-      e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] { return ttt::launch_scan_backward(ba, s); });
+      e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] {
+        return split ? ttt::launch_scan_backward_split(ba, s) : ttt::launch_scan_backward(ba, s);
+      });
       if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
     }
   } else {

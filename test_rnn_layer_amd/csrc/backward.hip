@@ -692,6 +692,7 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
     for (int64_t j = j1 - 1; j >= j0; --j) {
       // marks (measurement build): mini-batches of this launch in walking order
       const int64_t mk = (sg_hi - sg) * C + (j1 - 1 - j);
+      (void)mk;
       TTT_MARK(g_marks_scan_backward, mk, 0);
       const int n = (int)min((int64_t)b, T - j * b);
       float* sl = seg + (j - j0) * slot;
@@ -833,6 +834,259 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward scan over replayed windows with each chain's hidden units split over
+// two workgroups of one cooperative launch (the notes page's on-chip tensor
+// parallel: the state sharded over CUs, an all-reduce between them).  Workgroup
+// half (0 or 1) of chain sh takes units [half m/2, half m/2 + m/2): its half of
+// the mini-batch's state (W1 columns, W2 rows) and its half of the adjoint, both
+// in LDS (the adjoint goes to the workspace between launches), the b x d and
+// b x b panels in LDS, its b x m/2 panels in the workspace.  Every product over
+// units splits into the two halves' partial sums.  Those that only feed outputs
+// (dQ, dK, and dM, linear in them) are added into dQ|dK|dV by float atomics: two
+// addends onto zero, whose sum does not depend on their order.  The one that feeds
+// the rest of the step, dG2 = -eta N^T dZ - eta Hk dW2' + dGh W2 (N too is a sum
+// over units), is exchanged: each half publishes its partial as tagged 64-bit
+// device-scope stores (the mini-batch index + 1 in the high word, double-buffered
+// by its parity) and polls the other's; both add them as (half 0) + (half 1).
+// Polls are bounded: a workgroup that waits past the spin limit raises the abort
+// flag, which every poll checks, and takes NaN for the missing partial, so a lost
+// peer shows as NaN gradients rather than a hang.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSplitSpinMax = 1u << 20;
+
+// LDS floats of a split workgroup: the state half and the adjoint half (W1 columns as
+// [d][m/2 + 4], W2 rows as [m/2][d + 4]), then the b x d and b x b panels
+__host__ __device__ constexpr int64_t split_lds_floats(int d, int m, int b) {
+  return 2 * ((int64_t)d * (m / 2 + 4) + (int64_t)(m / 2) * (d + 4)) + panel_lds_floats(d, b);
+}
+// workspace floats of a split workgroup: its b x m/2 panels dAq, dHk, dG1 (then dA), dGh,
+// and its dQ and dK partials (b x d)
+__host__ __device__ constexpr int64_t split_scratch_floats(int d, int m, int b) {
+  return 4LL * b * (m / 2) + 2LL * b * d;
+}
+
+__global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int d = a.d, m = a.m, b = a.b, mh = m / 2, tid = threadIdx.x;
+  const int64_t BH = a.B * a.H;
+  const int half = blockIdx.x >= BH ? 1 : 0;
+  const int64_t sh = (int64_t)blockIdx.x - half * BH;  // sequence * H + head
+  const int s = (int)(sh / a.H), h = (int)(sh % a.H);
+  const int u0 = half * mh;
+  const int64_t T = a.T;
+  const int D = a.H * d;
+  const float eta = a.eta;
+  const int64_t dm = (int64_t)d * m, bm = (int64_t)b * m, slot = segment_slot_floats(d, m, b);
+  const int64_t nmb = (T + b - 1) / b;
+  const int C = a.ckpt_every;
+
+  St W;  // the mini-batch's state, this half
+  W.ld1 = mh + 4;
+  W.ld2 = d + 4;
+  W.w1 = lds;
+  W.w2 = W.w1 + (int64_t)d * W.ld1;
+  const int la1 = mh + 4, la2 = d + 4;  // the adjoint half, same layout
+  float* dW1 = W.w2 + (int64_t)mh * W.ld2;
+  float* dW2 = dW1 + (int64_t)d * la1;
+  MB t;  // only the b x d and b x b panels (LDS) of MB
+  t.K = dW2 + (int64_t)mh * la2;
+  t.Q = t.K + b * d;
+  t.G2 = t.Q + b * d;
+  t.dZ = t.G2 + b * d;
+  t.dG2 = t.dZ + b * d;  // this half's partial of dG2, then the whole dG2 times c, i.e. dYh
+  t.M = t.dG2 + b * d;
+  t.N = t.M + b * b;     // this half's part of tril(Hq Hk^T)
+  t.dM = t.N + b * b;    // this half's part of dM
+  t.dN = t.dM + b * b;
+  float* sc = a.scratch + sh * scratch_floats(d, m, b) + half * split_scratch_floats(d, m, b);
+  float* dAq = sc;
+  float* dHk = dAq + (int64_t)b * mh;
+  float* dG1 = dHk + (int64_t)b * mh;
+  float* dGh = dG1 + (int64_t)b * mh;
+  float* dQp = dGh + (int64_t)b * mh;
+  float* dKp = dQp + (int64_t)b * d;
+  uint64_t* xc = a.xchg + sh * 4 * (int64_t)(b * d);  // [half][parity][b d]
+
+  // the adjoint half: zero (the window that starts the walk) or as the previous window left it
+  float* gW = a.dstate + sh * 2 * dm;
+  if (a.first) {
+    for (int i = tid; i < d * la1; i += BW) dW1[i] = 0.0f;
+    for (int i = tid; i < mh * la2; i += BW) dW2[i] = 0.0f;
+  } else {
+    copy_rows(dW1, la1, gW + u0, m, d, mh);
+    copy_rows(dW2, la2, gW + dm + (int64_t)u0 * d, d, mh, d);
+  }
+
+  const int64_t plane = a.B * a.H * T * d;
+  Rows rw{a.qkv + sh * T * d, a.qkv + plane + sh * T * d, a.qkv + 2 * plane + sh * T * d, T, a.reverse};
+  bool failed = false;  // this thread saw an abort or a time-out
+
+  for (int64_t sg = a.seg_hi; sg >= a.seg_lo; --sg) {
+    const int64_t j0 = sg * C, j1 = min(nmb, j0 + C);
+    const float* seg = a.segst + ((sh * a.seg_count + (sg - a.seg_lo)) * C) * slot;
+    for (int64_t j = j1 - 1; j >= j0; --j) {
+      const int n = (int)min((int64_t)b, T - j * b);
+      const float* sl = seg + (j - j0) * slot;
+      // the slot's panels, this half's columns (row stride m)
+      const float* fq = sl + 2 * dm;
+      const float *A_ = fq + u0, *Hk_ = fq + bm + u0, *S1_ = fq + 2 * bm + u0, *Gh_ = fq + 3 * bm + u0,
+                  *G1_ = fq + 4 * bm + u0;
+      const float* ro = fq + 5 * bm + (int64_t)b * d;  // the read-out: Aq, Hq, GELU'(Aq), M
+      const float *Hq_ = ro + bm + u0, *S1q_ = ro + 2 * bm + u0;
+      // ---- the state half, K and Q rows, G2, M, dZ = tanh(alpha) dY
+      __syncthreads();  // the previous step's last reads of the LDS panels and state
+      copy_rows(W.w1, W.ld1, sl + u0, m, d, mh);
+      copy_rows(W.w2, W.ld2, sl + dm + (int64_t)u0 * d, d, mh, d);
+      load_qkv(t, rw, j * b, n, d, false);
+      copy_rows(t.G2, d, fq + 5 * bm, d, n, d);
+      for (int i = tid; i < b * b; i += BW) t.M[i] = ro[3 * bm + i];
+      for (int i = tid; i < n * d; i += BW) {
+        const int r = i / d, c = i - r * d;
+        const int ch = h * d + c;
+        t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + ch];
+      }
+      __syncthreads();
+      // ---- N (this half) = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
+      rowdot_tril(t.N, b, n, mh, Hq_, m, Hk_, m, 1.0f);
+      rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
+      prod<4, true>(dGh, mh, n, mh, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
+      __syncthreads();
+      // ---- dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dHk = dN^T Hq; dG2 (this half) = -eta N^T dZ
+      if (n % 16 == 0 && mh % 16 == 0 && d % 16 == 0) {  // on the matrix cores (N, dN are 0 above the diagonal)
+        prod_mfma<false, false>(dGh, mh, n, mh, n, t.dN, b, Hk_, m, 1.0f, true, 0);
+        prod_mfma<true, false>(dHk, mh, n, mh, n, t.dN, b, Hq_, m, 1.0f, false, 0);
+        prod_mfma<true, false>(t.dG2, d, n, d, n, t.N, b, t.dZ, d, -eta, false, 0);
+        __syncthreads();
+        for (int i = tid; i < n * mh; i += BW) {
+          const int r = i / mh, c = i - r * mh;
+          dAq[i] = S1q_[(int64_t)r * m + c] * dGh[i];
+        }
+      } else {
+        for (int i = tid; i < n * mh; i += BW) {
+          const int r = i / mh, c = i - r * mh;
+          float v = dGh[i];
+          for (int k = 0; k <= r; ++k) v = fmaf(t.dN[r * b + k], Hk_[(int64_t)k * m + c], v);
+          dAq[i] = S1q_[(int64_t)r * m + c] * v;
+          float w = 0.0f;
+          for (int k = r; k < n; ++k) w = fmaf(t.dN[k * b + r], Hq_[(int64_t)k * m + c], w);
+          dHk[i] = w;
+        }
+        for (int i = tid; i < n * d; i += BW) {
+          const int r = i / d, c = i - r * d;
+          float v = 0.0f;
+          for (int k = r; k < n; ++k) v = fmaf(t.N[k * b + r], t.dZ[k * d + c], v);
+          t.dG2[i] = -eta * v;
+        }
+      }
+      __syncthreads();
+      // ---- dQ (this half) = dAq W1^T; dM (this half) = tril(-eta dAq G1^T); with the adjoint half:
+      //      dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK (this half) = -eta G1 dW1'^T
+      prod<1, true>(dQp, d, n, d, mh, dAq, mh, W.w1, W.ld1, 1.0f, false);
+      rowdot_tril(t.dM, b, n, mh, dAq, mh, G1_, m, -eta, 4);
+      prod<4, true>(dHk, mh, n, mh, d, t.G2, d, dW2, la2, -eta, true, 5);
+      prod<1, false>(t.dG2, d, n, d, mh, Hk_, m, dW2, la2, -eta, true, 5);
+      prod<4, false>(dG1, mh, n, mh, d, t.K, d, dW1, la1, -eta, false, 9);
+      prod<1, true>(dKp, d, n, d, mh, G1_, m, dW1, la1, -eta, false, 9);
+      __syncthreads();
+      // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this half's dM)
+      for (int i = tid; i < n * mh; i += BW) {
+        const int r = i / mh, c = i - r * mh;
+        float v = 0.0f;
+        for (int k = r; k < n; ++k) v = fmaf(t.M[k * b + r], dAq[k * mh + c], v);
+        dG1[i] -= eta * v;
+      }
+      for (int i = tid; i < n * d; i += BW) {
+        const int r = i / d, c = i - r * d;
+        float q = 0.0f, k1 = 0.0f;
+        for (int k = 0; k < n; ++k) {
+          q = fmaf(t.dM[r * b + k], t.K[k * d + c], q);
+          k1 = fmaf(t.dM[k * b + r], t.Q[k * d + c], k1);
+        }
+        dQp[i] += q;
+        dKp[i] += k1;
+      }
+      __syncthreads();
+      // ---- dGh = dG1 * S1; dA (in dG1) = dG1 * Gh * GELU''(A)
+      for (int i = tid; i < n * mh; i += BW) {
+        const int r = i / mh, c = i - r * mh;
+        float g, dg, ddg;
+        gelu3(A_[(int64_t)r * m + c], a.gelu_tanh, &g, &dg, &ddg);
+        const float x = dG1[i];
+        dGh[i] = x * S1_[(int64_t)r * m + c];
+        dG1[i] = x * Gh_[(int64_t)r * m + c] * ddg;
+      }
+      __syncthreads();
+      prod<1, false>(t.dG2, d, n, d, mh, dGh, mh, W.w2, W.ld2, 1.0f, true);  // dG2 (this half) += dGh W2
+      __syncthreads();
+      // ---- dG2 = (half 0's part) + (half 1's part), exchanged; dYh = c dG2 (in dG2's place)
+      {
+        const uint32_t tag = (uint32_t)(j + 1);
+        const int par = (int)(j & 1);
+        uint64_t* mine = xc + (half * 2 + par) * (int64_t)(b * d);
+        const uint64_t* theirs = xc + ((1 - half) * 2 + par) * (int64_t)(b * d);
+        for (int i = tid; i < n * d; i += BW)
+          __hip_atomic_store(mine + i, ((uint64_t)tag << 32) | __float_as_uint(t.dG2[i]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = tid; i < n * d; i += BW) {
+          float other = __uint_as_float(0x7fc00000u);  // NaN unless the partial arrives
+          for (uint32_t spin = 0; !failed; ++spin) {
+            const uint64_t e = __hip_atomic_load(theirs + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(e >> 32) == tag) {
+              other = __uint_as_float((uint32_t)e);
+              break;
+            }
+            if (spin >= kSplitSpinMax) {
+              __hip_atomic_store(a.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              failed = true;
+            } else if ((spin & 15) == 15 &&
+                       __hip_atomic_load(a.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+              failed = true;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          const float own = t.dG2[i];
+          t.dG2[i] = a.gscale * (half == 0 ? own + other : other + own);
+        }
+      }
+      __syncthreads();
+      prod<4, true>(dHk, mh, n, mh, d, t.dG2, d, W.w2, W.ld2, 1.0f, true);  // dHk += dYh W2^T
+      __syncthreads();
+      for (int i = tid; i < n * mh; i += BW) {  // dA += dHk * S1
+        const int r = i / mh, c = i - r * mh;
+        dG1[i] += dHk[i] * S1_[(int64_t)r * m + c];
+      }
+      __syncthreads();
+      prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);  // dK (this half) += dA W1^T
+      __syncthreads();
+      // ---- dQ and dK: this half's parts added into [B, T, 3D] (zeroed before the walk), dV = -dYh
+      //      (half 0); the adjoint half handed to the mini-batch before:
+      //      dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
+      for (int i = tid; i < n * d; i += BW) {
+        const int r = i / d, c = i - r * d;
+        float* row = a.dqkv + ((int64_t)s * T + rw.tok(j * b + r)) * 3 * D + h * d + c;
+        atomicAdd(row, dQp[i]);
+        atomicAdd(row + D, dKp[i]);
+        if (half == 0) row[2 * D] = -t.dG2[i];
+      }
+      Terms u1{2, {t.Q, t.K}, {d, d}, {dAq, dG1}, {mh, mh}};
+      rank_update_any(dW1, la1, d, mh, n, u1, 1.0f);
+      Terms u2{3, {Hq_, dGh, Hk_}, {m, mh, m}, {t.dZ, t.G2, t.dG2}, {d, d, d}};
+      rank_update_any(dW2, la2, mh, d, n, u2, 1.0f);
+    }
+  }
+  __syncthreads();
+  // the adjoint half to the workspace for the next window, or out when the walk reached the start
+  float* o = (a.seg_lo == 0 ? a.dw_seq : a.dstate) + sh * 2 * dm;
+  copy_rows(o + u0, m, dW1, la1, d, mh);
+  copy_rows(o + dm + (int64_t)u0 * d, d, dW2, la2, mh, d);
+}
+
+__global__ void fill_zero_u64_kernel(uint64_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
 // C[M x N] = (accumulate ? C : Cadd or 0) + A B, fp32; A(r, k) = A[r lda + k], or
 // A[k lda + r] when AT; B(k, c) = B[k ldb + c] in fp32 or bf16.  64 x 64 tiles,
 // K-steps of 16, 4 x 4 outputs per thread.
@@ -949,6 +1203,44 @@ hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(scan_fwd_ckpt_kernel, dim3((unsigned)(a.B * a.H)), dim3(BW), lds,
                      s, a);
   return hipGetLastError();
+}
+
+size_t scan_backward_split_lds_bytes(int d, int m, int b) { return sizeof(float) * (size_t)split_lds_floats(d, m, b); }
+
+size_t scan_backward_split_xchg_elems(int64_t B, int H, int d, int b) { return (size_t)(B * H) * 4 * b * d; }
+
+bool scan_backward_split_fits(int64_t B, int H, int d, int m, int b) {
+  if (m % 32 != 0 || d % 16 != 0 || b > 16 || (int64_t)b * d > BW) return false;
+  const size_t lds = scan_backward_split_lds_bytes(d, m, b);
+  if (lds > 160 * 1024 || 2 * split_scratch_floats(d, m, b) > scratch_floats(d, m, b)) return false;
+  int dev = 0, cus = 0, coop = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  if (hipFuncSetAttribute((const void*)scan_backward_split_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess)
+    return false;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_backward_split_kernel, BW, lds) != hipSuccess)
+    return false;
+  return 2 * B * H <= (int64_t)cus * per_cu;
+}
+
+hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_zero_u64_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_backward_split(const BwdArgs& a, hipStream_t s) {
+  const size_t lds = scan_backward_split_lds_bytes(a.d, a.m, a.b);
+  hipError_t e = hipFuncSetAttribute((const void*)scan_backward_split_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  BwdArgs args = a;
+  void* kargs[] = {(void*)&args};
+  return hipLaunchCooperativeKernel((const void*)scan_backward_split_kernel, dim3((unsigned)(2 * a.B * a.H)),
+                                    dim3(BW), kargs, (unsigned)lds, s);
 }
 
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s) {

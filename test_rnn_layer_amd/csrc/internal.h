@@ -118,6 +118,10 @@ struct BwdArgs {
   // 0: one launch walks every segment, replaying each itself (segst: one segment per chain)
   int32_t replayed, first, seg_count;
   int64_t seg_lo, seg_hi;
+  // the split backward scan only: exchange entries (scan_backward_split_xchg_elems, zero before a
+  // direction's walk) and the abort flag; dqkv must be zero before the walk (dQ and dK are added)
+  uint64_t* xchg;
+  uint32_t* abort_flag;
 };
 // LDS bytes of the backward's scan kernels (the forward pass below too): the b x d and
 // b x b panels, and the state when it fits beside them (at most 160 KB); workspace
@@ -141,6 +145,12 @@ hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s);
 size_t scan_replay_f32_slot_elems();
 hipError_t launch_scan_replay_f32(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
+// The replayed windows' walk with each chain's hidden units split over two co-resident workgroups
+// (one cooperative launch of 2 B H workgroups; the state and adjoint halves in LDS).
+bool scan_backward_split_fits(int64_t B, int H, int d, int m, int b);
+size_t scan_backward_split_xchg_elems(int64_t B, int H, int d, int b);
+hipError_t launch_scan_backward_split(const BwdArgs& a, hipStream_t s);
+hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t s);
 // C = (accumulate ? C : Cadd or 0) + A B, fp32 (A [M, K] row-major, or [K, M] when
 // a_transposed; B [K, N] row-major, fp32 or bf16)
 hipError_t launch_gemm_f32(bool a_transposed, bool b_bf16, const float* A, int64_t lda, const void* Bm, int64_t ldb,
