@@ -893,10 +893,10 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   t.K = dW2 + (int64_t)mh * la2;
   t.Q = t.K + b * d;
   t.G2 = t.Q + b * d;
-  t.dZ = t.G2 + b * d;
+  t.M = t.G2 + b * d;
+  t.dZ = t.M + b * b;
   t.dG2 = t.dZ + b * d;  // this half's partial of dG2, then the whole dG2 times c, i.e. dYh
-  t.M = t.dG2 + b * d;
-  t.N = t.M + b * b;     // this half's part of tril(Hq Hk^T)
+  t.N = t.dG2 + b * d;   // this half's part of tril(Hq Hk^T)
   t.dM = t.N + b * b;    // this half's part of dM
   t.dN = t.dM + b * b;
   float* sc = a.scratch + sh * scratch_floats(d, m, b) + half * split_scratch_floats(d, m, b);
@@ -926,6 +926,9 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
     const int64_t j0 = sg * C, j1 = min(nmb, j0 + C);
     const float* seg = a.segst + ((sh * a.seg_count + (sg - a.seg_lo)) * C) * slot;
     for (int64_t j = j1 - 1; j >= j0; --j) {
+      const int64_t mk = (a.seg_hi - sg) * C + (j1 - 1 - j);  // marks: mini-batches of this launch
+      (void)mk;
+      TTT_MARK(g_marks_scan_backward, mk, 0);
       const int n = (int)min((int64_t)b, T - j * b);
       const float* sl = seg + (j - j0) * slot;
       // the slot's panels, this half's columns (row stride m)
@@ -947,11 +950,13 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + ch];
       }
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 1);
       // ---- N (this half) = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
       rowdot_tril(t.N, b, n, mh, Hq_, m, Hk_, m, 1.0f);
       rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
       prod<4, true>(dGh, mh, n, mh, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 2);
       // ---- dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dHk = dN^T Hq; dG2 (this half) = -eta N^T dZ
       if (n % 16 == 0 && mh % 16 == 0 && d % 16 == 0) {  // on the matrix cores (N, dN are 0 above the diagonal)
         prod_mfma<false, false>(dGh, mh, n, mh, n, t.dN, b, Hk_, m, 1.0f, true, 0);
@@ -980,6 +985,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         }
       }
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 3);
       // ---- dQ (this half) = dAq W1^T; dM (this half) = tril(-eta dAq G1^T); with the adjoint half:
       //      dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK (this half) = -eta G1 dW1'^T
       prod<1, true>(dQp, d, n, d, mh, dAq, mh, W.w1, W.ld1, 1.0f, false);
@@ -989,6 +995,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       prod<4, false>(dG1, mh, n, mh, d, t.K, d, dW1, la1, -eta, false, 9);
       prod<1, true>(dKp, d, n, d, mh, G1_, m, dW1, la1, -eta, false, 9);
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 4);
       // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this half's dM)
       for (int i = tid; i < n * mh; i += BW) {
         const int r = i / mh, c = i - r * mh;
@@ -1019,6 +1026,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       __syncthreads();
       prod<1, false>(t.dG2, d, n, d, mh, dGh, mh, W.w2, W.ld2, 1.0f, true);  // dG2 (this half) += dGh W2
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 5);
       // ---- dG2 = (half 0's part) + (half 1's part), exchanged; dYh = c dG2 (in dG2's place)
       {
         const uint32_t tag = (uint32_t)(j + 1);
@@ -1050,6 +1058,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         }
       }
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 6);
       prod<4, true>(dHk, mh, n, mh, d, t.dG2, d, W.w2, W.ld2, 1.0f, true);  // dHk += dYh W2^T
       __syncthreads();
       for (int i = tid; i < n * mh; i += BW) {  // dA += dHk * S1
@@ -1059,6 +1068,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       __syncthreads();
       prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);  // dK (this half) += dA W1^T
       __syncthreads();
+      TTT_MARK(g_marks_scan_backward, mk, 7);
       // ---- dQ and dK: this half's parts added into [B, T, 3D] (zeroed before the walk), dV = -dYh
       //      (half 0); the adjoint half handed to the mini-batch before:
       //      dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh

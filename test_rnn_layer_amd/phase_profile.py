@@ -50,15 +50,15 @@ PHASES = {
         "G1 of this token (its W1 update follows in the next token's exchange)",
         "loop to the next token",
     ],
-    "backward": [
-        "the mini-batch's slot state into LDS, its Q/K/V rows, dZ = tanh(alpha) dY, G2; barrier",
-        "read-out again: M = tril(Q K^T), Aq = Q W1 - eta M G1, Hq, GELU'(Aq)",
-        "N = tril(Hq Hk^T), dN, dZ W2^T; barrier",
-        "dN Hk, dN^T Hq, N^T dZ (matrix cores); barrier; dAq",
-        "dQ = dAq W1^T, dM, the products with the adjoint (dHk, dG2, dG1, dK); barrier",
-        "dG1 -= eta M^T dAq, dQ += dM K, dK += dM^T Q; barrier",
-        "dGh, dA (GELU''); dG2 += dGh W2; dYh; dHk += dYh W2^T; dA += dHk S1; dK += dA W1^T (five barriers)",
-        "dQ|dK|dV stores, the rank-16 adjoint updates; barrier; loop",
+    "backward": [  # the walk split over two workgroups per chain (bidir307k's shape)
+        "barrier; the state half into LDS, K/Q rows, G2, M, dZ = tanh(alpha) dY; barrier",
+        "N (this half), dN, dZ W2^T; barrier",
+        "dN Hk, dN^T Hq, N^T dZ; barrier; dAq",
+        "dQ, dM (this half), the products with the adjoint half (dHk, dG2, dG1, dK); barrier",
+        "dG1 -= eta M^T dAq, dQ += dM K, dK += dM^T Q; dGh, dA (GELU''); dG2 += dGh W2 (three barriers)",
+        "dG2's partials exchanged with the other half (publish, poll); barrier",
+        "dHk += dYh W2^T; dA += dHk S1; dK += dA W1^T (three barriers)",
+        "dQ, dK atomics and dV stores, the rank-16 updates of the adjoint half; loop",
     ],
 }
 ENTRY = {"mfma": "ttt_phase_marks_scan_mfma", "coop": "ttt_phase_marks_scan_coop",
