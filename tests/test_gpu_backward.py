@@ -180,6 +180,28 @@ def test_backward_f32_matrix_core_forward_properties():
     assert not torch.any(c["dX"][:, P:]) and torch.any(c["dX"][:, :P])
 
 
+def test_backward_many_chains_one_workgroup_walk():
+    """B H = 144 chains at the bidir307k head shape, twice as many workgroups as fit co-resident:
+    the walk over the replayed windows then runs on one workgroup per chain (the adjoint in the
+    workspace) instead of two.  dY on heads 0 and H-1 of every sequence (three checkpoint segments
+    and a ragged tail); the oracle on those heads gives every gradient."""
+    from test_rnn_layer_amd import _lib
+    wl = W.WORKLOADS["bidir307k"].replace(B=3, T=1100, seg_len=0, name="many_chains")
+    heads = [0, wl.H - 1]
+    print(f"[backward many chains] B{wl.B} H{wl.H} T{wl.T}, dY on heads {heads}", flush=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    dy = W.make_dy(wl, heads=heads)
+    g = _lib.backward(_cfg(wl), dev["X"], dev["theta"], dev["W1_0"], dev["W2_0"], dev["alpha_f"],
+                      torch.from_numpy(dy).cuda())
+    torch.cuda.synchronize()
+    f64 = f64_inputs(wl, inp)
+    ref = BO.ttt_mlp_backward(f64["X"], f64["theta"], f64["W1_0"], f64["W2_0"], f64["alpha_f"], dy.astype(np.float64),
+                              eta=wl.eta, b=wl.b, loss=wl.loss, gelu_form=wl.gelu, heads=heads)
+    for k in ["dX", "dtheta", "dW1_0", "dW2_0", "dalpha"]:
+        _check(k, from_device(g[k]), ref[k])
+
+
 def test_backward_no_tokens():
     from test_rnn_layer_amd import _lib
     wl = CASES["f32_b1"].replace(T=0)
