@@ -558,8 +558,10 @@ struct BwdPlan {
   size_t dqkv_off, dqkv2_off, z_off[2], y_off, xp_off, dxp_off, ckpt_off[2], segst_off, dstate_off, scratch_off,
       dwseq_off,
       dal_off, total;
-  // the split backward scan's exchange entries, then its abort flag (0 when it does not apply)
-  size_t bxchg_off = 0;
+  // the split backward scan: its workgroups per chain (4, 2, or 0: one workgroup per chain), its
+  // exchange entries then its abort flag, and with four its second [B, T, 2D] dQ|dK buffer
+  int split = 0;
+  size_t bxchg_off = 0, dqkvb_off = 0;
   // fp32 copies of bf16 operands of the gradient GEMMs (theta, X, X'; unused with fp32 io),
   // and the two rocBLAS workspace slices (caller's stream, side stream)
   size_t th32_off, x32_off, xp32_off, blas_off[2];
@@ -612,8 +614,15 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   p->dstate_off = take(BH * st2);
   p->scratch_off = take(BH * ttt::scan_backward_scratch_elems(c->d, c->m, c->b) * sizeof(float));
   p->dwseq_off = take(BH * st2);
-  if (bwd_f32mfma(c) && ttt::scan_backward_split_fits(c->B, c->H, c->d, c->m, c->b))
-    p->bxchg_off = take(ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b) * sizeof(uint64_t) + 256);
+  if (bwd_f32mfma(c)) {
+    p->split = ttt::scan_backward_split_fits(c->B, c->H, c->d, c->m, c->b, 4)   ? 4
+               : ttt::scan_backward_split_fits(c->B, c->H, c->d, c->m, c->b, 2) ? 2
+                                                                                 : 0;
+    if (p->split)
+      p->bxchg_off =
+          take(ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b, p->split) * sizeof(uint64_t) + 256);
+    if (p->split == 4) p->dqkvb_off = take(2 * BTD * sizeof(float));
+  }
   p->dal_off = take(ttt::dalpha_partial_elems((int)D) * sizeof(float));
   const bool bf16 = c->io_dtype == TTT_BF16;
   p->th32_off = bf16 ? take(3 * D * D * sizeof(float)) : 0;
@@ -767,13 +776,16 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* x
     ba.replayed = 1;
     // the split walk (two workgroups per chain) where its workgroups fit co-resident: dQ and dK
     // are added into dqkv, so it starts from zero, and so do the exchange entries and abort flag
-    const bool split = bp.bxchg_off != 0;
+    const bool split = bp.split != 0;
     if (split) {
-      const int64_t nx = (int64_t)ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b);
+      const int64_t nx = (int64_t)ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b, bp.split);
+      ba.split = bp.split;
       ba.xchg = (uint64_t*)(ws + bp.bxchg_off);
       ba.abort_flag = (uint32_t*)(ba.xchg + nx);
+      ba.dqkv_b = bp.split == 4 ? (float*)(ws + bp.dqkvb_off) : nullptr;
       e = ttt::launch_zero_u64(ba.xchg, nx + 1, s);
       if (e == hipSuccess) e = ttt::launch_zero_u64((uint64_t*)dqkv, 3 * BT * D / 2, s);
+      if (e == hipSuccess && ba.dqkv_b) e = ttt::launch_zero_u64((uint64_t*)ba.dqkv_b, BT * D, s);
       if (e != hipSuccess) return fail(TTT_ERR_HIP, "clearing launch: %s", hipGetErrorString(e));
     }
     for (int64_t hi = nseg - 1; hi >= 0; hi -= kReplayWindow) {
@@ -788,6 +800,10 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* x
         return split ? ttt::launch_scan_backward_split(ba, s) : ttt::launch_scan_backward(ba, s);
       });
       if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
+    }
+    if (ba.dqkv_b) {  // the four-part walk's parts 2 and 3
+      e = ttt::launch_add_dqk(dqkv, ba.dqkv_b, BT, (int)D, s);
+      if (e != hipSuccess) return fail(TTT_ERR_HIP, "dQ|dK sum launch: %s", hipGetErrorString(e));
     }
   } else {
     e = ov.side ? hipEventRecord(ov.ev_ready, s) : hipSuccess;

@@ -836,41 +836,44 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Backward scan over replayed windows with each chain's hidden units split over
-// two workgroups of one cooperative launch (the notes page's on-chip tensor
+// S = 2 or 4 workgroups of one cooperative launch (the notes page's on-chip tensor
 // parallel: the state sharded over CUs, an all-reduce between them).  Workgroup
-// half (0 or 1) of chain sh takes units [half m/2, half m/2 + m/2): its half of
-// the mini-batch's state (W1 columns, W2 rows) and its half of the adjoint, both
-// in LDS (the adjoint goes to the workspace between launches), the b x d and
-// b x b panels in LDS, its b x m/2 panels in the workspace.  Every product over
-// units splits into the two halves' partial sums.  Those that only feed outputs
-// (dQ, dK, and dM, linear in them) are added into dQ|dK|dV by float atomics: two
-// addends onto zero, whose sum does not depend on their order.  The one that feeds
-// the rest of the step, dG2 = -eta N^T dZ - eta Hk dW2' + dGh W2 (N too is a sum
-// over units), is exchanged: each half publishes its partial as tagged 64-bit
-// device-scope stores (the mini-batch index + 1 in the high word, double-buffered
-// by its parity) and polls the other's; both add them as (half 0) + (half 1).
+// part p (0 .. S-1) of chain sh takes units [p m/S, (p+1) m/S): its part of the
+// mini-batch's state (W1 columns, W2 rows) and its part of the adjoint, both in
+// LDS (the adjoint goes to the workspace between launches), the b x d and b x b
+// panels in LDS, its b x m/S panels in the workspace.  Every product over units
+// splits into the parts' partial sums.  Those that only feed outputs (dQ, dK, and
+// dM, linear in them) are added by float atomics into buffers that each take two
+// addends onto zero, so that the sums do not depend on their order: parts 0 and 1
+// into dQ|dK|dV, parts 2 and 3 into a second [B, T, 2D] buffer added to it after
+// the walk.  The one that feeds the rest of the step, dG2 = -eta N^T dZ - eta Hk
+// dW2' + dGh W2 (N too is a sum over units), is exchanged: each part publishes its
+// partial as tagged 64-bit device-scope stores (the mini-batch index + 1 in the
+// high word, double-buffered by its parity) and polls the others'; all add them in
+// the order of the parts.
 // Polls are bounded: a workgroup that waits past the spin limit raises the abort
 // flag, which every poll checks, and takes NaN for the missing partial, so a lost
 // peer shows as NaN gradients rather than a hang.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kSplitSpinMax = 1u << 20;
 
-// LDS floats of a split workgroup: the state half and the adjoint half (W1 columns as
-// [d][m/2 + 4], W2 rows as [m/2][d + 4]), then the b x d and b x b panels
-__host__ __device__ constexpr int64_t split_lds_floats(int d, int m, int b) {
-  return 2 * ((int64_t)d * (m / 2 + 4) + (int64_t)(m / 2) * (d + 4)) + panel_lds_floats(d, b);
+// LDS floats of a split workgroup: its part of the state and of the adjoint (W1 columns as
+// [d][m/S + 4], W2 rows as [m/S][d + 4]), then the b x d and b x b panels
+__host__ __device__ constexpr int64_t split_lds_floats(int d, int m, int b, int S) {
+  return 2 * ((int64_t)d * (m / S + 4) + (int64_t)(m / S) * (d + 4)) + panel_lds_floats(d, b);
 }
-// workspace floats of a split workgroup: its b x m/2 panels dAq, dHk, dG1 (then dA), dGh,
+// workspace floats of a split workgroup: its b x m/S panels dAq, dHk, dG1 (then dA), dGh,
 // and its dQ and dK partials (b x d)
-__host__ __device__ constexpr int64_t split_scratch_floats(int d, int m, int b) {
-  return 4LL * b * (m / 2) + 2LL * b * d;
+__host__ __device__ constexpr int64_t split_scratch_floats(int d, int m, int b, int S) {
+  return 4LL * b * (m / S) + 2LL * b * d;
 }
 
+template <int S>
 __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int d = a.d, m = a.m, b = a.b, mh = m / 2, tid = threadIdx.x;
+  const int d = a.d, m = a.m, b = a.b, mh = m / S, tid = threadIdx.x;  // mh: this part's units
   const int64_t BH = a.B * a.H;
-  const int half = blockIdx.x >= BH ? 1 : 0;
+  const int half = (int)(blockIdx.x / BH);             // the part
   const int64_t sh = (int64_t)blockIdx.x - half * BH;  // sequence * H + head
   const int s = (int)(sh / a.H), h = (int)(sh % a.H);
   const int u0 = half * mh;
@@ -881,12 +884,12 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   const int64_t nmb = (T + b - 1) / b;
   const int C = a.ckpt_every;
 
-  St W;  // the mini-batch's state, this half
+  St W;  // the mini-batch's state, this part
   W.ld1 = mh + 4;
   W.ld2 = d + 4;
   W.w1 = lds;
   W.w2 = W.w1 + (int64_t)d * W.ld1;
-  const int la1 = mh + 4, la2 = d + 4;  // the adjoint half, same layout
+  const int la1 = mh + 4, la2 = d + 4;  // the adjoint's part, same layout
   float* dW1 = W.w2 + (int64_t)mh * W.ld2;
   float* dW2 = dW1 + (int64_t)d * la1;
   MB t;  // only the b x d and b x b panels (LDS) of MB
@@ -895,20 +898,20 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   t.G2 = t.Q + b * d;
   t.M = t.G2 + b * d;
   t.dZ = t.M + b * b;
-  t.dG2 = t.dZ + b * d;  // this half's partial of dG2, then the whole dG2 times c, i.e. dYh
-  t.N = t.dG2 + b * d;   // this half's part of tril(Hq Hk^T)
-  t.dM = t.N + b * b;    // this half's part of dM
+  t.dG2 = t.dZ + b * d;  // this part's partial of dG2, then the whole dG2 times c, i.e. dYh
+  t.N = t.dG2 + b * d;   // this part's part of tril(Hq Hk^T)
+  t.dM = t.N + b * b;    // this part's part of dM
   t.dN = t.dM + b * b;
-  float* sc = a.scratch + sh * scratch_floats(d, m, b) + half * split_scratch_floats(d, m, b);
+  float* sc = a.scratch + sh * scratch_floats(d, m, b) + half * split_scratch_floats(d, m, b, S);
   float* dAq = sc;
   float* dHk = dAq + (int64_t)b * mh;
   float* dG1 = dHk + (int64_t)b * mh;
   float* dGh = dG1 + (int64_t)b * mh;
   float* dQp = dGh + (int64_t)b * mh;
   float* dKp = dQp + (int64_t)b * d;
-  uint64_t* xc = a.xchg + sh * 4 * (int64_t)(b * d);  // [half][parity][b d]
+  uint64_t* xc = a.xchg + sh * 2 * S * (int64_t)(b * d);  // [part][parity][b d]
 
-  // the adjoint half: zero (the window that starts the walk) or as the previous window left it
+  // the adjoint's part: zero (the window that starts the walk) or as the previous window left it
   float* gW = a.dstate + sh * 2 * dm;
   if (a.first) {
     for (int i = tid; i < d * la1; i += BW) dW1[i] = 0.0f;
@@ -931,7 +934,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       TTT_MARK(g_marks_scan_backward, mk, 0);
       const int n = (int)min((int64_t)b, T - j * b);
       const float* sl = seg + (j - j0) * slot;
-      // the slot's panels, this half's columns (row stride m)
+      // the slot's panels, this part's columns (row stride m)
       const float* fq = sl + 2 * dm;
       const float *A_ = fq + u0, *Hk_ = fq + bm + u0, *S1_ = fq + 2 * bm + u0, *Gh_ = fq + 3 * bm + u0,
                   *G1_ = fq + 4 * bm + u0;
@@ -951,13 +954,13 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       }
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 1);
-      // ---- N (this half) = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
+      // ---- N (this part) = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
       rowdot_tril(t.N, b, n, mh, Hq_, m, Hk_, m, 1.0f);
       rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
       prod<4, true>(dGh, mh, n, mh, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 2);
-      // ---- dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dHk = dN^T Hq; dG2 (this half) = -eta N^T dZ
+      // ---- dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dHk = dN^T Hq; dG2 (this part) = -eta N^T dZ
       if (n % 16 == 0 && mh % 16 == 0 && d % 16 == 0) {  // on the matrix cores (N, dN are 0 above the diagonal)
         prod_mfma<false, false>(dGh, mh, n, mh, n, t.dN, b, Hk_, m, 1.0f, true, 0);
         prod_mfma<true, false>(dHk, mh, n, mh, n, t.dN, b, Hq_, m, 1.0f, false, 0);
@@ -986,8 +989,8 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       }
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 3);
-      // ---- dQ (this half) = dAq W1^T; dM (this half) = tril(-eta dAq G1^T); with the adjoint half:
-      //      dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK (this half) = -eta G1 dW1'^T
+      // ---- dQ (this part) = dAq W1^T; dM (this part) = tril(-eta dAq G1^T); with the adjoint's part:
+      //      dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK (this part) = -eta G1 dW1'^T
       prod<1, true>(dQp, d, n, d, mh, dAq, mh, W.w1, W.ld1, 1.0f, false);
       rowdot_tril(t.dM, b, n, mh, dAq, mh, G1_, m, -eta, 4);
       prod<4, true>(dHk, mh, n, mh, d, t.G2, d, dW2, la2, -eta, true, 5);
@@ -996,7 +999,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       prod<1, true>(dKp, d, n, d, mh, G1_, m, dW1, la1, -eta, false, 9);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 4);
-      // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this half's dM)
+      // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this part's dM)
       for (int i = tid; i < n * mh; i += BW) {
         const int r = i / mh, c = i - r * mh;
         float v = 0.0f;
@@ -1024,37 +1027,46 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         dG1[i] = x * Gh_[(int64_t)r * m + c] * ddg;
       }
       __syncthreads();
-      prod<1, false>(t.dG2, d, n, d, mh, dGh, mh, W.w2, W.ld2, 1.0f, true);  // dG2 (this half) += dGh W2
+      prod<1, false>(t.dG2, d, n, d, mh, dGh, mh, W.w2, W.ld2, 1.0f, true);  // dG2 (this part) += dGh W2
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 5);
-      // ---- dG2 = (half 0's part) + (half 1's part), exchanged; dYh = c dG2 (in dG2's place)
+      // ---- dG2 = the parts' partials added in the parts' order, exchanged; dYh = c dG2 (in dG2's
+      //      place)
       {
         const uint32_t tag = (uint32_t)(j + 1);
         const int par = (int)(j & 1);
         uint64_t* mine = xc + (half * 2 + par) * (int64_t)(b * d);
-        const uint64_t* theirs = xc + ((1 - half) * 2 + par) * (int64_t)(b * d);
         for (int i = tid; i < n * d; i += BW)
           __hip_atomic_store(mine + i, ((uint64_t)tag << 32) | __float_as_uint(t.dG2[i]), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         for (int i = tid; i < n * d; i += BW) {
-          float other = __uint_as_float(0x7fc00000u);  // NaN unless the partial arrives
-          for (uint32_t spin = 0; !failed; ++spin) {
-            const uint64_t e = __hip_atomic_load(theirs + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((uint32_t)(e >> 32) == tag) {
-              other = __uint_as_float((uint32_t)e);
-              break;
+          float sum = 0.0f;
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            float v = __uint_as_float(0x7fc00000u);  // NaN unless the partial arrives
+            if (q == half) {
+              v = t.dG2[i];
+            } else {
+              const uint64_t* theirs = xc + (q * 2 + par) * (int64_t)(b * d);
+              for (uint32_t spin = 0; !failed; ++spin) {
+                const uint64_t e = __hip_atomic_load(theirs + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((uint32_t)(e >> 32) == tag) {
+                  v = __uint_as_float((uint32_t)e);
+                  break;
+                }
+                if (spin >= kSplitSpinMax) {
+                  __hip_atomic_store(a.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  failed = true;
+                } else if ((spin & 15) == 15 &&
+                           __hip_atomic_load(a.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                  failed = true;
+                }
+                __builtin_amdgcn_s_sleep(1);
+              }
             }
-            if (spin >= kSplitSpinMax) {
-              __hip_atomic_store(a.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              failed = true;
-            } else if ((spin & 15) == 15 &&
-                       __hip_atomic_load(a.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-              failed = true;
-            }
-            __builtin_amdgcn_s_sleep(1);
+            sum = q == 0 ? v : sum + v;
           }
-          const float own = t.dG2[i];
-          t.dG2[i] = a.gscale * (half == 0 ? own + other : other + own);
+          t.dG2[i] = a.gscale * sum;
         }
       }
       __syncthreads();
@@ -1066,15 +1078,16 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         dG1[i] += dHk[i] * S1_[(int64_t)r * m + c];
       }
       __syncthreads();
-      prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);  // dK (this half) += dA W1^T
+      prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);  // dK (this part) += dA W1^T
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 7);
-      // ---- dQ and dK: this half's parts added into [B, T, 3D] (zeroed before the walk), dV = -dYh
-      //      (half 0); the adjoint half handed to the mini-batch before:
-      //      dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
+      // ---- dQ and dK: this part's sums added into [B, T, 3D] (parts 0, 1) or the [B, T, 2D] buffer
+      //      (parts 2, 3), both zeroed before the walk; dV = -dYh (part 0); the adjoint's part
+      //      handed to the mini-batch before: dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
       for (int i = tid; i < n * d; i += BW) {
         const int r = i / d, c = i - r * d;
-        float* row = a.dqkv + ((int64_t)s * T + rw.tok(j * b + r)) * 3 * D + h * d + c;
+        const int64_t tr = (int64_t)s * T + rw.tok(j * b + r);
+        float* row = half < 2 ? a.dqkv + tr * 3 * D + h * d + c : a.dqkv_b + tr * 2 * D + h * d + c;
         atomicAdd(row, dQp[i]);
         atomicAdd(row + D, dKp[i]);
         if (half == 0) row[2 * D] = -t.dG2[i];
@@ -1086,7 +1099,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // the adjoint half to the workspace for the next window, or out when the walk reached the start
+  // the adjoint's part to the workspace for the next window, or out when the walk reached the start
   float* o = (a.seg_lo == 0 ? a.dw_seq : a.dstate) + sh * 2 * dm;
   copy_rows(o + u0, m, dW1, la1, d, mh);
   copy_rows(o + dm + (int64_t)u0 * d, d, dW2, la2, mh, d);
@@ -1215,24 +1228,33 @@ hipError_t launch_scan_fwd_ckpt(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t scan_backward_split_lds_bytes(int d, int m, int b) { return sizeof(float) * (size_t)split_lds_floats(d, m, b); }
+size_t scan_backward_split_lds_bytes(int d, int m, int b, int S) {
+  return sizeof(float) * (size_t)split_lds_floats(d, m, b, S);
+}
 
-size_t scan_backward_split_xchg_elems(int64_t B, int H, int d, int b) { return (size_t)(B * H) * 4 * b * d; }
+size_t scan_backward_split_xchg_elems(int64_t B, int H, int d, int b, int S) {
+  return (size_t)(B * H) * 2 * S * b * d;
+}
 
-bool scan_backward_split_fits(int64_t B, int H, int d, int m, int b) {
-  if (m % 32 != 0 || d % 16 != 0 || b > 16 || (int64_t)b * d > BW) return false;
-  const size_t lds = scan_backward_split_lds_bytes(d, m, b);
-  if (lds > 160 * 1024 || 2 * split_scratch_floats(d, m, b) > scratch_floats(d, m, b)) return false;
+const void* split_kernel_fn(int S) {
+  return S == 4 ? (const void*)scan_backward_split_kernel<4> : (const void*)scan_backward_split_kernel<2>;
+}
+
+bool scan_backward_split_fits(int64_t B, int H, int d, int m, int b, int S) {
+  if ((S != 2 && S != 4) || m % (16 * S) != 0 || d % 16 != 0 || b > 16 || (int64_t)b * d > BW) return false;
+  const size_t lds = scan_backward_split_lds_bytes(d, m, b, S);
+  if (lds > 160 * 1024 || S * split_scratch_floats(d, m, b, S) > scratch_floats(d, m, b)) return false;
   int dev = 0, cus = 0, coop = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  if (hipFuncSetAttribute((const void*)scan_backward_split_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
+  if (hipFuncSetAttribute(split_kernel_fn(S), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return false;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_backward_split_kernel, BW, lds) != hipSuccess)
-    return false;
-  return 2 * B * H <= (int64_t)cus * per_cu;
+  const hipError_t e =
+      S == 4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_backward_split_kernel<4>, BW, lds)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_backward_split_kernel<2>, BW, lds);
+  if (e != hipSuccess) return false;
+  return S * B * H <= (int64_t)cus * per_cu;
 }
 
 hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t s) {
@@ -1243,14 +1265,30 @@ hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_scan_backward_split(const BwdArgs& a, hipStream_t s) {
-  const size_t lds = scan_backward_split_lds_bytes(a.d, a.m, a.b);
-  hipError_t e = hipFuncSetAttribute((const void*)scan_backward_split_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (a.split != 2 && a.split != 4) return hipErrorInvalidValue;
+  const size_t lds = scan_backward_split_lds_bytes(a.d, a.m, a.b, a.split);
+  hipError_t e = hipFuncSetAttribute(split_kernel_fn(a.split), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   BwdArgs args = a;
   void* kargs[] = {(void*)&args};
-  return hipLaunchCooperativeKernel((const void*)scan_backward_split_kernel, dim3((unsigned)(2 * a.B * a.H)),
-                                    dim3(BW), kargs, (unsigned)lds, s);
+  return hipLaunchCooperativeKernel(split_kernel_fn(a.split), dim3((unsigned)(a.split * a.B * a.H)), dim3(BW), kargs,
+                                    (unsigned)lds, s);
+}
+
+// dQ|dK columns of dqkv [rows, 3D] += buf [rows, 2D] (the four-part walk's second buffer)
+__global__ void add_dqk_kernel(float* dqkv, const float* buf, int64_t rows, int D) {
+  const int64_t n = rows * 2 * D, stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / (2 * D), c = i - r * 2 * D;
+    dqkv[r * 3 * D + c] += buf[i];
+  }
+}
+
+hipError_t launch_add_dqk(float* dqkv, const float* buf, int64_t rows, int D, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t n = rows * 2 * D, blocks = std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(add_dqk_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dqkv, buf, rows, D);
+  return hipGetLastError();
 }
 
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s) {

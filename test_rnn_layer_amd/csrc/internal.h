@@ -122,6 +122,8 @@ struct BwdArgs {
   // direction's walk) and the abort flag; dqkv must be zero before the walk (dQ and dK are added)
   uint64_t* xchg;
   uint32_t* abort_flag;
+  int32_t split;   // workgroups per chain: 2 or 4
+  float* dqkv_b;   // four parts: [B, T, 2D], zero before the walk, added to dqkv's dQ|dK after it
 };
 // LDS bytes of the backward's scan kernels (the forward pass below too): the b x d and
 // b x b panels, and the state when it fits beside them (at most 160 KB); workspace
@@ -147,9 +149,10 @@ hipError_t launch_scan_replay_f32(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
 // The replayed windows' walk with each chain's hidden units split over two co-resident workgroups
 // (one cooperative launch of 2 B H workgroups; the state and adjoint halves in LDS).
-bool scan_backward_split_fits(int64_t B, int H, int d, int m, int b);
-size_t scan_backward_split_xchg_elems(int64_t B, int H, int d, int b);
+bool scan_backward_split_fits(int64_t B, int H, int d, int m, int b, int S);
+size_t scan_backward_split_xchg_elems(int64_t B, int H, int d, int b, int S);
 hipError_t launch_scan_backward_split(const BwdArgs& a, hipStream_t s);
+hipError_t launch_add_dqk(float* dqkv, const float* buf, int64_t rows, int D, hipStream_t s);
 hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t s);
 // C = (accumulate ? C : Cadd or 0) + A B, fp32 (A [M, K] row-major, or [K, M] when
 // a_transposed; B [K, N] row-major, fp32 or bf16)

@@ -180,13 +180,15 @@ def test_backward_f32_matrix_core_forward_properties():
     assert not torch.any(c["dX"][:, P:]) and torch.any(c["dX"][:, :P])
 
 
-def test_backward_many_chains_one_workgroup_walk():
-    """B H = 144 chains at the bidir307k head shape, twice as many workgroups as fit co-resident:
-    the walk over the replayed windows then runs on one workgroup per chain (the adjoint in the
-    workspace) instead of two.  dY on heads 0 and H-1 of every sequence (three checkpoint segments
-    and a ragged tail); the oracle on those heads gives every gradient."""
+@pytest.mark.parametrize("B", [2, 3])
+def test_backward_many_chains(B):
+    """B H chains at the bidir307k head shape.  Four workgroups per chain fit co-resident up to 64
+    chains (a CU each); at B = 2 (96 chains) the walk over the replayed windows runs on two
+    workgroups per chain, at B = 3 (144 chains) on one (the adjoint in the workspace).  dY on heads
+    0 and H-1 of every sequence (three checkpoint segments and a ragged tail); the oracle on those
+    heads gives every gradient."""
     from test_rnn_layer_amd import _lib
-    wl = W.WORKLOADS["bidir307k"].replace(B=3, T=1100, seg_len=0, name="many_chains")
+    wl = W.WORKLOADS["bidir307k"].replace(B=B, T=1100, seg_len=0, name="many_chains")
     heads = [0, wl.H - 1]
     print(f"[backward many chains] B{wl.B} H{wl.H} T{wl.T}, dY on heads {heads}", flush=True)
     inp = W.make_inputs(wl)
