@@ -857,15 +857,17 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 constexpr uint32_t kSplitSpinMax = 1u << 20;
 
-// LDS floats of a split workgroup: its part of the state and of the adjoint (W1 columns as
-// [d][m/S + 4], W2 rows as [m/S][d + 4]), then the b x d and b x b panels
-__host__ __device__ constexpr int64_t split_lds_floats(int d, int m, int b, int S) {
-  return 2 * ((int64_t)d * (m / S + 4) + (int64_t)(m / S) * (d + 4)) + panel_lds_floats(d, b);
-}
-// workspace floats of a split workgroup: its b x m/S panels dAq, dHk, dG1 (then dA), dGh,
-// and its dQ and dK partials (b x d)
+// floats of a split workgroup's scratch: its b x m/S panels dAq, dHk, dG1 (then dA), dGh, and
+// its dQ and dK partials (b x d); in LDS with four parts, in the workspace with two
 __host__ __device__ constexpr int64_t split_scratch_floats(int d, int m, int b, int S) {
   return 4LL * b * (m / S) + 2LL * b * d;
+}
+// LDS floats of a split workgroup: its part of the state and of the adjoint (W1 columns as
+// [d][m/S + 4], W2 rows as [m/S][d + 4]), the b x d and b x b panels, and with four parts its
+// scratch
+__host__ __device__ constexpr int64_t split_lds_floats(int d, int m, int b, int S) {
+  return 2 * ((int64_t)d * (m / S + 4) + (int64_t)(m / S) * (d + 4)) + panel_lds_floats(d, b) +
+         (S == 4 ? split_scratch_floats(d, m, b, S) : 0);
 }
 
 template <int S>
@@ -902,7 +904,8 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   t.N = t.dG2 + b * d;   // this part's part of tril(Hq Hk^T)
   t.dM = t.N + b * b;    // this part's part of dM
   t.dN = t.dM + b * b;
-  float* sc = a.scratch + sh * scratch_floats(d, m, b) + half * split_scratch_floats(d, m, b, S);
+  float* sc = S == 4 ? t.dN + b * b  // LDS, after the panels
+                     : a.scratch + sh * scratch_floats(d, m, b) + half * split_scratch_floats(d, m, b, S);
   float* dAq = sc;
   float* dHk = dAq + (int64_t)b * mh;
   float* dG1 = dHk + (int64_t)b * mh;
