@@ -50,15 +50,15 @@ PHASES = {
         "G1 of this token (its W1 update follows in the next token's exchange)",
         "loop to the next token",
     ],
-    "backward": [  # the walk split over two workgroups per chain (bidir307k's shape)
-        "barrier; the state half into LDS, K/Q rows, G2, M, dZ = tanh(alpha) dY; barrier",
-        "N (this half), dN, dZ W2^T; barrier",
+    "backward": [  # the walk split over several workgroups per chain (bidir307k's shape: four)
+        "barrier; the state part into LDS, K/Q rows, G2, M, dZ = tanh(alpha) dY; barrier",
+        "N (this part), dN, dZ W2^T; barrier",
         "dN Hk, dN^T Hq, N^T dZ; barrier; dAq",
-        "dQ, dM (this half), the products with the adjoint half (dHk, dG2, dG1, dK); barrier",
+        "dQ, dM (this part), the products with the adjoint part (dHk, dG2, dG1, dK); barrier",
         "dG1 -= eta M^T dAq, dQ += dM K, dK += dM^T Q; dGh, dA (GELU''); dG2 += dGh W2 (three barriers)",
-        "dG2's partials exchanged with the other half (publish, poll); barrier",
+        "dG2's partials exchanged with the other parts (publish, poll); barrier",
         "dHk += dYh W2^T; dA += dHk S1; dK += dA W1^T (three barriers)",
-        "dQ, dK atomics and dV stores, the rank-16 updates of the adjoint half; loop",
+        "dQ, dK atomics and dV stores, the rank-16 updates of the adjoint part; loop",
     ],
 }
 ENTRY = {"mfma": "ttt_phase_marks_scan_mfma", "coop": "ttt_phase_marks_scan_coop",
