@@ -372,8 +372,9 @@ def summarize_backward(d: str, out_md: str | None = None):
         "(projection, then the scan that keeps a checkpoint every 32 mini-batches: `scan_fwd_f32_kernel<false>`, "
         "fp32 matrix cores), then per direction windows of 4 checkpoint segments from the last, each replayed "
         "(`scan_fwd_f32_kernel<true>`, one workgroup per head and segment) and then walked by the backward scan "
-        "(`scan_backward_split_kernel`, two workgroups per head, one cooperative launch per window; a clearing "
-        "kernel zeroes dQ|dK|dV and the exchange entries per direction), the dalpha reduction and the two "
+        "(`scan_backward_split_kernel`, four workgroups per head, one cooperative launch per window; a clearing "
+        "kernel zeroes dQ|dK|dV, the second dQ|dK buffer and the exchange entries per direction, a small kernel "
+        "adds the second buffer in after the walk), the dalpha reduction and the two "
         "gradient GEMMs (dX, dθ; rocBLAS), all on one stream.", "",
         "Commands (repo root, MI355X):", "",
         f"    mkdir -p {d} && rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
