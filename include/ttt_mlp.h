@@ -227,7 +227,10 @@ int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* th
  * steps: both fp32, in different summation orders), then the backward scan, which
  * replays one segment of 32 mini-batches at a time from its checkpoint and
  * walks it backwards carrying the gradient of the state, then two GEMMs:
- * dX = dY + [dQ dK dV] theta and dtheta = [dQ dK dV]^T X.
+ * dX = dY + [dQ dK dV] theta and dtheta = [dQ dK dV]^T X.  With bf16 io (X and
+ * theta exact bf16 numbers) the fp32 [dQ dK dV] is split exactly into three bf16
+ * parts whose sum it is, and the GEMMs run on the bf16 matrix cores with fp32
+ * accumulation (every product exact); with fp32 io they are fp32 GEMMs.
  * Workspace: ttt_mlp_backward_workspace_size (bidir = 0 or 1).
  */
 int32_t ttt_mlp_backward_workspace_size(const ttt_mlp_config* cfg, int32_t bidir, size_t* bytes);
@@ -241,10 +244,12 @@ int32_t ttt_mlp_backward(const ttt_mlp_config* cfg, const void* X, const void* t
 /* The bidirectional layer (as ttt_mlp_bidir: X' is rounded to io_dtype and its
  * rounding is passed through unchanged): dX, dtheta and dW*_0 collect both
  * directions; dalpha_f and dalpha_b are the two gates' gradients.  The reversed
- * pass's dtheta GEMM runs on the library's second stream of the device, beside
- * the forward pass's backward scan, ordered by events after this call's earlier
- * work on `stream` and before its later work (its dQ|dK|dV get a buffer of their
- * own in the workspace); calls on one device are serialised while they enqueue. */
+ * pass's dtheta GEMM is deferred: with the fp32 matrix-core forward pass it runs
+ * on `stream` before the forward pass's backward scan; otherwise on the library's
+ * second stream of the device, beside that scan, ordered by events after this
+ * call's earlier work on `stream` and before its later work (its dQ|dK|dV get a
+ * buffer of their own in the workspace); calls on one device are serialised
+ * while they enqueue. */
 int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const void* theta_qkv, const float* W1_0,
                                const float* W2_0, const float* alpha_f, const float* alpha_b, const float* dY,
                                float* dX, float* dtheta, float* dW1_0, float* dW2_0, float* dalpha_f,

@@ -562,9 +562,11 @@ struct BwdPlan {
   // exchange entries then its abort flag, and with four its second [B, T, 2D] dQ|dK buffer
   int split = 0;
   size_t bxchg_off = 0, dqkvb_off = 0;
-  // fp32 copies of bf16 operands of the gradient GEMMs (theta, X, X'; unused with fp32 io),
-  // and the two rocBLAS workspace slices (caller's stream, side stream)
-  size_t th32_off, x32_off, xp32_off, blas_off[2];
+  // the gradient GEMMs' operands: with bf16 io (split3) the exact bf16 split [h | m | l] of a
+  // direction's dQ|dK|dV ([B T, 9D]) and theta stacked three times ([9D, D]); with fp32 io none.
+  // Then the two rocBLAS workspace slices (caller's stream, side stream).
+  bool split3 = false;
+  size_t sp_off = 0, th3_off = 0, blas_off[2];
 };
 
 int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
@@ -624,10 +626,11 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
     if (p->split == 4) p->dqkvb_off = take(2 * BTD * sizeof(float));
   }
   p->dal_off = take(ttt::dalpha_partial_elems((int)D) * sizeof(float));
-  const bool bf16 = c->io_dtype == TTT_BF16;
-  p->th32_off = bf16 ? take(3 * D * D * sizeof(float)) : 0;
-  p->x32_off = bf16 ? take(BTD * sizeof(float)) : 0;
-  p->xp32_off = bf16 && bidir ? take(BTD * sizeof(float)) : 0;
+  p->split3 = c->io_dtype == TTT_BF16;
+  if (p->split3) {
+    p->sp_off = take(9 * BTD * sizeof(uint16_t));
+    p->th3_off = take(9 * D * D * sizeof(uint16_t));
+  }
   p->blas_off[0] = take(ttt::grad_gemm_workspace_bytes());
   p->blas_off[1] = bidir ? take(ttt::grad_gemm_workspace_bytes()) : 0;
   p->total = off;
@@ -671,22 +674,27 @@ int32_t bwd_forward(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin,
 // prev_x; it writes dtheta) on the side stream, released together with this call's backward scan
 // (ev_ready) and enqueued after it, so that the scan's workgroups take their CUs first and the
 // GEMM fills the rest; this call's own dtheta GEMM then adds to it after ev_done.
+// With split3 the deferred GEMM reads the split of the workspace, which the next direction
+// overwrites only after it (same stream, or after ev_done); prev_dqkv serves fp32 io.
 struct ThetaOverlap {
   bool skip_theta = false;
   hipStream_t side = nullptr;
   hipEvent_t ev_ready = nullptr, ev_done = nullptr;
   const float* prev_dqkv = nullptr;
-  const float* prev_x32 = nullptr;  // fp32 X of the deferred GEMM
+  const void* prev_x = nullptr;  // the deferred GEMM's X (io dtype)
 };
 
-// The gradient GEMMs on rocBLAS (fp32 operands: theta32 and x32 are theta and the
-// direction's input, widened when the io dtype is bf16).
-int32_t grad_dx(const BwdPlan& bp, char* ws, int slot, const float* dqkv, const float* theta32, const float* dyin,
+// The gradient GEMMs on rocBLAS.  dq: the direction's dQ|dK|dV (fp32 io) or its bf16 split
+// (split3); thg: theta (fp32 io) or theta stacked three times (split3); xg: the direction's
+// input in the io dtype.
+int32_t grad_dx(const BwdPlan& bp, char* ws, int slot, const void* dq, const void* thg, const float* dyin,
                 float* dX, int64_t BT, int64_t D, hipStream_t s) {
   const char* err = nullptr;
   hipError_t e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
-    err = ttt::grad_gemm_dx(slot, dqkv, theta32, dyin, dX, BT, D, ws + bp.blas_off[slot],
-                            ttt::grad_gemm_workspace_bytes(), s);
+    err = bp.split3 ? ttt::grad_gemm_dx_split(slot, (const uint16_t*)dq, (const uint16_t*)thg, dyin, dX, BT, D,
+                                              ws + bp.blas_off[slot], ttt::grad_gemm_workspace_bytes(), s)
+                    : ttt::grad_gemm_dx(slot, (const float*)dq, (const float*)thg, dyin, dX, BT, D,
+                                        ws + bp.blas_off[slot], ttt::grad_gemm_workspace_bytes(), s);
     return err ? hipErrorUnknown : hipSuccess;
   });
   if (err) return fail(TTT_ERR_HIP, "rocBLAS dX GEMM: %s", err);
@@ -694,7 +702,7 @@ int32_t grad_dx(const BwdPlan& bp, char* ws, int slot, const float* dqkv, const 
   return TTT_OK;
 }
 
-int32_t grad_dtheta(const BwdPlan& bp, char* ws, int slot, const float* dqkv, const float* x32, float* dtheta,
+int32_t grad_dtheta(const BwdPlan& bp, char* ws, int slot, const void* dq, const void* xg, float* dtheta,
                     int64_t BT, int64_t D, int accumulate, hipStream_t s) {
   if (BT == 0) {  // no tokens: dtheta is zero, or unchanged
     if (accumulate) return TTT_OK;
@@ -703,8 +711,11 @@ int32_t grad_dtheta(const BwdPlan& bp, char* ws, int slot, const float* dqkv, co
   }
   const char* err = nullptr;
   hipError_t e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
-    err = ttt::grad_gemm_dtheta(slot, dqkv, x32, dtheta, BT, D, accumulate, ws + bp.blas_off[slot],
-                                ttt::grad_gemm_workspace_bytes(), s);
+    err = bp.split3 ? ttt::grad_gemm_dtheta_split(slot, (const uint16_t*)dq, (const uint16_t*)xg, dtheta, BT, D,
+                                                  accumulate, ws + bp.blas_off[slot],
+                                                  ttt::grad_gemm_workspace_bytes(), s)
+                    : ttt::grad_gemm_dtheta(slot, (const float*)dq, (const float*)xg, dtheta, BT, D, accumulate,
+                                            ws + bp.blas_off[slot], ttt::grad_gemm_workspace_bytes(), s);
     return err ? hipErrorUnknown : hipSuccess;
   });
   if (err) return fail(TTT_ERR_HIP, "rocBLAS dtheta GEMM: %s", err);
@@ -712,22 +723,21 @@ int32_t grad_dtheta(const BwdPlan& bp, char* ws, int slot, const float* dqkv, co
   return TTT_OK;
 }
 
-// fp32 view of an io-dtype buffer of n elements: the buffer itself (fp32 io) or its
-// widened copy at ws + off (bf16 io), written on s.
-int32_t as_f32(const ttt_mlp_config* c, const void* src, int64_t n, char* ws, size_t off, hipStream_t s,
-               const float** out) {
-  if (c->io_dtype != TTT_BF16) {
-    *out = (const float*)src;
+// The theta operand of the gradient GEMMs: theta itself (fp32 io) or theta stacked three times
+// in the workspace (split3), written on s.
+int32_t theta_operand(const BwdPlan& bp, const void* theta, int64_t D, char* ws, hipStream_t s, const void** out) {
+  if (!bp.split3) {
+    *out = theta;
     return TTT_OK;
   }
-  float* dst = (float*)(ws + off);
-  hipError_t e = ttt::widen_bf16((const uint16_t*)src, dst, n, s);
-  if (e != hipSuccess) return fail(TTT_ERR_HIP, "widening launch: %s", hipGetErrorString(e));
+  uint16_t* dst = (uint16_t*)(ws + bp.th3_off);
+  hipError_t e = ttt::stack3_u16((const uint16_t*)theta, dst, 3 * D * D, s);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "theta stacking launch: %s", hipGetErrorString(e));
   *out = dst;
   return TTT_OK;
 }
 
-int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* xin32, const float* theta32,
+int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xg, const void* thg,
                       const float* alpha, int reverse, const float* dyin, const float* ckpt, const float* z, float* dX,
                       float* dtheta, float* dW1_0, float* dW2_0, int accumulate, float* dalpha, char* ws,
                       hipStream_t s, float* dqkv, const ThetaOverlap& ov = ThetaOverlap()) {
@@ -762,7 +772,8 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* x
     // the deferred dtheta GEMM first, on this stream: beside the per-window launches below it
     // would hold the CUs that each relaunch needs
     if (ov.side) {
-      st = grad_dtheta(bp, ws, 0, ov.prev_dqkv, ov.prev_x32, dtheta, BT, D, 0, s);
+      st = grad_dtheta(bp, ws, 0, bp.split3 ? (const void*)(ws + bp.sp_off) : ov.prev_dqkv, ov.prev_x, dtheta,
+                       BT, D, 0, s);
       if (st != TTT_OK) return st;
     }
     // windows of kReplayWindow segments from the last: replay them (one workgroup per chain and
@@ -814,21 +825,31 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const float* x
   if (ov.side && !replay) {
     e = hipStreamWaitEvent(ov.side, ov.ev_ready, 0);
     if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream wait: %s", hipGetErrorString(e));
-    st = grad_dtheta(bp, ws, 1, ov.prev_dqkv, ov.prev_x32, dtheta, BT, D, 0, ov.side);
+    st = grad_dtheta(bp, ws, 1, bp.split3 ? (const void*)(ws + bp.sp_off) : ov.prev_dqkv, ov.prev_x, dtheta, BT,
+                     D, 0, ov.side);
     if (st != TTT_OK) return st;
     e = hipEventRecord(ov.ev_done, ov.side);
     if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream event: %s", hipGetErrorString(e));
   }
   e = ttt::launch_dalpha(dyin, z, alpha, (float*)(ws + bp.dal_off), dalpha, BT, (int)D, s);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "dalpha launch: %s", hipGetErrorString(e));
-  st = grad_dx(bp, ws, 0, dqkv, theta32, dyin, dX, BT, D, s);
-  if (st != TTT_OK) return st;
+  // the deferred GEMM on the side stream has read the split (or, with fp32 io, adds to dtheta
+  // before this direction's GEMM does) once ev_done is reached
   if (ov.side && !replay) {
     e = hipStreamWaitEvent(s, ov.ev_done, 0);
     if (e != hipSuccess) return fail(TTT_ERR_HIP, "stream wait: %s", hipGetErrorString(e));
   }
+  const void* dq = dqkv;
+  if (bp.split3) {
+    uint16_t* sp = (uint16_t*)(ws + bp.sp_off);
+    e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] { return ttt::split_bf16x3(dqkv, sp, BT, 3 * D, s); });
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "dQ|dK|dV split launch: %s", hipGetErrorString(e));
+    dq = sp;
+  }
+  st = grad_dx(bp, ws, 0, dq, thg, dyin, dX, BT, D, s);
+  if (st != TTT_OK) return st;
   if (!ov.skip_theta) {
-    st = grad_dtheta(bp, ws, 0, dqkv, xin32, dtheta, BT, D, accumulate, s);
+    st = grad_dtheta(bp, ws, 0, dq, xg, dtheta, BT, D, accumulate, s);
     if (st != TTT_OK) return st;
   }
   e = ttt::launch_sum_state(dw_seq, dW1_0, dW2_0, c->B, c->H, c->d, c->m, accumulate, s);
@@ -1138,12 +1159,11 @@ int32_t ttt_mlp_backward(const ttt_mlp_config* cfg, const void* X, const void* t
   float* ck = (float*)(ws + bp.ckpt_off[0]);
   st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha, reverse != 0, ws + bp.y_off, z, ck, ws, s);
   if (st != TTT_OK) return st;
-  const int64_t D_ = (int64_t)cfg->H * cfg->d, BTD_ = cfg->B * cfg->T * D_;
-  const float *th32 = nullptr, *x32 = nullptr;
-  st = as_f32(cfg, theta_qkv, 3 * D_ * D_, ws, bp.th32_off, s, &th32);
-  if (st == TTT_OK) st = as_f32(cfg, X, BTD_, ws, bp.x32_off, s, &x32);
+  const int64_t D_ = (int64_t)cfg->H * cfg->d;
+  const void* thg = nullptr;
+  st = theta_operand(bp, theta_qkv, D_, ws, s, &thg);
   if (st != TTT_OK) return st;
-  st = bwd_direction(cfg, bp, x32, th32, alpha, reverse != 0, dY, ck, z, dX, dtheta, dW1_0, dW2_0, 0, dalpha, ws, s,
+  st = bwd_direction(cfg, bp, X, thg, alpha, reverse != 0, dY, ck, z, dX, dtheta, dW1_0, dW2_0, 0, dalpha, ws, s,
                      (float*)(ws + bp.dqkv_off));
   return st == TTT_OK ? ok() : st;
 }
@@ -1185,12 +1205,10 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   // the two forward passes, keeping X', Z and the checkpoints
   st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha_f, 0, xp, zf, ckf, ws, s);
   if (st == TTT_OK) st = bwd_forward(cfg, bp, xp, theta_qkv, W1_0, W2_0, alpha_b, 1, ws + bp.y_off, zb, ckb, ws, s);
-  // fp32 operands of the gradient GEMMs: theta, X and X'
-  const int64_t D_ = (int64_t)cfg->H * cfg->d, BTD_ = cfg->B * cfg->T * D_;
-  const float *th32 = nullptr, *x32 = nullptr, *xp32 = nullptr;
-  if (st == TTT_OK) st = as_f32(cfg, theta_qkv, 3 * D_ * D_, ws, bp.th32_off, s, &th32);
-  if (st == TTT_OK) st = as_f32(cfg, X, BTD_, ws, bp.x32_off, s, &x32);
-  if (st == TTT_OK) st = as_f32(cfg, xp, BTD_, ws, bp.xp32_off, s, &xp32);
+  // the theta operand of the gradient GEMMs (X and X' serve as they are)
+  const int64_t D_ = (int64_t)cfg->H * cfg->d;
+  const void* thg = nullptr;
+  if (st == TTT_OK) st = theta_operand(bp, theta_qkv, D_, ws, s, &thg);
   // the reversed pass's backward (its Q/K/V, of X', are in the workspace): dX' = dY + ...; its
   // dtheta GEMM is deferred to the side stream, beside the forward pass's backward scan (which
   // takes one CU per head), and the forward pass's dtheta GEMM adds to it afterwards
@@ -1204,14 +1222,14 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   ov_f.ev_ready = sd->events[0];
   ov_f.ev_done = sd->events[1];
   ov_f.prev_dqkv = (const float*)(ws + bp.dqkv2_off);
-  ov_f.prev_x32 = xp32;
+  ov_f.prev_x = xp;
   if (st == TTT_OK)
-    st = bwd_direction(cfg, bp, xp32, th32, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws,
-                       s, (float*)(ws + bp.dqkv2_off), ov_b);
+    st = bwd_direction(cfg, bp, xp, thg, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws, s,
+                       (float*)(ws + bp.dqkv2_off), ov_b);
   // the forward pass's backward, with dY = dX' and X's Q/K/V projected again
   if (st == TTT_OK) st = bwd_project(cfg, bp, X, theta_qkv, ws, s);
   if (st == TTT_OK)
-    st = bwd_direction(cfg, bp, x32, th32, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s,
+    st = bwd_direction(cfg, bp, X, thg, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s,
                        (float*)(ws + bp.dqkv_off), ov_f);
   return st == TTT_OK ? ok() : st;
 }

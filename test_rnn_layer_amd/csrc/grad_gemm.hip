@@ -2,10 +2,19 @@
 // dtheta (+)= [dQ dK dV]^T X (the outer-loop projections of "One-Minute Video
 // Generation with Test-Time Training", paper-notes page, key designs
 // "TTT-MLP layer": theta_K, theta_V, theta_Q learned through the layer).  They
-// are plain fp32 GEMMs, so they run on rocBLAS (rocblas_gemm_ex_64, fp32
-// operands, fp32 accumulation, its fp32 matrix-core kernels).  bf16 operands
-// (X, X' and theta when the io dtype is bf16) are widened exactly to fp32 in the
-// caller's workspace first.
+// are plain GEMMs, so they run on rocBLAS (rocblas_gemm_ex_64, fp32 accumulation).
+//
+// With fp32 io all operands are fp32 and the GEMMs run on rocBLAS's fp32
+// matrix-core kernels.  With bf16 io, X, X' and theta are exact bf16 numbers and
+// only dQKV is fp32.  Then dQKV is split exactly into three bf16 parts,
+// x = h + m + l (h: x with its low 16 bits cleared, m: the same of x - h, l: the
+// rest, which has at most 8 significant bits, so the split is exact for
+// |x| >= 2^-103), and the GEMMs run on the bf16 matrix cores with fp32
+// accumulation: every product of two bf16 numbers is exact in fp32, so the
+// result has the accuracy of an fp32 GEMM at a third of the bf16 rate, about
+// five times the fp32 matrix-core rate.  dX takes the three parts as one
+// contraction of length 9D against theta stacked three times; dtheta adds the
+// three parts' products, the smallest first.
 //
 // rocBLAS takes column-major matrices; a row-major [R, C] matrix is the
 // column-major [C, R] one, so row-major C = A B is computed as C^T = B^T A^T.
@@ -25,10 +34,51 @@
 namespace ttt {
 namespace {
 
-__global__ void widen_bf16_kernel(const uint16_t* in, float* out, int64_t n) {
+// x -> (h, m, l), bf16 bit patterns with h + m + l = x; Inf and NaN go to h alone
+// (NaN as a quiet NaN), their m and l are zero.
+__device__ inline void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u) {
+    h = (u & 0x007FFFFFu) ? 0x7FC0u : u >> 16;
+    m = l = 0;
+    return;
+  }
+  h = u >> 16;
+  const float r = x - __uint_as_float(h << 16);  // exact: the low 16 bits of x
+  m = __float_as_uint(r) >> 16;
+  const float q = r - __uint_as_float(m << 16);  // exact, at most 8 significant bits
+  l = __float_as_uint(q) >> 16;
+}
+
+// in: row-major [rows, cols] fp32, cols % 4 == 0; out: row-major [rows, 3 cols] bf16,
+// row r = [h | m | l] of in's row r.  Block x covers 256 float4 columns of a row.
+__global__ void split_bf16x3_kernel(const float4* __restrict__ in, uint2* __restrict__ out, int64_t rows,
+                                    int64_t cols4) {
+  const int64_t c4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c4 >= cols4) return;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const float4 v = in[r * cols4 + c4];
+    uint32_t h[4], m[4], l[4];
+    split3(v.x, h[0], m[0], l[0]);
+    split3(v.y, h[1], m[1], l[1]);
+    split3(v.z, h[2], m[2], l[2]);
+    split3(v.w, h[3], m[3], l[3]);
+    uint2* o = out + r * 3 * cols4 + c4;
+    o[0] = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+    o[cols4] = make_uint2(m[0] | m[1] << 16, m[2] | m[3] << 16);
+    o[2 * cols4] = make_uint2(l[0] | l[1] << 16, l[2] | l[3] << 16);
+  }
+}
+
+// out[j n + i] = in[i] for j < 3 (n 16-bit elements)
+__global__ void stack3_u16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    out[i] = __uint_as_float((uint32_t)in[i] << 16);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint16_t v = in[i];
+    out[i] = v;
+    out[n + i] = v;
+    out[2 * n + i] = v;
+  }
 }
 
 struct Handles {
@@ -62,11 +112,58 @@ rocblas_status handle_for(int slot, hipStream_t s, void* ws, size_t ws_bytes, ro
 
 size_t grad_gemm_workspace_bytes() { return (size_t)256 << 20; }
 
-hipError_t widen_bf16(const uint16_t* in, float* out, int64_t n, hipStream_t s) {
+hipError_t split_bf16x3(const float* in, uint16_t* out, int64_t rows, int64_t cols, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (cols % 4 != 0) return hipErrorInvalidValue;
+  const int64_t cols4 = cols / 4;
+  const dim3 grid((unsigned)((cols4 + 255) / 256), (unsigned)std::min<int64_t>(rows, 8192));
+  hipLaunchKernelGGL(split_bf16x3_kernel, grid, dim3(256), 0, s, (const float4*)in, (uint2*)out, rows, cols4);
+  return hipGetLastError();
+}
+
+hipError_t stack3_u16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
-  hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, in, out, n);
+  hipLaunchKernelGGL(stack3_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, in, out, n);
   return hipGetLastError();
+}
+
+// dX [BT, D] = dY [BT, D] + S [BT, 9D] theta3 [9D, D], row-major; S = [h | m | l] of dQKV
+// (bf16), theta3 = theta stacked three times (bf16), fp32 accumulation and output.
+const char* grad_gemm_dx_split(int slot, const uint16_t* sp, const uint16_t* theta3, const float* dy, float* dx,
+                               int64_t BT, int64_t D, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (BT == 0 || D == 0) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  rocblas_handle h = nullptr;
+  rocblas_status st = handle_for(slot, s, ws, ws_bytes, &h);
+  const float one = 1.0f;
+  // column-major: dX^T [D, BT] = theta3^T [D, 9D] S^T [9D, BT] + dY^T
+  if (st == rocblas_status_success)
+    st = rocblas_gemm_ex_64(h, rocblas_operation_none, rocblas_operation_none, D, BT, 9 * D, &one, theta3,
+                            rocblas_datatype_bf16_r, D, sp, rocblas_datatype_bf16_r, 9 * D, &one, dy,
+                            rocblas_datatype_f32_r, D, dx, rocblas_datatype_f32_r, D, rocblas_datatype_f32_r,
+                            rocblas_gemm_algo_standard, 0, 0);
+  return st == rocblas_status_success ? nullptr : status_text(st);
+}
+
+// dtheta [3D, D] = (accumulate ? dtheta : 0) + l^T X + m^T X + h^T X, with h, m, l the column
+// blocks of S [BT, 9D] (bf16) and X [BT, D] bf16; fp32 accumulation and output.
+const char* grad_gemm_dtheta_split(int slot, const uint16_t* sp, const uint16_t* x16, float* dtheta, int64_t BT,
+                                   int64_t D, int accumulate, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (D == 0) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  rocblas_handle h = nullptr;
+  rocblas_status st = handle_for(slot, s, ws, ws_bytes, &h);
+  const float one = 1.0f;
+  for (int j = 2; j >= 0 && st == rocblas_status_success; --j) {
+    const float beta = (j < 2 || accumulate) ? 1.0f : 0.0f;
+    // column-major: dtheta^T [D, 3D] += X^T [D, BT] (S_j^T)^T, S_j^T the column-major [3D, BT], ld 9D
+    st = rocblas_gemm_ex_64(h, rocblas_operation_none, rocblas_operation_transpose, D, 3 * D, BT, &one, x16,
+                            rocblas_datatype_bf16_r, D, sp + j * 3 * D, rocblas_datatype_bf16_r, 9 * D, &beta,
+                            dtheta, rocblas_datatype_f32_r, D, dtheta, rocblas_datatype_f32_r, D,
+                            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  }
+  return st == rocblas_status_success ? nullptr : status_text(st);
 }
 
 // dX [BT, D] = dY [BT, D] + dQKV [BT, 3D] theta [3D, D], row-major, fp32.

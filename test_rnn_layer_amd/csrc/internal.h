@@ -147,8 +147,8 @@ hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s);
 size_t scan_replay_f32_slot_elems();
 hipError_t launch_scan_replay_f32(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
-// The replayed windows' walk with each chain's hidden units split over two co-resident workgroups
-// (one cooperative launch of 2 B H workgroups; the state and adjoint halves in LDS).
+// The replayed windows' walk with each chain's hidden units split over S co-resident workgroups
+// (S = 4 or 2; one cooperative launch of S B H workgroups; the state and adjoint parts in LDS).
 bool scan_backward_split_fits(int64_t B, int H, int d, int m, int b, int S);
 size_t scan_backward_split_xchg_elems(int64_t B, int H, int d, int b, int S);
 hipError_t launch_scan_backward_split(const BwdArgs& a, hipStream_t s);
@@ -164,11 +164,19 @@ hipError_t launch_gemm_f32(bool a_transposed, bool b_bf16, const float* A, int64
 // stream, 1: the side stream; ws: a workspace slice of grad_gemm_workspace_bytes() for that slot.
 // Return NULL or rocBLAS's description of its error.
 size_t grad_gemm_workspace_bytes();
-hipError_t widen_bf16(const uint16_t* in, float* out, int64_t n, hipStream_t s);
 const char* grad_gemm_dx(int slot, const float* dqkv, const float* theta32, const float* dy, float* dx, int64_t BT,
                          int64_t D, void* ws, size_t ws_bytes, hipStream_t s);
 const char* grad_gemm_dtheta(int slot, const float* dqkv, const float* x32, float* dtheta, int64_t BT, int64_t D,
                              int accumulate, void* ws, size_t ws_bytes, hipStream_t s);
+// With bf16 X and theta: S [BT, 9D] = the exact bf16 split [h | m | l] of dQKV [BT, 3D]
+// (split_bf16x3; cols % 4 == 0), theta3 [9D, D] = theta stacked three times (stack3_u16), and
+// the same two GEMMs on the bf16 matrix cores with fp32 accumulation.
+hipError_t split_bf16x3(const float* in, uint16_t* out, int64_t rows, int64_t cols, hipStream_t s);
+hipError_t stack3_u16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s);
+const char* grad_gemm_dx_split(int slot, const uint16_t* sp, const uint16_t* theta3, const float* dy, float* dx,
+                               int64_t BT, int64_t D, void* ws, size_t ws_bytes, hipStream_t s);
+const char* grad_gemm_dtheta_split(int slot, const uint16_t* sp, const uint16_t* x16, float* dtheta, int64_t BT,
+                                   int64_t D, int accumulate, void* ws, size_t ws_bytes, hipStream_t s);
 // dalpha[c] = (1 - tanh(alpha[c])^2) sum_r dy[r, c] z[r, c]; part: dalpha_partial_elems(D) floats
 size_t dalpha_partial_elems(int D);
 hipError_t launch_dalpha(const float* dy, const float* z, const float* alpha, float* part, float* dalpha,
