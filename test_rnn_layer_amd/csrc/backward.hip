@@ -40,6 +40,7 @@
 #include "internal.h"
 #include "mfma_common.h"
 #include "phase_marks.h"
+#include "token_block.h"
 
 TTT_MARKS_BUFFER(g_marks_scan_backward);
 
@@ -856,24 +857,36 @@ __global__ __launch_bounds__(BW) void scan_backward_kernel(BwdArgs a) {
 // peer shows as NaN gradients rather than a hang.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kSplitSpinMax = 1u << 20;
+// The split walk runs at the one shape the fp32 matrix-core forward pass and replay serve
+// (d = 64, m = 256, b = 16, the erf GELU): with the sizes compile-time constants its index
+// arithmetic folds.
+constexpr int kSplitD = 64, kSplitM = 256, kSplitB = 16;
 
 // floats of a split workgroup's scratch: its b x m/S panels dAq, dHk, dG1 (then dA), dGh, and
 // its dQ and dK partials (b x d); in LDS with four parts, in the workspace with two
 __host__ __device__ constexpr int64_t split_scratch_floats(int d, int m, int b, int S) {
   return 4LL * b * (m / S) + 2LL * b * d;
 }
+// floats of the seven b x m/S slot panels a four-part workgroup stages in LDS (A, Hk, GELU'(A),
+// Gh, G1, Hq, GELU'(Aq); rows of m/S + 4)
+__host__ __device__ constexpr int64_t split_slot_panel_floats(int m, int b, int S) {
+  return 7LL * b * (m / S + 4);
+}
 // LDS floats of a split workgroup: its part of the state and of the adjoint (W1 columns as
 // [d][m/S + 4], W2 rows as [m/S][d + 4]), the b x d and b x b panels, and with four parts its
-// scratch
+// scratch and its slot panels
 __host__ __device__ constexpr int64_t split_lds_floats(int d, int m, int b, int S) {
   return 2 * ((int64_t)d * (m / S + 4) + (int64_t)(m / S) * (d + 4)) + panel_lds_floats(d, b) +
-         (S == 4 ? split_scratch_floats(d, m, b, S) : 0);
+         (S == 4 ? split_scratch_floats(d, m, b, S) + split_slot_panel_floats(m, b, S) : 0);
 }
+
+__device__ float4 g_bwd_zero_chunk;  // zero-initialised, never written: the source of padding chunks
 
 template <int S>
 __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int d = a.d, m = a.m, b = a.b, mh = m / S, tid = threadIdx.x;  // mh: this part's units
+  constexpr int d = kSplitD, m = kSplitM, b = kSplitB, mh = m / S;  // mh: this part's units
+  const int tid = threadIdx.x;
   const int64_t BH = a.B * a.H;
   const int half = (int)(blockIdx.x / BH);             // the part
   const int64_t sh = (int64_t)blockIdx.x - half * BH;  // sequence * H + head
@@ -912,6 +925,9 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   float* dGh = dG1 + (int64_t)b * mh;
   float* dQp = dGh + (int64_t)b * mh;
   float* dKp = dQp + (int64_t)b * d;
+  // with four parts the step's slot panels in LDS (rows of mh + 4), after the scratch
+  constexpr int pld = S == 4 ? mh + 4 : m;  // their row stride (in the slot: m)
+  float* const spl = dKp + (int64_t)b * d;
   uint64_t* xc = a.xchg + sh * 2 * S * (int64_t)(b * d);  // [part][parity][b d]
 
   // the adjoint's part: zero (the window that starts the walk) or as the previous window left it
@@ -939,48 +955,100 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       const float* sl = seg + (j - j0) * slot;
       // the slot's panels, this part's columns (row stride m)
       const float* fq = sl + 2 * dm;
-      const float *A_ = fq + u0, *Hk_ = fq + bm + u0, *S1_ = fq + 2 * bm + u0, *Gh_ = fq + 3 * bm + u0,
-                  *G1_ = fq + 4 * bm + u0;
       const float* ro = fq + 5 * bm + (int64_t)b * d;  // the read-out: Aq, Hq, GELU'(Aq), M
-      const float *Hq_ = ro + bm + u0, *S1q_ = ro + 2 * bm + u0;
-      // ---- the state half, K and Q rows, G2, M, dZ = tanh(alpha) dY
+      // the seven panels this step reads: in the slot (two parts) or staged in LDS (four)
+      const float *A_, *Hk_, *S1_, *Gh_, *G1_, *Hq_, *S1q_;
+      if constexpr (S == 4) {
+        A_ = spl, Hk_ = spl + b * pld, S1_ = spl + 2 * b * pld, Gh_ = spl + 3 * b * pld, G1_ = spl + 4 * b * pld;
+        Hq_ = spl + 5 * b * pld, S1q_ = spl + 6 * b * pld;
+      } else {
+        A_ = fq + u0, Hk_ = fq + bm + u0, S1_ = fq + 2 * bm + u0, Gh_ = fq + 3 * bm + u0, G1_ = fq + 4 * bm + u0;
+        Hq_ = ro + bm + u0, S1q_ = ro + 2 * bm + u0;
+      }
+      // ---- the state part, K and Q rows, G2, M (and with four parts the seven panels), dZ = tanh(alpha) dY
       __syncthreads();  // the previous step's last reads of the LDS panels and state
-      copy_rows(W.w1, W.ld1, sl + u0, m, d, mh);
-      copy_rows(W.w2, W.ld2, sl + dm + (int64_t)u0 * d, d, mh, d);
-      load_qkv(t, rw, j * b, n, d, false);
-      copy_rows(t.G2, d, fq + 5 * bm, d, n, d);
-      for (int i = tid; i < b * b; i += BW) t.M[i] = ro[3 * bm + i];
+      if constexpr (S == 4) {
+        // direct global -> LDS loads, 16 bytes a lane, all in flight at once; each wave
+        // instruction fills 64 consecutive chunks of one of three LDS regions:
+        //   1: W1 columns then W2 rows of this part, 17 chunks a row (the 17th: padding)
+        //   2: K and Q rows (by token; rows past n zero), G2 (rows past n zero), M
+        //   3: the seven panels, 17 chunks a row (rows past n zero)
+        constexpr int RC = 17, N1 = (d + mh) * RC, N2 = 3 * b * d / 4 + b * b / 4, N3 = 7 * b * RC;
+        constexpr int I1 = (N1 + 63) / 64, I2 = (N2 + 63) / 64, I3 = (N3 + 63) / 64;
+        const int wv = tid >> 6, ln = tid & 63;
+        const void* zero = (const void*)&g_bwd_zero_chunk;
+        for (int i = wv; i < I1 + I2 + I3; i += kBwdWaves) {
+          const void* src = zero;
+          const float* base;
+          int g;
+          if (i < I1) {
+            base = W.w1;
+            g = 64 * i + ln;
+            if (g >= N1) continue;
+            const int r = g / RC, c = g - r * RC;
+            if (c < 16)
+              src = r < d ? sl + (int64_t)r * m + u0 + 4 * c : sl + dm + (int64_t)(u0 + r - d) * d + 4 * c;
+          } else if (i < I1 + I2) {
+            base = t.K;
+            g = 64 * (i - I1) + ln;
+            if (g >= N2) continue;
+            const int q = g >> 4, c = g & 15;  // q: row of K (0..b-1), Q (b..2b-1), G2 (2b..3b-1), then M
+            if (q < 2 * b) {
+              const int r = q < b ? q : q - b;
+              if (r < n) src = (q < b ? rw.kb : rw.qb) + rw.tok(j * b + r) * d + 4 * c;
+            } else if (q < 3 * b) {
+              if (q - 2 * b < n) src = fq + 5 * bm + (int64_t)(q - 2 * b) * d + 4 * c;
+            } else {
+              src = ro + 3 * bm + 4 * (g - 3 * b * d / 4);
+            }
+          } else {
+            base = spl;
+            g = 64 * (i - I1 - I2) + ln;
+            if (g >= N3) continue;
+            const int p = g / (b * RC), rr = g - p * (b * RC), r = rr / RC, c = rr - r * RC;
+            if (c < 16 && r < n) src = (p < 5 ? fq + p * bm : ro + (p - 4) * bm) + u0 + (int64_t)r * m + 4 * c;
+          }
+          tb::dma16(src, tb::lds_addr_uniform(base, 1024u * (uint32_t)(g >> 6)));
+        }
+      } else {
+        copy_rows(W.w1, W.ld1, sl + u0, m, d, mh);
+        copy_rows(W.w2, W.ld2, sl + dm + (int64_t)u0 * d, d, mh, d);
+        load_qkv(t, rw, j * b, n, d, false);
+        copy_rows(t.G2, d, fq + 5 * bm, d, n, d);
+        for (int i = tid; i < b * b; i += BW) t.M[i] = ro[3 * bm + i];
+      }
       for (int i = tid; i < n * d; i += BW) {
         const int r = i / d, c = i - r * d;
         const int ch = h * d + c;
         t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + ch];
       }
+      if constexpr (S == 4) vmem_done();  // this wave's direct loads have landed
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 1);
       // ---- N (this part) = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
-      rowdot_tril(t.N, b, n, mh, Hq_, m, Hk_, m, 1.0f);
+      rowdot_tril(t.N, b, n, mh, Hq_, pld, Hk_, pld, 1.0f);
       rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
       prod<4, true>(dGh, mh, n, mh, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 2);
       // ---- dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dHk = dN^T Hq; dG2 (this part) = -eta N^T dZ
       if (n % 16 == 0 && mh % 16 == 0 && d % 16 == 0) {  // on the matrix cores (N, dN are 0 above the diagonal)
-        prod_mfma<false, false>(dGh, mh, n, mh, n, t.dN, b, Hk_, m, 1.0f, true, 0);
-        prod_mfma<true, false>(dHk, mh, n, mh, n, t.dN, b, Hq_, m, 1.0f, false, 0);
+        prod_mfma<false, false>(dGh, mh, n, mh, n, t.dN, b, Hk_, pld, 1.0f, true, 0);
+        prod_mfma<true, false>(dHk, mh, n, mh, n, t.dN, b, Hq_, pld, 1.0f, false, 0);
         prod_mfma<true, false>(t.dG2, d, n, d, n, t.N, b, t.dZ, d, -eta, false, 0);
         __syncthreads();
         for (int i = tid; i < n * mh; i += BW) {
           const int r = i / mh, c = i - r * mh;
-          dAq[i] = S1q_[(int64_t)r * m + c] * dGh[i];
+          dAq[i] = S1q_[r * pld + c] * dGh[i];
         }
       } else {
         for (int i = tid; i < n * mh; i += BW) {
           const int r = i / mh, c = i - r * mh;
           float v = dGh[i];
-          for (int k = 0; k <= r; ++k) v = fmaf(t.dN[r * b + k], Hk_[(int64_t)k * m + c], v);
-          dAq[i] = S1q_[(int64_t)r * m + c] * v;
+          for (int k = 0; k <= r; ++k) v = fmaf(t.dN[r * b + k], Hk_[k * pld + c], v);
+          dAq[i] = S1q_[r * pld + c] * v;
           float w = 0.0f;
-          for (int k = r; k < n; ++k) w = fmaf(t.dN[k * b + r], Hq_[(int64_t)k * m + c], w);
+          for (int k = r; k < n; ++k) w = fmaf(t.dN[k * b + r], Hq_[k * pld + c], w);
           dHk[i] = w;
         }
         for (int i = tid; i < n * d; i += BW) {
@@ -995,11 +1063,11 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       // ---- dQ (this part) = dAq W1^T; dM (this part) = tril(-eta dAq G1^T); with the adjoint's part:
       //      dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK (this part) = -eta G1 dW1'^T
       prod<1, true>(dQp, d, n, d, mh, dAq, mh, W.w1, W.ld1, 1.0f, false);
-      rowdot_tril(t.dM, b, n, mh, dAq, mh, G1_, m, -eta, 4);
+      rowdot_tril(t.dM, b, n, mh, dAq, mh, G1_, pld, -eta, 4);
       prod<4, true>(dHk, mh, n, mh, d, t.G2, d, dW2, la2, -eta, true, 5);
-      prod<1, false>(t.dG2, d, n, d, mh, Hk_, m, dW2, la2, -eta, true, 5);
+      prod<1, false>(t.dG2, d, n, d, mh, Hk_, pld, dW2, la2, -eta, true, 5);
       prod<4, false>(dG1, mh, n, mh, d, t.K, d, dW1, la1, -eta, false, 9);
-      prod<1, true>(dKp, d, n, d, mh, G1_, m, dW1, la1, -eta, false, 9);
+      prod<1, true>(dKp, d, n, d, mh, G1_, pld, dW1, la1, -eta, false, 9);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 4);
       // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this part's dM)
@@ -1024,10 +1092,10 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       for (int i = tid; i < n * mh; i += BW) {
         const int r = i / mh, c = i - r * mh;
         float g, dg, ddg;
-        gelu3(A_[(int64_t)r * m + c], a.gelu_tanh, &g, &dg, &ddg);
+        gelu3(A_[r * pld + c], false, &g, &dg, &ddg);
         const float x = dG1[i];
-        dGh[i] = x * S1_[(int64_t)r * m + c];
-        dG1[i] = x * Gh_[(int64_t)r * m + c] * ddg;
+        dGh[i] = x * S1_[r * pld + c];
+        dG1[i] = x * Gh_[r * pld + c] * ddg;
       }
       __syncthreads();
       prod<1, false>(t.dG2, d, n, d, mh, dGh, mh, W.w2, W.ld2, 1.0f, true);  // dG2 (this part) += dGh W2
@@ -1078,7 +1146,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       __syncthreads();
       for (int i = tid; i < n * mh; i += BW) {  // dA += dHk * S1
         const int r = i / mh, c = i - r * mh;
-        dG1[i] += dHk[i] * S1_[(int64_t)r * m + c];
+        dG1[i] += dHk[i] * S1_[r * pld + c];
       }
       __syncthreads();
       prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);  // dK (this part) += dA W1^T
@@ -1097,7 +1165,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       }
       Terms u1{2, {t.Q, t.K}, {d, d}, {dAq, dG1}, {mh, mh}};
       rank_update_any(dW1, la1, d, mh, n, u1, 1.0f);
-      Terms u2{3, {Hq_, dGh, Hk_}, {m, mh, m}, {t.dZ, t.G2, t.dG2}, {d, d, d}};
+      Terms u2{3, {Hq_, dGh, Hk_}, {pld, mh, pld}, {t.dZ, t.G2, t.dG2}, {d, d, d}};
       rank_update_any(dW2, la2, mh, d, n, u2, 1.0f);
     }
   }
@@ -1244,7 +1312,7 @@ const void* split_kernel_fn(int S) {
 }
 
 bool scan_backward_split_fits(int64_t B, int H, int d, int m, int b, int S) {
-  if ((S != 2 && S != 4) || m % (16 * S) != 0 || d % 16 != 0 || b > 16 || (int64_t)b * d > BW) return false;
+  if ((S != 2 && S != 4) || d != kSplitD || m != kSplitM || b != kSplitB) return false;
   const size_t lds = scan_backward_split_lds_bytes(d, m, b, S);
   if (lds > 160 * 1024 || S * split_scratch_floats(d, m, b, S) > scratch_floats(d, m, b)) return false;
   int dev = 0, cus = 0, coop = 0, per_cu = 0;
@@ -1268,7 +1336,8 @@ hipError_t launch_zero_u64(uint64_t* p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_scan_backward_split(const BwdArgs& a, hipStream_t s) {
-  if (a.split != 2 && a.split != 4) return hipErrorInvalidValue;
+  if ((a.split != 2 && a.split != 4) || a.d != kSplitD || a.m != kSplitM || a.b != kSplitB || a.gelu_tanh)
+    return hipErrorInvalidValue;
   const size_t lds = scan_backward_split_lds_bytes(a.d, a.m, a.b, a.split);
   hipError_t e = hipFuncSetAttribute(split_kernel_fn(a.split), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
