@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(PKG, "libttt_mlp.so")
 MARKS_BUILD_DIR = os.path.join(PKG, "_build_marks")
 MARKS_LIB_PATH = os.path.join(PKG, "libttt_mlp_marks.so")
 SOURCES = ["api.hip", "generic.hip", "proj_mfma.hip", "scan_mfma.hip", "scan_linear.hip", "scan_coop.hip",
-           "backward.hip", "scan_fwd_f32.hip", "grad_gemm.hip", "attention.hip"]
+           "backward.hip", "backward_split.hip", "scan_fwd_f32.hip", "grad_gemm.hip", "attention.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
