@@ -546,8 +546,10 @@ constexpr int kCkptEvery = 32;
 constexpr size_t kBackwardLdsMax = 160 * 1024;
 // With the fp32 matrix-core forward steps (algo AUTO, d = 64, m = 256, b = 16, erf GELU), the
 // backward scan's segments are replayed beforehand, kReplayWindow segments of every chain per
-// launch on as many workgroups, and the backward scan walks them without replaying.
-constexpr int kReplayWindow = 4;
+// launch on as many workgroups, and the backward scan walks them without replaying.  16: at 48
+// chains a replay launch is 768 workgroups, three whole waves of a 256-CU chip (with 4 segments,
+// 192 workgroups left 64 CUs idle: 2.00 against 1.96 s per bidir307k backward call).
+constexpr int kReplayWindow = 16;
 
 bool bwd_f32mfma(const ttt_mlp_config* c) {
   return c->algo == TTT_ALGO_AUTO && ttt::scan_fwd_f32_supported(c->d, c->m, c->b) && c->gelu != TTT_GELU_TANH;
@@ -785,7 +787,7 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xg
     ra.ckpt_every = kCkptEvery;
     ra.seg_slots = ba.segst;
     ba.replayed = 1;
-    // the split walk (two workgroups per chain) where its workgroups fit co-resident: dQ and dK
+    // the split walk (four or two workgroups per chain) where they fit co-resident: dQ and dK
     // are added into dqkv, so it starts from zero, and so do the exchange entries and abort flag
     const bool split = bp.split != 0;
     if (split) {

@@ -370,7 +370,7 @@ def summarize_backward(d: str, out_md: str | None = None):
         f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ, fp32 arithmetic and "
         f"gradients; {steps} timed + {warm} warm-up calls under the trace.  One call: both forward passes again "
         "(projection, then the scan that keeps a checkpoint every 32 mini-batches: `scan_fwd_f32_kernel<false>`, "
-        "fp32 matrix cores), then per direction windows of 4 checkpoint segments from the last, each replayed "
+        "fp32 matrix cores), then per direction windows of 16 checkpoint segments from the last, each replayed "
         "(`scan_fwd_f32_kernel<true>`, one workgroup per head and segment) and then walked by the backward scan "
         "(`scan_backward_split_kernel`, four workgroups per head, one cooperative launch per window; a clearing "
         "kernel zeroes dQ|dK|dV, the second dQ|dK buffer and the exchange entries per direction, a small kernel "

@@ -36,8 +36,11 @@ CASES = {
     "bf16_d64": W.WORKLOADS["bidir307k"].replace(T=72, H=2, seg_len=0, name="bf16_d64"),
     "bf16_d64_generic": W.WORKLOADS["bidir307k"].replace(T=72, H=2, seg_len=0, name="bf16_d64_generic"),
     # the same shape over six checkpoint segments of 32 mini-batches and a 12-token tail: with algo
-    # AUTO the backward scan walks them in two windows of segments replayed beforehand
+    # AUTO the backward scan walks them in one window of segments replayed beforehand
     "bf16_d64_segments": W.WORKLOADS["bidir307k"].replace(T=2700, H=1, seg_len=0, name="bf16_d64_segments"),
+    # 18 checkpoint segments (556 mini-batches, a 12-token tail): two windows of replayed segments
+    # (16, then 2), so the adjoint crosses from one window's walk to the next through the workspace
+    "bf16_d64_windows": W.WORKLOADS["bidir307k"].replace(T=8892, H=1, seg_len=0, name="bf16_d64_windows"),
     # the bigstate307k head shape: a state too large for LDS stays in the workspace
     "bf16_d128_b1": W.WORKLOADS["bigstate307k"].replace(T=24, H=1, seg_len=0, name="bf16_d128_b1"),
 }
