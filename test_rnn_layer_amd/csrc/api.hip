@@ -557,7 +557,9 @@ bool bwd_f32mfma(const ttt_mlp_config* c) {
 
 struct BwdPlan {
   Plan fwd;  // the forward pass's Q/K/V and state slices (generic layout)
-  size_t dqkv_off, dqkv2_off, z_off[2], y_off, xp_off, dxp_off, ckpt_off[2], segst_off, dstate_off, scratch_off,
+  // qkv2_off: the reversed pass's Q/K/V (bidirectional), kept beside the forward pass's
+  size_t qkv2_off, dqkv_off, dqkv2_off, z_off[2], y_off, xp_off, dxp_off, ckpt_off[2], segst_off, dstate_off,
+      scratch_off,
       dwseq_off,
       dal_off, total;
   // the split backward scan: its workgroups per chain (4, 2, or 0: one workgroup per chain), its
@@ -602,10 +604,12 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   f.qkv_off = take(3 * BTD * sizeof(float));
   f.wst_bytes = align_up(BH * st2);
   f.wst_off = take(BH * st2);  // the forward scan's state, then the backward's replayed state
+  p->qkv2_off = bidir ? take(3 * BTD * sizeof(float)) : 0;
   p->dqkv_off = take(3 * BTD * sizeof(float));
-  // the reversed pass's dQ|dK|dV of its own: its dtheta GEMM reads them while the forward pass's
-  // backward scan writes the other buffer
-  p->dqkv2_off = bidir ? take(3 * BTD * sizeof(float)) : 0;
+  // the reversed pass's dQ|dK|dV: with fp32 io a buffer of its own, which its deferred dtheta GEMM
+  // reads while the forward pass's backward scan writes the other; with bf16 io that GEMM reads
+  // their bf16 split, so the two directions share one buffer
+  p->dqkv2_off = bidir && c->io_dtype != TTT_BF16 ? take(3 * BTD * sizeof(float)) : p->dqkv_off;
   p->z_off[0] = take(BTD * sizeof(float));
   p->z_off[1] = bidir ? take(BTD * sizeof(float)) : 0;
   p->y_off = take(BTD * io);
@@ -1204,16 +1208,21 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   float* zb = (float*)(ws + bp.z_off[1]);
   float* ckf = (float*)(ws + bp.ckpt_off[0]);
   float* ckb = (float*)(ws + bp.ckpt_off[1]);
-  // the two forward passes, keeping X', Z and the checkpoints
+  // the two forward passes, keeping X', Z, the checkpoints and both directions' Q/K/V (the
+  // reversed pass's in their own buffer: bpb)
+  BwdPlan bpb = bp;
+  bpb.fwd.qkv_off = bp.qkv2_off;
   st = bwd_forward(cfg, bp, X, theta_qkv, W1_0, W2_0, alpha_f, 0, xp, zf, ckf, ws, s);
-  if (st == TTT_OK) st = bwd_forward(cfg, bp, xp, theta_qkv, W1_0, W2_0, alpha_b, 1, ws + bp.y_off, zb, ckb, ws, s);
+  if (st == TTT_OK)
+    st = bwd_forward(cfg, bpb, xp, theta_qkv, W1_0, W2_0, alpha_b, 1, ws + bp.y_off, zb, ckb, ws, s);
   // the theta operand of the gradient GEMMs (X and X' serve as they are)
   const int64_t D_ = (int64_t)cfg->H * cfg->d;
   const void* thg = nullptr;
   if (st == TTT_OK) st = theta_operand(bp, theta_qkv, D_, ws, s, &thg);
   // the reversed pass's backward (its Q/K/V, of X', are in the workspace): dX' = dY + ...; its
-  // dtheta GEMM is deferred to the side stream, beside the forward pass's backward scan (which
-  // takes one CU per head), and the forward pass's dtheta GEMM adds to it afterwards
+  // dtheta GEMM is deferred, and the forward pass's dtheta GEMM adds to it afterwards: with the
+  // replayed windows it runs on `s` before the forward pass's backward scan, otherwise on the side
+  // stream beside that scan (which takes one CU per head)
   std::lock_guard<std::mutex> lk(g_side_mu);
   Side* sd = nullptr;
   hipError_t e = side_for_device(&sd, 2);
@@ -1226,10 +1235,9 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   ov_f.prev_dqkv = (const float*)(ws + bp.dqkv2_off);
   ov_f.prev_x = xp;
   if (st == TTT_OK)
-    st = bwd_direction(cfg, bp, xp, thg, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws, s,
+    st = bwd_direction(cfg, bpb, xp, thg, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws, s,
                        (float*)(ws + bp.dqkv2_off), ov_b);
-  // the forward pass's backward, with dY = dX' and X's Q/K/V projected again
-  if (st == TTT_OK) st = bwd_project(cfg, bp, X, theta_qkv, ws, s);
+  // the forward pass's backward, with dY = dX'
   if (st == TTT_OK)
     st = bwd_direction(cfg, bp, X, thg, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s,
                        (float*)(ws + bp.dqkv_off), ov_f);
