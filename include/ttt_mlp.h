@@ -226,7 +226,10 @@ int32_t ttt_mlp_project(const ttt_mlp_config* cfg, const void* X, const void* th
  * state in registers, otherwise, and with algo GENERIC, with the backward's own
  * steps: both fp32, in different summation orders), then the backward scan, which
  * replays one segment of 32 mini-batches at a time from its checkpoint and
- * walks it backwards carrying the gradient of the state, then two GEMMs:
+ * walks it backwards carrying the gradient of the state (with the fp32 matrix-core
+ * steps, windows of 16 segments are replayed beforehand, the next window on the
+ * library's second stream of the device beside the walk of this one, ordered
+ * by events), then two GEMMs:
  * dX = dY + [dQ dK dV] theta and dtheta = [dQ dK dV]^T X.  With bf16 io (X and
  * theta exact bf16 numbers) the fp32 [dQ dK dV] is split exactly into three bf16
  * parts whose sum it is, and the GEMMs run on the bf16 matrix cores with fp32

@@ -566,6 +566,8 @@ struct BwdPlan {
   // exchange entries then its abort flag, and with four its second [B, T, 2D] dQ|dK buffer
   int split = 0;
   size_t bxchg_off = 0, dqkvb_off = 0;
+  // the replayed segments' second buffer: the next window is replayed into it beside the walk
+  size_t segst2_off = 0;
   // the gradient GEMMs' operands: with bf16 io (split3) the exact bf16 split [h | m | l] of a
   // direction's dQ|dK|dV ([B T, 9D]) and theta stacked three times ([9D, D]); with fp32 io none.
   // Then the two rocBLAS workspace slices (caller's stream, side stream).
@@ -617,8 +619,10 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   p->dxp_off = bidir ? take(BTD * sizeof(float)) : 0;
   p->ckpt_off[0] = take(BH * nseg * st2);
   p->ckpt_off[1] = bidir ? take(BH * nseg * st2) : 0;
-  p->segst_off = take(BH * (bwd_f32mfma(c) ? kReplayWindow : 1) * kCkptEvery *
-                      ttt::scan_backward_segment_elems(c->d, c->m, c->b) * sizeof(float));
+  const size_t segst_bytes = BH * (bwd_f32mfma(c) ? kReplayWindow : 1) * kCkptEvery *
+                             ttt::scan_backward_segment_elems(c->d, c->m, c->b) * sizeof(float);
+  p->segst_off = take(segst_bytes);
+  p->segst2_off = bwd_f32mfma(c) ? take(segst_bytes) : 0;
   p->dstate_off = take(BH * st2);
   p->scratch_off = take(BH * ttt::scan_backward_scratch_elems(c->d, c->m, c->b) * sizeof(float));
   p->dwseq_off = take(BH * st2);
@@ -690,6 +694,26 @@ struct ThetaOverlap {
   const void* prev_x = nullptr;  // the deferred GEMM's X (io dtype)
 };
 
+// The replays beside the walk: a second stream and its events (start, replay done and walk done
+// per slot buffer), and the device's compute units.
+struct ReplayOverlap {
+  hipStream_t side = nullptr;
+  hipEvent_t start = nullptr, rep[2] = {nullptr, nullptr}, walk[2] = {nullptr, nullptr};
+  int cus = 0;
+};
+// from a device's side stream and its events 2 .. 6 (events 0 and 1 serve ThetaOverlap)
+ReplayOverlap replay_overlap(const Side& sd) {
+  ReplayOverlap ro;
+  ro.side = sd.stream;
+  ro.start = sd.events[2];
+  ro.rep[0] = sd.events[3];
+  ro.rep[1] = sd.events[4];
+  ro.walk[0] = sd.events[5];
+  ro.walk[1] = sd.events[6];
+  ro.cus = sd.cus;
+  return ro;
+}
+
 // The gradient GEMMs on rocBLAS.  dq: the direction's dQ|dK|dV (fp32 io) or its bf16 split
 // (split3); thg: theta (fp32 io) or theta stacked three times (split3); xg: the direction's
 // input in the io dtype.
@@ -746,7 +770,8 @@ int32_t theta_operand(const BwdPlan& bp, const void* theta, int64_t D, char* ws,
 int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xg, const void* thg,
                       const float* alpha, int reverse, const float* dyin, const float* ckpt, const float* z, float* dX,
                       float* dtheta, float* dW1_0, float* dW2_0, int accumulate, float* dalpha, char* ws,
-                      hipStream_t s, float* dqkv, const ThetaOverlap& ov = ThetaOverlap()) {
+                      hipStream_t s, float* dqkv, const ThetaOverlap& ov = ThetaOverlap(),
+                      const ReplayOverlap& ro = ReplayOverlap()) {
   const int64_t D = (int64_t)c->H * c->d, BT = c->B * c->T;
   float* dw_seq = (float*)(ws + bp.dwseq_off);
   ttt::BwdArgs ba{};
@@ -783,17 +808,27 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xg
       if (st != TTT_OK) return st;
     }
     // windows of kReplayWindow segments from the last: replay them (one workgroup per chain and
-    // segment), then walk them
+    // segment), then walk them.  With ro.side, where a chain per CU fits beside the walk's
+    // workgroups, window w + 1 is replayed on ro.side during the walk of window w, one segment
+    // (B H workgroups) per launch, into the other of two slot buffers.
     const int64_t nseg = ((c->T + c->b - 1) / c->b + kCkptEvery - 1) / kCkptEvery;
+    const int64_t nwin = (nseg + kReplayWindow - 1) / kReplayWindow;
+    const int64_t BHc = (int64_t)c->B * c->H;
+    const bool split = bp.split != 0;
+    const bool ovl = ro.side && bp.segst2_off && nwin > 1 && ((split ? bp.split : 1) + 1) * BHc <= ro.cus;
+    float* const segbuf[2] = {ba.segst, ovl ? (float*)(ws + bp.segst2_off) : ba.segst};
+    const int64_t seg_floats = kCkptEvery * (int64_t)ttt::scan_backward_segment_elems(c->d, c->m, c->b);
+    auto window = [&](int64_t w, int64_t* lo, int64_t* hi) {
+      *hi = nseg - 1 - w * kReplayWindow;
+      *lo = std::max<int64_t>(0, *hi - kReplayWindow + 1);
+    };
     ttt::ScanArgs ra = scan_args(c, bp.fwd, nullptr, nullptr, nullptr, nullptr, reverse, nullptr, nullptr, nullptr,
                                  nullptr, ws);
     ra.ckpt = const_cast<float*>(ckpt);
     ra.ckpt_every = kCkptEvery;
-    ra.seg_slots = ba.segst;
     ba.replayed = 1;
     // the split walk (four or two workgroups per chain) where they fit co-resident: dQ and dK
     // are added into dqkv, so it starts from zero, and so do the exchange entries and abort flag
-    const bool split = bp.split != 0;
     if (split) {
       const int64_t nx = (int64_t)ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b, bp.split);
       ba.split = bp.split;
@@ -805,17 +840,51 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xg
       if (e == hipSuccess && ba.dqkv_b) e = ttt::launch_zero_u64((uint64_t*)ba.dqkv_b, BT * D, s);
       if (e != hipSuccess) return fail(TTT_ERR_HIP, "clearing launch: %s", hipGetErrorString(e));
     }
-    for (int64_t hi = nseg - 1; hi >= 0; hi -= kReplayWindow) {
-      const int64_t lo = std::max<int64_t>(0, hi - kReplayWindow + 1);
-      ra.seg_lo = ba.seg_lo = lo;
+    if (ovl) {  // ro.side starts after this stream's work so far (the forward pass, the clearing)
+      e = hipEventRecord(ro.start, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(ro.side, ro.start, 0);
+      if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+    }
+    for (int64_t w = 0; w < nwin; ++w) {
+      int64_t lo, hi;
+      window(w, &lo, &hi);
+      const int buf = ovl ? (int)(w & 1) : 0;
+      if (w == 0 || !ovl) {  // the whole window on this stream
+        ra.seg_slots = segbuf[buf];
+        ra.seg_lo = lo;
+        ra.seg_count = (int32_t)(hi - lo + 1);
+        ra.seg_stride = 0;
+        e = timed_launch(TTT_KERNEL_SCAN, s, [&] { return ttt::launch_scan_replay_f32(ra, s); });
+        if (e != hipSuccess) return fail(TTT_ERR_HIP, "segment replay launch: %s", hipGetErrorString(e));
+      } else {
+        e = hipStreamWaitEvent(s, ro.rep[buf], 0);
+        if (e != hipSuccess) return fail(TTT_ERR_HIP, "stream wait: %s", hipGetErrorString(e));
+      }
+      if (ovl && w + 1 < nwin) {  // the next window, beside this one's walk
+        int64_t lo1, hi1;
+        window(w + 1, &lo1, &hi1);
+        const int b1 = (int)((w + 1) & 1);
+        if (w >= 1) e = hipStreamWaitEvent(ro.side, ro.walk[b1], 0);  // window w - 1's walk read it
+        for (int64_t sg = lo1; sg <= hi1 && e == hipSuccess; ++sg) {
+          ttt::ScanArgs r1 = ra;
+          r1.seg_slots = segbuf[b1] + (sg - lo1) * seg_floats;
+          r1.seg_lo = sg;
+          r1.seg_count = 1;
+          r1.seg_stride = (int32_t)(hi1 - lo1 + 1);
+          e = timed_launch(TTT_KERNEL_SCAN, ro.side, [&] { return ttt::launch_scan_replay_f32(r1, ro.side); });
+        }
+        if (e == hipSuccess) e = hipEventRecord(ro.rep[b1], ro.side);
+        if (e != hipSuccess) return fail(TTT_ERR_HIP, "segment replay (side stream): %s", hipGetErrorString(e));
+      }
+      ba.segst = segbuf[buf];
+      ba.seg_lo = lo;
       ba.seg_hi = hi;
-      ra.seg_count = ba.seg_count = (int32_t)(hi - lo + 1);
+      ba.seg_count = (int32_t)(hi - lo + 1);
       ba.first = hi == nseg - 1;
-      e = timed_launch(TTT_KERNEL_SCAN, s, [&] { return ttt::launch_scan_replay_f32(ra, s); });
-      if (e != hipSuccess) return fail(TTT_ERR_HIP, "segment replay launch: %s", hipGetErrorString(e));
       e = timed_launch(TTT_KERNEL_BACKWARD, s, [&] {
         return split ? ttt::launch_scan_backward_split(ba, s) : ttt::launch_scan_backward(ba, s);
       });
+      if (e == hipSuccess && ovl) e = hipEventRecord(ro.walk[buf], s);
       if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
     }
     if (ba.dqkv_b) {  // the four-part walk's parts 2 and 3
@@ -1169,8 +1238,12 @@ int32_t ttt_mlp_backward(const ttt_mlp_config* cfg, const void* X, const void* t
   const void* thg = nullptr;
   st = theta_operand(bp, theta_qkv, D_, ws, s, &thg);
   if (st != TTT_OK) return st;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side* sd = nullptr;
+  hipError_t e = side_for_device(&sd, 7);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
   st = bwd_direction(cfg, bp, X, thg, alpha, reverse != 0, dY, ck, z, dX, dtheta, dW1_0, dW2_0, 0, dalpha, ws, s,
-                     (float*)(ws + bp.dqkv_off));
+                     (float*)(ws + bp.dqkv_off), ThetaOverlap(), replay_overlap(*sd));
   return st == TTT_OK ? ok() : st;
 }
 
@@ -1225,8 +1298,9 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   // stream beside that scan (which takes one CU per head)
   std::lock_guard<std::mutex> lk(g_side_mu);
   Side* sd = nullptr;
-  hipError_t e = side_for_device(&sd, 2);
+  hipError_t e = side_for_device(&sd, 7);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+  const ReplayOverlap ro = replay_overlap(*sd);
   ThetaOverlap ov_b, ov_f;
   ov_b.skip_theta = true;
   ov_f.side = sd->stream;
@@ -1236,11 +1310,11 @@ int32_t ttt_mlp_bidir_backward(const ttt_mlp_config* cfg, const void* X, const v
   ov_f.prev_x = xp;
   if (st == TTT_OK)
     st = bwd_direction(cfg, bpb, xp, thg, alpha_b, 1, dY, ckb, zb, dxp, dtheta, dW1_0, dW2_0, 0, dalpha_b, ws, s,
-                       (float*)(ws + bp.dqkv2_off), ov_b);
+                       (float*)(ws + bp.dqkv2_off), ov_b, ro);
   // the forward pass's backward, with dY = dX'
   if (st == TTT_OK)
     st = bwd_direction(cfg, bp, X, thg, alpha_f, 0, dxp, ckf, zf, dX, dtheta, dW1_0, dW2_0, 1, dalpha_f, ws, s,
-                       (float*)(ws + bp.dqkv_off), ov_f);
+                       (float*)(ws + bp.dqkv_off), ov_f, ro);
   return st == TTT_OK ? ok() : st;
 }
 

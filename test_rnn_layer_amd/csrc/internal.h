@@ -63,9 +63,10 @@ struct ScanArgs {
   float* ckpt;           // forward pass for the backward only: the state (W1 then W2) at the
   int32_t ckpt_every;    // start of every ckpt_every-th mini-batch, [B, H, nseg, 2 d m],
   float* scratch;        // and its operand panels, scan_backward_scratch_elems per (sequence, head)
-  float* seg_slots;      // segment replay only: [B, H, seg_count, ckpt_every, slot] (see backward.hip)
+  float* seg_slots;      // segment replay only: [B, H, seg_stride, ckpt_every, slot] (see backward.hip)
   int64_t seg_lo;        // segment replay only: segments seg_lo .. seg_lo + seg_count - 1
   int32_t seg_count;
+  int32_t seg_stride;    // segment replay only: slots of a chain in seg_slots (0: seg_count)
 };
 
 // LDS bytes the generic scan needs for (d, m, b).

@@ -114,7 +114,8 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int64_t seg = REPLAY ? a.seg_lo + blockIdx.x % a.seg_count : 0;
   const int64_t j0 = REPLAY ? seg * C : 0;
   const int64_t j1 = REPLAY ? min(nblk_all, j0 + C) : nblk_all;
-  float* const slots = REPLAY ? a.seg_slots + (chain * a.seg_count + blockIdx.x % a.seg_count) * C * SLOT : nullptr;
+  const int64_t seg_stride = a.seg_stride > 0 ? a.seg_stride : a.seg_count;
+  float* const slots = REPLAY ? a.seg_slots + (chain * seg_stride + blockIdx.x % a.seg_count) * C * SLOT : nullptr;
 
   f32x4 W1[4][2], W2[2][4], W2T[4][2];
   {
@@ -451,7 +452,7 @@ hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s) {
 
 hipError_t launch_scan_replay_f32(const ScanArgs& a, hipStream_t s) {
   if (a.gelu_tanh || !scan_fwd_f32_supported(a.d, a.m, a.b) || a.ckpt_every <= 0 || a.seg_count <= 0 ||
-      !a.seg_slots)
+      !a.seg_slots || (a.seg_stride > 0 && a.seg_stride < a.seg_count))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(scan_fwd_f32_kernel<true>, dim3((unsigned)(a.B * a.H * a.seg_count)), dim3(FT), 0, s, a);
   return hipGetLastError();
