@@ -253,21 +253,27 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 4);
       // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this part's dM)
-      for (int i = tid; i < n * mh; i += BW) {
-        const int r = i / mh, c = i - r * mh;
-        float v = 0.0f;
-        for (int k = r; k < n; ++k) v = fmaf(t.M[k * b + r], dAq[k * mh + c], v);
-        dG1[i] -= eta * v;
-      }
-      for (int i = tid; i < n * d; i += BW) {
-        const int r = i / d, c = i - r * d;
-        float q = 0.0f, k1 = 0.0f;
-        for (int k = 0; k < n; ++k) {
-          q = fmaf(t.dM[r * b + k], t.K[k * d + c], q);
-          k1 = fmaf(t.dM[k * b + r], t.Q[k * d + c], k1);
+      if (n % 16 == 0) {  // on the matrix cores (M and dM are 0 above their diagonals)
+        prod_mfma<true, false>(dG1, mh, n, mh, n, t.M, b, dAq, mh, -eta, true, 0);
+        prod_mfma<false, false>(dQp, d, n, d, n, t.dM, b, t.K, d, 1.0f, true, 4);
+        prod_mfma<true, false>(dKp, d, n, d, n, t.dM, b, t.Q, d, 1.0f, true, 0);
+      } else {
+        for (int i = tid; i < n * mh; i += BW) {
+          const int r = i / mh, c = i - r * mh;
+          float v = 0.0f;
+          for (int k = r; k < n; ++k) v = fmaf(t.M[k * b + r], dAq[k * mh + c], v);
+          dG1[i] -= eta * v;
         }
-        dQp[i] += q;
-        dKp[i] += k1;
+        for (int i = tid; i < n * d; i += BW) {
+          const int r = i / d, c = i - r * d;
+          float q = 0.0f, k1 = 0.0f;
+          for (int k = 0; k < n; ++k) {
+            q = fmaf(t.dM[r * b + k], t.K[k * d + c], q);
+            k1 = fmaf(t.dM[k * b + r], t.Q[k * d + c], k1);
+          }
+          dQp[i] += q;
+          dKp[i] += k1;
+        }
       }
       __syncthreads();
       // ---- dGh = dG1 * S1; dA (in dG1) = dG1 * Gh * GELU''(A)
