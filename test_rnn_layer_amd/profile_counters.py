@@ -370,12 +370,14 @@ def summarize_backward(d: str, out_md: str | None = None):
         f"Workload: B={wl.B}, T={wl.T:,}, H={wl.H}, d={wl.d}, m={wl.m}, b={wl.b}, bf16 X/θ, fp32 arithmetic and "
         f"gradients; {steps} timed + {warm} warm-up calls under the trace.  One call: both forward passes again "
         "(projection, then the scan that keeps a checkpoint every 32 mini-batches: `scan_fwd_f32_kernel<false>`, "
-        "fp32 matrix cores), then per direction windows of 16 checkpoint segments from the last, each replayed "
-        "(`scan_fwd_f32_kernel<true>`, one workgroup per head and segment) and then walked by the backward scan "
-        "(`scan_backward_split_kernel`, four workgroups per head, one cooperative launch per window; a clearing "
-        "kernel zeroes dQ|dK|dV, the second dQ|dK buffer and the exchange entries per direction, a small kernel "
-        "adds the second buffer in after the walk), the dalpha reduction and the two "
-        "gradient GEMMs (dX, dθ; rocBLAS), all on one stream.", "",
+        "fp32 matrix cores), then per direction windows of 16 checkpoint segments from the last: the first "
+        "replayed on the call's stream (`scan_fwd_f32_kernel<true>`, one workgroup per head and segment), each "
+        "later one on the library's second stream beside the walk of the window before, one segment per launch; "
+        "each window walked by the backward scan (`scan_backward_split_kernel`, four workgroups per head, one "
+        "cooperative launch per window; a clearing kernel zeroes dQ|dK|dV, the second dQ|dK buffer and the "
+        "exchange entries per direction, a small kernel adds the second buffer in after the walk), the dalpha "
+        "reduction, the exact three-part bf16 split of dQ|dK|dV and the two gradient GEMMs (dX, dθ; rocBLAS, "
+        "bf16 operands, fp32 accumulation).", "",
         "Commands (repo root, MI355X):", "",
         f"    mkdir -p {d} && rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o run -- "
         f"python3 bench.py --backward{wl_arg} --steps {steps} --warmup {warm} --no-cpu-baseline > {d}/bench.json",
