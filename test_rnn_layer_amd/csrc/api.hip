@@ -572,7 +572,7 @@ struct BwdPlan {
   // direction's dQ|dK|dV ([B T, 9D]) and theta stacked three times ([9D, D]); with fp32 io none.
   // Then the two rocBLAS workspace slices (caller's stream, side stream).
   bool split3 = false;
-  size_t sp_off = 0, th3_off = 0, blas_off[2];
+  size_t sp_off = 0, th3_off = 0, p3_off = 0, blas_off[2];
 };
 
 int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
@@ -640,6 +640,7 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
   if (p->split3) {
     p->sp_off = take(9 * BTD * sizeof(uint16_t));
     p->th3_off = take(9 * D * D * sizeof(uint16_t));
+    p->p3_off = take(9 * D * D * sizeof(float));
   }
   p->blas_off[0] = take(ttt::grad_gemm_workspace_bytes());
   p->blas_off[1] = bidir ? take(ttt::grad_gemm_workspace_bytes()) : 0;
@@ -741,9 +742,9 @@ int32_t grad_dtheta(const BwdPlan& bp, char* ws, int slot, const void* dq, const
   }
   const char* err = nullptr;
   hipError_t e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] {
-    err = bp.split3 ? ttt::grad_gemm_dtheta_split(slot, (const uint16_t*)dq, (const uint16_t*)xg, dtheta, BT, D,
-                                                  accumulate, ws + bp.blas_off[slot],
-                                                  ttt::grad_gemm_workspace_bytes(), s)
+    err = bp.split3 ? ttt::grad_gemm_dtheta_split(slot, (const uint16_t*)dq, (const uint16_t*)xg, dtheta,
+                                                  (float*)(ws + bp.p3_off), BT, D, accumulate,
+                                                  ws + bp.blas_off[slot], ttt::grad_gemm_workspace_bytes(), s)
                     : ttt::grad_gemm_dtheta(slot, (const float*)dq, (const float*)xg, dtheta, BT, D, accumulate,
                                             ws + bp.blas_off[slot], ttt::grad_gemm_workspace_bytes(), s);
     return err ? hipErrorUnknown : hipSuccess;

@@ -13,8 +13,9 @@
 // accumulation: every product of two bf16 numbers is exact in fp32, so the
 // result has the accuracy of an fp32 GEMM at a third of the bf16 rate, about
 // five times the fp32 matrix-core rate.  dX takes the three parts as one
-// contraction of length 9D against theta stacked three times; dtheta adds the
-// three parts' products, the smallest first.
+// contraction of length 9D against theta stacked three times; dtheta is one
+// product over the 9D columns of the parts, whose three blocks are then added
+// smallest first.
 //
 // rocBLAS takes column-major matrices; a row-major [R, C] matrix is the
 // column-major [C, R] one, so row-major C = A B is computed as C^T = B^T A^T.
@@ -67,6 +68,16 @@ __global__ void split_bf16x3_kernel(const float4* __restrict__ in, uint2* __rest
     o[0] = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
     o[cols4] = make_uint2(m[0] | m[1] << 16, m[2] | m[3] << 16);
     o[2 * cols4] = make_uint2(l[0] | l[1] << 16, l[2] | l[3] << 16);
+  }
+}
+
+// out[i] = (((accumulate ? out[i] : 0) + p[2 n + i]) + p[n + i]) + p[i]: the three parts' products
+// added smallest first (p: [3][n] fp32)
+__global__ void sum3_kernel(const float* __restrict__ p, float* __restrict__ out, int64_t n, int accumulate) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float base = accumulate ? out[i] : 0.0f;
+    out[i] = ((base + p[2 * n + i]) + p[n + i]) + p[i];
   }
 }
 
@@ -147,23 +158,27 @@ const char* grad_gemm_dx_split(int slot, const uint16_t* sp, const uint16_t* the
 }
 
 // dtheta [3D, D] = (accumulate ? dtheta : 0) + l^T X + m^T X + h^T X, with h, m, l the column
-// blocks of S [BT, 9D] (bf16) and X [BT, D] bf16; fp32 accumulation and output.
-const char* grad_gemm_dtheta_split(int slot, const uint16_t* sp, const uint16_t* x16, float* dtheta, int64_t BT,
-                                   int64_t D, int accumulate, void* ws, size_t ws_bytes, hipStream_t s) {
+// blocks of S [BT, 9D] (bf16) and X [BT, D] bf16; fp32 accumulation and output.  One GEMM writes
+// the three products S^T X into p3 ([9D, D] fp32; one product over the 9D columns keeps every CU
+// busy, where three of 3D columns each left a third of the tiles' last round empty), then they
+// are added smallest first.
+const char* grad_gemm_dtheta_split(int slot, const uint16_t* sp, const uint16_t* x16, float* dtheta, float* p3,
+                                   int64_t BT, int64_t D, int accumulate, void* ws, size_t ws_bytes, hipStream_t s) {
   if (D == 0) return nullptr;
   std::lock_guard<std::mutex> lk(g_mu);
   rocblas_handle h = nullptr;
   rocblas_status st = handle_for(slot, s, ws, ws_bytes, &h);
-  const float one = 1.0f;
-  for (int j = 2; j >= 0 && st == rocblas_status_success; --j) {
-    const float beta = (j < 2 || accumulate) ? 1.0f : 0.0f;
-    // column-major: dtheta^T [D, 3D] += X^T [D, BT] (S_j^T)^T, S_j^T the column-major [3D, BT], ld 9D
-    st = rocblas_gemm_ex_64(h, rocblas_operation_none, rocblas_operation_transpose, D, 3 * D, BT, &one, x16,
-                            rocblas_datatype_bf16_r, D, sp + j * 3 * D, rocblas_datatype_bf16_r, 9 * D, &beta,
-                            dtheta, rocblas_datatype_f32_r, D, dtheta, rocblas_datatype_f32_r, D,
-                            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  }
-  return st == rocblas_status_success ? nullptr : status_text(st);
+  const float one = 1.0f, zero = 0.0f;
+  // column-major: p3^T [D, 9D] = X^T [D, BT] (S^T)^T, S^T the column-major [9D, BT]
+  if (st == rocblas_status_success)
+    st = rocblas_gemm_ex_64(h, rocblas_operation_none, rocblas_operation_transpose, D, 9 * D, BT, &one, x16,
+                            rocblas_datatype_bf16_r, D, sp, rocblas_datatype_bf16_r, 9 * D, &zero, p3,
+                            rocblas_datatype_f32_r, D, p3, rocblas_datatype_f32_r, D, rocblas_datatype_f32_r,
+                            rocblas_gemm_algo_standard, 0, 0);
+  if (st != rocblas_status_success) return status_text(st);
+  const int64_t n = 3 * D * D, blocks = std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(sum3_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p3, dtheta, n, accumulate);
+  return hipGetLastError() == hipSuccess ? nullptr : "sum3 launch failed";
 }
 
 // dX [BT, D] = dY [BT, D] + dQKV [BT, 3D] theta [3D, D], row-major, fp32.

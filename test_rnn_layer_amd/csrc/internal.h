@@ -176,8 +176,9 @@ hipError_t split_bf16x3(const float* in, uint16_t* out, int64_t rows, int64_t co
 hipError_t stack3_u16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s);
 const char* grad_gemm_dx_split(int slot, const uint16_t* sp, const uint16_t* theta3, const float* dy, float* dx,
                                int64_t BT, int64_t D, void* ws, size_t ws_bytes, hipStream_t s);
-const char* grad_gemm_dtheta_split(int slot, const uint16_t* sp, const uint16_t* x16, float* dtheta, int64_t BT,
-                                   int64_t D, int accumulate, void* ws, size_t ws_bytes, hipStream_t s);
+// (p3: [9D, D] fp32 scratch for the three parts' products)
+const char* grad_gemm_dtheta_split(int slot, const uint16_t* sp, const uint16_t* x16, float* dtheta, float* p3,
+                                   int64_t BT, int64_t D, int accumulate, void* ws, size_t ws_bytes, hipStream_t s);
 // dalpha[c] = (1 - tanh(alpha[c])^2) sum_r dy[r, c] z[r, c]; part: dalpha_partial_elems(D) floats
 size_t dalpha_partial_elems(int D);
 hipError_t launch_dalpha(const float* dy, const float* z, const float* alpha, float* part, float* dalpha,
