@@ -630,9 +630,12 @@ int32_t make_bwd_plan(const ttt_mlp_config* c, int bidir, BwdPlan* p) {
     p->split = ttt::scan_backward_split_fits(c->B, c->H, c->d, c->m, c->b, 4)   ? 4
                : ttt::scan_backward_split_fits(c->B, c->H, c->d, c->m, c->b, 2) ? 2
                                                                                  : 0;
+    // (the two-part forward pass uses the same entries before the walk)
     if (p->split)
-      p->bxchg_off =
-          take(ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b, p->split) * sizeof(uint64_t) + 256);
+      p->bxchg_off = take(std::max(ttt::scan_backward_split_xchg_elems(c->B, c->H, c->d, c->b, p->split),
+                                   ttt::scan_fwd_f32_split_xchg_elems(c->B, c->H)) *
+                              sizeof(uint64_t) +
+                          256);
     if (p->split == 4) p->dqkvb_off = take(2 * BTD * sizeof(float));
   }
   p->dal_off = take(ttt::dalpha_partial_elems((int)D) * sizeof(float));
@@ -668,11 +671,24 @@ int32_t bwd_forward(const ttt_mlp_config* c, const BwdPlan& bp, const void* xin,
   sa.ckpt = ckpt;
   sa.ckpt_every = kCkptEvery;
   sa.scratch = (float*)(ws + bp.scratch_off);
-  // AUTO: the fp32 matrix-core forward pass with the state in registers where it applies
+  // AUTO: the fp32 matrix-core forward pass with the state in registers where it applies, on two
+  // workgroups per chain where they fit co-resident (exchange entries: the split backward scan's,
+  // unused until the walk; the parts' Z: the dQ|dK|dV buffer, likewise)
   const bool f32mfma = bwd_f32mfma(c);
-  hipError_t e = timed_launch(TTT_KERNEL_SCAN, s, [&] {
+  hipError_t e = hipSuccess;
+  const bool split_fwd = f32mfma && bp.split != 0 && c->T > 0 && ttt::scan_fwd_f32_split_fits(c->B, c->H);
+  if (split_fwd) {
+    const int64_t nx = (int64_t)ttt::scan_fwd_f32_split_xchg_elems(c->B, c->H);
+    sa.xchg = (uint64_t*)(ws + bp.bxchg_off);
+    sa.abort_flag = (uint32_t*)(sa.xchg + nx);
+    sa.zpart = (float*)(ws + bp.dqkv_off);
+    e = ttt::launch_zero_u64(sa.xchg, nx + 1, s);
+    if (e != hipSuccess) return fail(TTT_ERR_HIP, "clearing launch: %s", hipGetErrorString(e));
+  }
+  e = timed_launch(TTT_KERNEL_SCAN, s, [&] {
     return f32mfma ? ttt::launch_scan_fwd_f32(sa, s) : ttt::launch_scan_fwd_ckpt(sa, s);
   });
+  if (e == hipSuccess && split_fwd) e = ttt::launch_fwd_f32_gate(sa, s);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   return TTT_OK;
 }

@@ -67,6 +67,9 @@ struct ScanArgs {
   int64_t seg_lo;        // segment replay only: segments seg_lo .. seg_lo + seg_count - 1
   int32_t seg_count;
   int32_t seg_stride;    // segment replay only: slots of a chain in seg_slots (0: seg_count)
+  // the forward pass on two parts per chain (its exchange entries, scan_fwd_f32_split_xchg_elems,
+  // and abort flag in xchg and abort_flag): the parts' Z partials [2, B, T, D] (fp32)
+  float* zpart;
 };
 
 // LDS bytes the generic scan needs for (d, m, b).
@@ -146,6 +149,13 @@ hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s);
 // mini-batch's slot gets its start state and forward quantities (scan_replay_f32_slot_elems
 // floats, the layout scan_backward_segment_elems describes).
 size_t scan_replay_f32_slot_elems();
+// The forward pass split over two workgroups per chain (launch_scan_fwd_f32 with ScanArgs zpart set:
+// one cooperative launch; xchg and abort_flag point at scan_fwd_f32_split_xchg_elems entries and a
+// flag, zeroed before the launch), where 2 B H of them fit co-resident; launch_fwd_f32_gate then
+// adds the parts' Z and writes Z and Y.
+bool scan_fwd_f32_split_fits(int64_t B, int H);
+size_t scan_fwd_f32_split_xchg_elems(int64_t B, int H);
+hipError_t launch_fwd_f32_gate(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_replay_f32(const ScanArgs& a, hipStream_t s);
 hipError_t launch_scan_backward(const BwdArgs& a, hipStream_t s);
 // The replayed windows' walk with each chain's hidden units split over S co-resident workgroups

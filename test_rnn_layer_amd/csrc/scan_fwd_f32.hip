@@ -36,6 +36,18 @@
 //   Z^T  = W2^T Hq^T + eta G2^T striu(Hq Hk^T)^T            partial -> LDS, summed
 // with y = x + tanh(alpha) z.  A last, short block is padded with zero tokens,
 // which add exact zeros to every sum.  Two workgroup barriers per step.
+//
+// Two parts per chain (the forward pass only): the notes page's on-chip tensor
+// parallel with the chain's hidden units split over two workgroups of one
+// cooperative launch, part p taking units [128 p, 128 p + 128), 16 a wave, so
+// that each CU does half the matrix-core work of a step.  The one contraction
+// over units the recurrence needs, Yhat, is exchanged: each part publishes its
+// sum over its units as tagged 64-bit device-scope stores (mini-batch index + 1
+// in the high word, double-buffered by its parity), polls the other part's and
+// adds the two (a sum of two terms does not depend on their order).  Polls are
+// bounded: past the spin limit a workgroup raises the abort flag and takes NaN.
+// Z, which only feeds the outputs, leaves each part as its partial in a buffer
+// of its own; a small kernel adds the two and applies the gate.
 #include "internal.h"
 #include "mfma_common.h"
 #include "token_block.h"
@@ -86,8 +98,13 @@ __device__ float4 g_zero_chunk;  // zero-initialised, never written: the source 
 // REPLAY false: the forward pass of a whole direction (grid: sequences x heads);
 // REPLAY true: segments seg_lo .. seg_lo + seg_count - 1 of every (sequence, head)
 // (grid: sequences x heads x seg_count)
-template <bool REPLAY>
+constexpr uint32_t kFwdSpinMax = 1u << 20;
+
+// UT: hidden-unit tiles of 16 per wave, 2 (one workgroup per chain) or 1 (two parts per chain)
+template <bool REPLAY, int UT>
 __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void scan_fwd_f32_kernel(ScanArgs a) {
+  constexpr int PARTS = 2 / UT;
+  static_assert(UT == 2 || (UT == 1 && !REPLAY), "the replay runs one workgroup per chain");
   __shared__ __attribute__((aligned(16))) float Stage[NSTG][BLKF];  // token blocks j-1 .. j+1
   __shared__ f32x4 Ypart[FW][4][64];                              // partial Yhat^T: wave, d-tile, lane
   __shared__ f32x4 Zpart[FW][4][64];                              // partial Z^T
@@ -99,11 +116,12 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t chain = REPLAY ? blockIdx.x / a.seg_count : blockIdx.x;  // sequence * H + head
+  const int part = PARTS == 1 ? 0 : (int)(blockIdx.x / (a.B * a.H));  // the chain's part (two parts)
+  const int64_t chain = REPLAY ? blockIdx.x / a.seg_count : blockIdx.x - part * (a.B * a.H);  // sequence * H + head
   const int s = (int)(chain / a.H), h = (int)(chain % a.H);
   const int64_t T = a.T;
   const int D = a.H * FD;
-  const int u0 = 32 * w;
+  const int u0 = (FM / PARTS) * part + 16 * UT * w;  // this wave's first hidden unit
   const int64_t sh = (int64_t)s * a.H + h;
   const int64_t dm = (int64_t)FD * FM;
   const float neta = -a.eta, gs = a.gscale;
@@ -117,7 +135,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int64_t seg_stride = a.seg_stride > 0 ? a.seg_stride : a.seg_count;
   float* const slots = REPLAY ? a.seg_slots + (chain * seg_stride + blockIdx.x % a.seg_count) * C * SLOT : nullptr;
 
-  f32x4 W1[4][2], W2[2][4], W2T[4][2];
+  f32x4 W1[4][UT], W2[UT][4], W2T[4][UT];
   {
     const float* w1 = REPLAY ? a.ckpt + (chain * nseg + seg) * 2 * dm
                              : a.w1_0 + (int64_t)s * a.w_seq_stride + (int64_t)h * dm;
@@ -127,7 +145,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int ut = 0; ut < 2; ++ut) {
+        for (int ut = 0; ut < UT; ++ut) {
           W1[dt][ut][r] = w1[(16 * dt + 4 * g + r) * FM + u0 + 16 * ut + c];
           W2[ut][dt][r] = w2[(u0 + 16 * ut + 4 * g + r) * FD + 16 * dt + c];
           W2T[dt][ut][r] = w2[(u0 + 16 * ut + c) * FD + 16 * dt + 4 * g + r];
@@ -157,6 +175,35 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     return acc;
   };
   auto tok = [&](int64_t p) -> int64_t { return a.reverse ? T - 1 - p : p; };
+  // two parts: this part's sum over its units of this thread's two Yhat values of block jb,
+  // published, and the other part's added (NaN for it after an abort or a time-out)
+  bool failed = false;
+  auto exchange = [&](float2 y, int64_t jb) -> float2 {
+    const uint32_t tag = (uint32_t)(jb + 1);
+    const int par = (int)(jb & 1);
+    uint64_t* mine = a.xchg + ((chain * 2 + part) * 2 + par) * (2 * FT) + 2 * tid;
+    const uint64_t* theirs = a.xchg + ((chain * 2 + (part ^ 1)) * 2 + par) * (2 * FT) + 2 * tid;
+    __hip_atomic_store(mine, ((uint64_t)tag << 32) | __float_as_uint(y.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + 1, ((uint64_t)tag << 32) | __float_as_uint(y.y), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    float2 o = make_float2(__uint_as_float(0x7fc00000u), __uint_as_float(0x7fc00000u));
+    for (uint32_t spin = 0; !failed; ++spin) {
+      const uint64_t e0 = __hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t e1 = __hip_atomic_load(theirs + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)(e0 >> 32) == tag && (uint32_t)(e1 >> 32) == tag) {
+        o = make_float2(__uint_as_float((uint32_t)e0), __uint_as_float((uint32_t)e1));
+        break;
+      }
+      if (spin >= kFwdSpinMax) {
+        __hip_atomic_store(a.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        failed = true;
+      } else if ((spin & 15) == 15 && __hip_atomic_load(a.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        failed = true;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    return make_float2(y.x + o.x, y.y + o.y);
+  };
 
   // token block jb into stage buf: chunk i (thread i, and i + 512 for the first 304
   // threads) is chunk q of row r of panel i / 272 (a wave fills 1 KB of consecutive
@@ -179,8 +226,9 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // carried from block j-1 to its read-out during step j
   f32x4 St_prev = zero4();                 // S^T = K Q^T of block j-1: [t'][t]
-  f32x4 g1_prev[2] = {zero4(), zero4()};   // NG1 = -eta G1 of block j-1, token-major [t][u]
-  f32x4 hkT_prev[2] = {zero4(), zero4()};  // Hk^T of block j-1: [u][t]
+  f32x4 g1_prev[UT], hkT_prev[UT];  // NG1 = -eta G1 of block j-1, token-major [t][u]; Hk^T of block j-1: [u][t]
+#pragma unroll
+  for (int ut = 0; ut < UT; ++ut) g1_prev[ut] = hkT_prev[ut] = zero4();
 
   // -striu of a D-layout [t'][t] tile: the entries with t' = 4g + r > t = c, negated
   bool later[4];
@@ -191,18 +239,20 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // follows that block); this wave's partial Z^T goes to Zpart[w].  Replaying, the
   // block's Aq, Hq, GELU'(Aq) and M go to its slot rs instead (no Z).
   auto readout = [&](const float* prev, const float* g2prev, float* rs) {
-    f32x4 aq[2] = {zero4(), zero4()};
+    f32x4 aq[UT];
+#pragma unroll
+    for (int ut = 0; ut < UT; ++ut) aq[ut] = zero4();
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const f32x4 qf = *(const f32x4*)&prev[OQ + sw(c, 16 * dt + 4 * g)];
 #pragma unroll
-      for (int ut = 0; ut < 2; ++ut)
+      for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
         for (int r = 0; r < 4; ++r) aq[ut] = mfma4(W1[dt][ut][r], qf[r], aq[ut]);
     }
-    f32x4 hqT[2];
+    f32x4 hqT[UT];
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut) {
+    for (int ut = 0; ut < UT; ++ut) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) aq[ut] = mfma4(g1_prev[ut][r], later[r] ? -St_prev[r] : 0.0f, aq[ut]);
       if (REPLAY) {  // [t][m]: lane (g, c) holds token c, units u0 + 16 ut + 4g .. +3
@@ -233,14 +283,14 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
     f32x4 pt = zero4();  // this wave's part of (Hq Hk^T)^T: [t'][t]
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut)
+    for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
       for (int r = 0; r < 4; ++r) pt = mfma4(hkT_prev[ut][r], hqT[ut][r], pt);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       f32x4 zp = zero4();
 #pragma unroll
-      for (int ut = 0; ut < 2; ++ut)
+      for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
         for (int r = 0; r < 4; ++r) zp = mfma4(W2[ut][dt][r], hqT[ut][r], zp);
 #pragma unroll
@@ -253,6 +303,10 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int64_t p = jb * FB + rd_t;
     if (jb < 0 || p >= T) return;
     const int64_t o = ((int64_t)s * T + tok(p)) * D + ch0;
+    if (PARTS == 2) {  // this part's partial; the gate follows once both are in
+      *(float2*)(a.zpart + part * (a.B * T * D) + o) = z;
+      return;
+    }
     *(float2*)(a.z + o) = z;
     const float2 tg = Tg[tid];
     float x0, x1;
@@ -290,7 +344,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int ut = 0; ut < 2; ++ut)
+        for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             o[(16 * dt + 4 * g + r) * FM + u0 + 16 * ut + c] = W1[dt][ut][r];
@@ -299,13 +353,15 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
 
     // ---- A^T = W1^T K^T (this wave's units), S^T = K Q^T
-    f32x4 At[2] = {zero4(), zero4()}, St = zero4();
+    f32x4 At[UT], St = zero4();
+#pragma unroll
+    for (int ut = 0; ut < UT; ++ut) At[ut] = zero4();
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const f32x4 kf = *(const f32x4*)&blk[OK + sw(c, 16 * dt + 4 * g)];
       const f32x4 qf = *(const f32x4*)&blk[OQ + sw(c, 16 * dt + 4 * g)];
 #pragma unroll
-      for (int ut = 0; ut < 2; ++ut)
+      for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
         for (int r = 0; r < 4; ++r) At[ut] = mfma4(W1[dt][ut][r], kf[r], At[ut]);
 #pragma unroll
@@ -313,9 +369,9 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
     // ---- Hk^T = GELU(A^T), S1^T = GELU'(A^T) (both also to this wave's LDS slices
     //      for the token-major reads); partial Yhat^T over this wave's units
-    f32x4 hkT[2];
+    f32x4 hkT[UT];
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut)
+    for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float hv, dv;
@@ -327,7 +383,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     if (REPLAY)  // A and Hk [t][m]: lane (g, c) holds token c, units u0 + 16 ut + 4g .. +3
 #pragma unroll
-      for (int ut = 0; ut < 2; ++ut) {
+      for (int ut = 0; ut < UT; ++ut) {
         *(f32x4*)&sl[SL_A + c * FM + u0 + 16 * ut + 4 * g] = At[ut];
         *(f32x4*)&sl[SL_HK + c * FM + u0 + 16 * ut + 4 * g] = hkT[ut];
       }
@@ -335,7 +391,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int dt = 0; dt < 4; ++dt) {
       f32x4 yp = zero4();
 #pragma unroll
-      for (int ut = 0; ut < 2; ++ut)
+      for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
         for (int r = 0; r < 4; ++r) yp = mfma4(W2[ut][dt][r], hkT[ut][r], yp);
       Ypart[w][dt][lane] = yp;
@@ -345,7 +401,8 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
     // ---- G2 = c (Yhat - V): this thread's two values
     {
-      const float2 y = reduce_part(Ypart);
+      float2 y = reduce_part(Ypart);
+      if (PARTS == 2) y = exchange(y, j);
       const float2 v = *(const float2*)&blk[OV + sw(rd_t, rd_d)];
       const float2 g2 = make_float2(gs * (y.x - v.x), gs * (y.y - v.y));
       *(float2*)&g2cur[rd_t * GS + rd_d] = g2;
@@ -356,9 +413,9 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (!REPLAY) readout(blk_prev, g2prev, nullptr);
     else if (j > j0) readout(blk_prev, g2prev, sl - SLOT);
     // ---- this wave's token-major Hk and S1: [t = 4g + r][u = c]
-    f32x4 hkF[2], s1F[2];
+    f32x4 hkF[UT], s1F[UT];
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut) {
+    for (int ut = 0; ut < UT; ++ut) {
       hkF[ut] = *(const f32x4*)&HkS[w][ut][c * TT + 4 * g];
       s1F[ut] = *(const f32x4*)&DgS[w][ut][c * TT + 4 * g];
     }
@@ -368,25 +425,27 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     __syncthreads();
 
     // ---- Gh = G2 W2^T (token-major), G1 = Gh * S1, NG1 = -eta G1
-    f32x4 g1[2] = {zero4(), zero4()};
+    f32x4 g1[UT];
+#pragma unroll
+    for (int ut = 0; ut < UT; ++ut) g1[ut] = zero4();
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const f32x4 gA = *(const f32x4*)&g2cur[c * GS + 16 * dt + 4 * g];
 #pragma unroll
-      for (int ut = 0; ut < 2; ++ut)
+      for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
         for (int r = 0; r < 4; ++r) g1[ut] = mfma4(gA[r], W2T[dt][ut][r], g1[ut]);
     }
     if (REPLAY)  // Gh, then G1 [t][m]: lane (g, c) holds tokens 4g .. 4g+3 of unit u0 + 16 ut + c
 #pragma unroll
-      for (int ut = 0; ut < 2; ++ut)
+      for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           sl[SL_GH + (4 * g + r) * FM + u0 + 16 * ut + c] = g1[ut][r];
           sl[SL_G1 + (4 * g + r) * FM + u0 + 16 * ut + c] = g1[ut][r] * s1F[ut][r];
         }
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut) g1[ut] = neta * (g1[ut] * s1F[ut]);
+    for (int ut = 0; ut < UT; ++ut) g1[ut] = neta * (g1[ut] * s1F[ut]);
     // ---- state update: W1 += K^T NG1, W2 += Hk^T NG2, W2T += NG2^T Hk (contraction over
     //      the 16 tokens: register r of a token-major tile is tokens 4g + r)
     f32x4 g2c[4];
@@ -399,12 +458,12 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         g2c[dt][r] = neta * g2cur[(4 * g + r) * GS + 16 * dt + c];
       }
 #pragma unroll
-      for (int ut = 0; ut < 2; ++ut)
+      for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
         for (int r = 0; r < 4; ++r) W1[dt][ut] = mfma4(kc[r], g1[ut][r], W1[dt][ut]);
     }
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut)
+    for (int ut = 0; ut < UT; ++ut)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -418,10 +477,11 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (j + NSTG - 1 < j1) stage_async(j + NSTG - 1, sp);
 
     St_prev = St;
-    g1_prev[0] = g1[0];
-    g1_prev[1] = g1[1];
-    hkT_prev[0] = hkT[0];
-    hkT_prev[1] = hkT[1];
+#pragma unroll
+    for (int ut = 0; ut < UT; ++ut) {
+      g1_prev[ut] = g1[ut];
+      hkT_prev[ut] = hkT[ut];
+    }
     sj = sj == NSTG - 1 ? 0 : sj + 1;
   }
 
@@ -444,9 +504,57 @@ bool scan_fwd_f32_supported(int d, int m, int b) { return d == FD && m == FM && 
 
 size_t scan_replay_f32_slot_elems() { return (size_t)SLOT; }
 
+bool scan_fwd_f32_split_fits(int64_t B, int H) {
+  int dev = 0, cus = 0, coop = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_fwd_f32_kernel<false, 1>, FT, 0) != hipSuccess)
+    return false;
+  return 2 * B * H <= (int64_t)cus * per_cu;
+}
+
+size_t scan_fwd_f32_split_xchg_elems(int64_t B, int H) { return (size_t)(B * H) * 2 * 2 * 2 * FT; }
+
+namespace {
+// z = the two parts' partials added; y = x + tanh(alpha) z (io dtype); rows x D elements
+__global__ void fwd_f32_gate_kernel(const float* zpart, int64_t n, int D, const float* alpha, const void* xin,
+                                    void* y, float* z, int bf16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float zv = zpart[i] + zpart[n + i];
+    if (z) z[i] = zv;
+    if (y) {
+      const float tg = tanhf(alpha[i % D]);
+      if (bf16) {
+        const float x = __uint_as_float((uint32_t)((const uint16_t*)xin)[i] << 16);
+        ((__bf16*)y)[i] = (__bf16)fmaf(tg, zv, x);
+      } else {
+        ((float*)y)[i] = fmaf(tg, zv, ((const float*)xin)[i]);
+      }
+    }
+  }
+}
+}  // namespace
+
+hipError_t launch_fwd_f32_gate(const ScanArgs& a, hipStream_t s) {
+  const int64_t n = a.B * a.T * a.H * FD;
+  if (n == 0 || (!a.z && !a.y)) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 16384);
+  hipLaunchKernelGGL(fwd_f32_gate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.zpart, n, (int)(a.H * FD), a.alpha,
+                     a.xin, a.y, a.z, a.bf16);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan_fwd_f32(const ScanArgs& a, hipStream_t s) {
   if (a.gelu_tanh || !scan_fwd_f32_supported(a.d, a.m, a.b) || a.ckpt_every <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(scan_fwd_f32_kernel<false>, dim3((unsigned)(a.B * a.H)), dim3(FT), 0, s, a);
+  if (a.zpart) {  // two parts per chain, one cooperative launch
+    ScanArgs args = a;
+    void* kargs[] = {(void*)&args};
+    return hipLaunchCooperativeKernel((const void*)scan_fwd_f32_kernel<false, 1>, dim3((unsigned)(2 * a.B * a.H)),
+                                      dim3(FT), kargs, 0, s);
+  }
+  hipLaunchKernelGGL((scan_fwd_f32_kernel<false, 2>), dim3((unsigned)(a.B * a.H)), dim3(FT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -454,7 +562,7 @@ hipError_t launch_scan_replay_f32(const ScanArgs& a, hipStream_t s) {
   if (a.gelu_tanh || !scan_fwd_f32_supported(a.d, a.m, a.b) || a.ckpt_every <= 0 || a.seg_count <= 0 ||
       !a.seg_slots || (a.seg_stride > 0 && a.seg_stride < a.seg_count))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(scan_fwd_f32_kernel<true>, dim3((unsigned)(a.B * a.H * a.seg_count)), dim3(FT), 0, s, a);
+  hipLaunchKernelGGL((scan_fwd_f32_kernel<true, 2>), dim3((unsigned)(a.B * a.H * a.seg_count)), dim3(FT), 0, s, a);
   return hipGetLastError();
 }
 
