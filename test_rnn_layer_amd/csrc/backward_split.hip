@@ -215,14 +215,14 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       TTT_MARK(g_marks_scan_backward, mk, 2);
       // ---- dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dHk = dN^T Hq; dG2 (this part) = -eta N^T dZ
       if (n % 16 == 0 && mh % 16 == 0 && d % 16 == 0) {  // on the matrix cores (N, dN are 0 above the diagonal)
-        prod_mfma<false, false>(dGh, mh, n, mh, n, t.dN, b, Hk_, pld, 1.0f, true, 0);
+        // dHq = dGh + dN Hk, and from each finished element dAq = GELU'(Aq) * dHq
+        prod_mfma_epi<false, false>(dGh, mh, n, mh, n, t.dN, b, Hk_, pld, 1.0f, true, 0,
+                                    [=](int r, int c, float v) {
+                                      dAq[r * mh + c] = S1q_[r * pld + c] * v;
+                                      return v;
+                                    });
         prod_mfma<true, false>(dHk, mh, n, mh, n, t.dN, b, Hq_, pld, 1.0f, false, 0);
         prod_mfma<true, false>(t.dG2, d, n, d, n, t.N, b, t.dZ, d, -eta, false, 0);
-        __syncthreads();
-        for (int i = tid; i < n * mh; i += BW) {
-          const int r = i / mh, c = i - r * mh;
-          dAq[i] = S1q_[r * pld + c] * dGh[i];
-        }
       } else {
         for (int i = tid; i < n * mh; i += BW) {
           const int r = i / mh, c = i - r * mh;
@@ -252,11 +252,19 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       prod<1, true>(dKp, d, n, d, mh, G1_, pld, dW1, la1, -eta, false, 9);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 4);
-      // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this part's dM)
-      if (n % 16 == 0) {  // on the matrix cores (M and dM are 0 above their diagonals)
-        prod_mfma<true, false>(dG1, mh, n, mh, n, t.M, b, dAq, mh, -eta, true, 0);
+      // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this part's dM); then dGh = dG1 * S1 and
+      //      dA (in dG1) = dG1 * Gh * GELU''(A); dG2 (this part) += dGh W2
+      if (n % 16 == 0) {  // on the matrix cores (M and dM are 0 above their diagonals); dGh and dA from
+                          // each finished element of dG1
+        prod_mfma_epi<true, false>(dG1, mh, n, mh, n, t.M, b, dAq, mh, -eta, true, 0, [=](int r, int c, float v) {
+          float g, dg, ddg;
+          gelu3(A_[r * pld + c], false, &g, &dg, &ddg);
+          dGh[r * mh + c] = v * S1_[r * pld + c];
+          return v * Gh_[r * pld + c] * ddg;
+        });
         prod_mfma<false, false>(dQp, d, n, d, n, t.dM, b, t.K, d, 1.0f, true, 4);
         prod_mfma<true, false>(dKp, d, n, d, n, t.dM, b, t.Q, d, 1.0f, true, 0);
+        __syncthreads();
       } else {
         for (int i = tid; i < n * mh; i += BW) {
           const int r = i / mh, c = i - r * mh;
@@ -274,18 +282,17 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
           dQp[i] += q;
           dKp[i] += k1;
         }
+        __syncthreads();
+        for (int i = tid; i < n * mh; i += BW) {
+          const int r = i / mh, c = i - r * mh;
+          float g, dg, ddg;
+          gelu3(A_[r * pld + c], false, &g, &dg, &ddg);
+          const float x = dG1[i];
+          dGh[i] = x * S1_[r * pld + c];
+          dG1[i] = x * Gh_[r * pld + c] * ddg;
+        }
+        __syncthreads();
       }
-      __syncthreads();
-      // ---- dGh = dG1 * S1; dA (in dG1) = dG1 * Gh * GELU''(A)
-      for (int i = tid; i < n * mh; i += BW) {
-        const int r = i / mh, c = i - r * mh;
-        float g, dg, ddg;
-        gelu3(A_[r * pld + c], false, &g, &dg, &ddg);
-        const float x = dG1[i];
-        dGh[i] = x * S1_[r * pld + c];
-        dG1[i] = x * Gh_[r * pld + c] * ddg;
-      }
-      __syncthreads();
       prod<1, false>(t.dG2, d, n, d, mh, dGh, mh, W.w2, W.ld2, 1.0f, true);  // dG2 (this part) += dGh W2
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 5);
@@ -330,12 +337,11 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       }
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 6);
-      prod<4, true>(dHk, mh, n, mh, d, t.dG2, d, W.w2, W.ld2, 1.0f, true);  // dHk += dYh W2^T
-      __syncthreads();
-      for (int i = tid; i < n * mh; i += BW) {  // dA += dHk * S1
-        const int r = i / mh, c = i - r * mh;
-        dG1[i] += dHk[i] * S1_[r * pld + c];
-      }
+      // dHk += dYh W2^T, and from each finished element dA += dHk * S1
+      prod_mfma_epi<false, true>(dHk, mh, n, mh, d, t.dG2, d, W.w2, W.ld2, 1.0f, true, 0, [=](int r, int c, float v) {
+        dG1[r * mh + c] += v * S1_[r * pld + c];
+        return v;
+      });
       __syncthreads();
       prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);  // dK (this part) += dA W1^T
       __syncthreads();

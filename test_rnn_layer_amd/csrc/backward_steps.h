@@ -238,6 +238,30 @@ __device__ __attribute__((noinline)) void prod_mfma(float* out, int ldo, int n, 
   }
 }
 
+// prod_mfma with an epilogue: each finished element v of out[r][c] is stored as epi(r, c, v),
+// which may also write elements of other arrays at (r, c) (the elementwise step that follows
+// the product, without a pass and a barrier of its own).  Inlined: an out-of-line call would take
+// the epilogue's closure through private memory.
+template <bool XT, bool WT, class Epi>
+__device__ __forceinline__ void prod_mfma_epi(float* out, int ldo, int n, int C, int K, const float* X,
+                                                        int ldx, const float* W, int ldw, float s, bool acc, int w0,
+                                                        Epi epi) {
+  const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+  const int ct = C >> 4, tiles = ((n + 15) >> 4) * ct;
+  for (int tile = (bwd_wave() + kBwdWaves - w0 % kBwdWaves) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
+    const int r0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
+    const f32x4 v = tile_xw<XT, WT>(X, ldx, min(r0 + i, n - 1), W, ldw, c0 + i, K, q);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = r0 + 4 * q + rr;
+      if (r < n) {
+        float* o = out + (int64_t)r * ldo + c0 + i;
+        *o = epi(r, c0 + i, (acc ? *o : 0.0f) + s * v[rr]);
+      }
+    }
+  }
+}
+
 // out = (acc ? out : 0) + s X W (see prod_valu): on the matrix cores when C and K are multiples of 16
 template <int RG, bool WT>
 __device__ inline void prod(float* out, int ldo, int n, int C, int K, const float* X, int ldx, const float* W,
