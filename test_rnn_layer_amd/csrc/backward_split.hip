@@ -248,23 +248,27 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       rowdot_tril(t.dM, b, n, mh, dAq, mh, G1_, pld, -eta, 4);
       prod<4, true>(dHk, mh, n, mh, d, t.G2, d, dW2, la2, -eta, true, 5);
       prod<1, false>(t.dG2, d, n, d, mh, Hk_, pld, dW2, la2, -eta, true, 5);
-      prod<4, false>(dG1, mh, n, mh, d, t.K, d, dW1, la1, -eta, false, 9);
+      const bool tiled = n % 16 == 0;  // the products below on the matrix cores
+      if (tiled) {  // dG1 = -eta (K dW1' + M^T dAq) (M is 0 above its diagonal), and from each finished
+                    // element dGh = dG1 * S1, dA (in dG1) = dG1 * Gh * GELU''(A)
+        prod_mfma2_epi<false, false, true, false>(dG1, mh, n, mh, d, t.K, d, dW1, la1, n, t.M, b, dAq, mh, -eta, false, 1,
+                                                  [=](int r, int c, float v) {
+                                                    float g, dg, ddg;
+                                                    gelu3(A_[r * pld + c], false, &g, &dg, &ddg);
+                                                    dGh[r * mh + c] = v * S1_[r * pld + c];
+                                                    return v * Gh_[r * pld + c] * ddg;
+                                                  });
+      } else {
+        prod<4, false>(dG1, mh, n, mh, d, t.K, d, dW1, la1, -eta, false, 9);
+      }
       prod<1, true>(dKp, d, n, d, mh, G1_, pld, dW1, la1, -eta, false, 9);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 4);
-      // ---- dG1 -= eta M^T dAq; dQ += dM K; dK += dM^T Q (this part's dM); then dGh = dG1 * S1 and
-      //      dA (in dG1) = dG1 * Gh * GELU''(A); dG2 (this part) += dGh W2
-      if (n % 16 == 0) {  // on the matrix cores (M and dM are 0 above their diagonals); dGh and dA from
-                          // each finished element of dG1
-        prod_mfma_epi<true, false>(dG1, mh, n, mh, n, t.M, b, dAq, mh, -eta, true, 0, [=](int r, int c, float v) {
-          float g, dg, ddg;
-          gelu3(A_[r * pld + c], false, &g, &dg, &ddg);
-          dGh[r * mh + c] = v * S1_[r * pld + c];
-          return v * Gh_[r * pld + c] * ddg;
-        });
+      // ---- dQ += dM K; dK += dM^T Q (this part's dM); dG2 (this part) += dGh W2 (the ragged last
+      //      mini-batch: first dG1 -= eta M^T dAq, dGh and dA, on the vector ALU)
+      if (tiled) {
         prod_mfma<false, false>(dQp, d, n, d, n, t.dM, b, t.K, d, 1.0f, true, 4);
         prod_mfma<true, false>(dKp, d, n, d, n, t.dM, b, t.Q, d, 1.0f, true, 0);
-        __syncthreads();
       } else {
         for (int i = tid; i < n * mh; i += BW) {
           const int r = i / mh, c = i - r * mh;

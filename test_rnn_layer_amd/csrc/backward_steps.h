@@ -262,6 +262,29 @@ __device__ __forceinline__ void prod_mfma_epi(float* out, int ldo, int n, int C,
   }
 }
 
+// The same for out = (acc ? out : 0) + s (X1 W1 + X2 W2): two contractions (lengths K1, K2, multiples
+// of 16) summed per output tile, then the epilogue
+template <bool XT1, bool WT1, bool XT2, bool WT2, class Epi>
+__device__ __forceinline__ void prod_mfma2_epi(float* out, int ldo, int n, int C, int K1, const float* X1, int ldx1,
+                                               const float* W1, int ldw1, int K2, const float* X2, int ldx2,
+                                               const float* W2, int ldw2, float s, bool acc, int w0, Epi epi) {
+  const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
+  const int ct = C >> 4, tiles = ((n + 15) >> 4) * ct;
+  for (int tile = (bwd_wave() + kBwdWaves - w0 % kBwdWaves) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
+    const int r0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
+    const f32x4 v = tile_xw<XT1, WT1>(X1, ldx1, min(r0 + i, n - 1), W1, ldw1, c0 + i, K1, q) +
+                    tile_xw<XT2, WT2>(X2, ldx2, min(r0 + i, n - 1), W2, ldw2, c0 + i, K2, q);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = r0 + 4 * q + rr;
+      if (r < n) {
+        float* o = out + (int64_t)r * ldo + c0 + i;
+        *o = epi(r, c0 + i, (acc ? *o : 0.0f) + s * v[rr]);
+      }
+    }
+  }
+}
+
 // out = (acc ? out : 0) + s X W (see prod_valu): on the matrix cores when C and K are multiples of 16
 template <int RG, bool WT>
 __device__ inline void prod(float* out, int ldo, int n, int C, int K, const float* X, int ldx, const float* W,
