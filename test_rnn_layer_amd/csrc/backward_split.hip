@@ -135,6 +135,12 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       TTT_MARK(g_marks_scan_backward, mk, 0);
       const int n = (int)min((int64_t)b, T - j * b);
       const float* sl = seg + (j - j0) * slot;
+      // this part's output row of mini-batch row r: dQ | dK | dV of [B, T, 3D] (parts 0, 1), or
+      // dQ | dK of the [B, T, 2D] buffer (parts 2, 3), at this head's columns
+      auto out_row = [=](int r) -> float* {
+        const int64_t tr = (int64_t)s * T + rw.tok(j * b + r);
+        return half < 2 ? a.dqkv + tr * 3 * D + h * d : a.dqkv_b + tr * 2 * D + h * d;
+      };
       // the slot's panels, this part's columns (row stride m)
       const float* fq = sl + 2 * dm;
       const float* ro = fq + 5 * bm + (int64_t)b * d;  // the read-out: Aq, Hq, GELU'(Aq), M
@@ -267,7 +273,11 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       // ---- dQ += dM K; dK += dM^T Q (this part's dM); dG2 (this part) += dGh W2 (the ragged last
       //      mini-batch: first dG1 -= eta M^T dAq, dGh and dA, on the vector ALU)
       if (tiled) {
-        prod_mfma<false, false>(dQp, d, n, d, n, t.dM, b, t.K, d, 1.0f, true, 4);
+        // dQ of this part is complete: each finished element goes straight to its output
+        prod_mfma_epi<false, false>(dQp, d, n, d, n, t.dM, b, t.K, d, 1.0f, true, 4, [=](int r, int c, float v) {
+          atomicAdd(out_row(r) + c, v);
+          return v;
+        });
         prod_mfma<true, false>(dKp, d, n, d, n, t.dM, b, t.Q, d, 1.0f, true, 0);
       } else {
         for (int i = tid; i < n * mh; i += BW) {
@@ -347,18 +357,27 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         return v;
       });
       __syncthreads();
-      prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);  // dK (this part) += dA W1^T
-      __syncthreads();
+      if (tiled) {  // dK (this part) += dA W1^T, each finished element straight to its output
+        prod_mfma_epi<false, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true, 0, [=](int r, int c, float v) {
+          atomicAdd(out_row(r) + D + c, v);
+          return v;
+        });
+      } else {
+        prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);
+        __syncthreads();
+      }
       TTT_MARK(g_marks_scan_backward, mk, 7);
-      // ---- dQ and dK: this part's sums added into [B, T, 3D] (parts 0, 1) or the [B, T, 2D] buffer
-      //      (parts 2, 3), both zeroed before the walk; dV = -dYh (part 0); the adjoint's part
-      //      handed to the mini-batch before: dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
+      // ---- dQ and dK (the ragged last mini-batch; the others' went out above): this part's sums
+      //      added into [B, T, 3D] (parts 0, 1) or the [B, T, 2D] buffer (parts 2, 3), both zeroed
+      //      before the walk; dV = -dYh (part 0); the adjoint's part handed to the mini-batch
+      //      before: dW1 += Q^T dAq + K^T dA; dW2 += Hq^T dZ + dGh^T G2 + Hk^T dYh
       for (int i = tid; i < n * d; i += BW) {
         const int r = i / d, c = i - r * d;
-        const int64_t tr = (int64_t)s * T + rw.tok(j * b + r);
-        float* row = half < 2 ? a.dqkv + tr * 3 * D + h * d + c : a.dqkv_b + tr * 2 * D + h * d + c;
-        atomicAdd(row, dQp[i]);
-        atomicAdd(row + D, dKp[i]);
+        float* row = out_row(r) + c;
+        if (!tiled) {
+          atomicAdd(row, dQp[i]);
+          atomicAdd(row + D, dKp[i]);
+        }
         if (half == 0) row[2 * D] = -t.dG2[i];
       }
       Terms u1{2, {t.Q, t.K}, {d, d}, {dAq, dG1}, {mh, mh}};
