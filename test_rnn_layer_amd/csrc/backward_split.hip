@@ -125,6 +125,10 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   const int64_t plane = a.B * a.H * T * d;
   Rows rw{a.qkv + sh * T * d, a.qkv + plane + sh * T * d, a.qkv + 2 * plane + sh * T * d, T, a.reverse};
   bool failed = false;  // this thread saw an abort or a time-out
+  // the gate factor of this thread's channel: its elements i of the b x d panels all have the
+  // column tid mod d (BW is a multiple of d)
+  static_assert(BW % kSplitD == 0, "a thread's column is fixed");
+  const float tg = tanhf(a.alpha[h * d + tid % d]);
 
   for (int64_t sg = a.seg_hi; sg >= a.seg_lo; --sg) {
     const int64_t j0 = sg * C, j1 = min(nmb, j0 + C);
@@ -206,9 +210,8 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         for (int i = tid; i < b * b; i += BW) t.M[i] = ro[3 * bm + i];
       }
       for (int i = tid; i < n * d; i += BW) {
-        const int r = i / d, c = i - r * d;
-        const int ch = h * d + c;
-        t.dZ[i] = tanhf(a.alpha[ch]) * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + ch];
+        const int r = i / d;
+        t.dZ[i] = tg * a.dy[((int64_t)s * T + rw.tok(j * b + r)) * D + h * d + (i - r * d)];
       }
       if constexpr (S == 4) vmem_done();  // this wave's direct loads have landed
       __syncthreads();
@@ -319,35 +322,61 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         for (int i = tid; i < n * d; i += BW)
           __hip_atomic_store(mine + i, ((uint64_t)tag << 32) | __float_as_uint(t.dG2[i]), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
-        for (int i = tid; i < n * d; i += BW) {
-          float sum = 0.0f;
+        // this thread's (up to) two elements i0 = tid, i1 = tid + BW; each round issues the loads of
+        // every partial still missing before looking at any, so a round costs one trip
+        static_assert(kSplitB * kSplitD <= 2 * BW, "two dG2 elements per thread");
+        const int i0 = tid, i1 = tid + BW;
+        const bool h0 = i0 < n * d, h1 = i1 < n * d;
+        float v0[S], v1[S];
+        uint32_t miss = 0;  // bit 2q: element 0 of part q missing, bit 2q + 1: element 1
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          v0[q] = v1[q] = __uint_as_float(0x7fc00000u);  // NaN unless the partial arrives
+          if (q == half) {
+            if (h0) v0[q] = t.dG2[i0];
+            if (h1) v1[q] = t.dG2[i1];
+          } else {
+            miss |= (h0 ? 1u : 0u) << (2 * q);
+            miss |= (h1 ? 1u : 0u) << (2 * q + 1);
+          }
+        }
+        for (uint32_t spin = 0; miss && !failed; ++spin) {
+          uint64_t e0[S], e1[S];
 #pragma unroll
           for (int q = 0; q < S; ++q) {
-            float v = __uint_as_float(0x7fc00000u);  // NaN unless the partial arrives
-            if (q == half) {
-              v = t.dG2[i];
-            } else {
-              const uint64_t* theirs = xc + (q * 2 + par) * (int64_t)(b * d);
-              for (uint32_t spin = 0; !failed; ++spin) {
-                const uint64_t e = __hip_atomic_load(theirs + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if ((uint32_t)(e >> 32) == tag) {
-                  v = __uint_as_float((uint32_t)e);
-                  break;
-                }
-                if (spin >= kSplitSpinMax) {
-                  __hip_atomic_store(a.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                  failed = true;
-                } else if ((spin & 15) == 15 &&
-                           __hip_atomic_load(a.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                  failed = true;
-                }
-                __builtin_amdgcn_s_sleep(1);
-              }
-            }
-            sum = q == 0 ? v : sum + v;
+            const uint64_t* theirs = xc + (q * 2 + par) * (int64_t)(b * d);
+            if (miss >> (2 * q) & 1u) e0[q] = __hip_atomic_load(theirs + i0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (miss >> (2 * q + 1) & 1u)
+              e1[q] = __hip_atomic_load(theirs + i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          t.dG2[i] = a.gscale * sum;
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            if ((miss >> (2 * q) & 1u) && (uint32_t)(e0[q] >> 32) == tag) {
+              v0[q] = __uint_as_float((uint32_t)e0[q]);
+              miss &= ~(1u << (2 * q));
+            }
+            if ((miss >> (2 * q + 1) & 1u) && (uint32_t)(e1[q] >> 32) == tag) {
+              v1[q] = __uint_as_float((uint32_t)e1[q]);
+              miss &= ~(1u << (2 * q + 1));
+            }
+          }
+          if (!miss) break;
+          if (spin >= kSplitSpinMax) {
+            __hip_atomic_store(a.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            failed = true;
+          } else if ((spin & 15) == 15 && __hip_atomic_load(a.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            failed = true;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
+        float s0 = v0[0], s1 = v1[0];  // the parts' partials added in the parts' order
+#pragma unroll
+        for (int q = 1; q < S; ++q) {
+          s0 += v0[q];
+          s1 += v1[q];
+        }
+        if (h0) t.dG2[i0] = a.gscale * s0;
+        if (h1) t.dG2[i1] = a.gscale * s1;
       }
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 6);
