@@ -109,6 +109,10 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
   float* dKp = dQp + (int64_t)b * d;
   // with four parts the step's slot panels in LDS (rows of mh + 4), after the scratch
   constexpr int pld = S == 4 ? mh + 4 : m;  // their row stride (in the slot: m)
+  // rounds of a product tile's contraction issued at once (all four with four parts; with two, the
+  // registers allow two)
+  constexpr int kUnr = S == 4 ? 4 : 2;
+  constexpr bool kInl = S == 4;  // the products inlined (with two parts they stay out of line)
   float* const spl = dKp + (int64_t)b * d;
   uint64_t* xc = a.xchg + sh * 2 * S * (int64_t)(b * d);  // [part][parity][b d]
 
@@ -219,19 +223,19 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       // ---- N (this part) = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
       rowdot_tril(t.N, b, n, mh, Hq_, pld, Hk_, pld, 1.0f);
       rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
-      prod<4, true>(dGh, mh, n, mh, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
+      prod_sel<false, true, kInl, kUnr>(dGh, mh, n, mh, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 2);
       // ---- dAq = (dZ W2^T + dN Hk) * GELU'(Aq); dHk = dN^T Hq; dG2 (this part) = -eta N^T dZ
       if (n % 16 == 0 && mh % 16 == 0 && d % 16 == 0) {  // on the matrix cores (N, dN are 0 above the diagonal)
         // dHq = dGh + dN Hk, and from each finished element dAq = GELU'(Aq) * dHq
-        prod_mfma_epi<false, false>(dGh, mh, n, mh, n, t.dN, b, Hk_, pld, 1.0f, true, 0,
+        prod_mfma_epi<false, false, kUnr>(dGh, mh, n, mh, n, t.dN, b, Hk_, pld, 1.0f, true, 0,
                                     [=](int r, int c, float v) {
                                       dAq[r * mh + c] = S1q_[r * pld + c] * v;
                                       return v;
                                     });
-        prod_mfma<true, false>(dHk, mh, n, mh, n, t.dN, b, Hq_, pld, 1.0f, false, 0);
-        prod_mfma<true, false>(t.dG2, d, n, d, n, t.N, b, t.dZ, d, -eta, false, 0);
+        prod_sel<true, false, kInl, kUnr>(dHk, mh, n, mh, n, t.dN, b, Hq_, pld, 1.0f, false, 0);
+        prod_sel<true, false, kInl, kUnr>(t.dG2, d, n, d, n, t.N, b, t.dZ, d, -eta, false, 0);
       } else {
         for (int i = tid; i < n * mh; i += BW) {
           const int r = i / mh, c = i - r * mh;
@@ -253,14 +257,14 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       TTT_MARK(g_marks_scan_backward, mk, 3);
       // ---- dQ (this part) = dAq W1^T; dM (this part) = tril(-eta dAq G1^T); with the adjoint's part:
       //      dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK (this part) = -eta G1 dW1'^T
-      prod<1, true>(dQp, d, n, d, mh, dAq, mh, W.w1, W.ld1, 1.0f, false);
+      prod_sel<false, true, kInl, kUnr>(dQp, d, n, d, mh, dAq, mh, W.w1, W.ld1, 1.0f, false, 0);
       rowdot_tril(t.dM, b, n, mh, dAq, mh, G1_, pld, -eta, 4);
-      prod<4, true>(dHk, mh, n, mh, d, t.G2, d, dW2, la2, -eta, true, 5);
-      prod<1, false>(t.dG2, d, n, d, mh, Hk_, pld, dW2, la2, -eta, true, 5);
+      prod_sel<false, true, kInl, kUnr>(dHk, mh, n, mh, d, t.G2, d, dW2, la2, -eta, true, 5);
+      prod_sel<false, false, kInl, kUnr>(t.dG2, d, n, d, mh, Hk_, pld, dW2, la2, -eta, true, 5);
       const bool tiled = n % 16 == 0;  // the products below on the matrix cores
       if (tiled) {  // dG1 = -eta (K dW1' + M^T dAq) (M is 0 above its diagonal), and from each finished
                     // element dGh = dG1 * S1, dA (in dG1) = dG1 * Gh * GELU''(A)
-        prod_mfma2_epi<false, false, true, false>(dG1, mh, n, mh, d, t.K, d, dW1, la1, n, t.M, b, dAq, mh, -eta, false, 1,
+        prod_mfma2_epi<false, false, true, false, kUnr>(dG1, mh, n, mh, d, t.K, d, dW1, la1, n, t.M, b, dAq, mh, -eta, false, 1,
                                                   [=](int r, int c, float v) {
                                                     float g, dg, ddg;
                                                     gelu3(A_[r * pld + c], false, &g, &dg, &ddg);
@@ -268,20 +272,20 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
                                                     return v * Gh_[r * pld + c] * ddg;
                                                   });
       } else {
-        prod<4, false>(dG1, mh, n, mh, d, t.K, d, dW1, la1, -eta, false, 9);
+        prod_sel<false, false, kInl, kUnr>(dG1, mh, n, mh, d, t.K, d, dW1, la1, -eta, false, 9);
       }
-      prod<1, true>(dKp, d, n, d, mh, G1_, pld, dW1, la1, -eta, false, 9);
+      prod_sel<false, true, kInl, kUnr>(dKp, d, n, d, mh, G1_, pld, dW1, la1, -eta, false, 9);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 4);
       // ---- dQ += dM K; dK += dM^T Q (this part's dM); dG2 (this part) += dGh W2 (the ragged last
       //      mini-batch: first dG1 -= eta M^T dAq, dGh and dA, on the vector ALU)
       if (tiled) {
         // dQ of this part is complete: each finished element goes straight to its output
-        prod_mfma_epi<false, false>(dQp, d, n, d, n, t.dM, b, t.K, d, 1.0f, true, 4, [=](int r, int c, float v) {
+        prod_mfma_epi<false, false, kUnr>(dQp, d, n, d, n, t.dM, b, t.K, d, 1.0f, true, 4, [=](int r, int c, float v) {
           atomicAdd(out_row(r) + c, v);
           return v;
         });
-        prod_mfma<true, false>(dKp, d, n, d, n, t.dM, b, t.Q, d, 1.0f, true, 0);
+        prod_sel<true, false, kInl, kUnr>(dKp, d, n, d, n, t.dM, b, t.Q, d, 1.0f, true, 0);
       } else {
         for (int i = tid; i < n * mh; i += BW) {
           const int r = i / mh, c = i - r * mh;
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         }
         __syncthreads();
       }
-      prod<1, false>(t.dG2, d, n, d, mh, dGh, mh, W.w2, W.ld2, 1.0f, true);  // dG2 (this part) += dGh W2
+      prod_sel<false, false, kInl, kUnr>(t.dG2, d, n, d, mh, dGh, mh, W.w2, W.ld2, 1.0f, true, 0);  // dG2 (this part) += dGh W2
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 5);
       // ---- dG2 = the parts' partials added in the parts' order, exchanged; dYh = c dG2 (in dG2's
@@ -381,18 +385,18 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 6);
       // dHk += dYh W2^T, and from each finished element dA += dHk * S1
-      prod_mfma_epi<false, true>(dHk, mh, n, mh, d, t.dG2, d, W.w2, W.ld2, 1.0f, true, 0, [=](int r, int c, float v) {
+      prod_mfma_epi<false, true, kUnr>(dHk, mh, n, mh, d, t.dG2, d, W.w2, W.ld2, 1.0f, true, 0, [=](int r, int c, float v) {
         dG1[r * mh + c] += v * S1_[r * pld + c];
         return v;
       });
       __syncthreads();
       if (tiled) {  // dK (this part) += dA W1^T, each finished element straight to its output
-        prod_mfma_epi<false, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true, 0, [=](int r, int c, float v) {
+        prod_mfma_epi<false, true, kUnr>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true, 0, [=](int r, int c, float v) {
           atomicAdd(out_row(r) + D + c, v);
           return v;
         });
       } else {
-        prod<1, true>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true);
+        prod_sel<false, true, kInl, kUnr>(dKp, d, n, d, mh, dG1, mh, W.w1, W.ld1, 1.0f, true, 0);
         __syncthreads();
       }
       TTT_MARK(g_marks_scan_backward, mk, 7);

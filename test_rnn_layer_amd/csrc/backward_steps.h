@@ -190,13 +190,14 @@ __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
 __device__ __forceinline__ int bwd_wave() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
 // sum_k X(row, k) W(k, col) over k < K (K a multiple of 16) for this lane's row and column;
-// X(r, k) = X[r ldx + k], or X[k ldx + r] when XT; W(k, c) = W[k ldw + c], or W[c ldw + k] when WT
-template <bool XT, bool WT>
+// X(r, k) = X[r ldx + k], or X[k ldx + r] when XT; W(k, c) = W[k ldw + c], or W[c ldw + k] when WT.
+// UNR: rounds of four k issued together (their loads before their products)
+template <bool XT, bool WT, int UNR = 2>
 __device__ __forceinline__ f32x4 tile_xw(const float* X, int ldx, int row, const float* W, int ldw, int col, int K,
                                          int q) {
   const int kq = K >> 2, kb = q * kq;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 2
+#pragma unroll UNR
   for (int k = 0; k < kq; k += 4) {
     float x[4], y[4];
     if (XT) {
@@ -241,8 +242,8 @@ __device__ __attribute__((noinline)) void prod_mfma(float* out, int ldo, int n, 
 // prod_mfma with an epilogue: each finished element v of out[r][c] is stored as epi(r, c, v),
 // which may also write elements of other arrays at (r, c) (the elementwise step that follows
 // the product, without a pass and a barrier of its own).  Inlined: an out-of-line call would take
-// the epilogue's closure through private memory.
-template <bool XT, bool WT, class Epi>
+// the epilogue's closure through private memory.  UNR: see tile_xw.
+template <bool XT, bool WT, int UNR, class Epi>
 __device__ __forceinline__ void prod_mfma_epi(float* out, int ldo, int n, int C, int K, const float* X,
                                                         int ldx, const float* W, int ldw, float s, bool acc, int w0,
                                                         Epi epi) {
@@ -250,7 +251,7 @@ __device__ __forceinline__ void prod_mfma_epi(float* out, int ldo, int n, int C,
   const int ct = C >> 4, tiles = ((n + 15) >> 4) * ct;
   for (int tile = (bwd_wave() + kBwdWaves - w0 % kBwdWaves) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
     const int r0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
-    const f32x4 v = tile_xw<XT, WT>(X, ldx, min(r0 + i, n - 1), W, ldw, c0 + i, K, q);
+    const f32x4 v = tile_xw<XT, WT, UNR>(X, ldx, min(r0 + i, n - 1), W, ldw, c0 + i, K, q);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int r = r0 + 4 * q + rr;
@@ -262,9 +263,19 @@ __device__ __forceinline__ void prod_mfma_epi(float* out, int ldo, int n, int C,
   }
 }
 
+// prod_mfma inlined with all UNR rounds at once (INL), or the out-of-line call
+template <bool XT, bool WT, bool INL, int UNR>
+__device__ __forceinline__ void prod_sel(float* out, int ldo, int n, int C, int K, const float* X, int ldx,
+                                         const float* W, int ldw, float s, bool acc, int w0) {
+  if constexpr (INL)
+    prod_mfma_epi<XT, WT, UNR>(out, ldo, n, C, K, X, ldx, W, ldw, s, acc, w0, [](int, int, float v) { return v; });
+  else
+    prod_mfma<XT, WT>(out, ldo, n, C, K, X, ldx, W, ldw, s, acc, w0);
+}
+
 // The same for out = (acc ? out : 0) + s (X1 W1 + X2 W2): two contractions (lengths K1, K2, multiples
 // of 16) summed per output tile, then the epilogue
-template <bool XT1, bool WT1, bool XT2, bool WT2, class Epi>
+template <bool XT1, bool WT1, bool XT2, bool WT2, int UNR, class Epi>
 __device__ __forceinline__ void prod_mfma2_epi(float* out, int ldo, int n, int C, int K1, const float* X1, int ldx1,
                                                const float* W1, int ldw1, int K2, const float* X2, int ldx2,
                                                const float* W2, int ldw2, float s, bool acc, int w0, Epi epi) {
@@ -272,8 +283,8 @@ __device__ __forceinline__ void prod_mfma2_epi(float* out, int ldo, int n, int C
   const int ct = C >> 4, tiles = ((n + 15) >> 4) * ct;
   for (int tile = (bwd_wave() + kBwdWaves - w0 % kBwdWaves) % kBwdWaves; tile < tiles; tile += kBwdWaves) {
     const int r0 = (tile / ct) * 16, c0 = (tile % ct) * 16;
-    const f32x4 v = tile_xw<XT1, WT1>(X1, ldx1, min(r0 + i, n - 1), W1, ldw1, c0 + i, K1, q) +
-                    tile_xw<XT2, WT2>(X2, ldx2, min(r0 + i, n - 1), W2, ldw2, c0 + i, K2, q);
+    const f32x4 v = tile_xw<XT1, WT1, UNR>(X1, ldx1, min(r0 + i, n - 1), W1, ldw1, c0 + i, K1, q) +
+                    tile_xw<XT2, WT2, UNR>(X2, ldx2, min(r0 + i, n - 1), W2, ldw2, c0 + i, K2, q);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int r = r0 + 4 * q + rr;
