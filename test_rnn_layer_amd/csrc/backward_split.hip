@@ -413,10 +413,15 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
         }
         if (half == 0) row[2 * D] = -t.dG2[i];
       }
-      Terms u1{2, {t.Q, t.K}, {d, d}, {dAq, dG1}, {mh, mh}};
-      rank_update_any(dW1, la1, d, mh, n, u1, 1.0f);
-      Terms u2{3, {Hq_, dGh, Hk_}, {pld, mh, pld}, {t.dZ, t.G2, t.dG2}, {d, d, d}};
-      rank_update_any(dW2, la2, mh, d, n, u2, 1.0f);
+      if constexpr (kInl) {  // inlined, like the products
+        rank_update_pipe_inl<2>(dW1, la1, d, mh, n, t.Q, d, dAq, mh, t.K, d, dG1, mh, nullptr, 0, nullptr, 0, 1.0f, 0);
+        rank_update_pipe_inl<3>(dW2, la2, mh, d, n, Hq_, pld, t.dZ, d, dGh, mh, t.G2, d, Hk_, pld, t.dG2, d, 1.0f, 0);
+      } else {
+        Terms u1{2, {t.Q, t.K}, {d, d}, {dAq, dG1}, {mh, mh}};
+        rank_update_any(dW1, la1, d, mh, n, u1, 1.0f);
+        Terms u2{3, {Hq_, dGh, Hk_}, {pld, mh, pld}, {t.dZ, t.G2, t.dG2}, {d, d, d}};
+        rank_update_any(dW2, la2, mh, d, n, u2, 1.0f);
+      }
     }
   }
   __syncthreads();

@@ -354,11 +354,10 @@ __device__ __attribute__((noinline)) void rank_update_mfma(float* S, int ldS, in
 // and old values while the current tile's products run, so that one tile's load latency is
 // paid per call rather than per tile (NP sizes the register sets: two of 8 NP + 4 floats).
 template <int NP>
-__device__ __attribute__((noinline)) void rank_update_pipe(float* S, int ldS, int R, int C, int n,
-                                                           const float* P0, int lp0, const float* Q0, int lq0,
-                                                           const float* P1, int lp1, const float* Q1, int lq1,
-                                                           const float* P2, int lp2, const float* Q2, int lq2,
-                                                           float s, int w0) {
+__device__ __forceinline__ void rank_update_pipe_inl(float* S, int ldS, int R, int C, int n, const float* P0, int lp0,
+                                                     const float* Q0, int lq0, const float* P1, int lp1,
+                                                     const float* Q1, int lq1, const float* P2, int lp2,
+                                                     const float* Q2, int lq2, float s, int w0) {
   const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
   const int ct = C >> 4, tiles = (R >> 4) * ct;
   const float* P[3] = {P0, P1, P2};
@@ -406,6 +405,16 @@ __device__ __attribute__((noinline)) void rank_update_pipe(float* S, int ldS, in
     if (next >= tiles) return;
     tile = next;
   }
+}
+
+// the same as an out-of-line call
+template <int NP>
+__device__ __attribute__((noinline)) void rank_update_pipe(float* S, int ldS, int R, int C, int n,
+                                                           const float* P0, int lp0, const float* Q0, int lq0,
+                                                           const float* P1, int lp1, const float* Q1, int lq1,
+                                                           const float* P2, int lp2, const float* Q2, int lq2,
+                                                           float s, int w0) {
+  rank_update_pipe_inl<NP>(S, ldS, R, C, n, P0, lp0, Q0, lq0, P1, lp1, Q1, lq1, P2, lp2, Q2, lq2, s, w0);
 }
 
 __device__ inline void rank_update_any(float* S, int ldS, int R, int C, int n, const Terms& tm, float s,
