@@ -221,8 +221,8 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 1);
       // ---- N (this part) = tril(Hq Hk^T); dN = tril(-eta dZ G2^T); dZ W2^T (into dGh for now)
-      rowdot_tril(t.N, b, n, mh, Hq_, pld, Hk_, pld, 1.0f);
-      rowdot_tril(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
+      rowdot_tril<kUnr>(t.N, b, n, mh, Hq_, pld, Hk_, pld, 1.0f);
+      rowdot_tril<kUnr>(t.dN, b, n, d, t.dZ, d, t.G2, d, -eta, 1);
       prod_sel<false, true, kInl, kUnr>(dGh, mh, n, mh, d, t.dZ, d, W.w2, W.ld2, 1.0f, false, 2);
       __syncthreads();
       TTT_MARK(g_marks_scan_backward, mk, 2);
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(BW) void scan_backward_split_kernel(BwdArgs a) {
       // ---- dQ (this part) = dAq W1^T; dM (this part) = tril(-eta dAq G1^T); with the adjoint's part:
       //      dHk -= eta G2 dW2'^T, dG2 -= eta Hk dW2', dG1 = -eta K dW1', dK (this part) = -eta G1 dW1'^T
       prod_sel<false, true, kInl, kUnr>(dQp, d, n, d, mh, dAq, mh, W.w1, W.ld1, 1.0f, false, 0);
-      rowdot_tril(t.dM, b, n, mh, dAq, mh, G1_, pld, -eta, 4);
+      rowdot_tril<kUnr>(t.dM, b, n, mh, dAq, mh, G1_, pld, -eta, 4);
       prod_sel<false, true, kInl, kUnr>(dHk, mh, n, mh, d, t.G2, d, dW2, la2, -eta, true, 5);
       prod_sel<false, false, kInl, kUnr>(t.dG2, d, n, d, mh, Hk_, pld, dW2, la2, -eta, true, 5);
       const bool tiled = n % 16 == 0;  // the products below on the matrix cores

@@ -437,6 +437,8 @@ __device__ inline void rank_update_any(float* S, int ldS, int R, int C, int n, c
 }
 
 // tril(s X Y^T) (see rowdot_tril_valu): one tile on wave w0 when n <= 16 and K is a multiple of 16
+// (UNR: see tile_xw)
+template <int UNR = 2>
 __device__ inline void rowdot_tril(float* out, int ldo, int n, int K, const float* X, int ldx, const float* Y,
                                    int ldy, float s, int w0 = 0) {
   if (n > 16 || K % 16 != 0) {
@@ -446,7 +448,7 @@ __device__ inline void rowdot_tril(float* out, int ldo, int n, int K, const floa
   if (bwd_wave() != w0 % kBwdWaves) return;
   const int lane = threadIdx.x & 63, i = lane & 15, q = lane >> 4;
   const int ci = min(i, n - 1);
-  const f32x4 v = tile_xw<false, true>(X, ldx, ci, Y, ldy, ci, K, q);
+  const f32x4 v = tile_xw<false, true, UNR>(X, ldx, ci, Y, ldy, ci, K, q);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int r = 4 * q + rr;

@@ -51,14 +51,14 @@ PHASES = {
         "loop to the next token",
     ],
     "backward": [  # the walk split over several workgroups per chain (bidir307k's shape: four)
-        "barrier; the state part into LDS, K/Q rows, G2, M, dZ = tanh(alpha) dY; barrier",
+        "barrier; the state part, K/Q rows, G2, M and the seven panels into LDS, dZ = tanh(alpha) dY; barrier",
         "N (this part), dN, dZ W2^T; barrier",
-        "dN Hk, dN^T Hq, N^T dZ; barrier; dAq",
-        "dQ, dM (this part), the products with the adjoint part (dHk, dG2, dG1, dK); barrier",
-        "dG1 -= eta M^T dAq, dQ += dM K, dK += dM^T Q; dGh, dA (GELU''); dG2 += dGh W2 (three barriers)",
+        "dHq = dZ W2^T + dN Hk (dAq in its epilogue), dN^T Hq, N^T dZ; barrier",
+        "dQ, dM (this part), the products with the adjoint part; dG1 = -eta (K dW1' + M^T dAq) (dGh, dA in its epilogue); barrier",
+        "dQ += dM K (dQ out from its epilogue), dK += dM^T Q, dG2 += dGh W2; barrier",
         "dG2's partials exchanged with the other parts (publish, poll); barrier",
-        "dHk += dYh W2^T; dA += dHk S1; dK += dA W1^T (three barriers)",
-        "dQ, dK atomics and dV stores, the rank-16 updates of the adjoint part; loop",
+        "dHk += dYh W2^T (dA += dHk S1 in its epilogue); barrier; dK += dA W1^T (dK out from its epilogue)",
+        "dV stores, the rank-16 updates of the adjoint part; loop",
     ],
 }
 ENTRY = {"mfma": "ttt_phase_marks_scan_mfma", "coop": "ttt_phase_marks_scan_coop",
