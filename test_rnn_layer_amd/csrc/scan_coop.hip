@@ -384,8 +384,9 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       }
       // ---- gather, spread over the workgroup: thread tid fetches yhat feature
       //      tid mod 128 from workgroups 2 (tid / 128) and 2 (tid / 128) + 1, and
-      //      (tid < 128) the z partial of channel tid mod 16 from workgroup tid / 16;
-      //      the sums follow through LDS in a fixed order
+      //      (tid < 128) the z partial of channel tid mod 16 from workgroup tid / 16,
+      //      all in one poll (one round trip); the sums follow through LDS in a fixed
+      //      order
       {
         int64_t e_idx[4] = {0, 0, 0, 0};
         float vals[4];
@@ -394,15 +395,12 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
           for (int i = 0; i < 2; ++i) e_idx[i] = slot + (2 * (tid >> 7) + i) * NVAL + (tid & 127);
           n = 2;
         }
-        bool ok = !failed && poll(a.xchg, n, e_idx, (uint32_t)t, a.abort_flag, vals);
+        const bool zr = t > 0 && tid < 16 * NCU;
+        if (zr) e_idx[n++] = slot + (tid >> 4) * NVAL + CD + 16 * cu + (tid & 15);
+        const bool ok = !failed && poll(a.xchg, n, e_idx, (uint32_t)t, a.abort_flag, vals);
         if (ok && live)
           for (int i = 0; i < 2; ++i) Xv[2 * (tid >> 7) + i][tid & 127] = vals[i];
-        if (ok && t > 0 && tid < 16 * NCU) {
-          const int64_t ze = slot + (tid >> 4) * NVAL + CD + 16 * cu + (tid & 15);
-          float zv;
-          ok = poll(a.xchg, 1, &ze, (uint32_t)t, a.abort_flag, &zv);
-          if (ok) Zv[tid >> 4][tid & 15] = zv;
-        }
+        if (ok && zr) Zv[tid >> 4][tid & 15] = vals[n - 1];
         failed = !ok;
       }
       TTT_MARK(g_marks_scan_coop, t, 4);
