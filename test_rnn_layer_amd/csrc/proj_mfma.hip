@@ -160,7 +160,8 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a) {
 // step issues the same loads.  The epilogue stages each wave's 128 x 64 bf16
 // sub-tile through LDS and writes whole 128-byte token rows of the scan's
 // token blocks, or (row-major mode) 128-byte row pieces of [B*T, N] with the
-// residual added.
+// residual added; in the fp32 mode (mode 0, [3, B, H, T, d] with d a multiple
+// of 64) each lane stores its accumulators directly, 64-byte row pieces.
 // ---------------------------------------------------------------------------
 constexpr int T_BM = 256, T_BN = 256, T_BK = 64, T_THREADS = 512;
 constexpr int T_STAGE = (T_BM + T_BN) * T_BK;  // bf16 elements per stage (64 KB)
@@ -169,7 +170,7 @@ constexpr int TOK_RS = 72;                     // row stride of a token block (b
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_tiles_kernel(
-    ProjArgs a, int mtiles, int ntiles, int group_m) {
+    ProjArgs a, int mtiles, int ntiles, int group_m, int mode) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T_STAGE];
   const int d = a.d;
   const int D = a.H * d;
@@ -271,8 +272,29 @@ __global__ __launch_bounds__(T_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)
       __builtin_amdgcn_sched_group_barrier(0x008, 40, 0);
     }
 
-    // ---- epilogue: this wave's 128 x 64 sub-tile as bf16 rows in LDS, then 16-byte stores
+    // ---- epilogue, fp32 mode: the 64 columns of this wave are features jj0 .. jj0 + 63
+    //      of one head and one of Q, K, V
     __syncthreads();
+    if (mode == 0) {
+      const int col0 = n0 + wn * 64;
+      if (col0 < N) {
+        const int p = col0 / D, hh = (col0 - p * D) / d, jj0 = (col0 - p * D) - hh * d;
+        float* out = (float*)a.out;
+  #pragma unroll
+        for (int i = 0; i < 8; ++i)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t grow = m0 + wm * 128 + i * 16 + 4 * g + r;
+            if (grow >= M) continue;
+            const int64_t sq = grow / Tw, tt = a.tt0 + (grow - sq * Tw);
+            float* o = out + ((((int64_t)p * a.B + sq) * a.H + hh) * a.T + tt) * d + jj0 + c;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) o[16 * j] = acc[i][j][r];
+          }
+      }
+      continue;  // the stages were last read before the barrier above
+    }
+    // ---- epilogue: this wave's 128 x 64 sub-tile as bf16 rows in LDS, then 16-byte stores
     uint16_t* ctile = smem + w * (128 * 64);
   #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -356,8 +378,11 @@ bool project_mfma_supported(const ProjArgs& a) { return a.bf16 && (a.H * a.d) % 
 
 hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s) {
   const int N = 3 * a.H * a.d;
-  // token blocks (mode 1, d = 64) and row-major output (mode 2, N a multiple of 8) on the 256 x 256 tiles
-  if (((mode == 1 && a.n_out <= 0 && a.d == 64) || (mode == 2 && a.n_out % 8 == 0)) && (a.H * a.d) % T_BK == 0) {
+  // fp32 output (mode 0, d a multiple of 64), token blocks (mode 1, d = 64) and row-major output
+  // (mode 2, N a multiple of 8) on the 256 x 256 tiles
+  if (((mode == 0 && a.n_out <= 0 && a.d % 64 == 0) || (mode == 1 && a.n_out <= 0 && a.d == 64) ||
+       (mode == 2 && a.n_out % 8 == 0)) &&
+      (a.H * a.d) % T_BK == 0) {
     const int64_t M = a.B * (a.tt1 - a.tt0);
     if (M == 0) return hipSuccess;
     const int Nt = mode == 2 ? a.n_out : N;
@@ -370,7 +395,8 @@ hipError_t launch_project_mfma(const ProjArgs& a, int mode, hipStream_t s) {
     // share the fewest A and theta slices in the XCD's L2
     const int resident = std::min(grid / 8, 32);
     const int group_m = std::max(1, std::min(8, (int)std::lround(std::sqrt((double)resident))));
-    hipLaunchKernelGGL(proj_tiles_kernel, dim3((unsigned)grid), dim3(T_THREADS), 0, s, a, mtiles, ntiles, group_m);
+    hipLaunchKernelGGL(proj_tiles_kernel, dim3((unsigned)grid), dim3(T_THREADS), 0, s, a, mtiles, ntiles, group_m,
+                       mode);
     return hipGetLastError();
   }
   if (a.tt0 != 0 || a.tt1 != a.T) return hipErrorInvalidValue;  // the other kernels cover whole sequences
