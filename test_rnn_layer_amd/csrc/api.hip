@@ -904,7 +904,7 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xg
       if (e == hipSuccess && ovl) e = hipEventRecord(ro.walk[buf], s);
       if (e != hipSuccess) return fail(TTT_ERR_HIP, "backward scan launch: %s", hipGetErrorString(e));
     }
-    if (ba.dqkv_b) {  // the four-part walk's parts 2 and 3
+    if (ba.dqkv_b && !bp.split3) {  // the four-part walk's parts 2 and 3 (else added in the split)
       e = ttt::launch_add_dqk(dqkv, ba.dqkv_b, BT, (int)D, s);
       if (e != hipSuccess) return fail(TTT_ERR_HIP, "dQ|dK sum launch: %s", hipGetErrorString(e));
     }
@@ -934,7 +934,11 @@ int32_t bwd_direction(const ttt_mlp_config* c, const BwdPlan& bp, const void* xg
   const void* dq = dqkv;
   if (bp.split3) {
     uint16_t* sp = (uint16_t*)(ws + bp.sp_off);
-    e = timed_launch(TTT_KERNEL_GRAD_GEMM, s, [&] { return ttt::split_bf16x3(dqkv, sp, BT, 3 * D, s); });
+    // with the four-part walk, its second dQ|dK buffer is added in first (nothing else reads the
+    // fp32 dQ|dK|dV after the walk when the GEMMs take the split)
+    const float* dqkv2 = ba.dqkv_b;
+    e = timed_launch(TTT_KERNEL_GRAD_GEMM, s,
+                     [&] { return ttt::split_bf16x3(dqkv, dqkv2, 2 * D, sp, BT, 3 * D, s); });
     if (e != hipSuccess) return fail(TTT_ERR_HIP, "dQ|dK|dV split launch: %s", hipGetErrorString(e));
     dq = sp;
   }

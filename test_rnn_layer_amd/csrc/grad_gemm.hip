@@ -53,12 +53,17 @@ __device__ inline void split3(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
 
 // in: row-major [rows, cols] fp32, cols % 4 == 0; out: row-major [rows, 3 cols] bf16,
 // row r = [h | m | l] of in's row r.  Block x covers 256 float4 columns of a row.
-__global__ void split_bf16x3_kernel(const float4* __restrict__ in, uint2* __restrict__ out, int64_t rows,
-                                    int64_t cols4) {
+// (in2, when given: [rows, add4 float4] added first to the row's first add4 float4 of in)
+__global__ void split_bf16x3_kernel(const float4* __restrict__ in, const float4* __restrict__ in2,
+                                    uint2* __restrict__ out, int64_t rows, int64_t cols4, int64_t add4) {
   const int64_t c4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c4 >= cols4) return;
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-    const float4 v = in[r * cols4 + c4];
+    float4 v = in[r * cols4 + c4];
+    if (in2 && c4 < add4) {
+      const float4 w = in2[r * add4 + c4];
+      v = make_float4(v.x + w.x, v.y + w.y, v.z + w.z, v.w + w.w);
+    }
     uint32_t h[4], m[4], l[4];
     split3(v.x, h[0], m[0], l[0]);
     split3(v.y, h[1], m[1], l[1]);
@@ -123,12 +128,14 @@ rocblas_status handle_for(int slot, hipStream_t s, void* ws, size_t ws_bytes, ro
 
 size_t grad_gemm_workspace_bytes() { return (size_t)256 << 20; }
 
-hipError_t split_bf16x3(const float* in, uint16_t* out, int64_t rows, int64_t cols, hipStream_t s) {
+hipError_t split_bf16x3(const float* in, const float* in2, int64_t cols2, uint16_t* out, int64_t rows, int64_t cols,
+                        hipStream_t s) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
-  if (cols % 4 != 0) return hipErrorInvalidValue;
+  if (cols % 4 != 0 || (in2 && (cols2 % 4 != 0 || cols2 > cols))) return hipErrorInvalidValue;
   const int64_t cols4 = cols / 4;
   const dim3 grid((unsigned)((cols4 + 255) / 256), (unsigned)std::min<int64_t>(rows, 8192));
-  hipLaunchKernelGGL(split_bf16x3_kernel, grid, dim3(256), 0, s, (const float4*)in, (uint2*)out, rows, cols4);
+  hipLaunchKernelGGL(split_bf16x3_kernel, grid, dim3(256), 0, s, (const float4*)in, (const float4*)in2, (uint2*)out,
+                     rows, cols4, in2 ? cols2 / 4 : (int64_t)0);
   return hipGetLastError();
 }
 

@@ -128,6 +128,7 @@ struct BwdArgs {
   uint32_t* abort_flag;
   int32_t split;   // workgroups per chain: 2 or 4
   float* dqkv_b;   // four parts: [B, T, 2D], zero before the walk, added to dqkv's dQ|dK after it
+                   // (by the bf16 split of the gradient GEMMs, else by launch_add_dqk)
 };
 // LDS bytes of the backward's scan kernels (the forward pass below too): the b x d and
 // b x b panels, and the state when it fits beside them (at most 160 KB); workspace
@@ -180,9 +181,11 @@ const char* grad_gemm_dx(int slot, const float* dqkv, const float* theta32, cons
 const char* grad_gemm_dtheta(int slot, const float* dqkv, const float* x32, float* dtheta, int64_t BT, int64_t D,
                              int accumulate, void* ws, size_t ws_bytes, hipStream_t s);
 // With bf16 X and theta: S [BT, 9D] = the exact bf16 split [h | m | l] of dQKV [BT, 3D]
-// (split_bf16x3; cols % 4 == 0), theta3 [9D, D] = theta stacked three times (stack3_u16), and
-// the same two GEMMs on the bf16 matrix cores with fp32 accumulation.
-hipError_t split_bf16x3(const float* in, uint16_t* out, int64_t rows, int64_t cols, hipStream_t s);
+// (split_bf16x3; cols % 4 == 0; in2, if not null, [rows, cols2] is added to the first cols2
+// columns of in before the split, cols2 % 4 == 0), theta3 [9D, D] = theta stacked three times
+// (stack3_u16), and the same two GEMMs on the bf16 matrix cores with fp32 accumulation.
+hipError_t split_bf16x3(const float* in, const float* in2, int64_t cols2, uint16_t* out, int64_t rows, int64_t cols,
+                        hipStream_t s);
 hipError_t stack3_u16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t s);
 const char* grad_gemm_dx_split(int slot, const uint16_t* sp, const uint16_t* theta3, const float* dy, float* dx,
                                int64_t BT, int64_t D, void* ws, size_t ws_bytes, hipStream_t s);
