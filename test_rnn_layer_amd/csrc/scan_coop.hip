@@ -179,6 +179,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) float Hb[NW][2][64];  // each wave's GELU(a), GELU(aq), by unit
   __shared__ float Xv[NCU][CD];       // gathered yhat partials, by workgroup and feature
   __shared__ float Zv[NCU][16];       // gathered z partials of this workgroup's 16 channels
+  __shared__ uint32_t stop_wg;        // set (never cleared) by a thread whose poll failed
 
   // Workgroup -> (sequence-head bh, slice cu).  The NCU slices of a head get
   // workgroup indices that are equal modulo 8, i.e. the same XCD under the
@@ -241,6 +242,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
     //      k_0, k_1, q_0, and the partial pre-activation k_0 W1_0 of token 0
     for (int i = tid; i < 4 * CD; i += NT) (&Ks[0][0])[i] = 0.0f;
     for (int i = tid; i < 2 * CD; i += NT) (&Qs[0][0])[i] = 0.0f;
+    if (tid == 0) stop_wg = 0u;
     __syncthreads();
     if (tid < CD) {
       Ks[0][tid] = kb[tok(0) * CD + tid];
@@ -257,6 +259,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       Apart[1][w][lane] = 0.0f;
       if (lane == 0) Sdot[w][0] = Sdot[w][1] = 0.0f;
     }
+    __syncthreads();  // the partial pre-activations and dot products of token 0 are complete
 
     // -eta G1 of unit `lane` for the previous token: its W1 update is applied in the
     // next iteration, while the exchange is in flight
@@ -278,8 +281,11 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         if (tid < 2 * CD) stage = tid < CD ? kb[tok(tk) * CD + tid] : qb[tok(tq) * CD + tid - CD];
       }
       if (writer && t > 0) xo = ld_io_bits(a.xin, ((int64_t)s * T + tok(t - 1)) * D + ch, bf16);
-
-      __syncthreads();  // the partial pre-activations and dot products of this iteration are complete
+      // No barrier here: this iteration's partial pre-activations and dot products
+      // (Apart, Sdot) were written in the previous iteration before its gather barrier,
+      // and nothing is written below before the next barrier that another wave reads
+      // before it (each wave writes only its own Hb and Ypart slices, whose readers
+      // finished before the gather barrier).
       TTT_MARK(g_marks_scan_coop, t, 1);
       // ---- unit u = lane: a_t = k_t W1_{t-1} = k_t W1_{t-2} + (k_t . k_{t-1}) (-eta G1_{t-1}), and
       //      aq_{t-1} = q_{t-1} W1_{t-1} likewise; their GELU
@@ -401,13 +407,16 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         if (ok && live)
           for (int i = 0; i < 2; ++i) Xv[2 * (tid >> 7) + i][tid & 127] = vals[i];
         if (ok && zr) Zv[tid >> 4][tid & 15] = vals[n - 1];
+        if (!ok) __hip_atomic_store(&stop_wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         failed = !ok;
       }
       TTT_MARK(g_marks_scan_coop, t, 4);
-      if (__syncthreads_or(failed)) {  // every thread of the workgroup leaves together
-        fill_nan(t > 0 ? t - 1 : 0);
-        return;
-      }
+      // A failed poll is acted on after the next barrier (the stop flag is read there
+      // by every thread; it is written only in this phase, so all threads read the
+      // same value).  Until then the workgroup runs on with whatever the failed
+      // entries held: it writes no state, and fill_nan rewrites every output from
+      // token t-1 on.
+      __syncthreads();
       TTT_MARK(g_marks_scan_coop, t, 5);
       float got[2] = {0.0f, 0.0f};
       if (live) {
@@ -465,15 +474,17 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       gp[0] = dpp_add<0x4e>(gp[0], gp[0]);   // quad_perm [2,3,0,1]: lane ^ 2
       gp[0] = dpp_add<0xb1>(gp[0], gp[0]);   // quad_perm [1,0,3,2]: lane ^ 1
       if ((lane & 7) == 0) GH[UW * w + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1)] = gp[0];
-      if (__syncthreads_or(failed)) {  // every thread of the workgroup leaves together
-        fill_nan(t > 0 ? t - 1 : 0);
+      __syncthreads();
+      if (__hip_atomic_load(&stop_wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
+        fill_nan(t > 0 ? t - 1 : 0);  // every thread of the workgroup leaves together
         return;
       }
       TTT_MARK(g_marks_scan_coop, t, 6);
       ng1_prev = neta * GH[lane] * dg;  // -eta G1_t of unit lane: applied to W1 next iteration
       TTT_MARK(g_marks_scan_coop, t, 7);
     }
-    if (__syncthreads_or(failed)) {
+    __syncthreads();
+    if (__hip_atomic_load(&stop_wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
       fill_nan(T - 1);
       return;
     }

@@ -41,12 +41,12 @@ PHASES = {
         "loop to the next step",
     ],
     "coop": [
-        "loads of v_t and the next k, q; barrier (partials of a complete)",
+        "loads of v_t and the next k, q (no barrier: the partials of a are complete since the last gather)",
         "GELU(a), GELU(aq); first W2 pass (partial yhat, z); barrier",
         "publish this workgroup's partials (device-scope stores)",
         "the previous token's W1 update and the next pre-activations; poll the other workgroups' partials",
         "barrier after the gather",
-        "sums, gate store; G2; W2 update; G2 W2^T reduction; barrier",
+        "sums, gate store; G2; W2 update; G2 W2^T reduction; barrier (and the stop flag of a failed poll)",
         "G1 of this token (its W1 update follows in the next token's exchange)",
         "loop to the next token",
     ],
