@@ -13,13 +13,16 @@
 // At d = 128, m = 512 a head's fp32 state is 512 KB, more than one CU's LDS
 // and, with working registers, its VGPR file.  The state is split by hidden
 // unit over NCU = 8 workgroups (one per CU), 64 units each, held entirely in
-// VGPRs:
-//   W1 slice (128 x 64): lane u of wave w (of 8) holds W1[16w .. 16w+15][u];
-//   W2 slice (64 x 128): lane l of wave w holds W2[8w .. 8w+7][l, l+64].
+// VGPRs; wave w (of 8) owns 8 units of them whole:
+//   W1 columns of its units (128 x 8): lane l holds rows 16 (l mod 8) .. +15 of
+//     unit 8w + l/8, so the 8 lanes of a unit sum its pre-activation by DPP;
+//   W2 rows of its units (8 x 128): lane l holds W2[8w .. 8w+7][l, l+64].
 // Per token every workgroup holds the full q, k, v of its head.  a = k W1 and
-// aq = q W1 are local to a unit, so only the contractions over hidden units,
-// yhat = GELU(a) W2 and z = GELU(aq) W2, need partial sums from all NCU
-// workgroups: one exchange per token.
+// aq = q W1 are local to a unit, and so to a wave, so only the contractions over
+// hidden units, yhat = GELU(a) W2 and z = GELU(aq) W2, need partial sums: over
+// the waves through LDS, then from all NCU workgroups: one exchange per token.
+// G2 W2^T of a unit comes out of its wave's own reduction over features, in the
+// lanes that own the unit, so G1 and the W1 update stay in registers.
 //
 // Read-out.  Iteration t runs token t's step with the state W_{t-1}, which is
 // also token t-1's post-update state, so token t-1's read-out is computed in
@@ -157,26 +160,30 @@ __device__ __forceinline__ float dpp_add(float keep, float send) {
   return keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xf, 0xf, false));
 }
 
-// Sum of x over lanes 0..31 (lanes 32..63 hold 0), in every lane of 0..31: halves of
-// 16 trade with the lane swap, then the DPP steps of the G2 W2^T reduction.
-__device__ __forceinline__ float wave_sum32(float x) {
-  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  x = dpp_add<0x128>(x, x);
+// Sum of x over each group of 8 consecutive lanes, in every lane of the group: the
+// half-row mirror (lane i with 7 - i) and two quad permutations (lane ^ 2, lane ^ 1).
+__device__ __forceinline__ float unit_sum8(float x) {
   x = dpp_add<0x141>(x, x);
   x = dpp_add<0x4e>(x, x);
   return dpp_add<0xb1>(x, x);
 }
 
+// Sum of x over the wave's 64 lanes, in every lane: halves of 32 and 16 lanes trade
+// with the lane swaps, halves of 8 with a DPP row rotation, then unit_sum8.
+__device__ __forceinline__ float wave_sum64(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  x = dpp_add<0x128>(x, x);
+  return unit_sum8(x);
+}
+
 template <bool TANH>
 __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
-  __shared__ float Apart[2][NW][64];  // per-wave partials of a (k W1) and aq (q W1), by unit
   __shared__ float Ypart[NW][4][64];  // per-wave partials of yhat (j = l, l + 64) and z (same)
-  __shared__ float GH[UNITS];         // G2 W2^T, by unit
   __shared__ __attribute__((aligned(16))) float Ks[4][CD];  // k_{t-1} .. k_{t+2} (by token mod 4)
   __shared__ __attribute__((aligned(16))) float Qs[2][CD];  // q_t, q_{t+1} (by token mod 2)
-  __shared__ float Sdot[NW][2];       // per-wave partials of k_{t+1} . k_t and q_t . k_t
-  __shared__ __attribute__((aligned(16))) float Hb[NW][2][64];  // each wave's GELU(a), GELU(aq), by unit
   __shared__ float Xv[NCU][CD];       // gathered yhat partials, by workgroup and feature
   __shared__ float Zv[NCU][16];       // gathered z partials of this workgroup's 16 channels
   __shared__ uint32_t stop_wg;        // set (never cleared) by a thread whose poll failed
@@ -197,6 +204,9 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   const int64_t T = a.T;
   const int D = a.H * CD;
   const int u0 = UNITS * cu;
+  // this lane's hidden unit (of the wave's UW) and its rows of W1
+  const int ul = lane >> 3, r0 = PW * (lane & 7);
+  const int unit = u0 + UW * w + ul;
   const bool bf16 = a.bf16;
   const float neta = -a.eta, gs = a.gscale;
   const bool writer = (w == 0) && lane < 16;  // writes channels h*d + 16*cu + lane
@@ -214,7 +224,6 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   bool failed = false;  // this thread saw an abort or a time-out
   const int64_t xslots = bh * 2 * NCU * NVAL;  // first entry of this head's slots
 
-
   // ---- state slices
   float W1r[PW];
   float W2r[UW][2];
@@ -222,7 +231,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
     const float* w1 = a.w1_0 + (int64_t)h * CD * CM;
     const float* w2 = a.w2_0 + (int64_t)h * CM * CD;
 #pragma unroll
-    for (int k = 0; k < PW; ++k) W1r[k] = w1[(int64_t)(PW * w + k) * CM + u0 + lane];
+    for (int k = 0; k < PW; ++k) W1r[k] = w1[(int64_t)(r0 + k) * CM + unit];
 #pragma unroll
     for (int i = 0; i < UW; ++i) {
       W2r[i][0] = w2[(int64_t)(u0 + UW * w + i) * CD + lane];
@@ -236,10 +245,25 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   const float* vb = qb + 2 * plane;
   const float tg = tanhf(a.alpha[ch]);
 
+  // sum over this lane's 16 rows of x . W1r (x: 16 consecutive floats in LDS)
+  auto rows_dot = [&](const float* x) -> float {
+    const float4* x4 = (const float4*)x;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k4 = 0; k4 < PW / 4; ++k4) {
+      const float4 v = x4[k4];
+      acc = fmaf(v.x, W1r[4 * k4], acc);
+      acc = fmaf(v.y, W1r[4 * k4 + 1], acc);
+      acc = fmaf(v.z, W1r[4 * k4 + 2], acc);
+      acc = fmaf(v.w, W1r[4 * k4 + 3], acc);
+    }
+    return acc;
+  };
+
   if (T > 0) {
     // ---- prologue: the k and q slots zeroed (the deferred update of token -1 and the
     //      pre-activations of the last iteration read slots that hold no token yet), then
-    //      k_0, k_1, q_0, and the partial pre-activation k_0 W1_0 of token 0
+    //      k_0, k_1, q_0, and the pre-activation k_0 W1_0 of token 0
     for (int i = tid; i < 4 * CD; i += NT) (&Ks[0][0])[i] = 0.0f;
     for (int i = tid; i < 2 * CD; i += NT) (&Qs[0][0])[i] = 0.0f;
     if (tid == 0) stop_wg = 0u;
@@ -251,24 +275,20 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       Ks[1][tid - CD] = kb[tok(1) * CD + tid - CD];
     }
     __syncthreads();
-    {
-      float acc = 0.0f;
-#pragma unroll
-      for (int k = 0; k < PW; ++k) acc = fmaf(Ks[0][PW * w + k], W1r[k], acc);
-      Apart[0][w][lane] = acc;
-      Apart[1][w][lane] = 0.0f;
-      if (lane == 0) Sdot[w][0] = Sdot[w][1] = 0.0f;
-    }
-    __syncthreads();  // the partial pre-activations and dot products of token 0 are complete
 
-    // -eta G1 of unit `lane` for the previous token: its W1 update is applied in the
-    // next iteration, while the exchange is in flight
+    // Carried from one iteration to the next, all in registers: the pre-activations
+    // k_{t+1} W1_{t-1} and q_t W1_{t-1} of this lane's unit (every lane of the unit's
+    // group of 8 holds them whole), the dot products k_{t+1} . k_t and q_t . k_t
+    // (every lane), and -eta G1 of the unit for the previous token, whose W1 update is
+    // applied in the next iteration while the exchange is in flight.
+    float a_pre = unit_sum8(rows_dot(Ks[0] + r0)), aq_pre = 0.0f;
+    float skk = 0.0f, sqk = 0.0f;
     float ng1_prev = 0.0f;
     for (int64_t t = 0; t <= T; ++t) {
       const bool live = t < T;
       TTT_MARK(g_marks_scan_coop, t, 0);
       // operands loaded now and used later in the iteration: v_t, the gate
-      // input of token t-1, and (staged into LDS after the second barrier) k_{t+2}, q_{t+1}
+      // input of token t-1, and (staged into LDS after the first barrier) k_{t+2}, q_{t+1}
       float v0 = 0.0f, v1 = 0.0f, stage = 0.0f;
       uint32_t xo = 0;
       if (live) {
@@ -281,51 +301,29 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         if (tid < 2 * CD) stage = tid < CD ? kb[tok(tk) * CD + tid] : qb[tok(tq) * CD + tid - CD];
       }
       if (writer && t > 0) xo = ld_io_bits(a.xin, ((int64_t)s * T + tok(t - 1)) * D + ch, bf16);
-      // No barrier here: this iteration's partial pre-activations and dot products
-      // (Apart, Sdot) were written in the previous iteration before its gather barrier,
-      // and nothing is written below before the next barrier that another wave reads
-      // before it (each wave writes only its own Hb and Ypart slices, whose readers
-      // finished before the gather barrier).
       TTT_MARK(g_marks_scan_coop, t, 1);
-      // ---- unit u = lane: a_t = k_t W1_{t-1} = k_t W1_{t-2} + (k_t . k_{t-1}) (-eta G1_{t-1}), and
-      //      aq_{t-1} = q_{t-1} W1_{t-1} likewise; their GELU
+      // ---- this lane's unit: a_t = k_t W1_{t-1} = k_t W1_{t-2} + (k_t . k_{t-1}) (-eta G1_{t-1}),
+      //      and aq_{t-1} = q_{t-1} W1_{t-1} likewise; their GELU
       float hk = 0.0f, dg = 0.0f, hq = 0.0f;
       {
-        float av = 0.0f, aqv = 0.0f, skk = 0.0f, sqk = 0.0f;
-#pragma unroll
-        for (int q = 0; q < NW; ++q) {
-          av += Apart[0][q][lane];
-          aqv += Apart[1][q][lane];
-          skk += Sdot[q][0];
-          sqk += Sdot[q][1];
-        }
-        av = fmaf(skk, ng1_prev, av);
-        aqv = fmaf(sqk, ng1_prev, aqv);
+        const float av = fmaf(skk, ng1_prev, a_pre);
+        const float aqv = fmaf(sqk, ng1_prev, aq_pre);
         if (live) gelu_both(av, TANH, &hk, &dg);
         if (t > 0) hq = gelu_val(aqv, TANH);
-        // this wave's 16 units to every lane of the wave: its own copy in LDS (the
-        // wave's LDS accesses execute in order)
-        Hb[w][0][lane] = hk;
-        Hb[w][1][lane] = hq;
       }
-      // ---- first W2 pass: partial yhat_t and z_{t-1} over this wave's 16 units
+      // ---- first W2 pass: partial yhat_t and z_{t-1} over this wave's 8 units, whose
+      //      activations every lane takes from the first lane of the unit's group
       float hks[UW];
       {
-        float hqs[UW];
-#pragma unroll
-        for (int i4 = 0; i4 < UW / 4; ++i4) {
-          const float4 k4 = *(const float4*)&Hb[w][0][UW * w + 4 * i4];
-          const float4 q4 = *(const float4*)&Hb[w][1][UW * w + 4 * i4];
-          hks[4 * i4] = k4.x, hks[4 * i4 + 1] = k4.y, hks[4 * i4 + 2] = k4.z, hks[4 * i4 + 3] = k4.w;
-          hqs[4 * i4] = q4.x, hqs[4 * i4 + 1] = q4.y, hqs[4 * i4 + 2] = q4.z, hqs[4 * i4 + 3] = q4.w;
-        }
         float y0 = 0.0f, y1 = 0.0f, z0 = 0.0f, z1 = 0.0f;
 #pragma unroll
         for (int i = 0; i < UW; ++i) {
+          hks[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hk), 8 * i));
+          const float hqi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hq), 8 * i));
           y0 = fmaf(hks[i], W2r[i][0], y0);
           y1 = fmaf(hks[i], W2r[i][1], y1);
-          z0 = fmaf(hqs[i], W2r[i][0], z0);
-          z1 = fmaf(hqs[i], W2r[i][1], z1);
+          z0 = fmaf(hqi, W2r[i][0], z0);
+          z1 = fmaf(hqi, W2r[i][1], z1);
         }
         Ypart[w][0][lane] = y0;
         Ypart[w][1][lane] = y1;
@@ -352,41 +350,29 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         put(a.xchg + slot + cu * NVAL + 64 * w + lane, (uint32_t)t, p);
       }
       TTT_MARK(g_marks_scan_coop, t, 3);
-      // ---- while the partials travel: token t-1's W1 update (with k_{t-1} and its G1),
-      //      then the partial pre-activations k_{t+1} W1_{t-1} and q_t W1_{t-1} and the
-      //      partial dot products k_{t+1} . k_t and q_t . k_t over this wave's 32 rows
-      //      (at t = T-1 and T the k and q slots past the end hold stale values; those
-      //      results are never used)
+      // ---- while the partials travel: token t-1's W1 update of this lane's rows (with
+      //      k_{t-1} and its G1), then the pre-activations k_{t+1} W1_{t-1} and
+      //      q_t W1_{t-1} of the unit (summed over its 8 lanes) and the dot products
+      //      k_{t+1} . k_t and q_t . k_t (summed over the wave; lane l takes features
+      //      l and l + 64).  At t = T-1 and T the k and q slots past the end hold stale
+      //      values; those results are never used.
       {
-        const float4* kp = (const float4*)(Ks[(t + 3) & 3] + PW * w);  // k_{t-1}
-        const float4* kn = (const float4*)(Ks[(t + 1) & 3] + PW * w);  // k_{t+1}
-        const float4* qc = (const float4*)(Qs[t & 1] + PW * w);        // q_t
-        float an = 0.0f, aq = 0.0f;
+        const float4* kp = (const float4*)(Ks[(t + 3) & 3] + r0);  // k_{t-1}
 #pragma unroll
         for (int k4 = 0; k4 < PW / 4; ++k4) {
-          const float4 pv = kp[k4], nv = kn[k4], qv = qc[k4];
-          const float pp[4] = {pv.x, pv.y, pv.z, pv.w}, nn[4] = {nv.x, nv.y, nv.z, nv.w},
-                      qq[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k = 4 * k4 + e;
-            W1r[k] = fmaf(ng1_prev, pp[e], W1r[k]);
-            an = fmaf(nn[e], W1r[k], an);
-            aq = fmaf(qq[e], W1r[k], aq);
-          }
+          const float4 pv = kp[k4];
+          W1r[4 * k4] = fmaf(ng1_prev, pv.x, W1r[4 * k4]);
+          W1r[4 * k4 + 1] = fmaf(ng1_prev, pv.y, W1r[4 * k4 + 1]);
+          W1r[4 * k4 + 2] = fmaf(ng1_prev, pv.z, W1r[4 * k4 + 2]);
+          W1r[4 * k4 + 3] = fmaf(ng1_prev, pv.w, W1r[4 * k4 + 3]);
         }
-        Apart[0][w][lane] = an;
-        Apart[1][w][lane] = aq;
-        // lanes 0..31 take one row each; the sum over the wave in registers
-        const float kc = lane < PW ? Ks[t & 3][PW * w + lane] : 0.0f;
-        float dkk = lane < PW ? Ks[(t + 1) & 3][PW * w + lane] * kc : 0.0f;
-        float dqk = lane < PW ? Qs[t & 1][PW * w + lane] * kc : 0.0f;
-        dkk = wave_sum32(dkk);
-        dqk = wave_sum32(dqk);
-        if (lane == 0) {
-          Sdot[w][0] = dkk;
-          Sdot[w][1] = dqk;
-        }
+        a_pre = unit_sum8(rows_dot(Ks[(t + 1) & 3] + r0));
+        aq_pre = unit_sum8(rows_dot(Qs[t & 1] + r0));
+        const float* kc = Ks[t & 3];
+        const float* kn = Ks[(t + 1) & 3];
+        const float* qc = Qs[t & 1];
+        skk = wave_sum64(fmaf(kn[lane], kc[lane], kn[lane + 64] * kc[lane + 64]));
+        sqk = wave_sum64(fmaf(qc[lane], kc[lane], qc[lane + 64] * kc[lane + 64]));
       }
       // ---- gather, spread over the workgroup: thread tid fetches yhat feature
       //      tid mod 128 from workgroups 2 (tid / 128) and 2 (tid / 128) + 1, and
@@ -411,12 +397,13 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         failed = !ok;
       }
       TTT_MARK(g_marks_scan_coop, t, 4);
-      // A failed poll is acted on after the next barrier (the stop flag is read there
-      // by every thread; it is written only in this phase, so all threads read the
-      // same value).  Until then the workgroup runs on with whatever the failed
-      // entries held: it writes no state, and fill_nan rewrites every output from
-      // token t-1 on.
+      // A failed poll stops the workgroup after this barrier: the stop flag is written
+      // only between the first barrier and this one, so every thread reads the same value.
       __syncthreads();
+      if (__hip_atomic_load(&stop_wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
+        fill_nan(t > 0 ? t - 1 : 0);  // every thread of the workgroup leaves together
+        return;
+      }
       TTT_MARK(g_marks_scan_coop, t, 5);
       float got[2] = {0.0f, 0.0f};
       if (live) {
@@ -447,13 +434,14 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         W2r[i][1] = fmaf(nh, g21, W2r[i][1]);
       }
       // ---- sum gp over the 64 lanes (recursive halving, in registers): lane ends
-      //      with unit 4 b5 + 2 b4 + b3 of its wave's 8 (b = bits of the lane index).
-      //      Each halving pairs every lane with one lane of the other half of its group;
-      //      the lane keeps the units of its half and adds the partner's partial of
-      //      them.  Halves of 32 and 16 lanes trade with the lane swaps (lanes 32..63 of
-      //      the first operand with lanes 0..31 of the second, and likewise odd with even
-      //      rows of 16), halves of 8 through a DPP row rotation; the 8 lanes that then
-      //      hold one unit sum it with the half-row mirror and quad permutations.
+      //      with unit 4 b5 + 2 b4 + b3 = lane / 8 of its wave's 8 (b = bits of the lane
+      //      index), the lane's own unit.  Each halving pairs every lane with one lane of
+      //      the other half of its group; the lane keeps the units of its half and adds
+      //      the partner's partial of them.  Halves of 32 and 16 lanes trade with the lane
+      //      swaps (lanes 32..63 of the first operand with lanes 0..31 of the second, and
+      //      likewise odd with even rows of 16), halves of 8 through a DPP row rotation;
+      //      the 8 lanes that then hold one unit sum it with the half-row mirror and quad
+      //      permutations.
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gp[i]), __float_as_uint(gp[4 + i]), false,
@@ -470,23 +458,9 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         const bool hi = lane & 8;
         gp[0] = dpp_add<0x128>(hi ? gp[1] : gp[0], hi ? gp[0] : gp[1]);  // row_ror:8: lane ^ 8
       }
-      gp[0] = dpp_add<0x141>(gp[0], gp[0]);  // row_half_mirror: lane ^ 7 in 8
-      gp[0] = dpp_add<0x4e>(gp[0], gp[0]);   // quad_perm [2,3,0,1]: lane ^ 2
-      gp[0] = dpp_add<0xb1>(gp[0], gp[0]);   // quad_perm [1,0,3,2]: lane ^ 1
-      if ((lane & 7) == 0) GH[UW * w + 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1)] = gp[0];
-      __syncthreads();
-      if (__hip_atomic_load(&stop_wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
-        fill_nan(t > 0 ? t - 1 : 0);  // every thread of the workgroup leaves together
-        return;
-      }
       TTT_MARK(g_marks_scan_coop, t, 6);
-      ng1_prev = neta * GH[lane] * dg;  // -eta G1_t of unit lane: applied to W1 next iteration
+      ng1_prev = neta * unit_sum8(gp[0]) * dg;  // -eta G1_t of this lane's unit: applied to W1 next iteration
       TTT_MARK(g_marks_scan_coop, t, 7);
-    }
-    __syncthreads();
-    if (__hip_atomic_load(&stop_wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
-      fill_nan(T - 1);
-      return;
     }
   }
 
@@ -494,7 +468,7 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   if (a.w1_T) {
     float* o = a.w1_T + bh * CD * CM;
 #pragma unroll
-    for (int k = 0; k < PW; ++k) o[(int64_t)(PW * w + k) * CM + u0 + lane] = W1r[k];
+    for (int k = 0; k < PW; ++k) o[(int64_t)(r0 + k) * CM + unit] = W1r[k];
   }
   if (a.w2_T) {
     float* o = a.w2_T + bh * CM * CD;

@@ -16,10 +16,11 @@
 //   G2 = c (Yhat - V)                   each thread finishes two values
 //   Gh^T = W2 G2^T, G1^T = Gh^T * GELU'(A^T)
 //   W1 -= eta K^T G1,  W2 -= eta Hk^T G2                 (K=16 MFMAs)
-// and block j-1's read-out with the state that follows block j-1 (exact):
+// and, after the second barrier beside the update's products, block j-1's
+// read-out with the state that follows block j-1 (exact):
 //   Aq^T = W1'^T Q^T + eta G1^T striu(Q K^T)^T, Hq^T = GELU(Aq^T)
 //   Z^T  = W2'^T Hq^T + eta G2^T striu(Hq Hk^T)^T       partial -> LDS reduce
-// with the gate y = x + tanh(alpha) z and the stores of block j-1.  The
+// with the gate y = x + tanh(alpha) z and the stores one step later.  The
 // transposed operands (W2 for Gh, contracted over d; token-major G1, Hk and
 // K for the updates) come from LDS transpose reads.  Two workgroup barriers
 // per block.
@@ -38,13 +39,19 @@ using namespace tb;  // SD = 64 head width, SB = 16 mini-batch, the token-block 
 constexpr int SM = 256;  // hidden width
 constexpr int NWAVE = 8;          // wave w owns hidden units [32w, 32w + 32)
 constexpr int NTHR = 64 * NWAVE;
-constexpr int NSTAGE = 4;         // token blocks in LDS: j-1 (read-out), j, j+1 and j+2 in flight
+constexpr int NSTAGE = 8;         // token-block buffers in LDS (indexed by block mod 8)
+constexpr int AHEAD = 3;          // blocks j+1 .. j+3 in flight during step j
 constexpr int TS = SB + 8;  // 24: rows of the [feature][token] G2 copy (48 bytes: the 8-byte reads of
                             // two lane groups fall on distinct banks)
 // Hk slice rows: source lane l at row l + 8 (l / 32), so that the 32 rows a transposed
 // read takes in one lane group pair map to distinct banks
 constexpr int HKS_ROWS = 72;
 __device__ __forceinline__ int hk_row(int l) { return l + 8 * (l >> 5); }
+// issue pattern after the second barrier: each of the step's MIX_PRODUCTS matrix-core
+// products there (28 of the update, 15 of the read-out) followed by MIX_VALU vector
+// instructions (measured: 90.7 ms per bidir307k call, against 92.0 with 28 x 2,
+// 92.0 with 43 x 4, 92.7 with 36 x 3 and 92.9 with no pattern)
+constexpr int MIX_PRODUCTS = 43, MIX_VALU = 3;
 constexpr int DGS = SB + 4;  // 20: rows of the fp32 [hidden][token] GELU' tiles (bank spread of the column writes)
 
 // GELU(a) = a Phi(a) and GELU'(a) = Phi(a) + a phi(a), with Phi from the
@@ -75,7 +82,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __shared__ f32x4 Zpart[NWAVE][4][64];                            // partial Z^T
   __shared__ __attribute__((aligned(16))) uint16_t G2a[SB * RS];    // -eta G2 [token][feature, pair order]
   __shared__ __attribute__((aligned(16))) uint16_t G2b[SD * TS];    // -eta G2 [feature][token]
-  __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+2
+  __shared__ __attribute__((aligned(16))) uint16_t Stage[NSTAGE][BLK];  // token blocks j-1 .. j+3
   // per-wave slices for the transposed reads: bf16 Hk^T (one 8-byte row per source lane
   // and hidden-unit tile, see hk_row), fp32 GELU'(A^T) as [m][t]
   __shared__ __attribute__((aligned(16))) bf16x4 HkS[NWAVE][2][HKS_ROWS];
@@ -158,8 +165,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   auto io_voff = [&](int nv, int elem_bytes) -> int {
     return ((a.reverse ? nv - 1 - rd_t : rd_t) * D + ch0) * elem_bytes;
   };
-  auto load_x = [&](int64_t jb) -> uint32_t {  // two bf16 gate inputs of this lane's values
-    const int nv = block_n(jb);
+  auto load_x = [&](int64_t jb, int nv) -> uint32_t {  // two bf16 gate inputs of this lane's values (nv = 0: none)
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc((void*)(x_seq + io_elem0(jb, nv)), 0, nv * D * 2, kRawBufferWord3);
     return __builtin_amdgcn_raw_buffer_load_b32(rx, io_voff(nv, 2), 0, 0);
@@ -259,13 +265,14 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     for (int dt = 0; dt < 4; ++dt) w2p[dt] = pack8(W2[0][dt], W2[1][dt]);
   };
 
-  for (int64_t jb = 0; jb < NSTAGE - 1 && jb < nblk; ++jb) stage_async(jb, (int)jb);
+  for (int64_t jb = 0; jb < AHEAD && jb < nblk; ++jb) stage_async(jb, (int)jb);
   vmem_done();
   __syncthreads();
 
-  // Step j runs block j's recurrence and, between its two barriers, block j-1's
-  // read-out (at j = 0 on zero operands, never stored); the last block's read-out
-  // follows the loop.
+  // Step j runs block j's recurrence; after its second barrier, beside the state
+  // update, block j-1's read-out (at j = 0 on zero operands, never stored), whose
+  // partial Z is summed between the next step's barriers and stored after them.  The
+  // last block's read-out follows the loop.
   for (int64_t j = 0; j < nblk; ++j) {
     const int n = block_n(j);
     const uint16_t* blk = Stage[j & (NSTAGE - 1)];
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // ---- between the barriers (no vector-memory operation: the second barrier
     //      waits for the wave's outstanding ones):
     //   G2 of block j from the wave-summed Yhat, this lane's two values;
-    //   block j-1's read-out, independent of the G2 chain;
+    //   Z of block j-2 summed over the waves' partials;
     //   this wave's transposed operands for the update.
     {
       const float2 y = reduce_part(Ypart);
@@ -335,7 +342,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
       G2b[(rd_d + 1) * TS + rd_t] = (uint16_t)(pk >> 16);
     }
     TTT_MARK(g_marks_scan_mfma, j, 3);
-    readout(blk_prev, w1p, w2p);
+    // Z of block j-2 (its read-out ran after the previous step's second barrier)
+    const float2 zfin = reduce_part(Zpart);
     TTT_MARK(g_marks_scan_mfma, j, 4);
     // GELU'(A^T) to this wave's LDS slice as [m][t], read back token-major below
 #pragma unroll
@@ -398,24 +406,25 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
         W2T[dt][mt] = mfma16(g2T[dt], hkT[mt], W2T[dt][mt]);
       }
 
-    // ---- Z of block j-1 and the vector-memory work of this step, waited for just
-    //      before the next step's second barrier: Y and Z of block j-1, the gate
-    //      inputs of block j (one register, consumed before it is reloaded: no
-    //      register rotation, which would make the compiler wait at once), block
-    //      j+3 into the buffer that held block j-1 (last read before this step's
-    //      second barrier)
-    const float2 zfin = reduce_part(Zpart);
-    store_z(j - 1, j > 0 ? block_n(j - 1) : 0, x_blk, zfin);  // nothing to store at j = 0
-    x_blk = load_x(j);
+    // ---- block j-1's read-out with the state that follows it (its bf16 operands
+    //      w1p, w2p) -> Zpart, summed between the next step's barriers
+    readout(blk_prev, w1p, w2p);
+    // ---- the vector-memory work of this step, waited for just before the next
+    //      step's second barrier: Y and Z of block j-2, the gate inputs of block j-1
+    //      (one register, consumed before it is reloaded: no register rotation,
+    //      which would make the compiler wait at once), block j+3 into the buffer
+    //      that held block j-5
+    store_z(j - 2, j > 1 ? block_n(j - 2) : 0, x_blk, zfin);  // nothing to store at j < 2
+    x_blk = load_x(j - 1, j > 0 ? block_n(j - 1) : 0);
     // issue order after the second barrier: every matrix-core product followed by
-    // two vector-ALU instructions, so that the reduction, gate and packing work
-    // runs beside the products instead of after them
+    // two vector-ALU instructions, so that the read-out's GELU, the gate and the
+    // packing work run beside the products instead of after them
 #pragma unroll
-    for (int i = 0; i < 28; ++i) {
+    for (int i = 0; i < MIX_PRODUCTS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, MIX_VALU, 0);
     }
-    if (j + NSTAGE - 1 < nblk) stage_async(j + NSTAGE - 1, (int)((j + NSTAGE - 1) & (NSTAGE - 1)));
+    if (j + AHEAD < nblk) stage_async(j + AHEAD, (int)((j + AHEAD) & (NSTAGE - 1)));
 
     St_prev = St;
     g1T_prev = cat8(g1T[0], g1T[1]);
@@ -425,12 +434,16 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     TTT_MARK(g_marks_scan_mfma, j, 7);
   }
 
-  // ---- read-out of the last block with the final state (after every wave's last
-  //      reads of Zpart)
+  // ---- Z of block nblk-2, then the read-out of the last block with the final
+  //      state (after every wave's reads of Zpart)
   if (nblk > 0) {
+    __syncthreads();
+    const float2 zl = reduce_part(Zpart);
     bf16x8 w1p[2][2], w2p[4];
     pack_state(w1p, w2p);
     __syncthreads();
+    store_z(nblk - 2, nblk > 1 ? block_n(nblk - 2) : 0, x_blk, zl);
+    x_blk = load_x(nblk - 1, block_n(nblk - 1));
     readout(Stage[(nblk - 1) & (NSTAGE - 1)], w1p, w2p);
     __syncthreads();
     store_z(nblk - 1, block_n(nblk - 1), x_blk, reduce_part(Zpart));

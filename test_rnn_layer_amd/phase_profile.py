@@ -34,10 +34,10 @@ PHASES = {
         "state to bf16; A = K W1, S = K Q^T; GELU(A); partial Yhat = Hk W2 -> LDS",
         "first barrier",
         "Yhat summed over the waves; -eta G2 -> LDS",
-        "read-out of block j-1: Aq, GELU(Aq), causal products, partial Z -> LDS",
+        "Z of block j-2 summed over the waves",
         "GELU'(A) -> LDS; transposed operands read back; wait for vector memory",
         "second barrier",
-        "Gh, G1; W1, W2, W2^T updates; Z summed; gate and stores; staging",
+        "Gh, G1; W1, W2, W2^T updates; read-out of block j-1 (Aq, GELU(Aq), causal products, partial Z -> LDS); gate and stores of block j-2; staging",
         "loop to the next step",
     ],
     "coop": [
