@@ -244,6 +244,11 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
   const float* kb = qb + plane;
   const float* vb = qb + 2 * plane;
   const float tg = tanhf(a.alpha[ch]);
+  // staging: threads 0..127 move k_{t+2}, threads 128..255 q_{t+1} (element tid mod 128)
+  // from global memory into their LDS slot, which holds token (t + ahead) mod 4 / mod 2
+  const bool stager = tid < 2 * CD;
+  const int st_ahead = tid < CD ? 2 : 1, st_mask = tid < CD ? 3 : 1;
+  const float* st_src = tid < CD ? kb + tid : qb + (tid & (CD - 1));
 
   // sum over this lane's 16 rows of x . W1r (x: 16 consecutive floats in LDS)
   auto rows_dot = [&](const float* x) -> float {
@@ -295,10 +300,9 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         v0 = vb[tok(t) * CD + lane];
         v1 = vb[tok(t) * CD + lane + 64];
         // one unconditional load per thread (token clamped into range; only
-        // valid values are written to LDS): divergent loads into one register
-        // would make the second wait for the first
-        const int64_t tk = t + 2 < T ? t + 2 : T - 1, tq = t + 1 < T ? t + 1 : T - 1;
-        if (tid < 2 * CD) stage = tid < CD ? kb[tok(tk) * CD + tid] : qb[tok(tq) * CD + tid - CD];
+        // valid values are written to LDS)
+        const int64_t ts = t + st_ahead < T ? t + st_ahead : T - 1;
+        if (stager) stage = st_src[tok(ts) * CD];
       }
       if (writer && t > 0) xo = ld_io_bits(a.xin, ((int64_t)s * T + tok(t - 1)) * D + ch, bf16);
       TTT_MARK(g_marks_scan_coop, t, 1);
@@ -334,12 +338,9 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
       TTT_MARK(g_marks_scan_coop, t, 2);
       // ---- stage k_{t+2}, q_{t+1} (loaded at the top of this iteration); their
       //      slots held k_{t-2}, q_{t-1}, last read in the previous iteration
-      if (live) {
-        if (tid < CD) {
-          if (t + 2 < T) Ks[(t + 2) & 3][tid] = stage;
-        } else if (tid < 2 * CD && t + 1 < T) {
-          Qs[(t + 1) & 1][tid - CD] = stage;
-        }
+      if (stager && t + st_ahead < T) {
+        float* st_dst = tid < CD ? &Ks[0][tid] : &Qs[0][tid & (CD - 1)];
+        st_dst[((t + st_ahead) & st_mask) * CD] = stage;
       }
       // ---- publish this workgroup's partial of value 64 w + lane (waves 0, 1: yhat; 2, 3: z)
       const int64_t slot = xslots + (t & 1) * NCU * NVAL;
