@@ -73,12 +73,31 @@ constexpr int NVAL = 2 * CD;          // exchanged values per workgroup and toke
 constexpr uint32_t SPIN_MAX = 1u << 20;
 static_assert(UNITS == 64 && UW == 8 && PW == 16 && CD == 128 && NT == 4 * CD, "lane mapping assumes these sizes");
 
+// Phi(a) = (1 + erf(a / sqrt 2)) / 2, with erf of x = |a| / sqrt 2 >= 0 by Abramowitz
+// and Stegun, formula 7.1.26: erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-x^2),
+// t = 1 / (1 + p x), |error| <= 1.5e-7 for every x >= 0.  It has no branches (the
+// device erff takes two ranges, both of which a wave with mixed arguments runs), and
+// its e^(-x^2) = e^(-a^2 / 2) is the factor that GELU'(a) needs as well, returned in *e.
+__device__ __forceinline__ float normal_cdf(float a, float* e) {
+  const float x = fabsf(a) * 0.7071067811865476f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float p = 1.061405429f;
+  p = fmaf(p, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  *e = __builtin_amdgcn_exp2f(a * (a * -0.7213475204444817f));  // e^(-a^2/2) = 2^(-a^2 log2(e) / 2)
+  const float tail = 0.5f * (p * t) * *e;                         // (1 - erf(x)) / 2 = Phi(-|a|)
+  return a >= 0.0f ? 1.0f - tail : tail;
+}
+
 __device__ __forceinline__ float gelu_val(float a, bool tanh_form) {
   if (tanh_form) {
     const float u = 0.7978845608028654f * (a + 0.044715f * a * a * a);
     return 0.5f * a * (1.0f + tanhf(u));
   }
-  return 0.5f * a * (1.0f + erff(a * 0.7071067811865476f));
+  float e;
+  return a * normal_cdf(a, &e);
 }
 
 __device__ __forceinline__ void gelu_both(float a, bool tanh_form, float* g, float* dg) {
@@ -90,9 +109,10 @@ __device__ __forceinline__ void gelu_both(float a, bool tanh_form, float* g, flo
     *dg = 0.5f * (1.0f + th) + 0.5f * a * (1.0f - th * th) * 0.7978845608028654f * (1.0f + 3.0f * 0.044715f * a2);
     return;
   }
-  const float cdf = 0.5f * (1.0f + erff(a * 0.7071067811865476f));
+  float e;
+  const float cdf = normal_cdf(a, &e);
   *g = a * cdf;
-  *dg = cdf + a * 0.3989422804014327f * expf(-0.5f * a * a);
+  *dg = fmaf(a * 0.3989422804014327f, e, cdf);  // Phi(a) + a phi(a), phi(a) = e^(-a^2/2) / sqrt(2 pi)
 }
 
 // Raw bits of an io element; converted where used, so that the load's latency
