@@ -146,17 +146,21 @@ __device__ __forceinline__ void put(uint64_t* e, uint32_t tag, float v) {
   __hip_atomic_store(e, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Polls the n (0..4) entries e_idx[0..n) of token `tag` until all carry the tag
-// and returns their values in out[].  A poll issues all its loads before it looks
-// at any of them, so it costs one round trip.  Returns false on abort or time-out.
-__device__ bool poll(const uint64_t* base, int n, const int64_t* e_idx, uint32_t tag, uint32_t* abort_flag,
-                     float* out) {
-  if (n == 0) return true;
-  uint64_t e[4];
-  for (uint32_t spin = 0;; ++spin) {
+// One round of loads of the n (0..4) entries e_idx[0..n) into e[] (all issued
+// before any is looked at, so a round costs one round trip).
+__device__ __forceinline__ void poll_issue(const uint64_t* base, int n, const int64_t* e_idx, uint64_t (&e)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      e[i] = __hip_atomic_load(base + e_idx[i < n ? i : 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < 4; ++i)
+    e[i] = __hip_atomic_load(base + e_idx[i < n ? i : 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Completes a poll of token `tag` whose first round of loads, e[], was issued
+// earlier (poll_issue): loads again until all n entries carry the tag, and returns
+// their values in out[].  Returns false on abort or time-out.
+__device__ bool poll_finish(const uint64_t* base, int n, const int64_t* e_idx, uint32_t tag, uint32_t* abort_flag,
+                            uint64_t (&e)[4], float* out) {
+  if (n == 0) return true;
+  for (uint32_t spin = 0;; ++spin) {
     bool all = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) all = all && (uint32_t)(e[i] >> 32) == tag;
@@ -166,7 +170,8 @@ __device__ bool poll(const uint64_t* base, int n, const int64_t* e_idx, uint32_t
       return false;
     }
     if ((spin & 15) == 15 && __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
-    __builtin_amdgcn_s_sleep(1);
+    if (spin > 0) __builtin_amdgcn_s_sleep(1);
+    poll_issue(base, n, e_idx, e);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -371,6 +376,23 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         put(a.xchg + slot + cu * NVAL + 64 * w + lane, (uint32_t)t, p);
       }
       TTT_MARK(g_marks_scan_coop, t, 3);
+      // ---- the gather's entries: thread tid fetches yhat feature tid mod 128 from
+      //      workgroups 2 (tid / 128) and 2 (tid / 128) + 1, and (tid < 128) the z
+      //      partial of channel tid mod 16 from workgroup tid / 16, all in each round
+      //      of loads (one round trip).  The first round goes out in the middle of the
+      //      W1 pass below, about when the peers' partials land (measured: 1.44 s per
+      //      bigstate307k call, against 1.52 with the first round after the W1 pass,
+      //      1.50 after the W1 update, 1.47 after both pre-activations and 1.70 right
+      //      after publishing, whose extra rounds of polls lowered the shader clock).
+      int64_t e_idx[4] = {0, 0, 0, 0};
+      int n_e = 0;
+      if (live) {
+        for (int i = 0; i < 2; ++i) e_idx[i] = slot + (2 * (tid >> 7) + i) * NVAL + (tid & 127);
+        n_e = 2;
+      }
+      const bool zr = t > 0 && tid < 16 * NCU;
+      if (zr) e_idx[n_e++] = slot + (tid >> 4) * NVAL + CD + 16 * cu + (tid & 15);
+      uint64_t e_got[4];
       // ---- while the partials travel: token t-1's W1 update of this lane's rows (with
       //      k_{t-1} and its G1), then the pre-activations k_{t+1} W1_{t-1} and
       //      q_t W1_{t-1} of the unit (summed over its 8 lanes) and the dot products
@@ -388,6 +410,9 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
           W1r[4 * k4 + 3] = fmaf(ng1_prev, pv.w, W1r[4 * k4 + 3]);
         }
         a_pre = unit_sum8(rows_dot(Ks[(t + 1) & 3] + r0));
+        __builtin_amdgcn_sched_barrier(0);  // the first round of the gather's loads: here, not moved
+        poll_issue(a.xchg, n_e, e_idx, e_got);
+        __builtin_amdgcn_sched_barrier(0);
         aq_pre = unit_sum8(rows_dot(Qs[t & 1] + r0));
         const float* kc = Ks[t & 3];
         const float* kn = Ks[(t + 1) & 3];
@@ -395,25 +420,13 @@ __global__ __launch_bounds__(NT) void scan_coop_kernel(ScanArgs a) {
         skk = wave_sum64(fmaf(kn[lane], kc[lane], kn[lane + 64] * kc[lane + 64]));
         sqk = wave_sum64(fmaf(qc[lane], kc[lane], qc[lane + 64] * kc[lane + 64]));
       }
-      // ---- gather, spread over the workgroup: thread tid fetches yhat feature
-      //      tid mod 128 from workgroups 2 (tid / 128) and 2 (tid / 128) + 1, and
-      //      (tid < 128) the z partial of channel tid mod 16 from workgroup tid / 16,
-      //      all in one poll (one round trip); the sums follow through LDS in a fixed
-      //      order
+      // ---- the gather completes (the sums follow through LDS in a fixed order)
       {
-        int64_t e_idx[4] = {0, 0, 0, 0};
         float vals[4];
-        int n = 0;
-        if (live) {
-          for (int i = 0; i < 2; ++i) e_idx[i] = slot + (2 * (tid >> 7) + i) * NVAL + (tid & 127);
-          n = 2;
-        }
-        const bool zr = t > 0 && tid < 16 * NCU;
-        if (zr) e_idx[n++] = slot + (tid >> 4) * NVAL + CD + 16 * cu + (tid & 15);
-        const bool ok = !failed && poll(a.xchg, n, e_idx, (uint32_t)t, a.abort_flag, vals);
+        const bool ok = !failed && poll_finish(a.xchg, n_e, e_idx, (uint32_t)t, a.abort_flag, e_got, vals);
         if (ok && live)
           for (int i = 0; i < 2; ++i) Xv[2 * (tid >> 7) + i][tid & 127] = vals[i];
-        if (ok && zr) Zv[tid >> 4][tid & 15] = vals[n - 1];
+        if (ok && zr) Zv[tid >> 4][tid & 15] = vals[n_e - 1];
         if (!ok) __hip_atomic_store(&stop_wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         failed = !ok;
       }
