@@ -47,11 +47,14 @@ constexpr int TS = SB + 8;  // 24: rows of the [feature][token] G2 copy (48 byte
 // read takes in one lane group pair map to distinct banks
 constexpr int HKS_ROWS = 72;
 __device__ __forceinline__ int hk_row(int l) { return l + 8 * (l >> 5); }
-// issue pattern after the second barrier: each of the step's MIX_PRODUCTS matrix-core
-// products there (28 of the update, 15 of the read-out) followed by MIX_VALU vector
-// instructions (measured: 90.7 ms per bidir307k call, against 92.0 with 28 x 2,
-// 92.0 with 43 x 4, 92.7 with 36 x 3 and 92.9 with no pattern)
-constexpr int MIX_PRODUCTS = 43, MIX_VALU = 3;
+// issue pattern after the second barrier: the step's 43 matrix-core products there (28 of
+// the update, 15 of the read-out) in MIX_GROUPS groups of MIX_PRODUCTS, each followed by
+// MIX_VALU vector instructions.  Measured per bidir307k call on one box: 87.6-88.2 ms with
+// 11 groups of (4, 12), against 88.8 with (4, 14), 91.5 with (4, 10), 89.0-89.8 with 22
+// groups of (2, 6), 90.1 with (2, 7), 91.0 with (2, 5), 89.1 with 15 groups of (3, 9),
+// 91.1 with 8 of (6, 18) and 92.1 with 6 of (8, 24); on another box 43 groups of (1, 3)
+// took 90.7 ms against 93.1 with (1, 2), 92.0 with (1, 4), and 92.9 with no fixed pattern.
+constexpr int MIX_GROUPS = 11, MIX_PRODUCTS = 4, MIX_VALU = 12;
 constexpr int DGS = SB + 4;  // 20: rows of the fp32 [hidden][token] GELU' tiles (bank spread of the column writes)
 
 // GELU(a) = a Phi(a) and GELU'(a) = Phi(a) + a phi(a), with Phi from the
@@ -420,8 +423,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
     // two vector-ALU instructions, so that the read-out's GELU, the gate and the
     // packing work run beside the products instead of after them
 #pragma unroll
-    for (int i = 0; i < MIX_PRODUCTS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int i = 0; i < MIX_GROUPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MIX_PRODUCTS, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, MIX_VALU, 0);
     }
     if (j + AHEAD < nblk) stage_async(j + AHEAD, (int)((j + AHEAD) & (NSTAGE - 1)));
