@@ -273,9 +273,10 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2))) vo
   __syncthreads();
 
   // Step j runs block j's recurrence; after its second barrier, beside the state
-  // update, block j-1's read-out (at j = 0 on zero operands, never stored), whose
-  // partial Z is summed between the next step's barriers and stored after them.  The
-  // last block's read-out follows the loop.
+  // update, block j-1's read-out, whose partial Z is summed between the next step's
+  // barriers and stored after them (at j = 0 a dummy read-out on zero carried operands
+  // and whatever the eighth token buffer holds, whose Z is never stored).  The last
+  // block's read-out follows the loop.
   for (int64_t j = 0; j < nblk; ++j) {
     const int n = block_n(j);
     const uint16_t* blk = Stage[j & (NSTAGE - 1)];
