@@ -410,7 +410,8 @@ Chunking chunking(int64_t T) {
 // fewer than kProjMinWorkgroups are free.  The chip shares one power budget:
 // every CU the projection keeps busy lowers the clock the scan runs at, so the
 // cap is the fewest workgroups that still keep the projection ahead of the
-// scan (bidirectional layer at 307,200 tokens, 48 heads: 96 beats 80 and 112-160).
+// scan (bidirectional layer at 307,200 tokens, 48 heads: 96 beats 80 and 112-160;
+// re-measured with the faster scan, 88.4 ms per call against 89.9 at 88 and 91.0 at 80).
 constexpr int kProjWorkgroupsBesideScan = 96, kProjMinWorkgroups = 64;
 
 int proj_workgroups_beside_scan(int cus, int64_t scan_workgroups) {
